@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the DFlash block-drafter proposal pass on one MI355X.
+
+Workload (one step = one decode cycle): 8192 resident context cells, a block
+of anchor + 7 masks (block 8) drafted at the next position, greedy
+verification against a seeded stand-in target that agrees with each
+candidate with probability 0.75, and the commit (fusion + K/V projection) of
+the accepted cells plus the anchor.  Jobs of 96 committed tokens restart at
+position 8192 (position-addressed cells make rejected drafts harmless).
+
+Prints one JSON line.  Inputs are resident in HBM before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+CTX = 8192
+BLOCK = 8
+JOB_TOKENS = 96
+HBM_PEAK_GBS = 8000.0
+METRIC = "DFlash draft passes/sec (ctx 8192, block 8) + achieved HBM GB/s vs peak"
+
+
+def pass_bytes(n_ctx: int, block: int = BLOCK) -> int:
+    """Algorithmic HBM bytes of one draft pass: every layer matrix and the LM
+    head once, the gains, the distinct embedding rows and n_ctx fp16 K/V
+    cells (5 layers x 2 KV heads x 256 x K and V)."""
+    from block_draft_model_pass_amd import synth as S
+    H, D, F = S.HIDDEN, S.HEAD_DIM, S.FFN
+    qkv = (S.N_Q_HEADS + 2 * S.N_KV_HEADS) * D * H
+    layer = qkv + H * S.N_Q_HEADS * D + 2 * F * H + H * F
+    mats = 2 * S.N_LAYERS * layer
+    gains = 2 * (S.N_LAYERS * (2 * H + 2 * D) + H)
+    lm = 2 * S.VOCAB * H if block > 1 else 0
+    emb = 2 * H * (2 if block > 1 else 1)
+    kv = n_ctx * S.N_LAYERS * S.N_KV_HEADS * D * 2 * 2
+    return mats + gains + lm + emb + kv
+
+
+def lm_head_bytes() -> int:
+    from block_draft_model_pass_amd import synth as S
+    return 2 * S.VOCAB * S.HIDDEN
+
+
+def cpu_baseline(host_w, budget_s: float):
+    """The oracle's decode cycle at ctx 8192 / block 8 on the host cores."""
+    from threadpoolctl import threadpool_info
+
+    from block_draft_model_pass_amd import synth
+    from oracle import dflash_oracle as O
+    w = O.enable_cache(dict(host_w))
+    store = O.ContextStore()
+    for s in range(0, CTX, 2048):
+        taps = synth.make_taps(range(s, s + 2048))
+        store.put(*O.project_ctx_kv(w, O.fuse_context(w, taps), s), s)
+    K = BLOCK - 1
+    p, anchor = CTX, synth.anchor_token(0)
+    ck, cv = store.window(p)
+    O.draft_block(w, ck, cv, p, anchor, synth.MASK_ID, BLOCK)  # fills the decode cache
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s or n < 2:
+        ck, cv = store.window(p)
+        ref = O.draft_block(w, ck, cv, p, anchor, synth.MASK_ID, BLOCK)
+        tgt = synth.synthetic_target(ref["cand"], n)
+        a, nxt = O.verify_greedy(ref["cand"], tgt)
+        taps = synth.make_taps(range(p, p + a + 1))
+        store.put(*O.project_ctx_kv(w, O.fuse_context(w, taps), p), p)
+        p, anchor = p + a + 1, nxt
+        n += 1
+    dt = time.perf_counter() - t0
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    return {"value": n / dt, "unit": "passes/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} decode cycles (draft + verify + commit) of the fp64 numpy oracle "
+                      f"at ctx {CTX}, block {BLOCK}, {dt:.1f} s; weights pre-decoded"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="time budget of the CPU-oracle baseline (0 = skip)")
+    ap.add_argument("--reps", type=int, default=50, help="repeats of the event-timed kernels")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the pass would shard as described in DESIGN.md but no multi-GPU path exists.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_draft_model_pass_amd import synth
+    from block_draft_model_pass_amd.device import DeviceWeights, Drafter, KVRing, to_device
+
+    torch.cuda.set_device(0)
+    host_w = synth.make_weights()
+    dw = DeviceWeights(host_w)
+    kv = KVRing(synth.WINDOW, synth.WINDOW)
+    dr = Drafter(dw, kv, max_rows=CTX)
+    V = dw.vocab
+    K = BLOCK - 1
+
+    # Context 0..8191 and the taps of every position a job can commit.
+    span = CTX + JOB_TOKENS + BLOCK
+    taps_all = to_device(synth.make_taps(range(span)))
+    dr.commit(taps_all[:CTX], 0)
+    n_pass = args.steps + args.warmup
+    draws = [synth.target_draws(t, K) for t in range(n_pass)]
+    match = torch.tensor(np.stack([d[0] for d in draws]), device="cuda")
+    offset = torch.tensor(np.stack([d[1] for d in draws]), dtype=torch.int64, device="cuda")
+    tail = torch.tensor([d[2] for d in draws], dtype=torch.int32, device="cuda")
+    cand = torch.empty(K, dtype=torch.int32, device="cuda")
+    out = torch.empty(2, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+
+    state = {"p": CTX, "anchor": synth.anchor_token(0), "job": 0, "acc": 0, "off": 0}
+
+    def cycle(t):
+        dr.draft(state["p"], state["anchor"], BLOCK, cand=cand)
+        c = cand.to(torch.int64)
+        tgt = torch.where(match[t], c, (c + 1 + offset[t]) % V).to(torch.int32)
+        tgt = torch.cat([tgt, tail[t:t + 1]])
+        dr.verify(cand, tgt, K, out=out)
+        a, nxt = out.tolist()  # the cycle's one device->host read
+        p = state["p"]
+        dr.commit(taps_all[p:p + a + 1], p)
+        state["acc"] += a
+        state["off"] += K
+        state["p"], state["anchor"] = p + a + 1, nxt
+        if state["p"] - CTX >= JOB_TOKENS:
+            state["job"] += 1
+            state["p"], state["anchor"] = CTX, synth.anchor_token(state["job"])
+
+    for t in range(args.warmup):
+        cycle(t)
+    state["acc"] = state["off"] = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.warmup, n_pass):
+        cycle(t)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    value = args.steps / dt
+
+    # Draft pass alone, back to back at ctx 8192 (HIP events on the stream).
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(5):
+        dr.draft(CTX, 11, BLOCK, cand=cand)
+    ev[0].record()
+    for _ in range(args.reps):
+        dr.draft(CTX, 11, BLOCK, cand=cand)
+    ev[1].record()
+    torch.cuda.synchronize()
+    draft_ms = ev[0].elapsed_time(ev[1]) / args.reps
+    draft_gbs = pass_bytes(CTX) / (draft_ms * 1e-3) / 1e9
+
+    # Dominant kernel: LM head + greedy argmax over the 151936-row vocabulary.
+    z = torch.randn((K, synth.HIDDEN), device="cuda").to(torch.bfloat16).view(torch.int16)
+    for _ in range(5):
+        dr.lm_head_argmax(z, cand)
+    ev[0].record()
+    for _ in range(args.reps):
+        dr.lm_head_argmax(z, cand)
+    ev[1].record()
+    torch.cuda.synchronize()
+    lm_ms = ev[0].elapsed_time(ev[1]) / args.reps
+    lm_gbs = lm_head_bytes() / (lm_ms * 1e-3) / 1e9
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(host_w, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "passes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * dt / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "DFlash decode cycle: 8192 resident context cells, block 8 "
+                               "(anchor + 7 masks), greedy verify vs Bernoulli(0.75) stand-in "
+                               "target, commit of accepted cells; 96-token jobs",
+                   "ctx": CTX, "block": BLOCK, "vocab": V, "backbone": "bf16"},
+        "draft_only": {"ms_per_pass": round(draft_ms, 4),
+                       "passes_per_s": round(1e3 / draft_ms, 2),
+                       "algorithmic_bytes": pass_bytes(CTX),
+                       "achieved_GBs": round(draft_gbs, 1),
+                       "frac_hbm_peak": round(draft_gbs / HBM_PEAK_GBS, 4)},
+        "roofline": {"kernel": "k_lmhead_bf16 (+ k_argmax_reduce), dflash_lm_head_argmax",
+                     "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "launch_ms": round(lm_ms, 4),
+                     "bytes_per_launch": lm_head_bytes()},
+        "accepted_offered": [state["acc"], state["off"]],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,369 @@
+// C ABI entry points: argument validation, workspace carving and the launch
+// sequence of each operation.  Everything is enqueued on the caller's stream;
+// positions and sizes travel as kernel arguments (no host staging buffers).
+#include "../../include/dflash.h"
+#include "common.h"
+
+#include <string.h>
+
+using namespace dfl;
+
+namespace {
+
+constexpr int NCH_MAX = 256;          // context chunks of the attention split
+constexpr int NCH_TARGET = 128;       // chunks per KV head aimed for
+constexpr int LMH_GRID = 1024;        // LM-head blocks (grid-stride over tiles)
+constexpr int SMALL_ROWS = 64;        // fuse/project: skinny path up to here
+constexpr int FC_SPLITS = 5;          // k splits of the fc GEMV (K = 12800)
+constexpr int O_SPLITS = 3;           // k splits of the O GEMV (K = 6144)
+constexpr int DOWN_SPLITS = 3;        // k splits of the down GEMV (K = 7680)
+constexpr size_t PART_FLOATS = static_cast<size_t>(FC_SPLITS) * GEMV_ROWS * H;
+
+struct Layout {
+  size_t h, xn, part, q16, kblk, vblkT, po, pm, pl, o16, u16, keys, y;
+  size_t fixed;  // bytes before y
+};
+
+size_t take(size_t& off, size_t bytes) {
+  const size_t o = off;
+  off = (off + bytes + 255) & ~static_cast<size_t>(255);
+  return o;
+}
+
+Layout layout() {
+  Layout L;
+  size_t off = 0;
+  const size_t nqt = 6, nc = NCH_MAX + 1;
+  L.h = take(off, sizeof(float) * MAXB * H);
+  L.xn = take(off, 2 * MAXB * H);
+  L.part = take(off, sizeof(float) * PART_FLOATS);
+  L.q16 = take(off, 2 * MAXB * NQ * D);
+  L.kblk = take(off, 2 * NKV * BLK_CELLS * D);
+  L.vblkT = take(off, 2 * NKV * D * BLK_CELLS);
+  L.po = take(off, sizeof(float) * NKV * nc * nqt * 16 * D);
+  L.pm = take(off, sizeof(float) * NKV * nc * nqt * 16);
+  L.pl = take(off, sizeof(float) * NKV * nc * nqt * 16);
+  L.o16 = take(off, 2 * MAXB * NQ * D);
+  L.u16 = take(off, 2 * MAXB * F);
+  L.keys = take(off, sizeof(uint64_t) * LMH_GRID * MAXB);
+  L.fixed = off;
+  L.y = off;
+  return L;
+}
+
+size_t rows_bytes(int rows) {
+  return rows > SMALL_ROWS ? sizeof(float) * static_cast<size_t>(rows) * KV_N : 0;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int check_weights(const dflash_weights* w) {
+  if (!w) return DFLASH_EINVAL;
+  if (w->hidden != H || w->n_layers != L || w->n_q_heads != NQ || w->n_kv_heads != NKV ||
+      w->head_dim != D || w->ffn != F || w->n_taps != T)
+    return DFLASH_EGEOMETRY;
+  if (w->vocab < 16 || w->vocab % 16 != 0 || w->vocab > (1 << 24)) return DFLASH_EGEOMETRY;
+  if (w->rope_theta != 1.0e7f || w->attn_scale != 0.0625f || w->rms_eps != 1.0e-6f)
+    return DFLASH_EGEOMETRY;
+  if (w->backbone_type != DFLASH_W_BF16) return DFLASH_EINVAL;
+  if (!w->fc || !w->hidden_norm || !w->final_norm || !w->embed || !w->lm_head)
+    return DFLASH_EINVAL;
+  for (int l = 0; l < L; ++l) {
+    const dflash_layer_weights& y = w->layer[l];
+    if (!y.in_norm || !y.wq || !y.wk || !y.wv || !y.q_norm || !y.k_norm || !y.wo ||
+        !y.post_norm || !y.wg || !y.wu || !y.wd)
+      return DFLASH_EINVAL;
+  }
+  return DFLASH_OK;
+}
+
+int check_kv(const dflash_kv* kv) {
+  if (!kv || !kv->k || !kv->vt) return DFLASH_EINVAL;
+  if (kv->capacity <= 0 || kv->capacity % 256 != 0) return DFLASH_ERANGE;
+  if (kv->window <= 0 || kv->window > kv->capacity) return DFLASH_ERANGE;
+  return DFLASH_OK;
+}
+
+SegTable seg1(const void* p, int rows) {
+  SegTable t;
+  memset(&t, 0, sizeof(t));
+  t.ptr[0] = p;
+  t.row_end[0] = rows;
+  t.nseg = 1;
+  return t;
+}
+
+SegTable seg_qkv(const dflash_layer_weights& y) {
+  SegTable t;
+  memset(&t, 0, sizeof(t));
+  t.ptr[0] = y.wq;
+  t.row_end[0] = NQ * D;
+  t.ptr[1] = y.wk;
+  t.row_end[1] = NQ * D + NKV * D;
+  t.ptr[2] = y.wv;
+  t.row_end[2] = QKV_N;
+  t.nseg = 3;
+  return t;
+}
+
+SegTable seg_kv(const dflash_weights* w) {
+  SegTable t;
+  memset(&t, 0, sizeof(t));
+  for (int l = 0; l < L; ++l) {
+    t.ptr[2 * l] = w->layer[l].wk;
+    t.row_end[2 * l] = (2 * l + 1) * NKV * D;
+    t.ptr[2 * l + 1] = w->layer[l].wv;
+    t.row_end[2 * l + 1] = (2 * l + 2) * NKV * D;
+  }
+  t.nseg = 2 * L;
+  return t;
+}
+
+#define HIP_TRY(expr)                                   \
+  do {                                                  \
+    if ((expr) != hipSuccess) return DFLASH_EHIP;       \
+  } while (0)
+
+const uint16_t* u16p(const void* p) { return static_cast<const uint16_t*>(p); }
+
+}  // namespace
+
+extern "C" size_t dflash_workspace_size(const dflash_weights* w, int32_t max_rows,
+                                        int32_t max_block) {
+  (void)w;
+  if (max_rows < 0 || max_block < 0 || max_block > MAXB) return 0;
+  return layout().fixed + rows_bytes(max_rows);
+}
+
+extern "C" int32_t dflash_fuse_context(const dflash_weights* w, const void* taps, int32_t n,
+                                       void* ctx, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_weights(w);
+  if (rc) return rc;
+  if (n < 0) return DFLASH_EINVAL;
+  if (n == 0) return DFLASH_OK;
+  if (!taps || !ctx || !ws) return DFLASH_EINVAL;
+  const Layout Lw = layout();
+  if (ws_bytes < Lw.fixed + rows_bytes(n)) return DFLASH_EWORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint16_t* x = u16p(taps);
+  uint16_t* out = static_cast<uint16_t*>(ctx);
+  if (n <= SMALL_ROWS) {
+    float* part = at<float>(ws, Lw.part);
+    for (int c0 = 0; c0 < n; c0 += GEMV_ROWS) {
+      const int rows = n - c0 < GEMV_ROWS ? n - c0 : GEMV_ROWS;
+      GemvArgs a;
+      a.w = seg1(w->fc, H);
+      a.fmt = W_BF16;
+      a.N = H;
+      a.K = T * H;
+      a.x = x + static_cast<size_t>(c0) * T * H;
+      a.x_stride = T * H;
+      a.B = rows;
+      a.out = part;
+      a.S = FC_SPLITS;
+      HIP_TRY(launch_gemv(a, st));
+      HIP_TRY(launch_rownorm(nullptr, part, FC_SPLITS, static_cast<size_t>(rows) * H, H, rows,
+                             u16p(w->hidden_norm), w->rms_eps, out + static_cast<size_t>(c0) * H,
+                             H, nullptr, st));
+    }
+  } else {
+    float* y = at<float>(ws, Lw.y);
+    HIP_TRY(launch_gemm_bf16(x, T * H, n, seg1(w->fc, H), T * H, y, H, H, st));
+    HIP_TRY(launch_rownorm(nullptr, y, 1, 0, H, n, u16p(w->hidden_norm), w->rms_eps, out, H,
+                           nullptr, st));
+  }
+  return DFLASH_OK;
+}
+
+extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ctx, int32_t n,
+                                         int64_t pos0, const dflash_kv* kv, void* ws,
+                                         size_t ws_bytes, void* stream) {
+  int rc = check_weights(w);
+  if (rc) return rc;
+  rc = check_kv(kv);
+  if (rc) return rc;
+  if (n < 0 || pos0 < 0) return DFLASH_EINVAL;
+  if (n > kv->capacity) return DFLASH_ERANGE;
+  if (n == 0) return DFLASH_OK;
+  if (!ctx || !ws) return DFLASH_EINVAL;
+  const Layout Lw = layout();
+  if (ws_bytes < Lw.fixed + rows_bytes(n)) return DFLASH_EWORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const void* knorms[L];
+  for (int l = 0; l < L; ++l) knorms[l] = w->layer[l].k_norm;
+  const uint16_t* x = u16p(ctx);
+  uint16_t* rk = static_cast<uint16_t*>(kv->k);
+  uint16_t* rv = static_cast<uint16_t*>(kv->vt);
+  const double theta = static_cast<double>(w->rope_theta);
+  if (n <= SMALL_ROWS) {
+    float* part = at<float>(ws, Lw.part);
+    for (int c0 = 0; c0 < n; c0 += GEMV_ROWS) {
+      const int rows = n - c0 < GEMV_ROWS ? n - c0 : GEMV_ROWS;
+      GemvArgs a;
+      a.w = seg_kv(w);
+      a.fmt = W_BF16;
+      a.N = KV_N;
+      a.K = H;
+      a.x = x + static_cast<size_t>(c0) * H;
+      a.x_stride = H;
+      a.B = rows;
+      a.out = part;
+      a.S = 1;
+      HIP_TRY(launch_gemv(a, st));
+      HIP_TRY(launch_kv_post(part, 1, 0, KV_N, rows, pos0 + c0, knorms, w->rms_eps, theta, rk, rv,
+                             kv->capacity, st));
+    }
+  } else {
+    float* y = at<float>(ws, Lw.y);
+    HIP_TRY(launch_gemm_bf16(x, H, n, seg_kv(w), H, y, KV_N, KV_N, st));
+    HIP_TRY(launch_kv_post(y, 1, 0, KV_N, n, pos0, knorms, w->rms_eps, theta, rk, rv,
+                           kv->capacity, st));
+  }
+  return DFLASH_OK;
+}
+
+extern "C" int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* kv, int64_t p,
+                                      int32_t anchor_id, int32_t mask_id, int32_t block,
+                                      int32_t* cand, void* logits_opt, void* hidden_opt,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_weights(w);
+  if (rc) return rc;
+  rc = check_kv(kv);
+  if (rc) return rc;
+  if (block < 1 || block > MAXB || p < 0) return DFLASH_EINVAL;
+  if (anchor_id < 0 || anchor_id >= w->vocab || mask_id < 0 || mask_id >= w->vocab)
+    return DFLASH_EINVAL;
+  if (!ws || (block > 1 && !cand)) return DFLASH_EINVAL;
+  const Layout Lw = layout();
+  if (ws_bytes < Lw.fixed) return DFLASH_EWORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int B = block;
+  const float eps = w->rms_eps;
+  const double theta = static_cast<double>(w->rope_theta);
+
+  float* h = at<float>(ws, Lw.h);
+  uint16_t* xn = at<uint16_t>(ws, Lw.xn);
+  float* part = at<float>(ws, Lw.part);
+  uint16_t* q16 = at<uint16_t>(ws, Lw.q16);
+  uint16_t* kblk = at<uint16_t>(ws, Lw.kblk);
+  uint16_t* vblkT = at<uint16_t>(ws, Lw.vblkT);
+  uint16_t* o16 = at<uint16_t>(ws, Lw.o16);
+  uint16_t* u16 = at<uint16_t>(ws, Lw.u16);
+
+  // Attention split over the visible context [lo, p).
+  AttnArgs at_args;
+  at_args.q16 = q16;
+  at_args.B = B;
+  at_args.nqt = (G * B + 15) / 16;
+  at_args.cap = kv->capacity;
+  at_args.lo = p - kv->window > 0 ? p - kv->window : 0;
+  at_args.hi = p;
+  if (p > at_args.lo) {
+    at_args.p0 = at_args.lo & ~static_cast<int64_t>(31);
+    at_args.nb = static_cast<int>((p - at_args.p0 + 31) / 32);
+    at_args.cb = (at_args.nb + NCH_TARGET - 1) / NCH_TARGET;
+    at_args.nch = (at_args.nb + at_args.cb - 1) / at_args.cb;
+  } else {
+    at_args.p0 = 0;
+    at_args.nb = 0;
+    at_args.cb = 1;
+    at_args.nch = 0;
+  }
+  if (at_args.nch > NCH_MAX) return DFLASH_ERANGE;
+  at_args.kblk = kblk;
+  at_args.vblkT = vblkT;
+  at_args.scale_log2 = w->attn_scale * 1.4426950408889634f;
+  at_args.po = at<float>(ws, Lw.po);
+  at_args.pm = at<float>(ws, Lw.pm);
+  at_args.pl = at<float>(ws, Lw.pl);
+  at_args.o16 = o16;
+
+  HIP_TRY(launch_embed_norm(u16p(w->embed), anchor_id, mask_id, B, u16p(w->layer[0].in_norm), eps,
+                            h, xn, st));
+  for (int l = 0; l < L; ++l) {
+    const dflash_layer_weights& y = w->layer[l];
+    GemvArgs a;
+    a.w = seg_qkv(y);
+    a.fmt = W_BF16;
+    a.N = QKV_N;
+    a.K = H;
+    a.x = xn;
+    a.x_stride = H;
+    a.B = B;
+    a.out = part;
+    a.S = 1;
+    HIP_TRY(launch_gemv(a, st));
+    HIP_TRY(launch_qkv_post(part, 1, B, p, u16p(y.q_norm), u16p(y.k_norm), eps, theta, q16, kblk,
+                            vblkT, st));
+    at_args.ring_k = static_cast<const uint16_t*>(kv->k) +
+                     static_cast<size_t>(l) * NKV * kv->capacity * D;
+    at_args.ring_vt = static_cast<const uint16_t*>(kv->vt) +
+                      static_cast<size_t>(l) * NKV * D * kv->capacity;
+    HIP_TRY(launch_attention(at_args, st));
+    a.w = seg1(y.wo, H);
+    a.N = H;
+    a.K = NQ * D;
+    a.x = o16;
+    a.x_stride = NQ * D;
+    a.S = O_SPLITS;
+    HIP_TRY(launch_gemv(a, st));
+    HIP_TRY(launch_rownorm(h, part, O_SPLITS, static_cast<size_t>(B) * H, H, B,
+                           u16p(y.post_norm), eps, xn, H, nullptr, st));
+    HIP_TRY(launch_gateup(y.wg, y.wu, W_BF16, xn, B, u16, st));
+    a.w = seg1(y.wd, H);
+    a.K = F;
+    a.x = u16;
+    a.x_stride = F;
+    a.S = DOWN_SPLITS;
+    HIP_TRY(launch_gemv(a, st));
+    const bool last = l == L - 1;
+    HIP_TRY(launch_rownorm(h, part, DOWN_SPLITS, static_cast<size_t>(B) * H, H, B,
+                           u16p(last ? w->final_norm : w->layer[l + 1].in_norm), eps, xn, H,
+                           last ? static_cast<uint16_t*>(hidden_opt) : nullptr, st));
+  }
+  if (B > 1) {
+    HIP_TRY(launch_lmhead_argmax(u16p(w->lm_head), w->vocab, xn + H, B - 1,
+                                 at<uint64_t>(ws, Lw.keys), LMH_GRID,
+                                 static_cast<uint16_t*>(logits_opt), cand, st));
+  }
+  return DFLASH_OK;
+}
+
+extern "C" int32_t dflash_lm_head_argmax(const dflash_weights* w, const void* hidden,
+                                         int32_t rows, int32_t* cand, void* logits_opt, void* ws,
+                                         size_t ws_bytes, void* stream) {
+  int rc = check_weights(w);
+  if (rc) return rc;
+  if (rows < 1 || rows > MAXB || !hidden || !cand || !ws) return DFLASH_EINVAL;
+  const Layout Lw = layout();
+  if (ws_bytes < Lw.fixed) return DFLASH_EWORKSPACE;
+  HIP_TRY(launch_lmhead_argmax(u16p(w->lm_head), w->vocab, u16p(hidden), rows,
+                               at<uint64_t>(ws, Lw.keys), LMH_GRID,
+                               static_cast<uint16_t*>(logits_opt), cand,
+                               static_cast<hipStream_t>(stream)));
+  return DFLASH_OK;
+}
+
+extern "C" int32_t dflash_verify_greedy(const int32_t* cand, const int32_t* target, int32_t k,
+                                        int32_t* out, void* stream) {
+  if (k < 0 || k > MAXB - 1) return DFLASH_EINVAL;
+  if (!target || !out || (k > 0 && !cand)) return DFLASH_EINVAL;
+  if (launch_verify(cand, target, k, out, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DFLASH_EHIP;
+  return DFLASH_OK;
+}
+
+extern "C" const char* dflash_strerror(int32_t code) {
+  switch (code) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_EINVAL: return "invalid argument";
+    case DFLASH_EGEOMETRY: return "descriptor does not match the DFlash geometry";
+    case DFLASH_ERANGE: return "K/V ring capacity/window/range violation";
+    case DFLASH_EWORKSPACE: return "workspace too small";
+    case DFLASH_EHIP: return "HIP launch failed";
+    default: return "unknown error";
+  }
+}

@@ -1,0 +1,203 @@
+// Device helpers and internal launch interfaces of the DFlash HIP library.
+// gfx950 (CDNA4) only: 64-lane wavefronts, MFMA 16x16x32 bf16/fp16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dfl {
+
+// Fixed geometry (Strata PR #1426 page, "Drafter runtime").
+constexpr int H = 2560;          // hidden
+constexpr int L = 5;             // layers
+constexpr int NQ = 24;           // query heads
+constexpr int NKV = 2;           // key/value heads
+constexpr int G = NQ / NKV;      // query heads per KV head (12)
+constexpr int D = 256;           // head dim
+constexpr int F = 7680;          // MLP width
+constexpr int T = 5;             // target taps
+constexpr int QKV_N = NQ * D + 2 * NKV * D;  // 7168 fused q|k|v rows
+constexpr int KV_N = L * 2 * NKV * D;        // 5120 rows of [Wk_l; Wv_l] x 5
+constexpr int MAXB = 8;          // max block rows
+constexpr int GEMV_ROWS = 16;    // max activation rows of one skinny GEMV
+constexpr int BLK_CELLS = 32;    // cells of the block-key buffer
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- numbers
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  _Float16 h = static_cast<_Float16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Order-preserving map of a finite fp32 to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t f32_order_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// argmax key: value in the high word, inverted index in the low word, so
+// that an unsigned max picks the largest value and, among equal values, the
+// lowest index.
+__device__ __forceinline__ uint64_t argmax_key(float v, uint32_t idx) {
+  return (static_cast<uint64_t>(f32_order_key(v)) << 32) | static_cast<uint64_t>(~idx);
+}
+
+// ---------------------------------------------------------------- MFMA
+
+// D[16][16] += A[16][32] * B[32][16].  Lane l supplies row (l % 16) of A and
+// column (l % 16) of B, 8 consecutive k values each (the same k slots for A
+// and B); it receives D rows 4*(l/16) .. 4*(l/16)+3 of column l % 16.
+__device__ __forceinline__ f32x4 mfma_bf16(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f16(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- reductions
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Sum over the 4 lanes l, l^16, l^32, l^48 (the four k-groups of an MFMA column).
+__device__ __forceinline__ float group4_sum(float v) {
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+__device__ __forceinline__ float group4_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+
+// Block-wide sum for blockDim.x == NT (multiple of 64); all threads get it.
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* scratch /* [NT/64] */) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) scratch[w] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) s += scratch[i];
+  __syncthreads();
+  return s;
+}
+
+// ---------------------------------------------------------------- launches
+
+// Row segments of one logical weight matrix stored in several buffers,
+// concatenated along the output dimension.  Every segment's row count is a
+// multiple of 128, so a 16- or 128-row tile never straddles two segments.
+struct SegTable {
+  const void* ptr[10];
+  int row_end[10];   // cumulative
+  int nseg;
+};
+
+enum WFormat { W_BF16 = 0, W_Q8_0 = 1, W_Q4_0 = 2 };
+
+// y[s][b][n] = sum over split s of k of W[n][k] * x[b][k]   (b < B <= 16)
+struct GemvArgs {
+  SegTable w;
+  int fmt;               // WFormat
+  int N, K;
+  const uint16_t* x;     // bf16 [B][x_stride]
+  int x_stride;
+  int B;
+  float* out;            // fp32 [S][B][N]
+  int S;
+};
+
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t st);
+
+// u[b][n] = silu(Wg x)[n] * (Wu x)[n], bf16 out [B][F]
+hipError_t launch_gateup(const void* wg, const void* wu, int fmt, const uint16_t* x, int B,
+                         uint16_t* u, hipStream_t st);
+
+// LM head + greedy argmax over the vocabulary.
+hipError_t launch_lmhead_argmax(const uint16_t* lm, int vocab, const uint16_t* z, int B,
+                                uint64_t* keys, int grid, uint16_t* logits_opt,
+                                int32_t* cand, hipStream_t st);
+
+// Row RMSNorm: v = (h ? h[b] : 0) + sum_s part[s][b]; if h, h[b] = v;
+// out[b] = bf16(v * rsqrt(mean(v^2) + eps) * gain); out2 (optional) the same.
+hipError_t launch_rownorm(float* h, const float* part, int S, size_t part_split_stride,
+                          int part_row_stride, int rows, const uint16_t* gain, float eps,
+                          uint16_t* out, int out_stride, uint16_t* out2, hipStream_t st);
+
+hipError_t launch_embed_norm(const uint16_t* embed, int anchor, int mask, int B,
+                             const uint16_t* gain, float eps, float* h, uint16_t* xn,
+                             hipStream_t st);
+
+// Per-head q/k RMSNorm + NeoX RoPE of the fused QKV output of the block rows.
+hipError_t launch_qkv_post(const float* part, int S, int B, int64_t p,
+                           const uint16_t* q_norm, const uint16_t* k_norm, float eps,
+                           double theta, uint16_t* q16, uint16_t* kblk, uint16_t* vblkT,
+                           hipStream_t st);
+
+// Context K/V epilogue: y [n][KV_N] (row stride ldy, S partial splits) ->
+// k-norm + RoPE + fp16 into the ring.
+hipError_t launch_kv_post(const float* y, int S, size_t split_stride, int ldy, int n,
+                          int64_t pos0, const void* const* k_norms, float eps, double theta,
+                          uint16_t* ring_k, uint16_t* ring_vt, int capacity, hipStream_t st);
+
+struct AttnArgs {
+  const uint16_t* q16;     // fp16 [B][24][256]
+  int B;
+  int nqt;                 // query tiles of 16 rows: ceil(12 B / 16)
+  // context segment (ring) for chunks < nch
+  const uint16_t* ring_k;  // fp16 [2][cap][256] for this layer
+  const uint16_t* ring_vt; // fp16 [2][256][cap]
+  int cap;
+  int64_t lo, hi;          // visible positions [lo, hi)
+  int64_t p0;              // first position of block 0 (multiple of 32)
+  int nb;                  // 32-cell blocks covering [p0, hi)
+  int cb;                  // blocks per chunk
+  int nch;                 // context chunks
+  // block keys (chunk index nch)
+  const uint16_t* kblk;    // fp16 [2][32][256]
+  const uint16_t* vblkT;   // fp16 [2][256][32]
+  float scale_log2;        // attn_scale * log2(e)
+  float* po;               // [2][nch+1][nqt][16][256]
+  float* pm;               // [2][nch+1][nqt][16]
+  float* pl;               // [2][nch+1][nqt][16]
+  uint16_t* o16;           // bf16 [B][24*256]
+};
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+
+// C[M][N] (fp32, ldc) = A[M][K] (bf16, lda) * W[N][K]^T
+hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w, int K,
+                            float* C, int ldc, int N, hipStream_t st);
+
+hipError_t launch_verify(const int32_t* cand, const int32_t* target, int k, int32_t* out,
+                         hipStream_t st);
+
+}  // namespace dfl

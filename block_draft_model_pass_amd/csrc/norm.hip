@@ -1,0 +1,192 @@
+// Row-wise epilogues of the pass: residual add + RMSNorm, the embedding
+// gather, and the per-head q/k RMSNorm + NeoX RoPE of block rows and of
+// context K/V cells (Strata PR #1426 page, "Drafter runtime": full-head NeoX
+// RoPE, theta 1e7; "Parity validation": q raw -> q normed -> q).
+#include "common.h"
+
+namespace dfl {
+
+namespace {
+
+constexpr int NT = 256;             // threads per row
+constexpr int PER = H / NT;         // 10 elements per thread
+
+__global__ __launch_bounds__(NT) void k_rownorm(float* h, const float* part, int S,
+                                                size_t sstride, int rstride, const uint16_t* gain,
+                                                float eps, uint16_t* out, int ostride,
+                                                uint16_t* out2) {
+  __shared__ float red[NT / 64];
+  const int b = blockIdx.x;
+  float v[PER];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = threadIdx.x + NT * i;
+    float x = h ? h[static_cast<size_t>(b) * H + e] : 0.f;
+    for (int s = 0; s < S; ++s) x += part[s * sstride + static_cast<size_t>(b) * rstride + e];
+    v[i] = x;
+    ss += x * x;
+  }
+  if (h) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) h[static_cast<size_t>(b) * H + threadIdx.x + NT * i] = v[i];
+  }
+  ss = block_sum<NT>(ss, red);
+  const float sc = 1.0f / sqrtf(ss / static_cast<float>(H) + eps);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = threadIdx.x + NT * i;
+    const uint16_t y = f32_to_bf16(v[i] * sc * bf16_to_f32(gain[e]));
+    out[static_cast<size_t>(b) * ostride + e] = y;
+    if (out2) out2[static_cast<size_t>(b) * H + e] = y;
+  }
+}
+
+__global__ __launch_bounds__(NT) void k_embed_norm(const uint16_t* embed, int anchor, int mask,
+                                                   const uint16_t* gain, float eps, float* h,
+                                                   uint16_t* xn) {
+  __shared__ float red[NT / 64];
+  const int b = blockIdx.x;
+  const int tok = b == 0 ? anchor : mask;
+  const uint16_t* row = embed + static_cast<size_t>(tok) * H;
+  float v[PER];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = threadIdx.x + NT * i;
+    v[i] = bf16_to_f32(row[e]);
+    h[static_cast<size_t>(b) * H + e] = v[i];
+    ss += v[i] * v[i];
+  }
+  ss = block_sum<NT>(ss, red);
+  const float sc = 1.0f / sqrtf(ss / static_cast<float>(H) + eps);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = threadIdx.x + NT * i;
+    xn[static_cast<size_t>(b) * H + e] = f32_to_bf16(v[i] * sc * bf16_to_f32(gain[e]));
+  }
+}
+
+// RMSNorm over one 256-wide head held as (a, c) = elements (t, t + 128) of
+// thread t, then NeoX rotation of the pair by angle pos * theta^(-2t/256).
+// The angle, its sine and its cosine are computed in fp64.
+__device__ __forceinline__ void norm_rope(float& a, float& c, const uint16_t* gain, float eps,
+                                          int64_t pos, double theta, float* red) {
+  const int t = threadIdx.x;
+  const float ss = block_sum<128>(a * a + c * c, red);
+  const float sc = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
+  a *= sc * bf16_to_f32(gain[t]);
+  c *= sc * bf16_to_f32(gain[t + 128]);
+  const double inv = pow(theta, -2.0 * static_cast<double>(t) / static_cast<double>(D));
+  const double ang = static_cast<double>(pos) * inv;
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  const float fc = static_cast<float>(cs), fs = static_cast<float>(sn);
+  const float a2 = a * fc - c * fs;
+  const float c2 = c * fc + a * fs;
+  a = a2;
+  c = c2;
+}
+
+// grid (B, 28): heads 0..23 = q, 24..25 = k, 26..27 = v; block 128.
+__global__ __launch_bounds__(128) void k_qkv_post(const float* part, int S, int B, int64_t p,
+                                                  const uint16_t* q_norm, const uint16_t* k_norm,
+                                                  float eps, double theta, uint16_t* q16,
+                                                  uint16_t* kblk, uint16_t* vblkT) {
+  __shared__ float red[2];
+  const int b = blockIdx.x, hd = blockIdx.y, t = threadIdx.x;
+  const int col = hd < NQ ? hd * D : (hd < NQ + NKV ? NQ * D + (hd - NQ) * D
+                                                    : NQ * D + NKV * D + (hd - NQ - NKV) * D);
+  float a = 0.f, c = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float* r = part + (static_cast<size_t>(s) * B + b) * QKV_N + col;
+    a += r[t];
+    c += r[t + 128];
+  }
+  if (hd < NQ) {
+    norm_rope(a, c, q_norm, eps, p + b, theta, red);
+    uint16_t* q = q16 + (static_cast<size_t>(b) * NQ + hd) * D;
+    q[t] = f32_to_f16_bits(a);
+    q[t + 128] = f32_to_f16_bits(c);
+  } else if (hd < NQ + NKV) {
+    norm_rope(a, c, k_norm, eps, p + b, theta, red);
+    uint16_t* k = kblk + (static_cast<size_t>(hd - NQ) * BLK_CELLS + b) * D;
+    k[t] = f32_to_f16_bits(a);
+    k[t + 128] = f32_to_f16_bits(c);
+  } else {
+    uint16_t* v = vblkT + static_cast<size_t>(hd - NQ - NKV) * D * BLK_CELLS;
+    v[static_cast<size_t>(t) * BLK_CELLS + b] = f32_to_f16_bits(a);
+    v[static_cast<size_t>(t + 128) * BLK_CELLS + b] = f32_to_f16_bits(c);
+  }
+}
+
+struct KNorms {
+  const uint16_t* g[L];
+};
+
+// grid (n, 20): for layer l = y/4, w = y%4: w<2 key head w, else value head w-2.
+__global__ __launch_bounds__(128) void k_kv_post(const float* y, int S, size_t split_stride,
+                                                 int ldy, int64_t pos0, KNorms kn, float eps,
+                                                 double theta, uint16_t* ring_k,
+                                                 uint16_t* ring_vt, int cap) {
+  __shared__ float red[2];
+  const int row = blockIdx.x, l = blockIdx.y >> 2, w = blockIdx.y & 3, t = threadIdx.x;
+  const int col = l * (2 * NKV * D) + w * D;
+  float a = 0.f, c = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float* r = y + s * split_stride + static_cast<size_t>(row) * ldy + col;
+    a += r[t];
+    c += r[t + 128];
+  }
+  const int64_t pos = pos0 + row;
+  const size_t cell = static_cast<size_t>(pos % cap);
+  if (w < NKV) {
+    norm_rope(a, c, kn.g[l], eps, pos, theta, red);
+    uint16_t* k = ring_k + ((static_cast<size_t>(l) * NKV + w) * cap + cell) * D;
+    k[t] = f32_to_f16_bits(a);
+    k[t + 128] = f32_to_f16_bits(c);
+  } else {
+    uint16_t* v = ring_vt + (static_cast<size_t>(l) * NKV + (w - NKV)) * D * cap;
+    v[static_cast<size_t>(t) * cap + cell] = f32_to_f16_bits(a);
+    v[static_cast<size_t>(t + 128) * cap + cell] = f32_to_f16_bits(c);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rownorm(float* h, const float* part, int S, size_t part_split_stride,
+                          int part_row_stride, int rows, const uint16_t* gain, float eps,
+                          uint16_t* out, int out_stride, uint16_t* out2, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rownorm, dim3(rows), dim3(NT), 0, st, h, part, S, part_split_stride,
+                     part_row_stride, gain, eps, out, out_stride, out2);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_norm(const uint16_t* embed, int anchor, int mask, int B,
+                             const uint16_t* gain, float eps, float* h, uint16_t* xn,
+                             hipStream_t st) {
+  hipLaunchKernelGGL(k_embed_norm, dim3(B), dim3(NT), 0, st, embed, anchor, mask, gain, eps, h, xn);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_post(const float* part, int S, int B, int64_t p, const uint16_t* q_norm,
+                           const uint16_t* k_norm, float eps, double theta, uint16_t* q16,
+                           uint16_t* kblk, uint16_t* vblkT, hipStream_t st) {
+  hipLaunchKernelGGL(k_qkv_post, dim3(B, NQ + 2 * NKV), dim3(128), 0, st, part, S, B, p, q_norm,
+                     k_norm, eps, theta, q16, kblk, vblkT);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_post(const float* y, int S, size_t split_stride, int ldy, int n,
+                          int64_t pos0, const void* const* k_norms, float eps, double theta,
+                          uint16_t* ring_k, uint16_t* ring_vt, int capacity, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  KNorms kn;
+  for (int l = 0; l < L; ++l) kn.g[l] = static_cast<const uint16_t*>(k_norms[l]);
+  hipLaunchKernelGGL(k_kv_post, dim3(n, L * 2 * NKV), dim3(128), 0, st, y, S, split_stride, ldy,
+                     pos0, kn, eps, theta, ring_k, ring_vt, capacity);
+  return hipGetLastError();
+}
+
+}  // namespace dfl

@@ -1,0 +1,131 @@
+"""Device-memory plumbing over the C ABI: weights resident in HBM with their
+descriptor, the fp16 K/V ring, the workspace, and thin methods that pass
+pointers to the library on torch's current HIP stream.  PyTorch only
+allocates and owns memory here; all computation happens in libdflash.so."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib, synth
+from ._lib import (dflash_draft_block, dflash_fuse_context, dflash_kv,
+                   dflash_project_ctx_kv, dflash_verify_greedy, dflash_weights,
+                   dflash_workspace_size)
+
+_FORMATS = {"bf16": _lib.DFLASH_W_BF16, "q8_0": _lib.DFLASH_W_Q8_0,
+            "q4_0": _lib.DFLASH_W_Q4_0}
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        raise RuntimeError("no HIP device visible: the DFlash library runs on the GPU only")
+    _lib.load()
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """Copy a host array's bytes to HBM (uint16 arrays travel as int16)."""
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    elif a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def stream_ptr() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+class DeviceWeights:
+    """All drafter tensors in HBM plus the dflash_weights descriptor."""
+
+    def __init__(self, host: dict, device="cuda"):
+        require_gpu()
+        self.format = host.get("__format__", "bf16")
+        self.t = {k: to_device(v, device) for k, v in host.items() if not k.startswith("__")}
+        d = dflash_weights()
+        d.hidden, d.n_layers, d.n_q_heads = synth.HIDDEN, synth.N_LAYERS, synth.N_Q_HEADS
+        d.n_kv_heads, d.head_dim, d.ffn = synth.N_KV_HEADS, synth.HEAD_DIM, synth.FFN
+        d.vocab, d.n_taps = self.t["embed"].shape[0], synth.N_TAPS
+        d.rope_theta, d.attn_scale, d.rms_eps = synth.ROPE_THETA, synth.ATTN_SCALE, synth.RMS_EPS
+        d.backbone_type = _FORMATS[self.format]
+        d.fc = self.t["fc"].data_ptr()
+        d.hidden_norm = self.t["hidden_norm"].data_ptr()
+        for l in range(synth.N_LAYERS):
+            for f in _lib.LAYER_FIELDS:
+                setattr(d.layer[l], f, self.t[f"layers.{l}.{f}"].data_ptr())
+        d.final_norm = self.t["final_norm"].data_ptr()
+        d.embed = self.t["embed"].data_ptr()
+        d.lm_head = self.t["lm_head"].data_ptr()
+        self.desc = d
+        self.vocab = d.vocab
+
+
+class KVRing:
+    """fp16 K [5][2][cap][256] and transposed V [5][2][256][cap]."""
+
+    def __init__(self, capacity: int, window: int = synth.WINDOW, device="cuda"):
+        self.k = torch.zeros((synth.N_LAYERS, synth.N_KV_HEADS, capacity, synth.HEAD_DIM),
+                             dtype=torch.float16, device=device)
+        self.vt = torch.zeros((synth.N_LAYERS, synth.N_KV_HEADS, synth.HEAD_DIM, capacity),
+                              dtype=torch.float16, device=device)
+        self.desc = dflash_kv(self.k.data_ptr(), self.vt.data_ptr(), capacity, window)
+        self.capacity = capacity
+        self.window = window
+
+
+class Drafter:
+    """Calls of the four entry points with device buffers."""
+
+    def __init__(self, weights: DeviceWeights, kv: KVRing, max_rows: int = 16,
+                 max_block: int = synth.MAX_BLOCK, device="cuda"):
+        self.w = weights
+        self.kv = kv
+        self.ws_bytes = dflash_workspace_size(weights.desc, max_rows, max_block)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.max_rows = max_rows
+        self.device = device
+
+    def fuse(self, taps: torch.Tensor, ctx: torch.Tensor | None = None) -> torch.Tensor:
+        n = taps.shape[0]
+        if ctx is None:
+            ctx = torch.empty((n, synth.HIDDEN), dtype=torch.int16, device=self.device)
+        dflash_fuse_context(self.w.desc, taps.data_ptr(), n, ctx.data_ptr(),
+                            self.ws.data_ptr(), self.ws_bytes, stream_ptr())
+        return ctx
+
+    def project(self, ctx: torch.Tensor, pos0: int):
+        dflash_project_ctx_kv(self.w.desc, ctx.data_ptr(), ctx.shape[0], pos0, self.kv.desc,
+                              self.ws.data_ptr(), self.ws_bytes, stream_ptr())
+
+    def commit(self, taps: torch.Tensor, pos0: int) -> torch.Tensor:
+        ctx = self.fuse(taps)
+        self.project(ctx, pos0)
+        return ctx
+
+    def draft(self, p: int, anchor: int, block: int, mask_id: int = synth.MASK_ID,
+              cand: torch.Tensor | None = None, logits: torch.Tensor | None = None,
+              hidden: torch.Tensor | None = None) -> torch.Tensor:
+        if cand is None:
+            cand = torch.empty(max(block - 1, 1), dtype=torch.int32, device=self.device)
+        dflash_draft_block(self.w.desc, self.kv.desc, p, anchor, mask_id, block,
+                           cand.data_ptr(),
+                           logits.data_ptr() if logits is not None else None,
+                           hidden.data_ptr() if hidden is not None else None,
+                           self.ws.data_ptr(), self.ws_bytes, stream_ptr())
+        return cand
+
+    def lm_head_argmax(self, hidden: torch.Tensor, cand: torch.Tensor,
+                       logits: torch.Tensor | None = None) -> torch.Tensor:
+        _lib.dflash_lm_head_argmax(self.w.desc, hidden.data_ptr(), hidden.shape[0],
+                                   cand.data_ptr(),
+                                   logits.data_ptr() if logits is not None else None,
+                                   self.ws.data_ptr(), self.ws_bytes, stream_ptr())
+        return cand
+
+    def verify(self, cand: torch.Tensor, target: torch.Tensor, k: int,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty(2, dtype=torch.int32, device=self.device)
+        dflash_verify_greedy(cand.data_ptr(), target.data_ptr(), k, out.data_ptr(),
+                             stream_ptr())
+        return out

@@ -98,10 +98,12 @@ def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
             >> np.uint32(16)).astype(np.uint16)
 
 
-def _normal_f32(seed_words, n: int, std: float, mean: float) -> np.ndarray:
-    """n fp32 samples of N(mean, std^2), drawn in fixed-size chunks that each
-    have their own seed so the result does not depend on threading."""
-    out = np.empty(n, dtype=np.float32)
+def _normal_f32(seed_words, n: int, std: float, mean: float,
+                bf16: bool = False) -> np.ndarray:
+    """n fp32 samples of N(mean, std^2) (or their bf16 bit patterns), drawn in
+    fixed-size chunks that each have their own seed so the result does not
+    depend on threading."""
+    out = np.empty(n, dtype=np.uint16 if bf16 else np.float32)
     starts = list(range(0, n, _CHUNK))
 
     def work(ci):
@@ -114,7 +116,7 @@ def _normal_f32(seed_words, n: int, std: float, mean: float) -> np.ndarray:
             v *= np.float32(std)
         if mean != 0.0:
             v += np.float32(mean)
-        out[s:e] = v
+        out[s:e] = bf16_bits_from_f32(v) if bf16 else v
 
     if len(starts) == 1:
         work(0)
@@ -126,8 +128,7 @@ def _normal_f32(seed_words, n: int, std: float, mean: float) -> np.ndarray:
 
 def _bf16_normal(seed_words, shape, std, mean=0.0) -> np.ndarray:
     n = int(np.prod(shape))
-    v = _normal_f32(seed_words, n, std, mean)
-    return bf16_bits_from_f32(v).reshape(shape)
+    return _normal_f32(seed_words, n, std, mean, bf16=True).reshape(shape)
 
 
 def quantize_q8_0(w: np.ndarray) -> np.ndarray:
@@ -251,3 +252,12 @@ def synthetic_target(cand: np.ndarray, pass_index: int,
     match, offset, tail = target_draws(pass_index, k, seed, p_match, vocab)
     tgt = np.where(match, cand, (cand + 1 + offset) % vocab)
     return np.concatenate([tgt, [tail]]).astype(np.int32)
+
+
+def make_rows(n: int, width: int, seed: int, dtype: str = "bf16",
+              std: float = 1.0) -> np.ndarray:
+    """n seeded rows of N(0, std^2): bf16 bits (uint16) or fp16 bits (uint16)."""
+    v = _normal_f32((seed, 1 << 24, width), n * width, std, 0.0)
+    if dtype == "bf16":
+        return bf16_bits_from_f32(v).reshape(n, width)
+    return v.astype(np.float16).view(np.uint16).reshape(n, width)

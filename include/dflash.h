@@ -1,0 +1,189 @@
+/*
+ * dflash.h -- C ABI of the MI355X (gfx950) DFlash block-drafter library.
+ *
+ * The library computes the proposal pass of the standalone DeepSpec DFlash
+ * block drafter described on the Strata PR #1426 page ("dflash: experimental
+ * standalone DeepSpec DFlash block drafter for Qwen3.8-Flash-Next"):
+ *   - context fusion rmsnorm(fc(concat(taps)))          (section "Drafter runtime")
+ *   - per-layer context K/V projection, fp16 cells      ("Drafter runtime",
+ *                                                         "Owned DFlash K/V state")
+ *   - one parallel, non-causal five-layer forward over [anchor, mask x K]
+ *     with a greedy argmax through the shared LM head   ("Target feature taps",
+ *                                                         "Drafter runtime")
+ *   - greedy verification of the K candidates           ("Speculative decode
+ *                                                         integration"; Strata RFC
+ *                                                         #366, "Verification and
+ *                                                         state management")
+ *
+ * Conventions for every entry point
+ *   - Pointers are device pointers (HBM of the current HIP device) unless a
+ *     comment says "host".  The caller owns every buffer: weights, K/V ring,
+ *     workspace and outputs.  The library allocates nothing, frees nothing and
+ *     keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     device work is enqueued on it and the call returns without waiting;
+ *     results are valid once the stream has been synchronised.  Calls that
+ *     share a workspace must be ordered on one stream.
+ *   - Argument checks happen on the host before anything is enqueued; a
+ *     non-zero return means nothing was enqueued (except DFLASH_EHIP, which
+ *     reports a failed launch).
+ *   - bf16 is the upper half of an IEEE binary32; fp16 is IEEE binary16.
+ *     Matrices are row-major [out][in].
+ *   - Not thread-safe beyond stream order.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define DFLASH_OK          0
+#define DFLASH_EINVAL     -1 /* null pointer, negative size, block outside 1..8,
+                                token id outside [0, vocab), position < 0 */
+#define DFLASH_EGEOMETRY  -2 /* descriptor differs from the DFlash geometry */
+#define DFLASH_ERANGE     -3 /* K/V ring: window > capacity, capacity not a
+                                multiple of 256, or n > capacity in one call */
+#define DFLASH_EWORKSPACE -4 /* workspace smaller than dflash_workspace_size() */
+#define DFLASH_EHIP       -5 /* a kernel launch failed */
+
+/* Fixed drafter geometry ("Drafter runtime" on the PR #1426 page). */
+#define DFLASH_HIDDEN     2560
+#define DFLASH_LAYERS     5
+#define DFLASH_Q_HEADS    24
+#define DFLASH_KV_HEADS   2
+#define DFLASH_HEAD_DIM   256
+#define DFLASH_FFN        7680
+#define DFLASH_TAPS       5
+#define DFLASH_MAX_BLOCK  8   /* anchor + at most 7 candidates ("Current limitations") */
+
+/* Storage format of the 36 backbone matrices (fc and the 35 layer matrices).
+ * Q8_0 / Q4_0 use 32-element blocks along the input dimension of each output
+ * row, one fp16 scale per block.  A quantized [N][K] matrix is one buffer:
+ *   Q8_0: N*K int8 values (row-major), then N*K/32 fp16 scales (row-major);
+ *         weight = scale * q.
+ *   Q4_0: N*K/2 bytes (row-major, 16 bytes per block: element j of a block in
+ *         the low nibble of byte j, element j+16 in the high nibble), then
+ *         N*K/32 fp16 scales; weight = scale * (nibble - 8).
+ * Gains, the embedding and the LM head are always bf16. */
+typedef enum {
+  DFLASH_W_BF16 = 0,
+  DFLASH_W_Q8_0 = 1,
+  DFLASH_W_Q4_0 = 2
+} dflash_wtype;
+
+typedef struct {
+  const void* in_norm;   /* bf16 [2560]       input RMSNorm gain            */
+  const void* wq;        /* [6144][2560]       query projection              */
+  const void* wk;        /* [512][2560]        key projection                */
+  const void* wv;        /* [512][2560]        value projection              */
+  const void* q_norm;    /* bf16 [256]         per-head query RMSNorm gain   */
+  const void* k_norm;    /* bf16 [256]         per-head key RMSNorm gain     */
+  const void* wo;        /* [2560][6144]       output projection             */
+  const void* post_norm; /* bf16 [2560]        post-attention RMSNorm gain   */
+  const void* wg;        /* [7680][2560]       MLP gate                      */
+  const void* wu;        /* [7680][2560]       MLP up                        */
+  const void* wd;        /* [2560][7680]       MLP down                      */
+} dflash_layer_weights;
+
+/* Caller-owned weight descriptor; must not change during a call. */
+typedef struct {
+  int32_t hidden, n_layers, n_q_heads, n_kv_heads, head_dim, ffn, vocab, n_taps;
+  float rope_theta;      /* 1e7                                               */
+  float attn_scale;      /* 1/16                                              */
+  float rms_eps;         /* 1e-6                                              */
+  int32_t backbone_type; /* dflash_wtype                                      */
+  const void* fc;        /* [2560][12800]      fusion projection             */
+  const void* hidden_norm; /* bf16 [2560]      fusion RMSNorm gain           */
+  dflash_layer_weights layer[DFLASH_LAYERS];
+  const void* final_norm;  /* bf16 [2560]                                     */
+  const void* embed;       /* bf16 [vocab][2560] target embedding (shared)    */
+  const void* lm_head;     /* bf16 [vocab][2560] target LM head (shared)      */
+} dflash_weights;
+
+/* Drafter-owned context K/V ("Owned DFlash K/V state": fp16, one state per
+ * layer).  Position m lives in cell m % capacity ("Speculative decode
+ * integration": position-addressed cells, overwritten on a later commit).
+ *   k : fp16 [5 layers][2 kv heads][capacity cells][256]
+ *   vt: fp16 [5 layers][2 kv heads][256][capacity cells]   (values transposed:
+ *       cell index fastest, so one dimension of consecutive cells is contiguous)
+ * capacity must be a multiple of 256 and >= window.  A draft at anchor
+ * position p reads positions max(0, p-window) .. p-1, which must have been
+ * projected (and not overwritten since) by the caller. */
+typedef struct {
+  void* k;
+  void* vt;
+  int32_t capacity;
+  int32_t window;        /* 32768 by default ("Current limitations")         */
+} dflash_kv;
+
+/* Bytes of device workspace needed for calls with up to `max_rows` context
+ * rows (fuse/project) and blocks of up to `max_block` rows (draft).  Returns 0
+ * for invalid arguments. */
+size_t dflash_workspace_size(const dflash_weights* w, int32_t max_rows,
+                             int32_t max_block);
+
+/* Context fusion ("Drafter runtime": rmsnorm(fc(concat(target taps)))).
+ *   taps: bf16 [n][5][2560], the five target taps of each position in tap order
+ *   ctx : bf16 [n][2560] output, ctx[t] = rmsnorm(fc . concat(taps[t]), hidden_norm)
+ * n may be 0 (no work).  ws/ws_bytes: workspace. */
+int32_t dflash_fuse_context(const dflash_weights* w, const void* taps, int32_t n,
+                            void* ctx, void* ws, size_t ws_bytes, void* stream);
+
+/* Per-layer context K/V projection ("Drafter runtime": the fused context is
+ * projected into independent per-layer K/V state).  For t in [0, n) and each
+ * layer l and KV head j, position m = pos0 + t:
+ *   K_l[j][m % cap] = fp16(RoPE_m(rmsnorm(Wk_l ctx[t])_j, k_norm_l))
+ *   V_l[j][m % cap] = fp16((Wv_l ctx[t])_j)
+ *   ctx: bf16 [n][2560] (output of dflash_fuse_context); pos0 >= 0; n <= capacity. */
+int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ctx, int32_t n,
+                              int64_t pos0, const dflash_kv* kv, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* One parallel proposal pass ("Target feature taps", "Drafter runtime").
+ * Block row 0 is the anchor token at position p, rows 1..block-1 the mask
+ * token at p+1..p+block-1; attention is non-causal over the context window
+ * and all block rows, scale 1/16.  Mask row i proposes position p+i:
+ *   cand      : int32 [block-1]            greedy ids (lowest id on ties)
+ *   logits_opt: bf16 [block-1][vocab] or NULL   LM-head logits of the mask rows
+ *   hidden_opt: bf16 [block][2560] or NULL      final-normed hidden states
+ * block in [1, 8]; anchor_id, mask_id in [0, vocab); p >= 0. */
+int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* kv, int64_t p,
+                           int32_t anchor_id, int32_t mask_id, int32_t block,
+                           int32_t* cand, void* logits_opt, void* hidden_opt,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Greedy argmax through the shared LM head ("Drafter runtime": target LM head
+ * reused directly; greedy proposal path) for final-normed hidden rows:
+ *   hidden    : bf16 [rows][2560]  final-normed hidden states
+ *   cand      : int32 [rows]       argmax_v (lm_head[v] . hidden[r]), lowest v on ties,
+ *                                   decided on fp32 logits
+ *   logits_opt: bf16 [rows][vocab] or NULL
+ * rows in [1, 8].  dflash_draft_block runs the same kernels on its mask rows. */
+int32_t dflash_lm_head_argmax(const dflash_weights* w, const void* hidden, int32_t rows,
+                              int32_t* cand, void* logits_opt, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* Greedy verification ("Speculative decode integration"; RFC #366
+ * "Verification and state management").
+ *   cand  : int32 [k]   proposals for positions p+1..p+k
+ *   target: int32 [k+1] the target's greedy tokens for the same positions and
+ *           the one after
+ *   out   : int32 [2] = {accepted, next}: accepted = longest prefix with
+ *           cand[i] == target[i]; next = target[accepted] (the verifier's
+ *           continuation token).  k in [0, 7]. */
+int32_t dflash_verify_greedy(const int32_t* cand, const int32_t* target, int32_t k,
+                             int32_t* out, void* stream);
+
+/* Static description of a return code (host string, never NULL). */
+const char* dflash_strerror(int32_t code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

@@ -127,13 +127,24 @@ def gain(w: dict, name: str) -> np.ndarray:
     return bf16_decode(w[name])
 
 
+def enable_cache(w: dict) -> dict:
+    """Keep decoded float64 matrices with the weights so that repeated passes
+    skip the decoding (about 8 bytes per weight of host memory)."""
+    w["__cache__"] = {}
+    return w
+
+
 def matvec_rows(w: dict, name: str, shape, x: np.ndarray,
                 chunk: int = 8192) -> np.ndarray:
     """y[b][o] = sum_i W[o][i] x[b][i], W converted to float64 a block of
     output rows at a time to bound memory."""
     rows, cols = shape
+    cache = w.get("__cache__")
+    if cache is not None:
+        if name not in cache:
+            cache[name] = matrix(w, name, shape)
+        return x @ cache[name].T
     out = np.empty((x.shape[0], rows), dtype=np.float64)
-    fmt = w.get("__format__", "bf16")
     a = w[name]
     if a.dtype == np.uint16:
         a2 = a.reshape(rows, cols)
@@ -209,8 +220,13 @@ def fuse_context(w: dict, taps_bits: np.ndarray, g: dict | None = None,
     H, T = g["hidden"], g["n_taps"]
     n = taps_bits.shape[0]
     out = np.empty((n, H), dtype=np.uint16)
-    fc = bf16_decode(w["fc"]).reshape(H, T * H) if w["fc"].dtype == np.uint16 \
-        else matrix(w, "fc", (H, T * H))
+    cache = w.get("__cache__")
+    if cache is not None:
+        if "fc" not in cache:
+            cache["fc"] = matrix(w, "fc", (H, T * H))
+        fc = cache["fc"]
+    else:
+        fc = matrix(w, "fc", (H, T * H))
     gh = gain(w, "hidden_norm")
     for s in range(0, n, chunk):
         e = min(n, s + chunk)
@@ -347,28 +363,55 @@ def verify_greedy(cand, target):
 class ContextStore:
     """Drafter context K/V by absolute position (fp16 values as float64).
     Committing a position again overwrites its cell, so rejected proposals
-    need no rollback ("Speculative decode integration")."""
+    need no rollback ("Speculative decode integration").  Positions live in
+    one contiguous range [base, base + size)."""
 
     def __init__(self, g: dict | None = None):
         self.g = g or GEOMETRY
-        self.k = {}
-        self.v = {}
+        self.base = None
+        self.k = None
+        self.v = None
+        self.written = None
+
+    def _ensure(self, lo, hi):
+        L, nkv, D = self.g["n_layers"], self.g["n_kv_heads"], self.g["head_dim"]
+        if self.base is None:
+            self.base = lo
+            self.k = np.zeros((L, nkv, 0, D))
+            self.v = np.zeros((L, nkv, 0, D))
+            self.written = np.zeros(0, dtype=bool)
+        assert lo >= self.base, "positions below the first committed one"
+        need = hi - self.base
+        if need > self.k.shape[2]:
+            grow = max(need, 2 * self.k.shape[2])
+            k = np.zeros((L, nkv, grow, D))
+            v = np.zeros((L, nkv, grow, D))
+            wr = np.zeros(grow, dtype=bool)
+            n0 = self.k.shape[2]
+            k[:, :, :n0] = self.k
+            v[:, :, :n0] = self.v
+            wr[:n0] = self.written
+            self.k, self.v, self.written = k, v, wr
 
     def put(self, K, V, pos0):
-        for t in range(K.shape[2]):
-            self.k[pos0 + t] = K[:, :, t, :].copy()
-            self.v[pos0 + t] = V[:, :, t, :].copy()
+        n = K.shape[2]
+        self._ensure(pos0, pos0 + n)
+        s = pos0 - self.base
+        self.k[:, :, s:s + n] = K
+        self.v[:, :, s:s + n] = V
+        self.written[s:s + n] = True
 
     def window(self, p):
+        """K, V [L][n_kv][n][D] of positions max(0, p - window) .. p - 1."""
         lo = max(0, p - self.g["window"])
-        ps = range(lo, p)
         L, nkv, D = self.g["n_layers"], self.g["n_kv_heads"], self.g["head_dim"]
         if p - lo == 0:
             z = np.zeros((L, nkv, 0, D))
             return z, z.copy()
-        K = np.stack([self.k[m] for m in ps], axis=2)
-        V = np.stack([self.v[m] for m in ps], axis=2)
-        return K, V
+        s, e = lo - self.base, p - self.base
+        assert s >= 0 and e <= self.k.shape[2] and self.written[s:e].all(), \
+            "context window holds positions that were never committed"
+        return self.k[:, :, s:e], self.v[:, :, s:e]
 
 
 def commit(w: dict, store: ContextStore, taps_bits, pos0: int, g=None):

@@ -1,0 +1,164 @@
+"""The C-ABI library on the host: it loads, exports every entry point the
+header declares (and nothing from torch), and its argument checks return the
+documented codes before anything reaches a GPU.  Runs without a GPU: every
+call below fails validation on the host, so no kernel is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_draft_model_pass_amd import _lib, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+
+
+def header_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libdflash.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_header_declares_the_four_operations():
+    syms = header_symbols()
+    for s in ("dflash_fuse_context", "dflash_project_ctx_kv", "dflash_draft_block",
+              "dflash_verify_greedy", "dflash_workspace_size", "dflash_strerror",
+              "dflash_lm_head_argmax"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    for s in header_symbols():
+        assert s in exported, s
+        assert hasattr(lib, s)
+
+
+def test_library_has_no_torch_dependency():
+    out = subprocess.run(["readelf", "-d", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    needed = re.findall(r"NEEDED.*\[(.*)\]", out)
+    assert any("amdhip64" in n for n in needed)
+    assert not any("torch" in n or "c10" in n or "cuda" in n for n in needed), needed
+
+
+def fake_weights(**over):
+    """A descriptor with the DFlash geometry and non-null dummy pointers; only
+    ever used with calls that fail validation on the host."""
+    w = _lib.dflash_weights()
+    w.hidden, w.n_layers, w.n_q_heads, w.n_kv_heads = 2560, 5, 24, 2
+    w.head_dim, w.ffn, w.vocab, w.n_taps = 256, 7680, synth.VOCAB, 5
+    w.rope_theta, w.attn_scale, w.rms_eps = 1e7, 1.0 / 16, 1e-6
+    w.backbone_type = _lib.DFLASH_W_BF16
+    dummy = 0x10000
+    w.fc = w.hidden_norm = w.final_norm = w.embed = w.lm_head = dummy
+    for l in range(5):
+        for f in _lib.LAYER_FIELDS:
+            setattr(w.layer[l], f, dummy)
+    for k, v in over.items():
+        setattr(w, k, v)
+    return w
+
+
+def fake_kv(capacity=32768, window=32768):
+    return _lib.dflash_kv(0x20000, 0x30000, capacity, window)
+
+
+def test_workspace_size(lib):
+    w = fake_weights()
+    base = _lib.dflash_workspace_size(w, 0, 8)
+    assert base > 0
+    assert _lib.dflash_workspace_size(w, 64, 8) == base       # skinny path
+    big = _lib.dflash_workspace_size(w, 32768, 8)
+    assert big >= base + 32768 * 5120 * 4
+    assert _lib.dflash_workspace_size(w, -1, 8) == 0
+    assert _lib.dflash_workspace_size(w, 16, 9) == 0
+
+
+def test_strerror_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, -99):
+        assert isinstance(_lib.dflash_strerror(code), str)
+    assert _lib.dflash_strerror(-4) == "workspace too small"
+
+
+@pytest.mark.parametrize("field,value", [
+    ("hidden", 4096), ("n_layers", 4), ("n_q_heads", 32), ("n_kv_heads", 8),
+    ("head_dim", 128), ("ffn", 9728), ("n_taps", 4), ("vocab", 151937),
+    ("rope_theta", 1e6), ("attn_scale", 0.125), ("rms_eps", 1e-5)])
+def test_geometry_mismatch_is_rejected(lib, field, value):
+    w = fake_weights(**{field: value})
+    rc = _lib.dflash_fuse_context(w, 1, 4, 1, 1, 1 << 40, check=False)
+    assert rc == _lib.DFLASH_EGEOMETRY
+    rc = _lib.dflash_draft_block(w, fake_kv(), 8192, 1, 2, 8, 1, None, None, 1, 1 << 40,
+                                 check=False)
+    assert rc == _lib.DFLASH_EGEOMETRY
+
+
+def test_null_and_bad_arguments(lib):
+    w = fake_weights()
+    kv = fake_kv()
+    big = 1 << 40
+    E = _lib.DFLASH_EINVAL
+    assert _lib.dflash_fuse_context(None, 1, 4, 1, 1, big, check=False) == E
+    assert _lib.dflash_fuse_context(w, None, 4, 1, 1, big, check=False) == E
+    assert _lib.dflash_fuse_context(w, 1, -1, 1, 1, big, check=False) == E
+    assert _lib.dflash_fuse_context(w, 1, 0, 1, 1, big, check=False) == 0  # no work
+    w2 = fake_weights()
+    w2.layer[3].wd = None
+    assert _lib.dflash_fuse_context(w2, 1, 4, 1, 1, big, check=False) == E
+    w3 = fake_weights(backbone_type=7)
+    assert _lib.dflash_fuse_context(w3, 1, 4, 1, 1, big, check=False) == E
+    for block in (0, 9, -3):
+        assert _lib.dflash_draft_block(w, kv, 100, 1, 2, block, 1, None, None, 1, big,
+                                       check=False) == E
+    for anchor, mask in ((-1, 2), (synth.VOCAB, 2), (1, synth.VOCAB)):
+        assert _lib.dflash_draft_block(w, kv, 100, anchor, mask, 8, 1, None, None, 1, big,
+                                       check=False) == E
+    assert _lib.dflash_draft_block(w, kv, -1, 1, 2, 8, 1, None, None, 1, big,
+                                   check=False) == E
+    assert _lib.dflash_draft_block(w, kv, 5, 1, 2, 8, None, None, None, 1, big,
+                                   check=False) == E
+    assert _lib.dflash_project_ctx_kv(w, 1, 4, -5, kv, 1, big, check=False) == E
+    assert _lib.dflash_lm_head_argmax(w, 1, 0, 1, None, 1, big, check=False) == E
+    assert _lib.dflash_lm_head_argmax(w, 1, 9, 1, None, 1, big, check=False) == E
+    assert _lib.dflash_lm_head_argmax(w, None, 3, 1, None, 1, big, check=False) == E
+    assert _lib.dflash_verify_greedy(1, 1, 8, 1, check=False) == E
+    assert _lib.dflash_verify_greedy(1, 1, -1, 1, check=False) == E
+    assert _lib.dflash_verify_greedy(1, None, 3, 1, check=False) == E
+
+
+def test_ring_range_violations(lib):
+    w = fake_weights()
+    big = 1 << 40
+    R = _lib.DFLASH_ERANGE
+    assert _lib.dflash_draft_block(w, fake_kv(1000, 1000), 10, 1, 2, 8, 1, None, None, 1, big,
+                                   check=False) == R
+    assert _lib.dflash_draft_block(w, fake_kv(1024, 2048), 10, 1, 2, 8, 1, None, None, 1, big,
+                                   check=False) == R
+    assert _lib.dflash_draft_block(w, fake_kv(1024, 0), 10, 1, 2, 8, 1, None, None, 1, big,
+                                   check=False) == R
+    assert _lib.dflash_project_ctx_kv(w, 1, 2048, 0, fake_kv(1024, 1024), 1, big,
+                                      check=False) == R
+
+
+def test_workspace_too_small(lib):
+    w = fake_weights()
+    kv = fake_kv()
+    need = _lib.dflash_workspace_size(w, 0, 8)
+    W = _lib.DFLASH_EWORKSPACE
+    assert _lib.dflash_draft_block(w, kv, 10, 1, 2, 8, 1, None, None, 1, need - 1,
+                                   check=False) == W
+    need_rows = _lib.dflash_workspace_size(w, 4096, 8)
+    assert _lib.dflash_fuse_context(w, 1, 4096, 1, 1, need_rows - 1, check=False) == W
+    assert _lib.dflash_project_ctx_kv(w, 1, 4096, 0, kv, 1, need_rows - 1, check=False) == W
