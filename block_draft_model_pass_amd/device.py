@@ -63,7 +63,8 @@ class DeviceWeights:
 class KVRing:
     """fp16 K [5][2][cap][256] and transposed V [5][2][256][cap]."""
 
-    def __init__(self, capacity: int, window: int = synth.WINDOW, device="cuda"):
+    def __init__(self, capacity: int, window: int | None = None, device="cuda"):
+        window = min(synth.WINDOW, capacity) if window is None else window
         self.k = torch.zeros((synth.N_LAYERS, synth.N_KV_HEADS, capacity, synth.HEAD_DIM),
                              dtype=torch.float16, device=device)
         self.vt = torch.zeros((synth.N_LAYERS, synth.N_KV_HEADS, synth.HEAD_DIM, capacity),
