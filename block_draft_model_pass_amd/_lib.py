@@ -59,6 +59,10 @@ def load() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    try:  # let the library bind to the HIP runtime torch already loaded
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with "

@@ -11,8 +11,23 @@ using namespace dfl;
 namespace {
 
 constexpr int NCH_MAX = 256;          // context chunks of the attention split
-constexpr int NCH_TARGET = 128;       // chunks per KV head aimed for
-constexpr int LMH_GRID = 1024;        // LM-head blocks (grid-stride over tiles)
+constexpr int NCH_TARGET = 64;        // chunks per KV head aimed for
+constexpr int LMH_GRID = 256;         // standalone LM-head kernel: one block per CU
+constexpr int KEYS_MAX = 1024;        // argmax key slots (blocks of either LM-head launch)
+constexpr unsigned SPIN_LIMIT = 1u << 24;  // grid-barrier wait bound (~0.5 s)
+
+// Co-resident grid of the pass kernel per device (a hardware property).
+int pass_grid() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int g = 0;
+    if (draft_pass_max_grid(dev, &g) != hipSuccess) return 0;
+    cache[dev] = g > KEYS_MAX ? KEYS_MAX : g;
+  }
+  return cache[dev];
+}
 constexpr int SMALL_ROWS = 64;        // fuse/project: skinny path up to here
 constexpr int FC_SPLITS = 5;          // k splits of the fc GEMV (K = 12800)
 constexpr int O_SPLITS = 3;           // k splits of the O GEMV (K = 6144)
@@ -20,7 +35,7 @@ constexpr int DOWN_SPLITS = 3;        // k splits of the down GEMV (K = 7680)
 constexpr size_t PART_FLOATS = static_cast<size_t>(FC_SPLITS) * GEMV_ROWS * H;
 
 struct Layout {
-  size_t h, xn, part, q16, kblk, vblkT, po, pm, pl, o16, u16, keys, y;
+  size_t h, xn, part, q16, kblk, vblkT, po, pm, pl, o16, u16, keys, rope, ss, qkv, bar, tab, y;
   size_t fixed;  // bytes before y
 };
 
@@ -45,7 +60,12 @@ Layout layout() {
   L.pl = take(off, sizeof(float) * NKV * nc * nqt * 16);
   L.o16 = take(off, 2 * MAXB * NQ * D);
   L.u16 = take(off, 2 * MAXB * F);
-  L.keys = take(off, sizeof(uint64_t) * LMH_GRID * MAXB);
+  L.keys = take(off, sizeof(uint64_t) * KEYS_MAX * MAXB);
+  L.rope = take(off, sizeof(float) * 2 * MAXB * (D / 2));
+  L.ss = take(off, sizeof(float) * (H / 16) * MAXB);
+  L.qkv = take(off, sizeof(float) * MAXB * QKV_N);
+  L.bar = take(off, pass_bar_bytes());
+  L.tab = take(off, pass_tab_bytes());
   L.fixed = off;
   L.y = off;
   return L;
@@ -240,95 +260,72 @@ extern "C" int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* 
   const Layout Lw = layout();
   if (ws_bytes < Lw.fixed) return DFLASH_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int B = block;
-  const float eps = w->rms_eps;
-  const double theta = static_cast<double>(w->rope_theta);
-
-  float* h = at<float>(ws, Lw.h);
-  uint16_t* xn = at<uint16_t>(ws, Lw.xn);
-  float* part = at<float>(ws, Lw.part);
-  uint16_t* q16 = at<uint16_t>(ws, Lw.q16);
-  uint16_t* kblk = at<uint16_t>(ws, Lw.kblk);
-  uint16_t* vblkT = at<uint16_t>(ws, Lw.vblkT);
-  uint16_t* o16 = at<uint16_t>(ws, Lw.o16);
-  uint16_t* u16 = at<uint16_t>(ws, Lw.u16);
-
-  // Attention split over the visible context [lo, p).
-  AttnArgs at_args;
-  at_args.q16 = q16;
-  at_args.B = B;
-  at_args.nqt = (G * B + 15) / 16;
-  at_args.cap = kv->capacity;
-  at_args.lo = p - kv->window > 0 ? p - kv->window : 0;
-  at_args.hi = p;
-  if (p > at_args.lo) {
-    at_args.p0 = at_args.lo & ~static_cast<int64_t>(31);
-    at_args.nb = static_cast<int>((p - at_args.p0 + 31) / 32);
-    at_args.cb = (at_args.nb + NCH_TARGET - 1) / NCH_TARGET;
-    at_args.nch = (at_args.nb + at_args.cb - 1) / at_args.cb;
-  } else {
-    at_args.p0 = 0;
-    at_args.nb = 0;
-    at_args.cb = 1;
-    at_args.nch = 0;
-  }
-  if (at_args.nch > NCH_MAX) return DFLASH_ERANGE;
-  at_args.kblk = kblk;
-  at_args.vblkT = vblkT;
-  at_args.scale_log2 = w->attn_scale * 1.4426950408889634f;
-  at_args.po = at<float>(ws, Lw.po);
-  at_args.pm = at<float>(ws, Lw.pm);
-  at_args.pl = at<float>(ws, Lw.pl);
-  at_args.o16 = o16;
-
-  HIP_TRY(launch_embed_norm(u16p(w->embed), anchor_id, mask_id, B, u16p(w->layer[0].in_norm), eps,
-                            h, xn, st));
+  const int grid = pass_grid();
+  if (grid < QKV_N / 32) return DFLASH_EHIP;  // the pass needs >= 224 resident blocks
+  PassLaunch q;
   for (int l = 0; l < L; ++l) {
     const dflash_layer_weights& y = w->layer[l];
-    GemvArgs a;
-    a.w = seg_qkv(y);
-    a.fmt = W_BF16;
-    a.N = QKV_N;
-    a.K = H;
-    a.x = xn;
-    a.x_stride = H;
-    a.B = B;
-    a.out = part;
-    a.S = 1;
-    HIP_TRY(launch_gemv(a, st));
-    HIP_TRY(launch_qkv_post(part, 1, B, p, u16p(y.q_norm), u16p(y.k_norm), eps, theta, q16, kblk,
-                            vblkT, st));
-    at_args.ring_k = static_cast<const uint16_t*>(kv->k) +
-                     static_cast<size_t>(l) * NKV * kv->capacity * D;
-    at_args.ring_vt = static_cast<const uint16_t*>(kv->vt) +
-                      static_cast<size_t>(l) * NKV * D * kv->capacity;
-    HIP_TRY(launch_attention(at_args, st));
-    a.w = seg1(y.wo, H);
-    a.N = H;
-    a.K = NQ * D;
-    a.x = o16;
-    a.x_stride = NQ * D;
-    a.S = O_SPLITS;
-    HIP_TRY(launch_gemv(a, st));
-    HIP_TRY(launch_rownorm(h, part, O_SPLITS, static_cast<size_t>(B) * H, H, B,
-                           u16p(y.post_norm), eps, xn, H, nullptr, st));
-    HIP_TRY(launch_gateup(y.wg, y.wu, W_BF16, xn, B, u16, st));
-    a.w = seg1(y.wd, H);
-    a.K = F;
-    a.x = u16;
-    a.x_stride = F;
-    a.S = DOWN_SPLITS;
-    HIP_TRY(launch_gemv(a, st));
-    const bool last = l == L - 1;
-    HIP_TRY(launch_rownorm(h, part, DOWN_SPLITS, static_cast<size_t>(B) * H, H, B,
-                           u16p(last ? w->final_norm : w->layer[l + 1].in_norm), eps, xn, H,
-                           last ? static_cast<uint16_t*>(hidden_opt) : nullptr, st));
+    q.wq[l] = u16p(y.wq);
+    q.wk[l] = u16p(y.wk);
+    q.wv[l] = u16p(y.wv);
+    q.wo[l] = u16p(y.wo);
+    q.wg[l] = u16p(y.wg);
+    q.wu[l] = u16p(y.wu);
+    q.wd[l] = u16p(y.wd);
+    q.in_norm[l] = u16p(y.in_norm);
+    q.q_norm[l] = u16p(y.q_norm);
+    q.k_norm[l] = u16p(y.k_norm);
+    q.post_norm[l] = u16p(y.post_norm);
   }
-  if (B > 1) {
-    HIP_TRY(launch_lmhead_argmax(u16p(w->lm_head), w->vocab, xn + H, B - 1,
-                                 at<uint64_t>(ws, Lw.keys), LMH_GRID,
-                                 static_cast<uint16_t*>(logits_opt), cand, st));
+  q.final_norm = u16p(w->final_norm);
+  q.embed = u16p(w->embed);
+  q.lm = u16p(w->lm_head);
+  q.vocab = w->vocab;
+  q.eps = w->rms_eps;
+  q.scale_log2 = w->attn_scale * 1.4426950408889634f;
+  q.theta = static_cast<double>(w->rope_theta);
+  q.ring_k = static_cast<const uint16_t*>(kv->k);
+  q.ring_vt = static_cast<const uint16_t*>(kv->vt);
+  q.cap = kv->capacity;
+  // Attention split over the visible context [lo, p): one block per (KV head,
+  // chunk of cb 32-cell blocks), at most min(grid / 2, 128) chunks per head;
+  // the last chunk of each head also takes the block rows.
+  q.lo = p - kv->window > 0 ? p - kv->window : 0;
+  q.hi = p;
+  if (p > q.lo) {
+    const int maxch = grid / 2 < 128 ? grid / 2 : 128;
+    q.p0 = q.lo & ~static_cast<int64_t>(31);
+    q.nb = static_cast<int>((p - q.p0 + 31) / 32);
+    q.cb = (q.nb + maxch - 1) / maxch;
+    q.nch = (q.nb + q.cb - 1) / q.cb;
+  } else {
+    q.p0 = 0;
+    q.nb = 0;
+    q.cb = 1;
+    q.nch = 1;  // block rows only
   }
+  q.B = block;
+  q.p = p;
+  q.anchor = anchor_id;
+  q.mask = mask_id;
+  q.h = at<float>(ws, Lw.h);
+  q.ss = at<float>(ws, Lw.ss);
+  q.qkv = at<float>(ws, Lw.qkv);
+  q.rope = at<float2>(ws, Lw.rope);
+  q.po = at<float>(ws, Lw.po);
+  q.pm = at<float>(ws, Lw.pm);
+  q.pl = at<float>(ws, Lw.pl);
+  q.o16 = at<uint16_t>(ws, Lw.o16);
+  q.u16 = at<uint16_t>(ws, Lw.u16);
+  q.keys = at<uint64_t>(ws, Lw.keys);
+  q.bar = at<unsigned>(ws, Lw.bar);
+  q.tab = at<void>(ws, Lw.tab);
+  q.spin_limit = SPIN_LIMIT;
+  q.grid = grid;
+  q.cand = cand;
+  q.logits = static_cast<uint16_t*>(logits_opt);
+  q.hidden = static_cast<uint16_t*>(hidden_opt);
+  HIP_TRY(launch_draft_pass(q, st));
   return DFLASH_OK;
 }
 

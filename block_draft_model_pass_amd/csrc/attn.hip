@@ -11,8 +11,9 @@
 //   S^T = K Q^T  : 2 cell tiles x 8 k-steps of MFMA 16x16x32 f16; the lane
 //                  holding S^T[4g+i][n] and S^T[16+4g+i][n] owns exactly the
 //                  8 probabilities it must feed as the B operand of P V,
-//   O^T += V^T P^T: 16 MFMAs; V is stored transposed (cell index fastest) so
-//                  the A operand is two 8-byte loads per lane.
+//   O^T += V^T P^T: 16 MFMAs; V is stored transposed in 32-cell blocks
+//                  ([block][dim][cell]) so the A operand is two 8-byte loads
+//                  per lane and a block's values are one contiguous run.
 // No LDS, no transposes.  A second kernel merges the chunks' (max, sum, O)
 // partials flash-decoding style.
 #include "common.h"
@@ -46,13 +47,12 @@ __global__ __launch_bounds__(384) void k_attn_partial(AttnArgs a) {
     qf[s] = qv ? *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0);
 
   const uint16_t *kb, *vb;
-  int vstride, nblk;
+  int nblk;
   int64_t lo, hi, pstart;
   int cap;
   if (c < a.nch) {
     kb = a.ring_k + static_cast<size_t>(j) * a.cap * D;
     vb = a.ring_vt + static_cast<size_t>(j) * D * a.cap;
-    vstride = a.cap;
     cap = a.cap;
     const int blk0 = c * a.cb;
     nblk = min(a.cb, a.nb - blk0);
@@ -62,7 +62,6 @@ __global__ __launch_bounds__(384) void k_attn_partial(AttnArgs a) {
   } else {
     kb = a.kblk + static_cast<size_t>(j) * BLK_CELLS * D;
     vb = a.vblkT + static_cast<size_t>(j) * D * BLK_CELLS;
-    vstride = BLK_CELLS;
     cap = BLK_CELLS;
     nblk = 1;
     pstart = 0;
@@ -80,11 +79,35 @@ __global__ __launch_bounds__(384) void k_attn_partial(AttnArgs a) {
     const int cidx = static_cast<int>(pb % cap);  // 32 consecutive ring cells
     const uint16_t* k0 = kb + static_cast<size_t>(cidx + n) * D + 8 * g;
     const uint16_t* k1 = k0 + 16 * D;
+    // Issue the block's K loads and the first half of its V loads together
+    // so the V latency hides behind the score MFMAs and the softmax; the
+    // second V half is issued once the K registers are free.
+    const uint16_t* vbase = vb + static_cast<size_t>(cidx / 32) * (D * 32) + n * 32 + 4 * g;
+    uint4 kr0[8], kr1[8];
+    uint2 va0[8], va1[8], vb0[8], vb1[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      kr0[s] = *reinterpret_cast<const uint4*>(k0 + 32 * s);
+      kr1[s] = *reinterpret_cast<const uint4*>(k1 + 32 * s);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint16_t* vp = vbase + 16 * dt * 32;
+      va0[dt] = *reinterpret_cast<const uint2*>(vp);
+      va1[dt] = *reinterpret_cast<const uint2*>(vp + 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      s0 = mfma_f16(*reinterpret_cast<const uint4*>(k0 + 32 * s), qf[s], s0);
-      s1 = mfma_f16(*reinterpret_cast<const uint4*>(k1 + 32 * s), qf[s], s1);
+      s0 = mfma_f16(kr0[s], qf[s], s0);
+      s1 = mfma_f16(kr1[s], qf[s], s1);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint16_t* vp = vbase + 16 * (dt + 8) * 32;
+      vb0[dt] = *reinterpret_cast<const uint2*>(vp);
+      vb1[dt] = *reinterpret_cast<const uint2*>(vp + 16);
     }
     const bool full = pb >= lo && pb + 32 <= hi;
     float x[8];
@@ -127,11 +150,10 @@ __global__ __launch_bounds__(384) void k_attn_partial(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) {
       o[dt] *= alpha;
-      const uint16_t* vp = vb + static_cast<size_t>(16 * dt + n) * vstride + cidx + 4 * g;
-      uint2 v0 = *reinterpret_cast<const uint2*>(vp);
-      uint2 v1 = *reinterpret_cast<const uint2*>(vp + 16);
-      uint4 va = make_uint4(v0.x & vm[0], v0.y & vm[1], v1.x & vm[2], v1.y & vm[3]);
-      o[dt] = mfma_f16(va, pf, o[dt]);
+      const uint2 x0 = dt < 8 ? va0[dt] : vb0[dt - 8];
+      const uint2 x1 = dt < 8 ? va1[dt] : vb1[dt - 8];
+      const uint4 v = make_uint4(x0.x & vm[0], x0.y & vm[1], x1.x & vm[2], x1.y & vm[3]);
+      o[dt] = mfma_f16(v, pf, o[dt]);
     }
   }
 
@@ -146,29 +168,50 @@ __global__ __launch_bounds__(384) void k_attn_partial(AttnArgs a) {
   for (int dt = 0; dt < 16; ++dt) *reinterpret_cast<f32x4*>(op + 16 * dt) = o[dt];
 }
 
-// One block per (KV head, query tile, query row); thread = head dimension.
+// One block per (KV head, query tile, 16 head dims); thread (qrow, dim).
+// Chunks are combined 16 at a time with every load of a group in flight,
+// rescaling the running sum whenever the running max grows.
+constexpr int MG = 16;
+
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int id = blockIdx.x;
-  const int n = id & 15;
+  const int dtile = id & 15;
   const int t = (id >> 4) % a.nqt;
   const int j = (id >> 4) / a.nqt;
+  const int n = threadIdx.x >> 4, dd = threadIdx.x & 15;
   const int r = t * 16 + n;
   if (r >= G * a.B) return;
-  const int bi = r / G, hl = r % G;
+  const int d = dtile * 16 + dd;
   const int nc = a.nch + 1;
-  const int d = threadIdx.x;
-  float M = NEG_INF;
-  for (int c = 0; c < nc; ++c) {
-    const size_t base = (static_cast<size_t>(j) * nc + c) * a.nqt + t;
-    M = fmaxf(M, a.pm[base * 16 + n]);
+  const size_t cstride = static_cast<size_t>(a.nqt) * 16;  // (chunk -> chunk) in rows
+  const size_t row0 = (static_cast<size_t>(j) * nc * a.nqt + t) * 16 + n;
+  float M = NEG_INF, lsum = 0.f, acc = 0.f;
+  for (int c0 = 0; c0 < nc; c0 += MG) {
+    float mv[MG], lv[MG], ov[MG];
+#pragma unroll
+    for (int u = 0; u < MG; ++u) {
+      const int c = c0 + u;
+      const size_t row = row0 + static_cast<size_t>(c) * cstride;
+      const bool ok = c < nc;
+      mv[u] = ok ? a.pm[row] : NEG_INF;
+      lv[u] = ok ? a.pl[row] : 0.f;
+      ov[u] = ok ? a.po[row * D + d] : 0.f;
+    }
+    float gm = M;
+#pragma unroll
+    for (int u = 0; u < MG; ++u) gm = fmaxf(gm, mv[u]);
+    const float sc = M == NEG_INF ? 0.f : exp2f(M - gm);
+    lsum *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int u = 0; u < MG; ++u) {
+      const float w = exp2f(mv[u] - gm);
+      lsum += lv[u] * w;
+      acc += ov[u] * w;
+    }
+    M = gm;
   }
-  float lsum = 0.f, acc = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const size_t base = (static_cast<size_t>(j) * nc + c) * a.nqt + t;
-    const float w = exp2f(a.pm[base * 16 + n] - M);
-    lsum += a.pl[base * 16 + n] * w;
-    acc += a.po[(base * 16 + n) * D + d] * w;
-  }
+  const int bi = r / G, hl = r % G;
   a.o16[static_cast<size_t>(bi) * NQ * D + (j * G + hl) * D + d] = f32_to_bf16(acc / lsum);
 }
 

@@ -152,15 +152,16 @@ hipError_t launch_rownorm(float* h, const float* part, int S, size_t part_split_
                           int part_row_stride, int rows, const uint16_t* gain, float eps,
                           uint16_t* out, int out_stride, uint16_t* out2, hipStream_t st);
 
+// Embedding gather + input norm of the block rows, and the RoPE (cos, sin)
+// table of positions p .. p+B-1: rope[b][t], t < 128.
 hipError_t launch_embed_norm(const uint16_t* embed, int anchor, int mask, int B,
-                             const uint16_t* gain, float eps, float* h, uint16_t* xn,
-                             hipStream_t st);
+                             const uint16_t* gain, float eps, float* h, uint16_t* xn, int64_t p,
+                             double theta, float2* rope, hipStream_t st);
 
 // Per-head q/k RMSNorm + NeoX RoPE of the fused QKV output of the block rows.
-hipError_t launch_qkv_post(const float* part, int S, int B, int64_t p,
+hipError_t launch_qkv_post(const float* part, int S, int B, const float2* rope,
                            const uint16_t* q_norm, const uint16_t* k_norm, float eps,
-                           double theta, uint16_t* q16, uint16_t* kblk, uint16_t* vblkT,
-                           hipStream_t st);
+                           uint16_t* q16, uint16_t* kblk, uint16_t* vblkT, hipStream_t st);
 
 // Context K/V epilogue: y [n][KV_N] (row stride ldy, S partial splits) ->
 // k-norm + RoPE + fp16 into the ring.
@@ -174,7 +175,7 @@ struct AttnArgs {
   int nqt;                 // query tiles of 16 rows: ceil(12 B / 16)
   // context segment (ring) for chunks < nch
   const uint16_t* ring_k;  // fp16 [2][cap][256] for this layer
-  const uint16_t* ring_vt; // fp16 [2][256][cap]
+  const uint16_t* ring_vt; // fp16 [2][cap/32][256][32]
   int cap;
   int64_t lo, hi;          // visible positions [lo, hi)
   int64_t p0;              // first position of block 0 (multiple of 32)
@@ -196,6 +197,59 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 // C[M][N] (fp32, ldc) = A[M][K] (bf16, lda) * W[N][K]^T
 hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w, int K,
                             float* C, int ldc, int N, hipStream_t st);
+
+// The whole proposal pass as one persistent kernel (plus a small init kernel).
+struct PassLaunch {
+  const uint16_t* wq[L];
+  const uint16_t* wk[L];
+  const uint16_t* wv[L];
+  const uint16_t* wo[L];
+  const uint16_t* wg[L];
+  const uint16_t* wu[L];
+  const uint16_t* wd[L];
+  const uint16_t* in_norm[L];
+  const uint16_t* q_norm[L];
+  const uint16_t* k_norm[L];
+  const uint16_t* post_norm[L];
+  const uint16_t* final_norm;
+  const uint16_t* embed;
+  const uint16_t* lm;
+  int vocab;
+  float eps, scale_log2;
+  double theta;
+  const uint16_t* ring_k;    // layer 0 of the ring
+  const uint16_t* ring_vt;
+  int cap;
+  int64_t lo, hi, p0;        // visible positions [lo, hi); first block position
+  int nb, cb, nch;           // 32-cell blocks, blocks per chunk, chunks
+  int B;
+  int64_t p;
+  int anchor, mask;
+  float* h;
+  float* ss;
+  float* qkv;
+  float2* rope;
+  float* po;
+  float* pm;
+  float* pl;
+  uint16_t* o16;
+  uint16_t* u16;
+  uint64_t* keys;
+  unsigned* bar;
+  void* tab;                 // workspace room for the per-layer pointer table
+  unsigned spin_limit;
+  int grid;
+  int32_t* cand;
+  uint16_t* logits;
+  uint16_t* hidden;
+};
+
+hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st);
+// Largest co-resident grid of the pass kernel on `device` (0 if it cannot run).
+hipError_t draft_pass_max_grid(int device, int* grid);
+size_t pass_smem_bytes();
+size_t pass_tab_bytes();
+size_t pass_bar_bytes();
 
 hipError_t launch_verify(const int32_t* cand, const int32_t* target, int k, int32_t* out,
                          hipStream_t st);

@@ -8,6 +8,12 @@
 // at k = 8*(4j + g), j = 0..3: every load instruction reads 64 contiguous
 // bytes of each of 16 rows, and the same k slots are used for the weights and
 // the activations, so the k order inside the MFMA does not matter.
+//
+// Bytes in flight decide the achieved bandwidth: every wave issues all the
+// weight loads of its slice (KBW blocks = KBW KiB per wave) before its first
+// MFMA (a scheduling barrier keeps the compiler from interleaving them), and
+// the LM head double-buffers whole tiles while reusing the activation
+// fragments it loaded once.
 #include "common.h"
 
 namespace dfl {
@@ -18,6 +24,13 @@ __device__ __forceinline__ uint4 ld16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// Streamed once: keep weights from displacing reusable lines in the caches.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld16_stream(const uint16_t* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+
 __device__ __forceinline__ const uint16_t* seg_row(const SegTable& t, int row, int K) {
   int seg = 0, base = 0;
   for (int i = 0; i + 1 < t.nseg; ++i)
@@ -25,23 +38,26 @@ __device__ __forceinline__ const uint16_t* seg_row(const SegTable& t, int row, i
   return static_cast<const uint16_t*>(t.ptr[seg]) + static_cast<size_t>(row - base) * K;
 }
 
-// Partial dot products of one wave: 16 weight rows x KBW*128 k, bf16.
 template <int KBW>
-__device__ __forceinline__ f32x4 wave_tile_bf16(const uint16_t* wrow, const uint16_t* xrow,
-                                                bool xvalid, int kbeg, int g) {
+__device__ __forceinline__ void load_w(uint4 (&w)[4 * KBW], const uint16_t* wrow, int kbeg,
+                                       int g) {
+#pragma unroll
+  for (int i = 0; i < 4 * KBW; ++i) w[i] = ld16_stream(wrow + kbeg + 8 * (4 * i + g));
+}
+
+template <int KBW>
+__device__ __forceinline__ void load_x(uint4 (&x)[4 * KBW], const uint16_t* xrow, bool valid,
+                                       int kbeg, int g) {
+#pragma unroll
+  for (int i = 0; i < 4 * KBW; ++i)
+    x[i] = valid ? ld16(xrow + kbeg + 8 * (4 * i + g)) : make_uint4(0, 0, 0, 0);
+}
+
+template <int KBW>
+__device__ __forceinline__ f32x4 mma_chain(const uint4 (&w)[4 * KBW], const uint4 (&x)[4 * KBW]) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kb = 0; kb < KBW; ++kb) {
-    uint4 w[4], x[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = kbeg + kb * 128 + 8 * (4 * j + g);
-      w[j] = ld16(wrow + k);
-      x[j] = xvalid ? ld16(xrow + k) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc = mfma_bf16(w[j], x[j], acc);
-  }
+  for (int i = 0; i < 4 * KBW; ++i) acc = mfma_bf16(w[i], x[i], acc);
   return acc;
 }
 
@@ -67,7 +83,11 @@ __global__ __launch_bounds__(NW * 64) void k_gemv_bf16(GemvArgs a) {
   const bool xv = r < a.B;
   const uint16_t* xrow = a.x + static_cast<size_t>(xv ? r : 0) * a.x_stride;
   const int kbeg = (blockIdx.y * NW + wave) * (KBW * 128);
-  f32x4 acc = wave_tile_bf16<KBW>(wrow, xrow, xv, kbeg, g);
+  uint4 w[4 * KBW], x[4 * KBW];
+  load_w<KBW>(w, wrow, kbeg, g);
+  load_x<KBW>(x, xrow, xv, kbeg, g);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 acc = mma_chain<KBW>(w, x);
   acc = reduce_waves<NW>(acc, red, wave, lane);
   if (wave == 0 && xv) {
     float* o = a.out + (static_cast<size_t>(blockIdx.y) * a.B + r) * a.N + row0 + 4 * g;
@@ -88,23 +108,13 @@ __global__ __launch_bounds__(NW * 64) void k_gateup_bf16(const uint16_t* wg, con
   const uint16_t* xrow = x + static_cast<size_t>(xv ? r : 0) * H;
   const size_t roff = static_cast<size_t>(row0 + r) * H;
   const int kbeg = wave * (KBW * 128);
-  f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kb = 0; kb < KBW; ++kb) {
-    uint4 w1[4], w2[4], xx[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = kbeg + kb * 128 + 8 * (4 * j + g);
-      w1[j] = ld16(wg + roff + k);
-      w2[j] = ld16(wu + roff + k);
-      xx[j] = xv ? ld16(xrow + k) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ag = mfma_bf16(w1[j], xx[j], ag);
-      au = mfma_bf16(w2[j], xx[j], au);
-    }
-  }
+  uint4 w1[4 * KBW], w2[4 * KBW], xx[4 * KBW];
+  load_w<KBW>(w1, wg + roff, kbeg, g);
+  load_w<KBW>(w2, wu + roff, kbeg, g);
+  load_x<KBW>(xx, xrow, xv, kbeg, g);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 ag = mma_chain<KBW>(w1, xx);
+  f32x4 au = mma_chain<KBW>(w2, xx);
   if (wave > 0) {
     red[0][wave - 1][lane] = ag;
     red[1][wave - 1][lane] = au;
@@ -137,80 +147,120 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-// LM head: grid-stride over 16-row vocabulary tiles; each block keeps the
-// best (value, lowest index) key per activation row and writes it once.
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// One LM-head tile's epilogue on wave 0: argmax key update and optional
+// bf16 logits.
+__device__ __forceinline__ void lm_epilogue(f32x4 acc, int row0, int r, int g, bool xv,
+                                            int vocab, uint16_t* logits, uint64_t& best) {
+  if (!xv) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    best = umax64(best, argmax_key(acc[i], static_cast<uint32_t>(row0 + 4 * g + i)));
+  if (logits) {
+    uint16_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16(acc[i]);
+    uint2 pk = make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
+                          o[2] | (static_cast<uint32_t>(o[3]) << 16));
+    *reinterpret_cast<uint2*>(logits + static_cast<size_t>(r) * vocab + row0 + 4 * g) = pk;
+  }
+}
+
+// LM head: grid-stride over 16-row vocabulary tiles.  Each wave keeps the
+// activation fragments of its k quarter in registers and double-buffers the
+// weight tiles; each block keeps the best (value, lowest index) key per
+// activation row and writes it once.
 template <int NW, int KBW>
 __global__ __launch_bounds__(NW * 64) void k_lmhead_bf16(const uint16_t* lm, int ntiles, int vocab,
                                                          const uint16_t* z, int B, uint64_t* keys,
                                                          uint16_t* logits) {
-  __shared__ f32x4 red[NW - 1][64];
+  __shared__ f32x4 red[2][NW - 1][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const bool xv = r < B;
-  const uint16_t* xrow = z + static_cast<size_t>(xv ? r : 0) * H;
   const int kbeg = wave * (KBW * 128);
+  uint4 x[4 * KBW];
+  load_x<KBW>(x, z + static_cast<size_t>(xv ? r : 0) * H, xv, kbeg, g);
+  const size_t roff = static_cast<size_t>(r) * H;
   uint64_t best = 0;
-  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int row0 = t * 16;
-    const uint16_t* wrow = lm + static_cast<size_t>(row0 + r) * H;
-    f32x4 acc = wave_tile_bf16<KBW>(wrow, xrow, xv, kbeg, g);
-    acc = reduce_waves<NW>(acc, red, wave, lane);
-    if (wave == 0 && xv) {
+  const int step = gridDim.x;
+  int t = blockIdx.x;
+  uint4 wa[4 * KBW], wb[4 * KBW];
+  if (t < ntiles) load_w<KBW>(wa, lm + static_cast<size_t>(t) * 16 * H + roff, kbeg, g);
+  int parity = 0;
+  while (t < ntiles) {
+    // tile t is in wa; prefetch t + step into wb, compute wa (then the roles swap)
+    const int tn = t + step;
+    if (tn < ntiles) load_w<KBW>(wb, lm + static_cast<size_t>(tn) * 16 * H + roff, kbeg, g);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc = mma_chain<KBW>(wa, x);
+    if (wave > 0) red[parity][wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint64_t k = argmax_key(acc[i], static_cast<uint32_t>(row0 + 4 * g + i));
-        best = k > best ? k : best;
-      }
-      if (logits) {
-        uint16_t o[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16(acc[i]);
-        uint2 pk = make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
-                              o[2] | (static_cast<uint32_t>(o[3]) << 16));
-        *reinterpret_cast<uint2*>(logits + static_cast<size_t>(r) * vocab + row0 + 4 * g) = pk;
-      }
+      for (int w = 0; w < NW - 1; ++w) acc += red[parity][w][lane];
+      lm_epilogue(acc, t * 16, r, g, xv, vocab, logits, best);
     }
-    __syncthreads();  // red[] is reused by the next tile
+    parity ^= 1;
+    t = tn;
+    if (t >= ntiles) break;
+    const int tn2 = t + step;
+    if (tn2 < ntiles) load_w<KBW>(wa, lm + static_cast<size_t>(tn2) * 16 * H + roff, kbeg, g);
+    __builtin_amdgcn_sched_barrier(0);
+    acc = mma_chain<KBW>(wb, x);
+    if (wave > 0) red[parity][wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 0; w < NW - 1; ++w) acc += red[parity][w][lane];
+      lm_epilogue(acc, t * 16, r, g, xv, vocab, logits, best);
+    }
+    parity ^= 1;
+    t = tn2;
   }
   if (wave == 0) {
-    uint64_t o = shfl_xor_u64(best, 16);
-    best = o > best ? o : best;
-    o = shfl_xor_u64(best, 32);
-    best = o > best ? o : best;
+    best = umax64(best, shfl_xor_u64(best, 16));
+    best = umax64(best, shfl_xor_u64(best, 32));
     if (g == 0 && xv) keys[static_cast<size_t>(blockIdx.x) * MAXB + r] = best;
   }
 }
 
-// cand[b] = index part of the largest key over all blocks.
-__global__ __launch_bounds__(256) void k_argmax_reduce(const uint64_t* keys, int nblk, int B,
-                                                       int32_t* cand) {
-  __shared__ uint64_t s[256];
-  for (int b = 0; b < B; ++b) {
-    uint64_t best = 0;
-    for (int i = threadIdx.x; i < nblk; i += 256) {
-      const uint64_t k = keys[static_cast<size_t>(i) * MAXB + b];
-      best = k > best ? k : best;
+// cand[b] = index part of the largest key over all blocks; wave b takes row b.
+__global__ __launch_bounds__(MAXB * 64) void k_argmax_reduce(const uint64_t* keys, int nblk,
+                                                             int B, int32_t* cand) {
+  const int b = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (b >= B) return;
+  uint64_t best = 0;
+  constexpr int U = 16;
+  for (int i0 = lane; i0 < nblk; i0 += 64 * U) {
+    uint64_t k[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + 64 * u;
+      k[u] = i < nblk ? keys[static_cast<size_t>(i) * MAXB + b] : 0;
     }
-    s[threadIdx.x] = best;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-      if (threadIdx.x < w) {
-        const uint64_t o = s[threadIdx.x + w];
-        if (o > s[threadIdx.x]) s[threadIdx.x] = o;
-      }
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) cand[b] = static_cast<int32_t>(~static_cast<uint32_t>(s[0]));
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < U; ++u) best = umax64(best, k[u]);
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) best = umax64(best, shfl_xor_u64(best, o));
+  if (lane == 0) cand[b] = static_cast<int32_t>(~static_cast<uint32_t>(best));
 }
 
+// accepted = longest prefix with cand == target; all loads issued at once.
 __global__ void k_verify(const int32_t* cand, const int32_t* target, int k, int32_t* out) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int a = 0;
-  while (a < k && cand[a] == target[a]) ++a;
-  out[0] = a;
-  out[1] = target[a];
+  const int lane = threadIdx.x;
+  const int c = lane < k ? cand[lane] : 0;
+  const int t = lane <= k ? target[lane] : 0;
+  const bool miss = lane < k && c != t;
+  const uint64_t m = __ballot(miss || lane == k);
+  const int a = __ffsll(static_cast<unsigned long long>(m)) - 1;  // first mismatch or k
+  const int nxt = __shfl(t, a, 64);
+  if (lane == 0) {
+    out[0] = a;
+    out[1] = nxt;
+  }
 }
 
 }  // namespace
@@ -248,7 +298,7 @@ hipError_t launch_lmhead_argmax(const uint16_t* lm, int vocab, const uint16_t* z
                      keys, logits_opt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_argmax_reduce, dim3(1), dim3(256), 0, st, keys, grid, B, cand);
+  hipLaunchKernelGGL(k_argmax_reduce, dim3(1), dim3(MAXB * 64), 0, st, keys, grid, B, cand);
   return hipGetLastError();
 }
 

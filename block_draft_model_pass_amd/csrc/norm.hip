@@ -11,21 +11,27 @@ namespace {
 constexpr int NT = 256;             // threads per row
 constexpr int PER = H / NT;         // 10 elements per thread
 
-__global__ __launch_bounds__(NT) void k_rownorm(float* h, const float* part, int S,
-                                                size_t sstride, int rstride, const uint16_t* gain,
-                                                float eps, uint16_t* out, int ostride,
-                                                uint16_t* out2) {
+template <int S>
+__global__ __launch_bounds__(NT) void k_rownorm(float* h, const float* part, size_t sstride,
+                                                int rstride, const uint16_t* gain, float eps,
+                                                uint16_t* out, int ostride, uint16_t* out2) {
   __shared__ float red[NT / 64];
   const int b = blockIdx.x;
   float v[PER];
-  float ss = 0.f;
+  float pv[S][PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = threadIdx.x + NT * i;
-    float x = h ? h[static_cast<size_t>(b) * H + e] : 0.f;
-    for (int s = 0; s < S; ++s) x += part[s * sstride + static_cast<size_t>(b) * rstride + e];
-    v[i] = x;
-    ss += x * x;
+    v[i] = h ? h[static_cast<size_t>(b) * H + e] : 0.f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) pv[s][i] = part[s * sstride + static_cast<size_t>(b) * rstride + e];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) v[i] += pv[s][i];
+    ss += v[i] * v[i];
   }
   if (h) {
 #pragma unroll
@@ -42,11 +48,29 @@ __global__ __launch_bounds__(NT) void k_rownorm(float* h, const float* part, int
   }
 }
 
+// cos/sin of the NeoX RoPE angle pos * theta^(-2t/256), computed in fp64.
+__device__ __forceinline__ void rope_cs(int64_t pos, int t, double theta, float& fc, float& fs) {
+  const double inv = pow(theta, -2.0 * static_cast<double>(t) / static_cast<double>(D));
+  const double ang = static_cast<double>(pos) * inv;
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  fc = static_cast<float>(cs);
+  fs = static_cast<float>(sn);
+}
+
+// Embedding rows of the block plus the RoPE table of the block positions
+// p .. p+B-1 (shared by all five layers): rope[b][t] = (cos, sin).
 __global__ __launch_bounds__(NT) void k_embed_norm(const uint16_t* embed, int anchor, int mask,
                                                    const uint16_t* gain, float eps, float* h,
-                                                   uint16_t* xn) {
+                                                   uint16_t* xn, int64_t p, double theta,
+                                                   float2* rope) {
   __shared__ float red[NT / 64];
   const int b = blockIdx.x;
+  if (threadIdx.x < D / 2) {
+    float fc, fs;
+    rope_cs(p + b, threadIdx.x, theta, fc, fs);
+    rope[b * (D / 2) + threadIdx.x] = make_float2(fc, fs);
+  }
   const int tok = b == 0 ? anchor : mask;
   const uint16_t* row = embed + static_cast<size_t>(tok) * H;
   float v[PER];
@@ -68,20 +92,15 @@ __global__ __launch_bounds__(NT) void k_embed_norm(const uint16_t* embed, int an
 }
 
 // RMSNorm over one 256-wide head held as (a, c) = elements (t, t + 128) of
-// thread t, then NeoX rotation of the pair by angle pos * theta^(-2t/256).
-// The angle, its sine and its cosine are computed in fp64.
+// thread t, then NeoX rotation of the pair by the angle whose cos/sin are
+// (fc, fs).
 __device__ __forceinline__ void norm_rope(float& a, float& c, const uint16_t* gain, float eps,
-                                          int64_t pos, double theta, float* red) {
+                                          float fc, float fs, float* red) {
   const int t = threadIdx.x;
   const float ss = block_sum<128>(a * a + c * c, red);
   const float sc = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
   a *= sc * bf16_to_f32(gain[t]);
   c *= sc * bf16_to_f32(gain[t + 128]);
-  const double inv = pow(theta, -2.0 * static_cast<double>(t) / static_cast<double>(D));
-  const double ang = static_cast<double>(pos) * inv;
-  double sn, cs;
-  sincos(ang, &sn, &cs);
-  const float fc = static_cast<float>(cs), fs = static_cast<float>(sn);
   const float a2 = a * fc - c * fs;
   const float c2 = c * fc + a * fs;
   a = a2;
@@ -89,10 +108,11 @@ __device__ __forceinline__ void norm_rope(float& a, float& c, const uint16_t* ga
 }
 
 // grid (B, 28): heads 0..23 = q, 24..25 = k, 26..27 = v; block 128.
-__global__ __launch_bounds__(128) void k_qkv_post(const float* part, int S, int B, int64_t p,
-                                                  const uint16_t* q_norm, const uint16_t* k_norm,
-                                                  float eps, double theta, uint16_t* q16,
-                                                  uint16_t* kblk, uint16_t* vblkT) {
+__global__ __launch_bounds__(128) void k_qkv_post(const float* part, int S, int B,
+                                                  const float2* rope, const uint16_t* q_norm,
+                                                  const uint16_t* k_norm, float eps,
+                                                  uint16_t* q16, uint16_t* kblk,
+                                                  uint16_t* vblkT) {
   __shared__ float red[2];
   const int b = blockIdx.x, hd = blockIdx.y, t = threadIdx.x;
   const int col = hd < NQ ? hd * D : (hd < NQ + NKV ? NQ * D + (hd - NQ) * D
@@ -103,13 +123,14 @@ __global__ __launch_bounds__(128) void k_qkv_post(const float* part, int S, int 
     a += r[t];
     c += r[t + 128];
   }
+  const float2 cs = rope[b * (D / 2) + t];
   if (hd < NQ) {
-    norm_rope(a, c, q_norm, eps, p + b, theta, red);
+    norm_rope(a, c, q_norm, eps, cs.x, cs.y, red);
     uint16_t* q = q16 + (static_cast<size_t>(b) * NQ + hd) * D;
     q[t] = f32_to_f16_bits(a);
     q[t + 128] = f32_to_f16_bits(c);
   } else if (hd < NQ + NKV) {
-    norm_rope(a, c, k_norm, eps, p + b, theta, red);
+    norm_rope(a, c, k_norm, eps, cs.x, cs.y, red);
     uint16_t* k = kblk + (static_cast<size_t>(hd - NQ) * BLK_CELLS + b) * D;
     k[t] = f32_to_f16_bits(a);
     k[t + 128] = f32_to_f16_bits(c);
@@ -141,14 +162,17 @@ __global__ __launch_bounds__(128) void k_kv_post(const float* y, int S, size_t s
   const int64_t pos = pos0 + row;
   const size_t cell = static_cast<size_t>(pos % cap);
   if (w < NKV) {
-    norm_rope(a, c, kn.g[l], eps, pos, theta, red);
+    float fc, fs;
+    rope_cs(pos, t, theta, fc, fs);
+    norm_rope(a, c, kn.g[l], eps, fc, fs, red);
     uint16_t* k = ring_k + ((static_cast<size_t>(l) * NKV + w) * cap + cell) * D;
     k[t] = f32_to_f16_bits(a);
     k[t + 128] = f32_to_f16_bits(c);
   } else {
-    uint16_t* v = ring_vt + (static_cast<size_t>(l) * NKV + (w - NKV)) * D * cap;
-    v[static_cast<size_t>(t) * cap + cell] = f32_to_f16_bits(a);
-    v[static_cast<size_t>(t + 128) * cap + cell] = f32_to_f16_bits(c);
+    uint16_t* v = ring_vt + (static_cast<size_t>(l) * NKV + (w - NKV)) * D * cap +
+                  (cell / BLK_CELLS) * (D * BLK_CELLS) + (cell % BLK_CELLS);
+    v[static_cast<size_t>(t) * BLK_CELLS] = f32_to_f16_bits(a);
+    v[static_cast<size_t>(t + 128) * BLK_CELLS] = f32_to_f16_bits(c);
   }
 }
 
@@ -158,23 +182,38 @@ hipError_t launch_rownorm(float* h, const float* part, int S, size_t part_split_
                           int part_row_stride, int rows, const uint16_t* gain, float eps,
                           uint16_t* out, int out_stride, uint16_t* out2, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rownorm, dim3(rows), dim3(NT), 0, st, h, part, S, part_split_stride,
-                     part_row_stride, gain, eps, out, out_stride, out2);
+  switch (S) {
+    case 1:
+      hipLaunchKernelGGL(k_rownorm<1>, dim3(rows), dim3(NT), 0, st, h, part, part_split_stride,
+                         part_row_stride, gain, eps, out, out_stride, out2);
+      break;
+    case 3:
+      hipLaunchKernelGGL(k_rownorm<3>, dim3(rows), dim3(NT), 0, st, h, part, part_split_stride,
+                         part_row_stride, gain, eps, out, out_stride, out2);
+      break;
+    case 5:
+      hipLaunchKernelGGL(k_rownorm<5>, dim3(rows), dim3(NT), 0, st, h, part, part_split_stride,
+                         part_row_stride, gain, eps, out, out_stride, out2);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_embed_norm(const uint16_t* embed, int anchor, int mask, int B,
-                             const uint16_t* gain, float eps, float* h, uint16_t* xn,
-                             hipStream_t st) {
-  hipLaunchKernelGGL(k_embed_norm, dim3(B), dim3(NT), 0, st, embed, anchor, mask, gain, eps, h, xn);
+                             const uint16_t* gain, float eps, float* h, uint16_t* xn, int64_t p,
+                             double theta, float2* rope, hipStream_t st) {
+  hipLaunchKernelGGL(k_embed_norm, dim3(B), dim3(NT), 0, st, embed, anchor, mask, gain, eps, h, xn,
+                     p, theta, rope);
   return hipGetLastError();
 }
 
-hipError_t launch_qkv_post(const float* part, int S, int B, int64_t p, const uint16_t* q_norm,
-                           const uint16_t* k_norm, float eps, double theta, uint16_t* q16,
-                           uint16_t* kblk, uint16_t* vblkT, hipStream_t st) {
-  hipLaunchKernelGGL(k_qkv_post, dim3(B, NQ + 2 * NKV), dim3(128), 0, st, part, S, B, p, q_norm,
-                     k_norm, eps, theta, q16, kblk, vblkT);
+hipError_t launch_qkv_post(const float* part, int S, int B, const float2* rope,
+                           const uint16_t* q_norm, const uint16_t* k_norm, float eps,
+                           uint16_t* q16, uint16_t* kblk, uint16_t* vblkT, hipStream_t st) {
+  hipLaunchKernelGGL(k_qkv_post, dim3(B, NQ + 2 * NKV), dim3(128), 0, st, part, S, B, rope, q_norm,
+                     k_norm, eps, q16, kblk, vblkT);
   return hipGetLastError();
 }
 

@@ -1,0 +1,1080 @@
+// The whole proposal pass as one persistent kernel (Strata PR #1426 page:
+// "Drafter runtime" -- five dense layers, shared LM head, greedy proposals;
+// "Target feature taps" -- anchor and mask rows, non-causal block attention,
+// scale 1/16; "Parity validation" -- stage order).
+//
+// One 8-wave block per CU, launched cooperatively so all blocks are resident.
+// Phases are separated by a grid barrier (generation counter, bounded spin):
+//
+//   per layer: QKV  -> ATTN (q/k norm + RoPE + partials) -> MERGE
+//              -> O (+ residual, row sums of squares) -> GATE/UP -> DOWN (+ residual)
+//   then:      LM head + greedy argmax -> final reduction by block 0
+//
+// Weights never depend on activations, so every wave issues the loads of its
+// next weight slice *before* it waits at a barrier; HBM keeps streaming while
+// the grid synchronises and while activations are rebuilt in LDS.
+//
+// The L2 caches of the eight XCDs are not coherent with each other, and an
+// agent-scope fence (L2 writeback or invalidate) costs about 2 us per
+// barrier.  Instead, every value that one block writes and another block
+// reads inside the kernel moves through device-coherent accesses (agent-scope
+// relaxed atomic loads and stores, which write through and read past the
+// non-coherent caches); a wave waits for its own stores to complete before it
+// arrives at a barrier, and the barrier itself is two-level (one counter per
+// XCD, then one across XCDs) so that no single address takes 256 atomics.
+//
+// GEMV phases read bf16 activations from LDS (built once per phase; RMSNorm
+// is folded into that build from fp32 h and per-tile sums of squares) and
+// stream 16-row weight tiles through MFMA 16x16x32 bf16 exactly as the
+// skinny GEMV kernels do (same k slots for weights and activations).
+#include "common.h"
+
+namespace dfl {
+
+namespace {
+
+constexpr int NWAVE = 8;
+constexpr int NTHR = NWAVE * 64;
+constexpr int XS_PAD = 8;                 // bf16 padding of an LDS activation row
+constexpr int XS_MAX = F + XS_PAD;        // widest activation row (down projection)
+constexpr int NT_H = H / 16;              // 160 row tiles of the hidden size
+constexpr float NEG_INF = -__builtin_huge_valf();
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ldw(const uint16_t* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+
+// LDS-only rendezvous: waits for this wave's LDS operations, not for its
+// outstanding global loads (the weight prefetch stays in flight).
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// threadIdx.x as a value the compiler cannot see through: address math is
+// then recomputed inside each phase instead of being hoisted out of the layer
+// loop (which would keep hundreds of addresses alive and spill them).
+__device__ __forceinline__ int otid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// Per-layer weight pointers; the init kernel copies them into the workspace
+// so the pass kernel can index them by layer with plain global loads.
+struct LayerTab {
+  const uint16_t* wq[L];
+  const uint16_t* wk[L];
+  const uint16_t* wv[L];
+  const uint16_t* wo[L];
+  const uint16_t* wg[L];
+  const uint16_t* wu[L];
+  const uint16_t* wd[L];
+  const uint16_t* in_norm[L];
+  const uint16_t* q_norm[L];
+  const uint16_t* k_norm[L];
+  const uint16_t* post_norm[L];
+};
+
+struct PassArgs {
+  const LayerTab* tab;   // in the workspace, written by the init kernel
+  const uint16_t* final_norm;
+  const uint16_t* lm;
+  int vocab;
+  float eps, scale_log2;
+  // context ring of layer 0 (layer l adds l * layer stride)
+  const uint16_t* ring_k;
+  const uint16_t* ring_vt;
+  int cap;
+  int64_t lo, hi, p0;
+  int nb, cb, nch;
+  int B, nqt;
+  // workspace
+  float* h;          // [8][H] residual stream
+  float* ss;         // [NT_H][8] per-tile sums of squares of h rows
+  float* qkv;        // [8][QKV_N]
+  const float2* rope;  // [8][128] (cos, sin)
+  float* po;
+  float* pm;
+  float* pl;
+  uint16_t* o16;     // [8][NQ*D]
+  uint16_t* u16;     // [8][F]
+  uint64_t* keys;    // [grid][8]
+  unsigned* bar;     // barrier words (BAR_*)
+  unsigned spin_limit;
+  // outputs
+  int32_t* cand;
+  uint16_t* logits;
+  uint16_t* hidden;
+};
+
+struct Smem {
+  uint16_t x[MAXB * XS_MAX];   // activations (GEMV phases) / block keys+values (ATTN)
+  f32x4 red[NWAVE][64];        // cross-wave reduction
+  float scal[64];              // per-row scales / merge weights
+  float mw[4 * 256];           // merge: chunk weights and partial sums
+  uint64_t best[2][64];
+};
+
+// ---------------------------------------------------------------- coherence
+
+__device__ __forceinline__ uint64_t ld_coh64(const void* p) {
+  return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh64(void* p, uint64_t v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_cohf(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_cohf(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint4 ld_coh128(const void* p) {
+  const uint64_t a = ld_coh64(p), b = ld_coh64(static_cast<const char*>(p) + 8);
+  return make_uint4(static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32),
+                    static_cast<uint32_t>(b), static_cast<uint32_t>(b >> 32));
+}
+__device__ __forceinline__ void st_coh128(void* p, uint4 v) {
+  st_coh64(p, static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32));
+  st_coh64(static_cast<char*>(p) + 8, static_cast<uint64_t>(v.z) | (static_cast<uint64_t>(v.w) << 32));
+}
+__device__ __forceinline__ float4 ld_coh_f4(const float* p) {
+  const uint4 u = ld_coh128(p);
+  return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                     __uint_as_float(u.w));
+}
+__device__ __forceinline__ void st_coh_f4(float* p, f32x4 v) {
+  st_coh128(p, make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                          __float_as_uint(v[3])));
+}
+
+// ---------------------------------------------------------------- barrier
+
+// Barrier words (unsigned): generation at [0], status at [32], cross-XCD
+// counter at [64], per-XCD counters at [128 + 64 x] -- each in its own
+// 256-byte line.
+constexpr int BAR_GEN = 0, BAR_STATUS = 32, BAR_TOP = 64, BAR_XCD = 128, BAR_WORDS = 1024;
+
+__device__ __forceinline__ unsigned ald(unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void grid_sync(const PassArgs& a) {
+  lds_sync();
+  if (otid() == 0) {
+    unsigned* bar = a.bar;
+    const unsigned g = ald(bar + BAR_GEN);
+    const unsigned x = blockIdx.x & 7;  // blocks are dealt to the XCDs round robin
+    const unsigned per = (gridDim.x + 7 - x) / 8;
+    bool wait = true;
+    if (__hip_atomic_fetch_add(bar + BAR_XCD + 64 * x, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT) == per - 1) {
+      // Resets complete (wait on store completion) before the next step, so
+      // they are visible before anyone can see the new generation; no L2
+      // writeback is needed because shared data never sits dirty in L2.
+      __hip_atomic_store(bar + BAR_XCD + 64 * x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_stores();
+      const unsigned groups = gridDim.x < 8 ? gridDim.x : 8;
+      if (__hip_atomic_fetch_add(bar + BAR_TOP, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+          groups - 1) {
+        __hip_atomic_store(bar + BAR_TOP, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wait_stores();
+        __hip_atomic_store(bar + BAR_GEN, g + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wait = false;
+      }
+    }
+    if (wait) {
+      unsigned n = 0;
+      while (ald(bar + BAR_GEN) == g) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++n > a.spin_limit) {  // bounded: never hang the device
+          __hip_atomic_store(bar + BAR_STATUS, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+  }
+  lds_sync();
+}
+
+// ---------------------------------------------------------------- GEMV pieces
+
+// nw weight uint4 of one lane: k = kbeg + 32 i + 8 g, i < nw (row = wrow).
+// Every element is defined on every path (zero when !valid or i >= nw) so
+// that no stale register value stays live across phases.
+template <int NMAX>
+__device__ __forceinline__ void load_tile(uint4 (&w)[NMAX], const uint16_t* wrow, int kbeg, int g,
+                                          int nw, bool valid) {
+  if (valid) {
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i)
+      w[i] = i < nw ? ldw(wrow + kbeg + 32 * i + 8 * g) : make_uint4(0, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) w[i] = make_uint4(0, 0, 0, 0);
+  }
+}
+
+// acc over the same k slots, activations from LDS row xr (zero if !xv).
+template <int NMAX>
+__device__ __forceinline__ f32x4 mma_tile(const uint4 (&w)[NMAX], const uint16_t* xr, bool xv,
+                                          int kbeg, int g, int nw) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i) {
+    if (i < nw) {
+      const uint4 x = xv ? *reinterpret_cast<const uint4*>(xr + kbeg + 32 * i + 8 * g)
+                         : make_uint4(0, 0, 0, 0);
+      acc = mfma_bf16(w[i], x, acc);
+    }
+  }
+  return acc;
+}
+
+// Sum of red[w0 .. w0+n) for this lane (after lds_sync).
+__device__ __forceinline__ f32x4 group_sum(Smem& s, int w0, int n, int lane) {
+  f32x4 acc = s.red[w0][lane];
+  for (int w = 1; w < n; ++w) acc += s.red[w0 + w][lane];
+  return acc;
+}
+
+// x[b][k] = bf16(h[b][k] * rsqrt(mean_k h^2 + eps) * gain[k]) for b < B, into
+// LDS rows of stride H + pad.  np per-tile sums of squares are reduced in a
+// fixed order.  Every load (h and the sums) is issued in one round.
+constexpr int XN4 = MAXB * (H / 4) / NTHR;  // float4 of h per thread (10)
+
+__device__ __forceinline__ void build_x_norm(const PassArgs& a, Smem& s, int np, const uint16_t* gain) {
+  const int tid = otid(), wave = tid >> 6, lane = tid & 63;
+  const int n4 = a.B * (H / 4);
+  float4 hv[XN4];
+#pragma unroll
+  for (int u = 0; u < XN4; ++u) {
+    const int e = tid + u * NTHR;
+    hv[u] = e < n4 ? ld_coh_f4(a.h + 4 * e) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (wave < a.B) {
+    float v = 0.f;
+    float sv[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int i = lane + 64 * q;
+      sv[q] = i < np ? ld_cohf(a.ss + i * MAXB + wave) : 0.f;
+    }
+    v = sv[0] + sv[1] + sv[2];
+    v = wave_sum(v);
+    if (lane == 0) s.scal[wave] = 1.0f / sqrtf(v / static_cast<float>(H) + a.eps);
+  }
+  lds_sync();
+  constexpr int XS = H + XS_PAD;
+#pragma unroll
+  for (int u = 0; u < XN4; ++u) {
+    const int e = tid + u * NTHR;
+    if (e < n4) {
+      const int b = e / (H / 4), k = (e % (H / 4)) * 4;
+      const float sc = s.scal[b];
+      const uint2 gg = *reinterpret_cast<const uint2*>(gain + k);
+      const uint16_t y0 = f32_to_bf16(hv[u].x * sc * bf16_to_f32(gg.x & 0xffff));
+      const uint16_t y1 = f32_to_bf16(hv[u].y * sc * bf16_to_f32(gg.x >> 16));
+      const uint16_t y2 = f32_to_bf16(hv[u].z * sc * bf16_to_f32(gg.y & 0xffff));
+      const uint16_t y3 = f32_to_bf16(hv[u].w * sc * bf16_to_f32(gg.y >> 16));
+      *reinterpret_cast<uint2*>(s.x + b * XS + k) =
+          make_uint2(y0 | (static_cast<uint32_t>(y1) << 16), y2 | (static_cast<uint32_t>(y3) << 16));
+    }
+  }
+  lds_sync();
+}
+
+// Copy bf16 activations [B][K] from global into LDS rows of stride K + pad,
+// all loads in one round (K <= F: at most 15 uint4 per thread).
+__device__ __forceinline__ void copy_x(const PassArgs& a, Smem& s, const uint16_t* src, int K) {
+  const int tid = otid();
+  const int XS = K + XS_PAD;
+  const int n8 = a.B * (K / 8);
+  constexpr int U = (MAXB * F / 8 + NTHR - 1) / NTHR;
+  uint4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int e = tid + u * NTHR;
+    v[u] = e < n8 ? ld_coh128(src + 8 * e) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int e = tid + u * NTHR;
+    if (e < n8) {
+      const int b = e / (K / 8), k = (e % (K / 8)) * 8;
+      *reinterpret_cast<uint4*>(s.x + b * XS + k) = v[u];
+    }
+  }
+  lds_sync();
+}
+
+// h rows (this tile's 16 columns) += acc; per-tile sums of squares.  Runs on
+// the lanes of one wave holding the reduced tile.
+__device__ __forceinline__ void residual_epilogue(const PassArgs& a, Smem& s, f32x4 acc, int tile,
+                                                  int r, int g) {
+  float sq = 0.f;
+  if (r < a.B) {
+    float* hp = a.h + static_cast<size_t>(r) * H + tile * 16 + 4 * g;
+    const float4 hv = ld_coh_f4(hp);
+    const f32x4 hn = {hv.x + acc[0], hv.y + acc[1], hv.z + acc[2], hv.w + acc[3]};
+    st_coh_f4(hp, hn);
+    sq = hn[0] * hn[0] + hn[1] * hn[1] + hn[2] * hn[2] + hn[3] * hn[3];
+  }
+  sq = group4_sum(sq);
+  if (g == 0 && r < MAXB) st_cohf(a.ss + tile * MAXB + r, r < a.B ? sq : 0.f);
+}
+
+// ---------------------------------------------------------------- phases
+
+// Work of one block for the QKV phase: tiles 2w and 2w+1 of the 448 fused
+// q|k|v row tiles; wave v takes tile 2w + v/4 and k quarter v%4 (640 k).
+__device__ __forceinline__ const uint16_t* qkv_row(const PassArgs& a, int l, int tile, int r) {
+  const int row = tile * 16 + r;
+  if (row < NQ * D) return a.tab->wq[l] + static_cast<size_t>(row) * H;
+  if (row < NQ * D + NKV * D) return a.tab->wk[l] + static_cast<size_t>(row - NQ * D) * H;
+  return a.tab->wv[l] + static_cast<size_t>(row - NQ * D - NKV * D) * H;
+}
+
+__device__ __forceinline__ bool qkv_has(int w) { return w < QKV_N / 32; }
+
+__device__ __forceinline__ void qkv_prefetch(const PassArgs& a, int l, uint4 (&W)[20], bool go) {
+  const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
+  const bool has = qkv_has(w);
+  const int tile = has ? 2 * w + (wave >> 2) : 0;
+  load_tile<20>(W, qkv_row(a, l, tile, lane & 15), (wave & 3) * 640, lane >> 4, 20, go && has);
+}
+
+__device__ __forceinline__ void qkv_phase(const PassArgs& a, Smem& s, int l, int np, uint4 (&W)[20]) {
+  const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const bool has = qkv_has(w);
+  if (wave == 0) qkv_prefetch(a, l, W, true);
+  if (has) build_x_norm(a, s, np, a.tab->in_norm[l]);
+  if (has) {
+    const int tile = 2 * w + (wave >> 2);
+    constexpr int XS = H + XS_PAD;
+    f32x4 acc = mma_tile<20>(W, s.x + r * XS, r < a.B, (wave & 3) * 640, g, 20);
+    s.red[wave][lane] = acc;
+    lds_sync();
+    if ((wave & 3) == 0) {
+      acc = group_sum(s, wave, 4, lane);
+      if (r < a.B) st_coh_f4(a.qkv + static_cast<size_t>(r) * QKV_N + tile * 16 + 4 * g, acc);
+    }
+  }
+  wait_stores();
+}
+
+// ---------------------------------------------------------------- attention
+//
+// Block w < 2 nch takes KV head j = w / nch and chunk c = w % nch of the
+// visible context (cb blocks of 32 cells); the last chunk of each head also
+// takes the block rows' own keys.  Context K/V never depends on this pass, so
+// each thread loads its share of the chunk's first 32-cell block (16 KiB of K
+// and 16 KiB of V^T, 4 x 16 bytes per thread) *before* the barrier that
+// precedes the phase; blocks then rotate through two LDS buffers while the
+// next one is in flight.  Waves t < nqt own 16 query rows each.
+
+struct KVRegs {
+  uint4 v[4];
+};
+
+__device__ __forceinline__ bool attn_block_src(const PassArgs& a, int l, int ib_global,
+                                               const uint16_t*& kp, const uint16_t*& vp, int j) {
+  if (ib_global >= a.nb) return false;
+  const int64_t pb = a.p0 + 32 * static_cast<int64_t>(ib_global);
+  const int cidx = static_cast<int>(pb % a.cap);
+  kp = a.ring_k + ((static_cast<size_t>(l) * NKV + j) * a.cap + cidx) * D;
+  vp = a.ring_vt + (static_cast<size_t>(l) * NKV + j) * D * a.cap + static_cast<size_t>(cidx) * D;
+  return true;
+}
+
+// Thread's share of one block: K (1024 uint4) then V^T (1024 uint4).
+__device__ __forceinline__ void attn_load(const PassArgs& a, int l, int ib_global, int j,
+                                          KVRegs& R, bool go) {
+  const uint16_t *kp = nullptr, *vp = nullptr;
+  const bool ok = go && attn_block_src(a, l, ib_global, kp, vp, j);
+  const int tid = otid();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    R.v[u] = ok ? ldw(kp + 8 * (tid + u * NTHR)) : make_uint4(0, 0, 0, 0);
+    R.v[2 + u] = ok ? ldw(vp + 8 * (tid + u * NTHR)) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void attn_store(const KVRegs& R, uint16_t* kbuf, uint16_t* vbuf) {
+  const int tid = otid();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    *reinterpret_cast<uint4*>(kbuf + 8 * (tid + u * NTHR)) = R.v[u];
+    *reinterpret_cast<uint4*>(vbuf + 8 * (tid + u * NTHR)) = R.v[2 + u];
+  }
+}
+
+// Waves other than 0 load their share of the chunk's first block before the
+// barrier; wave 0 (which runs the barrier) loads its share right after it.
+__device__ __forceinline__ void attn_prefetch(const PassArgs& a, int l, KVRegs& R, bool go) {
+  const int w = blockIdx.x;
+  const bool has = w < NKV * a.nch;
+  const int j = has ? w / a.nch : 0, c = has ? w % a.nch : 0;
+  attn_load(a, l, c * a.cb, j, R, go && has && c * a.cb < a.nb);
+}
+
+// One 32-cell block from LDS (keys [32][256], values [256][32]) for this
+// wave's 16 query rows; cells at positions outside [lo, hi) are masked.
+__device__ __forceinline__ void attn_block(const uint16_t* kb, const uint16_t* vb, int64_t pb,
+                                           int64_t lo, int64_t hi, float scale_log2,
+                                           const uint4 (&qf)[8], f32x4 (&o)[16], float& m,
+                                           float& lsum, int n, int g) {
+  const uint16_t* k0 = kb + n * D + 8 * g;
+  const uint16_t* k1 = k0 + 16 * D;
+  const uint16_t* vbase = vb + n * 32 + 4 * g;
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int si = 0; si < 8; ++si) {
+    s0 = mfma_f16(*reinterpret_cast<const uint4*>(k0 + 32 * si), qf[si], s0);
+    s1 = mfma_f16(*reinterpret_cast<const uint4*>(k1 + 32 * si), qf[si], s1);
+  }
+  const bool full = pb >= lo && pb + 32 <= hi;
+  float x[8];
+  bool ok[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t q0 = pb + 4 * g + i, q1 = q0 + 16;
+    ok[i] = full || (q0 >= lo && q0 < hi);
+    ok[4 + i] = full || (q1 >= lo && q1 < hi);
+    x[i] = ok[i] ? s0[i] * scale_log2 : NEG_INF;
+    x[4 + i] = ok[4 + i] ? s1[i] * scale_log2 : NEG_INF;
+  }
+  float bm = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) bm = fmaxf(bm, x[i]);
+  bm = group4_max(bm);
+  const float mnew = fmaxf(m, bm);
+  const float muse = mnew == NEG_INF ? 0.f : mnew;
+  const float alpha = exp2f(m - muse);
+  float pr[8], ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    pr[i] = exp2f(x[i] - muse);
+    ps += pr[i];
+  }
+  lsum = lsum * alpha + ps;
+  m = mnew;
+  uint32_t pp[4], vm[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pp[i] = static_cast<uint32_t>(f32_to_f16_bits(pr[2 * i])) |
+            (static_cast<uint32_t>(f32_to_f16_bits(pr[2 * i + 1])) << 16);
+    vm[i] = (ok[2 * i] ? 0x0000ffffu : 0u) | (ok[2 * i + 1] ? 0xffff0000u : 0u);
+  }
+  const uint4 pf = make_uint4(pp[0], pp[1], pp[2], pp[3]);
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) {
+    o[dt] *= alpha;
+    const uint2 x0 = *reinterpret_cast<const uint2*>(vbase + 16 * dt * 32);
+    const uint2 x1 = *reinterpret_cast<const uint2*>(vbase + 16 * dt * 32 + 16);
+    const uint4 v = make_uint4(x0.x & vm[0], x0.y & vm[1], x1.x & vm[2], x1.y & vm[3]);
+    o[dt] = mfma_f16(v, pf, o[dt]);
+  }
+}
+
+// Query operand of this wave: qrow r = 16 t + n -> (row r / 12, head 12 j +
+// r % 12); RMSNorm over the head (the lane holds 64 of its 256 values), then
+// NeoX RoPE: dims 32 s + 8 g + e and 32 (s + 4) + 8 g + e form a pair.
+__device__ __forceinline__ void attn_query(const PassArgs& a, int l, int j, int t, int n, int g,
+                                           uint4 (&qf)[8]) {
+  const int r = t * 16 + n;
+  const bool qv = r < G * a.B;
+  const int bi = qv ? r / G : 0, hl = qv ? r % G : 0;
+  const float* qraw = a.qkv + static_cast<size_t>(bi) * QKV_N + (j * G + hl) * D;
+  float qv8[8][8];
+#pragma unroll
+  for (int si = 0; si < 8; ++si) {
+    const float4 u0 = ld_coh_f4(qraw + 32 * si + 8 * g);
+    const float4 u1 = ld_coh_f4(qraw + 32 * si + 8 * g + 4);
+    qv8[si][0] = u0.x; qv8[si][1] = u0.y; qv8[si][2] = u0.z; qv8[si][3] = u0.w;
+    qv8[si][4] = u1.x; qv8[si][5] = u1.y; qv8[si][6] = u1.z; qv8[si][7] = u1.w;
+  }
+  float sq = 0.f;
+#pragma unroll
+  for (int si = 0; si < 8; ++si)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sq += qv8[si][e] * qv8[si][e];
+  sq = group4_sum(sq);
+  const float sc = 1.0f / sqrtf(sq / static_cast<float>(D) + a.eps);
+  const uint16_t* gq = a.tab->q_norm[l];
+  uint32_t pk[8][4];
+#pragma unroll
+  for (int si = 0; si < 4; ++si) {
+    const uint4 ga = *reinterpret_cast<const uint4*>(gq + 32 * si + 8 * g);
+    const uint4 gb = *reinterpret_cast<const uint4*>(gq + 32 * (si + 4) + 8 * g);
+    const uint32_t gav[4] = {ga.x, ga.y, ga.z, ga.w}, gbv[4] = {gb.x, gb.y, gb.z, gb.w};
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      float lo2[2], hi2[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int ee = e + h2;
+        const float ga_f = bf16_to_f32((gav[ee >> 1] >> (16 * (ee & 1))) & 0xffff);
+        const float gb_f = bf16_to_f32((gbv[ee >> 1] >> (16 * (ee & 1))) & 0xffff);
+        const float x0 = qv8[si][ee] * sc * ga_f, x1 = qv8[si + 4][ee] * sc * gb_f;
+        const float2 cs = a.rope[bi * (D / 2) + 32 * si + 8 * g + ee];
+        lo2[h2] = x0 * cs.x - x1 * cs.y;
+        hi2[h2] = x1 * cs.x + x0 * cs.y;
+      }
+      pk[si][e >> 1] = static_cast<uint32_t>(f32_to_f16_bits(lo2[0])) |
+                       (static_cast<uint32_t>(f32_to_f16_bits(lo2[1])) << 16);
+      pk[si + 4][e >> 1] = static_cast<uint32_t>(f32_to_f16_bits(hi2[0])) |
+                           (static_cast<uint32_t>(f32_to_f16_bits(hi2[1])) << 16);
+    }
+  }
+#pragma unroll
+  for (int si = 0; si < 8; ++si)
+    qf[si] = qv ? make_uint4(pk[si][0], pk[si][1], pk[si][2], pk[si][3]) : make_uint4(0, 0, 0, 0);
+}
+
+// Block rows' keys and values of KV head j into LDS (keys [32][256] with rows
+// b < B, values [256][32]); wave b = row b.
+__device__ __forceinline__ void attn_block_rows(const PassArgs& a, int l, int j, uint16_t* kl,
+                                                uint16_t* vl) {
+  const int wave = otid() >> 6, lane = otid() & 63;
+  if (wave >= a.B) return;
+  const int b = wave;
+  const float* kr = a.qkv + static_cast<size_t>(b) * QKV_N + NQ * D + j * D;
+  const float* vr = a.qkv + static_cast<size_t>(b) * QKV_N + NQ * D + NKV * D + j * D;
+  float k0 = ld_cohf(kr + lane), k1 = ld_cohf(kr + lane + 64);
+  float k2 = ld_cohf(kr + lane + 128), k3 = ld_cohf(kr + lane + 192);
+  float vv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) vv[q] = ld_cohf(vr + lane + 64 * q);
+  const float sq = wave_sum(k0 * k0 + k1 * k1 + k2 * k2 + k3 * k3);
+  const float sc = 1.0f / sqrtf(sq / static_cast<float>(D) + a.eps);
+  const uint16_t* gn = a.tab->k_norm[l];
+  k0 *= sc * bf16_to_f32(gn[lane]);
+  k1 *= sc * bf16_to_f32(gn[lane + 64]);
+  k2 *= sc * bf16_to_f32(gn[lane + 128]);
+  k3 *= sc * bf16_to_f32(gn[lane + 192]);
+  const float2 c0 = a.rope[b * (D / 2) + lane], c1 = a.rope[b * (D / 2) + lane + 64];
+  uint16_t* kd = kl + b * D;
+  kd[lane] = f32_to_f16_bits(k0 * c0.x - k2 * c0.y);
+  kd[lane + 64] = f32_to_f16_bits(k1 * c1.x - k3 * c1.y);
+  kd[lane + 128] = f32_to_f16_bits(k2 * c0.x + k0 * c0.y);
+  kd[lane + 192] = f32_to_f16_bits(k3 * c1.x + k1 * c1.y);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) vl[(lane + 64 * q) * BLK_CELLS + b] = f32_to_f16_bits(vv[q]);
+}
+
+__device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KVRegs& R) {
+  const int w = blockIdx.x;
+  if (w < NKV * a.nch) {
+    const int j = w / a.nch, c = w % a.nch;
+    const int wave = otid() >> 6, lane = otid() & 63;
+    const int n = lane & 15, g = lane >> 4;
+    const int blk0 = c * a.cb;
+    const int nblk = a.nb > blk0 ? min(a.cb, a.nb - blk0) : 0;
+    const bool rows = c == a.nch - 1;  // this chunk also takes the block rows
+    // LDS: block buffers (keys then values) at 0 and 2 x 8192, block rows at 4 x 8192
+    uint16_t* kl = s.x + 4 * BLK_CELLS * D;
+    uint16_t* vl = s.x + 5 * BLK_CELLS * D;
+    if (wave == 0) attn_load(a, l, blk0, j, R, nblk > 0);
+    uint4 qf[8];
+    if (wave < a.nqt) attn_query(a, l, j, wave, n, g, qf);
+    if (rows) attn_block_rows(a, l, j, kl, vl);
+    float m = NEG_INF, lsum = 0.f;
+    f32x4 o[16];
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ib = 0; ib < nblk; ++ib) {
+      uint16_t* kbuf = s.x + (ib & 1) * (2 * BLK_CELLS * D);
+      uint16_t* vbuf = kbuf + BLK_CELLS * D;
+      attn_store(R, kbuf, vbuf);
+      attn_load(a, l, blk0 + ib + 1, j, R, ib + 1 < nblk);
+      lds_sync();
+      if (wave < a.nqt)
+        attn_block(kbuf, vbuf, a.p0 + 32 * static_cast<int64_t>(blk0 + ib), a.lo, a.hi,
+                   a.scale_log2, qf, o, m, lsum, n, g);
+    }
+    if (rows) {
+      lds_sync();
+      if (wave < a.nqt) attn_block(kl, vl, 0, 0, a.B, a.scale_log2, qf, o, m, lsum, n, g);
+    }
+    if (wave < a.nqt) {
+      lsum = group4_sum(lsum);
+      const size_t base = (static_cast<size_t>(j) * a.nch + c) * a.nqt + wave;
+      if (g == 0) {
+        st_cohf(a.pm + base * 16 + n, m);
+        st_cohf(a.pl + base * 16 + n, lsum);
+      }
+      float* op = a.po + (base * 16 + n) * D + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) st_coh_f4(op + 16 * dt, o[dt]);
+    }
+  }
+  wait_stores();
+}
+
+// Merge of the chunks of one (KV head, query tile, query row): wave 0 turns
+// the chunks' maxima and sums into weights while every thread already has its
+// partial outputs in flight; 512 threads = 4 quarters of the chunks x 128
+// pairs of head dims.
+constexpr int MQ = 32;  // chunks per quarter (nch <= 128)
+
+__device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s) {
+  const int ngroup = NKV * a.nqt * 16;
+  const int w = blockIdx.x;
+  if (w < ngroup) {
+    const int n = w & 15, t = (w >> 4) % a.nqt, j = (w >> 4) / a.nqt;
+    const int r = t * 16 + n;
+    if (r < G * a.B) {
+      const int tid = otid(), wave = tid >> 6, lane = tid & 63;
+      const int nc = a.nch;
+      const size_t cstride = static_cast<size_t>(a.nqt) * 16;
+      const size_t row0 = (static_cast<size_t>(j) * nc * a.nqt + t) * 16 + n;
+      const int d2 = 2 * (tid & 127), quarter = tid >> 7;
+      uint64_t ov[MQ];
+#pragma unroll
+      for (int u = 0; u < MQ; ++u) {
+        const int cc = quarter + 4 * u;
+        ov[u] = cc < nc ? ld_coh64(a.po + (row0 + cc * cstride) * D + d2) : 0ull;
+      }
+      if (wave == 0) {
+        float mv[2], lv[2];
+        float M = NEG_INF;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int cc = lane + 64 * q;
+          mv[q] = cc < nc ? ld_cohf(a.pm + row0 + cc * cstride) : NEG_INF;
+          lv[q] = cc < nc ? ld_cohf(a.pl + row0 + cc * cstride) : 0.f;
+          M = fmaxf(M, mv[q]);
+        }
+#pragma unroll
+        for (int o2 = 32; o2 > 0; o2 >>= 1) M = fmaxf(M, __shfl_xor(M, o2, 64));
+        float Ls = 0.f;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int cc = lane + 64 * q;
+          const float wt = cc < nc ? exp2f(mv[q] - M) : 0.f;
+          s.mw[cc] = wt;
+          Ls += lv[q] * wt;
+        }
+        Ls = wave_sum(Ls);
+        if (lane == 0) s.scal[0] = 1.0f / Ls;
+      }
+      lds_sync();
+      float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+      for (int u = 0; u < MQ; ++u) {
+        const int cc = quarter + 4 * u;
+        if (cc < nc) {
+          const float wt = s.mw[cc];
+          acc0 += __uint_as_float(static_cast<uint32_t>(ov[u])) * wt;
+          acc1 += __uint_as_float(static_cast<uint32_t>(ov[u] >> 32)) * wt;
+        }
+      }
+      if (quarter > 0) {
+        s.mw[256 + (quarter - 1) * 256 + d2] = acc0;
+        s.mw[256 + (quarter - 1) * 256 + d2 + 1] = acc1;
+      }
+      lds_sync();
+      if (quarter == 0) {
+#pragma unroll
+        for (int q2 = 0; q2 < 3; ++q2) {
+          acc0 += s.mw[256 + q2 * 256 + d2];
+          acc1 += s.mw[256 + q2 * 256 + d2 + 1];
+        }
+        const int bi = r / G, hl = r % G;
+        const uint32_t pk = static_cast<uint32_t>(f32_to_bf16(acc0 * s.scal[0])) |
+                            (static_cast<uint32_t>(f32_to_bf16(acc1 * s.scal[0])) << 16);
+        st_coh32(reinterpret_cast<uint32_t*>(a.o16 + static_cast<size_t>(bi) * NQ * D +
+                                             (j * G + hl) * D + d2),
+                 pk);
+      }
+    }
+  }
+  wait_stores();
+}
+
+// O projection: block w < 160 owns row tile w; wave v takes k in
+// [768 v, 768 v + 768) (6 k blocks).
+__device__ __forceinline__ void o_prefetch(const PassArgs& a, int l, uint4 (&W)[24], bool go) {
+  const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
+  const bool has = w < NT_H;
+  load_tile<24>(W, a.tab->wo[l] + static_cast<size_t>((has ? w : 0) * 16 + (lane & 15)) * (NQ * D),
+                wave * 768, lane >> 4, 24, go && has);
+}
+
+__device__ __forceinline__ void o_phase(const PassArgs& a, Smem& s, int l, uint4 (&W)[24]) {
+  const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
+  const int r = lane & 15, g = lane >> 4;
+  if (w < NT_H) {
+    if (wave == 0) o_prefetch(a, l, W, true);
+    copy_x(a, s, a.o16, NQ * D);
+    constexpr int XS = NQ * D + XS_PAD;
+    f32x4 acc = mma_tile<24>(W, s.x + r * XS, r < a.B, wave * 768, g, 24);
+    s.red[wave][lane] = acc;
+    lds_sync();
+    if (wave == 0) residual_epilogue(a, s, group_sum(s, 0, NWAVE, lane), w, r, g);
+  }
+  wait_stores();
+}
+
+// Gate/up: 480 tile pairs; round q handles pair w + q * grid.  Waves 0-3 the
+// gate tile's k quarters, waves 4-7 the up tile's.
+__device__ __forceinline__ void gu_prefetch(const PassArgs& a, int l, int pair, uint4 (&W)[20],
+                                            bool go) {
+  const int wave = otid() >> 6, lane = otid() & 63;
+  const bool has = pair < F / 16;
+  const uint16_t* m = wave < 4 ? a.tab->wg[l] : a.tab->wu[l];
+  load_tile<20>(W, m + static_cast<size_t>((has ? pair : 0) * 16 + (lane & 15)) * H,
+                (wave & 3) * 640, lane >> 4, 20, go && has);
+}
+
+__device__ __forceinline__ void gu_phase(const PassArgs& a, Smem& s, int l, int np, uint4 (&W)[20]) {
+  const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const bool has = w < F / 16;
+  if (wave == 0) gu_prefetch(a, l, w, W, true);
+  if (has) build_x_norm(a, s, np, a.tab->post_norm[l]);
+  constexpr int XS = H + XS_PAD;
+  for (int pair = w; pair < F / 16; pair += gridDim.x) {
+    f32x4 acc = mma_tile<20>(W, s.x + r * XS, r < a.B, (wave & 3) * 640, g, 20);
+    s.red[wave][lane] = acc;
+    lds_sync();
+    const int nxt = pair + gridDim.x;
+    if (nxt < F / 16) gu_prefetch(a, l, nxt, W, true);  // next round's tiles
+    if (wave == 0) {
+      const f32x4 ag = group_sum(s, 0, 4, lane);
+      const f32x4 au = group_sum(s, 4, 4, lane);
+      if (r < a.B) {
+        uint16_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float z = ag[i];
+          o[i] = f32_to_bf16(z / (1.0f + __expf(-z)) * au[i]);
+        }
+        st_coh64(a.u16 + static_cast<size_t>(r) * F + pair * 16 + 4 * g,
+                 static_cast<uint64_t>(o[0] | (static_cast<uint32_t>(o[1]) << 16)) |
+                     (static_cast<uint64_t>(o[2] | (static_cast<uint32_t>(o[3]) << 16)) << 32));
+      }
+    }
+    lds_sync();  // red[] reuse
+  }
+  wait_stores();
+}
+
+// Down projection: block w < 160 owns row tile w; waves 0-3 take 8 k blocks
+// each (k < 4096), waves 4-7 take 7 (k >= 4096).
+__device__ __forceinline__ void down_range(int wave, int& kbeg, int& nw) {
+  if (wave < 4) {
+    kbeg = wave * 1024;
+    nw = 32;
+  } else {
+    kbeg = 4096 + (wave - 4) * 896;
+    nw = 28;
+  }
+}
+
+__device__ __forceinline__ void down_prefetch(const PassArgs& a, int l, uint4 (&W)[32], bool go) {
+  const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
+  const bool has = w < NT_H;
+  int kbeg, nw;
+  down_range(wave, kbeg, nw);
+  load_tile<32>(W, a.tab->wd[l] + static_cast<size_t>((has ? w : 0) * 16 + (lane & 15)) * F, kbeg,
+                lane >> 4, nw, go && has);
+}
+
+__device__ __forceinline__ void down_phase(const PassArgs& a, Smem& s, int l, uint4 (&W)[32]) {
+  const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
+  const int r = lane & 15, g = lane >> 4;
+  if (w < NT_H) {
+    if (wave == 0) down_prefetch(a, l, W, true);
+    copy_x(a, s, a.u16, F);
+    int kbeg, nw;
+    down_range(wave, kbeg, nw);
+    constexpr int XS = F + XS_PAD;
+    f32x4 acc = mma_tile<32>(W, s.x + r * XS, r < a.B, kbeg, g, nw);
+    s.red[wave][lane] = acc;
+    lds_sync();
+    if (wave == 0) residual_epilogue(a, s, group_sum(s, 0, NWAVE, lane), w, r, g);
+  }
+  wait_stores();
+}
+
+// LM head: tile pairs p = w, w + grid, ...; wave v takes tile 2p + v/4 and k
+// quarter v%4.  Activations: final-normed rows 1..B-1 (row b in LDS row b).
+__device__ __forceinline__ void lm_prefetch(const PassArgs& a, int pair, uint4 (&W)[20], bool go) {
+  const int wave = otid() >> 6, lane = otid() & 63;
+  const int tile = 2 * pair + (wave >> 2);
+  const bool has = tile < a.vocab / 16;
+  load_tile<20>(W, a.lm + static_cast<size_t>((has ? tile : 0) * 16 + (lane & 15)) * H,
+                (wave & 3) * 640, lane >> 4, 20, go && has);
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t x, uint64_t y) { return x > y ? x : y; }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+  lo = __shfl_xor(lo, m, 64);
+  hi = __shfl_xor(hi, m, 64);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, uint4 (&W)[20]) {
+  const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int ntiles = a.vocab / 16, npairs = (ntiles + 1) / 2;
+  if (wave == 0) lm_prefetch(a, w, W, true);
+  build_x_norm(a, s, np, a.final_norm);
+  constexpr int XS = H + XS_PAD;
+  if (w == 0 && a.hidden) {
+    for (int e = otid(); e < a.B * H; e += NTHR)
+      a.hidden[e] = s.x[(e / H) * XS + (e % H)];
+  }
+  // mask row r + 1 of the block feeds MFMA column r
+  const bool xv = r + 1 < a.B;
+  const uint16_t* xr = s.x + (r + 1) * XS;
+  uint64_t best = 0;
+  uint4 W2[20];
+  int p = w;
+  while (p < npairs) {
+    // round with W, prefetch into W2
+    const int pn = p + gridDim.x;
+    lm_prefetch(a, pn, W2, pn < npairs);
+    const int tile = 2 * p + (wave >> 2);
+    f32x4 acc = tile < ntiles ? mma_tile<20>(W, xr, xv, (wave & 3) * 640, g, 20)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+    s.red[wave][lane] = acc;
+    lds_sync();
+    if ((wave & 3) == 0 && tile < ntiles) {
+      acc = group_sum(s, wave, 4, lane);
+      if (xv) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          best = umax64(best, argmax_key(acc[i], static_cast<uint32_t>(tile * 16 + 4 * g + i)));
+        if (a.logits) {
+          uint16_t o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16(acc[i]);
+          *reinterpret_cast<uint2*>(a.logits + static_cast<size_t>(r) * a.vocab + tile * 16 + 4 * g) =
+              make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
+                         o[2] | (static_cast<uint32_t>(o[3]) << 16));
+        }
+      }
+    }
+    lds_sync();
+    p = pn;
+    if (p >= npairs) break;
+    // round with W2, prefetch into W
+    const int pn2 = p + gridDim.x;
+    lm_prefetch(a, pn2, W, pn2 < npairs);
+    const int tile2 = 2 * p + (wave >> 2);
+    acc = tile2 < ntiles ? mma_tile<20>(W2, xr, xv, (wave & 3) * 640, g, 20)
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+    s.red[wave][lane] = acc;
+    lds_sync();
+    if ((wave & 3) == 0 && tile2 < ntiles) {
+      acc = group_sum(s, wave, 4, lane);
+      if (xv) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          best = umax64(best, argmax_key(acc[i], static_cast<uint32_t>(tile2 * 16 + 4 * g + i)));
+        if (a.logits) {
+          uint16_t o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16(acc[i]);
+          *reinterpret_cast<uint2*>(a.logits + static_cast<size_t>(r) * a.vocab + tile2 * 16 + 4 * g) =
+              make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
+                         o[2] | (static_cast<uint32_t>(o[3]) << 16));
+        }
+      }
+    }
+    lds_sync();
+    p = pn2;
+  }
+  // per-block best of mask row r + 1: waves 0 and 4 hold candidates
+  if ((wave & 3) == 0) {
+    best = umax64(best, shfl_xor_u64(best, 16));
+    best = umax64(best, shfl_xor_u64(best, 32));
+    if (g == 0) s.best[wave >> 2][r] = best;
+  }
+  lds_sync();
+  if (otid() < MAXB)
+    st_coh64(a.keys + static_cast<size_t>(w) * MAXB + otid(),
+             umax64(s.best[0][otid()], s.best[1][otid()]));
+  wait_stores();
+}
+
+__device__ __forceinline__ void argmax_final(const PassArgs& a) {
+  if (blockIdx.x != 0) return;
+  const int wave = otid() >> 6, lane = otid() & 63;
+  if (wave + 1 >= a.B) return;  // wave b reduces mask row b + 1
+  uint64_t best = 0;
+  for (int i = lane; i < static_cast<int>(gridDim.x); i += 64)
+    best = umax64(best, ld_coh64(a.keys + static_cast<size_t>(i) * MAXB + wave));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) best = umax64(best, shfl_xor_u64(best, o));
+  if (lane == 0) a.cand[wave] = static_cast<int32_t>(~static_cast<uint32_t>(best));
+}
+
+__global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
+  __shared__ Smem s;
+  const bool pre = (otid() >> 6) != 0;  // waves other than 0 prefetch before barriers
+  uint4 Wq[20];
+  // Layer 0 QKV weights stream while the grid lines up.
+  qkv_prefetch(a, 0, Wq, pre);
+  grid_sync(a);  // h, ss, the RoPE table and the layer table come from the init kernel
+  int np = 1;    // sums of squares of h: one entry per row from the init kernel
+  for (int l = 0; l < L; ++l) {
+    qkv_phase(a, s, l, np, Wq);
+    KVRegs R;
+    attn_prefetch(a, l, R, pre);
+    grid_sync(a);
+    attn_phase(a, s, l, R);
+    grid_sync(a);
+    merge_phase(a, s);
+    uint4 Wo[24];
+    o_prefetch(a, l, Wo, pre);
+    grid_sync(a);
+    o_phase(a, s, l, Wo);
+    uint4 Wg[20];
+    gu_prefetch(a, l, blockIdx.x, Wg, pre);
+    grid_sync(a);
+    gu_phase(a, s, l, NT_H, Wg);
+    uint4 Wd[32];
+    down_prefetch(a, l, Wd, pre);
+    grid_sync(a);
+    down_phase(a, s, l, Wd);
+    if (l + 1 < L) qkv_prefetch(a, l + 1, Wq, pre);
+    else lm_prefetch(a, blockIdx.x, Wq, pre && a.B > 1);
+    grid_sync(a);
+    np = NT_H;
+  }
+  if (a.B > 1) {
+    lm_phase(a, s, np, Wq);
+    grid_sync(a);
+    argmax_final(a);
+  } else if (blockIdx.x == 0 && a.hidden) {
+    build_x_norm(a, s, np, a.final_norm);
+    for (int e = otid(); e < H; e += NTHR) a.hidden[e] = s.x[e];
+  }
+}
+
+// h[b] = E[token_b], per-row sum of squares, RoPE table of p .. p+B-1, and the
+// barrier words of the pass kernel.  grid B, block 256.
+__global__ __launch_bounds__(256) void k_pass_init(LayerTab tab, LayerTab* tab_out,
+                                                   const uint16_t* embed, int anchor, int mask,
+                                                   int64_t p, double theta, float* h, float* ss,
+                                                   float2* rope, unsigned* bar) {
+  __shared__ float red[4];
+  const int b = blockIdx.x;
+  if (b == 0)
+    for (int i = threadIdx.x; i < BAR_WORDS; i += 256) bar[i] = 0u;
+  if (b == 0 && threadIdx.x == 0) *tab_out = tab;
+  const int tok = b == 0 ? anchor : mask;
+  const uint16_t* row = embed + static_cast<size_t>(tok) * H;
+  float sq = 0.f;
+  for (int e = threadIdx.x; e < H; e += 256) {
+    const float v = bf16_to_f32(row[e]);
+    h[static_cast<size_t>(b) * H + e] = v;
+    sq += v * v;
+  }
+  sq = block_sum<256>(sq, red);
+  if (threadIdx.x == 0) ss[b] = sq;
+  if (threadIdx.x < D / 2) {
+    const double inv = pow(theta, -2.0 * static_cast<double>(threadIdx.x) / static_cast<double>(D));
+    double sn, cs;
+    sincos(static_cast<double>(p + b) * inv, &sn, &cs);
+    rope[b * (D / 2) + threadIdx.x] = make_float2(static_cast<float>(cs), static_cast<float>(sn));
+  }
+}
+
+}  // namespace
+
+size_t pass_smem_bytes() { return sizeof(Smem); }
+size_t pass_tab_bytes() { return sizeof(LayerTab); }
+size_t pass_bar_bytes() { return sizeof(unsigned) * BAR_WORDS; }
+
+hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
+  LayerTab tab;
+  for (int l = 0; l < L; ++l) {
+    tab.wq[l] = q.wq[l];
+    tab.wk[l] = q.wk[l];
+    tab.wv[l] = q.wv[l];
+    tab.wo[l] = q.wo[l];
+    tab.wg[l] = q.wg[l];
+    tab.wu[l] = q.wu[l];
+    tab.wd[l] = q.wd[l];
+    tab.in_norm[l] = q.in_norm[l];
+    tab.q_norm[l] = q.q_norm[l];
+    tab.k_norm[l] = q.k_norm[l];
+    tab.post_norm[l] = q.post_norm[l];
+  }
+  PassArgs a;
+  a.tab = reinterpret_cast<const LayerTab*>(q.tab);
+  a.final_norm = q.final_norm;
+  a.lm = q.lm;
+  a.vocab = q.vocab;
+  a.eps = q.eps;
+  a.scale_log2 = q.scale_log2;
+  a.ring_k = q.ring_k;
+  a.ring_vt = q.ring_vt;
+  a.cap = q.cap;
+  a.lo = q.lo;
+  a.hi = q.hi;
+  a.p0 = q.p0;
+  a.nb = q.nb;
+  a.cb = q.cb;
+  a.nch = q.nch;
+  a.B = q.B;
+  a.nqt = (G * q.B + 15) / 16;
+  a.h = q.h;
+  a.ss = q.ss;
+  a.qkv = q.qkv;
+  a.rope = q.rope;
+  a.po = q.po;
+  a.pm = q.pm;
+  a.pl = q.pl;
+  a.o16 = q.o16;
+  a.u16 = q.u16;
+  a.keys = q.keys;
+  a.bar = q.bar;
+  a.spin_limit = q.spin_limit;
+  a.cand = q.cand;
+  a.logits = q.logits;
+  a.hidden = q.hidden;
+  // every phase assumes at least one block per work item of its first round
+  if (q.nch < 1 || q.nch > 128 || q.grid < NKV * q.nch || q.grid < QKV_N / 32 ||
+      q.grid < NKV * a.nqt * 16 || q.grid > 1024)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_pass_init, dim3(q.B), dim3(256), 0, st, tab,
+                     reinterpret_cast<LayerTab*>(q.tab), q.embed, q.anchor, q.mask, q.p, q.theta,
+                     q.h, q.ss, q.rope, q.bar);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  void* args[] = {&a};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_draft_pass), dim3(q.grid),
+                                    dim3(NTHR), args, 0, st);
+}
+
+hipError_t draft_pass_max_grid(int device, int* grid) {
+  int cus = 0, per = 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void*>(k_draft_pass),
+                                                   NTHR, 0);
+  if (e != hipSuccess) return e;
+  *grid = cus * (per > 0 ? 1 : 0);
+  return hipSuccess;
+}
+
+}  // namespace dfl

@@ -61,17 +61,27 @@ class DeviceWeights:
 
 
 class KVRing:
-    """fp16 K [5][2][cap][256] and transposed V [5][2][256][cap]."""
+    """fp16 K [5][2][cap][256] and block-transposed V [5][2][cap/32][256][32]."""
 
     def __init__(self, capacity: int, window: int | None = None, device="cuda"):
         window = min(synth.WINDOW, capacity) if window is None else window
         self.k = torch.zeros((synth.N_LAYERS, synth.N_KV_HEADS, capacity, synth.HEAD_DIM),
                              dtype=torch.float16, device=device)
-        self.vt = torch.zeros((synth.N_LAYERS, synth.N_KV_HEADS, synth.HEAD_DIM, capacity),
-                              dtype=torch.float16, device=device)
+        self.vt = torch.zeros((synth.N_LAYERS, synth.N_KV_HEADS, capacity // 32,
+                               synth.HEAD_DIM, 32), dtype=torch.float16, device=device)
         self.desc = dflash_kv(self.k.data_ptr(), self.vt.data_ptr(), capacity, window)
         self.capacity = capacity
         self.window = window
+
+    def values(self) -> torch.Tensor:
+        """V as [5][2][cap][256] (a transposed copy of the ring's values)."""
+        L, J, nb, D, c = self.vt.shape
+        return self.vt.permute(0, 1, 2, 4, 3).reshape(L, J, nb * c, D)
+
+    def set_values(self, v: torch.Tensor):
+        """Fill the ring's values from V [5][2][cap][256]."""
+        L, J, nb, D, c = self.vt.shape
+        self.vt.copy_(v.reshape(L, J, nb, c, D).permute(0, 1, 2, 4, 3))
 
 
 class Drafter:

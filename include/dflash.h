@@ -109,8 +109,9 @@ typedef struct {
  * layer).  Position m lives in cell m % capacity ("Speculative decode
  * integration": position-addressed cells, overwritten on a later commit).
  *   k : fp16 [5 layers][2 kv heads][capacity cells][256]
- *   vt: fp16 [5 layers][2 kv heads][256][capacity cells]   (values transposed:
- *       cell index fastest, so one dimension of consecutive cells is contiguous)
+ *   vt: fp16 [5 layers][2 kv heads][capacity/32][256][32]  (values transposed in
+ *       blocks of 32 cells: cell c, dimension d is at [c/32][d][c%32], so each
+ *       32-cell block of values is one contiguous 16 KiB run)
  * capacity must be a multiple of 256 and >= window.  A draft at anchor
  * position p reads positions max(0, p-window) .. p-1, which must have been
  * projected (and not overwritten since) by the caller. */

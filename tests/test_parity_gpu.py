@@ -141,7 +141,7 @@ def test_fuse_context_full_size_sampled(dev_w, ow):
 def ring_cells(kv: KVRing, positions):
     cells = np.asarray(positions) % kv.capacity
     K = dec_f16(kv.k)[:, :, cells, :]
-    V = dec_f16(kv.vt)[:, :, :, cells].transpose(0, 1, 3, 2)
+    V = dec_f16(kv.values())[:, :, cells, :]
     return K, V
 
 
@@ -240,9 +240,10 @@ def test_draft_long_resident_context(dev_w, ow):
     kv = KVRing(32768)
     Kh = synth.make_rows(5 * 2 * n, 256, seed=91, dtype="f16").reshape(5, 2, n, 256)
     Vh = synth.make_rows(5 * 2 * n, 256, seed=92, dtype="f16").reshape(5, 2, n, 256)
-    cells = (np.arange(lo, p) % 32768)
-    kv.k[:, :, cells, :] = to_device(Kh).view(torch.float16)
-    kv.vt[:, :, :, cells] = to_device(Vh).view(torch.float16).transpose(2, 3)
+    cells = np.arange(lo, p) % 32768
+    assert np.array_equal(cells, np.arange(n))  # 229376 = 7 * 32768: cells in order
+    kv.k.copy_(to_device(Kh).view(torch.float16))
+    kv.set_values(to_device(Vh).view(torch.float16))
     dr = Drafter(dev_w, kv, max_rows=16)
     anchor = synth.anchor_token(p)
     res = gpu_draft(dr, p, anchor, 8, dev_w.vocab)
