@@ -35,7 +35,8 @@ constexpr int DOWN_SPLITS = 3;        // k splits of the down GEMV (K = 7680)
 constexpr size_t PART_FLOATS = static_cast<size_t>(FC_SPLITS) * GEMV_ROWS * H;
 
 struct Layout {
-  size_t h, xn, part, q16, kblk, vblkT, po, pm, pl, o16, u16, keys, rope, ss, qkv, bar, tab, y;
+  size_t h, xn, part, q16, kblk, vblkT, po, pm, pl, o16, u16, keys, rope, ss, qkv, hv, ov, uv, bar,
+      tab, y;
   size_t fixed;  // bytes before y
 };
 
@@ -62,8 +63,13 @@ Layout layout() {
   L.u16 = take(off, 2 * MAXB * F);
   L.keys = take(off, sizeof(uint64_t) * KEYS_MAX * MAXB);
   L.rope = take(off, sizeof(float) * 2 * MAXB * (D / 2));
-  L.ss = take(off, sizeof(float) * (H / 16) * MAXB);
-  L.qkv = take(off, sizeof(float) * MAXB * QKV_N);
+  // per-layer / per-version copies used by the persistent pass
+  constexpr size_t HV = 2 * dfl::L + 1, NL = dfl::L;
+  L.ss = take(off, sizeof(float) * HV * (H / 16) * MAXB);
+  L.qkv = take(off, sizeof(float) * NL * MAXB * QKV_N);
+  L.hv = take(off, sizeof(float) * HV * MAXB * H);
+  L.ov = take(off, 2 * NL * MAXB * NQ * D);
+  L.uv = take(off, 2 * NL * MAXB * F);
   L.bar = take(off, pass_bar_bytes());
   L.tab = take(off, pass_tab_bytes());
   L.fixed = off;
@@ -308,15 +314,15 @@ extern "C" int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* 
   q.p = p;
   q.anchor = anchor_id;
   q.mask = mask_id;
-  q.h = at<float>(ws, Lw.h);
+  q.h = at<float>(ws, Lw.hv);
   q.ss = at<float>(ws, Lw.ss);
   q.qkv = at<float>(ws, Lw.qkv);
   q.rope = at<float2>(ws, Lw.rope);
   q.po = at<float>(ws, Lw.po);
   q.pm = at<float>(ws, Lw.pm);
   q.pl = at<float>(ws, Lw.pl);
-  q.o16 = at<uint16_t>(ws, Lw.o16);
-  q.u16 = at<uint16_t>(ws, Lw.u16);
+  q.o16 = at<uint16_t>(ws, Lw.ov);
+  q.u16 = at<uint16_t>(ws, Lw.uv);
   q.keys = at<uint64_t>(ws, Lw.keys);
   q.bar = at<unsigned>(ws, Lw.bar);
   q.tab = at<void>(ws, Lw.tab);

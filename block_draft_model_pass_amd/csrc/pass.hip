@@ -39,11 +39,43 @@ constexpr int XS_PAD = 8;                 // bf16 padding of an LDS activation r
 constexpr int XS_MAX = F + XS_PAD;        // widest activation row (down projection)
 constexpr int NT_H = H / 16;              // 160 row tiles of the hidden size
 constexpr float NEG_INF = -__builtin_huge_valf();
+// Versions: h_0 from the embedding, then after O(l) -> h_{2l+1}, after
+// DOWN(l) -> h_{2l+2}.
+constexpr int HV = 2 * L + 1;
+constexpr size_t HSTRIDE = static_cast<size_t>(MAXB) * H;        // floats per h version
+constexpr size_t SSTRIDE = static_cast<size_t>(H / 16) * MAXB;   // floats per ss version
+constexpr size_t QSTRIDE = static_cast<size_t>(MAXB) * QKV_N;
+constexpr size_t OSTRIDE = static_cast<size_t>(MAXB) * NQ * D;
+constexpr size_t USTRIDE = static_cast<size_t>(MAXB) * F;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Global-address-space views of pointers the compiler cannot classify
+// (pointers read from memory are generic): generic accesses would compile to
+// flat instructions, which also count against the LDS wait counter and so
+// would make every LDS rendezvous wait for the in-flight weight prefetch.
+#define GA __attribute__((address_space(1)))
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <class T>
+__device__ __forceinline__ T gld(const void* p) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  if constexpr (sizeof(T) == 16) {
+    return __builtin_bit_cast(T, *reinterpret_cast<const GA u32x4*>(a));
+  } else if constexpr (sizeof(T) == 8) {
+    return __builtin_bit_cast(T, *reinterpret_cast<const GA u32x2*>(a));
+  } else if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, *reinterpret_cast<const GA uint32_t*>(a));
+  } else {
+    static_assert(sizeof(T) == 2, "gld: 2, 4, 8 or 16 bytes");
+    return __builtin_bit_cast(T, *reinterpret_cast<const GA uint16_t*>(a));
+  }
+}
+
 __device__ __forceinline__ uint4 ldw(const uint16_t* p) {
-  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+  return __builtin_bit_cast(
+      uint4, __builtin_nontemporal_load(reinterpret_cast<const GA u32x4*>(reinterpret_cast<uintptr_t>(p))));
 }
 
 // LDS-only rendezvous: waits for this wave's LDS operations, not for its
@@ -95,15 +127,18 @@ struct PassArgs {
   int nb, cb, nch;
   int B, nqt;
   // workspace
-  float* h;          // [8][H] residual stream
-  float* ss;         // [NT_H][8] per-tile sums of squares of h rows
-  float* qkv;        // [8][QKV_N]
+  // Single-assignment buffers: every version of a shared tensor has its own
+  // region, written once (coherent stores) and read after a barrier with
+  // ordinary cached loads -- no cache can hold an older value of it.
+  float* h;          // [HV][8][H] residual stream versions
+  float* ss;         // [HV][NT_H][8] per-tile sums of squares of each h version
+  float* qkv;        // [L][8][QKV_N]
   const float2* rope;  // [8][128] (cos, sin)
   float* po;
   float* pm;
   float* pl;
-  uint16_t* o16;     // [8][NQ*D]
-  uint16_t* u16;     // [8][F]
+  uint16_t* o16;     // [L][8][NQ*D]
+  uint16_t* u16;     // [L][8][F]
   uint64_t* keys;    // [grid][8]
   unsigned* bar;     // barrier words (BAR_*)
   unsigned spin_limit;
@@ -123,21 +158,26 @@ struct Smem {
 
 // ---------------------------------------------------------------- coherence
 
+__device__ __forceinline__ GA uint64_t* g64(const void* p) {
+  return reinterpret_cast<GA uint64_t*>(reinterpret_cast<uintptr_t>(p));
+}
+__device__ __forceinline__ GA uint32_t* g32(const void* p) {
+  return reinterpret_cast<GA uint32_t*>(reinterpret_cast<uintptr_t>(p));
+}
 __device__ __forceinline__ uint64_t ld_coh64(const void* p) {
-  return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(g64(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_coh64(void* p, uint64_t v) {
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(g64(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float ld_cohf(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __uint_as_float(__hip_atomic_load(g32(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 __device__ __forceinline__ void st_cohf(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(g32(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_coh32(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(g32(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint4 ld_coh128(const void* p) {
   const uint64_t a = ld_coh64(p), b = ld_coh64(static_cast<const char*>(p) + 8);
@@ -253,14 +293,17 @@ __device__ __forceinline__ f32x4 group_sum(Smem& s, int w0, int n, int lane) {
 // fixed order.  Every load (h and the sums) is issued in one round.
 constexpr int XN4 = MAXB * (H / 4) / NTHR;  // float4 of h per thread (10)
 
-__device__ __forceinline__ void build_x_norm(const PassArgs& a, Smem& s, int np, const uint16_t* gain) {
+__device__ __forceinline__ void build_x_norm(const PassArgs& a, Smem& s, int ver, int np,
+                                             const uint16_t* gain) {
   const int tid = otid(), wave = tid >> 6, lane = tid & 63;
   const int n4 = a.B * (H / 4);
+  const float* hsrc = a.h + ver * HSTRIDE;
+  const float* ssrc = a.ss + ver * SSTRIDE;
   float4 hv[XN4];
 #pragma unroll
   for (int u = 0; u < XN4; ++u) {
     const int e = tid + u * NTHR;
-    hv[u] = e < n4 ? ld_coh_f4(a.h + 4 * e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    hv[u] = e < n4 ? gld<float4>(hsrc + 4 * e) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   if (wave < a.B) {
     float v = 0.f;
@@ -268,7 +311,7 @@ __device__ __forceinline__ void build_x_norm(const PassArgs& a, Smem& s, int np,
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
       const int i = lane + 64 * q;
-      sv[q] = i < np ? ld_cohf(a.ss + i * MAXB + wave) : 0.f;
+      sv[q] = i < np ? gld<float>(ssrc + i * MAXB + wave) : 0.f;
     }
     v = sv[0] + sv[1] + sv[2];
     v = wave_sum(v);
@@ -282,7 +325,7 @@ __device__ __forceinline__ void build_x_norm(const PassArgs& a, Smem& s, int np,
     if (e < n4) {
       const int b = e / (H / 4), k = (e % (H / 4)) * 4;
       const float sc = s.scal[b];
-      const uint2 gg = *reinterpret_cast<const uint2*>(gain + k);
+      const uint2 gg = gld<uint2>(gain + k);
       const uint16_t y0 = f32_to_bf16(hv[u].x * sc * bf16_to_f32(gg.x & 0xffff));
       const uint16_t y1 = f32_to_bf16(hv[u].y * sc * bf16_to_f32(gg.x >> 16));
       const uint16_t y2 = f32_to_bf16(hv[u].z * sc * bf16_to_f32(gg.y & 0xffff));
@@ -305,7 +348,7 @@ __device__ __forceinline__ void copy_x(const PassArgs& a, Smem& s, const uint16_
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int e = tid + u * NTHR;
-    v[u] = e < n8 ? ld_coh128(src + 8 * e) : make_uint4(0, 0, 0, 0);
+    v[u] = e < n8 ? gld<uint4>(src + 8 * e) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -320,18 +363,19 @@ __device__ __forceinline__ void copy_x(const PassArgs& a, Smem& s, const uint16_
 
 // h rows (this tile's 16 columns) += acc; per-tile sums of squares.  Runs on
 // the lanes of one wave holding the reduced tile.
-__device__ __forceinline__ void residual_epilogue(const PassArgs& a, Smem& s, f32x4 acc, int tile,
-                                                  int r, int g) {
+__device__ __forceinline__ void residual_epilogue(const PassArgs& a, f32x4 acc, int tile, int r,
+                                                  int g, int vin) {
   float sq = 0.f;
   if (r < a.B) {
-    float* hp = a.h + static_cast<size_t>(r) * H + tile * 16 + 4 * g;
-    const float4 hv = ld_coh_f4(hp);
+    const size_t off = static_cast<size_t>(r) * H + tile * 16 + 4 * g;
+    const float4 hv = gld<float4>(a.h + vin * HSTRIDE + off);
     const f32x4 hn = {hv.x + acc[0], hv.y + acc[1], hv.z + acc[2], hv.w + acc[3]};
-    st_coh_f4(hp, hn);
+    st_coh_f4(a.h + (vin + 1) * HSTRIDE + off, hn);
     sq = hn[0] * hn[0] + hn[1] * hn[1] + hn[2] * hn[2] + hn[3] * hn[3];
   }
   sq = group4_sum(sq);
-  if (g == 0 && r < MAXB) st_cohf(a.ss + tile * MAXB + r, r < a.B ? sq : 0.f);
+  if (g == 0 && r < MAXB)
+    st_cohf(a.ss + (vin + 1) * SSTRIDE + tile * MAXB + r, r < a.B ? sq : 0.f);
 }
 
 // ---------------------------------------------------------------- phases
@@ -359,7 +403,7 @@ __device__ __forceinline__ void qkv_phase(const PassArgs& a, Smem& s, int l, int
   const int r = lane & 15, g = lane >> 4;
   const bool has = qkv_has(w);
   if (wave == 0) qkv_prefetch(a, l, W, true);
-  if (has) build_x_norm(a, s, np, a.tab->in_norm[l]);
+  if (has) build_x_norm(a, s, 2 * l, np, a.tab->in_norm[l]);
   if (has) {
     const int tile = 2 * w + (wave >> 2);
     constexpr int XS = H + XS_PAD;
@@ -368,7 +412,8 @@ __device__ __forceinline__ void qkv_phase(const PassArgs& a, Smem& s, int l, int
     lds_sync();
     if ((wave & 3) == 0) {
       acc = group_sum(s, wave, 4, lane);
-      if (r < a.B) st_coh_f4(a.qkv + static_cast<size_t>(r) * QKV_N + tile * 16 + 4 * g, acc);
+      if (r < a.B)
+        st_coh_f4(a.qkv + l * QSTRIDE + static_cast<size_t>(r) * QKV_N + tile * 16 + 4 * g, acc);
     }
   }
   wait_stores();
@@ -496,12 +541,12 @@ __device__ __forceinline__ void attn_query(const PassArgs& a, int l, int j, int 
   const int r = t * 16 + n;
   const bool qv = r < G * a.B;
   const int bi = qv ? r / G : 0, hl = qv ? r % G : 0;
-  const float* qraw = a.qkv + static_cast<size_t>(bi) * QKV_N + (j * G + hl) * D;
+  const float* qraw = a.qkv + l * QSTRIDE + static_cast<size_t>(bi) * QKV_N + (j * G + hl) * D;
   float qv8[8][8];
 #pragma unroll
   for (int si = 0; si < 8; ++si) {
-    const float4 u0 = ld_coh_f4(qraw + 32 * si + 8 * g);
-    const float4 u1 = ld_coh_f4(qraw + 32 * si + 8 * g + 4);
+    const float4 u0 = gld<float4>(qraw + 32 * si + 8 * g);
+    const float4 u1 = gld<float4>(qraw + 32 * si + 8 * g + 4);
     qv8[si][0] = u0.x; qv8[si][1] = u0.y; qv8[si][2] = u0.z; qv8[si][3] = u0.w;
     qv8[si][4] = u1.x; qv8[si][5] = u1.y; qv8[si][6] = u1.z; qv8[si][7] = u1.w;
   }
@@ -516,8 +561,8 @@ __device__ __forceinline__ void attn_query(const PassArgs& a, int l, int j, int 
   uint32_t pk[8][4];
 #pragma unroll
   for (int si = 0; si < 4; ++si) {
-    const uint4 ga = *reinterpret_cast<const uint4*>(gq + 32 * si + 8 * g);
-    const uint4 gb = *reinterpret_cast<const uint4*>(gq + 32 * (si + 4) + 8 * g);
+    const uint4 ga = gld<uint4>(gq + 32 * si + 8 * g);
+    const uint4 gb = gld<uint4>(gq + 32 * (si + 4) + 8 * g);
     const uint32_t gav[4] = {ga.x, ga.y, ga.z, ga.w}, gbv[4] = {gb.x, gb.y, gb.z, gb.w};
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
@@ -528,7 +573,7 @@ __device__ __forceinline__ void attn_query(const PassArgs& a, int l, int j, int 
         const float ga_f = bf16_to_f32((gav[ee >> 1] >> (16 * (ee & 1))) & 0xffff);
         const float gb_f = bf16_to_f32((gbv[ee >> 1] >> (16 * (ee & 1))) & 0xffff);
         const float x0 = qv8[si][ee] * sc * ga_f, x1 = qv8[si + 4][ee] * sc * gb_f;
-        const float2 cs = a.rope[bi * (D / 2) + 32 * si + 8 * g + ee];
+        const float2 cs = gld<float2>(a.rope + bi * (D / 2) + 32 * si + 8 * g + ee);
         lo2[h2] = x0 * cs.x - x1 * cs.y;
         hi2[h2] = x1 * cs.x + x0 * cs.y;
       }
@@ -550,21 +595,22 @@ __device__ __forceinline__ void attn_block_rows(const PassArgs& a, int l, int j,
   const int wave = otid() >> 6, lane = otid() & 63;
   if (wave >= a.B) return;
   const int b = wave;
-  const float* kr = a.qkv + static_cast<size_t>(b) * QKV_N + NQ * D + j * D;
-  const float* vr = a.qkv + static_cast<size_t>(b) * QKV_N + NQ * D + NKV * D + j * D;
-  float k0 = ld_cohf(kr + lane), k1 = ld_cohf(kr + lane + 64);
-  float k2 = ld_cohf(kr + lane + 128), k3 = ld_cohf(kr + lane + 192);
+  const float* kr = a.qkv + l * QSTRIDE + static_cast<size_t>(b) * QKV_N + NQ * D + j * D;
+  const float* vr = kr + NKV * D;
+  float k0 = gld<float>(kr + lane), k1 = gld<float>(kr + lane + 64);
+  float k2 = gld<float>(kr + lane + 128), k3 = gld<float>(kr + lane + 192);
   float vv[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) vv[q] = ld_cohf(vr + lane + 64 * q);
+  for (int q = 0; q < 4; ++q) vv[q] = gld<float>(vr + lane + 64 * q);
   const float sq = wave_sum(k0 * k0 + k1 * k1 + k2 * k2 + k3 * k3);
   const float sc = 1.0f / sqrtf(sq / static_cast<float>(D) + a.eps);
   const uint16_t* gn = a.tab->k_norm[l];
-  k0 *= sc * bf16_to_f32(gn[lane]);
-  k1 *= sc * bf16_to_f32(gn[lane + 64]);
-  k2 *= sc * bf16_to_f32(gn[lane + 128]);
-  k3 *= sc * bf16_to_f32(gn[lane + 192]);
-  const float2 c0 = a.rope[b * (D / 2) + lane], c1 = a.rope[b * (D / 2) + lane + 64];
+  k0 *= sc * bf16_to_f32(gld<uint16_t>(gn + lane));
+  k1 *= sc * bf16_to_f32(gld<uint16_t>(gn + lane + 64));
+  k2 *= sc * bf16_to_f32(gld<uint16_t>(gn + lane + 128));
+  k3 *= sc * bf16_to_f32(gld<uint16_t>(gn + lane + 192));
+  const float2 c0 = gld<float2>(a.rope + b * (D / 2) + lane);
+  const float2 c1 = gld<float2>(a.rope + b * (D / 2) + lane + 64);
   uint16_t* kd = kl + b * D;
   kd[lane] = f32_to_f16_bits(k0 * c0.x - k2 * c0.y);
   kd[lane + 64] = f32_to_f16_bits(k1 * c1.x - k3 * c1.y);
@@ -629,7 +675,7 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KV
 // pairs of head dims.
 constexpr int MQ = 32;  // chunks per quarter (nch <= 128)
 
-__device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s) {
+__device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
   const int ngroup = NKV * a.nqt * 16;
   const int w = blockIdx.x;
   if (w < ngroup) {
@@ -695,7 +741,7 @@ __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s) {
         const int bi = r / G, hl = r % G;
         const uint32_t pk = static_cast<uint32_t>(f32_to_bf16(acc0 * s.scal[0])) |
                             (static_cast<uint32_t>(f32_to_bf16(acc1 * s.scal[0])) << 16);
-        st_coh32(reinterpret_cast<uint32_t*>(a.o16 + static_cast<size_t>(bi) * NQ * D +
+        st_coh32(reinterpret_cast<uint32_t*>(a.o16 + l * OSTRIDE + static_cast<size_t>(bi) * NQ * D +
                                              (j * G + hl) * D + d2),
                  pk);
       }
@@ -718,12 +764,12 @@ __device__ __forceinline__ void o_phase(const PassArgs& a, Smem& s, int l, uint4
   const int r = lane & 15, g = lane >> 4;
   if (w < NT_H) {
     if (wave == 0) o_prefetch(a, l, W, true);
-    copy_x(a, s, a.o16, NQ * D);
+    copy_x(a, s, a.o16 + l * OSTRIDE, NQ * D);
     constexpr int XS = NQ * D + XS_PAD;
     f32x4 acc = mma_tile<24>(W, s.x + r * XS, r < a.B, wave * 768, g, 24);
     s.red[wave][lane] = acc;
     lds_sync();
-    if (wave == 0) residual_epilogue(a, s, group_sum(s, 0, NWAVE, lane), w, r, g);
+    if (wave == 0) residual_epilogue(a, group_sum(s, 0, NWAVE, lane), w, r, g, 2 * l);
   }
   wait_stores();
 }
@@ -744,7 +790,7 @@ __device__ __forceinline__ void gu_phase(const PassArgs& a, Smem& s, int l, int 
   const int r = lane & 15, g = lane >> 4;
   const bool has = w < F / 16;
   if (wave == 0) gu_prefetch(a, l, w, W, true);
-  if (has) build_x_norm(a, s, np, a.tab->post_norm[l]);
+  if (has) build_x_norm(a, s, 2 * l + 1, np, a.tab->post_norm[l]);
   constexpr int XS = H + XS_PAD;
   for (int pair = w; pair < F / 16; pair += gridDim.x) {
     f32x4 acc = mma_tile<20>(W, s.x + r * XS, r < a.B, (wave & 3) * 640, g, 20);
@@ -762,7 +808,7 @@ __device__ __forceinline__ void gu_phase(const PassArgs& a, Smem& s, int l, int 
           const float z = ag[i];
           o[i] = f32_to_bf16(z / (1.0f + __expf(-z)) * au[i]);
         }
-        st_coh64(a.u16 + static_cast<size_t>(r) * F + pair * 16 + 4 * g,
+        st_coh64(a.u16 + l * USTRIDE + static_cast<size_t>(r) * F + pair * 16 + 4 * g,
                  static_cast<uint64_t>(o[0] | (static_cast<uint32_t>(o[1]) << 16)) |
                      (static_cast<uint64_t>(o[2] | (static_cast<uint32_t>(o[3]) << 16)) << 32));
       }
@@ -798,14 +844,14 @@ __device__ __forceinline__ void down_phase(const PassArgs& a, Smem& s, int l, ui
   const int r = lane & 15, g = lane >> 4;
   if (w < NT_H) {
     if (wave == 0) down_prefetch(a, l, W, true);
-    copy_x(a, s, a.u16, F);
+    copy_x(a, s, a.u16 + l * USTRIDE, F);
     int kbeg, nw;
     down_range(wave, kbeg, nw);
     constexpr int XS = F + XS_PAD;
     f32x4 acc = mma_tile<32>(W, s.x + r * XS, r < a.B, kbeg, g, nw);
     s.red[wave][lane] = acc;
     lds_sync();
-    if (wave == 0) residual_epilogue(a, s, group_sum(s, 0, NWAVE, lane), w, r, g);
+    if (wave == 0) residual_epilogue(a, group_sum(s, 0, NWAVE, lane), w, r, g, 2 * l + 1);
   }
   wait_stores();
 }
@@ -834,7 +880,7 @@ __device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, uin
   const int r = lane & 15, g = lane >> 4;
   const int ntiles = a.vocab / 16, npairs = (ntiles + 1) / 2;
   if (wave == 0) lm_prefetch(a, w, W, true);
-  build_x_norm(a, s, np, a.final_norm);
+  build_x_norm(a, s, 2 * L, np, a.final_norm);
   constexpr int XS = H + XS_PAD;
   if (w == 0 && a.hidden) {
     for (int e = otid(); e < a.B * H; e += NTHR)
@@ -941,7 +987,7 @@ __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
     grid_sync(a);
     attn_phase(a, s, l, R);
     grid_sync(a);
-    merge_phase(a, s);
+    merge_phase(a, s, l);
     uint4 Wo[24];
     o_prefetch(a, l, Wo, pre);
     grid_sync(a);
@@ -964,7 +1010,7 @@ __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
     grid_sync(a);
     argmax_final(a);
   } else if (blockIdx.x == 0 && a.hidden) {
-    build_x_norm(a, s, np, a.final_norm);
+    build_x_norm(a, s, 2 * L, np, a.final_norm);
     for (int e = otid(); e < H; e += NTHR) a.hidden[e] = s.x[e];
   }
 }
