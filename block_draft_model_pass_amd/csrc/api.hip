@@ -318,7 +318,7 @@ extern "C" int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* 
   q.ss = at<float>(ws, Lw.ss);
   q.qkv = at<float>(ws, Lw.qkv);
   q.rope = at<float2>(ws, Lw.rope);
-  q.po = at<float>(ws, Lw.po);
+  q.po = at<uint16_t>(ws, Lw.po);
   q.pm = at<float>(ws, Lw.pm);
   q.pl = at<float>(ws, Lw.pl);
   q.o16 = at<uint16_t>(ws, Lw.ov);

@@ -47,6 +47,10 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, b));
+}
+
 // Order-preserving map of a finite fp32 to uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t f32_order_key(float v) {
   uint32_t u = __float_as_uint(v);
@@ -229,7 +233,7 @@ struct PassLaunch {
   float* ss;
   float* qkv;
   float2* rope;
-  float* po;
+  uint16_t* po;            // chunk outputs, fp16, normalised by the chunk sum
   float* pm;
   float* pl;
   uint16_t* o16;

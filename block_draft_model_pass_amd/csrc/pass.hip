@@ -4,7 +4,8 @@
 // scale 1/16; "Parity validation" -- stage order).
 //
 // One 8-wave block per CU, launched cooperatively so all blocks are resident.
-// Phases are separated by a grid barrier (generation counter, bounded spin):
+// Phases are separated by a grid barrier (monotonic arrival counters, bounded
+// spin):
 //
 //   per layer: QKV  -> ATTN (q/k norm + RoPE + partials) -> MERGE
 //              -> O (+ residual, row sums of squares) -> GATE/UP -> DOWN (+ residual)
@@ -17,10 +18,16 @@
 // The L2 caches of the eight XCDs are not coherent with each other, and an
 // agent-scope fence (L2 writeback or invalidate) costs about 2 us per
 // barrier.  Instead, every value that one block writes and another block
-// reads inside the kernel moves through device-coherent accesses (agent-scope
-// relaxed atomic loads and stores, which write through and read past the
-// non-coherent caches); a wave waits for its own stores to complete before it
-// arrives at a barrier, and the barrier itself is two-level (one counter per
+// reads inside the kernel is written with device-coherent stores (agent-scope
+// relaxed atomic stores, which write through to memory), and a wave waits for
+// its own stores to complete before it arrives at a barrier.  Activations are
+// single-assignment: each version of h, its row sums, qkv, the attention
+// output and the MLP product has its own region, written once and only read
+// after the barrier that follows, so no L2 can hold an older copy of a line
+// (kernel launches start with invalidated L2s) and readers use ordinary cached
+// loads -- the 80-120 KB every block reads comes from its XCD's L2.  Buffers
+// that are rewritten within one pass (attention partials, argmax keys) are
+// read with device-coherent loads.  The barrier is two-level (one counter per
 // XCD, then one across XCDs) so that no single address takes 256 atomics.
 //
 // GEMV phases read bf16 activations from LDS (built once per phase; RMSNorm
@@ -134,7 +141,7 @@ struct PassArgs {
   float* ss;         // [HV][NT_H][8] per-tile sums of squares of each h version
   float* qkv;        // [L][8][QKV_N]
   const float2* rope;  // [8][128] (cos, sin)
-  float* po;
+  uint16_t* po;
   float* pm;
   float* pl;
   uint16_t* o16;     // [L][8][NQ*D]
@@ -176,6 +183,9 @@ __device__ __forceinline__ float ld_cohf(const float* p) {
 __device__ __forceinline__ void st_cohf(float* p, float v) {
   __hip_atomic_store(g32(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint32_t ld_coh32(const void* p) {
+  return __hip_atomic_load(g32(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void st_coh32(uint32_t* p, uint32_t v) {
   __hip_atomic_store(g32(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -200,42 +210,37 @@ __device__ __forceinline__ void st_coh_f4(float* p, f32x4 v) {
 
 // ---------------------------------------------------------------- barrier
 
-// Barrier words (unsigned): generation at [0], status at [32], cross-XCD
-// counter at [64], per-XCD counters at [128 + 64 x] -- each in its own
-// 256-byte line.
-constexpr int BAR_GEN = 0, BAR_STATUS = 32, BAR_TOP = 64, BAR_XCD = 128, BAR_WORDS = 1024;
+// Barrier words (unsigned): status at [0], cross-XCD counter at [64], per-XCD
+// counters at [128 + 64 x] -- each in its own 256-byte line.  The counters
+// only grow during a pass (the init kernel zeroes them), so barrier k
+// (1-based, counted by every block itself) is complete once the cross-XCD
+// counter reaches k * groups.  No resets and no separate release word: the
+// critical path is two atomics and the waiters' next poll, which matters
+// because every memory round trip is slow while the weight stream saturates
+// HBM.
+constexpr int BAR_STATUS = 0, BAR_TOP = 64, BAR_XCD = 128, BAR_WORDS = 1024;
 
 __device__ __forceinline__ unsigned ald(unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void grid_sync(const PassArgs& a) {
+__device__ __forceinline__ void grid_sync(const PassArgs& a, unsigned& k) {
   lds_sync();
+  ++k;
   if (otid() == 0) {
     unsigned* bar = a.bar;
-    const unsigned g = ald(bar + BAR_GEN);
     const unsigned x = blockIdx.x & 7;  // blocks are dealt to the XCDs round robin
     const unsigned per = (gridDim.x + 7 - x) / 8;
+    const unsigned groups = gridDim.x < 8 ? gridDim.x : 8;
+    const unsigned goal = k * groups;
     bool wait = true;
     if (__hip_atomic_fetch_add(bar + BAR_XCD + 64 * x, 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT) == per - 1) {
-      // Resets complete (wait on store completion) before the next step, so
-      // they are visible before anyone can see the new generation; no L2
-      // writeback is needed because shared data never sits dirty in L2.
-      __hip_atomic_store(bar + BAR_XCD + 64 * x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      wait_stores();
-      const unsigned groups = gridDim.x < 8 ? gridDim.x : 8;
-      if (__hip_atomic_fetch_add(bar + BAR_TOP, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-          groups - 1) {
-        __hip_atomic_store(bar + BAR_TOP, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        wait_stores();
-        __hip_atomic_store(bar + BAR_GEN, g + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        wait = false;
-      }
-    }
+                               __HIP_MEMORY_SCOPE_AGENT) == k * per - 1)
+      wait = __hip_atomic_fetch_add(bar + BAR_TOP, 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) != goal - 1;
     if (wait) {
       unsigned n = 0;
-      while (ald(bar + BAR_GEN) == g) {
+      while (ald(bar + BAR_TOP) < goal) {
         __builtin_amdgcn_s_sleep(2);
         if (++n > a.spin_limit) {  // bounded: never hang the device
           __hip_atomic_store(bar + BAR_STATUS, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -424,10 +429,12 @@ __device__ __forceinline__ void qkv_phase(const PassArgs& a, Smem& s, int l, int
 // Block w < 2 nch takes KV head j = w / nch and chunk c = w % nch of the
 // visible context (cb blocks of 32 cells); the last chunk of each head also
 // takes the block rows' own keys.  Context K/V never depends on this pass, so
-// each thread loads its share of the chunk's first 32-cell block (16 KiB of K
-// and 16 KiB of V^T, 4 x 16 bytes per thread) *before* the barrier that
-// precedes the phase; blocks then rotate through two LDS buffers while the
-// next one is in flight.  Waves t < nqt own 16 query rows each.
+// each thread loads its share of the chunk's first two 32-cell blocks (16 KiB
+// of K and 16 KiB of V^T each, 4 x 16 bytes per thread per block) *before*
+// the barrier that precedes the phase; blocks then rotate through two LDS
+// buffers, the register slot of a block being refilled two blocks ahead.
+// Waves t < nqt own 16 query rows each.  A chunk leaves its output
+// normalised by its own softmax sum, in fp16, with its maximum and sum.
 
 struct KVRegs {
   uint4 v[4];
@@ -456,22 +463,40 @@ __device__ __forceinline__ void attn_load(const PassArgs& a, int l, int ib_globa
   }
 }
 
+// LDS layouts of one 32-cell block, XOR-swizzled so that an MFMA operand
+// read (16 rows at the same offset) touches every bank once:
+//   keys   [32 cells][256]: 16-byte chunk c of cell r sits at chunk c ^ (r & 15)
+//   values [256 dims][32] : 8-byte chunk c of dim d sits at chunk c ^ ((d >> 1) & 7)
+// Offsets are in fp16 elements.
+__device__ __forceinline__ int kswz(int cell, int c16) { return cell * D + ((c16 ^ (cell & 15)) << 3); }
+__device__ __forceinline__ int vswz(int dim, int c8) {
+  return dim * BLK_CELLS + ((c8 ^ ((dim >> 1) & 7)) << 2);
+}
+
 __device__ __forceinline__ void attn_store(const KVRegs& R, uint16_t* kbuf, uint16_t* vbuf) {
   const int tid = otid();
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    *reinterpret_cast<uint4*>(kbuf + 8 * (tid + u * NTHR)) = R.v[u];
-    *reinterpret_cast<uint4*>(vbuf + 8 * (tid + u * NTHR)) = R.v[2 + u];
+    const int e = tid + u * NTHR;
+    *reinterpret_cast<uint4*>(kbuf + kswz(e >> 5, e & 31)) = R.v[u];
+    const int dim = e >> 2, c8 = 2 * (e & 3);
+    const uint4 v = R.v[2 + u];
+    *reinterpret_cast<uint2*>(vbuf + vswz(dim, c8)) = make_uint2(v.x, v.y);
+    *reinterpret_cast<uint2*>(vbuf + vswz(dim, c8 + 1)) = make_uint2(v.z, v.w);
   }
 }
 
 // Waves other than 0 load their share of the chunk's first block before the
 // barrier; wave 0 (which runs the barrier) loads its share right after it.
-__device__ __forceinline__ void attn_prefetch(const PassArgs& a, int l, KVRegs& R, bool go) {
+__device__ __forceinline__ void attn_prefetch(const PassArgs& a, int l, KVRegs& R0, KVRegs& R1,
+                                              bool go) {
   const int w = blockIdx.x;
   const bool has = w < NKV * a.nch;
   const int j = has ? w / a.nch : 0, c = has ? w % a.nch : 0;
-  attn_load(a, l, c * a.cb, j, R, go && has && c * a.cb < a.nb);
+  const int blk0 = c * a.cb;
+  const int nblk = has && a.nb > blk0 ? min(a.cb, a.nb - blk0) : 0;
+  attn_load(a, l, blk0, j, R0, go && nblk > 0);
+  attn_load(a, l, blk0 + 1, j, R1, go && nblk > 1);
 }
 
 // One 32-cell block from LDS (keys [32][256], values [256][32]) for this
@@ -480,14 +505,11 @@ __device__ __forceinline__ void attn_block(const uint16_t* kb, const uint16_t* v
                                            int64_t lo, int64_t hi, float scale_log2,
                                            const uint4 (&qf)[8], f32x4 (&o)[16], float& m,
                                            float& lsum, int n, int g) {
-  const uint16_t* k0 = kb + n * D + 8 * g;
-  const uint16_t* k1 = k0 + 16 * D;
-  const uint16_t* vbase = vb + n * 32 + 4 * g;
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int si = 0; si < 8; ++si) {
-    s0 = mfma_f16(*reinterpret_cast<const uint4*>(k0 + 32 * si), qf[si], s0);
-    s1 = mfma_f16(*reinterpret_cast<const uint4*>(k1 + 32 * si), qf[si], s1);
+    s0 = mfma_f16(*reinterpret_cast<const uint4*>(kb + kswz(n, g + 4 * si)), qf[si], s0);
+    s1 = mfma_f16(*reinterpret_cast<const uint4*>(kb + kswz(16 + n, g + 4 * si)), qf[si], s1);
   }
   const bool full = pb >= lo && pb + 32 <= hi;
   float x[8];
@@ -526,8 +548,8 @@ __device__ __forceinline__ void attn_block(const uint16_t* kb, const uint16_t* v
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt) {
     o[dt] *= alpha;
-    const uint2 x0 = *reinterpret_cast<const uint2*>(vbase + 16 * dt * 32);
-    const uint2 x1 = *reinterpret_cast<const uint2*>(vbase + 16 * dt * 32 + 16);
+    const uint2 x0 = *reinterpret_cast<const uint2*>(vb + vswz(16 * dt + n, g));
+    const uint2 x1 = *reinterpret_cast<const uint2*>(vb + vswz(16 * dt + n, g + 4));
     const uint4 v = make_uint4(x0.x & vm[0], x0.y & vm[1], x1.x & vm[2], x1.y & vm[3]);
     o[dt] = mfma_f16(v, pf, o[dt]);
   }
@@ -611,16 +633,33 @@ __device__ __forceinline__ void attn_block_rows(const PassArgs& a, int l, int j,
   k3 *= sc * bf16_to_f32(gld<uint16_t>(gn + lane + 192));
   const float2 c0 = gld<float2>(a.rope + b * (D / 2) + lane);
   const float2 c1 = gld<float2>(a.rope + b * (D / 2) + lane + 64);
-  uint16_t* kd = kl + b * D;
-  kd[lane] = f32_to_f16_bits(k0 * c0.x - k2 * c0.y);
-  kd[lane + 64] = f32_to_f16_bits(k1 * c1.x - k3 * c1.y);
-  kd[lane + 128] = f32_to_f16_bits(k2 * c0.x + k0 * c0.y);
-  kd[lane + 192] = f32_to_f16_bits(k3 * c1.x + k1 * c1.y);
+  const float kv[4] = {k0 * c0.x - k2 * c0.y, k1 * c1.x - k3 * c1.y, k2 * c0.x + k0 * c0.y,
+                       k3 * c1.x + k1 * c1.y};
 #pragma unroll
-  for (int q = 0; q < 4; ++q) vl[(lane + 64 * q) * BLK_CELLS + b] = f32_to_f16_bits(vv[q]);
+  for (int q = 0; q < 4; ++q) {
+    const int d = lane + 64 * q;
+    kl[kswz(b, d >> 3) + (d & 7)] = f32_to_f16_bits(kv[q]);
+    vl[vswz(d, b >> 2) + (b & 3)] = f32_to_f16_bits(vv[q]);
+  }
 }
 
-__device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KVRegs& R) {
+// One block step: the block sits in register slot R; it goes to LDS buffer
+// ib & 1, the slot is refilled with block ib + 2, and the waves run it.
+__device__ __forceinline__ void attn_step(const PassArgs& a, Smem& s, int l, int j, int blk0,
+                                          int nblk, int ib, KVRegs& R, int wave, const uint4 (&qf)[8],
+                                          f32x4 (&o)[16], float& m, float& lsum, int n, int g) {
+  uint16_t* kbuf = s.x + (ib & 1) * (2 * BLK_CELLS * D);
+  uint16_t* vbuf = kbuf + BLK_CELLS * D;
+  attn_store(R, kbuf, vbuf);
+  attn_load(a, l, blk0 + ib + 2, j, R, ib + 2 < nblk);
+  lds_sync();
+  if (wave < a.nqt)
+    attn_block(kbuf, vbuf, a.p0 + 32 * static_cast<int64_t>(blk0 + ib), a.lo, a.hi, a.scale_log2,
+               qf, o, m, lsum, n, g);
+}
+
+__device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KVRegs& R0,
+                                           KVRegs& R1) {
   const int w = blockIdx.x;
   if (w < NKV * a.nch) {
     const int j = w / a.nch, c = w % a.nch;
@@ -632,7 +671,10 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KV
     // LDS: block buffers (keys then values) at 0 and 2 x 8192, block rows at 4 x 8192
     uint16_t* kl = s.x + 4 * BLK_CELLS * D;
     uint16_t* vl = s.x + 5 * BLK_CELLS * D;
-    if (wave == 0) attn_load(a, l, blk0, j, R, nblk > 0);
+    if (wave == 0) {
+      attn_load(a, l, blk0, j, R0, nblk > 0);
+      attn_load(a, l, blk0 + 1, j, R1, nblk > 1);
+    }
     uint4 qf[8];
     if (wave < a.nqt) attn_query(a, l, j, wave, n, g, qf);
     if (rows) attn_block_rows(a, l, j, kl, vl);
@@ -640,15 +682,9 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KV
     f32x4 o[16];
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int ib = 0; ib < nblk; ++ib) {
-      uint16_t* kbuf = s.x + (ib & 1) * (2 * BLK_CELLS * D);
-      uint16_t* vbuf = kbuf + BLK_CELLS * D;
-      attn_store(R, kbuf, vbuf);
-      attn_load(a, l, blk0 + ib + 1, j, R, ib + 1 < nblk);
-      lds_sync();
-      if (wave < a.nqt)
-        attn_block(kbuf, vbuf, a.p0 + 32 * static_cast<int64_t>(blk0 + ib), a.lo, a.hi,
-                   a.scale_log2, qf, o, m, lsum, n, g);
+    for (int ib = 0; ib < nblk; ib += 2) {
+      attn_step(a, s, l, j, blk0, nblk, ib, R0, wave, qf, o, m, lsum, n, g);
+      if (ib + 1 < nblk) attn_step(a, s, l, j, blk0, nblk, ib + 1, R1, wave, qf, o, m, lsum, n, g);
     }
     if (rows) {
       lds_sync();
@@ -661,17 +697,25 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KV
         st_cohf(a.pm + base * 16 + n, m);
         st_cohf(a.pl + base * 16 + n, lsum);
       }
-      float* op = a.po + (base * 16 + n) * D + 4 * g;
+      const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+      uint16_t* op = a.po + (base * 16 + n) * D + 4 * g;
 #pragma unroll
-      for (int dt = 0; dt < 16; ++dt) st_coh_f4(op + 16 * dt, o[dt]);
+      for (int dt = 0; dt < 16; ++dt) {
+        const uint64_t lo = static_cast<uint64_t>(f32_to_f16_bits(o[dt][0] * inv)) |
+                            (static_cast<uint64_t>(f32_to_f16_bits(o[dt][1] * inv)) << 16);
+        const uint64_t hi = static_cast<uint64_t>(f32_to_f16_bits(o[dt][2] * inv)) |
+                            (static_cast<uint64_t>(f32_to_f16_bits(o[dt][3] * inv)) << 16);
+        st_coh64(op + 16 * dt, lo | (hi << 32));
+      }
     }
   }
   wait_stores();
 }
 
 // Merge of the chunks of one (KV head, query tile, query row): wave 0 turns
-// the chunks' maxima and sums into weights while every thread already has its
-// partial outputs in flight; 512 threads = 4 quarters of the chunks x 128
+// the chunks' maxima and sums into weights (w_c = 2^(m_c - M) l_c, chunk
+// outputs being already normalised by l_c) while every thread already has
+// its partial outputs in flight; 512 threads = 4 quarters of the chunks x 128
 // pairs of head dims.
 constexpr int MQ = 32;  // chunks per quarter (nch <= 128)
 
@@ -687,11 +731,11 @@ __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
       const size_t cstride = static_cast<size_t>(a.nqt) * 16;
       const size_t row0 = (static_cast<size_t>(j) * nc * a.nqt + t) * 16 + n;
       const int d2 = 2 * (tid & 127), quarter = tid >> 7;
-      uint64_t ov[MQ];
+      uint32_t ov[MQ];
 #pragma unroll
       for (int u = 0; u < MQ; ++u) {
         const int cc = quarter + 4 * u;
-        ov[u] = cc < nc ? ld_coh64(a.po + (row0 + cc * cstride) * D + d2) : 0ull;
+        ov[u] = cc < nc ? ld_coh32(a.po + (row0 + cc * cstride) * D + d2) : 0u;
       }
       if (wave == 0) {
         float mv[2], lv[2];
@@ -709,9 +753,9 @@ __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int cc = lane + 64 * q;
-          const float wt = cc < nc ? exp2f(mv[q] - M) : 0.f;
+          const float wt = cc < nc ? exp2f(mv[q] - M) * lv[q] : 0.f;
           s.mw[cc] = wt;
-          Ls += lv[q] * wt;
+          Ls += wt;
         }
         Ls = wave_sum(Ls);
         if (lane == 0) s.scal[0] = 1.0f / Ls;
@@ -723,8 +767,8 @@ __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
         const int cc = quarter + 4 * u;
         if (cc < nc) {
           const float wt = s.mw[cc];
-          acc0 += __uint_as_float(static_cast<uint32_t>(ov[u])) * wt;
-          acc1 += __uint_as_float(static_cast<uint32_t>(ov[u] >> 32)) * wt;
+          acc0 += f16_bits_to_f32(static_cast<uint16_t>(ov[u])) * wt;
+          acc1 += f16_bits_to_f32(static_cast<uint16_t>(ov[u] >> 16)) * wt;
         }
       }
       if (quarter > 0) {
@@ -975,39 +1019,40 @@ __device__ __forceinline__ void argmax_final(const PassArgs& a) {
 __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
   __shared__ Smem s;
   const bool pre = (otid() >> 6) != 0;  // waves other than 0 prefetch before barriers
+  unsigned bk = 0;  // barriers passed
   uint4 Wq[20];
   // Layer 0 QKV weights stream while the grid lines up.
   qkv_prefetch(a, 0, Wq, pre);
-  grid_sync(a);  // h, ss, the RoPE table and the layer table come from the init kernel
+  grid_sync(a, bk);  // h, ss, the RoPE table and the layer table come from the init kernel
   int np = 1;    // sums of squares of h: one entry per row from the init kernel
   for (int l = 0; l < L; ++l) {
     qkv_phase(a, s, l, np, Wq);
-    KVRegs R;
-    attn_prefetch(a, l, R, pre);
-    grid_sync(a);
-    attn_phase(a, s, l, R);
-    grid_sync(a);
+    KVRegs R0, R1;
+    attn_prefetch(a, l, R0, R1, pre);
+    grid_sync(a, bk);
+    attn_phase(a, s, l, R0, R1);
+    grid_sync(a, bk);
     merge_phase(a, s, l);
     uint4 Wo[24];
     o_prefetch(a, l, Wo, pre);
-    grid_sync(a);
+    grid_sync(a, bk);
     o_phase(a, s, l, Wo);
     uint4 Wg[20];
     gu_prefetch(a, l, blockIdx.x, Wg, pre);
-    grid_sync(a);
+    grid_sync(a, bk);
     gu_phase(a, s, l, NT_H, Wg);
     uint4 Wd[32];
     down_prefetch(a, l, Wd, pre);
-    grid_sync(a);
+    grid_sync(a, bk);
     down_phase(a, s, l, Wd);
     if (l + 1 < L) qkv_prefetch(a, l + 1, Wq, pre);
     else lm_prefetch(a, blockIdx.x, Wq, pre && a.B > 1);
-    grid_sync(a);
+    grid_sync(a, bk);
     np = NT_H;
   }
   if (a.B > 1) {
     lm_phase(a, s, np, Wq);
-    grid_sync(a);
+    grid_sync(a, bk);
     argmax_final(a);
   } else if (blockIdx.x == 0 && a.hidden) {
     build_x_norm(a, s, 2 * L, np, a.final_norm);
