@@ -30,13 +30,10 @@ int pass_grid() {
 }
 constexpr int SMALL_ROWS = 64;        // fuse/project: skinny path up to here
 constexpr int FC_SPLITS = 5;          // k splits of the fc GEMV (K = 12800)
-constexpr int O_SPLITS = 3;           // k splits of the O GEMV (K = 6144)
-constexpr int DOWN_SPLITS = 3;        // k splits of the down GEMV (K = 7680)
 constexpr size_t PART_FLOATS = static_cast<size_t>(FC_SPLITS) * GEMV_ROWS * H;
 
 struct Layout {
-  size_t h, xn, part, q16, kblk, vblkT, po, pm, pl, o16, u16, keys, rope, ss, qkv, hv, ov, uv, bar,
-      tab, y;
+  size_t part, po, pm, pl, keys, rope, ss, qkv, hv, ov, uv, bar, tab, y;
   size_t fixed;  // bytes before y
 };
 
@@ -50,17 +47,10 @@ Layout layout() {
   Layout L;
   size_t off = 0;
   const size_t nqt = 6, nc = NCH_MAX + 1;
-  L.h = take(off, sizeof(float) * MAXB * H);
-  L.xn = take(off, 2 * MAXB * H);
   L.part = take(off, sizeof(float) * PART_FLOATS);
-  L.q16 = take(off, 2 * MAXB * NQ * D);
-  L.kblk = take(off, 2 * NKV * BLK_CELLS * D);
-  L.vblkT = take(off, 2 * NKV * D * BLK_CELLS);
   L.po = take(off, sizeof(float) * NKV * nc * nqt * 16 * D);
   L.pm = take(off, sizeof(float) * NKV * nc * nqt * 16);
   L.pl = take(off, sizeof(float) * NKV * nc * nqt * 16);
-  L.o16 = take(off, 2 * MAXB * NQ * D);
-  L.u16 = take(off, 2 * MAXB * F);
   L.keys = take(off, sizeof(uint64_t) * KEYS_MAX * MAXB);
   L.rope = take(off, sizeof(float) * 2 * MAXB * (D / 2));
   // per-layer / per-version copies used by the persistent pass

@@ -141,10 +141,6 @@ struct GemvArgs {
 
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t st);
 
-// u[b][n] = silu(Wg x)[n] * (Wu x)[n], bf16 out [B][F]
-hipError_t launch_gateup(const void* wg, const void* wu, int fmt, const uint16_t* x, int B,
-                         uint16_t* u, hipStream_t st);
-
 // LM head + greedy argmax over the vocabulary.
 hipError_t launch_lmhead_argmax(const uint16_t* lm, int vocab, const uint16_t* z, int B,
                                 uint64_t* keys, int grid, uint16_t* logits_opt,
@@ -156,47 +152,11 @@ hipError_t launch_rownorm(float* h, const float* part, int S, size_t part_split_
                           int part_row_stride, int rows, const uint16_t* gain, float eps,
                           uint16_t* out, int out_stride, uint16_t* out2, hipStream_t st);
 
-// Embedding gather + input norm of the block rows, and the RoPE (cos, sin)
-// table of positions p .. p+B-1: rope[b][t], t < 128.
-hipError_t launch_embed_norm(const uint16_t* embed, int anchor, int mask, int B,
-                             const uint16_t* gain, float eps, float* h, uint16_t* xn, int64_t p,
-                             double theta, float2* rope, hipStream_t st);
-
-// Per-head q/k RMSNorm + NeoX RoPE of the fused QKV output of the block rows.
-hipError_t launch_qkv_post(const float* part, int S, int B, const float2* rope,
-                           const uint16_t* q_norm, const uint16_t* k_norm, float eps,
-                           uint16_t* q16, uint16_t* kblk, uint16_t* vblkT, hipStream_t st);
-
 // Context K/V epilogue: y [n][KV_N] (row stride ldy, S partial splits) ->
 // k-norm + RoPE + fp16 into the ring.
 hipError_t launch_kv_post(const float* y, int S, size_t split_stride, int ldy, int n,
                           int64_t pos0, const void* const* k_norms, float eps, double theta,
                           uint16_t* ring_k, uint16_t* ring_vt, int capacity, hipStream_t st);
-
-struct AttnArgs {
-  const uint16_t* q16;     // fp16 [B][24][256]
-  int B;
-  int nqt;                 // query tiles of 16 rows: ceil(12 B / 16)
-  // context segment (ring) for chunks < nch
-  const uint16_t* ring_k;  // fp16 [2][cap][256] for this layer
-  const uint16_t* ring_vt; // fp16 [2][cap/32][256][32]
-  int cap;
-  int64_t lo, hi;          // visible positions [lo, hi)
-  int64_t p0;              // first position of block 0 (multiple of 32)
-  int nb;                  // 32-cell blocks covering [p0, hi)
-  int cb;                  // blocks per chunk
-  int nch;                 // context chunks
-  // block keys (chunk index nch)
-  const uint16_t* kblk;    // fp16 [2][32][256]
-  const uint16_t* vblkT;   // fp16 [2][256][32]
-  float scale_log2;        // attn_scale * log2(e)
-  float* po;               // [2][nch+1][nqt][16][256]
-  float* pm;               // [2][nch+1][nqt][16]
-  float* pl;               // [2][nch+1][nqt][16]
-  uint16_t* o16;           // bf16 [B][24*256]
-};
-
-hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 
 // C[M][N] (fp32, ldc) = A[M][K] (bf16, lda) * W[N][K]^T
 hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w, int K,

@@ -95,51 +95,6 @@ __global__ __launch_bounds__(NW * 64) void k_gemv_bf16(GemvArgs a) {
   }
 }
 
-// u[b][n] = silu(gate) * up for one 16-row tile of the MLP; each wave streams
-// both the gate and the up rows of its k range against the same activations.
-template <int NW, int KBW>
-__global__ __launch_bounds__(NW * 64) void k_gateup_bf16(const uint16_t* wg, const uint16_t* wu,
-                                                         const uint16_t* x, int B, uint16_t* u) {
-  __shared__ f32x4 red[2][NW - 1][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane & 15, g = lane >> 4;
-  const int row0 = blockIdx.x * 16;
-  const bool xv = r < B;
-  const uint16_t* xrow = x + static_cast<size_t>(xv ? r : 0) * H;
-  const size_t roff = static_cast<size_t>(row0 + r) * H;
-  const int kbeg = wave * (KBW * 128);
-  uint4 w1[4 * KBW], w2[4 * KBW], xx[4 * KBW];
-  load_w<KBW>(w1, wg + roff, kbeg, g);
-  load_w<KBW>(w2, wu + roff, kbeg, g);
-  load_x<KBW>(xx, xrow, xv, kbeg, g);
-  __builtin_amdgcn_sched_barrier(0);
-  f32x4 ag = mma_chain<KBW>(w1, xx);
-  f32x4 au = mma_chain<KBW>(w2, xx);
-  if (wave > 0) {
-    red[0][wave - 1][lane] = ag;
-    red[1][wave - 1][lane] = au;
-  }
-  __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int w = 0; w < NW - 1; ++w) {
-      ag += red[0][w][lane];
-      au += red[1][w][lane];
-    }
-    if (xv) {
-      uint16_t o[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float z = ag[i];
-        o[i] = f32_to_bf16(z / (1.0f + __expf(-z)) * au[i]);
-      }
-      uint2 pk = make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
-                            o[2] | (static_cast<uint32_t>(o[3]) << 16));
-      *reinterpret_cast<uint2*>(u + static_cast<size_t>(r) * F + row0 + 4 * g) = pk;
-    }
-  }
-}
-
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
   lo = __shfl_xor(lo, m, 64);
@@ -277,14 +232,6 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t st) {
   } else {
     return hipErrorInvalidValue;
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_gateup(const void* wg, const void* wu, int fmt, const uint16_t* x, int B,
-                         uint16_t* u, hipStream_t st) {
-  if (fmt != W_BF16 || B < 1 || B > GEMV_ROWS) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gateup_bf16<4, 5>), dim3(F / 16), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(wg), static_cast<const uint16_t*>(wu), x, B, u);
   return hipGetLastError();
 }
 

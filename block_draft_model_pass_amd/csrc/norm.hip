@@ -1,6 +1,6 @@
-// Row-wise epilogues of the pass: residual add + RMSNorm, the embedding
-// gather, and the per-head q/k RMSNorm + NeoX RoPE of block rows and of
-// context K/V cells (Strata PR #1426 page, "Drafter runtime": full-head NeoX
+// Row-wise epilogues of the context path: sum of split partials + RMSNorm of
+// fused context rows, and the per-head k RMSNorm + NeoX RoPE of context K/V
+// cells (Strata PR #1426 page, "Drafter runtime": full-head NeoX
 // RoPE, theta 1e7; "Parity validation": q raw -> q normed -> q).
 #include "common.h"
 
@@ -58,39 +58,6 @@ __device__ __forceinline__ void rope_cs(int64_t pos, int t, double theta, float&
   fs = static_cast<float>(sn);
 }
 
-// Embedding rows of the block plus the RoPE table of the block positions
-// p .. p+B-1 (shared by all five layers): rope[b][t] = (cos, sin).
-__global__ __launch_bounds__(NT) void k_embed_norm(const uint16_t* embed, int anchor, int mask,
-                                                   const uint16_t* gain, float eps, float* h,
-                                                   uint16_t* xn, int64_t p, double theta,
-                                                   float2* rope) {
-  __shared__ float red[NT / 64];
-  const int b = blockIdx.x;
-  if (threadIdx.x < D / 2) {
-    float fc, fs;
-    rope_cs(p + b, threadIdx.x, theta, fc, fs);
-    rope[b * (D / 2) + threadIdx.x] = make_float2(fc, fs);
-  }
-  const int tok = b == 0 ? anchor : mask;
-  const uint16_t* row = embed + static_cast<size_t>(tok) * H;
-  float v[PER];
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = threadIdx.x + NT * i;
-    v[i] = bf16_to_f32(row[e]);
-    h[static_cast<size_t>(b) * H + e] = v[i];
-    ss += v[i] * v[i];
-  }
-  ss = block_sum<NT>(ss, red);
-  const float sc = 1.0f / sqrtf(ss / static_cast<float>(H) + eps);
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = threadIdx.x + NT * i;
-    xn[static_cast<size_t>(b) * H + e] = f32_to_bf16(v[i] * sc * bf16_to_f32(gain[e]));
-  }
-}
-
 // RMSNorm over one 256-wide head held as (a, c) = elements (t, t + 128) of
 // thread t, then NeoX rotation of the pair by the angle whose cos/sin are
 // (fc, fs).
@@ -105,40 +72,6 @@ __device__ __forceinline__ void norm_rope(float& a, float& c, const uint16_t* ga
   const float c2 = c * fc + a * fs;
   a = a2;
   c = c2;
-}
-
-// grid (B, 28): heads 0..23 = q, 24..25 = k, 26..27 = v; block 128.
-__global__ __launch_bounds__(128) void k_qkv_post(const float* part, int S, int B,
-                                                  const float2* rope, const uint16_t* q_norm,
-                                                  const uint16_t* k_norm, float eps,
-                                                  uint16_t* q16, uint16_t* kblk,
-                                                  uint16_t* vblkT) {
-  __shared__ float red[2];
-  const int b = blockIdx.x, hd = blockIdx.y, t = threadIdx.x;
-  const int col = hd < NQ ? hd * D : (hd < NQ + NKV ? NQ * D + (hd - NQ) * D
-                                                    : NQ * D + NKV * D + (hd - NQ - NKV) * D);
-  float a = 0.f, c = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float* r = part + (static_cast<size_t>(s) * B + b) * QKV_N + col;
-    a += r[t];
-    c += r[t + 128];
-  }
-  const float2 cs = rope[b * (D / 2) + t];
-  if (hd < NQ) {
-    norm_rope(a, c, q_norm, eps, cs.x, cs.y, red);
-    uint16_t* q = q16 + (static_cast<size_t>(b) * NQ + hd) * D;
-    q[t] = f32_to_f16_bits(a);
-    q[t + 128] = f32_to_f16_bits(c);
-  } else if (hd < NQ + NKV) {
-    norm_rope(a, c, k_norm, eps, cs.x, cs.y, red);
-    uint16_t* k = kblk + (static_cast<size_t>(hd - NQ) * BLK_CELLS + b) * D;
-    k[t] = f32_to_f16_bits(a);
-    k[t + 128] = f32_to_f16_bits(c);
-  } else {
-    uint16_t* v = vblkT + static_cast<size_t>(hd - NQ - NKV) * D * BLK_CELLS;
-    v[static_cast<size_t>(t) * BLK_CELLS + b] = f32_to_f16_bits(a);
-    v[static_cast<size_t>(t + 128) * BLK_CELLS + b] = f32_to_f16_bits(c);
-  }
 }
 
 struct KNorms {
@@ -198,22 +131,6 @@ hipError_t launch_rownorm(float* h, const float* part, int S, size_t part_split_
     default:
       return hipErrorInvalidValue;
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_embed_norm(const uint16_t* embed, int anchor, int mask, int B,
-                             const uint16_t* gain, float eps, float* h, uint16_t* xn, int64_t p,
-                             double theta, float2* rope, hipStream_t st) {
-  hipLaunchKernelGGL(k_embed_norm, dim3(B), dim3(NT), 0, st, embed, anchor, mask, gain, eps, h, xn,
-                     p, theta, rope);
-  return hipGetLastError();
-}
-
-hipError_t launch_qkv_post(const float* part, int S, int B, const float2* rope,
-                           const uint16_t* q_norm, const uint16_t* k_norm, float eps,
-                           uint16_t* q16, uint16_t* kblk, uint16_t* vblkT, hipStream_t st) {
-  hipLaunchKernelGGL(k_qkv_post, dim3(B, NQ + 2 * NKV), dim3(128), 0, st, part, S, B, rope, q_norm,
-                     k_norm, eps, q16, kblk, vblkT);
   return hipGetLastError();
 }
 
