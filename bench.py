@@ -31,15 +31,21 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "DFlash draft passes/sec (ctx 8192, block 8) + achieved HBM GB/s vs peak"
 
 
-def pass_bytes(n_ctx: int, block: int = BLOCK) -> int:
-    """Algorithmic HBM bytes of one draft pass: every layer matrix and the LM
-    head once, the gains, the distinct embedding rows and n_ctx fp16 K/V
-    cells (5 layers x 2 KV heads x 256 x K and V)."""
+# Stored bytes per weight of the layer matrices: bf16, Q8_0 (32 int8 + fp16
+# scale per 32 weights), Q4_0 (16 bytes of nibbles + fp16 scale per 32).
+BYTES_PER_WEIGHT = {"bf16": 2.0, "q8_0": 34 / 32, "q4_0": 18 / 32}
+
+
+def pass_bytes(n_ctx: int, block: int = BLOCK, fmt: str = "bf16") -> int:
+    """Algorithmic HBM bytes of one draft pass: every layer matrix (in its
+    storage format) and the bf16 LM head once, the gains, the distinct
+    embedding rows and n_ctx fp16 K/V cells (5 layers x 2 KV heads x 256 x
+    K and V)."""
     from block_draft_model_pass_amd import synth as S
     H, D, F = S.HIDDEN, S.HEAD_DIM, S.FFN
     qkv = (S.N_Q_HEADS + 2 * S.N_KV_HEADS) * D * H
     layer = qkv + H * S.N_Q_HEADS * D + 2 * F * H + H * F
-    mats = 2 * S.N_LAYERS * layer
+    mats = int(round(BYTES_PER_WEIGHT[fmt] * S.N_LAYERS * layer))
     gains = 2 * (S.N_LAYERS * (2 * H + 2 * D) + H)
     lm = 2 * S.VOCAB * H if block > 1 else 0
     emb = 2 * H * (2 if block > 1 else 1)
@@ -92,6 +98,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the CPU-oracle baseline (0 = skip)")
     ap.add_argument("--reps", type=int, default=50, help="repeats of the event-timed kernels")
+    ap.add_argument("--no-quant", action="store_true",
+                    help="skip the Q8_0 / Q4_0 backbone passes (ctx 8192, block 4)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -166,7 +174,8 @@ def main():
     draft_ms = ev[0].elapsed_time(ev[1]) / args.reps
     draft_gbs = pass_bytes(CTX) / (draft_ms * 1e-3) / 1e9
 
-    # Dominant kernel: LM head + greedy argmax over the 151936-row vocabulary.
+    # Standalone LM head + greedy argmax (the pass's largest single stream),
+    # for reference beside the whole-pass kernel.
     z = torch.randn((K, synth.HIDDEN), device="cuda").to(torch.bfloat16).view(torch.int16)
     for _ in range(5):
         dr.lm_head_argmax(z, cand)
@@ -177,6 +186,34 @@ def main():
     torch.cuda.synchronize()
     lm_ms = ev[0].elapsed_time(ev[1]) / args.reps
     lm_gbs = lm_head_bytes() / (lm_ms * 1e-3) / 1e9
+
+    # Quantized backbone (Q8_0 / Q4_0 layer matrices, bf16 LM head): draft
+    # passes at ctx 8192, block 4, on a context projected by those weights.
+    quant = {}
+    if not args.no_quant:
+        for fmt in ("q8_0", "q4_0"):
+            qw = DeviceWeights(synth.make_weights(fmt=fmt))
+            qkv_ring = KVRing(synth.WINDOW, synth.WINDOW)
+            qdr = Drafter(qw, qkv_ring, max_rows=2048)
+            for s0 in range(0, CTX, 2048):
+                qdr.commit(to_device(synth.make_taps(range(s0, s0 + 2048))), s0)
+            qb = 4
+            for _ in range(5):
+                qdr.draft(CTX, 11, qb, cand=cand)
+            ev[0].record()
+            for _ in range(args.reps):
+                qdr.draft(CTX, 11, qb, cand=cand)
+            ev[1].record()
+            torch.cuda.synchronize()
+            q_ms = ev[0].elapsed_time(ev[1]) / args.reps
+            q_bytes = pass_bytes(CTX, qb, fmt)
+            q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
+            quant[fmt] = {"ctx": CTX, "block": qb, "ms_per_pass": round(q_ms, 4),
+                          "passes_per_s": round(1e3 / q_ms, 2), "algorithmic_bytes": q_bytes,
+                          "achieved_GBs": round(q_gbs, 1),
+                          "frac_hbm_peak": round(q_gbs / HBM_PEAK_GBS, 4)}
+            del qdr, qkv_ring, qw
+            torch.cuda.empty_cache()
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -204,11 +241,18 @@ def main():
                        "algorithmic_bytes": pass_bytes(CTX),
                        "achieved_GBs": round(draft_gbs, 1),
                        "frac_hbm_peak": round(draft_gbs / HBM_PEAK_GBS, 4)},
-        "roofline": {"kernel": "k_lmhead_bf16 (+ k_argmax_reduce), dflash_lm_head_argmax",
-                     "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "launch_ms": round(lm_ms, 4),
-                     "bytes_per_launch": lm_head_bytes()},
+        # The draft pass is one persistent kernel (k_draft_pass, after the tiny
+        # k_pass_init); events bracket both on the stream they run on.
+        "roofline": {"kernel": "k_draft_pass (dflash_draft_block, ctx 8192, block 8)",
+                     "bound": "hbm", "achieved": round(draft_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(draft_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "launch_ms": round(draft_ms, 4),
+                     "bytes_per_launch": pass_bytes(CTX)},
+        "lm_head_standalone": {"kernel": "k_lmhead_bf16 + k_argmax_reduce (dflash_lm_head_argmax)",
+                               "ms": round(lm_ms, 4), "bytes": lm_head_bytes(),
+                               "achieved_GBs": round(lm_gbs, 1),
+                               "frac_hbm_peak": round(lm_gbs / HBM_PEAK_GBS, 4)},
+        "quantized_backbone": quant or None,
         "accepted_offered": [state["acc"], state["off"]],
         "cpu_baseline": cpu,
     }

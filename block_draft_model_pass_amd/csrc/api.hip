@@ -67,8 +67,17 @@ Layout layout() {
   return L;
 }
 
-size_t rows_bytes(int rows) {
-  return rows > SMALL_ROWS ? sizeof(float) * static_cast<size_t>(rows) * KV_N : 0;
+// Row-dependent tail of the workspace: fp32 GEMM output [rows][5120] and,
+// for quantized weights, the bf16 copy of the widest matrix the GEMM path
+// decodes (fc, 2560 x 12800).
+constexpr size_t DQ_ELEMS = static_cast<size_t>(H) * T * H;
+
+size_t y_bytes(int rows) { return sizeof(float) * static_cast<size_t>(rows) * KV_N; }
+
+size_t rows_bytes(int rows, int fmt) {
+  if (rows <= SMALL_ROWS) return 0;
+  const size_t y = (y_bytes(rows) + 255) & ~static_cast<size_t>(255);
+  return y + (fmt != W_BF16 ? 2 * DQ_ELEMS : 0);
 }
 
 template <class T>
@@ -84,7 +93,9 @@ int check_weights(const dflash_weights* w) {
   if (w->vocab < 16 || w->vocab % 16 != 0 || w->vocab > (1 << 24)) return DFLASH_EGEOMETRY;
   if (w->rope_theta != 1.0e7f || w->attn_scale != 0.0625f || w->rms_eps != 1.0e-6f)
     return DFLASH_EGEOMETRY;
-  if (w->backbone_type != DFLASH_W_BF16) return DFLASH_EINVAL;
+  if (w->backbone_type != DFLASH_W_BF16 && w->backbone_type != DFLASH_W_Q8_0 &&
+      w->backbone_type != DFLASH_W_Q4_0)
+    return DFLASH_EINVAL;
   if (!w->fc || !w->hidden_norm || !w->final_norm || !w->embed || !w->lm_head)
     return DFLASH_EINVAL;
   for (int l = 0; l < L; ++l) {
@@ -151,7 +162,8 @@ extern "C" size_t dflash_workspace_size(const dflash_weights* w, int32_t max_row
                                         int32_t max_block) {
   (void)w;
   if (max_rows < 0 || max_block < 0 || max_block > MAXB) return 0;
-  return layout().fixed + rows_bytes(max_rows);
+  const int fmt = w ? w->backbone_type : W_BF16;
+  return layout().fixed + rows_bytes(max_rows, fmt);
 }
 
 extern "C" int32_t dflash_fuse_context(const dflash_weights* w, const void* taps, int32_t n,
@@ -162,7 +174,8 @@ extern "C" int32_t dflash_fuse_context(const dflash_weights* w, const void* taps
   if (n == 0) return DFLASH_OK;
   if (!taps || !ctx || !ws) return DFLASH_EINVAL;
   const Layout Lw = layout();
-  if (ws_bytes < Lw.fixed + rows_bytes(n)) return DFLASH_EWORKSPACE;
+  const int fmt = w->backbone_type;
+  if (ws_bytes < Lw.fixed + rows_bytes(n, fmt)) return DFLASH_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint16_t* x = u16p(taps);
   uint16_t* out = static_cast<uint16_t*>(ctx);
@@ -172,7 +185,7 @@ extern "C" int32_t dflash_fuse_context(const dflash_weights* w, const void* taps
       const int rows = n - c0 < GEMV_ROWS ? n - c0 : GEMV_ROWS;
       GemvArgs a;
       a.w = seg1(w->fc, H);
-      a.fmt = W_BF16;
+      a.fmt = fmt;
       a.N = H;
       a.K = T * H;
       a.x = x + static_cast<size_t>(c0) * T * H;
@@ -187,7 +200,13 @@ extern "C" int32_t dflash_fuse_context(const dflash_weights* w, const void* taps
     }
   } else {
     float* y = at<float>(ws, Lw.y);
-    HIP_TRY(launch_gemm_bf16(x, T * H, n, seg1(w->fc, H), T * H, y, H, H, st));
+    SegTable wt = seg1(w->fc, H);
+    if (fmt != W_BF16) {  // decode once to bf16, then the bf16 GEMM
+      uint16_t* dq = at<uint16_t>(ws, Lw.y + rows_bytes(n, fmt) - 2 * DQ_ELEMS);
+      HIP_TRY(launch_dequant_bf16(w->fc, fmt, H, T * H, dq, st));
+      wt = seg1(dq, H);
+    }
+    HIP_TRY(launch_gemm_bf16(x, T * H, n, wt, T * H, y, H, H, st));
     HIP_TRY(launch_rownorm(nullptr, y, 1, 0, H, n, u16p(w->hidden_norm), w->rms_eps, out, H,
                            nullptr, st));
   }
@@ -206,7 +225,8 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
   if (n == 0) return DFLASH_OK;
   if (!ctx || !ws) return DFLASH_EINVAL;
   const Layout Lw = layout();
-  if (ws_bytes < Lw.fixed + rows_bytes(n)) return DFLASH_EWORKSPACE;
+  const int fmt = w->backbone_type;
+  if (ws_bytes < Lw.fixed + rows_bytes(n, fmt)) return DFLASH_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const void* knorms[L];
   for (int l = 0; l < L; ++l) knorms[l] = w->layer[l].k_norm;
@@ -220,7 +240,7 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
       const int rows = n - c0 < GEMV_ROWS ? n - c0 : GEMV_ROWS;
       GemvArgs a;
       a.w = seg_kv(w);
-      a.fmt = W_BF16;
+      a.fmt = fmt;
       a.N = KV_N;
       a.K = H;
       a.x = x + static_cast<size_t>(c0) * H;
@@ -234,7 +254,17 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
     }
   } else {
     float* y = at<float>(ws, Lw.y);
-    HIP_TRY(launch_gemm_bf16(x, H, n, seg_kv(w), H, y, KV_N, KV_N, st));
+    SegTable wt = seg_kv(w);
+    if (fmt != W_BF16) {  // decode the ten K/V matrices into one bf16 [5120][2560]
+      uint16_t* dq = at<uint16_t>(ws, Lw.y + rows_bytes(n, fmt) - 2 * DQ_ELEMS);
+      for (int s = 0; s < wt.nseg; ++s) {
+        const int r0 = s ? wt.row_end[s - 1] : 0;
+        HIP_TRY(launch_dequant_bf16(wt.ptr[s], fmt, wt.row_end[s] - r0, H,
+                                    dq + static_cast<size_t>(r0) * H, st));
+      }
+      wt = seg1(dq, KV_N);
+    }
+    HIP_TRY(launch_gemm_bf16(x, H, n, wt, H, y, KV_N, KV_N, st));
     HIP_TRY(launch_kv_post(y, 1, 0, KV_N, n, pos0, knorms, w->rms_eps, theta, rk, rv,
                            kv->capacity, st));
   }
@@ -259,6 +289,7 @@ extern "C" int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* 
   const int grid = pass_grid();
   if (grid < QKV_N / 32) return DFLASH_EHIP;  // the pass needs >= 224 resident blocks
   PassLaunch q;
+  q.fmt = w->backbone_type;
   for (int l = 0; l < L; ++l) {
     const dflash_layer_weights& y = w->layer[l];
     q.wq[l] = u16p(y.wq);

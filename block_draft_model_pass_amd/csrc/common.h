@@ -127,6 +127,58 @@ struct SegTable {
 
 enum WFormat { W_BF16 = 0, W_Q8_0 = 1, W_Q4_0 = 2 };
 
+// ---------------------------------------------------------------- quantized weights
+// Q8_0 / Q4_0 blocks ("Quantized drafter" formats: 32 consecutive input-dim
+// weights of one output row share an fp16 scale) are decoded to fp16 in
+// registers.  The integer (q, or nibble - 8) is exact in fp16; the only
+// rounding is that of q * scale (relative 2^-11).  A decoded group is the 8
+// fp16 values one lane feeds to one MFMA 16x16x32 f16.
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// Bytes 2j, 2j+1 of x as the fp16 pair (1024 + byte): 0x64 is the high byte
+// of fp16 1024, so a byte in the low mantissa bits is added exactly.  One
+// byte permute: selector bytes 0-3 pick from x, 4 picks 0x64.
+__device__ __forceinline__ uint32_t u8pair_f16(uint32_t x, int j) {
+  return __builtin_amdgcn_perm(0x64646464u, x, j ? 0x04030402u : 0x04010400u);
+}
+
+__device__ __forceinline__ uint32_t dq_pair(uint32_t t, h2 off, h2 s) {
+  h2 v = __builtin_bit_cast(h2, t) - off;  // exact small integers
+  v = v * s;                               // one rounding
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ h2 scale_h2(uint32_t s16) {
+  return __builtin_bit_cast(h2, (s16 & 0xffffu) | (s16 << 16));
+}
+
+// Q8_0: 8 int8 (w0 bytes then w1 bytes, element order kept) times s.
+__device__ __forceinline__ uint4 dq8(uint32_t w0, uint32_t w1, h2 s) {
+  const h2 off = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+  const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;  // q + 128
+  return make_uint4(dq_pair(u8pair_f16(u0, 0), off, s), dq_pair(u8pair_f16(u0, 1), off, s),
+                    dq_pair(u8pair_f16(u1, 0), off, s), dq_pair(u8pair_f16(u1, 1), off, s));
+}
+
+// Q4_0: the low (hi = false) or high nibbles of the 8 bytes w0, w1 times s.
+// Byte j of a block holds element j (low nibble) and element j + 16 (high).
+__device__ __forceinline__ uint4 dq4(uint32_t w0, uint32_t w1, bool hi, h2 s) {
+  const h2 off = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+  const uint32_t n0 = (hi ? w0 >> 4 : w0) & 0x0f0f0f0fu;
+  const uint32_t n1 = (hi ? w1 >> 4 : w1) & 0x0f0f0f0fu;
+  return make_uint4(dq_pair(u8pair_f16(n0, 0), off, s), dq_pair(u8pair_f16(n0, 1), off, s),
+                    dq_pair(u8pair_f16(n1, 0), off, s), dq_pair(u8pair_f16(n1, 1), off, s));
+}
+
+// Activation element in the MFMA input format of a weight format: bf16 next
+// to bf16 weights, fp16 next to decoded quantized weights.
+template <int FMT>
+__device__ __forceinline__ uint16_t act16(float v) {
+  if constexpr (FMT == W_BF16) return f32_to_bf16(v);
+  else return f32_to_f16_bits(v);
+}
+
 // y[s][b][n] = sum over split s of k of W[n][k] * x[b][k]   (b < B <= 16)
 struct GemvArgs {
   SegTable w;
@@ -140,6 +192,10 @@ struct GemvArgs {
 };
 
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t st);
+
+// Quantized [rows][K] matrix (fmt Q8_0 / Q4_0) -> bf16 [rows][K].
+hipError_t launch_dequant_bf16(const void* src, int fmt, int rows, int K, uint16_t* dst,
+                               hipStream_t st);
 
 // LM head + greedy argmax over the vocabulary.
 hipError_t launch_lmhead_argmax(const uint16_t* lm, int vocab, const uint16_t* z, int B,
@@ -164,6 +220,7 @@ hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w
 
 // The whole proposal pass as one persistent kernel (plus a small init kernel).
 struct PassLaunch {
+  int fmt;                 // WFormat of the layer matrices (bytes behind the pointers)
   const uint16_t* wq[L];
   const uint16_t* wk[L];
   const uint16_t* wv[L];

@@ -72,26 +72,145 @@ __device__ __forceinline__ f32x4 reduce_waves(f32x4 acc, f32x4 (*red)[64], int w
   return acc;
 }
 
+// The matrix segment holding rows row0 .. row0+15 (segments are whole
+// multiples of 16 rows): its buffer, its row count and row0 inside it.
+struct SegRef {
+  const uint8_t* base;
+  int rows, row0;
+};
+
+__device__ __forceinline__ SegRef seg_ref(const SegTable& t, int row0) {
+  int seg = 0, prev = 0;
+  for (int i = 0; i + 1 < t.nseg; ++i)
+    if (row0 >= t.row_end[i]) { seg = i + 1; prev = t.row_end[i]; }
+  return SegRef{static_cast<const uint8_t*>(t.ptr[seg]), t.row_end[seg] - prev, row0 - prev};
+}
+
+template <int FMT> struct KPerLoad;  // k covered by one 16-byte load of all four lane groups
+template <> struct KPerLoad<W_BF16> { static constexpr int v = 32; };
+template <> struct KPerLoad<W_Q8_0> { static constexpr int v = 64; };
+template <> struct KPerLoad<W_Q4_0> { static constexpr int v = 128; };
+
+// k offset (from the wave's kbeg) of the i-th 8-element activation group of
+// lane group g, matching the weight slots of each format:
+//   bf16 load i -> k = 32 i + 8 g;  Q8_0 load i -> 16 elements at 64 i + 16 g;
+//   Q4_0 load i -> the 32-element quant block at 128 i + 32 g.
+template <int FMT>
+__device__ __forceinline__ int xslot(int i, int g) {
+  if constexpr (FMT == W_BF16) return 32 * i + 8 * g;
+  else if constexpr (FMT == W_Q8_0) return 64 * (i >> 1) + 16 * g + 8 * (i & 1);
+  else return 128 * (i >> 2) + 32 * g + 8 * (i & 3);
+}
+
+// 8 bf16 -> 8 fp16 (round to nearest even).
+__device__ __forceinline__ uint4 bf16x8_to_f16(uint4 v) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
+    w[i] = static_cast<uint32_t>(f32_to_f16_bits(lo)) | (static_cast<uint32_t>(f32_to_f16_bits(hi)) << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // out[split][b][n] for one 16-row tile; grid = (N/16, S), block = NW waves.
-template <int NW, int KBW>
-__global__ __launch_bounds__(NW * 64) void k_gemv_bf16(GemvArgs a) {
+// Quantized weights are decoded to fp16 in registers (the same slot scheme
+// and decode as the pass kernel) and run on MFMA f16 against the
+// activations converted to fp16.
+template <int FMT, int NW, int KBW>
+__global__ __launch_bounds__(NW * 64) void k_gemv(GemvArgs a) {
   __shared__ f32x4 red[NW > 1 ? NW - 1 : 1][64];
+  constexpr int NX = 4 * KBW;                           // 8-element activation groups per lane
+  constexpr int NL = KBW * 128 / KPerLoad<FMT>::v;      // 16-byte weight loads per lane
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int row0 = blockIdx.x * 16;
-  const uint16_t* wrow = seg_row(a.w, row0, a.K) + static_cast<size_t>(r) * a.K;
+  const SegRef sr = seg_ref(a.w, blockIdx.x * 16);
+  const int row = sr.row0 + r;
   const bool xv = r < a.B;
   const uint16_t* xrow = a.x + static_cast<size_t>(xv ? r : 0) * a.x_stride;
   const int kbeg = (blockIdx.y * NW + wave) * (KBW * 128);
-  uint4 w[4 * KBW], x[4 * KBW];
-  load_w<KBW>(w, wrow, kbeg, g);
-  load_x<KBW>(x, xrow, xv, kbeg, g);
+  const size_t rk = static_cast<size_t>(row) * a.K;
+  const size_t sb = static_cast<size_t>(row) * (a.K / 32) + kbeg / 32;
+  uint4 w[NL];
+  uint32_t sc[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    if constexpr (FMT == W_BF16) {
+      w[i] = ld16_stream(reinterpret_cast<const uint16_t*>(sr.base) + rk + kbeg + 32 * i + 8 * g);
+      sc[i] = 0;
+    } else if constexpr (FMT == W_Q8_0) {
+      w[i] = ld16_stream(reinterpret_cast<const uint16_t*>(sr.base + rk + kbeg + 64 * i + 16 * g));
+      sc[i] = *reinterpret_cast<const uint16_t*>(sr.base + static_cast<size_t>(sr.rows) * a.K +
+                                                 2 * (sb + 2 * i + (g >> 1)));
+    } else {
+      w[i] = ld16_stream(reinterpret_cast<const uint16_t*>(sr.base + (rk + kbeg) / 2 + 64 * i + 16 * g));
+      sc[i] = *reinterpret_cast<const uint16_t*>(sr.base + static_cast<size_t>(sr.rows) * a.K / 2 +
+                                                 2 * (sb + 4 * i + g));
+    }
+  }
+  uint4 x[NX];
+#pragma unroll
+  for (int i = 0; i < NX; ++i)
+    x[i] = xv ? ld16(xrow + kbeg + xslot<FMT>(i, g)) : make_uint4(0, 0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
-  f32x4 acc = mma_chain<KBW>(w, x);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    if constexpr (FMT == W_BF16) {
+      acc = mfma_bf16(w[i], x[i], acc);
+    } else if constexpr (FMT == W_Q8_0) {
+      const h2 s2 = scale_h2(sc[i]);
+      acc = mfma_f16(dq8(w[i].x, w[i].y, s2), bf16x8_to_f16(x[2 * i]), acc);
+      acc = mfma_f16(dq8(w[i].z, w[i].w, s2), bf16x8_to_f16(x[2 * i + 1]), acc);
+    } else {
+      const h2 s2 = scale_h2(sc[i]);
+      acc = mfma_f16(dq4(w[i].x, w[i].y, false, s2), bf16x8_to_f16(x[4 * i]), acc);
+      acc = mfma_f16(dq4(w[i].z, w[i].w, false, s2), bf16x8_to_f16(x[4 * i + 1]), acc);
+      acc = mfma_f16(dq4(w[i].x, w[i].y, true, s2), bf16x8_to_f16(x[4 * i + 2]), acc);
+      acc = mfma_f16(dq4(w[i].z, w[i].w, true, s2), bf16x8_to_f16(x[4 * i + 3]), acc);
+    }
+  }
   acc = reduce_waves<NW>(acc, red, wave, lane);
   if (wave == 0 && xv) {
-    float* o = a.out + (static_cast<size_t>(blockIdx.y) * a.B + r) * a.N + row0 + 4 * g;
+    float* o = a.out + (static_cast<size_t>(blockIdx.y) * a.B + r) * a.N + blockIdx.x * 16 + 4 * g;
     *reinterpret_cast<f32x4*>(o) = acc;
+  }
+}
+
+// Quantized matrix -> bf16 copy (value q * scale, rounded once), for the
+// many-row GEMM path.  One thread per 8 output elements.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_dequant_bf16(const uint8_t* src, int rows, int K,
+                                                      uint16_t* dst) {
+  const size_t n8 = static_cast<size_t>(rows) * K / 8;
+  for (size_t e = blockIdx.x * 256ull + threadIdx.x; e < n8; e += static_cast<size_t>(gridDim.x) * 256) {
+    const size_t k0 = e * 8;  // first element (row-major)
+    const size_t blk = k0 / 32;
+    const float s = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(
+        src + (FMT == W_Q8_0 ? static_cast<size_t>(rows) * K : static_cast<size_t>(rows) * K / 2) + 2 * blk));
+    float v[8];
+    if constexpr (FMT == W_Q8_0) {
+      const uint2 q = *reinterpret_cast<const uint2*>(src + k0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t word = i < 4 ? q.x : q.y;
+        v[i] = static_cast<float>(static_cast<int8_t>(word >> (8 * (i & 3)))) * s;
+      }
+    } else {
+      // element j of a block: byte j % 16, low nibble if j < 16 else high
+      const int j0 = static_cast<int>(k0 % 32);
+      const uint8_t* by = src + blk * 16 + (j0 & 15);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int nib = j0 < 16 ? (by[i] & 15) : (by[i] >> 4);
+        v[i] = static_cast<float>(nib - 8) * s;
+      }
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(dst + k0) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -221,17 +340,32 @@ __global__ void k_verify(const int32_t* cand, const int32_t* target, int k, int3
 }  // namespace
 
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t st) {
-  if (a.fmt != W_BF16) return hipErrorInvalidValue;
   if (a.B < 1 || a.B > GEMV_ROWS || a.N % 16 || a.K % 128) return hipErrorInvalidValue;
-  const int kblocks = a.K / 128;
-  constexpr int NW = 4;
-  if (kblocks % (NW * 5) == 0 && a.S == kblocks / (NW * 5)) {
-    hipLaunchKernelGGL((k_gemv_bf16<NW, 5>), dim3(a.N / 16, a.S), dim3(NW * 64), 0, st, a);
-  } else if (kblocks % (NW * 4) == 0 && a.S == kblocks / (NW * 4)) {
-    hipLaunchKernelGGL((k_gemv_bf16<NW, 4>), dim3(a.N / 16, a.S), dim3(NW * 64), 0, st, a);
-  } else {
-    return hipErrorInvalidValue;
+  constexpr int NW = 4, KBW = 5;  // 4 waves x 640 k per block and split
+  if ((a.K / 128) % (NW * KBW) != 0 || a.S != a.K / (128 * NW * KBW)) return hipErrorInvalidValue;
+  const dim3 grid(a.N / 16, a.S), block(NW * 64);
+  switch (a.fmt) {
+    case W_BF16: hipLaunchKernelGGL((k_gemv<W_BF16, NW, KBW>), grid, block, 0, st, a); break;
+    case W_Q8_0: hipLaunchKernelGGL((k_gemv<W_Q8_0, NW, KBW>), grid, block, 0, st, a); break;
+    case W_Q4_0: hipLaunchKernelGGL((k_gemv<W_Q4_0, NW, KBW>), grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_bf16(const void* src, int fmt, int rows, int K, uint16_t* dst,
+                               hipStream_t st) {
+  if (rows < 0 || K % 32) return hipErrorInvalidValue;
+  if (rows == 0) return hipSuccess;
+  const size_t n8 = static_cast<size_t>(rows) * K / 8;
+  const int grid = static_cast<int>(n8 / 256 < 4096 ? (n8 + 255) / 256 : 4096);
+  const uint8_t* s8 = static_cast<const uint8_t*>(src);
+  if (fmt == W_Q8_0)
+    hipLaunchKernelGGL(k_dequant_bf16<W_Q8_0>, dim3(grid), dim3(256), 0, st, s8, rows, K, dst);
+  else if (fmt == W_Q4_0)
+    hipLaunchKernelGGL(k_dequant_bf16<W_Q4_0>, dim3(grid), dim3(256), 0, st, s8, rows, K, dst);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

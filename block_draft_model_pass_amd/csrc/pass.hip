@@ -270,17 +270,107 @@ __device__ __forceinline__ void load_tile(uint4 (&w)[NMAX], const uint16_t* wrow
   }
 }
 
-// acc over the same k slots, activations from LDS row xr (zero if !xv).
+// acc over the same k slots, activations from LDS row xr.  MFMA column n
+// only depends on the activation lanes of column n, so lanes past the
+// block's rows read a valid row (see xrow) and their columns are ignored.
 template <int NMAX>
-__device__ __forceinline__ f32x4 mma_tile(const uint4 (&w)[NMAX], const uint16_t* xr, bool xv,
-                                          int kbeg, int g, int nw) {
+__device__ __forceinline__ f32x4 mma_tile(const uint4 (&w)[NMAX], const uint16_t* xr, int kbeg,
+                                          int g, int nw) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < NMAX; ++i) {
-    if (i < nw) {
-      const uint4 x = xv ? *reinterpret_cast<const uint4*>(xr + kbeg + 32 * i + 8 * g)
-                         : make_uint4(0, 0, 0, 0);
-      acc = mfma_bf16(w[i], x, acc);
+  for (int i = 0; i < NMAX; ++i)
+    if (i < nw) acc = mfma_bf16(w[i], *reinterpret_cast<const uint4*>(xr + kbeg + 32 * i + 8 * g), acc);
+  return acc;
+}
+
+// LDS activation row fed to MFMA column r: r itself for the block's rows,
+// else row 0 (a finite stand-in whose output column is never used).
+__device__ __forceinline__ int xrow(int r, int B) { return r < B ? r : 0; }
+
+// ---------------------------------------------------------------- weight formats
+
+// One lane's share of a weight tile: N 16-byte loads.
+//   bf16 : load i holds k = kbeg + 32 i + 8 g .. +8 (one MFMA bf16).
+//   Q8_0 : load i holds 16 int8 at k = kbeg + 64 i + 16 g (two MFMAs, slots
+//          + 8 m), all inside quant block kbeg/32 + 2 i + g/2.
+//   Q4_0 : load i is the whole quant block kbeg/32 + 4 i + g (four MFMAs:
+//          elements 8 m .. 8 m + 7 of the block).
+// A quantized load carries its block's fp16 scale (raw bits, splatted at use
+// so that the load stays asynchronous); activations use the same k slots.
+template <int FMT> struct KPerLoad;  // k covered by one load of all four lane groups
+template <> struct KPerLoad<W_BF16> { static constexpr int v = 32; };
+template <> struct KPerLoad<W_Q8_0> { static constexpr int v = 64; };
+template <> struct KPerLoad<W_Q4_0> { static constexpr int v = 128; };
+
+template <int FMT, int N>
+struct WTile {
+  uint4 q[N];
+  uint32_t s[FMT == W_BF16 ? 1 : N];
+};
+
+struct WMat {
+  const void* base;  // the matrix buffer in its storage format
+  int rows, K;       // [rows][K]
+};
+
+__device__ __forceinline__ uint4 ldb(const uint8_t* p) {
+  return __builtin_bit_cast(
+      uint4, __builtin_nontemporal_load(reinterpret_cast<const GA u32x4*>(reinterpret_cast<uintptr_t>(p))));
+}
+
+// nl loads of row `row` from kbeg; every element defined on every path.
+template <int FMT, int N>
+__device__ __forceinline__ void load_wt(WTile<FMT, N>& t, WMat m, int row, int kbeg, int g, int nl,
+                                        bool valid) {
+  const uint8_t* b = static_cast<const uint8_t*>(m.base);
+  const size_t rk = static_cast<size_t>(row) * m.K;
+  const size_t sb = static_cast<size_t>(row) * (m.K / 32) + kbeg / 32;  // first scale of the row range
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const bool on = valid && i < nl;
+    if constexpr (FMT == W_BF16) {
+      t.q[i] = on ? ldb(b + 2 * (rk + kbeg + 32 * i + 8 * g)) : make_uint4(0, 0, 0, 0);
+    } else if constexpr (FMT == W_Q8_0) {
+      t.q[i] = on ? ldb(b + rk + kbeg + 64 * i + 16 * g) : make_uint4(0, 0, 0, 0);
+      t.s[i] = on ? gld<uint16_t>(b + static_cast<size_t>(m.rows) * m.K + 2 * (sb + 2 * i + (g >> 1)))
+                  : 0u;
+    } else {
+      t.q[i] = on ? ldb(b + (rk + kbeg) / 2 + 64 * i + 16 * g) : make_uint4(0, 0, 0, 0);
+      t.s[i] = on ? gld<uint16_t>(b + static_cast<size_t>(m.rows) * m.K / 2 + 2 * (sb + 4 * i + g))
+                  : 0u;
+    }
+  }
+  if constexpr (FMT == W_BF16) t.s[0] = 0u;
+}
+
+template <int FMT, int N>
+__device__ __forceinline__ f32x4 mma_wt(const WTile<FMT, N>& t, const uint16_t* xr, int kbeg, int g,
+                                        int nl) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i < nl) {
+      if constexpr (FMT == W_BF16) {
+        acc = mfma_bf16(t.q[i], *reinterpret_cast<const uint4*>(xr + kbeg + 32 * i + 8 * g), acc);
+      } else if constexpr (FMT == W_Q8_0) {
+        const h2 sc = scale_h2(t.s[i]);
+        const uint16_t* xp = xr + kbeg + 64 * i + 16 * g;
+        const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
+        const uint4 x1 = *reinterpret_cast<const uint4*>(xp + 8);
+        acc = mfma_f16(dq8(t.q[i].x, t.q[i].y, sc), x0, acc);
+        acc = mfma_f16(dq8(t.q[i].z, t.q[i].w, sc), x1, acc);
+      } else {
+        const h2 sc = scale_h2(t.s[i]);
+        const uint16_t* xp = xr + kbeg + 128 * i + 32 * g;
+        const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
+        const uint4 x1 = *reinterpret_cast<const uint4*>(xp + 8);
+        const uint4 x2 = *reinterpret_cast<const uint4*>(xp + 16);
+        const uint4 x3 = *reinterpret_cast<const uint4*>(xp + 24);
+        acc = mfma_f16(dq4(t.q[i].x, t.q[i].y, false, sc), x0, acc);
+        acc = mfma_f16(dq4(t.q[i].z, t.q[i].w, false, sc), x1, acc);
+        acc = mfma_f16(dq4(t.q[i].x, t.q[i].y, true, sc), x2, acc);
+        acc = mfma_f16(dq4(t.q[i].z, t.q[i].w, true, sc), x3, acc);
+      }
     }
   }
   return acc;
@@ -293,11 +383,13 @@ __device__ __forceinline__ f32x4 group_sum(Smem& s, int w0, int n, int lane) {
   return acc;
 }
 
-// x[b][k] = bf16(h[b][k] * rsqrt(mean_k h^2 + eps) * gain[k]) for b < B, into
+// x[b][k] = h[b][k] * rsqrt(mean_k h^2 + eps) * gain[k] for b < B, rounded to
+// the activation format XF (bf16, or fp16 beside quantized weights), into
 // LDS rows of stride H + pad.  np per-tile sums of squares are reduced in a
 // fixed order.  Every load (h and the sums) is issued in one round.
 constexpr int XN4 = MAXB * (H / 4) / NTHR;  // float4 of h per thread (10)
 
+template <int XF>
 __device__ __forceinline__ void build_x_norm(const PassArgs& a, Smem& s, int ver, int np,
                                              const uint16_t* gain) {
   const int tid = otid(), wave = tid >> 6, lane = tid & 63;
@@ -331,10 +423,10 @@ __device__ __forceinline__ void build_x_norm(const PassArgs& a, Smem& s, int ver
       const int b = e / (H / 4), k = (e % (H / 4)) * 4;
       const float sc = s.scal[b];
       const uint2 gg = gld<uint2>(gain + k);
-      const uint16_t y0 = f32_to_bf16(hv[u].x * sc * bf16_to_f32(gg.x & 0xffff));
-      const uint16_t y1 = f32_to_bf16(hv[u].y * sc * bf16_to_f32(gg.x >> 16));
-      const uint16_t y2 = f32_to_bf16(hv[u].z * sc * bf16_to_f32(gg.y & 0xffff));
-      const uint16_t y3 = f32_to_bf16(hv[u].w * sc * bf16_to_f32(gg.y >> 16));
+      const uint16_t y0 = act16<XF>(hv[u].x * sc * bf16_to_f32(gg.x & 0xffff));
+      const uint16_t y1 = act16<XF>(hv[u].y * sc * bf16_to_f32(gg.x >> 16));
+      const uint16_t y2 = act16<XF>(hv[u].z * sc * bf16_to_f32(gg.y & 0xffff));
+      const uint16_t y3 = act16<XF>(hv[u].w * sc * bf16_to_f32(gg.y >> 16));
       *reinterpret_cast<uint2*>(s.x + b * XS + k) =
           make_uint2(y0 | (static_cast<uint32_t>(y1) << 16), y2 | (static_cast<uint32_t>(y3) << 16));
     }
@@ -387,32 +479,41 @@ __device__ __forceinline__ void residual_epilogue(const PassArgs& a, f32x4 acc, 
 
 // Work of one block for the QKV phase: tiles 2w and 2w+1 of the 448 fused
 // q|k|v row tiles; wave v takes tile 2w + v/4 and k quarter v%4 (640 k).
-__device__ __forceinline__ const uint16_t* qkv_row(const PassArgs& a, int l, int tile, int r) {
-  const int row = tile * 16 + r;
-  if (row < NQ * D) return a.tab->wq[l] + static_cast<size_t>(row) * H;
-  if (row < NQ * D + NKV * D) return a.tab->wk[l] + static_cast<size_t>(row - NQ * D) * H;
-  return a.tab->wv[l] + static_cast<size_t>(row - NQ * D - NKV * D) * H;
+// Tiles never straddle the q / k / v matrices (6144 and 512 rows).
+__device__ __forceinline__ WMat qkv_mat(const PassArgs& a, int l, int tile, int& row0) {
+  const int r0 = tile * 16;
+  if (r0 < NQ * D) { row0 = r0; return WMat{a.tab->wq[l], NQ * D, H}; }
+  if (r0 < NQ * D + NKV * D) { row0 = r0 - NQ * D; return WMat{a.tab->wk[l], NKV * D, H}; }
+  row0 = r0 - NQ * D - NKV * D;
+  return WMat{a.tab->wv[l], NKV * D, H};
 }
 
 __device__ __forceinline__ bool qkv_has(int w) { return w < QKV_N / 32; }
 
-__device__ __forceinline__ void qkv_prefetch(const PassArgs& a, int l, uint4 (&W)[20], bool go) {
+template <int FMT> using QkvTile = WTile<FMT, 640 / KPerLoad<FMT>::v>;
+
+template <int FMT>
+__device__ __forceinline__ void qkv_prefetch(const PassArgs& a, int l, QkvTile<FMT>& W, bool go) {
   const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
   const bool has = qkv_has(w);
-  const int tile = has ? 2 * w + (wave >> 2) : 0;
-  load_tile<20>(W, qkv_row(a, l, tile, lane & 15), (wave & 3) * 640, lane >> 4, 20, go && has);
+  int row0;
+  const WMat m = qkv_mat(a, l, has ? 2 * w + (wave >> 2) : 0, row0);
+  constexpr int N = 640 / KPerLoad<FMT>::v;
+  load_wt<FMT, N>(W, m, row0 + (lane & 15), (wave & 3) * 640, lane >> 4, N, go && has);
 }
 
-__device__ __forceinline__ void qkv_phase(const PassArgs& a, Smem& s, int l, int np, uint4 (&W)[20]) {
+template <int FMT>
+__device__ __forceinline__ void qkv_phase(const PassArgs& a, Smem& s, int l, int np, QkvTile<FMT>& W) {
   const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
   const int r = lane & 15, g = lane >> 4;
   const bool has = qkv_has(w);
-  if (wave == 0) qkv_prefetch(a, l, W, true);
-  if (has) build_x_norm(a, s, 2 * l, np, a.tab->in_norm[l]);
+  if (wave == 0) qkv_prefetch<FMT>(a, l, W, true);
+  if (has) build_x_norm<FMT>(a, s, 2 * l, np, a.tab->in_norm[l]);
   if (has) {
     const int tile = 2 * w + (wave >> 2);
     constexpr int XS = H + XS_PAD;
-    f32x4 acc = mma_tile<20>(W, s.x + r * XS, r < a.B, (wave & 3) * 640, g, 20);
+    constexpr int N = 640 / KPerLoad<FMT>::v;
+    f32x4 acc = mma_wt<FMT, N>(W, s.x + xrow(r, a.B) * XS, (wave & 3) * 640, g, N);
     s.red[wave][lane] = acc;
     lds_sync();
     if ((wave & 3) == 0) {
@@ -719,6 +820,7 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KV
 // pairs of head dims.
 constexpr int MQ = 32;  // chunks per quarter (nch <= 128)
 
+template <int FMT>
 __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
   const int ngroup = NKV * a.nqt * 16;
   const int w = blockIdx.x;
@@ -783,8 +885,8 @@ __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
           acc1 += s.mw[256 + q2 * 256 + d2 + 1];
         }
         const int bi = r / G, hl = r % G;
-        const uint32_t pk = static_cast<uint32_t>(f32_to_bf16(acc0 * s.scal[0])) |
-                            (static_cast<uint32_t>(f32_to_bf16(acc1 * s.scal[0])) << 16);
+        const uint32_t pk = static_cast<uint32_t>(act16<FMT>(acc0 * s.scal[0])) |
+                            (static_cast<uint32_t>(act16<FMT>(acc1 * s.scal[0])) << 16);
         st_coh32(reinterpret_cast<uint32_t*>(a.o16 + l * OSTRIDE + static_cast<size_t>(bi) * NQ * D +
                                              (j * G + hl) * D + d2),
                  pk);
@@ -796,21 +898,27 @@ __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
 
 // O projection: block w < 160 owns row tile w; wave v takes k in
 // [768 v, 768 v + 768) (6 k blocks).
-__device__ __forceinline__ void o_prefetch(const PassArgs& a, int l, uint4 (&W)[24], bool go) {
+template <int FMT> using OTile = WTile<FMT, 768 / KPerLoad<FMT>::v>;
+
+template <int FMT>
+__device__ __forceinline__ void o_prefetch(const PassArgs& a, int l, OTile<FMT>& W, bool go) {
   const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
   const bool has = w < NT_H;
-  load_tile<24>(W, a.tab->wo[l] + static_cast<size_t>((has ? w : 0) * 16 + (lane & 15)) * (NQ * D),
-                wave * 768, lane >> 4, 24, go && has);
+  constexpr int N = 768 / KPerLoad<FMT>::v;
+  load_wt<FMT, N>(W, WMat{a.tab->wo[l], H, NQ * D}, (has ? w : 0) * 16 + (lane & 15), wave * 768,
+                  lane >> 4, N, go && has);
 }
 
-__device__ __forceinline__ void o_phase(const PassArgs& a, Smem& s, int l, uint4 (&W)[24]) {
+template <int FMT>
+__device__ __forceinline__ void o_phase(const PassArgs& a, Smem& s, int l, OTile<FMT>& W) {
   const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
   const int r = lane & 15, g = lane >> 4;
   if (w < NT_H) {
-    if (wave == 0) o_prefetch(a, l, W, true);
+    if (wave == 0) o_prefetch<FMT>(a, l, W, true);
     copy_x(a, s, a.o16 + l * OSTRIDE, NQ * D);
     constexpr int XS = NQ * D + XS_PAD;
-    f32x4 acc = mma_tile<24>(W, s.x + r * XS, r < a.B, wave * 768, g, 24);
+    constexpr int N = 768 / KPerLoad<FMT>::v;
+    f32x4 acc = mma_wt<FMT, N>(W, s.x + xrow(r, a.B) * XS, wave * 768, g, N);
     s.red[wave][lane] = acc;
     lds_sync();
     if (wave == 0) residual_epilogue(a, group_sum(s, 0, NWAVE, lane), w, r, g, 2 * l);
@@ -820,28 +928,33 @@ __device__ __forceinline__ void o_phase(const PassArgs& a, Smem& s, int l, uint4
 
 // Gate/up: 480 tile pairs; round q handles pair w + q * grid.  Waves 0-3 the
 // gate tile's k quarters, waves 4-7 the up tile's.
-__device__ __forceinline__ void gu_prefetch(const PassArgs& a, int l, int pair, uint4 (&W)[20],
+template <int FMT> using GuTile = WTile<FMT, 640 / KPerLoad<FMT>::v>;
+
+template <int FMT>
+__device__ __forceinline__ void gu_prefetch(const PassArgs& a, int l, int pair, GuTile<FMT>& W,
                                             bool go) {
   const int wave = otid() >> 6, lane = otid() & 63;
   const bool has = pair < F / 16;
-  const uint16_t* m = wave < 4 ? a.tab->wg[l] : a.tab->wu[l];
-  load_tile<20>(W, m + static_cast<size_t>((has ? pair : 0) * 16 + (lane & 15)) * H,
-                (wave & 3) * 640, lane >> 4, 20, go && has);
+  constexpr int N = 640 / KPerLoad<FMT>::v;
+  load_wt<FMT, N>(W, WMat{wave < 4 ? a.tab->wg[l] : a.tab->wu[l], F, H},
+                  (has ? pair : 0) * 16 + (lane & 15), (wave & 3) * 640, lane >> 4, N, go && has);
 }
 
-__device__ __forceinline__ void gu_phase(const PassArgs& a, Smem& s, int l, int np, uint4 (&W)[20]) {
+template <int FMT>
+__device__ __forceinline__ void gu_phase(const PassArgs& a, Smem& s, int l, int np, GuTile<FMT>& W) {
   const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
   const int r = lane & 15, g = lane >> 4;
   const bool has = w < F / 16;
-  if (wave == 0) gu_prefetch(a, l, w, W, true);
-  if (has) build_x_norm(a, s, 2 * l + 1, np, a.tab->post_norm[l]);
+  if (wave == 0) gu_prefetch<FMT>(a, l, w, W, true);
+  if (has) build_x_norm<FMT>(a, s, 2 * l + 1, np, a.tab->post_norm[l]);
   constexpr int XS = H + XS_PAD;
+  constexpr int N = 640 / KPerLoad<FMT>::v;
   for (int pair = w; pair < F / 16; pair += gridDim.x) {
-    f32x4 acc = mma_tile<20>(W, s.x + r * XS, r < a.B, (wave & 3) * 640, g, 20);
+    f32x4 acc = mma_wt<FMT, N>(W, s.x + xrow(r, a.B) * XS, (wave & 3) * 640, g, N);
     s.red[wave][lane] = acc;
     lds_sync();
     const int nxt = pair + gridDim.x;
-    if (nxt < F / 16) gu_prefetch(a, l, nxt, W, true);  // next round's tiles
+    if (nxt < F / 16) gu_prefetch<FMT>(a, l, nxt, W, true);  // next round's tiles
     if (wave == 0) {
       const f32x4 ag = group_sum(s, 0, 4, lane);
       const f32x4 au = group_sum(s, 4, 4, lane);
@@ -850,7 +963,7 @@ __device__ __forceinline__ void gu_phase(const PassArgs& a, Smem& s, int l, int 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float z = ag[i];
-          o[i] = f32_to_bf16(z / (1.0f + __expf(-z)) * au[i]);
+          o[i] = act16<FMT>(z / (1.0f + __expf(-z)) * au[i]);
         }
         st_coh64(a.u16 + l * USTRIDE + static_cast<size_t>(r) * F + pair * 16 + 4 * g,
                  static_cast<uint64_t>(o[0] | (static_cast<uint32_t>(o[1]) << 16)) |
@@ -862,37 +975,43 @@ __device__ __forceinline__ void gu_phase(const PassArgs& a, Smem& s, int l, int 
   wait_stores();
 }
 
-// Down projection: block w < 160 owns row tile w; waves 0-3 take 8 k blocks
-// each (k < 4096), waves 4-7 take 7 (k >= 4096).
-__device__ __forceinline__ void down_range(int wave, int& kbeg, int& nw) {
+// Down projection: block w < 160 owns row tile w; waves 0-3 take k ranges of
+// 1024 (k < 4096), waves 4-7 ranges of 896 (k >= 4096).
+__device__ __forceinline__ void down_range(int wave, int& kbeg, int& klen) {
   if (wave < 4) {
     kbeg = wave * 1024;
-    nw = 32;
+    klen = 1024;
   } else {
     kbeg = 4096 + (wave - 4) * 896;
-    nw = 28;
+    klen = 896;
   }
 }
 
-__device__ __forceinline__ void down_prefetch(const PassArgs& a, int l, uint4 (&W)[32], bool go) {
+template <int FMT> using DownTile = WTile<FMT, 1024 / KPerLoad<FMT>::v>;
+
+template <int FMT>
+__device__ __forceinline__ void down_prefetch(const PassArgs& a, int l, DownTile<FMT>& W, bool go) {
   const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
   const bool has = w < NT_H;
-  int kbeg, nw;
-  down_range(wave, kbeg, nw);
-  load_tile<32>(W, a.tab->wd[l] + static_cast<size_t>((has ? w : 0) * 16 + (lane & 15)) * F, kbeg,
-                lane >> 4, nw, go && has);
+  int kbeg, klen;
+  down_range(wave, kbeg, klen);
+  constexpr int N = 1024 / KPerLoad<FMT>::v;
+  load_wt<FMT, N>(W, WMat{a.tab->wd[l], H, F}, (has ? w : 0) * 16 + (lane & 15), kbeg, lane >> 4,
+                  klen / KPerLoad<FMT>::v, go && has);
 }
 
-__device__ __forceinline__ void down_phase(const PassArgs& a, Smem& s, int l, uint4 (&W)[32]) {
+template <int FMT>
+__device__ __forceinline__ void down_phase(const PassArgs& a, Smem& s, int l, DownTile<FMT>& W) {
   const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
   const int r = lane & 15, g = lane >> 4;
   if (w < NT_H) {
-    if (wave == 0) down_prefetch(a, l, W, true);
+    if (wave == 0) down_prefetch<FMT>(a, l, W, true);
     copy_x(a, s, a.u16 + l * USTRIDE, F);
-    int kbeg, nw;
-    down_range(wave, kbeg, nw);
+    int kbeg, klen;
+    down_range(wave, kbeg, klen);
     constexpr int XS = F + XS_PAD;
-    f32x4 acc = mma_tile<32>(W, s.x + r * XS, r < a.B, kbeg, g, nw);
+    constexpr int N = 1024 / KPerLoad<FMT>::v;
+    f32x4 acc = mma_wt<FMT, N>(W, s.x + xrow(r, a.B) * XS, kbeg, g, klen / KPerLoad<FMT>::v);
     s.red[wave][lane] = acc;
     lds_sync();
     if (wave == 0) residual_epilogue(a, group_sum(s, 0, NWAVE, lane), w, r, g, 2 * l + 1);
@@ -924,7 +1043,7 @@ __device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, uin
   const int r = lane & 15, g = lane >> 4;
   const int ntiles = a.vocab / 16, npairs = (ntiles + 1) / 2;
   if (wave == 0) lm_prefetch(a, w, W, true);
-  build_x_norm(a, s, 2 * L, np, a.final_norm);
+  build_x_norm<W_BF16>(a, s, 2 * L, np, a.final_norm);
   constexpr int XS = H + XS_PAD;
   if (w == 0 && a.hidden) {
     for (int e = otid(); e < a.B * H; e += NTHR)
@@ -932,7 +1051,7 @@ __device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, uin
   }
   // mask row r + 1 of the block feeds MFMA column r
   const bool xv = r + 1 < a.B;
-  const uint16_t* xr = s.x + (r + 1) * XS;
+  const uint16_t* xr = s.x + (xv ? r + 1 : 1) * XS;
   uint64_t best = 0;
   uint4 W2[20];
   int p = w;
@@ -941,7 +1060,7 @@ __device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, uin
     const int pn = p + gridDim.x;
     lm_prefetch(a, pn, W2, pn < npairs);
     const int tile = 2 * p + (wave >> 2);
-    f32x4 acc = tile < ntiles ? mma_tile<20>(W, xr, xv, (wave & 3) * 640, g, 20)
+    f32x4 acc = tile < ntiles ? mma_tile<20>(W, xr, (wave & 3) * 640, g, 20)
                               : f32x4{0.f, 0.f, 0.f, 0.f};
     s.red[wave][lane] = acc;
     lds_sync();
@@ -968,7 +1087,7 @@ __device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, uin
     const int pn2 = p + gridDim.x;
     lm_prefetch(a, pn2, W, pn2 < npairs);
     const int tile2 = 2 * p + (wave >> 2);
-    acc = tile2 < ntiles ? mma_tile<20>(W2, xr, xv, (wave & 3) * 640, g, 20)
+    acc = tile2 < ntiles ? mma_tile<20>(W2, xr, (wave & 3) * 640, g, 20)
                          : f32x4{0.f, 0.f, 0.f, 0.f};
     s.red[wave][lane] = acc;
     lds_sync();
@@ -1016,46 +1135,51 @@ __device__ __forceinline__ void argmax_final(const PassArgs& a) {
   if (lane == 0) a.cand[wave] = static_cast<int32_t>(~static_cast<uint32_t>(best));
 }
 
+template <int FMT>
 __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
   __shared__ Smem s;
   const bool pre = (otid() >> 6) != 0;  // waves other than 0 prefetch before barriers
   unsigned bk = 0;  // barriers passed
-  uint4 Wq[20];
+  QkvTile<FMT> Wq;
+  uint4 Wl[20];     // LM head (bf16) slice, prefetched after the last layer
   // Layer 0 QKV weights stream while the grid lines up.
-  qkv_prefetch(a, 0, Wq, pre);
+  qkv_prefetch<FMT>(a, 0, Wq, pre);
   grid_sync(a, bk);  // h, ss, the RoPE table and the layer table come from the init kernel
   int np = 1;    // sums of squares of h: one entry per row from the init kernel
   for (int l = 0; l < L; ++l) {
-    qkv_phase(a, s, l, np, Wq);
+    qkv_phase<FMT>(a, s, l, np, Wq);
     KVRegs R0, R1;
     attn_prefetch(a, l, R0, R1, pre);
     grid_sync(a, bk);
     attn_phase(a, s, l, R0, R1);
     grid_sync(a, bk);
-    merge_phase(a, s, l);
-    uint4 Wo[24];
-    o_prefetch(a, l, Wo, pre);
+    merge_phase<FMT>(a, s, l);
+    OTile<FMT> Wo;
+    o_prefetch<FMT>(a, l, Wo, pre);
     grid_sync(a, bk);
-    o_phase(a, s, l, Wo);
-    uint4 Wg[20];
-    gu_prefetch(a, l, blockIdx.x, Wg, pre);
+    o_phase<FMT>(a, s, l, Wo);
+    GuTile<FMT> Wg;
+    gu_prefetch<FMT>(a, l, blockIdx.x, Wg, pre);
     grid_sync(a, bk);
-    gu_phase(a, s, l, NT_H, Wg);
-    uint4 Wd[32];
-    down_prefetch(a, l, Wd, pre);
+    gu_phase<FMT>(a, s, l, NT_H, Wg);
+    DownTile<FMT> Wd;
+    down_prefetch<FMT>(a, l, Wd, pre);
     grid_sync(a, bk);
-    down_phase(a, s, l, Wd);
-    if (l + 1 < L) qkv_prefetch(a, l + 1, Wq, pre);
-    else lm_prefetch(a, blockIdx.x, Wq, pre && a.B > 1);
+    down_phase<FMT>(a, s, l, Wd);
+    // Both prefetch targets are assigned on every iteration (zeros when
+    // idle), so neither carries a value around the loop.
+    const bool last = l + 1 == L;
+    qkv_prefetch<FMT>(a, last ? l : l + 1, Wq, pre && !last);
+    lm_prefetch(a, blockIdx.x, Wl, pre && last && a.B > 1);
     grid_sync(a, bk);
     np = NT_H;
   }
   if (a.B > 1) {
-    lm_phase(a, s, np, Wq);
+    lm_phase(a, s, np, Wl);
     grid_sync(a, bk);
     argmax_final(a);
   } else if (blockIdx.x == 0 && a.hidden) {
-    build_x_norm(a, s, 2 * L, np, a.final_norm);
+    build_x_norm<W_BF16>(a, s, 2 * L, np, a.final_norm);
     for (int e = otid(); e < H; e += NTHR) a.hidden[e] = s.x[e];
   }
 }
@@ -1144,6 +1268,7 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
   a.logits = q.logits;
   a.hidden = q.hidden;
   // every phase assumes at least one block per work item of its first round
+  if (q.fmt < W_BF16 || q.fmt > W_Q4_0) return hipErrorInvalidValue;
   if (q.nch < 1 || q.nch > 128 || q.grid < NKV * q.nch || q.grid < QKV_N / 32 ||
       q.grid < NKV * a.nqt * 16 || q.grid > 1024)
     return hipErrorInvalidValue;
@@ -1152,19 +1277,28 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
                      q.h, q.ss, q.rope, q.bar);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const void* kern = q.fmt == W_Q8_0   ? reinterpret_cast<const void*>(k_draft_pass<W_Q8_0>)
+                     : q.fmt == W_Q4_0 ? reinterpret_cast<const void*>(k_draft_pass<W_Q4_0>)
+                                       : reinterpret_cast<const void*>(k_draft_pass<W_BF16>);
   void* args[] = {&a};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_draft_pass), dim3(q.grid),
-                                    dim3(NTHR), args, 0, st);
+  return hipLaunchCooperativeKernel(kern, dim3(q.grid), dim3(NTHR), args, 0, st);
 }
 
 hipError_t draft_pass_max_grid(int device, int* grid) {
   int cus = 0, per = 0;
   hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
   if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void*>(k_draft_pass),
-                                                   NTHR, 0);
-  if (e != hipSuccess) return e;
-  *grid = cus * (per > 0 ? 1 : 0);
+  // one block per CU for every weight format's instantiation
+  const void* kerns[3] = {reinterpret_cast<const void*>(k_draft_pass<W_BF16>),
+                          reinterpret_cast<const void*>(k_draft_pass<W_Q8_0>),
+                          reinterpret_cast<const void*>(k_draft_pass<W_Q4_0>)};
+  int ok = 1;
+  for (const void* k : kerns) {
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k, NTHR, 0);
+    if (e != hipSuccess) return e;
+    ok = ok && per > 0;
+  }
+  *grid = ok ? cus : 0;
   return hipSuccess;
 }
 

@@ -1,0 +1,75 @@
+"""GPU parity of the quantized backbone (Q8_0 and Q4_0 storage of fc and the
+35 layer matrices; gains, embedding and LM head stay bf16) against the CPU
+oracle, which decodes every block exactly (scale * q in fp64).
+
+Same bars as the bf16 cases: ids exact where the oracle's top-2 margin
+exceeds 0.05; logits, hidden states, fused context and fp16 K/V within 2e-2
+per-row relative error.  The GPU decodes weights to fp16 (one rounding of
+q * scale, relative 2^-11) for the MFMA paths and to bf16 for the many-row
+GEMM path, well inside that bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_draft_model_pass_amd import synth
+from block_draft_model_pass_amd.device import DeviceWeights, Drafter, KVRing, to_device
+from oracle import dflash_oracle as O
+from test_parity_gpu import TOL, dec_bf16, end_to_end, ring_cells, row_rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", params=["q8_0", "q4_0"])
+def qset(request):
+    fmt = request.param
+    say(f"quantized weights {fmt}")
+    host = synth.make_weights(fmt=fmt)
+    dev = DeviceWeights(host)
+    ow = O.enable_cache(dict(host))
+    yield fmt, dev, ow
+    del dev
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("n", [13, 300])
+def test_quant_fuse_context(qset, n):
+    """13 rows: skinny GEMV with in-register decode; 300 rows: decode to bf16
+    then the MFMA GEMM."""
+    fmt, dev, ow = qset
+    taps = synth.make_taps(range(500, 500 + n))
+    dr = Drafter(dev, KVRing(256), max_rows=n)
+    ctx = dr.fuse(to_device(taps))
+    torch.cuda.synchronize()
+    err = row_rel_err(dec_bf16(ctx), O.bf16_decode(O.fuse_context(ow, taps)))
+    say(f"[{fmt}] fuse n={n} rel err {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("n", [40, 300])
+def test_quant_project_ctx_kv(qset, n):
+    fmt, dev, ow = qset
+    pos0 = 1000
+    ctx = synth.make_rows(n, synth.HIDDEN, seed=79)
+    kv = KVRing(2048, window=2048)
+    dr = Drafter(dev, kv, max_rows=n)
+    dr.project(to_device(ctx), pos0)
+    torch.cuda.synchronize()
+    K, V = O.project_ctx_kv(ow, ctx, pos0)
+    gK, gV = ring_cells(kv, range(pos0, pos0 + n))
+    ek, ev = row_rel_err(gK, K), row_rel_err(gV, V)
+    say(f"[{fmt}] project n={n} K err {ek:.3e} V err {ev:.3e}")
+    assert ek <= TOL and ev <= TOL
+
+
+@pytest.mark.parametrize("n,block", [(40, 4), (300, 8)])
+def test_quant_draft(qset, n, block):
+    """Context built on each side from its own fusion and projection (skinny
+    path for 40 positions, GEMM path for 300), then one block."""
+    fmt, dev, ow = qset
+    end_to_end(dev, ow, n, block, tag=f"{fmt} ctx{n} b{block}")
+
+
+def test_quant_draft_no_context(qset):
+    fmt, dev, ow = qset
+    end_to_end(dev, ow, 0, 8, tag=f"{fmt} ctx0 b8")
