@@ -53,6 +53,35 @@ def pass_bytes(n_ctx: int, block: int = BLOCK, fmt: str = "bf16") -> int:
     return mats + gains + lm + emb + kv
 
 
+PROFILE = os.path.join(ROOT, "profiles", "k_draft_pass_ctx8192_block8_bf16.md")
+
+
+def kernel_source_hash() -> str:
+    """First 16 hex digits of sha256 over the pass kernel's sources."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("pass.hip", "common.h"):
+        with open(os.path.join(ROOT, "block_draft_model_pass_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per pass from the committed FETCH_SIZE / WRITE_SIZE counter
+    runs, or None when the kernel sources changed since they were taken."""
+    import re
+    try:
+        with open(PROFILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    t = re.search(r"^traffic_bytes_per_launch: (\d+)", text, re.M)
+    h = re.search(r"^kernel_source_sha256_16: ([0-9a-f]+)", text, re.M)
+    if not t or not h or h.group(1) != kernel_source_hash():
+        return None
+    return int(t.group(1))
+
+
 def lm_head_bytes() -> int:
     from block_draft_model_pass_amd import synth as S
     return 2 * S.VOCAB * S.HIDDEN
@@ -246,7 +275,7 @@ def main():
         "roofline": {"kernel": "k_draft_pass (dflash_draft_block, ctx 8192, block 8)",
                      "bound": "hbm", "achieved": round(draft_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(draft_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "launch_ms": round(draft_ms, 4),
+                     "traffic": measured_traffic(), "launch_ms": round(draft_ms, 4),
                      "bytes_per_launch": pass_bytes(CTX)},
         "lm_head_standalone": {"kernel": "k_lmhead_bf16 + k_argmax_reduce (dflash_lm_head_argmax)",
                                "ms": round(lm_ms, 4), "bytes": lm_head_bytes(),

@@ -1,0 +1,57 @@
+"""Profiling driver: draft passes at ctx 8192 for rocprofv3 runs.
+
+Builds the synthetic drafter (bf16 by default), commits context positions
+0..8191, then runs `--passes` draft passes of `--block` rows at position 8192
+back to back.  With `--copy-mib M` it first copies an M MiB device buffer
+`--copies` times (a plain copy kernel of known size, whose HBM counters
+calibrate those of the pass kernel).  Prints one line per step it finishes.
+
+    python -m block_draft_model_pass_amd.profile_pass --passes 20
+"""
+from __future__ import annotations
+
+import argparse
+import sys
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--passes", type=int, default=20)
+    ap.add_argument("--block", type=int, default=8)
+    ap.add_argument("--ctx", type=int, default=8192)
+    ap.add_argument("--fmt", default="bf16", choices=["bf16", "q8_0", "q4_0"])
+    ap.add_argument("--copy-mib", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=3)
+    args = ap.parse_args(argv)
+
+    import torch
+
+    from block_draft_model_pass_amd import synth
+    from block_draft_model_pass_amd.device import DeviceWeights, Drafter, KVRing, to_device
+
+    torch.cuda.set_device(0)
+    if args.copy_mib > 0:
+        n = args.copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.copies):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copied {args.copy_mib} MiB x {args.copies}", flush=True)
+        del src, dst
+    dw = DeviceWeights(synth.make_weights(fmt=args.fmt))
+    dr = Drafter(dw, KVRing(synth.WINDOW, synth.WINDOW), max_rows=2048)
+    for s0 in range(0, args.ctx, 2048):
+        dr.commit(to_device(synth.make_taps(range(s0, min(args.ctx, s0 + 2048)))), s0)
+    torch.cuda.synchronize()
+    print(f"context 0..{args.ctx - 1} committed ({args.fmt})", flush=True)
+    cand = torch.empty(8, dtype=torch.int32, device="cuda")
+    for i in range(args.passes):
+        dr.draft(args.ctx, 11, args.block, cand=cand)
+    torch.cuda.synchronize()
+    print(f"{args.passes} draft passes done, block {args.block}", flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
