@@ -127,6 +127,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the CPU-oracle baseline (0 = skip)")
     ap.add_argument("--reps", type=int, default=50, help="repeats of the event-timed kernels")
+    ap.add_argument("--fusion-rows", type=int, default=32768,
+                    help="rows of the timed context-fusion GEMM (0 = skip)")
     ap.add_argument("--no-quant", action="store_true",
                     help="skip the Q8_0 / Q4_0 backbone passes (ctx 8192, block 4)")
     args = ap.parse_args()
@@ -216,6 +218,33 @@ def main():
     lm_ms = ev[0].elapsed_time(ev[1]) / args.reps
     lm_gbs = lm_head_bytes() / (lm_ms * 1e-3) / 1e9
 
+    # Context fusion at long context: [n][12800] x [12800][2560] bf16 on MFMA
+    # plus the RMSNorm epilogue (dflash_fuse_context), n = 32768 by default.
+    fusion = None
+    if args.fusion_rows > 0:
+        nf = args.fusion_rows
+        gen = torch.Generator(device="cuda").manual_seed(5)
+        taps_f = torch.randn((nf, synth.N_TAPS * synth.HIDDEN), generator=gen, device="cuda")
+        taps_f = taps_f.to(torch.bfloat16).view(torch.int16)
+        fdr = Drafter(dw, KVRing(256), max_rows=nf)
+        ctx_f = fdr.fuse(taps_f)
+        fdr.fuse(taps_f, ctx_f)
+        reps_f = max(3, args.reps // 10)
+        ev[0].record()
+        for _ in range(reps_f):
+            fdr.fuse(taps_f, ctx_f)
+        ev[1].record()
+        torch.cuda.synchronize()
+        f_ms = ev[0].elapsed_time(ev[1]) / reps_f
+        flops = 2.0 * nf * synth.N_TAPS * synth.HIDDEN * synth.HIDDEN
+        fusion = {"rows": nf, "shape": f"{nf}x{synth.N_TAPS * synth.HIDDEN} @ "
+                                       f"{synth.N_TAPS * synth.HIDDEN}x{synth.HIDDEN} bf16",
+                  "ms": round(f_ms, 4), "TFLOPs": round(flops / (f_ms * 1e-3) / 1e12, 1),
+                  "frac_bf16_mfma_peak": round(flops / (f_ms * 1e-3) / 2.5e15, 4),
+                  "includes": "k_gemm_bf16_nt + k_rownorm (dflash_fuse_context)"}
+        del fdr, taps_f, ctx_f
+        torch.cuda.empty_cache()
+
     # Quantized backbone (Q8_0 / Q4_0 layer matrices, bf16 LM head): draft
     # passes at ctx 8192, block 4, on a context projected by those weights.
     quant = {}
@@ -281,6 +310,7 @@ def main():
                                "ms": round(lm_ms, 4), "bytes": lm_head_bytes(),
                                "achieved_GBs": round(lm_gbs, 1),
                                "frac_hbm_peak": round(lm_gbs / HBM_PEAK_GBS, 4)},
+        "fusion_gemm": fusion,
         "quantized_backbone": quant or None,
         "accepted_offered": [state["acc"], state["off"]],
         "cpu_baseline": cpu,

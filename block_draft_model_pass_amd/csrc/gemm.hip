@@ -4,92 +4,187 @@
 // k-contiguous, which is the native operand layout of MFMA 16x16x32: a lane
 // reads 8 consecutive k of one row of A and of one row of W.
 //
-// Tile 128 x 128 x 64, 256 threads (2 x 2 waves of 64 x 64 = 4 x 4 MFMA
-// tiles), double-buffered LDS with padded rows.
+// Block tile 256 x 256, 512 threads: 8 waves as 2 (m) x 4 (n), each owning a
+// 128 x 64 sub-tile (8 x 4 MFMA tiles, 128 accumulator registers).  Per
+// 32-wide k step a wave reads 12 operand fragments (12 KiB) from LDS for 32
+// MFMAs, 384 bytes per 16-cycle MFMA, below what the four SIMDs of a CU need
+// at full MFMA rate.
+//
+// k advances in 32-wide stages through a 4-deep LDS ring (32 KiB per stage)
+// filled by direct global -> LDS loads (16 bytes per lane, no registers), so
+// three stages are in flight while one is multiplied.  Stage rows are 64
+// bytes (32 bf16); 16-byte chunk c of row r sits at chunk
+// c ^ (((r >> 1) ^ (r >> 3)) & 3), which keeps the 16-row fragment reads free
+// of bank conflicts; each load instruction fills 1 KiB of LDS (16 rows) in
+// lane order, so a lane fetches the global chunk that the swizzle places at
+// its slot.
+//
+// Tiles are dealt to the XCDs in contiguous runs (the hardware deals blocks
+// round robin), so the blocks on one XCD share A panels in its L2.
 #include "common.h"
 
 namespace dfl {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64, LDSK = BK + 8;
+constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int NT = 512;
+constexpr int STAGES = 4;
+constexpr int STAGE_ELEMS = (BM + BN) * BK;  // bf16 per stage: A rows then W rows
 
-__global__ __launch_bounds__(256) void k_gemm_bf16_nt(const uint16_t* __restrict__ A, int lda,
-                                                      int M, SegTable w, int K,
-                                                      float* __restrict__ C, int ldc) {
-  __shared__ uint16_t As[2][BM][LDSK];
-  __shared__ uint16_t Ws[2][BN][LDSK];
+__device__ __forceinline__ int kswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// LDS byte address of a __shared__ element.
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint16_t*)p));
+}
+
+// Fragment read issued as its own instruction: the compiler's wait-count
+// pass cannot tell which stage a plain LDS read touches and would wait for
+// every direct-to-LDS load in flight, serialising the stages.  The caller
+// waits with lds_wait* before using the value.
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+
+// Wait for this wave's LDS reads; the values pass through the statement so
+// that nothing using them is scheduled before the wait.
+__device__ __forceinline__ void lds_wait4(u32x4& a, u32x4& b, u32x4& c, u32x4& d) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) :: "memory");
+}
+
+__device__ __forceinline__ uint4 as_uint4(u32x4 v) { return __builtin_bit_cast(uint4, v); }
+
+// LDS element offset of chunk c of stage row `row` (A rows 0..255, W rows 256..511).
+__device__ __forceinline__ int lds_off(int row, int c) { return row * BK + ((c ^ kswz(row)) << 3); }
+
+__global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict__ A, int lda,
+                                                     int M, SegTable w, int K,
+                                                     float* __restrict__ C, int ldc, int nN) {
+  // Four separate stage arrays (not one indexed ring): every access names its
+  // stage statically, so the compiler can tell a stage being read from the
+  // stages still being filled and does not wait for those loads.
+  __shared__ __attribute__((aligned(16))) uint16_t st0[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t st1[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t st2[STAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t st3[STAGE_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // Tiles of one block row of C are spread over consecutive block ids so
-  // that the blocks sharing an A panel run close together in time.
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+
+  // block b runs on XCD b % 8; XCD x owns the contiguous tile run
+  // [x q + min(x, r), ...) of the nb = 8 q + r tiles (n fastest).
+  const int nb = gridDim.x;
+  const int x = blockIdx.x & 7, jb = blockIdx.x >> 3;
+  const int q = nb >> 3, rem = nb & 7;
+  const int t = x * q + (x < rem ? x : rem) + jb;
+  const int m0 = (t / nN) * BM, n0 = (t % nN) * BN;
+
   int seg = 0, base = 0;
   for (int i = 0; i + 1 < w.nseg; ++i)
     if (n0 >= w.row_end[i]) { seg = i + 1; base = w.row_end[i]; }
   const uint16_t* wb = static_cast<const uint16_t*>(w.ptr[seg]) + static_cast<size_t>(n0 - base) * K;
 
-  uint4 ra[4], rw[4];
-  auto gload = [&](int k0) {
+  // The stages are written only by direct-to-LDS loads; ordinary stores keep
+  // the compiler from treating their contents as undefined.
+  st0[tid] = 0;
+  st1[tid] = 0;
+  st2[tid] = 0;
+  st3[tid] = 0;
+  __syncthreads();
+
+  // Loader: stage rows are 32 blocks of 16 (A blocks 0..15, W blocks 16..31);
+  // wave v fills blocks 4v .. 4v+3.  Lane L writes stage row 16 b + L/4,
+  // slot L%4, and fetches global chunk slot ^ kswz(row).  A rows past M
+  // re-read row M-1 (their C rows are never stored).
+  const uint16_t* src[4];
+  int ldst[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i, row = idx >> 3, kc = idx & 7;
-      ra[i] = (m0 + row < M)
-                  ? *reinterpret_cast<const uint4*>(A + static_cast<size_t>(m0 + row) * lda + k0 + 8 * kc)
-                  : make_uint4(0, 0, 0, 0);
-      rw[i] = *reinterpret_cast<const uint4*>(wb + static_cast<size_t>(row) * K + k0 + 8 * kc);
+  for (int i = 0; i < 4; ++i) {
+    const int blk = 4 * wave + i, row = 16 * blk + (lane >> 2), c = (lane & 3) ^ kswz(row);
+    if (row < BM) {
+      const int gm = m0 + row < M ? m0 + row : M - 1;
+      src[i] = A + static_cast<size_t>(gm) * lda + 8 * c;
+    } else {
+      src[i] = wb + static_cast<size_t>(row - BM) * K + 8 * c;
     }
-  };
-  auto sstore = [&](int buf) {
+    ldst[i] = blk * 16 * BK;  // element offset of the block inside a stage
+  }
+  auto issue = [&](uint16_t* st, int kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i, row = idx >> 3, kc = idx & 7;
-      *reinterpret_cast<uint4*>(&As[buf][row][8 * kc]) = ra[i];
-      *reinterpret_cast<uint4*>(&Ws[buf][row][8 * kc]) = rw[i];
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(src[i] + kt * BK, st + ldst[i], 16, 0, 0);
   };
 
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int r = lane & 15, g = lane >> 4;
-  f32x4 acc[4][4];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  const int nk = K / BK;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  // One k stage: wait for this wave's loads of stage kt (at most the later
+  // stages' loads, 4 per stage, still outstanding), rendezvous, refill the
+  // slot freed by stage kt-1 with stage kt+3, multiply stage kt.
+  auto step = [&](const uint16_t* cur, uint16_t* refill, int kt, int nk) {
+    const int later = nk - 1 - kt;
+    if (later >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Plain rendezvous (no fence: a fence would also wait for the stages
+    // still in flight); LDS reads of the previous stage were consumed by the
+    // MFMAs before this point.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + STAGES - 1 < nk) issue(refill, kt + STAGES - 1);
+    const uint32_t cb = lds_addr(cur);
+    u32x4 wf[4], af[8];
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      uint4 af[4], wf[4];
+    for (int jn = 0; jn < 4; ++jn) wf[jn] = lds_read16(cb + 2 * lds_off(BM + wn * 64 + jn * 16 + r, g));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        af[i] = *reinterpret_cast<const uint4*>(&As[cur][wm * 64 + i * 16 + r][ks * 32 + 8 * g]);
-        wf[i] = *reinterpret_cast<const uint4*>(&Ws[cur][wn * 64 + i * 16 + r][ks * 32 + 8 * g]);
-      }
+    for (int i = 0; i < 4; ++i) af[i] = lds_read16(cb + 2 * lds_off(wm * 128 + i * 16 + r, g));
+    lds_wait4(wf[0], wf[1], wf[2], wf[3]);
+    lds_wait4(af[0], af[1], af[2], af[3]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = 4; i < 8; ++i) af[i] = lds_read16(cb + 2 * lds_off(wm * 128 + i * 16 + r, g));
 #pragma unroll
-        for (int jn = 0; jn < 4; ++jn) acc[i][jn] = mfma_bf16(af[i], wf[jn], acc[i][jn]);
-    }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn) acc[i][jn] = mfma_bf16(as_uint4(af[i]), as_uint4(wf[jn]), acc[i][jn]);
+    lds_wait4(af[4], af[5], af[6], af[7]);
+#pragma unroll
+    for (int i = 4; i < 8; ++i)
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn) acc[i][jn] = mfma_bf16(as_uint4(af[i]), as_uint4(wf[jn]), acc[i][jn]);
+  };
+
+  const int nk = K / BK;  // a multiple of 4 (K % 128 == 0)
+  issue(st0, 0);
+  issue(st1, 1);
+  issue(st2, 2);
+  for (int kt = 0; kt < nk; kt += STAGES) {
+    step(st0, st3, kt, nk);
+    step(st1, st0, kt + 1, nk);
+    step(st2, st1, kt + 2, nk);
+    step(st3, st2, kt + 3, nk);
   }
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int jn = 0; jn < 4; ++jn)
+    for (int e = 0; e < 4; ++e) {
+      const int row = m0 + wm * 128 + i * 16 + 4 * g + e;
+      if (row < M) {
+        float* cr = C + static_cast<size_t>(row) * ldc + n0 + wn * 64 + r;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = m0 + wm * 64 + i * 16 + 4 * g + e;
-        const int col = n0 + wn * 64 + jn * 16 + r;
-        if (row < M) C[static_cast<size_t>(row) * ldc + col] = acc[i][jn][e];
+        for (int jn = 0; jn < 4; ++jn) cr[jn * 16] = acc[i][jn][e];
       }
+    }
 }
 
 }  // namespace
@@ -97,9 +192,14 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_nt(const uint16_t* __restrict
 hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w, int K, float* C,
                             int ldc, int N, hipStream_t st) {
   if (M <= 0) return hipSuccess;
-  if (N % BN || K % BK || lda % 8) return hipErrorInvalidValue;
-  dim3 grid(N / BN, (M + BM - 1) / BM);
-  hipLaunchKernelGGL(k_gemm_bf16_nt, grid, dim3(256), 0, st, A, lda, M, w, K, C, ldc);
+  if (N % BN || K % (STAGES * BK) || lda % 8) return hipErrorInvalidValue;
+  for (int i = 0; i < w.nseg; ++i)  // a block's 256 rows never straddle two matrices
+    if (w.row_end[i] % BN) return hipErrorInvalidValue;
+  const int nN = N / BN, nM = (M + BM - 1) / BM;
+  const long long tiles = static_cast<long long>(nN) * nM;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_gemm_bf16_nt, dim3(static_cast<unsigned>(tiles)), dim3(NT), 0, st, A, lda, M,
+                     w, K, C, ldc, nN);
   return hipGetLastError();
 }
 
