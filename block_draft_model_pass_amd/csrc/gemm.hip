@@ -13,9 +13,9 @@
 // k advances in 32-wide stages through a 4-deep LDS ring (32 KiB per stage)
 // filled by direct global -> LDS loads (16 bytes per lane, no registers), so
 // three stages are in flight while one is multiplied.  Stage rows are 64
-// bytes (32 bf16); 16-byte chunk c of row r sits at chunk
-// c ^ (((r >> 1) ^ (r >> 3)) & 3), which keeps the 16-row fragment reads free
-// of bank conflicts; each load instruction fills 1 KiB of LDS (16 rows) in
+// bytes (32 bf16); 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 3),
+// which keeps the 16-row fragment reads free of bank conflicts (measured);
+// each load instruction fills 1 KiB of LDS (16 rows) in
 // lane order, so a lane fetches the global chunk that the swizzle places at
 // its slot.
 //
@@ -32,7 +32,11 @@ constexpr int NT = 512;
 constexpr int STAGES = 4;
 constexpr int STAGE_ELEMS = (BM + BN) * BK;  // bf16 per stage: A rows then W rows
 
-__device__ __forceinline__ int kswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// Measured on gfx950 (SQ_LDS_BANK_CONFLICT of single-wave ds_read_b128
+// patterns): with 64-byte rows, 16 rows x one chunk per lane group read
+// conflict-free when chunk c of row r sits at c ^ ((r >> 1) & 3); the same
+// read is 2-way conflicted unswizzled or with c ^ (r & 3).
+__device__ __forceinline__ int kswz(int row) { return (row >> 1) & 3; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -52,10 +56,12 @@ __device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
   return v;
 }
 
-// Wait for this wave's LDS reads; the values pass through the statement so
-// that nothing using them is scheduled before the wait.
-__device__ __forceinline__ void lds_wait4(u32x4& a, u32x4& b, u32x4& c, u32x4& d) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) :: "memory");
+// Wait until at most N of this wave's LDS reads are outstanding (they
+// complete in order); the value passes through the statement so that nothing
+// using it is scheduled before the wait.
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4& a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N) : "memory");
 }
 
 __device__ __forceinline__ uint4 as_uint4(u32x4 v) { return __builtin_bit_cast(uint4, v); }
@@ -142,25 +148,32 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (kt + STAGES - 1 < nk) issue(refill, kt + STAGES - 1);
+    // All 12 fragment reads go out at once; row i of MFMAs waits only for
+    // the reads up to its own A fragment.
     const uint32_t cb = lds_addr(cur);
     u32x4 wf[4], af[8];
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) wf[jn] = lds_read16(cb + 2 * lds_off(BM + wn * 64 + jn * 16 + r, g));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = lds_read16(cb + 2 * lds_off(wm * 128 + i * 16 + r, g));
-    lds_wait4(wf[0], wf[1], wf[2], wf[3]);
-    lds_wait4(af[0], af[1], af[2], af[3]);
-#pragma unroll
-    for (int i = 4; i < 8; ++i) af[i] = lds_read16(cb + 2 * lds_off(wm * 128 + i * 16 + r, g));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int jn = 0; jn < 4; ++jn) acc[i][jn] = mfma_bf16(as_uint4(af[i]), as_uint4(wf[jn]), acc[i][jn]);
-    lds_wait4(af[4], af[5], af[6], af[7]);
-#pragma unroll
-    for (int i = 4; i < 8; ++i)
-#pragma unroll
-      for (int jn = 0; jn < 4; ++jn) acc[i][jn] = mfma_bf16(as_uint4(af[i]), as_uint4(wf[jn]), acc[i][jn]);
+    for (int i = 0; i < 8; ++i) af[i] = lds_read16(cb + 2 * lds_off(wm * 128 + i * 16 + r, g));
+    lds_wait<7>(wf[0]);
+    lds_wait<7>(wf[1]);
+    lds_wait<7>(wf[2]);
+    lds_wait<7>(wf[3]);
+#define GEMM_ROW(I, N)                                                                   \
+    lds_wait<N>(af[I]);                                                                  \
+    _Pragma("unroll") for (int jn = 0; jn < 4; ++jn)                                     \
+        acc[I][jn] = mfma_bf16(as_uint4(af[I]), as_uint4(wf[jn]), acc[I][jn]);           \
+    __builtin_amdgcn_sched_barrier(0);  /* keep this row between its wait and the next */
+    GEMM_ROW(0, 7)
+    GEMM_ROW(1, 6)
+    GEMM_ROW(2, 5)
+    GEMM_ROW(3, 4)
+    GEMM_ROW(4, 3)
+    GEMM_ROW(5, 2)
+    GEMM_ROW(6, 1)
+    GEMM_ROW(7, 0)
+#undef GEMM_ROW
   };
 
   const int nk = K / BK;  // a multiple of 4 (K % 128 == 0)

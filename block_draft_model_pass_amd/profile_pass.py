@@ -2,9 +2,10 @@
 
 Builds the synthetic drafter (bf16 by default), commits context positions
 0..8191, then runs `--passes` draft passes of `--block` rows at position 8192
-back to back.  With `--copy-mib M` it first copies an M MiB device buffer
-`--copies` times (a plain copy kernel of known size, whose HBM counters
-calibrate those of the pass kernel).  Prints one line per step it finishes.
+back to back (or, with `--fuse-rows n`, `--passes` context fusions of n
+rows).  With `--copy-mib M` it first copies an M MiB device buffer `--copies`
+times (a plain copy kernel of known size, whose HBM counters calibrate those
+of the pass kernel).  Prints one line per step it finishes.
 
     python -m block_draft_model_pass_amd.profile_pass --passes 20
 """
@@ -22,6 +23,9 @@ def main(argv=None) -> int:
     ap.add_argument("--fmt", default="bf16", choices=["bf16", "q8_0", "q4_0"])
     ap.add_argument("--copy-mib", type=int, default=0)
     ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--fuse-rows", type=int, default=0,
+                    help="instead of draft passes: context fusion of this many rows "
+                         "(the bf16 GEMM + RMSNorm), --passes times")
     args = ap.parse_args(argv)
 
     import torch
@@ -40,6 +44,18 @@ def main(argv=None) -> int:
         print(f"copied {args.copy_mib} MiB x {args.copies}", flush=True)
         del src, dst
     dw = DeviceWeights(synth.make_weights(fmt=args.fmt))
+    if args.fuse_rows > 0:
+        nf = args.fuse_rows
+        gen = torch.Generator(device="cuda").manual_seed(5)
+        taps = torch.randn((nf, synth.N_TAPS * synth.HIDDEN), generator=gen, device="cuda")
+        taps = taps.to(torch.bfloat16).view(torch.int16)
+        fdr = Drafter(dw, KVRing(256), max_rows=nf)
+        ctx = fdr.fuse(taps)
+        for _ in range(args.passes):
+            fdr.fuse(taps, ctx)
+        torch.cuda.synchronize()
+        print(f"{args.passes} fusions of {nf} rows done", flush=True)
+        return 0
     dr = Drafter(dw, KVRing(synth.WINDOW, synth.WINDOW), max_rows=2048)
     for s0 in range(0, args.ctx, 2048):
         dr.commit(to_device(synth.make_taps(range(s0, min(args.ctx, s0 + 2048)))), s0)
