@@ -10,7 +10,6 @@ using namespace dfl;
 
 namespace {
 
-constexpr int NCH_MAX = 256;          // context chunks of the attention split
 constexpr int NCH_TARGET = 64;        // chunks per KV head aimed for
 constexpr int LMH_GRID = 256;         // standalone LM-head kernel: one block per CU
 constexpr int KEYS_MAX = 1024;        // argmax key slots (blocks of either LM-head launch)
@@ -33,7 +32,7 @@ constexpr int FC_SPLITS = 5;          // k splits of the fc GEMV (K = 12800)
 constexpr size_t PART_FLOATS = static_cast<size_t>(FC_SPLITS) * GEMV_ROWS * H;
 
 struct Layout {
-  size_t part, po, pm, pl, keys, rope, ss, qkv, hv, ov, uv, bar, tab, y;
+  size_t part, po, pm, pl, keys, rope, ss, qkv, hv, h16, ov, uv, bar, tab, y;
   size_t fixed;  // bytes before y
 };
 
@@ -46,18 +45,18 @@ size_t take(size_t& off, size_t bytes) {
 Layout layout() {
   Layout L;
   size_t off = 0;
-  const size_t nqt = 6, nc = NCH_MAX + 1;
   L.part = take(off, sizeof(float) * PART_FLOATS);
-  L.po = take(off, sizeof(float) * NKV * nc * nqt * 16 * D);
-  L.pm = take(off, sizeof(float) * NKV * nc * nqt * 16);
-  L.pl = take(off, sizeof(float) * NKV * nc * nqt * 16);
+  L.po = take(off, pass_po_bytes());
+  L.pm = take(off, pass_pml_bytes());
+  L.pl = take(off, pass_pml_bytes());
   L.keys = take(off, sizeof(uint64_t) * KEYS_MAX * MAXB);
   L.rope = take(off, sizeof(float) * 2 * MAXB * (D / 2));
   // per-layer / per-version copies used by the persistent pass
   constexpr size_t HV = 2 * dfl::L + 1, NL = dfl::L;
   L.ss = take(off, sizeof(float) * HV * (H / 16) * MAXB);
-  L.qkv = take(off, sizeof(float) * NL * MAXB * QKV_N);
+  L.qkv = take(off, sizeof(uint16_t) * NL * MAXB * QKV_N);
   L.hv = take(off, sizeof(float) * HV * MAXB * H);
+  L.h16 = take(off, sizeof(uint16_t) * HV * MAXB * H);
   L.ov = take(off, 2 * NL * MAXB * NQ * D);
   L.uv = take(off, 2 * NL * MAXB * F);
   L.bar = take(off, pass_bar_bytes());
@@ -336,8 +335,9 @@ extern "C" int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* 
   q.anchor = anchor_id;
   q.mask = mask_id;
   q.h = at<float>(ws, Lw.hv);
+  q.h16 = at<uint16_t>(ws, Lw.h16);
   q.ss = at<float>(ws, Lw.ss);
-  q.qkv = at<float>(ws, Lw.qkv);
+  q.qkv = at<uint16_t>(ws, Lw.qkv);
   q.rope = at<float2>(ws, Lw.rope);
   q.po = at<uint16_t>(ws, Lw.po);
   q.pm = at<float>(ws, Lw.pm);

@@ -247,8 +247,9 @@ struct PassLaunch {
   int64_t p;
   int anchor, mask;
   float* h;
+  uint16_t* h16;
   float* ss;
-  float* qkv;
+  uint16_t* qkv;           // fp16 [5][8][7168]
   float2* rope;
   uint16_t* po;            // chunk outputs, fp16, normalised by the chunk sum
   float* pm;
@@ -268,6 +269,8 @@ struct PassLaunch {
 hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st);
 // Largest co-resident grid of the pass kernel on `device` (0 if it cannot run).
 hipError_t draft_pass_max_grid(int device, int* grid);
+size_t pass_po_bytes();   // attention chunk outputs, all layers
+size_t pass_pml_bytes();  // chunk maxima (or sums), all layers
 size_t pass_smem_bytes();
 size_t pass_tab_bytes();
 size_t pass_bar_bytes();

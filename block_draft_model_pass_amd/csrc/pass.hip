@@ -54,6 +54,11 @@ constexpr size_t SSTRIDE = static_cast<size_t>(H / 16) * MAXB;   // floats per s
 constexpr size_t QSTRIDE = static_cast<size_t>(MAXB) * QKV_N;
 constexpr size_t OSTRIDE = static_cast<size_t>(MAXB) * NQ * D;
 constexpr size_t USTRIDE = static_cast<size_t>(MAXB) * F;
+// Attention partials are single-assignment per layer too (chunk outputs fp16,
+// chunk max / sum fp32); at most 128 chunks per KV head and 6 query tiles.
+constexpr int NCH_PASS = 128, NQT_MAX = (G * MAXB + 15) / 16;
+constexpr size_t PMSTRIDE = static_cast<size_t>(NKV) * NCH_PASS * NQT_MAX * 16;
+constexpr size_t POSTRIDE = PMSTRIDE * D;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -138,8 +143,9 @@ struct PassArgs {
   // region, written once (coherent stores) and read after a barrier with
   // ordinary cached loads -- no cache can hold an older value of it.
   float* h;          // [HV][8][H] residual stream versions
+  uint16_t* h16;     // [HV][8][H] fp16 copies: the input of the RMSNorm builds
   float* ss;         // [HV][NT_H][8] per-tile sums of squares of each h version
-  float* qkv;        // [L][8][QKV_N]
+  uint16_t* qkv;     // [L][8][QKV_N] fp16 (raw q, k, v before the head norms)
   const float2* rope;  // [8][128] (cos, sin)
   uint16_t* po;
   float* pm;
@@ -387,48 +393,52 @@ __device__ __forceinline__ f32x4 group_sum(Smem& s, int w0, int n, int lane) {
 // the activation format XF (bf16, or fp16 beside quantized weights), into
 // LDS rows of stride H + pad.  np per-tile sums of squares are reduced in a
 // fixed order.  Every load (h and the sums) is issued in one round.
-constexpr int XN4 = MAXB * (H / 4) / NTHR;  // float4 of h per thread (10)
+constexpr int XN8 = MAXB * (H / 8) / NTHR;  // 8-element fp16 groups of h per thread (5)
 
 template <int XF>
 __device__ __forceinline__ void build_x_norm(const PassArgs& a, Smem& s, int ver, int np,
                                              const uint16_t* gain) {
   const int tid = otid(), wave = tid >> 6, lane = tid & 63;
-  const int n4 = a.B * (H / 4);
-  const float* hsrc = a.h + ver * HSTRIDE;
+  const int n8 = a.B * (H / 8);
+  const uint16_t* hsrc = a.h16 + ver * HSTRIDE;
   const float* ssrc = a.ss + ver * SSTRIDE;
-  float4 hv[XN4];
+  uint4 hv[XN8];
 #pragma unroll
-  for (int u = 0; u < XN4; ++u) {
+  for (int u = 0; u < XN8; ++u) {
     const int e = tid + u * NTHR;
-    hv[u] = e < n4 ? gld<float4>(hsrc + 4 * e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    hv[u] = e < n8 ? gld<uint4>(hsrc + 8 * e) : make_uint4(0, 0, 0, 0);
   }
   if (wave < a.B) {
-    float v = 0.f;
     float sv[3];
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
       const int i = lane + 64 * q;
       sv[q] = i < np ? gld<float>(ssrc + i * MAXB + wave) : 0.f;
     }
-    v = sv[0] + sv[1] + sv[2];
-    v = wave_sum(v);
+    const float v = wave_sum(sv[0] + sv[1] + sv[2]);
     if (lane == 0) s.scal[wave] = 1.0f / sqrtf(v / static_cast<float>(H) + a.eps);
   }
   lds_sync();
   constexpr int XS = H + XS_PAD;
 #pragma unroll
-  for (int u = 0; u < XN4; ++u) {
+  for (int u = 0; u < XN8; ++u) {
     const int e = tid + u * NTHR;
-    if (e < n4) {
-      const int b = e / (H / 4), k = (e % (H / 4)) * 4;
+    if (e < n8) {
+      const int b = e / (H / 8), k = (e % (H / 8)) * 8;
       const float sc = s.scal[b];
-      const uint2 gg = gld<uint2>(gain + k);
-      const uint16_t y0 = act16<XF>(hv[u].x * sc * bf16_to_f32(gg.x & 0xffff));
-      const uint16_t y1 = act16<XF>(hv[u].y * sc * bf16_to_f32(gg.x >> 16));
-      const uint16_t y2 = act16<XF>(hv[u].z * sc * bf16_to_f32(gg.y & 0xffff));
-      const uint16_t y3 = act16<XF>(hv[u].w * sc * bf16_to_f32(gg.y >> 16));
-      *reinterpret_cast<uint2*>(s.x + b * XS + k) =
-          make_uint2(y0 | (static_cast<uint32_t>(y1) << 16), y2 | (static_cast<uint32_t>(y3) << 16));
+      const uint4 gg = gld<uint4>(gain + k);
+      const uint32_t hw[4] = {hv[u].x, hv[u].y, hv[u].z, hv[u].w};
+      const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t y0 = act16<XF>(f16_bits_to_f32(static_cast<uint16_t>(hw[i])) * sc *
+                                      bf16_to_f32(static_cast<uint16_t>(gw[i])));
+        const uint16_t y1 = act16<XF>(f16_bits_to_f32(static_cast<uint16_t>(hw[i] >> 16)) * sc *
+                                      bf16_to_f32(static_cast<uint16_t>(gw[i] >> 16)));
+        o[i] = y0 | (static_cast<uint32_t>(y1) << 16);
+      }
+      *reinterpret_cast<uint4*>(s.x + b * XS + k) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
   lds_sync();
@@ -468,6 +478,11 @@ __device__ __forceinline__ void residual_epilogue(const PassArgs& a, f32x4 acc, 
     const float4 hv = gld<float4>(a.h + vin * HSTRIDE + off);
     const f32x4 hn = {hv.x + acc[0], hv.y + acc[1], hv.z + acc[2], hv.w + acc[3]};
     st_coh_f4(a.h + (vin + 1) * HSTRIDE + off, hn);
+    st_coh64(a.h16 + (vin + 1) * HSTRIDE + off,
+             static_cast<uint64_t>(f32_to_f16_bits(hn[0])) |
+                 (static_cast<uint64_t>(f32_to_f16_bits(hn[1])) << 16) |
+                 (static_cast<uint64_t>(f32_to_f16_bits(hn[2])) << 32) |
+                 (static_cast<uint64_t>(f32_to_f16_bits(hn[3])) << 48));
     sq = hn[0] * hn[0] + hn[1] * hn[1] + hn[2] * hn[2] + hn[3] * hn[3];
   }
   sq = group4_sum(sq);
@@ -519,7 +534,11 @@ __device__ __forceinline__ void qkv_phase(const PassArgs& a, Smem& s, int l, int
     if ((wave & 3) == 0) {
       acc = group_sum(s, wave, 4, lane);
       if (r < a.B)
-        st_coh_f4(a.qkv + l * QSTRIDE + static_cast<size_t>(r) * QKV_N + tile * 16 + 4 * g, acc);
+        st_coh64(a.qkv + l * QSTRIDE + static_cast<size_t>(r) * QKV_N + tile * 16 + 4 * g,
+                 static_cast<uint64_t>(f32_to_f16_bits(acc[0])) |
+                     (static_cast<uint64_t>(f32_to_f16_bits(acc[1])) << 16) |
+                     (static_cast<uint64_t>(f32_to_f16_bits(acc[2])) << 32) |
+                     (static_cast<uint64_t>(f32_to_f16_bits(acc[3])) << 48));
     }
   }
   wait_stores();
@@ -664,14 +683,17 @@ __device__ __forceinline__ void attn_query(const PassArgs& a, int l, int j, int 
   const int r = t * 16 + n;
   const bool qv = r < G * a.B;
   const int bi = qv ? r / G : 0, hl = qv ? r % G : 0;
-  const float* qraw = a.qkv + l * QSTRIDE + static_cast<size_t>(bi) * QKV_N + (j * G + hl) * D;
+  const uint16_t* qraw = a.qkv + l * QSTRIDE + static_cast<size_t>(bi) * QKV_N + (j * G + hl) * D;
   float qv8[8][8];
 #pragma unroll
   for (int si = 0; si < 8; ++si) {
-    const float4 u0 = gld<float4>(qraw + 32 * si + 8 * g);
-    const float4 u1 = gld<float4>(qraw + 32 * si + 8 * g + 4);
-    qv8[si][0] = u0.x; qv8[si][1] = u0.y; qv8[si][2] = u0.z; qv8[si][3] = u0.w;
-    qv8[si][4] = u1.x; qv8[si][5] = u1.y; qv8[si][6] = u1.z; qv8[si][7] = u1.w;
+    const uint4 u = gld<uint4>(qraw + 32 * si + 8 * g);
+    const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qv8[si][2 * i] = f16_bits_to_f32(static_cast<uint16_t>(uw[i]));
+      qv8[si][2 * i + 1] = f16_bits_to_f32(static_cast<uint16_t>(uw[i] >> 16));
+    }
   }
   float sq = 0.f;
 #pragma unroll
@@ -718,13 +740,13 @@ __device__ __forceinline__ void attn_block_rows(const PassArgs& a, int l, int j,
   const int wave = otid() >> 6, lane = otid() & 63;
   if (wave >= a.B) return;
   const int b = wave;
-  const float* kr = a.qkv + l * QSTRIDE + static_cast<size_t>(b) * QKV_N + NQ * D + j * D;
-  const float* vr = kr + NKV * D;
-  float k0 = gld<float>(kr + lane), k1 = gld<float>(kr + lane + 64);
-  float k2 = gld<float>(kr + lane + 128), k3 = gld<float>(kr + lane + 192);
+  const uint16_t* kr = a.qkv + l * QSTRIDE + static_cast<size_t>(b) * QKV_N + NQ * D + j * D;
+  const uint16_t* vr = kr + NKV * D;
+  float k0 = f16_bits_to_f32(gld<uint16_t>(kr + lane)), k1 = f16_bits_to_f32(gld<uint16_t>(kr + lane + 64));
+  float k2 = f16_bits_to_f32(gld<uint16_t>(kr + lane + 128)), k3 = f16_bits_to_f32(gld<uint16_t>(kr + lane + 192));
   float vv[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) vv[q] = gld<float>(vr + lane + 64 * q);
+  for (int q = 0; q < 4; ++q) vv[q] = f16_bits_to_f32(gld<uint16_t>(vr + lane + 64 * q));
   const float sq = wave_sum(k0 * k0 + k1 * k1 + k2 * k2 + k3 * k3);
   const float sc = 1.0f / sqrtf(sq / static_cast<float>(D) + a.eps);
   const uint16_t* gn = a.tab->k_norm[l];
@@ -795,11 +817,11 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KV
       lsum = group4_sum(lsum);
       const size_t base = (static_cast<size_t>(j) * a.nch + c) * a.nqt + wave;
       if (g == 0) {
-        st_cohf(a.pm + base * 16 + n, m);
-        st_cohf(a.pl + base * 16 + n, lsum);
+        st_cohf(a.pm + l * PMSTRIDE + base * 16 + n, m);
+        st_cohf(a.pl + l * PMSTRIDE + base * 16 + n, lsum);
       }
       const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-      uint16_t* op = a.po + (base * 16 + n) * D + 4 * g;
+      uint16_t* op = a.po + l * POSTRIDE + (base * 16 + n) * D + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) {
         const uint64_t lo = static_cast<uint64_t>(f32_to_f16_bits(o[dt][0] * inv)) |
@@ -813,84 +835,101 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KV
   wait_stores();
 }
 
-// Merge of the chunks of one (KV head, query tile, query row): wave 0 turns
-// the chunks' maxima and sums into weights (w_c = 2^(m_c - M) l_c, chunk
-// outputs being already normalised by l_c) while every thread already has
-// its partial outputs in flight; 512 threads = 4 quarters of the chunks x 128
-// pairs of head dims.
-constexpr int MQ = 32;  // chunks per quarter (nch <= 128)
+// Merge of the chunks of one (KV head, query tile, query row) -- a group.
+// The last ceil(groups / 2) blocks merge two groups each, one per 256-thread
+// half, so that the O-projection blocks (the first 160) are free to stream
+// their weights during this phase.  In a half, 32 threads cover the 256 head
+// dims of one chunk (8 each) and 8 such slots take chunks slot, slot + 8, ...
+// with 16-byte loads; wave 0 of the half turns the chunks' maxima and sums
+// into weights w_c = 2^(m_c - M) l_c (chunk outputs are already normalised
+// by l_c).  Partials of this layer were written once, so plain loads read
+// them.
+constexpr int MRG_U = NCH_PASS / 8;  // chunks per slot (16)
 
 template <int FMT>
 __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
   const int ngroup = NKV * a.nqt * 16;
-  const int w = blockIdx.x;
-  if (w < ngroup) {
-    const int n = w & 15, t = (w >> 4) % a.nqt, j = (w >> 4) / a.nqt;
-    const int r = t * 16 + n;
-    if (r < G * a.B) {
-      const int tid = otid(), wave = tid >> 6, lane = tid & 63;
-      const int nc = a.nch;
-      const size_t cstride = static_cast<size_t>(a.nqt) * 16;
-      const size_t row0 = (static_cast<size_t>(j) * nc * a.nqt + t) * 16 + n;
-      const int d2 = 2 * (tid & 127), quarter = tid >> 7;
-      uint32_t ov[MQ];
+  const int nmb = (ngroup + 1) / 2;
+  const int w0 = gridDim.x - nmb;
+  if (blockIdx.x >= w0) {
+    const int tid = otid(), half = tid >> 8, ht = tid & 255, lane = tid & 63;
+    const int grp = 2 * (blockIdx.x - w0) + half;
+    const int n = grp & 15, t = (grp >> 4) % a.nqt, j = (grp >> 4) / a.nqt;
+    const bool act = grp < ngroup && t * 16 + n < G * a.B;
+    const int nc = a.nch;
+    const size_t cstride = static_cast<size_t>(a.nqt) * 16;
+    const size_t row0 = (static_cast<size_t>(j) * nc * a.nqt + t) * 16 + n;
+    const uint16_t* po = a.po + l * POSTRIDE;
+    const float* pm = a.pm + l * PMSTRIDE;
+    const float* pl = a.pl + l * PMSTRIDE;
+    const int slot = ht >> 5, dp = ht & 31;
+    uint4 ov[MRG_U];
 #pragma unroll
-      for (int u = 0; u < MQ; ++u) {
-        const int cc = quarter + 4 * u;
-        ov[u] = cc < nc ? ld_coh32(a.po + (row0 + cc * cstride) * D + d2) : 0u;
+    for (int u = 0; u < MRG_U; ++u) {
+      const int c = slot + 8 * u;
+      ov[u] = act && c < nc ? gld<uint4>(po + (row0 + c * cstride) * D + 8 * dp) : make_uint4(0, 0, 0, 0);
+    }
+    if ((ht >> 6) == 0) {  // wave 0 of the half: chunk weights
+      float mv[2], lv[2];
+      float M = NEG_INF;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int c = lane + 64 * q;
+        mv[q] = act && c < nc ? gld<float>(pm + row0 + c * cstride) : NEG_INF;
+        lv[q] = act && c < nc ? gld<float>(pl + row0 + c * cstride) : 0.f;
+        M = fmaxf(M, mv[q]);
       }
-      if (wave == 0) {
-        float mv[2], lv[2];
-        float M = NEG_INF;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int cc = lane + 64 * q;
-          mv[q] = cc < nc ? ld_cohf(a.pm + row0 + cc * cstride) : NEG_INF;
-          lv[q] = cc < nc ? ld_cohf(a.pl + row0 + cc * cstride) : 0.f;
-          M = fmaxf(M, mv[q]);
+      for (int o2 = 32; o2 > 0; o2 >>= 1) M = fmaxf(M, __shfl_xor(M, o2, 64));
+      float Ls = 0.f;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int c = lane + 64 * q;
+        const float wt = act && c < nc ? exp2f(mv[q] - M) * lv[q] : 0.f;
+        s.mw[half * NCH_PASS + c] = wt;
+        Ls += wt;
+      }
+      Ls = wave_sum(Ls);
+      if (lane == 0) s.scal[half] = Ls > 0.f ? 1.0f / Ls : 0.f;
+    }
+    lds_sync();
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int u = 0; u < MRG_U; ++u) {
+      const int c = slot + 8 * u;
+      if (c < nc) {
+        const float wt = s.mw[half * NCH_PASS + c];
+        const uint32_t wd[4] = {ov[u].x, ov[u].y, ov[u].z, ov[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += f16_bits_to_f32(static_cast<uint16_t>(wd[i])) * wt;
+          acc[2 * i + 1] += f16_bits_to_f32(static_cast<uint16_t>(wd[i] >> 16)) * wt;
         }
-#pragma unroll
-        for (int o2 = 32; o2 > 0; o2 >>= 1) M = fmaxf(M, __shfl_xor(M, o2, 64));
-        float Ls = 0.f;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int cc = lane + 64 * q;
-          const float wt = cc < nc ? exp2f(mv[q] - M) * lv[q] : 0.f;
-          s.mw[cc] = wt;
-          Ls += wt;
-        }
-        Ls = wave_sum(Ls);
-        if (lane == 0) s.scal[0] = 1.0f / Ls;
       }
-      lds_sync();
-      float acc0 = 0.f, acc1 = 0.f;
+    }
+    // slots 1..7 hand their sums to slot 0 (fixed order: deterministic)
+    float* red = reinterpret_cast<float*>(s.x);  // [2][8][256]
+    if (slot > 0) {
 #pragma unroll
-      for (int u = 0; u < MQ; ++u) {
-        const int cc = quarter + 4 * u;
-        if (cc < nc) {
-          const float wt = s.mw[cc];
-          acc0 += f16_bits_to_f32(static_cast<uint16_t>(ov[u])) * wt;
-          acc1 += f16_bits_to_f32(static_cast<uint16_t>(ov[u] >> 16)) * wt;
-        }
-      }
-      if (quarter > 0) {
-        s.mw[256 + (quarter - 1) * 256 + d2] = acc0;
-        s.mw[256 + (quarter - 1) * 256 + d2 + 1] = acc1;
-      }
-      lds_sync();
-      if (quarter == 0) {
+      for (int i = 0; i < 8; ++i) red[(half * 8 + slot) * D + 8 * dp + i] = acc[i];
+    }
+    lds_sync();
+    if (slot == 0 && act) {
+      for (int sl = 1; sl < 8; ++sl) {
 #pragma unroll
-        for (int q2 = 0; q2 < 3; ++q2) {
-          acc0 += s.mw[256 + q2 * 256 + d2];
-          acc1 += s.mw[256 + q2 * 256 + d2 + 1];
-        }
-        const int bi = r / G, hl = r % G;
-        const uint32_t pk = static_cast<uint32_t>(act16<FMT>(acc0 * s.scal[0])) |
-                            (static_cast<uint32_t>(act16<FMT>(acc1 * s.scal[0])) << 16);
-        st_coh32(reinterpret_cast<uint32_t*>(a.o16 + l * OSTRIDE + static_cast<size_t>(bi) * NQ * D +
-                                             (j * G + hl) * D + d2),
-                 pk);
+        for (int i = 0; i < 8; ++i) acc[i] += red[(half * 8 + sl) * D + 8 * dp + i];
       }
+      const float sc = s.scal[half];
+      uint32_t pk[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pk[i] = static_cast<uint32_t>(act16<FMT>(acc[2 * i] * sc)) |
+                (static_cast<uint32_t>(act16<FMT>(acc[2 * i + 1] * sc)) << 16);
+      const int r = t * 16 + n, bi = r / G, hl = r % G;
+      st_coh128(a.o16 + l * OSTRIDE + static_cast<size_t>(bi) * NQ * D + (j * G + hl) * D + 8 * dp,
+                make_uint4(pk[0], pk[1], pk[2], pk[3]));
     }
   }
   wait_stores();
@@ -989,6 +1028,15 @@ __device__ __forceinline__ void down_range(int wave, int& kbeg, int& klen) {
 
 template <int FMT> using DownTile = WTile<FMT, 1024 / KPerLoad<FMT>::v>;
 
+// Down projection tile w for blocks w < 160.  Only waves 1..DOWN_PRE_LAST
+// prefetch their k range during the gate/up phase (which those blocks spend
+// streaming two gate/up tile pairs): a full prefetch would lengthen that
+// phase by as much as it shortens this one.  The other waves load after the
+// barrier.
+constexpr int DOWN_PRE_LAST = 3;
+
+__device__ __forceinline__ bool down_pre(int wave) { return wave >= 1 && wave <= DOWN_PRE_LAST; }
+
 template <int FMT>
 __device__ __forceinline__ void down_prefetch(const PassArgs& a, int l, DownTile<FMT>& W, bool go) {
   const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
@@ -1004,8 +1052,9 @@ template <int FMT>
 __device__ __forceinline__ void down_phase(const PassArgs& a, Smem& s, int l, DownTile<FMT>& W) {
   const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
   const int r = lane & 15, g = lane >> 4;
+  const int tile = w;
   if (w < NT_H) {
-    if (wave == 0) down_prefetch<FMT>(a, l, W, true);
+    if (!down_pre(wave)) down_prefetch<FMT>(a, l, W, true);
     copy_x(a, s, a.u16 + l * USTRIDE, F);
     int kbeg, klen;
     down_range(wave, kbeg, klen);
@@ -1014,7 +1063,7 @@ __device__ __forceinline__ void down_phase(const PassArgs& a, Smem& s, int l, Do
     f32x4 acc = mma_wt<FMT, N>(W, s.x + xrow(r, a.B) * XS, kbeg, g, klen / KPerLoad<FMT>::v);
     s.red[wave][lane] = acc;
     lds_sync();
-    if (wave == 0) residual_epilogue(a, group_sum(s, 0, NWAVE, lane), w, r, g, 2 * l + 1);
+    if (wave == 0) residual_epilogue(a, group_sum(s, 0, NWAVE, lane), tile, r, g, 2 * l + 1);
   }
   wait_stores();
 }
@@ -1163,7 +1212,7 @@ __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
     grid_sync(a, bk);
     gu_phase<FMT>(a, s, l, NT_H, Wg);
     DownTile<FMT> Wd;
-    down_prefetch<FMT>(a, l, Wd, pre);
+    down_prefetch<FMT>(a, l, Wd, down_pre(otid() >> 6));
     grid_sync(a, bk);
     down_phase<FMT>(a, s, l, Wd);
     // Both prefetch targets are assigned on every iteration (zeros when
@@ -1188,8 +1237,9 @@ __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
 // barrier words of the pass kernel.  grid B, block 256.
 __global__ __launch_bounds__(256) void k_pass_init(LayerTab tab, LayerTab* tab_out,
                                                    const uint16_t* embed, int anchor, int mask,
-                                                   int64_t p, double theta, float* h, float* ss,
-                                                   float2* rope, unsigned* bar) {
+                                                   int64_t p, double theta, float* h,
+                                                   uint16_t* h16, float* ss, float2* rope,
+                                                   unsigned* bar) {
   __shared__ float red[4];
   const int b = blockIdx.x;
   if (b == 0)
@@ -1201,6 +1251,7 @@ __global__ __launch_bounds__(256) void k_pass_init(LayerTab tab, LayerTab* tab_o
   for (int e = threadIdx.x; e < H; e += 256) {
     const float v = bf16_to_f32(row[e]);
     h[static_cast<size_t>(b) * H + e] = v;
+    h16[static_cast<size_t>(b) * H + e] = f32_to_f16_bits(v);
     sq += v * v;
   }
   sq = block_sum<256>(sq, red);
@@ -1218,6 +1269,8 @@ __global__ __launch_bounds__(256) void k_pass_init(LayerTab tab, LayerTab* tab_o
 size_t pass_smem_bytes() { return sizeof(Smem); }
 size_t pass_tab_bytes() { return sizeof(LayerTab); }
 size_t pass_bar_bytes() { return sizeof(unsigned) * BAR_WORDS; }
+size_t pass_po_bytes() { return sizeof(uint16_t) * L * POSTRIDE; }
+size_t pass_pml_bytes() { return sizeof(float) * L * PMSTRIDE; }
 
 hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
   LayerTab tab;
@@ -1253,6 +1306,7 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
   a.B = q.B;
   a.nqt = (G * q.B + 15) / 16;
   a.h = q.h;
+  a.h16 = q.h16;
   a.ss = q.ss;
   a.qkv = q.qkv;
   a.rope = q.rope;
@@ -1274,7 +1328,7 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_pass_init, dim3(q.B), dim3(256), 0, st, tab,
                      reinterpret_cast<LayerTab*>(q.tab), q.embed, q.anchor, q.mask, q.p, q.theta,
-                     q.h, q.ss, q.rope, q.bar);
+                     q.h, q.h16, q.ss, q.rope, q.bar);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const void* kern = q.fmt == W_Q8_0   ? reinterpret_cast<const void*>(k_draft_pass<W_Q8_0>)
