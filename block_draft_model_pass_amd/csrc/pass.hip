@@ -551,8 +551,7 @@ __device__ __forceinline__ void qkv_phase(const PassArgs& a, Smem& s, int l, int
 // takes the block rows' own keys.  Context K/V never depends on this pass, so
 // each thread loads its share of the chunk's first two 32-cell blocks (16 KiB
 // of K and 16 KiB of V^T each, 4 x 16 bytes per thread per block) *before*
-// the barrier that precedes the phase; blocks then rotate through two LDS
-// buffers, the register slot of a block being refilled two blocks ahead.
+// the barrier that precedes the phase; blocks then go through LDS in pairs.
 // Waves t < nqt own 16 query rows each.  A chunk leaves its output
 // normalised by its own softmax sum, in fp16, with its maximum and sum.
 
@@ -648,11 +647,11 @@ __device__ __forceinline__ void attn_block(const uint16_t* kb, const uint16_t* v
   bm = group4_max(bm);
   const float mnew = fmaxf(m, bm);
   const float muse = mnew == NEG_INF ? 0.f : mnew;
-  const float alpha = exp2f(m - muse);
+  const float alpha = __builtin_amdgcn_exp2f(m - muse);
   float pr[8], ps = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    pr[i] = exp2f(x[i] - muse);
+    pr[i] = __builtin_amdgcn_exp2f(x[i] - muse);
     ps += pr[i];
   }
   lsum = lsum * alpha + ps;
@@ -672,6 +671,63 @@ __device__ __forceinline__ void attn_block(const uint16_t* kb, const uint16_t* v
     const uint2 x1 = *reinterpret_cast<const uint2*>(vb + vswz(16 * dt + n, g + 4));
     const uint4 v = make_uint4(x0.x & vm[0], x0.y & vm[1], x1.x & vm[2], x1.y & vm[3]);
     o[dt] = mfma_f16(v, pf, o[dt]);
+  }
+}
+
+// Two 32-cell blocks that lie entirely inside the visible range: one
+// softmax update for all 64 cells (one rescale of the outputs) and no
+// masking of scores or values.
+__device__ __forceinline__ void attn_pair_full(const uint16_t* kb0, const uint16_t* vb0,
+                                               const uint16_t* kb1, const uint16_t* vb1,
+                                               float scale_log2, const uint4 (&qf)[8],
+                                               f32x4 (&o)[16], float& m, float& lsum, int n, int g) {
+  f32x4 sc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int si = 0; si < 8; ++si) {
+    const int c = g + 4 * si;
+    sc[0] = mfma_f16(*reinterpret_cast<const uint4*>(kb0 + kswz(n, c)), qf[si], sc[0]);
+    sc[1] = mfma_f16(*reinterpret_cast<const uint4*>(kb0 + kswz(16 + n, c)), qf[si], sc[1]);
+    sc[2] = mfma_f16(*reinterpret_cast<const uint4*>(kb1 + kswz(n, c)), qf[si], sc[2]);
+    sc[3] = mfma_f16(*reinterpret_cast<const uint4*>(kb1 + kswz(16 + n, c)), qf[si], sc[3]);
+  }
+  float x[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[4 * q + i] = sc[q][i] * scale_log2;
+  float bm = x[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) bm = fmaxf(bm, x[i]);
+  bm = group4_max(bm);
+  const float mnew = fmaxf(m, bm);
+  const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+  float pr[16], ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    pr[i] = __builtin_amdgcn_exp2f(x[i] - mnew);
+    ps += pr[i];
+  }
+  lsum = lsum * alpha + ps;
+  m = mnew;
+  uint32_t pp[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    pp[i] = static_cast<uint32_t>(f32_to_f16_bits(pr[2 * i])) |
+            (static_cast<uint32_t>(f32_to_f16_bits(pr[2 * i + 1])) << 16);
+  const uint4 pf0 = make_uint4(pp[0], pp[1], pp[2], pp[3]);
+  const uint4 pf1 = make_uint4(pp[4], pp[5], pp[6], pp[7]);
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) {
+    o[dt] *= alpha;
+    const int d = 16 * dt + n;
+    const uint2 a0 = *reinterpret_cast<const uint2*>(vb0 + vswz(d, g));
+    const uint2 a1 = *reinterpret_cast<const uint2*>(vb0 + vswz(d, g + 4));
+    o[dt] = mfma_f16(make_uint4(a0.x, a0.y, a1.x, a1.y), pf0, o[dt]);
+    const uint2 b0 = *reinterpret_cast<const uint2*>(vb1 + vswz(d, g));
+    const uint2 b1 = *reinterpret_cast<const uint2*>(vb1 + vswz(d, g + 4));
+    o[dt] = mfma_f16(make_uint4(b0.x, b0.y, b1.x, b1.y), pf1, o[dt]);
   }
 }
 
@@ -766,21 +822,6 @@ __device__ __forceinline__ void attn_block_rows(const PassArgs& a, int l, int j,
   }
 }
 
-// One block step: the block sits in register slot R; it goes to LDS buffer
-// ib & 1, the slot is refilled with block ib + 2, and the waves run it.
-__device__ __forceinline__ void attn_step(const PassArgs& a, Smem& s, int l, int j, int blk0,
-                                          int nblk, int ib, KVRegs& R, int wave, const uint4 (&qf)[8],
-                                          f32x4 (&o)[16], float& m, float& lsum, int n, int g) {
-  uint16_t* kbuf = s.x + (ib & 1) * (2 * BLK_CELLS * D);
-  uint16_t* vbuf = kbuf + BLK_CELLS * D;
-  attn_store(R, kbuf, vbuf);
-  attn_load(a, l, blk0 + ib + 2, j, R, ib + 2 < nblk);
-  lds_sync();
-  if (wave < a.nqt)
-    attn_block(kbuf, vbuf, a.p0 + 32 * static_cast<int64_t>(blk0 + ib), a.lo, a.hi, a.scale_log2,
-               qf, o, m, lsum, n, g);
-}
-
 __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KVRegs& R0,
                                            KVRegs& R1) {
   const int w = blockIdx.x;
@@ -805,9 +846,34 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KV
     f32x4 o[16];
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Blocks go through LDS in pairs (buffers at 0 and 2 x 8192): both are
+    // stored, then run together -- in one softmax update when both lie
+    // entirely inside the visible range.
+    uint16_t* k0b = s.x;
+    uint16_t* v0b = k0b + BLK_CELLS * D;
+    uint16_t* k1b = s.x + 2 * BLK_CELLS * D;
+    uint16_t* v1b = k1b + BLK_CELLS * D;
     for (int ib = 0; ib < nblk; ib += 2) {
-      attn_step(a, s, l, j, blk0, nblk, ib, R0, wave, qf, o, m, lsum, n, g);
-      if (ib + 1 < nblk) attn_step(a, s, l, j, blk0, nblk, ib + 1, R1, wave, qf, o, m, lsum, n, g);
+      const bool two = ib + 1 < nblk;
+      if (ib > 0) lds_sync();  // every wave is done with the previous pair
+      attn_store(R0, k0b, v0b);
+      if (two) attn_store(R1, k1b, v1b);
+      lds_sync();
+      if (wave < a.nqt) {
+        const int64_t pb0 = a.p0 + 32 * static_cast<int64_t>(blk0 + ib), pb1 = pb0 + 32;
+        const bool f0 = pb0 >= a.lo && pb0 + 32 <= a.hi;
+        const bool f1 = two && pb1 >= a.lo && pb1 + 32 <= a.hi;
+        if (f0 && f1) {
+          attn_pair_full(k0b, v0b, k1b, v1b, a.scale_log2, qf, o, m, lsum, n, g);
+        } else {
+          attn_block(k0b, v0b, pb0, a.lo, a.hi, a.scale_log2, qf, o, m, lsum, n, g);
+          if (two) attn_block(k1b, v1b, pb1, a.lo, a.hi, a.scale_log2, qf, o, m, lsum, n, g);
+        }
+      }
+      // next pair (long contexts): loaded after this pair ran, so that the
+      // register slots are free while it runs
+      attn_load(a, l, blk0 + ib + 2, j, R0, ib + 2 < nblk);
+      attn_load(a, l, blk0 + ib + 3, j, R1, ib + 3 < nblk);
     }
     if (rows) {
       lds_sync();
