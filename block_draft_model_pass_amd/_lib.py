@@ -38,6 +38,7 @@ class dflash_weights(ctypes.Structure):
         ("fc", c_void_p), ("hidden_norm", c_void_p),
         ("layer", dflash_layer_weights * 5),
         ("final_norm", c_void_p), ("embed", c_void_p), ("lm_head", c_void_p),
+        ("packed", c_void_p),
     ]
 
 
@@ -71,6 +72,10 @@ def load() -> ctypes.CDLL:
     P = ctypes.POINTER
     lib.dflash_workspace_size.argtypes = [P(dflash_weights), c_int32, c_int32]
     lib.dflash_workspace_size.restype = c_size_t
+    lib.dflash_packed_size.argtypes = [P(dflash_weights)]
+    lib.dflash_packed_size.restype = c_size_t
+    lib.dflash_pack_weights.argtypes = [P(dflash_weights), c_void_p]
+    lib.dflash_pack_weights.restype = c_int32
     lib.dflash_fuse_context.argtypes = [P(dflash_weights), c_void_p, c_int32, c_void_p,
                                         c_void_p, c_size_t, c_void_p]
     lib.dflash_fuse_context.restype = c_int32
@@ -108,6 +113,15 @@ def dflash_strerror(code: int) -> str:
 
 def dflash_workspace_size(w, max_rows: int, max_block: int) -> int:
     return int(load().dflash_workspace_size(_ref(w), max_rows, max_block))
+
+
+def dflash_packed_size(w) -> int:
+    return int(load().dflash_packed_size(_ref(w)))
+
+
+def dflash_pack_weights(w, stream=None, check=True):
+    rc = load().dflash_pack_weights(_ref(w), stream)
+    return _check(rc, "dflash_pack_weights") if check else rc
 
 
 def dflash_fuse_context(w, taps, n, ctx, ws, ws_bytes, stream=None, check=True):

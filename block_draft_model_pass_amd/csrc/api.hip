@@ -113,6 +113,11 @@ int check_kv(const dflash_kv* kv) {
   return DFLASH_OK;
 }
 
+// The streaming copy inside w->packed: the LM head.
+size_t packed_bytes(const dflash_weights* w) {
+  return sizeof(uint16_t) * static_cast<size_t>(w->vocab) * H;
+}
+
 SegTable seg1(const void* p, int rows) {
   SegTable t;
   memset(&t, 0, sizeof(t));
@@ -163,6 +168,19 @@ extern "C" size_t dflash_workspace_size(const dflash_weights* w, int32_t max_row
   if (max_rows < 0 || max_block < 0 || max_block > MAXB) return 0;
   const int fmt = w ? w->backbone_type : W_BF16;
   return layout().fixed + rows_bytes(max_rows, fmt);
+}
+
+extern "C" size_t dflash_packed_size(const dflash_weights* w) {
+  if (check_weights(w) != DFLASH_OK) return 0;
+  return packed_bytes(w);
+}
+
+extern "C" int32_t dflash_pack_weights(const dflash_weights* w, void* stream) {
+  int rc = check_weights(w);
+  if (rc) return rc;
+  if (!w->packed) return DFLASH_EINVAL;
+  HIP_TRY(launch_pack_bf16(w->lm_head, w->vocab, H, w->packed, static_cast<hipStream_t>(stream)));
+  return DFLASH_OK;
 }
 
 extern "C" int32_t dflash_fuse_context(const dflash_weights* w, const void* taps, int32_t n,
@@ -285,6 +303,7 @@ extern "C" int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* 
   const Layout Lw = layout();
   if (ws_bytes < Lw.fixed) return DFLASH_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!w->packed) return DFLASH_EINVAL;  // the streaming copy (dflash_pack_weights)
   const int grid = pass_grid();
   if (grid < QKV_N / 32) return DFLASH_EHIP;  // the pass needs >= 224 resident blocks
   PassLaunch q;
@@ -305,7 +324,7 @@ extern "C" int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* 
   }
   q.final_norm = u16p(w->final_norm);
   q.embed = u16p(w->embed);
-  q.lm = u16p(w->lm_head);
+  q.lm = u16p(w->packed);  // streaming copy of the LM head
   q.vocab = w->vocab;
   q.eps = w->rms_eps;
   q.scale_log2 = w->attn_scale * 1.4426950408889634f;

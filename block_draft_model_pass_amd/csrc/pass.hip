@@ -260,16 +260,28 @@ __device__ __forceinline__ void grid_sync(const PassArgs& a, unsigned& k) {
 
 // ---------------------------------------------------------------- GEMV pieces
 
-// nw weight uint4 of one lane: k = kbeg + 32 i + 8 g, i < nw (row = wrow).
+// The LM head is read from its streaming copy: 16-row tiles, then 32-wide
+// k blocks, then the 64 MFMA lanes (lane = row % 16 + 16 g), 16 bytes each,
+// so a wave's load of one k block is 1 KiB of contiguous memory -- 1.5x the
+// streaming rate of 64 bytes from each of 16 rows.  (The layer matrices,
+// which every block fetches in a burst ahead of a grid barrier, are faster
+// in their row-major layout, measured.)  Element offset of lane
+// (row % 16, g)'s 8 values of k block kb:
+__device__ __forceinline__ size_t packed_off(int K, int row, int kb, int g) {
+  return ((static_cast<size_t>(row >> 4) * (K >> 5) + kb) * 64 + (row & 15) + 16 * g) * 8;
+}
+
+// nw weight uint4 of one lane: k = kbeg + 32 i + 8 g, i < nw, of row `row`
+// of the packed bf16 matrix m (K columns).
 // Every element is defined on every path (zero when !valid or i >= nw) so
 // that no stale register value stays live across phases.
 template <int NMAX>
-__device__ __forceinline__ void load_tile(uint4 (&w)[NMAX], const uint16_t* wrow, int kbeg, int g,
-                                          int nw, bool valid) {
+__device__ __forceinline__ void load_tile(uint4 (&w)[NMAX], const uint16_t* m, int K, int row,
+                                          int kbeg, int g, int nw, bool valid) {
   if (valid) {
 #pragma unroll
     for (int i = 0; i < NMAX; ++i)
-      w[i] = i < nw ? ldw(wrow + kbeg + 32 * i + 8 * g) : make_uint4(0, 0, 0, 0);
+      w[i] = i < nw ? ldw(m + packed_off(K, row, (kbeg >> 5) + i, g)) : make_uint4(0, 0, 0, 0);
   } else {
 #pragma unroll
     for (int i = 0; i < NMAX; ++i) w[i] = make_uint4(0, 0, 0, 0);
@@ -1140,8 +1152,8 @@ __device__ __forceinline__ void lm_prefetch(const PassArgs& a, int pair, uint4 (
   const int wave = otid() >> 6, lane = otid() & 63;
   const int tile = 2 * pair + (wave >> 2);
   const bool has = tile < a.vocab / 16;
-  load_tile<20>(W, a.lm + static_cast<size_t>((has ? tile : 0) * 16 + (lane & 15)) * H,
-                (wave & 3) * 640, lane >> 4, 20, go && has);
+  load_tile<20>(W, a.lm, H, (has ? tile : 0) * 16 + (lane & 15), (wave & 3) * 640, lane >> 4, 20,
+                go && has);
 }
 
 __device__ __forceinline__ uint64_t umax64(uint64_t x, uint64_t y) { return x > y ? x : y; }

@@ -9,6 +9,7 @@ import torch
 
 from . import _lib, synth
 from ._lib import (dflash_draft_block, dflash_fuse_context, dflash_kv,
+                   dflash_lm_head_argmax, dflash_pack_weights, dflash_packed_size,
                    dflash_project_ctx_kv, dflash_verify_greedy, dflash_weights,
                    dflash_workspace_size)
 
@@ -56,6 +57,10 @@ class DeviceWeights:
         d.final_norm = self.t["final_norm"].data_ptr()
         d.embed = self.t["embed"].data_ptr()
         d.lm_head = self.t["lm_head"].data_ptr()
+        # streaming copy of the bf16 matrices the draft pass reads
+        self.packed = torch.empty(dflash_packed_size(d), dtype=torch.uint8, device=device)
+        d.packed = self.packed.data_ptr()
+        dflash_pack_weights(d, stream_ptr())
         self.desc = d
         self.vocab = d.vocab
 

@@ -103,6 +103,12 @@ typedef struct {
   const void* final_norm;  /* bf16 [2560]                                     */
   const void* embed;       /* bf16 [vocab][2560] target embedding (shared)    */
   const void* lm_head;     /* bf16 [vocab][2560] target LM head (shared)      */
+  /* Device buffer of dflash_packed_size() bytes holding the streaming copy
+   * of the LM head that the draft pass reads, written by dflash_pack_weights
+   * after the weights are loaded (and again whenever lm_head changes).
+   * Required by dflash_draft_block (NULL -> DFLASH_EINVAL); every other call
+   * reads the row-major tensors above.  Caller-owned, like everything else. */
+  void* packed;
 } dflash_weights;
 
 /* Drafter-owned context K/V ("Owned DFlash K/V state": fp16, one state per
@@ -128,6 +134,19 @@ typedef struct {
 size_t dflash_workspace_size(const dflash_weights* w, int32_t max_rows,
                              int32_t max_block);
 
+/* Bytes of the streaming copy of the LM head (2 * vocab * 2560).  0 for an
+ * invalid descriptor. */
+size_t dflash_packed_size(const dflash_weights* w);
+
+/* Writes the streaming copy of the LM head into w->packed, enqueued on
+ * `stream`.  The [vocab][2560] bf16 matrix becomes, in order, its 16-row
+ * tiles; within a tile its 32-wide k blocks; within a block the 64 lanes of
+ * an MFMA 16x16x32 A operand (lane L holds row L%16, k 8*(L/16) .. +8), 16
+ * bytes per lane -- so every 64-lane load of the draft pass's LM head sweep
+ * reads 1 KiB of contiguous memory instead of 64 bytes from each of 16 rows.
+ * Returns DFLASH_EINVAL if w->packed is NULL. */
+int32_t dflash_pack_weights(const dflash_weights* w, void* stream);
+
 /* Context fusion ("Drafter runtime": rmsnorm(fc(concat(target taps)))).
  *   taps: bf16 [n][5][2560], the five target taps of each position in tap order
  *   ctx : bf16 [n][2560] output, ctx[t] = rmsnorm(fc . concat(taps[t]), hidden_norm)
@@ -152,7 +171,8 @@ int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ctx, int32_t 
  *   cand      : int32 [block-1]            greedy ids (lowest id on ties)
  *   logits_opt: bf16 [block-1][vocab] or NULL   LM-head logits of the mask rows
  *   hidden_opt: bf16 [block][2560] or NULL      final-normed hidden states
- * block in [1, 8]; anchor_id, mask_id in [0, vocab); p >= 0. */
+ * block in [1, 8]; anchor_id, mask_id in [0, vocab); p >= 0.  Reads the
+ * streaming copy w->packed (see dflash_pack_weights), which must be current. */
 int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* kv, int64_t p,
                            int32_t anchor_id, int32_t mask_id, int32_t block,
                            int32_t* cand, void* logits_opt, void* hidden_opt,

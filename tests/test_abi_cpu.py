@@ -162,3 +162,17 @@ def test_workspace_too_small(lib):
     need_rows = _lib.dflash_workspace_size(w, 4096, 8)
     assert _lib.dflash_fuse_context(w, 1, 4096, 1, 1, need_rows - 1, check=False) == W
     assert _lib.dflash_project_ctx_kv(w, 1, 4096, 0, kv, 1, need_rows - 1, check=False) == W
+
+
+def test_packed_copy_size_and_checks(lib):
+    """The streaming copy holds the LM head; packing needs a buffer and the
+    draft pass needs the copy."""
+    w = fake_weights()
+    lm = 2 * synth.VOCAB * 2560
+    assert _lib.dflash_packed_size(w) == lm
+    assert _lib.dflash_packed_size(fake_weights(backbone_type=_lib.DFLASH_W_Q8_0)) == lm
+    assert _lib.dflash_packed_size(fake_weights(hidden=4096)) == 0
+    assert _lib.dflash_pack_weights(w, None, check=False) == _lib.DFLASH_EINVAL
+    big = 1 << 40
+    assert _lib.dflash_draft_block(w, fake_kv(), 10, 1, 2, 8, 1, None, None, 1, big,
+                                   check=False) == _lib.DFLASH_EINVAL
