@@ -383,7 +383,8 @@ extern "C" int32_t dflash_lm_head_argmax(const dflash_weights* w, const void* hi
   if (rows < 1 || rows > MAXB || !hidden || !cand || !ws) return DFLASH_EINVAL;
   const Layout Lw = layout();
   if (ws_bytes < Lw.fixed) return DFLASH_EWORKSPACE;
-  HIP_TRY(launch_lmhead_argmax(u16p(w->lm_head), w->vocab, u16p(hidden), rows,
+  HIP_TRY(launch_lmhead_argmax(w->packed ? u16p(w->packed) : u16p(w->lm_head), w->packed != nullptr,
+                               w->vocab, u16p(hidden), rows,
                                at<uint64_t>(ws, Lw.keys), LMH_GRID,
                                static_cast<uint16_t*>(logits_opt), cand,
                                static_cast<hipStream_t>(stream)));

@@ -203,8 +203,9 @@ hipError_t launch_dequant_bf16(const void* src, int fmt, int rows, int K, uint16
                                hipStream_t st);
 
 // LM head + greedy argmax over the vocabulary.
-hipError_t launch_lmhead_argmax(const uint16_t* lm, int vocab, const uint16_t* z, int B,
-                                uint64_t* keys, int grid, uint16_t* logits_opt,
+// lm: row-major [vocab][2560], or its streaming copy when `packed`.
+hipError_t launch_lmhead_argmax(const uint16_t* lm, bool packed, int vocab, const uint16_t* z,
+                                int B, uint64_t* keys, int grid, uint16_t* logits_opt,
                                 int32_t* cand, hipStream_t st);
 
 // Row RMSNorm: v = (h ? h[b] : 0) + sum_s part[s][b]; if h, h[b] = v;

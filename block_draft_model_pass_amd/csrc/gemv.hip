@@ -45,6 +45,21 @@ __device__ __forceinline__ void load_w(uint4 (&w)[4 * KBW], const uint16_t* wrow
   for (int i = 0; i < 4 * KBW; ++i) w[i] = ld16_stream(wrow + kbeg + 8 * (4 * i + g));
 }
 
+// Tile t's 16 rows from the LM head: row-major, or its streaming copy
+// (16-row tiles, 32-wide k blocks, 64 MFMA lanes of 16 bytes: one 1 KiB
+// contiguous run per wave load).
+template <int KBW, bool PACKED>
+__device__ __forceinline__ void load_lm(uint4 (&w)[4 * KBW], const uint16_t* lm, int t, int r,
+                                        int kbeg, int g) {
+  if constexpr (PACKED) {
+    const uint16_t* b = lm + ((static_cast<size_t>(t) * (H / 32) + kbeg / 32) * 64 + r + 16 * g) * 8;
+#pragma unroll
+    for (int i = 0; i < 4 * KBW; ++i) w[i] = ld16_stream(b + 512 * i);
+  } else {
+    load_w<KBW>(w, lm + (static_cast<size_t>(t) * 16 + r) * H, kbeg, g);
+  }
+}
+
 template <int KBW>
 __device__ __forceinline__ void load_x(uint4 (&x)[4 * KBW], const uint16_t* xrow, bool valid,
                                        int kbeg, int g) {
@@ -245,7 +260,7 @@ __device__ __forceinline__ void lm_epilogue(f32x4 acc, int row0, int r, int g, b
 // activation fragments of its k quarter in registers and double-buffers the
 // weight tiles; each block keeps the best (value, lowest index) key per
 // activation row and writes it once.
-template <int NW, int KBW>
+template <int NW, int KBW, bool PACKED>
 __global__ __launch_bounds__(NW * 64) void k_lmhead_bf16(const uint16_t* lm, int ntiles, int vocab,
                                                          const uint16_t* z, int B, uint64_t* keys,
                                                          uint16_t* logits) {
@@ -256,17 +271,16 @@ __global__ __launch_bounds__(NW * 64) void k_lmhead_bf16(const uint16_t* lm, int
   const int kbeg = wave * (KBW * 128);
   uint4 x[4 * KBW];
   load_x<KBW>(x, z + static_cast<size_t>(xv ? r : 0) * H, xv, kbeg, g);
-  const size_t roff = static_cast<size_t>(r) * H;
   uint64_t best = 0;
   const int step = gridDim.x;
   int t = blockIdx.x;
   uint4 wa[4 * KBW], wb[4 * KBW];
-  if (t < ntiles) load_w<KBW>(wa, lm + static_cast<size_t>(t) * 16 * H + roff, kbeg, g);
+  if (t < ntiles) load_lm<KBW, PACKED>(wa, lm, t, r, kbeg, g);
   int parity = 0;
   while (t < ntiles) {
     // tile t is in wa; prefetch t + step into wb, compute wa (then the roles swap)
     const int tn = t + step;
-    if (tn < ntiles) load_w<KBW>(wb, lm + static_cast<size_t>(tn) * 16 * H + roff, kbeg, g);
+    if (tn < ntiles) load_lm<KBW, PACKED>(wb, lm, tn, r, kbeg, g);
     __builtin_amdgcn_sched_barrier(0);
     f32x4 acc = mma_chain<KBW>(wa, x);
     if (wave > 0) red[parity][wave - 1][lane] = acc;
@@ -280,7 +294,7 @@ __global__ __launch_bounds__(NW * 64) void k_lmhead_bf16(const uint16_t* lm, int
     t = tn;
     if (t >= ntiles) break;
     const int tn2 = t + step;
-    if (tn2 < ntiles) load_w<KBW>(wa, lm + static_cast<size_t>(tn2) * 16 * H + roff, kbeg, g);
+    if (tn2 < ntiles) load_lm<KBW, PACKED>(wa, lm, tn2, r, kbeg, g);
     __builtin_amdgcn_sched_barrier(0);
     acc = mma_chain<KBW>(wb, x);
     if (wave > 0) red[parity][wave - 1][lane] = acc;
@@ -369,14 +383,18 @@ hipError_t launch_dequant_bf16(const void* src, int fmt, int rows, int K, uint16
   return hipGetLastError();
 }
 
-hipError_t launch_lmhead_argmax(const uint16_t* lm, int vocab, const uint16_t* z, int B,
-                                uint64_t* keys, int grid, uint16_t* logits_opt, int32_t* cand,
-                                hipStream_t st) {
+hipError_t launch_lmhead_argmax(const uint16_t* lm, bool packed, int vocab, const uint16_t* z,
+                                int B, uint64_t* keys, int grid, uint16_t* logits_opt,
+                                int32_t* cand, hipStream_t st) {
   if (B < 1 || B > MAXB || vocab % 16) return hipErrorInvalidValue;
   const int ntiles = vocab / 16;
   if (grid > ntiles) grid = ntiles;
-  hipLaunchKernelGGL((k_lmhead_bf16<4, 5>), dim3(grid), dim3(256), 0, st, lm, ntiles, vocab, z, B,
-                     keys, logits_opt);
+  if (packed)
+    hipLaunchKernelGGL((k_lmhead_bf16<4, 5, true>), dim3(grid), dim3(256), 0, st, lm, ntiles, vocab,
+                       z, B, keys, logits_opt);
+  else
+    hipLaunchKernelGGL((k_lmhead_bf16<4, 5, false>), dim3(grid), dim3(256), 0, st, lm, ntiles, vocab,
+                       z, B, keys, logits_opt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_argmax_reduce, dim3(1), dim3(MAXB * 64), 0, st, keys, grid, B, cand);

@@ -106,8 +106,9 @@ typedef struct {
   /* Device buffer of dflash_packed_size() bytes holding the streaming copy
    * of the LM head that the draft pass reads, written by dflash_pack_weights
    * after the weights are loaded (and again whenever lm_head changes).
-   * Required by dflash_draft_block (NULL -> DFLASH_EINVAL); every other call
-   * reads the row-major tensors above.  Caller-owned, like everything else. */
+   * Required by dflash_draft_block (NULL -> DFLASH_EINVAL) and used by
+   * dflash_lm_head_argmax when set; every other call reads the row-major
+   * tensors above.  Caller-owned, like everything else. */
   void* packed;
 } dflash_weights;
 
@@ -184,7 +185,8 @@ int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* kv, int64_t
  *   cand      : int32 [rows]       argmax_v (lm_head[v] . hidden[r]), lowest v on ties,
  *                                   decided on fp32 logits
  *   logits_opt: bf16 [rows][vocab] or NULL
- * rows in [1, 8].  dflash_draft_block runs the same kernels on its mask rows. */
+ * rows in [1, 8].  Reads w->packed when set, else w->lm_head; both give the
+ * same bits.  dflash_draft_block computes the same readout on its mask rows. */
 int32_t dflash_lm_head_argmax(const dflash_weights* w, const void* hidden, int32_t rows,
                               int32_t* cand, void* logits_opt, void* ws, size_t ws_bytes,
                               void* stream);

@@ -1,0 +1,83 @@
+"""GPU parity of the standalone LM-head argmax (the candidate readout of a
+block: logits = lm_head . hidden, greedy argmax with the lowest id on ties)
+against the oracle, through both layouts the entry point reads: the
+row-major bf16 matrix and its streaming copy.  Also checks that the
+streaming copy holds exactly the layout the header documents.
+
+Bars as for the draft pass: ids exact where the oracle's top-2 margin exceeds
+0.05; bf16 logits within 2e-2 per-row relative error.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_draft_model_pass_amd import _lib, synth
+from block_draft_model_pass_amd.device import Drafter, KVRing, stream_ptr
+from oracle import dflash_oracle as O
+from test_parity_gpu import MARGIN, TOL, dec_bf16, dev_w, host_w, ow, row_rel_err, say  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+H = synth.HIDDEN
+
+
+def lm_gpu(dev_w, packed: bool, z_bits: np.ndarray):
+    """Run dflash_lm_head_argmax on bf16 rows z_bits with or without the
+    streaming copy in the descriptor."""
+    d = _lib.dflash_weights.from_buffer_copy(dev_w.desc)
+    if not packed:
+        d.packed = None
+    rows = z_bits.shape[0]
+    dr = Drafter(dev_w, KVRing(256))
+    z = torch.from_numpy(z_bits.view(np.int16)).cuda()
+    cand = torch.empty(rows, dtype=torch.int32, device="cuda")
+    logits = torch.empty((rows, dev_w.vocab), dtype=torch.int16, device="cuda")
+    _lib.dflash_lm_head_argmax(d, z.data_ptr(), rows, cand.data_ptr(), logits.data_ptr(),
+                               dr.ws.data_ptr(), dr.ws_bytes, stream_ptr())
+    torch.cuda.synchronize()
+    return cand.cpu().numpy(), dec_bf16(logits)
+
+
+@pytest.mark.parametrize("rows", [1, 5, 8])
+@pytest.mark.parametrize("packed", [False, True], ids=["row_major", "streaming_copy"])
+def test_lm_head_argmax(dev_w, ow, rows, packed):
+    z_bits = synth.make_rows(rows, H, seed=91 + rows)
+    cand, logits = lm_gpu(dev_w, packed, z_bits)
+    ref = O.matvec_rows(ow, "lm_head", (dev_w.vocab, H), O.bf16_decode(z_bits))
+    err = row_rel_err(logits, ref)
+    ocand = np.array([O.argmax_lowest(r.astype(np.float32)) for r in ref])
+    top2 = np.sort(ref.astype(np.float32), axis=1)[:, -2:]
+    margin = top2[:, 1].astype(np.float64) - top2[:, 0]
+    say(f"lm head rows={rows} packed={packed} logits err {err:.3e} cand {cand.tolist()} "
+        f"ref {ocand.tolist()} margins {np.round(margin, 3).tolist()}")
+    assert err <= TOL
+    sure = margin > MARGIN
+    assert np.array_equal(cand[sure], ocand[sure])
+
+
+def test_lm_head_layouts_agree_bitwise(dev_w):
+    """Same sums in the same order from either layout: identical outputs."""
+    z_bits = synth.make_rows(8, H, seed=7)
+    c0, l0 = lm_gpu(dev_w, False, z_bits)
+    c1, l1 = lm_gpu(dev_w, True, z_bits)
+    assert np.array_equal(c0, c1)
+    assert np.array_equal(l0, l1)
+
+
+def test_streaming_copy_layout(dev_w, host_w):
+    """Element (row, k) of the LM head sits at 16-byte unit
+    ((row/16) * (2560/32) + k/32) * 64 + (row%16) + 16 * ((k%32)/8), element k%8."""
+    packed = dev_w.packed.view(torch.int16).cpu().numpy().view(np.uint16)
+    lm = host_w["lm_head"].reshape(dev_w.vocab, H)
+    assert packed.size == lm.size
+    rng = np.random.default_rng(3)
+    row = np.concatenate([rng.integers(0, dev_w.vocab, 20000), [0, dev_w.vocab - 1]])
+    k = np.concatenate([rng.integers(0, H, 20000), [0, H - 1]])
+    unit = ((row // 16) * (H // 32) + k // 32) * 64 + (row % 16) + 16 * ((k % 32) // 8)
+    assert np.array_equal(packed[unit * 8 + k % 8], lm[row, k])
+    # and whole first and last tiles
+    for t in (0, dev_w.vocab // 16 - 1):
+        r = np.repeat(np.arange(16) + 16 * t, H)
+        kk = np.tile(np.arange(H), 16)
+        unit = ((r // 16) * (H // 32) + kk // 32) * 64 + (r % 16) + 16 * ((kk % 32) // 8)
+        assert np.array_equal(packed[unit * 8 + kk % 8], lm[r, kk])
