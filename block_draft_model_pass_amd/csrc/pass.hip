@@ -109,6 +109,10 @@ __device__ __forceinline__ int otid() {
   return t;
 }
 
+// Wave index as a wave-uniform (scalar) value: conditions on it become scalar
+// branches, and pointers chosen by it come from scalar loads.
+__device__ __forceinline__ int wid() { return __builtin_amdgcn_readfirstlane(otid() >> 6); }
+
 // Per-layer weight pointers; the init kernel copies them into the workspace
 // so the pass kernel can index them by layer with plain global loads.
 struct LayerTab {
@@ -168,6 +172,15 @@ struct Smem {
   float mw[4 * 256];           // merge: chunk weights and partial sums
   uint64_t best[2][64];
 };
+
+// The layer table through the constant address space: indexed by the
+// (uniform) layer, its pointers arrive by scalar loads, which never make the
+// vector memory counter wait -- a vector load of a pointer would make the
+// loads that use it wait for every weight load still in flight.
+typedef const __attribute__((address_space(4))) LayerTab CLayerTab;
+__device__ __forceinline__ CLayerTab* ctab(const PassArgs& a) {
+  return reinterpret_cast<CLayerTab*>(reinterpret_cast<uintptr_t>(a.tab));
+}
 
 // ---------------------------------------------------------------- coherence
 
@@ -230,32 +243,43 @@ __device__ __forceinline__ unsigned ald(unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void grid_sync(const PassArgs& a, unsigned& k) {
+// Grid barrier whose waiting wave (wave 0) issues its share of the next
+// phase's weight loads between its arrival and its polling: its arrival
+// atomics go out ahead of those loads, while its loads still stream during
+// the wait.  (A wave's loads complete in order, so a prefetch issued before
+// the arrival would hold the arrival back by the prefetch's latency.)
+template <class Pf>
+__device__ __forceinline__ void grid_sync_pf(const PassArgs& a, unsigned& k, Pf&& wave0_prefetch) {
   lds_sync();
   ++k;
+  const unsigned goal = k * (gridDim.x < 8 ? gridDim.x : 8);
+  bool wait = false;
   if (otid() == 0) {
     unsigned* bar = a.bar;
     const unsigned x = blockIdx.x & 7;  // blocks are dealt to the XCDs round robin
     const unsigned per = (gridDim.x + 7 - x) / 8;
-    const unsigned groups = gridDim.x < 8 ? gridDim.x : 8;
-    const unsigned goal = k * groups;
-    bool wait = true;
+    wait = true;
     if (__hip_atomic_fetch_add(bar + BAR_XCD + 64 * x, 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT) == k * per - 1)
       wait = __hip_atomic_fetch_add(bar + BAR_TOP, 1u, __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT) != goal - 1;
-    if (wait) {
-      unsigned n = 0;
-      while (ald(bar + BAR_TOP) < goal) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++n > a.spin_limit) {  // bounded: never hang the device
-          __hip_atomic_store(bar + BAR_STATUS, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
+  }
+  if (wid() == 0) wave0_prefetch();
+  if (otid() == 0 && wait) {
+    unsigned n = 0;
+    while (ald(a.bar + BAR_TOP) < goal) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++n > a.spin_limit) {  // bounded: never hang the device
+        __hip_atomic_store(a.bar + BAR_STATUS, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
       }
     }
   }
   lds_sync();
+}
+
+__device__ __forceinline__ void grid_sync(const PassArgs& a, unsigned& k) {
+  grid_sync_pf(a, k, [] {});
 }
 
 // ---------------------------------------------------------------- GEMV pieces
@@ -336,26 +360,36 @@ __device__ __forceinline__ uint4 ldb(const uint8_t* p) {
       uint4, __builtin_nontemporal_load(reinterpret_cast<const GA u32x4*>(reinterpret_cast<uintptr_t>(p))));
 }
 
-// nl loads of row `row` from kbeg; every element defined on every path.
+// nl loads of row `row` from kbeg (loads i >= nl repeat load 0 and are never
+// used).  One branch around the whole tile and straight-line loads inside:
+// per-load branches leave join points at which the compiler's wait-count
+// pass has to assume any load may still be in flight, and it then drains
+// the whole queue (weight prefetch included) before reusing a register.
 template <int FMT, int N>
 __device__ __forceinline__ void load_wt(WTile<FMT, N>& t, WMat m, int row, int kbeg, int g, int nl,
                                         bool valid) {
   const uint8_t* b = static_cast<const uint8_t*>(m.base);
   const size_t rk = static_cast<size_t>(row) * m.K;
   const size_t sb = static_cast<size_t>(row) * (m.K / 32) + kbeg / 32;  // first scale of the row range
+  if (valid) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const bool on = valid && i < nl;
-    if constexpr (FMT == W_BF16) {
-      t.q[i] = on ? ldb(b + 2 * (rk + kbeg + 32 * i + 8 * g)) : make_uint4(0, 0, 0, 0);
-    } else if constexpr (FMT == W_Q8_0) {
-      t.q[i] = on ? ldb(b + rk + kbeg + 64 * i + 16 * g) : make_uint4(0, 0, 0, 0);
-      t.s[i] = on ? gld<uint16_t>(b + static_cast<size_t>(m.rows) * m.K + 2 * (sb + 2 * i + (g >> 1)))
-                  : 0u;
-    } else {
-      t.q[i] = on ? ldb(b + (rk + kbeg) / 2 + 64 * i + 16 * g) : make_uint4(0, 0, 0, 0);
-      t.s[i] = on ? gld<uint16_t>(b + static_cast<size_t>(m.rows) * m.K / 2 + 2 * (sb + 4 * i + g))
-                  : 0u;
+    for (int i0 = 0; i0 < N; ++i0) {
+      const int i = i0 < nl ? i0 : 0;
+      if constexpr (FMT == W_BF16) {
+        t.q[i0] = ldb(b + 2 * (rk + kbeg + 32 * i + 8 * g));
+      } else if constexpr (FMT == W_Q8_0) {
+        t.q[i0] = ldb(b + rk + kbeg + 64 * i + 16 * g);
+        t.s[i0] = gld<uint16_t>(b + static_cast<size_t>(m.rows) * m.K + 2 * (sb + 2 * i + (g >> 1)));
+      } else {
+        t.q[i0] = ldb(b + (rk + kbeg) / 2 + 64 * i + 16 * g);
+        t.s[i0] = gld<uint16_t>(b + static_cast<size_t>(m.rows) * m.K / 2 + 2 * (sb + 4 * i + g));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i0 = 0; i0 < N; ++i0) {
+      t.q[i0] = make_uint4(0, 0, 0, 0);
+      if constexpr (FMT != W_BF16) t.s[i0] = 0u;
     }
   }
   if constexpr (FMT == W_BF16) t.s[0] = 0u;
@@ -404,30 +438,43 @@ __device__ __forceinline__ f32x4 group_sum(Smem& s, int w0, int n, int lane) {
 // x[b][k] = h[b][k] * rsqrt(mean_k h^2 + eps) * gain[k] for b < B, rounded to
 // the activation format XF (bf16, or fp16 beside quantized weights), into
 // LDS rows of stride H + pad.  np per-tile sums of squares are reduced in a
-// fixed order.  Every load (h and the sums) is issued in one round.
+// fixed order.  Split in two so that a phase can issue its own weight loads
+// between them: xn_load issues every load (h, the gains and the sums) in one
+// round, xn_finish reduces, scales and stores.
 constexpr int XN8 = MAXB * (H / 8) / NTHR;  // 8-element fp16 groups of h per thread (5)
 
-template <int XF>
-__device__ __forceinline__ void build_x_norm(const PassArgs& a, Smem& s, int ver, int np,
-                                             const uint16_t* gain) {
-  const int tid = otid(), wave = tid >> 6, lane = tid & 63;
+struct XnRegs {
+  uint4 h[XN8], g[XN8];
+  float sv[3];
+};
+
+__device__ __forceinline__ void xn_load(const PassArgs& a, XnRegs& x, int ver, int np,
+                                        const uint16_t* gain) {
+  const int tid = otid(), wave = wid(), lane = tid & 63;
   const int n8 = a.B * (H / 8);
   const uint16_t* hsrc = a.h16 + ver * HSTRIDE;
   const float* ssrc = a.ss + ver * SSTRIDE;
-  uint4 hv[XN8];
 #pragma unroll
   for (int u = 0; u < XN8; ++u) {
     const int e = tid + u * NTHR;
-    hv[u] = e < n8 ? gld<uint4>(hsrc + 8 * e) : make_uint4(0, 0, 0, 0);
+    // e >= n8 re-reads group 0 (never stored): no branch around the loads
+    x.h[u] = gld<uint4>(hsrc + 8 * (e < n8 ? e : 0));
+    x.g[u] = gld<uint4>(gain + (e % (H / 8)) * 8);
   }
-  if (wave < a.B) {
-    float sv[3];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int i = lane + 64 * q;
-      sv[q] = i < np ? gld<float>(ssrc + i * MAXB + wave) : 0.f;
-    }
-    const float v = wave_sum(sv[0] + sv[1] + sv[2]);
+  for (int q = 0; q < 3; ++q) {
+    const int i = lane + 64 * q;
+    const float v = gld<float>(ssrc + (i < np ? i : 0) * MAXB + (wave < MAXB ? wave : 0));
+    x.sv[q] = wave < a.B && i < np ? v : 0.f;
+  }
+}
+
+template <int XF>
+__device__ __forceinline__ void xn_finish(const PassArgs& a, Smem& s, const XnRegs& x) {
+  const int tid = otid(), wave = wid(), lane = tid & 63;
+  const int n8 = a.B * (H / 8);
+  if (wave < a.B) {
+    const float v = wave_sum(x.sv[0] + x.sv[1] + x.sv[2]);
     if (lane == 0) s.scal[wave] = 1.0f / sqrtf(v / static_cast<float>(H) + a.eps);
   }
   lds_sync();
@@ -438,9 +485,8 @@ __device__ __forceinline__ void build_x_norm(const PassArgs& a, Smem& s, int ver
     if (e < n8) {
       const int b = e / (H / 8), k = (e % (H / 8)) * 8;
       const float sc = s.scal[b];
-      const uint4 gg = gld<uint4>(gain + k);
-      const uint32_t hw[4] = {hv[u].x, hv[u].y, hv[u].z, hv[u].w};
-      const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
+      const uint32_t hw[4] = {x.h[u].x, x.h[u].y, x.h[u].z, x.h[u].w};
+      const uint32_t gw[4] = {x.g[u].x, x.g[u].y, x.g[u].z, x.g[u].w};
       uint32_t o[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -456,38 +502,65 @@ __device__ __forceinline__ void build_x_norm(const PassArgs& a, Smem& s, int ver
   lds_sync();
 }
 
-// Copy bf16 activations [B][K] from global into LDS rows of stride K + pad,
-// all loads in one round (K <= F: at most 15 uint4 per thread).
-__device__ __forceinline__ void copy_x(const PassArgs& a, Smem& s, const uint16_t* src, int K) {
-  const int tid = otid();
-  const int XS = K + XS_PAD;
-  const int n8 = a.B * (K / 8);
-  constexpr int U = (MAXB * F / 8 + NTHR - 1) / NTHR;
+template <int XF>
+__device__ __forceinline__ void build_x_norm(const PassArgs& a, Smem& s, int ver, int np,
+                                             const uint16_t* gain) {
+  XnRegs x;
+  xn_load(a, x, ver, np, gain);
+  xn_finish<XF>(a, s, x);
+}
+
+// Copy activations [B][K] from global into LDS rows of stride K + pad, in
+// two halves like the norm: cx_load issues every load in one round (groups
+// past the block's rows re-read group 0 and are never stored), cx_store
+// writes LDS.
+template <int K>
+struct CxRegs {
+  static constexpr int U = (MAXB * K / 8 + NTHR - 1) / NTHR;
   uint4 v[U];
+};
+
+template <int K>
+__device__ __forceinline__ void cx_load(const PassArgs& a, CxRegs<K>& c, const uint16_t* src) {
+  const int tid = otid();
+  const int n8 = a.B * (K / 8);
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
+  for (int u = 0; u < CxRegs<K>::U; ++u) {
     const int e = tid + u * NTHR;
-    v[u] = e < n8 ? gld<uint4>(src + 8 * e) : make_uint4(0, 0, 0, 0);
+    c.v[u] = gld<uint4>(src + 8 * (e < n8 ? e : 0));
   }
+}
+
+template <int K>
+__device__ __forceinline__ void cx_store(const PassArgs& a, Smem& s, const CxRegs<K>& c) {
+  const int tid = otid();
+  constexpr int XS = K + XS_PAD;
+  const int n8 = a.B * (K / 8);
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
+  for (int u = 0; u < CxRegs<K>::U; ++u) {
     const int e = tid + u * NTHR;
     if (e < n8) {
       const int b = e / (K / 8), k = (e % (K / 8)) * 8;
-      *reinterpret_cast<uint4*>(s.x + b * XS + k) = v[u];
+      *reinterpret_cast<uint4*>(s.x + b * XS + k) = c.v[u];
     }
   }
   lds_sync();
 }
 
-// h rows (this tile's 16 columns) += acc; per-tile sums of squares.  Runs on
-// the lanes of one wave holding the reduced tile.
-__device__ __forceinline__ void residual_epilogue(const PassArgs& a, f32x4 acc, int tile, int r,
-                                                  int g, int vin) {
+// The residual rows this lane updates (tile's 16 columns, row r), loaded at
+// the start of a phase so that the epilogue does not wait for them.
+__device__ __forceinline__ float4 residual_load(const PassArgs& a, int tile, int r, int g, int vin) {
+  // rows past the block re-read row 0 (never used): no branch around the load
+  return gld<float4>(a.h + vin * HSTRIDE + static_cast<size_t>(r < a.B ? r : 0) * H + tile * 16 + 4 * g);
+}
+
+// h rows (this tile's 16 columns) += acc, hv = residual_load(...); per-tile
+// sums of squares.  Runs on the lanes of one wave holding the reduced tile.
+__device__ __forceinline__ void residual_epilogue(const PassArgs& a, f32x4 acc, float4 hv,
+                                                  int tile, int r, int g, int vin) {
   float sq = 0.f;
   if (r < a.B) {
     const size_t off = static_cast<size_t>(r) * H + tile * 16 + 4 * g;
-    const float4 hv = gld<float4>(a.h + vin * HSTRIDE + off);
     const f32x4 hn = {hv.x + acc[0], hv.y + acc[1], hv.z + acc[2], hv.w + acc[3]};
     st_coh_f4(a.h + (vin + 1) * HSTRIDE + off, hn);
     st_coh64(a.h16 + (vin + 1) * HSTRIDE + off,
@@ -509,10 +582,10 @@ __device__ __forceinline__ void residual_epilogue(const PassArgs& a, f32x4 acc, 
 // Tiles never straddle the q / k / v matrices (6144 and 512 rows).
 __device__ __forceinline__ WMat qkv_mat(const PassArgs& a, int l, int tile, int& row0) {
   const int r0 = tile * 16;
-  if (r0 < NQ * D) { row0 = r0; return WMat{a.tab->wq[l], NQ * D, H}; }
-  if (r0 < NQ * D + NKV * D) { row0 = r0 - NQ * D; return WMat{a.tab->wk[l], NKV * D, H}; }
+  if (r0 < NQ * D) { row0 = r0; return WMat{ctab(a)->wq[l], NQ * D, H}; }
+  if (r0 < NQ * D + NKV * D) { row0 = r0 - NQ * D; return WMat{ctab(a)->wk[l], NKV * D, H}; }
   row0 = r0 - NQ * D - NKV * D;
-  return WMat{a.tab->wv[l], NKV * D, H};
+  return WMat{ctab(a)->wv[l], NKV * D, H};
 }
 
 __device__ __forceinline__ bool qkv_has(int w) { return w < QKV_N / 32; }
@@ -521,7 +594,7 @@ template <int FMT> using QkvTile = WTile<FMT, 640 / KPerLoad<FMT>::v>;
 
 template <int FMT>
 __device__ __forceinline__ void qkv_prefetch(const PassArgs& a, int l, QkvTile<FMT>& W, bool go) {
-  const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
+  const int w = blockIdx.x, wave = wid(), lane = otid() & 63;
   const bool has = qkv_has(w);
   int row0;
   const WMat m = qkv_mat(a, l, has ? 2 * w + (wave >> 2) : 0, row0);
@@ -531,11 +604,14 @@ __device__ __forceinline__ void qkv_prefetch(const PassArgs& a, int l, QkvTile<F
 
 template <int FMT>
 __device__ __forceinline__ void qkv_phase(const PassArgs& a, Smem& s, int l, int np, QkvTile<FMT>& W) {
-  const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
+  const int w = blockIdx.x, wave = wid(), lane = otid() & 63;
   const int r = lane & 15, g = lane >> 4;
   const bool has = qkv_has(w);
-  if (wave == 0) qkv_prefetch<FMT>(a, l, W, true);
-  if (has) build_x_norm<FMT>(a, s, 2 * l, np, a.tab->in_norm[l]);
+  // activation loads first: a wave's loads complete in order, and every wave
+  // waits for the activations at the LDS rendezvous
+  XnRegs x;
+  if (has) xn_load(a, x, 2 * l, np, ctab(a)->in_norm[l]);
+  if (has) xn_finish<FMT>(a, s, x);
   if (has) {
     const int tile = 2 * w + (wave >> 2);
     constexpr int XS = H + XS_PAD;
@@ -587,10 +663,15 @@ __device__ __forceinline__ void attn_load(const PassArgs& a, int l, int ib_globa
   const uint16_t *kp = nullptr, *vp = nullptr;
   const bool ok = go && attn_block_src(a, l, ib_global, kp, vp, j);
   const int tid = otid();
+  if (ok) {
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    R.v[u] = ok ? ldw(kp + 8 * (tid + u * NTHR)) : make_uint4(0, 0, 0, 0);
-    R.v[2 + u] = ok ? ldw(vp + 8 * (tid + u * NTHR)) : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < 2; ++u) {
+      R.v[u] = ldw(kp + 8 * (tid + u * NTHR));
+      R.v[2 + u] = ldw(vp + 8 * (tid + u * NTHR));
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) R.v[u] = make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -618,7 +699,7 @@ __device__ __forceinline__ void attn_store(const KVRegs& R, uint16_t* kbuf, uint
 }
 
 // Waves other than 0 load their share of the chunk's first block before the
-// barrier; wave 0 (which runs the barrier) loads its share right after it.
+// barrier; wave 0 (which runs the barrier) loads its share while it waits.
 __device__ __forceinline__ void attn_prefetch(const PassArgs& a, int l, KVRegs& R0, KVRegs& R1,
                                               bool go) {
   const int w = blockIdx.x;
@@ -770,7 +851,7 @@ __device__ __forceinline__ void attn_query(const PassArgs& a, int l, int j, int 
     for (int e = 0; e < 8; ++e) sq += qv8[si][e] * qv8[si][e];
   sq = group4_sum(sq);
   const float sc = 1.0f / sqrtf(sq / static_cast<float>(D) + a.eps);
-  const uint16_t* gq = a.tab->q_norm[l];
+  const uint16_t* gq = ctab(a)->q_norm[l];
   uint32_t pk[8][4];
 #pragma unroll
   for (int si = 0; si < 4; ++si) {
@@ -805,7 +886,7 @@ __device__ __forceinline__ void attn_query(const PassArgs& a, int l, int j, int 
 // b < B, values [256][32]); wave b = row b.
 __device__ __forceinline__ void attn_block_rows(const PassArgs& a, int l, int j, uint16_t* kl,
                                                 uint16_t* vl) {
-  const int wave = otid() >> 6, lane = otid() & 63;
+  const int wave = wid(), lane = otid() & 63;
   if (wave >= a.B) return;
   const int b = wave;
   const uint16_t* kr = a.qkv + l * QSTRIDE + static_cast<size_t>(b) * QKV_N + NQ * D + j * D;
@@ -817,7 +898,7 @@ __device__ __forceinline__ void attn_block_rows(const PassArgs& a, int l, int j,
   for (int q = 0; q < 4; ++q) vv[q] = f16_bits_to_f32(gld<uint16_t>(vr + lane + 64 * q));
   const float sq = wave_sum(k0 * k0 + k1 * k1 + k2 * k2 + k3 * k3);
   const float sc = 1.0f / sqrtf(sq / static_cast<float>(D) + a.eps);
-  const uint16_t* gn = a.tab->k_norm[l];
+  const uint16_t* gn = ctab(a)->k_norm[l];
   k0 *= sc * bf16_to_f32(gld<uint16_t>(gn + lane));
   k1 *= sc * bf16_to_f32(gld<uint16_t>(gn + lane + 64));
   k2 *= sc * bf16_to_f32(gld<uint16_t>(gn + lane + 128));
@@ -839,7 +920,7 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KV
   const int w = blockIdx.x;
   if (w < NKV * a.nch) {
     const int j = w / a.nch, c = w % a.nch;
-    const int wave = otid() >> 6, lane = otid() & 63;
+    const int wave = wid(), lane = otid() & 63;
     const int n = lane & 15, g = lane >> 4;
     const int blk0 = c * a.cb;
     const int nblk = a.nb > blk0 ? min(a.cb, a.nb - blk0) : 0;
@@ -847,10 +928,6 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KV
     // LDS: block buffers (keys then values) at 0 and 2 x 8192, block rows at 4 x 8192
     uint16_t* kl = s.x + 4 * BLK_CELLS * D;
     uint16_t* vl = s.x + 5 * BLK_CELLS * D;
-    if (wave == 0) {
-      attn_load(a, l, blk0, j, R0, nblk > 0);
-      attn_load(a, l, blk0 + 1, j, R1, nblk > 1);
-    }
     uint4 qf[8];
     if (wave < a.nqt) attn_query(a, l, j, wave, n, g, qf);
     if (rows) attn_block_rows(a, l, j, kl, vl);
@@ -932,7 +1009,8 @@ __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
   if (blockIdx.x >= w0) {
     const int tid = otid(), half = tid >> 8, ht = tid & 255, lane = tid & 63;
     const int grp = 2 * (blockIdx.x - w0) + half;
-    const int n = grp & 15, t = (grp >> 4) % a.nqt, j = (grp >> 4) / a.nqt;
+    const int gc = grp < ngroup ? grp : 0;  // addresses stay inside the partials
+    const int n = gc & 15, t = (gc >> 4) % a.nqt, j = (gc >> 4) / a.nqt;
     const bool act = grp < ngroup && t * 16 + n < G * a.B;
     const int nc = a.nch;
     const size_t cstride = static_cast<size_t>(a.nqt) * 16;
@@ -945,7 +1023,7 @@ __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
 #pragma unroll
     for (int u = 0; u < MRG_U; ++u) {
       const int c = slot + 8 * u;
-      ov[u] = act && c < nc ? gld<uint4>(po + (row0 + c * cstride) * D + 8 * dp) : make_uint4(0, 0, 0, 0);
+      ov[u] = gld<uint4>(po + (row0 + (c < nc ? c : 0) * cstride) * D + 8 * dp);  // c >= nc: unused
     }
     if ((ht >> 6) == 0) {  // wave 0 of the half: chunk weights
       float mv[2], lv[2];
@@ -953,8 +1031,10 @@ __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int c = lane + 64 * q;
-        mv[q] = act && c < nc ? gld<float>(pm + row0 + c * cstride) : NEG_INF;
-        lv[q] = act && c < nc ? gld<float>(pl + row0 + c * cstride) : 0.f;
+        const float mraw = gld<float>(pm + row0 + (c < nc ? c : 0) * cstride);
+        const float lraw = gld<float>(pl + row0 + (c < nc ? c : 0) * cstride);
+        mv[q] = act && c < nc ? mraw : NEG_INF;
+        lv[q] = act && c < nc ? lraw : 0.f;
         M = fmaxf(M, mv[q]);
       }
 #pragma unroll
@@ -1019,26 +1099,28 @@ template <int FMT> using OTile = WTile<FMT, 768 / KPerLoad<FMT>::v>;
 
 template <int FMT>
 __device__ __forceinline__ void o_prefetch(const PassArgs& a, int l, OTile<FMT>& W, bool go) {
-  const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
+  const int w = blockIdx.x, wave = wid(), lane = otid() & 63;
   const bool has = w < NT_H;
   constexpr int N = 768 / KPerLoad<FMT>::v;
-  load_wt<FMT, N>(W, WMat{a.tab->wo[l], H, NQ * D}, (has ? w : 0) * 16 + (lane & 15), wave * 768,
+  load_wt<FMT, N>(W, WMat{ctab(a)->wo[l], H, NQ * D}, (has ? w : 0) * 16 + (lane & 15), wave * 768,
                   lane >> 4, N, go && has);
 }
 
 template <int FMT>
 __device__ __forceinline__ void o_phase(const PassArgs& a, Smem& s, int l, OTile<FMT>& W) {
-  const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
+  const int w = blockIdx.x, wave = wid(), lane = otid() & 63;
   const int r = lane & 15, g = lane >> 4;
   if (w < NT_H) {
-    if (wave == 0) o_prefetch<FMT>(a, l, W, true);
-    copy_x(a, s, a.o16 + l * OSTRIDE, NQ * D);
+    CxRegs<NQ * D> cx;
+    cx_load(a, cx, a.o16 + l * OSTRIDE);
+    const float4 hres = residual_load(a, w, r, g, 2 * l);  // used by wave 0
+    cx_store(a, s, cx);
     constexpr int XS = NQ * D + XS_PAD;
     constexpr int N = 768 / KPerLoad<FMT>::v;
     f32x4 acc = mma_wt<FMT, N>(W, s.x + xrow(r, a.B) * XS, wave * 768, g, N);
     s.red[wave][lane] = acc;
     lds_sync();
-    if (wave == 0) residual_epilogue(a, group_sum(s, 0, NWAVE, lane), w, r, g, 2 * l);
+    if (wave == 0) residual_epilogue(a, group_sum(s, 0, NWAVE, lane), hres, w, r, g, 2 * l);
   }
   wait_stores();
 }
@@ -1050,52 +1132,85 @@ template <int FMT> using GuTile = WTile<FMT, 640 / KPerLoad<FMT>::v>;
 template <int FMT>
 __device__ __forceinline__ void gu_prefetch(const PassArgs& a, int l, int pair, GuTile<FMT>& W,
                                             bool go) {
-  const int wave = otid() >> 6, lane = otid() & 63;
+  const int wave = wid(), lane = otid() & 63;
   const bool has = pair < F / 16;
   constexpr int N = 640 / KPerLoad<FMT>::v;
-  load_wt<FMT, N>(W, WMat{wave < 4 ? a.tab->wg[l] : a.tab->wu[l], F, H},
+  load_wt<FMT, N>(W, WMat{wave < 4 ? ctab(a)->wg[l] : ctab(a)->wu[l], F, H},
                   (has ? pair : 0) * 16 + (lane & 15), (wave & 3) * 640, lane >> 4, N, go && has);
 }
 
+// One gate/up tile pair from the weights in W: reduce the k quarters, write
+// silu(gate) * up for the block rows.
 template <int FMT>
-__device__ __forceinline__ void gu_phase(const PassArgs& a, Smem& s, int l, int np, GuTile<FMT>& W) {
-  const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
+__device__ __forceinline__ void gu_round(const PassArgs& a, Smem& s, int l, int pair,
+                                         const GuTile<FMT>& W) {
+  const int wave = wid(), lane = otid() & 63;
   const int r = lane & 15, g = lane >> 4;
-  const bool has = w < F / 16;
-  if (wave == 0) gu_prefetch<FMT>(a, l, w, W, true);
-  if (has) build_x_norm<FMT>(a, s, 2 * l + 1, np, a.tab->post_norm[l]);
   constexpr int XS = H + XS_PAD;
   constexpr int N = 640 / KPerLoad<FMT>::v;
-  for (int pair = w; pair < F / 16; pair += gridDim.x) {
-    f32x4 acc = mma_wt<FMT, N>(W, s.x + xrow(r, a.B) * XS, (wave & 3) * 640, g, N);
-    s.red[wave][lane] = acc;
-    lds_sync();
-    const int nxt = pair + gridDim.x;
-    if (nxt < F / 16) gu_prefetch<FMT>(a, l, nxt, W, true);  // next round's tiles
-    if (wave == 0) {
-      const f32x4 ag = group_sum(s, 0, 4, lane);
-      const f32x4 au = group_sum(s, 4, 4, lane);
-      if (r < a.B) {
-        uint16_t o[4];
+  f32x4 acc = mma_wt<FMT, N>(W, s.x + xrow(r, a.B) * XS, (wave & 3) * 640, g, N);
+  s.red[wave][lane] = acc;
+  lds_sync();
+  if (wave == 0) {
+    const f32x4 ag = group_sum(s, 0, 4, lane);
+    const f32x4 au = group_sum(s, 4, 4, lane);
+    if (r < a.B) {
+      uint16_t o[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float z = ag[i];
-          o[i] = act16<FMT>(z / (1.0f + __expf(-z)) * au[i]);
-        }
-        st_coh64(a.u16 + l * USTRIDE + static_cast<size_t>(r) * F + pair * 16 + 4 * g,
-                 static_cast<uint64_t>(o[0] | (static_cast<uint32_t>(o[1]) << 16)) |
-                     (static_cast<uint64_t>(o[2] | (static_cast<uint32_t>(o[3]) << 16)) << 32));
+      for (int i = 0; i < 4; ++i) {
+        const float z = ag[i];
+        o[i] = act16<FMT>(z / (1.0f + __expf(-z)) * au[i]);
       }
+      st_coh64(a.u16 + l * USTRIDE + static_cast<size_t>(r) * F + pair * 16 + 4 * g,
+               static_cast<uint64_t>(o[0] | (static_cast<uint32_t>(o[1]) << 16)) |
+                   (static_cast<uint64_t>(o[2] | (static_cast<uint32_t>(o[3]) << 16)) << 32));
     }
-    lds_sync();  // red[] reuse
+  }
+  lds_sync();  // red[] reuse
+}
+
+// The first pair's tiles were prefetched before the barrier (wave 0: during
+// it); the second pair's go out right behind the activation loads, into
+// a second register tile, so that they stream while the first pair runs.
+// Grids under 240 blocks take further pairs one at a time.
+template <int FMT>
+__device__ __forceinline__ void gu_phase(const PassArgs& a, Smem& s, int l, int np, GuTile<FMT>& W) {
+  const int w = blockIdx.x, wave = wid();
+  const bool has = w < F / 16;
+  if (has) {
+    XnRegs x;
+    xn_load(a, x, 2 * l + 1, np, ctab(a)->post_norm[l]);
+    // Unconditional: a block without a second pair re-reads its first (no
+    // branch, so the norm below waits only for the activation loads).
+    GuTile<FMT> W2;
+    const int p2 = w + gridDim.x;
+    {
+      const int lane = otid() & 63;
+      constexpr int N = 640 / KPerLoad<FMT>::v;
+      load_wt<FMT, N>(W2, WMat{wave < 4 ? ctab(a)->wg[l] : ctab(a)->wu[l], F, H},
+                      (p2 < F / 16 ? p2 : w) * 16 + (lane & 15), (wave & 3) * 640, lane >> 4, N,
+                      true);
+    }
+    xn_finish<FMT>(a, s, x);
+    gu_round<FMT>(a, s, l, w, W);
+    if (p2 < F / 16) gu_round<FMT>(a, s, l, p2, W2);
+    for (int pair = p2 + gridDim.x; pair < F / 16; pair += gridDim.x) {
+      gu_prefetch<FMT>(a, l, pair, W, true);
+      gu_round<FMT>(a, s, l, pair, W);
+    }
   }
   wait_stores();
 }
 
-// Down projection: block w < 160 owns row tile w; waves 0-3 take k ranges of
-// 1024 (k < 4096), waves 4-7 ranges of 896 (k >= 4096).
+// Down projection: block w < 160 owns row tile w and wave v a k range: 960
+// each for bf16 and Q8_0 (30 and 15 loads); Q4_0 loads cover 128 k, so its
+// waves 0-3 take 1024 (k < 4096) and waves 4-7 take 896.
+template <int FMT>
 __device__ __forceinline__ void down_range(int wave, int& kbeg, int& klen) {
-  if (wave < 4) {
+  if constexpr (FMT != W_Q4_0) {
+    kbeg = wave * (F / NWAVE);
+    klen = F / NWAVE;
+  } else if (wave < 4) {
     kbeg = wave * 1024;
     klen = 1024;
   } else {
@@ -1104,44 +1219,49 @@ __device__ __forceinline__ void down_range(int wave, int& kbeg, int& klen) {
   }
 }
 
-template <int FMT> using DownTile = WTile<FMT, 1024 / KPerLoad<FMT>::v>;
+template <int FMT>
+using DownTile = WTile<FMT, (FMT == W_Q4_0 ? 1024 : F / NWAVE) / KPerLoad<FMT>::v>;
 
 // Down projection tile w for blocks w < 160.  Only waves 1..DOWN_PRE_LAST
 // prefetch their k range during the gate/up phase (which those blocks spend
 // streaming two gate/up tile pairs): a full prefetch would lengthen that
-// phase by as much as it shortens this one.  The other waves load after the
-// barrier.
+// phase by as much as it shortens this one.  Wave 0 loads its range while it
+// waits at the barrier, the others after it.
 constexpr int DOWN_PRE_LAST = 3;
 
 __device__ __forceinline__ bool down_pre(int wave) { return wave >= 1 && wave <= DOWN_PRE_LAST; }
 
 template <int FMT>
 __device__ __forceinline__ void down_prefetch(const PassArgs& a, int l, DownTile<FMT>& W, bool go) {
-  const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
+  const int w = blockIdx.x, wave = wid(), lane = otid() & 63;
   const bool has = w < NT_H;
   int kbeg, klen;
-  down_range(wave, kbeg, klen);
-  constexpr int N = 1024 / KPerLoad<FMT>::v;
-  load_wt<FMT, N>(W, WMat{a.tab->wd[l], H, F}, (has ? w : 0) * 16 + (lane & 15), kbeg, lane >> 4,
+  down_range<FMT>(wave, kbeg, klen);
+  constexpr int N = sizeof(W.q) / sizeof(uint4);
+  load_wt<FMT, N>(W, WMat{ctab(a)->wd[l], H, F}, (has ? w : 0) * 16 + (lane & 15), kbeg, lane >> 4,
                   klen / KPerLoad<FMT>::v, go && has);
 }
 
 template <int FMT>
 __device__ __forceinline__ void down_phase(const PassArgs& a, Smem& s, int l, DownTile<FMT>& W) {
-  const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
+  const int w = blockIdx.x, wave = wid(), lane = otid() & 63;
   const int r = lane & 15, g = lane >> 4;
   const int tile = w;
   if (w < NT_H) {
-    if (!down_pre(wave)) down_prefetch<FMT>(a, l, W, true);
-    copy_x(a, s, a.u16 + l * USTRIDE, F);
+    CxRegs<F> cx;
+    cx_load(a, cx, a.u16 + l * USTRIDE);
+    const float4 hres = residual_load(a, tile, r, g, 2 * l + 1);  // used by wave 0
+    if (wave > DOWN_PRE_LAST) down_prefetch<FMT>(a, l, W, true);
+    cx_store(a, s, cx);
     int kbeg, klen;
-    down_range(wave, kbeg, klen);
+    down_range<FMT>(wave, kbeg, klen);
     constexpr int XS = F + XS_PAD;
-    constexpr int N = 1024 / KPerLoad<FMT>::v;
+    constexpr int N = sizeof(W.q) / sizeof(uint4);
     f32x4 acc = mma_wt<FMT, N>(W, s.x + xrow(r, a.B) * XS, kbeg, g, klen / KPerLoad<FMT>::v);
     s.red[wave][lane] = acc;
     lds_sync();
-    if (wave == 0) residual_epilogue(a, group_sum(s, 0, NWAVE, lane), tile, r, g, 2 * l + 1);
+    if (wave == 0)
+      residual_epilogue(a, group_sum(s, 0, NWAVE, lane), hres, tile, r, g, 2 * l + 1);
   }
   wait_stores();
 }
@@ -1149,7 +1269,7 @@ __device__ __forceinline__ void down_phase(const PassArgs& a, Smem& s, int l, Do
 // LM head: tile pairs p = w, w + grid, ...; wave v takes tile 2p + v/4 and k
 // quarter v%4.  Activations: final-normed rows 1..B-1 (row b in LDS row b).
 __device__ __forceinline__ void lm_prefetch(const PassArgs& a, int pair, uint4 (&W)[20], bool go) {
-  const int wave = otid() >> 6, lane = otid() & 63;
+  const int wave = wid(), lane = otid() & 63;
   const int tile = 2 * pair + (wave >> 2);
   const bool has = tile < a.vocab / 16;
   load_tile<20>(W, a.lm, H, (has ? tile : 0) * 16 + (lane & 15), (wave & 3) * 640, lane >> 4, 20,
@@ -1166,10 +1286,9 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
 }
 
 __device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, uint4 (&W)[20]) {
-  const int w = blockIdx.x, wave = otid() >> 6, lane = otid() & 63;
+  const int w = blockIdx.x, wave = wid(), lane = otid() & 63;
   const int r = lane & 15, g = lane >> 4;
   const int ntiles = a.vocab / 16, npairs = (ntiles + 1) / 2;
-  if (wave == 0) lm_prefetch(a, w, W, true);
   build_x_norm<W_BF16>(a, s, 2 * L, np, a.final_norm);
   constexpr int XS = H + XS_PAD;
   if (w == 0 && a.hidden) {
@@ -1252,7 +1371,7 @@ __device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, uin
 
 __device__ __forceinline__ void argmax_final(const PassArgs& a) {
   if (blockIdx.x != 0) return;
-  const int wave = otid() >> 6, lane = otid() & 63;
+  const int wave = wid(), lane = otid() & 63;
   if (wave + 1 >= a.B) return;  // wave b reduces mask row b + 1
   uint64_t best = 0;
   for (int i = lane; i < static_cast<int>(gridDim.x); i += 64)
@@ -1265,40 +1384,44 @@ __device__ __forceinline__ void argmax_final(const PassArgs& a) {
 template <int FMT>
 __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
   __shared__ Smem s;
-  const bool pre = (otid() >> 6) != 0;  // waves other than 0 prefetch before barriers
+  const bool pre = wid() != 0;  // waves other than 0 prefetch before barriers
   unsigned bk = 0;  // barriers passed
   QkvTile<FMT> Wq;
   uint4 Wl[20];     // LM head (bf16) slice, prefetched after the last layer
   // Layer 0 QKV weights stream while the grid lines up.
   qkv_prefetch<FMT>(a, 0, Wq, pre);
-  grid_sync(a, bk);  // h, ss, the RoPE table and the layer table come from the init kernel
+  // h, ss, the RoPE table and the layer table come from the init kernel
+  grid_sync_pf(a, bk, [&] { qkv_prefetch<FMT>(a, 0, Wq, true); });
   int np = 1;    // sums of squares of h: one entry per row from the init kernel
   for (int l = 0; l < L; ++l) {
     qkv_phase<FMT>(a, s, l, np, Wq);
     KVRegs R0, R1;
     attn_prefetch(a, l, R0, R1, pre);
-    grid_sync(a, bk);
+    grid_sync_pf(a, bk, [&] { attn_prefetch(a, l, R0, R1, true); });
     attn_phase(a, s, l, R0, R1);
     grid_sync(a, bk);
     merge_phase<FMT>(a, s, l);
     OTile<FMT> Wo;
     o_prefetch<FMT>(a, l, Wo, pre);
-    grid_sync(a, bk);
+    grid_sync_pf(a, bk, [&] { o_prefetch<FMT>(a, l, Wo, true); });
     o_phase<FMT>(a, s, l, Wo);
     GuTile<FMT> Wg;
     gu_prefetch<FMT>(a, l, blockIdx.x, Wg, pre);
-    grid_sync(a, bk);
+    grid_sync_pf(a, bk, [&] { gu_prefetch<FMT>(a, l, blockIdx.x, Wg, true); });
     gu_phase<FMT>(a, s, l, NT_H, Wg);
     DownTile<FMT> Wd;
-    down_prefetch<FMT>(a, l, Wd, down_pre(otid() >> 6));
-    grid_sync(a, bk);
+    down_prefetch<FMT>(a, l, Wd, down_pre(wid()));
+    grid_sync_pf(a, bk, [&] { down_prefetch<FMT>(a, l, Wd, true); });
     down_phase<FMT>(a, s, l, Wd);
     // Both prefetch targets are assigned on every iteration (zeros when
     // idle), so neither carries a value around the loop.
     const bool last = l + 1 == L;
     qkv_prefetch<FMT>(a, last ? l : l + 1, Wq, pre && !last);
     lm_prefetch(a, blockIdx.x, Wl, pre && last && a.B > 1);
-    grid_sync(a, bk);
+    grid_sync_pf(a, bk, [&] {
+      qkv_prefetch<FMT>(a, last ? l : l + 1, Wq, !last);
+      lm_prefetch(a, blockIdx.x, Wl, last && a.B > 1);
+    });
     np = NT_H;
   }
   if (a.B > 1) {
