@@ -1378,7 +1378,10 @@ __device__ __forceinline__ void argmax_final(const PassArgs& a) {
     best = umax64(best, ld_coh64(a.keys + static_cast<size_t>(i) * MAXB + wave));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) best = umax64(best, shfl_xor_u64(best, o));
-  if (lane == 0) a.cand[wave] = static_cast<int32_t>(~static_cast<uint32_t>(best));
+  // a grid barrier that gave up waiting leaves the pass's results undefined:
+  // report it through the candidates
+  const bool timed_out = ld_coh32(a.bar + BAR_STATUS) != 0u;
+  if (lane == 0) a.cand[wave] = timed_out ? -1 : static_cast<int32_t>(~static_cast<uint32_t>(best));
 }
 
 template <int FMT>
@@ -1536,7 +1539,13 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
                      : q.fmt == W_Q4_0 ? reinterpret_cast<const void*>(k_draft_pass<W_Q4_0>)
                                        : reinterpret_cast<const void*>(k_draft_pass<W_BF16>);
   void* args[] = {&a};
-  return hipLaunchCooperativeKernel(kern, dim3(q.grid), dim3(NTHR), args, 0, st);
+  // A plain launch: the grid is at most one block per CU, the most the device
+  // holds at once (draft_pass_max_grid), so every block is resident as soon
+  // as the device is not busy with other work.  (A cooperative launch adds
+  // about 20 us per pass on MI355X, measured.)  If other work keeps blocks
+  // from becoming resident for longer than the barriers' bounded wait, the
+  // pass reports it through cand = -1 instead of hanging.
+  return hipLaunchKernel(kern, dim3(q.grid), dim3(NTHR), args, 0, st);
 }
 
 hipError_t draft_pass_max_grid(int device, int* grid) {

@@ -173,7 +173,11 @@ int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ctx, int32_t 
  *   logits_opt: bf16 [block-1][vocab] or NULL   LM-head logits of the mask rows
  *   hidden_opt: bf16 [block][2560] or NULL      final-normed hidden states
  * block in [1, 8]; anchor_id, mask_id in [0, vocab); p >= 0.  Reads the
- * streaming copy w->packed (see dflash_pack_weights), which must be current. */
+ * streaming copy w->packed (see dflash_pack_weights), which must be current.
+ * The pass is one persistent kernel of one block per compute unit whose
+ * blocks wait for each other: it needs the whole device.  If other work keeps
+ * some of its blocks from starting for about half a second, the pass gives up
+ * waiting and sets every cand to -1 (its outputs are then undefined). */
 int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* kv, int64_t p,
                            int32_t anchor_id, int32_t mask_id, int32_t block,
                            int32_t* cand, void* logits_opt, void* hidden_opt,
