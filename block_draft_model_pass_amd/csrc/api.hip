@@ -113,9 +113,32 @@ int check_kv(const dflash_kv* kv) {
   return DFLASH_OK;
 }
 
-// The streaming copy inside w->packed: the LM head.
+// The streaming copies inside w->packed: the LM head, then (bf16 backbones)
+// every layer's wq, wk, wv, wo, wg, wu, wd.
+constexpr size_t LAYER_ELEMS = static_cast<size_t>(NQ * D) * H + 2 * static_cast<size_t>(NKV * D) * H +
+                               static_cast<size_t>(H) * NQ * D + 2 * static_cast<size_t>(F) * H +
+                               static_cast<size_t>(H) * F;
 size_t packed_bytes(const dflash_weights* w) {
-  return sizeof(uint16_t) * static_cast<size_t>(w->vocab) * H;
+  size_t e = static_cast<size_t>(w->vocab) * H;
+  if (w->backbone_type == DFLASH_W_BF16) e += L * LAYER_ELEMS;
+  return sizeof(uint16_t) * e;
+}
+
+// Packed copies of layer l's matrices (bf16 backbones).
+struct PackedLayer {
+  uint16_t *wq, *wk, *wv, *wo, *wg, *wu, *wd;
+};
+PackedLayer packed_layer(const dflash_weights* w, int l) {
+  uint16_t* p = static_cast<uint16_t*>(w->packed) + static_cast<size_t>(w->vocab) * H + l * LAYER_ELEMS;
+  PackedLayer r;
+  r.wq = p; p += static_cast<size_t>(NQ * D) * H;
+  r.wk = p; p += static_cast<size_t>(NKV * D) * H;
+  r.wv = p; p += static_cast<size_t>(NKV * D) * H;
+  r.wo = p; p += static_cast<size_t>(H) * NQ * D;
+  r.wg = p; p += static_cast<size_t>(F) * H;
+  r.wu = p; p += static_cast<size_t>(F) * H;
+  r.wd = p;
+  return r;
 }
 
 SegTable seg1(const void* p, int rows) {
@@ -179,7 +202,21 @@ extern "C" int32_t dflash_pack_weights(const dflash_weights* w, void* stream) {
   int rc = check_weights(w);
   if (rc) return rc;
   if (!w->packed) return DFLASH_EINVAL;
-  HIP_TRY(launch_pack_bf16(w->lm_head, w->vocab, H, w->packed, static_cast<hipStream_t>(stream)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIP_TRY(launch_pack_bf16(w->lm_head, w->vocab, H, w->packed, st));
+  if (w->backbone_type == DFLASH_W_BF16) {
+    for (int l = 0; l < L; ++l) {
+      const dflash_layer_weights& y = w->layer[l];
+      const PackedLayer p = packed_layer(w, l);
+      HIP_TRY(launch_pack_bf16(y.wq, NQ * D, H, p.wq, st));
+      HIP_TRY(launch_pack_bf16(y.wk, NKV * D, H, p.wk, st));
+      HIP_TRY(launch_pack_bf16(y.wv, NKV * D, H, p.wv, st));
+      HIP_TRY(launch_pack_bf16(y.wo, H, NQ * D, p.wo, st));
+      HIP_TRY(launch_pack_bf16(y.wg, F, H, p.wg, st));
+      HIP_TRY(launch_pack_bf16(y.wu, F, H, p.wu, st));
+      HIP_TRY(launch_pack_bf16(y.wd, H, F, p.wd, st));
+    }
+  }
   return DFLASH_OK;
 }
 
@@ -317,6 +354,16 @@ extern "C" int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* 
     q.wg[l] = u16p(y.wg);
     q.wu[l] = u16p(y.wu);
     q.wd[l] = u16p(y.wd);
+    if (w->backbone_type == DFLASH_W_BF16) {  // the pass streams the packed copies
+      const PackedLayer p = packed_layer(w, l);
+      q.wq[l] = p.wq;
+      q.wk[l] = p.wk;
+      q.wv[l] = p.wv;
+      q.wo[l] = p.wo;
+      q.wg[l] = p.wg;
+      q.wu[l] = p.wu;
+      q.wd[l] = p.wd;
+    }
     q.in_norm[l] = u16p(y.in_norm);
     q.q_norm[l] = u16p(y.q_norm);
     q.k_norm[l] = u16p(y.k_norm);

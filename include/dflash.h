@@ -103,10 +103,11 @@ typedef struct {
   const void* final_norm;  /* bf16 [2560]                                     */
   const void* embed;       /* bf16 [vocab][2560] target embedding (shared)    */
   const void* lm_head;     /* bf16 [vocab][2560] target LM head (shared)      */
-  /* Device buffer of dflash_packed_size() bytes holding the streaming copy
-   * of the LM head that the draft pass reads, written by dflash_pack_weights
-   * after the weights are loaded (and again whenever lm_head changes).
-   * Required by dflash_draft_block (NULL -> DFLASH_EINVAL) and used by
+  /* Device buffer of dflash_packed_size() bytes holding the streaming
+   * copies the draft pass reads (the LM head; with a bf16 backbone also every
+   * layer's seven matrices), written by dflash_pack_weights after the weights
+   * are loaded (and again whenever those tensors change).  Required by
+   * dflash_draft_block (NULL -> DFLASH_EINVAL) and used by
    * dflash_lm_head_argmax when set; every other call reads the row-major
    * tensors above.  Caller-owned, like everything else. */
   void* packed;
@@ -135,16 +136,22 @@ typedef struct {
 size_t dflash_workspace_size(const dflash_weights* w, int32_t max_rows,
                              int32_t max_block);
 
-/* Bytes of the streaming copy of the LM head (2 * vocab * 2560).  0 for an
- * invalid descriptor. */
+/* Bytes of the streaming copies: 2 * vocab * 2560 for the LM head, plus, for
+ * a bf16 backbone, 2 * 5 * (6144*2560 + 2*512*2560 + 2560*6144 + 2*7680*2560
+ * + 2560*7680) for the layer matrices.  0 for an invalid descriptor. */
 size_t dflash_packed_size(const dflash_weights* w);
 
-/* Writes the streaming copy of the LM head into w->packed, enqueued on
- * `stream`.  The [vocab][2560] bf16 matrix becomes, in order, its 16-row
- * tiles; within a tile its 32-wide k blocks; within a block the 64 lanes of
- * an MFMA 16x16x32 A operand (lane L holds row L%16, k 8*(L/16) .. +8), 16
- * bytes per lane -- so every 64-lane load of the draft pass's LM head sweep
- * reads 1 KiB of contiguous memory instead of 64 bytes from each of 16 rows.
+/* Writes the streaming copies into w->packed, enqueued on `stream`.  A bf16
+ * [N][K] matrix becomes, in order, its 16-row tiles; within a tile its
+ * 32-wide k blocks; within a block the 64 lanes of an MFMA 16x16x32 A operand
+ * (lane L holds row L%16, k 8*(L/16) .. +8), 16 bytes per lane -- so every
+ * 64-lane load of the draft pass reads 1 KiB of contiguous memory instead of
+ * 64 bytes from each of 16 rows.  Element (n, k) sits at
+ * ((n/16 * K/32 + k/32) * 64 + n%16 + 16 * ((k%32)/8)) * 8 + k%8.
+ * Order in the buffer: lm_head [vocab][2560]; then, for a bf16 backbone, for
+ * each layer 0..4: wq [6144][2560], wk [512][2560], wv [512][2560],
+ * wo [2560][6144], wg [7680][2560], wu [7680][2560], wd [2560][7680].
+ * (Q8_0 / Q4_0 layer matrices are read in their own layout.)
  * Returns DFLASH_EINVAL if w->packed is NULL. */
 int32_t dflash_pack_weights(const dflash_weights* w, void* stream);
 

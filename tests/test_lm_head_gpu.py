@@ -64,20 +64,39 @@ def test_lm_head_layouts_agree_bitwise(dev_w):
     assert np.array_equal(l0, l1)
 
 
+def packed_index(rows, cols, K):
+    """Element index of (row, k) in a streaming copy of a [N][K] matrix."""
+    unit = ((rows // 16) * (K // 32) + cols // 32) * 64 + (rows % 16) + 16 * ((cols % 32) // 8)
+    return unit * 8 + cols % 8
+
+
+def check_packed(packed, mat, rng, n_samples=20000):
+    N, K = mat.shape
+    row = np.concatenate([rng.integers(0, N, n_samples), [0, N - 1]])
+    k = np.concatenate([rng.integers(0, K, n_samples), [0, K - 1]])
+    assert np.array_equal(packed[packed_index(row, k, K)], mat[row, k])
+    # whole first and last tiles
+    for t in (0, N // 16 - 1):
+        r = np.repeat(np.arange(16) + 16 * t, K)
+        kk = np.tile(np.arange(K), 16)
+        assert np.array_equal(packed[packed_index(r, kk, K)], mat[r, kk])
+
+
 def test_streaming_copy_layout(dev_w, host_w):
-    """Element (row, k) of the LM head sits at 16-byte unit
-    ((row/16) * (2560/32) + k/32) * 64 + (row%16) + 16 * ((k%32)/8), element k%8."""
+    """Element (n, k) of each streamed matrix sits at 16-byte unit
+    ((n/16) * (K/32) + k/32) * 64 + (n%16) + 16 * ((k%32)/8), element k%8;
+    the LM head first, then layer by layer wq, wk, wv, wo, wg, wu, wd."""
     packed = dev_w.packed.view(torch.int16).cpu().numpy().view(np.uint16)
-    lm = host_w["lm_head"].reshape(dev_w.vocab, H)
-    assert packed.size == lm.size
     rng = np.random.default_rng(3)
-    row = np.concatenate([rng.integers(0, dev_w.vocab, 20000), [0, dev_w.vocab - 1]])
-    k = np.concatenate([rng.integers(0, H, 20000), [0, H - 1]])
-    unit = ((row // 16) * (H // 32) + k // 32) * 64 + (row % 16) + 16 * ((k % 32) // 8)
-    assert np.array_equal(packed[unit * 8 + k % 8], lm[row, k])
-    # and whole first and last tiles
-    for t in (0, dev_w.vocab // 16 - 1):
-        r = np.repeat(np.arange(16) + 16 * t, H)
-        kk = np.tile(np.arange(H), 16)
-        unit = ((r // 16) * (H // 32) + kk // 32) * 64 + (r % 16) + 16 * ((kk % 32) // 8)
-        assert np.array_equal(packed[unit * 8 + kk % 8], lm[r, kk])
+    V = dev_w.vocab
+    shapes = [("wq", 6144, H), ("wk", 512, H), ("wv", 512, H), ("wo", H, 6144),
+              ("wg", 7680, H), ("wu", 7680, H), ("wd", H, 7680)]
+    layer_elems = sum(n * k for _, n, k in shapes)
+    assert packed.size == V * H + 5 * layer_elems
+    check_packed(packed[:V * H], host_w["lm_head"].reshape(V, H), rng)
+    for l in (0, 4):
+        off = V * H + l * layer_elems
+        for name, n, k in shapes:
+            check_packed(packed[off:off + n * k], host_w[f"layers.{l}.{name}"].reshape(n, k), rng,
+                         n_samples=4000)
+            off += n * k
