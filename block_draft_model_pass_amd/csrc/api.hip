@@ -113,32 +113,56 @@ int check_kv(const dflash_kv* kv) {
   return DFLASH_OK;
 }
 
-// The streaming copies inside w->packed: the LM head, then (bf16 backbones)
-// every layer's wq, wk, wv, wo, wg, wu, wd.
-constexpr size_t LAYER_ELEMS = static_cast<size_t>(NQ * D) * H + 2 * static_cast<size_t>(NKV * D) * H +
-                               static_cast<size_t>(H) * NQ * D + 2 * static_cast<size_t>(F) * H +
-                               static_cast<size_t>(H) * F;
-size_t packed_bytes(const dflash_weights* w) {
-  size_t e = static_cast<size_t>(w->vocab) * H;
-  if (w->backbone_type == DFLASH_W_BF16) e += L * LAYER_ELEMS;
-  return sizeof(uint16_t) * e;
+// The streaming copies inside w->packed: the LM head (bf16), then every
+// layer's wq, wk, wv, wo, wg, wu, wd in the backbone's format: bf16, or the
+// Q8_0 / Q4_0 quants followed by their block scales, both regrouped per
+// 16-row tile and 64-byte row piece.
+struct PackedMat {
+  int N, K;
+};
+constexpr PackedMat LAYER_MATS[7] = {{NQ * D, H}, {NKV * D, H}, {NKV * D, H}, {H, NQ * D},
+                                     {F, H},      {F, H},       {H, F}};
+
+// Bytes of one [N][K] matrix in format fmt (quants, then scales).
+size_t mat_bytes(int fmt, size_t N, size_t K) {
+  if (fmt == DFLASH_W_Q8_0) return N * K + N * (K / 32) * 2;
+  if (fmt == DFLASH_W_Q4_0) return N * K / 2 + N * (K / 32) * 2;
+  return 2 * N * K;
 }
 
-// Packed copies of layer l's matrices (bf16 backbones).
-struct PackedLayer {
-  uint16_t *wq, *wk, *wv, *wo, *wg, *wu, *wd;
-};
-PackedLayer packed_layer(const dflash_weights* w, int l) {
-  uint16_t* p = static_cast<uint16_t*>(w->packed) + static_cast<size_t>(w->vocab) * H + l * LAYER_ELEMS;
-  PackedLayer r;
-  r.wq = p; p += static_cast<size_t>(NQ * D) * H;
-  r.wk = p; p += static_cast<size_t>(NKV * D) * H;
-  r.wv = p; p += static_cast<size_t>(NKV * D) * H;
-  r.wo = p; p += static_cast<size_t>(H) * NQ * D;
-  r.wg = p; p += static_cast<size_t>(F) * H;
-  r.wu = p; p += static_cast<size_t>(F) * H;
-  r.wd = p;
-  return r;
+size_t layer_bytes(int fmt) {
+  size_t b = 0;
+  for (const PackedMat& m : LAYER_MATS) b += mat_bytes(fmt, m.N, m.K);
+  return b;
+}
+
+size_t packed_bytes(const dflash_weights* w) {
+  return sizeof(uint16_t) * static_cast<size_t>(w->vocab) * H + L * layer_bytes(w->backbone_type);
+}
+
+// Packed copies of layer l's seven matrices, in LAYER_MATS order.
+void packed_layer(const dflash_weights* w, int l, uint8_t* (&out)[7]) {
+  uint8_t* p = static_cast<uint8_t*>(w->packed) + sizeof(uint16_t) * static_cast<size_t>(w->vocab) * H +
+               l * layer_bytes(w->backbone_type);
+  for (int i = 0; i < 7; ++i) {
+    out[i] = p;
+    p += mat_bytes(w->backbone_type, LAYER_MATS[i].N, LAYER_MATS[i].K);
+  }
+}
+
+// One matrix into its streaming copy: the 64-byte row pieces of the quants
+// (or bf16 values) move as the bf16 shuffle moves 32-element blocks; the
+// scales of a quantized matrix follow as 4-byte (Q8_0: one 64-k piece) or
+// 8-byte (Q4_0: one 128-k piece) units per row.
+hipError_t pack_matrix(int fmt, const void* src, int N, int K, void* dst, hipStream_t st) {
+  if (fmt == DFLASH_W_BF16) return launch_pack_bf16(src, N, K, dst, st);
+  const size_t qbytes = fmt == DFLASH_W_Q8_0 ? static_cast<size_t>(N) * K : static_cast<size_t>(N) * K / 2;
+  const int kq = fmt == DFLASH_W_Q8_0 ? K / 2 : K / 4;  // row bytes / 2 (bf16 units)
+  hipError_t e = launch_pack_bf16(src, N, kq, dst, st);
+  if (e != hipSuccess) return e;
+  const int per_row = fmt == DFLASH_W_Q8_0 ? K / 64 : K / 128;
+  return launch_pack_units(static_cast<const uint8_t*>(src) + qbytes, N, per_row,
+                           fmt == DFLASH_W_Q8_0 ? 4 : 8, static_cast<uint8_t*>(dst) + qbytes, st);
 }
 
 SegTable seg1(const void* p, int rows) {
@@ -204,18 +228,13 @@ extern "C" int32_t dflash_pack_weights(const dflash_weights* w, void* stream) {
   if (!w->packed) return DFLASH_EINVAL;
   hipStream_t st = static_cast<hipStream_t>(stream);
   HIP_TRY(launch_pack_bf16(w->lm_head, w->vocab, H, w->packed, st));
-  if (w->backbone_type == DFLASH_W_BF16) {
-    for (int l = 0; l < L; ++l) {
-      const dflash_layer_weights& y = w->layer[l];
-      const PackedLayer p = packed_layer(w, l);
-      HIP_TRY(launch_pack_bf16(y.wq, NQ * D, H, p.wq, st));
-      HIP_TRY(launch_pack_bf16(y.wk, NKV * D, H, p.wk, st));
-      HIP_TRY(launch_pack_bf16(y.wv, NKV * D, H, p.wv, st));
-      HIP_TRY(launch_pack_bf16(y.wo, H, NQ * D, p.wo, st));
-      HIP_TRY(launch_pack_bf16(y.wg, F, H, p.wg, st));
-      HIP_TRY(launch_pack_bf16(y.wu, F, H, p.wu, st));
-      HIP_TRY(launch_pack_bf16(y.wd, H, F, p.wd, st));
-    }
+  for (int l = 0; l < L; ++l) {
+    const dflash_layer_weights& y = w->layer[l];
+    const void* src[7] = {y.wq, y.wk, y.wv, y.wo, y.wg, y.wu, y.wd};
+    uint8_t* dst[7];
+    packed_layer(w, l, dst);
+    for (int i = 0; i < 7; ++i)
+      HIP_TRY(pack_matrix(w->backbone_type, src[i], LAYER_MATS[i].N, LAYER_MATS[i].K, dst[i], st));
   }
   return DFLASH_OK;
 }
@@ -347,23 +366,15 @@ extern "C" int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* 
   q.fmt = w->backbone_type;
   for (int l = 0; l < L; ++l) {
     const dflash_layer_weights& y = w->layer[l];
-    q.wq[l] = u16p(y.wq);
-    q.wk[l] = u16p(y.wk);
-    q.wv[l] = u16p(y.wv);
-    q.wo[l] = u16p(y.wo);
-    q.wg[l] = u16p(y.wg);
-    q.wu[l] = u16p(y.wu);
-    q.wd[l] = u16p(y.wd);
-    if (w->backbone_type == DFLASH_W_BF16) {  // the pass streams the packed copies
-      const PackedLayer p = packed_layer(w, l);
-      q.wq[l] = p.wq;
-      q.wk[l] = p.wk;
-      q.wv[l] = p.wv;
-      q.wo[l] = p.wo;
-      q.wg[l] = p.wg;
-      q.wu[l] = p.wu;
-      q.wd[l] = p.wd;
-    }
+    uint8_t* pm[7];  // the pass streams the packed copies
+    packed_layer(w, l, pm);
+    q.wq[l] = u16p(pm[0]);
+    q.wk[l] = u16p(pm[1]);
+    q.wv[l] = u16p(pm[2]);
+    q.wo[l] = u16p(pm[3]);
+    q.wg[l] = u16p(pm[4]);
+    q.wu[l] = u16p(pm[5]);
+    q.wd[l] = u16p(pm[6]);
     q.in_norm[l] = u16p(y.in_norm);
     q.q_norm[l] = u16p(y.q_norm);
     q.k_norm[l] = u16p(y.k_norm);

@@ -197,6 +197,10 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t st);
 // order, 16 bytes per lane); element (r, k) lands at
 // ((r/16 * K/32 + k/32) * 64 + r%16 + 16 * (k%32 / 8)) * 8 + k%8.
 hipError_t launch_pack_bf16(const void* src, int N, int K, void* dst, hipStream_t st);
+// Units of `unit` (4 or 8) bytes of an [N][per_row] array regrouped as 16-row
+// tiles x per_row x 16 rows (the block scales of a packed quantized matrix).
+hipError_t launch_pack_units(const void* src, int N, int per_row, int unit, void* dst,
+                             hipStream_t st);
 
 // Quantized [rows][K] matrix (fmt Q8_0 / Q4_0) -> bf16 [rows][K].
 hipError_t launch_dequant_bf16(const void* src, int fmt, int rows, int K, uint16_t* dst,

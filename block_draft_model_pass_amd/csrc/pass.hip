@@ -337,6 +337,9 @@ __device__ __forceinline__ int xrow(int r, int B) { return r < B ? r : 0; }
 //          + 8 m), all inside quant block kbeg/32 + 2 i + g/2.
 //   Q4_0 : load i is the whole quant block kbeg/32 + 4 i + g (four MFMAs:
 //          elements 8 m .. 8 m + 7 of the block).
+// Every format is read from the matrix's streaming copy, where the 64 lanes'
+// 16 bytes of one load are 1 KiB of contiguous memory (and the quantized
+// formats' scales of that load 64 or 128 contiguous bytes).
 // A quantized load carries its block's fp16 scale (raw bits, splatted at use
 // so that the load stays asynchronous); activations use the same k slots.
 template <int FMT> struct KPerLoad;  // k covered by one load of all four lane groups
@@ -369,20 +372,22 @@ template <int FMT, int N>
 __device__ __forceinline__ void load_wt(WTile<FMT, N>& t, WMat m, int row, int kbeg, int g, int nl,
                                         bool valid) {
   const uint8_t* b = static_cast<const uint8_t*>(m.base);
-  const size_t rk = static_cast<size_t>(row) * m.K;
-  const size_t sb = static_cast<size_t>(row) * (m.K / 32) + kbeg / 32;  // first scale of the row range
   if (valid) {
 #pragma unroll
     for (int i0 = 0; i0 < N; ++i0) {
       const int i = i0 < nl ? i0 : 0;
       if constexpr (FMT == W_BF16) {
         t.q[i0] = ldb(b + 2 * packed_off(m.K, row, (kbeg >> 5) + i, g));
-      } else if constexpr (FMT == W_Q8_0) {
-        t.q[i0] = ldb(b + rk + kbeg + 64 * i + 16 * g);
-        t.s[i0] = gld<uint16_t>(b + static_cast<size_t>(m.rows) * m.K + 2 * (sb + 2 * i + (g >> 1)));
-      } else {
-        t.q[i0] = ldb(b + (rk + kbeg) / 2 + 64 * i + 16 * g);
-        t.s[i0] = gld<uint16_t>(b + static_cast<size_t>(m.rows) * m.K / 2 + 2 * (sb + 4 * i + g));
+      } else if constexpr (FMT == W_Q8_0) {  // piece = 64 k: 1 KiB of quants, 64 B of scales
+        const size_t pc = static_cast<size_t>(row >> 4) * (m.K >> 6) + (kbeg >> 6) + i;
+        t.q[i0] = ldb(b + (pc * 64 + (row & 15) + 16 * g) * 16);
+        t.s[i0] = gld<uint16_t>(b + static_cast<size_t>(m.rows) * m.K +
+                                2 * (pc * 32 + (row & 15) * 2 + (g >> 1)));
+      } else {  // piece = 128 k: 1 KiB of quants, 128 B of scales
+        const size_t pc = static_cast<size_t>(row >> 4) * (m.K >> 7) + (kbeg >> 7) + i;
+        t.q[i0] = ldb(b + (pc * 64 + (row & 15) + 16 * g) * 16);
+        t.s[i0] = gld<uint16_t>(b + static_cast<size_t>(m.rows) * m.K / 2 +
+                                2 * (pc * 64 + (row & 15) * 4 + g));
       }
     }
   } else {

@@ -104,8 +104,8 @@ typedef struct {
   const void* embed;       /* bf16 [vocab][2560] target embedding (shared)    */
   const void* lm_head;     /* bf16 [vocab][2560] target LM head (shared)      */
   /* Device buffer of dflash_packed_size() bytes holding the streaming
-   * copies the draft pass reads (the LM head; with a bf16 backbone also every
-   * layer's seven matrices), written by dflash_pack_weights after the weights
+   * copies the draft pass reads (the LM head and every layer's seven
+   * matrices, in the backbone's format), written by dflash_pack_weights after the weights
    * are loaded (and again whenever those tensors change).  Required by
    * dflash_draft_block (NULL -> DFLASH_EINVAL) and used by
    * dflash_lm_head_argmax when set; every other call reads the row-major
@@ -136,9 +136,10 @@ typedef struct {
 size_t dflash_workspace_size(const dflash_weights* w, int32_t max_rows,
                              int32_t max_block);
 
-/* Bytes of the streaming copies: 2 * vocab * 2560 for the LM head, plus, for
- * a bf16 backbone, 2 * 5 * (6144*2560 + 2*512*2560 + 2560*6144 + 2*7680*2560
- * + 2560*7680) for the layer matrices.  0 for an invalid descriptor. */
+/* Bytes of the streaming copies: 2 * vocab * 2560 for the LM head plus the
+ * 35 layer matrices (5 x (6144*2560 + 2*512*2560 + 2560*6144 + 2*7680*2560 +
+ * 2560*7680) weights) at 2 (bf16), 34/32 (Q8_0) or 18/32 (Q4_0) bytes per
+ * weight.  0 for an invalid descriptor. */
 size_t dflash_packed_size(const dflash_weights* w);
 
 /* Writes the streaming copies into w->packed, enqueued on `stream`.  A bf16
@@ -148,10 +149,15 @@ size_t dflash_packed_size(const dflash_weights* w);
  * 64-lane load of the draft pass reads 1 KiB of contiguous memory instead of
  * 64 bytes from each of 16 rows.  Element (n, k) sits at
  * ((n/16 * K/32 + k/32) * 64 + n%16 + 16 * ((k%32)/8)) * 8 + k%8.
- * Order in the buffer: lm_head [vocab][2560]; then, for a bf16 backbone, for
- * each layer 0..4: wq [6144][2560], wk [512][2560], wv [512][2560],
- * wo [2560][6144], wg [7680][2560], wu [7680][2560], wd [2560][7680].
- * (Q8_0 / Q4_0 layer matrices are read in their own layout.)
+ * Order in the buffer: lm_head [vocab][2560]; then for each layer 0..4:
+ * wq [6144][2560], wk [512][2560], wv [512][2560], wo [2560][6144],
+ * wg [7680][2560], wu [7680][2560], wd [2560][7680].  A Q8_0 / Q4_0 matrix
+ * keeps its two parts: its quants get the same shuffle with each row seen as
+ * 64-byte pieces (64 k for Q8_0, 128 k for Q4_0) in place of 32-element bf16
+ * blocks, i.e. byte j of piece kb of row n at ((n/16 * P + kb) * 64 + n%16 +
+ * 16 * (j/16)) * 16 + j%16 with P pieces per row; its fp16 scales follow,
+ * the S = 2 (Q8_0) or 4 (Q4_0) scales of piece kb of row n at
+ * ((n/16 * P + kb) * 16 + n%16) * S + s.
  * Returns DFLASH_EINVAL if w->packed is NULL. */
 int32_t dflash_pack_weights(const dflash_weights* w, void* stream);
 

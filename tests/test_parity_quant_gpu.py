@@ -73,3 +73,44 @@ def test_quant_draft(qset, n, block):
 def test_quant_draft_no_context(qset):
     fmt, dev, ow = qset
     end_to_end(dev, ow, 0, 8, tag=f"{fmt} ctx0 b8")
+
+
+def test_quant_streaming_copy_layout(qset):
+    """Packed quants and scales of wq and wd (layers 0 and 4) against the
+    host bytes, by the layout the header documents: byte j of 64-byte piece
+    kb of row n at ((n/16 * P + kb) * 64 + n%16 + 16 * (j/16)) * 16 + j%16;
+    the S scales of piece kb of row n at ((n/16 * P + kb) * 16 + n%16) * S + s."""
+    fmt, dev, _ = qset
+    host = synth.make_weights(fmt=fmt)
+    packed = dev.packed.cpu().numpy()
+    H, V = synth.HIDDEN, dev.vocab
+    shapes = [("wq", 6144, H), ("wk", 512, H), ("wv", 512, H), ("wo", H, 6144),
+              ("wg", 7680, H), ("wu", 7680, H), ("wd", H, 7680)]
+    qb = (lambda n, k: n * k) if fmt == "q8_0" else (lambda n, k: n * k // 2)
+    mat_bytes = {name: qb(n, k) + n * (k // 32) * 2 for name, n, k in shapes}
+    layer_bytes = sum(mat_bytes.values())
+    rng = np.random.default_rng(11)
+    for l in (0, 4):
+        off = 2 * V * H + l * layer_bytes
+        for name, n, k in shapes:
+            raw = host[f"layers.{l}.{name}"].view(np.uint8)
+            mb = mat_bytes[name]
+            if name in ("wq", "wd"):
+                got = packed[off:off + mb]
+                rowb = qb(n, k) // n  # quant bytes per row
+                P = rowb // 64
+                rows = rng.integers(0, n, 3000)
+                js = rng.integers(0, rowb, 3000)
+                kb, j = js // 64, js % 64
+                idx = ((rows // 16 * P + kb) * 64 + rows % 16 + 16 * (j // 16)) * 16 + j % 16
+                assert np.array_equal(got[idx], raw[rows * rowb + js])
+                S = 2 if fmt == "q8_0" else 4
+                scales = raw[qb(n, k):].view(np.uint16).reshape(n, k // 32)
+                gs = got[qb(n, k):].view(np.uint16)
+                rows = rng.integers(0, n, 3000)
+                blk = rng.integers(0, k // 32, 3000)
+                kb, sidx = blk // S, blk % S
+                assert np.array_equal(gs[((rows // 16 * P + kb) * 16 + rows % 16) * S + sidx],
+                                      scales[rows, blk])
+            off += mb
+    assert packed.size == 2 * V * H + 5 * layer_bytes
