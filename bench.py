@@ -158,8 +158,12 @@ def main():
     n_pass = args.steps + args.warmup
     draws = [synth.target_draws(t, K) for t in range(n_pass)]
     match = torch.tensor(np.stack([d[0] for d in draws]), device="cuda")
-    offset = torch.tensor(np.stack([d[1] for d in draws]), dtype=torch.int64, device="cuda")
-    tail = torch.tensor([d[2] for d in draws], dtype=torch.int32, device="cuda")
+    # int32 throughout: cand + 1 + r < 2 V < 2^31
+    offset = torch.tensor(np.stack([d[1] for d in draws]) + 1, dtype=torch.int32, device="cuda")
+    # targets per pass: K slots filled from the candidates each cycle, then the
+    # stand-in target's continuation token
+    tgt_all = torch.zeros((n_pass, K + 1), dtype=torch.int32, device="cuda")
+    tgt_all[:, K] = torch.tensor([d[2] for d in draws], dtype=torch.int32, device="cuda")
     cand = torch.empty(K, dtype=torch.int32, device="cuda")
     out = torch.empty(2, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
@@ -168,9 +172,9 @@ def main():
 
     def cycle(t):
         dr.draft(state["p"], state["anchor"], BLOCK, cand=cand)
-        c = cand.to(torch.int64)
-        tgt = torch.where(match[t], c, (c + 1 + offset[t]) % V).to(torch.int32)
-        tgt = torch.cat([tgt, tail[t:t + 1]])
+        # stand-in target: the candidate where the draw matched, else another id
+        tgt = tgt_all[t]
+        torch.where(match[t], cand, torch.remainder(cand + offset[t], V), out=tgt[:K])
         dr.verify(cand, tgt, K, out=out)
         a, nxt = out.tolist()  # the cycle's one device->host read
         p = state["p"]

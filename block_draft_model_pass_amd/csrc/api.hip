@@ -137,7 +137,14 @@ size_t layer_bytes(int fmt) {
 }
 
 size_t packed_bytes(const dflash_weights* w) {
-  return sizeof(uint16_t) * static_cast<size_t>(w->vocab) * H + L * layer_bytes(w->backbone_type);
+  return sizeof(uint16_t) * static_cast<size_t>(w->vocab) * H + L * layer_bytes(w->backbone_type) +
+         mat_bytes(w->backbone_type, H, static_cast<size_t>(T) * H);
+}
+
+// Packed copy of fc [2560][12800], after the layers.
+uint8_t* packed_fc(const dflash_weights* w) {
+  return static_cast<uint8_t*>(w->packed) + sizeof(uint16_t) * static_cast<size_t>(w->vocab) * H +
+         L * layer_bytes(w->backbone_type);
 }
 
 // Packed copies of layer l's seven matrices, in LAYER_MATS order.
@@ -236,6 +243,7 @@ extern "C" int32_t dflash_pack_weights(const dflash_weights* w, void* stream) {
     for (int i = 0; i < 7; ++i)
       HIP_TRY(pack_matrix(w->backbone_type, src[i], LAYER_MATS[i].N, LAYER_MATS[i].K, dst[i], st));
   }
+  HIP_TRY(pack_matrix(w->backbone_type, w->fc, H, T * H, packed_fc(w), st));
   return DFLASH_OK;
 }
 
@@ -257,7 +265,8 @@ extern "C" int32_t dflash_fuse_context(const dflash_weights* w, const void* taps
     for (int c0 = 0; c0 < n; c0 += GEMV_ROWS) {
       const int rows = n - c0 < GEMV_ROWS ? n - c0 : GEMV_ROWS;
       GemvArgs a;
-      a.w = seg1(w->fc, H);
+      a.w = seg1(w->packed ? packed_fc(w) : w->fc, H);
+      a.packed = w->packed != nullptr;
       a.fmt = fmt;
       a.N = H;
       a.K = T * H;
@@ -313,6 +322,15 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
       const int rows = n - c0 < GEMV_ROWS ? n - c0 : GEMV_ROWS;
       GemvArgs a;
       a.w = seg_kv(w);
+      a.packed = w->packed != nullptr;
+      if (a.packed) {  // the layers' packed Wk / Wv
+        for (int l = 0; l < L; ++l) {
+          uint8_t* pm[7];
+          packed_layer(w, l, pm);
+          a.w.ptr[2 * l] = pm[1];
+          a.w.ptr[2 * l + 1] = pm[2];
+        }
+      }
       a.fmt = fmt;
       a.N = KV_N;
       a.K = H;

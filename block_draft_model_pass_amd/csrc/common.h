@@ -189,6 +189,7 @@ struct GemvArgs {
   int B;
   float* out;            // fp32 [S][B][N]
   int S;
+  int packed;            // segments are streaming copies (16-row tiles, lane order)
 };
 
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t st);

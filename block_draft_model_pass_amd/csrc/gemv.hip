@@ -132,7 +132,7 @@ __device__ __forceinline__ uint4 bf16x8_to_f16(uint4 v) {
 // Quantized weights are decoded to fp16 in registers (the same slot scheme
 // and decode as the pass kernel) and run on MFMA f16 against the
 // activations converted to fp16.
-template <int FMT, int NW, int KBW>
+template <int FMT, int NW, int KBW, bool PACKED>
 __global__ __launch_bounds__(NW * 64) void k_gemv(GemvArgs a) {
   __shared__ f32x4 red[NW > 1 ? NW - 1 : 1][64];
   constexpr int NX = 4 * KBW;                           // 8-element activation groups per lane
@@ -150,7 +150,21 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(GemvArgs a) {
   uint32_t sc[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    if constexpr (FMT == W_BF16) {
+    if constexpr (PACKED) {
+      // streaming copy: 16-row tile, then 64-byte row pieces (32 bf16, 64
+      // Q8_0 or 128 Q4_0 k), then the lanes; scales per tile and piece
+      constexpr int PK = FMT == W_BF16 ? 32 : (FMT == W_Q8_0 ? 64 : 128);
+      const size_t pc = static_cast<size_t>(row >> 4) * (a.K / PK) + kbeg / PK + i;
+      w[i] = ld16_stream(reinterpret_cast<const uint16_t*>(sr.base + (pc * 64 + r + 16 * g) * 16));
+      if constexpr (FMT == W_BF16)
+        sc[i] = 0;
+      else if constexpr (FMT == W_Q8_0)
+        sc[i] = *reinterpret_cast<const uint16_t*>(sr.base + static_cast<size_t>(sr.rows) * a.K +
+                                                   2 * (pc * 32 + r * 2 + (g >> 1)));
+      else
+        sc[i] = *reinterpret_cast<const uint16_t*>(sr.base + static_cast<size_t>(sr.rows) * a.K / 2 +
+                                                   2 * (pc * 64 + r * 4 + g));
+    } else if constexpr (FMT == W_BF16) {
       w[i] = ld16_stream(reinterpret_cast<const uint16_t*>(sr.base) + rk + kbeg + 32 * i + 8 * g);
       sc[i] = 0;
     } else if constexpr (FMT == W_Q8_0) {
@@ -358,11 +372,20 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t st) {
   constexpr int NW = 4, KBW = 5;  // 4 waves x 640 k per block and split
   if ((a.K / 128) % (NW * KBW) != 0 || a.S != a.K / (128 * NW * KBW)) return hipErrorInvalidValue;
   const dim3 grid(a.N / 16, a.S), block(NW * 64);
-  switch (a.fmt) {
-    case W_BF16: hipLaunchKernelGGL((k_gemv<W_BF16, NW, KBW>), grid, block, 0, st, a); break;
-    case W_Q8_0: hipLaunchKernelGGL((k_gemv<W_Q8_0, NW, KBW>), grid, block, 0, st, a); break;
-    case W_Q4_0: hipLaunchKernelGGL((k_gemv<W_Q4_0, NW, KBW>), grid, block, 0, st, a); break;
-    default: return hipErrorInvalidValue;
+  if (a.packed) {
+    switch (a.fmt) {
+      case W_BF16: hipLaunchKernelGGL((k_gemv<W_BF16, NW, KBW, true>), grid, block, 0, st, a); break;
+      case W_Q8_0: hipLaunchKernelGGL((k_gemv<W_Q8_0, NW, KBW, true>), grid, block, 0, st, a); break;
+      case W_Q4_0: hipLaunchKernelGGL((k_gemv<W_Q4_0, NW, KBW, true>), grid, block, 0, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (a.fmt) {
+      case W_BF16: hipLaunchKernelGGL((k_gemv<W_BF16, NW, KBW, false>), grid, block, 0, st, a); break;
+      case W_Q8_0: hipLaunchKernelGGL((k_gemv<W_Q8_0, NW, KBW, false>), grid, block, 0, st, a); break;
+      case W_Q4_0: hipLaunchKernelGGL((k_gemv<W_Q4_0, NW, KBW, false>), grid, block, 0, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }

@@ -104,12 +104,14 @@ typedef struct {
   const void* embed;       /* bf16 [vocab][2560] target embedding (shared)    */
   const void* lm_head;     /* bf16 [vocab][2560] target LM head (shared)      */
   /* Device buffer of dflash_packed_size() bytes holding the streaming
-   * copies the draft pass reads (the LM head and every layer's seven
-   * matrices, in the backbone's format), written by dflash_pack_weights after the weights
-   * are loaded (and again whenever those tensors change).  Required by
-   * dflash_draft_block (NULL -> DFLASH_EINVAL) and used by
-   * dflash_lm_head_argmax when set; every other call reads the row-major
-   * tensors above.  Caller-owned, like everything else. */
+   * copies of the matrices the calls stream (the LM head, every layer's seven
+   * matrices and fc, in the backbone's format), written by
+   * dflash_pack_weights after the weights are loaded (and again whenever
+   * those tensors change).  Required by dflash_draft_block (NULL ->
+   * DFLASH_EINVAL); used when set by dflash_lm_head_argmax and by the
+   * few-row (<= 64) paths of dflash_fuse_context / dflash_project_ctx_kv,
+   * which otherwise read the row-major tensors above, as the many-row paths
+   * always do.  Caller-owned, like everything else. */
   void* packed;
 } dflash_weights;
 
@@ -138,8 +140,8 @@ size_t dflash_workspace_size(const dflash_weights* w, int32_t max_rows,
 
 /* Bytes of the streaming copies: 2 * vocab * 2560 for the LM head plus the
  * 35 layer matrices (5 x (6144*2560 + 2*512*2560 + 2560*6144 + 2*7680*2560 +
- * 2560*7680) weights) at 2 (bf16), 34/32 (Q8_0) or 18/32 (Q4_0) bytes per
- * weight.  0 for an invalid descriptor. */
+ * 2560*7680) weights) and fc (2560*12800 weights) at 2 (bf16), 34/32 (Q8_0)
+ * or 18/32 (Q4_0) bytes per weight.  0 for an invalid descriptor. */
 size_t dflash_packed_size(const dflash_weights* w);
 
 /* Writes the streaming copies into w->packed, enqueued on `stream`.  A bf16
@@ -151,7 +153,8 @@ size_t dflash_packed_size(const dflash_weights* w);
  * ((n/16 * K/32 + k/32) * 64 + n%16 + 16 * ((k%32)/8)) * 8 + k%8.
  * Order in the buffer: lm_head [vocab][2560]; then for each layer 0..4:
  * wq [6144][2560], wk [512][2560], wv [512][2560], wo [2560][6144],
- * wg [7680][2560], wu [7680][2560], wd [2560][7680].  A Q8_0 / Q4_0 matrix
+ * wg [7680][2560], wu [7680][2560], wd [2560][7680]; then fc [2560][12800].
+ * A Q8_0 / Q4_0 matrix
  * keeps its two parts: its quants get the same shuffle with each row seen as
  * 64-byte pieces (64 k for Q8_0, 128 k for Q4_0) in place of 32-element bf16
  * blocks, i.e. byte j of piece kb of row n at ((n/16 * P + kb) * 64 + n%16 +

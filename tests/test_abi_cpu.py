@@ -165,17 +165,18 @@ def test_workspace_too_small(lib):
 
 
 def test_packed_copy_size_and_checks(lib):
-    """The streaming copies hold the LM head and the 35 layer matrices in the
-    backbone's format; packing needs a buffer and the draft pass needs the
+    """The streaming copies hold the LM head, the 35 layer matrices and fc in
+    the backbone's format; packing needs a buffer and the draft pass needs the
     copies."""
     w = fake_weights()
     lm = 2 * synth.VOCAB * 2560
-    layer = 2 * (6144 * 2560 + 2 * 512 * 2560 + 2560 * 6144 + 2 * 7680 * 2560 + 2560 * 7680)
-    assert _lib.dflash_packed_size(w) == lm + 5 * layer
+    weights = 5 * (6144 * 2560 + 2 * 512 * 2560 + 2560 * 6144 + 2 * 7680 * 2560 + 2560 * 7680) \
+        + 2560 * 12800
+    assert _lib.dflash_packed_size(w) == lm + 2 * weights
     q8 = _lib.dflash_packed_size(fake_weights(backbone_type=_lib.DFLASH_W_Q8_0))
     q4 = _lib.dflash_packed_size(fake_weights(backbone_type=_lib.DFLASH_W_Q4_0))
-    assert q8 == lm + 5 * layer // 2 * 34 // 32
-    assert q4 == lm + 5 * layer // 2 * 18 // 32
+    assert q8 == lm + weights * 34 // 32
+    assert q4 == lm + weights * 18 // 32
     assert _lib.dflash_packed_size(fake_weights(hidden=4096)) == 0
     assert _lib.dflash_pack_weights(w, None, check=False) == _lib.DFLASH_EINVAL
     big = 1 << 40

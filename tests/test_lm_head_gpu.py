@@ -85,14 +85,15 @@ def check_packed(packed, mat, rng, n_samples=20000):
 def test_streaming_copy_layout(dev_w, host_w):
     """Element (n, k) of each streamed matrix sits at 16-byte unit
     ((n/16) * (K/32) + k/32) * 64 + (n%16) + 16 * ((k%32)/8), element k%8;
-    the LM head first, then layer by layer wq, wk, wv, wo, wg, wu, wd."""
+    the LM head first, then layer by layer wq, wk, wv, wo, wg, wu, wd, then fc."""
     packed = dev_w.packed.view(torch.int16).cpu().numpy().view(np.uint16)
     rng = np.random.default_rng(3)
     V = dev_w.vocab
     shapes = [("wq", 6144, H), ("wk", 512, H), ("wv", 512, H), ("wo", H, 6144),
               ("wg", 7680, H), ("wu", 7680, H), ("wd", H, 7680)]
     layer_elems = sum(n * k for _, n, k in shapes)
-    assert packed.size == V * H + 5 * layer_elems
+    fc_off = V * H + 5 * layer_elems
+    assert packed.size == fc_off + H * 5 * H
     check_packed(packed[:V * H], host_w["lm_head"].reshape(V, H), rng)
     for l in (0, 4):
         off = V * H + l * layer_elems
@@ -100,3 +101,4 @@ def test_streaming_copy_layout(dev_w, host_w):
             check_packed(packed[off:off + n * k], host_w[f"layers.{l}.{name}"].reshape(n, k), rng,
                          n_samples=4000)
             off += n * k
+    check_packed(packed[fc_off:], host_w["fc"].reshape(H, 5 * H), rng, n_samples=4000)

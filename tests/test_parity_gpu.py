@@ -118,6 +118,29 @@ def test_fuse_context(dev_w, ow, n):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("n", [13, 40])
+def test_few_row_paths_without_streaming_copies(dev_w, ow, n):
+    """The few-row fusion and projection read the row-major tensors when the
+    descriptor carries no streaming copies: same bars."""
+    saved = dev_w.desc.packed
+    dev_w.desc.packed = None
+    try:
+        taps = synth.make_taps(range(700, 700 + n))
+        dr = Drafter(dev_w, KVRing(2048, window=2048), max_rows=n)
+        ctx = dr.fuse(to_device(taps))
+        dr.project(ctx, 900)
+        torch.cuda.synchronize()
+    finally:
+        dev_w.desc.packed = saved
+    octx = O.fuse_context(ow, taps)
+    err = row_rel_err(dec_bf16(ctx), O.bf16_decode(octx))
+    K, V = O.project_ctx_kv(ow, ctx.cpu().numpy().view(np.uint16), 900)
+    gK, gV = ring_cells(dr.kv, range(900, 900 + n))
+    ek, ev = row_rel_err(gK, K), row_rel_err(gV, V)
+    say(f"row-major few-row paths n={n}: fuse {err:.3e} K {ek:.3e} V {ev:.3e}")
+    assert err <= TOL and ek <= TOL and ev <= TOL
+
+
 def test_fuse_context_full_size_sampled(dev_w, ow):
     """32768 x 12800 @ 12800 x 2560 (the long-context fusion GEMM); the
     oracle recomputes 40 sampled rows including both ends."""

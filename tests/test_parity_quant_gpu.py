@@ -113,4 +113,4 @@ def test_quant_streaming_copy_layout(qset):
                 assert np.array_equal(gs[((rows // 16 * P + kb) * 16 + rows % 16) * S + sidx],
                                       scales[rows, blk])
             off += mb
-    assert packed.size == 2 * V * H + 5 * layer_bytes
+    assert packed.size == 2 * V * H + 5 * layer_bytes + qb(H, 5 * H) + H * (5 * H // 32) * 2
