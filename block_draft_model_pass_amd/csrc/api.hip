@@ -84,6 +84,9 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
+// Device buffers are read and written with 16-byte vector accesses.
+bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 int check_weights(const dflash_weights* w) {
   if (!w) return DFLASH_EINVAL;
   if (w->hidden != H || w->n_layers != L || w->n_q_heads != NQ || w->n_kv_heads != NKV ||
@@ -97,17 +100,21 @@ int check_weights(const dflash_weights* w) {
     return DFLASH_EINVAL;
   if (!w->fc || !w->hidden_norm || !w->final_norm || !w->embed || !w->lm_head)
     return DFLASH_EINVAL;
+  if (!a16(w->fc) || !a16(w->hidden_norm) || !a16(w->final_norm) || !a16(w->embed) ||
+      !a16(w->lm_head) || !a16(w->packed))
+    return DFLASH_EINVAL;
   for (int l = 0; l < L; ++l) {
     const dflash_layer_weights& y = w->layer[l];
-    if (!y.in_norm || !y.wq || !y.wk || !y.wv || !y.q_norm || !y.k_norm || !y.wo ||
-        !y.post_norm || !y.wg || !y.wu || !y.wd)
-      return DFLASH_EINVAL;
+    const void* t[11] = {y.in_norm, y.wq, y.wk, y.wv, y.q_norm, y.k_norm,
+                         y.wo,      y.post_norm, y.wg, y.wu, y.wd};
+    for (const void* p : t)
+      if (!p || !a16(p)) return DFLASH_EINVAL;
   }
   return DFLASH_OK;
 }
 
 int check_kv(const dflash_kv* kv) {
-  if (!kv || !kv->k || !kv->vt) return DFLASH_EINVAL;
+  if (!kv || !kv->k || !kv->vt || !a16(kv->k) || !a16(kv->vt)) return DFLASH_EINVAL;
   if (kv->capacity <= 0 || kv->capacity % 256 != 0) return DFLASH_ERANGE;
   if (kv->window <= 0 || kv->window > kv->capacity) return DFLASH_ERANGE;
   return DFLASH_OK;
@@ -253,7 +260,7 @@ extern "C" int32_t dflash_fuse_context(const dflash_weights* w, const void* taps
   if (rc) return rc;
   if (n < 0) return DFLASH_EINVAL;
   if (n == 0) return DFLASH_OK;
-  if (!taps || !ctx || !ws) return DFLASH_EINVAL;
+  if (!taps || !ctx || !ws || !a16(taps) || !a16(ctx) || !a16(ws)) return DFLASH_EINVAL;
   const Layout Lw = layout();
   const int fmt = w->backbone_type;
   if (ws_bytes < Lw.fixed + rows_bytes(n, fmt)) return DFLASH_EWORKSPACE;
@@ -305,7 +312,7 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
   if (n < 0 || pos0 < 0) return DFLASH_EINVAL;
   if (n > kv->capacity) return DFLASH_ERANGE;
   if (n == 0) return DFLASH_OK;
-  if (!ctx || !ws) return DFLASH_EINVAL;
+  if (!ctx || !ws || !a16(ctx) || !a16(ws)) return DFLASH_EINVAL;
   const Layout Lw = layout();
   const int fmt = w->backbone_type;
   if (ws_bytes < Lw.fixed + rows_bytes(n, fmt)) return DFLASH_EWORKSPACE;
@@ -374,6 +381,8 @@ extern "C" int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* 
   if (anchor_id < 0 || anchor_id >= w->vocab || mask_id < 0 || mask_id >= w->vocab)
     return DFLASH_EINVAL;
   if (!ws || (block > 1 && !cand)) return DFLASH_EINVAL;
+  if (!a16(ws) || !a16(logits_opt) || !a16(hidden_opt) || (reinterpret_cast<uintptr_t>(cand) & 3u))
+    return DFLASH_EINVAL;
   const Layout Lw = layout();
   if (ws_bytes < Lw.fixed) return DFLASH_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -457,6 +466,8 @@ extern "C" int32_t dflash_lm_head_argmax(const dflash_weights* w, const void* hi
   int rc = check_weights(w);
   if (rc) return rc;
   if (rows < 1 || rows > MAXB || !hidden || !cand || !ws) return DFLASH_EINVAL;
+  if (!a16(hidden) || !a16(ws) || !a16(logits_opt) || (reinterpret_cast<uintptr_t>(cand) & 3u))
+    return DFLASH_EINVAL;
   const Layout Lw = layout();
   if (ws_bytes < Lw.fixed) return DFLASH_EWORKSPACE;
   HIP_TRY(launch_lmhead_argmax(w->packed ? u16p(w->packed) : u16p(w->lm_head), w->packed != nullptr,

@@ -10,9 +10,10 @@
 // MFMAs, 384 bytes per 16-cycle MFMA, below what the four SIMDs of a CU need
 // at full MFMA rate.
 //
-// k advances in 32-wide stages through a 4-deep LDS ring (32 KiB per stage)
-// filled by direct global -> LDS loads (16 bytes per lane, no registers), so
-// three stages are in flight while one is multiplied.  Stage rows are 64
+// k advances in 32-wide stages through a 5-deep LDS ring (32 KiB per stage,
+// all 160 KiB of the CU's LDS) filled by direct global -> LDS loads (16 bytes
+// per lane, no registers), so four stages are in flight while one is
+// multiplied.  Stage rows are 64
 // bytes (32 bf16); 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 3),
 // which keeps the 16-row fragment reads free of bank conflicts (measured);
 // each load instruction fills 1 KiB of LDS (16 rows) in
@@ -29,7 +30,7 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int NT = 512;
-constexpr int STAGES = 4;
+constexpr int STAGES = 5;
 constexpr int STAGE_ELEMS = (BM + BN) * BK;  // bf16 per stage: A rows then W rows
 
 // Measured on gfx950 (SQ_LDS_BANK_CONFLICT of single-wave ds_read_b128
@@ -72,14 +73,15 @@ __device__ __forceinline__ int lds_off(int row, int c) { return row * BK + ((c ^
 __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict__ A, int lda,
                                                      int M, SegTable w, int K,
                                                      float* __restrict__ C, int ldc, int nN) {
-  // Four separate stage arrays (not one indexed ring): every access names its
+  // Five separate stage arrays (not one indexed ring): every access names its
   // stage statically, so the compiler can tell a stage being read from the
   // stages still being filled and does not wait for those loads.
   __shared__ __attribute__((aligned(16))) uint16_t st0[STAGE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t st1[STAGE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t st2[STAGE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t st3[STAGE_ELEMS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __attribute__((aligned(16))) uint16_t st4[STAGE_ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // block b runs on XCD b % 8; XCD x owns the contiguous tile run
   // [x q + min(x, r), ...) of the nb = 8 q + r tiles (n fastest).
@@ -100,29 +102,35 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
   st1[tid] = 0;
   st2[tid] = 0;
   st3[tid] = 0;
+  st4[tid] = 0;
   __syncthreads();
 
   // Loader: stage rows are 32 blocks of 16 (A blocks 0..15, W blocks 16..31);
   // wave v fills blocks 4v .. 4v+3.  Lane L writes stage row 16 b + L/4,
   // slot L%4, and fetches global chunk slot ^ kswz(row).  A rows past M
   // re-read row M-1 (their C rows are never stored).
-  const uint16_t* src[4];
+  // Each block's 16 rows: a wave-uniform base pointer (scalar registers) and
+  // a small per-lane element offset, to keep vector registers for the tile.
+  const uint16_t* gbase[4];
+  int goff[4];
   int ldst[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int blk = 4 * wave + i, row = 16 * blk + (lane >> 2), c = (lane & 3) ^ kswz(row);
-    if (row < BM) {
+    if (blk < BM / 16) {
+      gbase[i] = A + static_cast<size_t>(m0 + 16 * blk) * lda;
       const int gm = m0 + row < M ? m0 + row : M - 1;
-      src[i] = A + static_cast<size_t>(gm) * lda + 8 * c;
+      goff[i] = (gm - (m0 + 16 * blk)) * lda + 8 * c;
     } else {
-      src[i] = wb + static_cast<size_t>(row - BM) * K + 8 * c;
+      gbase[i] = wb + static_cast<size_t>(16 * blk - BM) * K;
+      goff[i] = (lane >> 2) * K + 8 * c;
     }
     ldst[i] = blk * 16 * BK;  // element offset of the block inside a stage
   }
   auto issue = [&](uint16_t* st, int kt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(src[i] + kt * BK, st + ldst[i], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(gbase[i] + goff[i] + kt * BK, st + ldst[i], 16, 0, 0);
   };
 
   const int wm = wave >> 2, wn = wave & 3;
@@ -135,10 +143,11 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
 
   // One k stage: wait for this wave's loads of stage kt (at most the later
   // stages' loads, 4 per stage, still outstanding), rendezvous, refill the
-  // slot freed by stage kt-1 with stage kt+3, multiply stage kt.
+  // slot freed by stage kt-1 with stage kt+4, multiply stage kt.
   auto step = [&](const uint16_t* cur, uint16_t* refill, int kt, int nk) {
     const int later = nk - 1 - kt;
-    if (later >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    if (later >= 3) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if (later == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else if (later == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     // Plain rendezvous (no fence: a fence would also wait for the stages
@@ -176,15 +185,17 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
 #undef GEMM_ROW
   };
 
-  const int nk = K / BK;  // a multiple of 4 (K % 128 == 0)
+  const int nk = K / BK;  // a multiple of 5
   issue(st0, 0);
   issue(st1, 1);
   issue(st2, 2);
+  issue(st3, 3);
   for (int kt = 0; kt < nk; kt += STAGES) {
-    step(st0, st3, kt, nk);
+    step(st0, st4, kt, nk);
     step(st1, st0, kt + 1, nk);
     step(st2, st1, kt + 2, nk);
     step(st3, st2, kt + 3, nk);
+    step(st4, st3, kt + 4, nk);
   }
 
 #pragma unroll
@@ -205,7 +216,7 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
 hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w, int K, float* C,
                             int ldc, int N, hipStream_t st) {
   if (M <= 0) return hipSuccess;
-  if (N % BN || K % (STAGES * BK) || lda % 8) return hipErrorInvalidValue;
+  if (N % BN || K % (STAGES * BK) || lda % 8) return hipErrorInvalidValue;  // 12800: 80 x 5 x 32
   for (int i = 0; i < w.nseg; ++i)  // a block's 256 rows never straddle two matrices
     if (w.row_end[i] % BN) return hipErrorInvalidValue;
   const int nN = N / BN, nM = (M + BM - 1) / BM;

@@ -8,43 +8,56 @@ namespace dfl {
 
 namespace {
 
-constexpr int NT = 256;             // threads per row
-constexpr int PER = H / NT;         // 10 elements per thread
+constexpr int NT = 128;             // threads per row
+constexpr int PER4 = H / (4 * NT);  // 5 groups of 4 consecutive elements per thread
 
+// One row per block; thread t owns elements 4 (t + 128 i) .. +3, so every
+// access is a 16-byte (fp32) or 8-byte (bf16) vector access.
 template <int S>
 __global__ __launch_bounds__(NT) void k_rownorm(float* h, const float* part, size_t sstride,
                                                 int rstride, const uint16_t* gain, float eps,
                                                 uint16_t* out, int ostride, uint16_t* out2) {
   __shared__ float red[NT / 64];
   const int b = blockIdx.x;
-  float v[PER];
-  float pv[S][PER];
+  f32x4 v[PER4];
+  f32x4 pv[S][PER4];
+  uint2 gv[PER4];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = threadIdx.x + NT * i;
-    v[i] = h ? h[static_cast<size_t>(b) * H + e] : 0.f;
+  for (int i = 0; i < PER4; ++i) {
+    const int e = 4 * (threadIdx.x + NT * i);
+    v[i] = h ? *reinterpret_cast<const f32x4*>(h + static_cast<size_t>(b) * H + e)
+             : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < S; ++s) pv[s][i] = part[s * sstride + static_cast<size_t>(b) * rstride + e];
+    for (int s = 0; s < S; ++s)
+      pv[s][i] = *reinterpret_cast<const f32x4*>(part + s * sstride + static_cast<size_t>(b) * rstride + e);
+    gv[i] = *reinterpret_cast<const uint2*>(gain + e);
   }
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
+  for (int i = 0; i < PER4; ++i) {
 #pragma unroll
     for (int s = 0; s < S; ++s) v[i] += pv[s][i];
-    ss += v[i] * v[i];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ss += v[i][q] * v[i][q];
   }
   if (h) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) h[static_cast<size_t>(b) * H + threadIdx.x + NT * i] = v[i];
+    for (int i = 0; i < PER4; ++i)
+      *reinterpret_cast<f32x4*>(h + static_cast<size_t>(b) * H + 4 * (threadIdx.x + NT * i)) = v[i];
   }
   ss = block_sum<NT>(ss, red);
   const float sc = 1.0f / sqrtf(ss / static_cast<float>(H) + eps);
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = threadIdx.x + NT * i;
-    const uint16_t y = f32_to_bf16(v[i] * sc * bf16_to_f32(gain[e]));
-    out[static_cast<size_t>(b) * ostride + e] = y;
-    if (out2) out2[static_cast<size_t>(b) * H + e] = y;
+  for (int i = 0; i < PER4; ++i) {
+    const int e = 4 * (threadIdx.x + NT * i);
+    const uint32_t g01 = gv[i].x, g23 = gv[i].y;
+    const uint32_t y0 = f32_to_bf16(v[i][0] * sc * bf16_to_f32(static_cast<uint16_t>(g01)));
+    const uint32_t y1 = f32_to_bf16(v[i][1] * sc * bf16_to_f32(static_cast<uint16_t>(g01 >> 16)));
+    const uint32_t y2 = f32_to_bf16(v[i][2] * sc * bf16_to_f32(static_cast<uint16_t>(g23)));
+    const uint32_t y3 = f32_to_bf16(v[i][3] * sc * bf16_to_f32(static_cast<uint16_t>(g23 >> 16)));
+    const uint2 o = make_uint2(y0 | (y1 << 16), y2 | (y3 << 16));
+    *reinterpret_cast<uint2*>(out + static_cast<size_t>(b) * ostride + e) = o;
+    if (out2) *reinterpret_cast<uint2*>(out2 + static_cast<size_t>(b) * H + e) = o;
   }
 }
 

@@ -27,6 +27,9 @@
  *   - Argument checks happen on the host before anything is enqueued; a
  *     non-zero return means nothing was enqueued (except DFLASH_EHIP, which
  *     reports a failed launch).
+ *   - Device buffers (weights, streaming copies, K/V ring, workspace, inputs
+ *     and outputs) must be 16-byte aligned; int32 buffers 4-byte aligned.
+ *     Otherwise the call returns DFLASH_EINVAL.
  *   - bf16 is the upper half of an IEEE binary32; fp16 is IEEE binary16.
  *     Matrices are row-major [out][in].
  *   - Not thread-safe beyond stream order.
@@ -43,8 +46,9 @@ extern "C" {
 
 /* Return codes. */
 #define DFLASH_OK          0
-#define DFLASH_EINVAL     -1 /* null pointer, negative size, block outside 1..8,
-                                token id outside [0, vocab), position < 0 */
+#define DFLASH_EINVAL     -1 /* null or misaligned pointer, negative size, block
+                                outside 1..8, token id outside [0, vocab),
+                                position < 0 */
 #define DFLASH_EGEOMETRY  -2 /* descriptor differs from the DFlash geometry */
 #define DFLASH_ERANGE     -3 /* K/V ring: window > capacity, capacity not a
                                 multiple of 256, or n > capacity in one call */

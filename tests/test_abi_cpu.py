@@ -71,6 +71,9 @@ def fake_weights(**over):
     return w
 
 
+A = 0x40000  # a 16-byte-aligned dummy device pointer (never dereferenced)
+
+
 def fake_kv(capacity=32768, window=32768):
     return _lib.dflash_kv(0x20000, 0x30000, capacity, window)
 
@@ -110,45 +113,45 @@ def test_null_and_bad_arguments(lib):
     kv = fake_kv()
     big = 1 << 40
     E = _lib.DFLASH_EINVAL
-    assert _lib.dflash_fuse_context(None, 1, 4, 1, 1, big, check=False) == E
-    assert _lib.dflash_fuse_context(w, None, 4, 1, 1, big, check=False) == E
-    assert _lib.dflash_fuse_context(w, 1, -1, 1, 1, big, check=False) == E
-    assert _lib.dflash_fuse_context(w, 1, 0, 1, 1, big, check=False) == 0  # no work
+    assert _lib.dflash_fuse_context(None, A, 4, A, A, big, check=False) == E
+    assert _lib.dflash_fuse_context(w, None, 4, A, A, big, check=False) == E
+    assert _lib.dflash_fuse_context(w, A, -1, A, A, big, check=False) == E
+    assert _lib.dflash_fuse_context(w, A, 0, A, A, big, check=False) == 0  # no work
     w2 = fake_weights()
     w2.layer[3].wd = None
-    assert _lib.dflash_fuse_context(w2, 1, 4, 1, 1, big, check=False) == E
+    assert _lib.dflash_fuse_context(w2, A, 4, A, A, big, check=False) == E
     w3 = fake_weights(backbone_type=7)
-    assert _lib.dflash_fuse_context(w3, 1, 4, 1, 1, big, check=False) == E
+    assert _lib.dflash_fuse_context(w3, A, 4, A, A, big, check=False) == E
     for block in (0, 9, -3):
-        assert _lib.dflash_draft_block(w, kv, 100, 1, 2, block, 1, None, None, 1, big,
+        assert _lib.dflash_draft_block(w, kv, 100, 1, 2, block, A, None, None, A, big,
                                        check=False) == E
     for anchor, mask in ((-1, 2), (synth.VOCAB, 2), (1, synth.VOCAB)):
-        assert _lib.dflash_draft_block(w, kv, 100, anchor, mask, 8, 1, None, None, 1, big,
+        assert _lib.dflash_draft_block(w, kv, 100, anchor, mask, 8, A, None, None, A, big,
                                        check=False) == E
-    assert _lib.dflash_draft_block(w, kv, -1, 1, 2, 8, 1, None, None, 1, big,
+    assert _lib.dflash_draft_block(w, kv, -1, 1, 2, 8, A, None, None, A, big,
                                    check=False) == E
-    assert _lib.dflash_draft_block(w, kv, 5, 1, 2, 8, None, None, None, 1, big,
+    assert _lib.dflash_draft_block(w, kv, 5, 1, 2, 8, None, None, None, A, big,
                                    check=False) == E
-    assert _lib.dflash_project_ctx_kv(w, 1, 4, -5, kv, 1, big, check=False) == E
-    assert _lib.dflash_lm_head_argmax(w, 1, 0, 1, None, 1, big, check=False) == E
-    assert _lib.dflash_lm_head_argmax(w, 1, 9, 1, None, 1, big, check=False) == E
-    assert _lib.dflash_lm_head_argmax(w, None, 3, 1, None, 1, big, check=False) == E
-    assert _lib.dflash_verify_greedy(1, 1, 8, 1, check=False) == E
-    assert _lib.dflash_verify_greedy(1, 1, -1, 1, check=False) == E
-    assert _lib.dflash_verify_greedy(1, None, 3, 1, check=False) == E
+    assert _lib.dflash_project_ctx_kv(w, A, 4, -5, kv, A, big, check=False) == E
+    assert _lib.dflash_lm_head_argmax(w, A, 0, A, None, A, big, check=False) == E
+    assert _lib.dflash_lm_head_argmax(w, A, 9, A, None, A, big, check=False) == E
+    assert _lib.dflash_lm_head_argmax(w, None, 3, A, None, A, big, check=False) == E
+    assert _lib.dflash_verify_greedy(A, A, 8, A, check=False) == E
+    assert _lib.dflash_verify_greedy(A, A, -1, A, check=False) == E
+    assert _lib.dflash_verify_greedy(A, None, 3, A, check=False) == E
 
 
 def test_ring_range_violations(lib):
     w = fake_weights()
     big = 1 << 40
     R = _lib.DFLASH_ERANGE
-    assert _lib.dflash_draft_block(w, fake_kv(1000, 1000), 10, 1, 2, 8, 1, None, None, 1, big,
+    assert _lib.dflash_draft_block(w, fake_kv(1000, 1000), 10, 1, 2, 8, A, None, None, A, big,
                                    check=False) == R
-    assert _lib.dflash_draft_block(w, fake_kv(1024, 2048), 10, 1, 2, 8, 1, None, None, 1, big,
+    assert _lib.dflash_draft_block(w, fake_kv(1024, 2048), 10, 1, 2, 8, A, None, None, A, big,
                                    check=False) == R
-    assert _lib.dflash_draft_block(w, fake_kv(1024, 0), 10, 1, 2, 8, 1, None, None, 1, big,
+    assert _lib.dflash_draft_block(w, fake_kv(1024, 0), 10, 1, 2, 8, A, None, None, A, big,
                                    check=False) == R
-    assert _lib.dflash_project_ctx_kv(w, 1, 2048, 0, fake_kv(1024, 1024), 1, big,
+    assert _lib.dflash_project_ctx_kv(w, A, 2048, 0, fake_kv(1024, 1024), A, big,
                                       check=False) == R
 
 
@@ -157,11 +160,11 @@ def test_workspace_too_small(lib):
     kv = fake_kv()
     need = _lib.dflash_workspace_size(w, 0, 8)
     W = _lib.DFLASH_EWORKSPACE
-    assert _lib.dflash_draft_block(w, kv, 10, 1, 2, 8, 1, None, None, 1, need - 1,
+    assert _lib.dflash_draft_block(w, kv, 10, 1, 2, 8, A, None, None, A, need - 1,
                                    check=False) == W
     need_rows = _lib.dflash_workspace_size(w, 4096, 8)
-    assert _lib.dflash_fuse_context(w, 1, 4096, 1, 1, need_rows - 1, check=False) == W
-    assert _lib.dflash_project_ctx_kv(w, 1, 4096, 0, kv, 1, need_rows - 1, check=False) == W
+    assert _lib.dflash_fuse_context(w, A, 4096, A, A, need_rows - 1, check=False) == W
+    assert _lib.dflash_project_ctx_kv(w, A, 4096, 0, kv, A, need_rows - 1, check=False) == W
 
 
 def test_packed_copy_size_and_checks(lib):
@@ -180,5 +183,32 @@ def test_packed_copy_size_and_checks(lib):
     assert _lib.dflash_packed_size(fake_weights(hidden=4096)) == 0
     assert _lib.dflash_pack_weights(w, None, check=False) == _lib.DFLASH_EINVAL
     big = 1 << 40
-    assert _lib.dflash_draft_block(w, fake_kv(), 10, 1, 2, 8, 1, None, None, 1, big,
+    assert _lib.dflash_draft_block(w, fake_kv(), 10, 1, 2, 8, A, None, None, A, big,
                                    check=False) == _lib.DFLASH_EINVAL
+
+
+def test_misaligned_pointers_are_rejected(lib):
+    """Device buffers are accessed 16 bytes at a time: a misaligned weight,
+    ring, workspace, input or output pointer is refused before any launch."""
+    big = 1 << 40
+    E = _lib.DFLASH_EINVAL
+    kv = fake_kv()
+    assert _lib.dflash_fuse_context(fake_weights(fc=A + 2), A, 4, A, A, big, check=False) == E
+    w = fake_weights()
+    w.layer[2].wo = A + 8
+    assert _lib.dflash_fuse_context(w, A, 4, A, A, big, check=False) == E
+    w = fake_weights()
+    assert _lib.dflash_fuse_context(w, A + 2, 4, A, A, big, check=False) == E
+    assert _lib.dflash_fuse_context(w, A, 4, A + 4, A, big, check=False) == E
+    assert _lib.dflash_project_ctx_kv(w, A, 4, 0, kv, A + 8, big, check=False) == E
+    assert _lib.dflash_project_ctx_kv(w, A, 4, 0, _lib.dflash_kv(A + 2, A, 32768, 32768), A,
+                                      big, check=False) == E
+    w.packed = A
+    assert _lib.dflash_draft_block(w, kv, 10, 1, 2, 8, A + 2, None, None, A, big,
+                                   check=False) == E
+    assert _lib.dflash_draft_block(w, kv, 10, 1, 2, 8, A, A + 8, None, A, big,
+                                   check=False) == E
+    assert _lib.dflash_lm_head_argmax(w, A + 2, 3, A, None, A, big, check=False) == E
+    w.packed = A + 4
+    assert _lib.dflash_draft_block(w, kv, 10, 1, 2, 8, A, None, None, A, big,
+                                   check=False) == E
