@@ -4,6 +4,7 @@
 #include "../../include/dflash.h"
 #include "common.h"
 
+#include <stdlib.h>
 #include <string.h>
 
 using namespace dfl;
@@ -14,6 +15,15 @@ constexpr int NCH_TARGET = 64;        // chunks per KV head aimed for
 constexpr int LMH_GRID = 256;         // standalone LM-head kernel: one block per CU
 constexpr int KEYS_MAX = 1024;        // argmax key slots (blocks of either LM-head launch)
 constexpr unsigned SPIN_LIMIT = 1u << 24;  // grid-barrier wait bound (~0.5 s)
+
+// The barrier wait bound in polls: SPIN_LIMIT, or DFLASH_SPIN_LIMIT from the
+// environment (read on every call) so that tests can drive the timeout path.
+unsigned spin_limit() {
+  const char* e = getenv("DFLASH_SPIN_LIMIT");
+  if (!e || !*e) return SPIN_LIMIT;
+  const unsigned long v = strtoul(e, nullptr, 10);
+  return v >= 1 && v <= SPIN_LIMIT ? static_cast<unsigned>(v) : SPIN_LIMIT;
+}
 
 // Co-resident grid of the pass kernel per device (a hardware property).
 int pass_grid() {
@@ -451,7 +461,7 @@ extern "C" int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* 
   q.keys = at<uint64_t>(ws, Lw.keys);
   q.bar = at<unsigned>(ws, Lw.bar);
   q.tab = at<void>(ws, Lw.tab);
-  q.spin_limit = SPIN_LIMIT;
+  q.spin_limit = spin_limit();
   q.grid = grid;
   q.cand = cand;
   q.logits = static_cast<uint16_t*>(logits_opt);

@@ -197,7 +197,10 @@ int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ctx, int32_t 
  * The pass is one persistent kernel of one block per compute unit whose
  * blocks wait for each other: it needs the whole device.  If other work keeps
  * some of its blocks from starting for about half a second, the pass gives up
- * waiting and sets every cand to -1 (its outputs are then undefined). */
+ * waiting and sets every cand to -1 (its outputs are then undefined).  The
+ * bound, in barrier polls, is 2^24 unless the environment variable
+ * DFLASH_SPIN_LIMIT (read by the host on each call, 1 .. 2^24) sets a smaller
+ * one -- meant for tests of this path. */
 int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* kv, int64_t p,
                            int32_t anchor_id, int32_t mask_id, int32_t block,
                            int32_t* cand, void* logits_opt, void* hidden_opt,
