@@ -5,15 +5,18 @@
 // reads 8 consecutive k of one row of A and of one row of W.
 //
 // Block tile 256 x 256, 512 threads: 8 waves as 2 (m) x 4 (n), each owning a
-// 128 x 64 sub-tile (8 x 4 MFMA tiles, 128 accumulator registers).  Per
+// 128 x 64 sub-tile (8 x 4 MFMA tiles, 128 accumulators held in AGPRs).  Per
 // 32-wide k step a wave reads 12 operand fragments (12 KiB) from LDS for 32
-// MFMAs, 384 bytes per 16-cycle MFMA, below what the four SIMDs of a CU need
-// at full MFMA rate.
+// MFMAs.
 //
 // k advances in 32-wide stages through a 5-deep LDS ring (32 KiB per stage,
-// all 160 KiB of the CU's LDS) filled by direct global -> LDS loads (16 bytes
-// per lane, no registers), so four stages are in flight while one is
-// multiplied.  Stage rows are 64
+// all 160 KiB of the CU's LDS) filled by direct buffer -> LDS loads (16 bytes
+// per lane, no registers).  The fragments of a stage are read into one of two
+// register sets while the MFMAs of the previous stage run from the other, so
+// a stage's slot is free as soon as the rendezvous after its reads has
+// passed and five stages are in flight while one is multiplied.  The MFMAs
+// of a step start right after its rendezvous; the next stage's reads and the
+// refill loads go out between groups of 8 MFMAs.  Stage rows are 64
 // bytes (32 bf16); 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 3),
 // which keeps the 16-row fragment reads free of bank conflicts (measured);
 // each load instruction fills 1 KiB of LDS (16 rows) in
@@ -47,22 +50,35 @@ __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
       reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint16_t*)p));
 }
 
-// Fragment read issued as its own instruction: the compiler's wait-count
-// pass cannot tell which stage a plain LDS read touches and would wait for
-// every direct-to-LDS load in flight, serialising the stages.  The caller
-// waits with lds_wait* before using the value.
+// Fragment read issued as its own instruction, at a byte offset the
+// instruction carries: the compiler's wait-count pass cannot tell which stage
+// a plain LDS read touches and would wait for every direct-to-LDS load in
+// flight, serialising the stages.  The caller waits with lds_wait_all before
+// using the value.
+template <int OFF>
 __device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
   u32x4 v;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
   return v;
 }
 
-// Wait until at most N of this wave's LDS reads are outstanding (they
-// complete in order); the value passes through the statement so that nothing
-// using it is scheduled before the wait.
-template <int N>
-__device__ __forceinline__ void lds_wait(u32x4& a) {
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N) : "memory");
+// Wait for all of this wave's LDS reads; the 12 fragments pass through the
+// statement, so nothing that uses them is scheduled before the wait and no
+// copy of a register still being loaded is taken.
+__device__ __forceinline__ void lds_wait_all(u32x4 (&w)[4], u32x4 (&a)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(a[0]), "+v"(a[1]),
+                 "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7])
+               :
+               : "memory");
+}
+
+// Stage base + lane offset, computed where it is used (a plain add would be
+// hoisted out of the loop as ten live registers, one per stage and operand).
+__device__ __forceinline__ uint32_t lds_base(uint32_t stage, uint32_t lane_off) {
+  uint32_t a;
+  asm volatile("v_add_u32 %0, %1, %2" : "=v"(a) : "s"(stage), "v"(lane_off));
+  return a;
 }
 
 __device__ __forceinline__ uint4 as_uint4(u32x4 v) { return __builtin_bit_cast(uint4, v); }
@@ -106,33 +122,47 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
   __syncthreads();
 
   // Loader: stage rows are 32 blocks of 16 (A blocks 0..15, W blocks 16..31);
-  // wave v fills blocks 4v .. 4v+3.  Lane L writes stage row 16 b + L/4,
-  // slot L%4, and fetches global chunk slot ^ kswz(row).  A rows past M
-  // re-read row M-1 (their C rows are never stored).
-  // Each block's 16 rows: a wave-uniform base pointer (scalar registers) and
-  // a small per-lane element offset, to keep vector registers for the tile.
-  const uint16_t* gbase[4];
-  int goff[4];
+  // wave v fills blocks 4v .. 4v+3, so waves 0-3 load A and waves 4-7 load W.
+  // Lane L writes stage row 16 b + L/4, slot L%4, and fetches global chunk
+  // slot ^ kswz(row).  A rows past M re-read row M-1 (their C rows are never
+  // stored).  The loads go through a buffer resource over the rows this block
+  // reads (scalar registers, exact byte extent), a constant per-lane byte
+  // offset and the stage's k offset as the scalar offset, so no per-lane
+  // address arithmetic is repeated per stage.
+  const bool loads_a = wave < 4;
+  const int last_a = (m0 + BM <= M ? m0 + BM : M) - 1;
+  const char* rbase = loads_a ? reinterpret_cast<const char*>(A + static_cast<size_t>(m0) * lda)
+                              : reinterpret_cast<const char*>(wb);
+  const uint32_t extent = loads_a ? 2u * static_cast<uint32_t>((last_a - m0) * lda + K)
+                                  : 2u * static_cast<uint32_t>(BN * K);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rbase), 0, static_cast<int>(extent), 0x00020000);
+  uint32_t voff[4];
   int ldst[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int blk = 4 * wave + i, row = 16 * blk + (lane >> 2), c = (lane & 3) ^ kswz(row);
-    if (blk < BM / 16) {
-      gbase[i] = A + static_cast<size_t>(m0 + 16 * blk) * lda;
+    if (loads_a) {
       const int gm = m0 + row < M ? m0 + row : M - 1;
-      goff[i] = (gm - (m0 + 16 * blk)) * lda + 8 * c;
+      voff[i] = 2u * static_cast<uint32_t>((gm - m0) * lda + 8 * c);
     } else {
-      gbase[i] = wb + static_cast<size_t>(16 * blk - BM) * K;
-      goff[i] = (lane >> 2) * K + 8 * c;
+      voff[i] = 2u * static_cast<uint32_t>((row - BM) * K + 8 * c);
     }
     ldst[i] = blk * 16 * BK;  // element offset of the block inside a stage
   }
+  auto issue_one = [&](uint16_t* st, int kt, int i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(st + ldst[i]),
+                                             16, static_cast<int>(voff[i]), kt * (2 * BK), 0, 0);
+  };
   auto issue = [&](uint16_t* st, int kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(gbase[i] + goff[i] + kt * BK, st + ldst[i], 16, 0, 0);
+    for (int i = 0; i < 4; ++i) issue_one(st, kt, i);
   };
 
+  // An (empty) statement naming an accumulation register lets the register
+  // allocator place the 128 accumulators in AGPRs, leaving the VGPRs to the
+  // two fragment sets.
+  asm volatile("" ::"a"(0));
   const int wm = wave >> 2, wn = wave & 3;
   const int r = lane & 15, g = lane >> 4;
   f32x4 acc[8][4];
@@ -141,62 +171,108 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One k stage: wait for this wave's loads of stage kt (at most the later
-  // stages' loads, 4 per stage, still outstanding), rendezvous, refill the
-  // slot freed by stage kt-1 with stage kt+4, multiply stage kt.
-  auto step = [&](const uint16_t* cur, uint16_t* refill, int kt, int nk) {
-    const int later = nk - 1 - kt;
-    if (later >= 3) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    else if (later == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if (later == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // Plain rendezvous (no fence: a fence would also wait for the stages
-    // still in flight); LDS reads of the previous stage were consumed by the
-    // MFMAs before this point.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (kt + STAGES - 1 < nk) issue(refill, kt + STAGES - 1);
-    // All 12 fragment reads go out at once; row i of MFMAs waits only for
-    // the reads up to its own A fragment.
-    const uint32_t cb = lds_addr(cur);
-    u32x4 wf[4], af[8];
+  // Fragment rows start at multiples of 16, so the swizzle of every row a
+  // lane reads is that of its row r, and the 12 fragment addresses of a
+  // stage are two per-wave bases plus 1 KiB steps (instruction offsets).
+  const uint32_t lane_w = 2 * lds_off(BM + wn * 64 + r, g);
+  const uint32_t lane_a = 2 * lds_off(wm * 128 + r, g);
+
+  // Two register sets of the 12 fragments of a stage: the MFMAs of stage kt
+  // run from one set while the reads of stage kt+1 fill the other.  Reads go
+  // out in three-fragment groups q = 0..3 (W 0-2; W 3, A 0-1; A 2-4; A 5-7).
+  u32x4 wfa[4], afa[8], wfb[4], afb[8];
+  auto read_group = [&](const uint16_t* st, u32x4 (&wf)[4], u32x4 (&af)[8], int q) {
+    if (q == 0) {
+      const uint32_t bw = lds_base(lds_addr(st), lane_w);
+      wf[0] = lds_read16<0>(bw);
+      wf[1] = lds_read16<1024>(bw);
+      wf[2] = lds_read16<2048>(bw);
+    } else if (q == 1) {
+      const uint32_t bw = lds_base(lds_addr(st), lane_w), ba = lds_base(lds_addr(st), lane_a);
+      wf[3] = lds_read16<3072>(bw);
+      af[0] = lds_read16<0>(ba);
+      af[1] = lds_read16<1024>(ba);
+    } else if (q == 2) {
+      const uint32_t ba = lds_base(lds_addr(st), lane_a);
+      af[2] = lds_read16<2048>(ba);
+      af[3] = lds_read16<3072>(ba);
+      af[4] = lds_read16<4096>(ba);
+    } else {
+      const uint32_t ba = lds_base(lds_addr(st), lane_a);
+      af[5] = lds_read16<5120>(ba);
+      af[6] = lds_read16<6144>(ba);
+      af[7] = lds_read16<7168>(ba);
+    }
+  };
+  auto read_frags = [&](const uint16_t* st, u32x4 (&wf)[4], u32x4 (&af)[8]) {
 #pragma unroll
-    for (int jn = 0; jn < 4; ++jn) wf[jn] = lds_read16(cb + 2 * lds_off(BM + wn * 64 + jn * 16 + r, g));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) af[i] = lds_read16(cb + 2 * lds_off(wm * 128 + i * 16 + r, g));
-    lds_wait<7>(wf[0]);
-    lds_wait<7>(wf[1]);
-    lds_wait<7>(wf[2]);
-    lds_wait<7>(wf[3]);
-#define GEMM_ROW(I, N)                                                                   \
-    lds_wait<N>(af[I]);                                                                  \
-    _Pragma("unroll") for (int jn = 0; jn < 4; ++jn)                                     \
-        acc[I][jn] = mfma_bf16(as_uint4(af[I]), as_uint4(wf[jn]), acc[I][jn]);           \
-    __builtin_amdgcn_sched_barrier(0);  /* keep this row between its wait and the next */
-    GEMM_ROW(0, 7)
-    GEMM_ROW(1, 6)
-    GEMM_ROW(2, 5)
-    GEMM_ROW(3, 4)
-    GEMM_ROW(4, 3)
-    GEMM_ROW(5, 2)
-    GEMM_ROW(6, 1)
-    GEMM_ROW(7, 0)
-#undef GEMM_ROW
+    for (int q = 0; q < 4; ++q) read_group(st, wf, af, q);
   };
 
-  const int nk = K / BK;  // a multiple of 5
+  // Step kt: wait for this wave's loads of stage kt+1 (the loads of the three
+  // later stages, 4 each, may still be in flight) and for its reads of stage
+  // kt; rendezvous (stage kt+1 has landed for every wave and no wave reads
+  // stage kt's slot any more); multiply stage kt while reading stage kt+1
+  // into the other register set and refilling stage kt's slot with stage
+  // kt+5.
+  auto step = [&](const uint16_t* nxt, uint16_t* refill, u32x4 (&wc)[4], u32x4 (&ac)[8],
+                  u32x4 (&wn_)[4], u32x4 (&an)[8], int kt, int nk) {
+    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    lds_wait_all(wc, ac);
+    // Plain rendezvous (no fence: a fence would also wait for the stages
+    // still in flight).
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // The MFMAs start right after the rendezvous: stage kt+1's fragment
+    // reads and the refill's loads go out between groups of 8 MFMAs (issued
+    // together by all eight waves at the rendezvous, the loads filled the
+    // address queue of the vector memory unit and held the MFMAs back).
+    // Both are unconditional: after the last stage the reads hit a slot no
+    // load fills and are never used (a conditional read would keep the
+    // set's previous contents live as well, a third set of registers), and
+    // the refill loads the last stage again (in bounds, into a slot nothing
+    // reads any more), so every step has the same loads in flight.
+    const int ks = kt + STAGES < nk ? kt + STAGES : nk - 1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int i = 2 * q; i < 2 * q + 2; ++i)
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) acc[i][jn] = mfma_bf16(as_uint4(ac[i]), as_uint4(wc[jn]), acc[i][jn]);
+      __builtin_amdgcn_sched_barrier(0);
+      read_group(nxt, wn_, an, q);
+      issue_one(refill, ks, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  const int nk = K / BK;  // a multiple of 10
   issue(st0, 0);
   issue(st1, 1);
   issue(st2, 2);
   issue(st3, 3);
-  for (int kt = 0; kt < nk; kt += STAGES) {
-    step(st0, st4, kt, nk);
-    step(st1, st0, kt + 1, nk);
-    step(st2, st1, kt + 2, nk);
-    step(st3, st2, kt + 3, nk);
-    step(st4, st3, kt + 4, nk);
+  issue(st4, 4);
+  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  read_frags(st0, wfa, afa);
+  for (int kt = 0; kt < nk; kt += 2 * STAGES) {
+    step(st1, st0, wfa, afa, wfb, afb, kt, nk);
+    step(st2, st1, wfb, afb, wfa, afa, kt + 1, nk);
+    step(st3, st2, wfa, afa, wfb, afb, kt + 2, nk);
+    step(st4, st3, wfb, afb, wfa, afa, kt + 3, nk);
+    step(st0, st4, wfa, afa, wfb, afb, kt + 4, nk);
+    step(st1, st0, wfb, afb, wfa, afa, kt + 5, nk);
+    step(st2, st1, wfa, afa, wfb, afb, kt + 6, nk);
+    step(st3, st2, wfb, afb, wfa, afa, kt + 7, nk);
+    step(st4, st3, wfa, afa, wfb, afb, kt + 8, nk);
+    step(st0, st4, wfb, afb, wfa, afa, kt + 9, nk);
   }
+  // The last step's reads land before their registers can be reused, and
+  // the repeated loads of the last stage land before the block's LDS is
+  // released.
+  lds_wait_all(wfa, afa);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -216,7 +292,7 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
 hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w, int K, float* C,
                             int ldc, int N, hipStream_t st) {
   if (M <= 0) return hipSuccess;
-  if (N % BN || K % (STAGES * BK) || lda % 8) return hipErrorInvalidValue;  // 12800: 80 x 5 x 32
+  if (N % BN || K % (2 * STAGES * BK) || lda % 8) return hipErrorInvalidValue;  // 12800: 40 x 10 x 32
   for (int i = 0; i < w.nseg; ++i)  // a block's 256 rows never straddle two matrices
     if (w.row_end[i] % BN) return hipErrorInvalidValue;
   const int nN = N / BN, nM = (M + BM - 1) / BM;
