@@ -233,6 +233,8 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
     // the refill loads the last stage again (in bounds, into a slot nothing
     // reads any more), so every step has the same loads in flight.
     const int ks = kt + STAGES < nk ? kt + STAGES : nk - 1;
+    // Raised wave priority while this wave issues its MFMAs (measured: ~0.5%).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
@@ -244,6 +246,7 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
       issue_one(refill, ks, q);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   const int nk = K / BK;  // a multiple of 10
