@@ -222,33 +222,88 @@ def main():
     lm_ms = ev[0].elapsed_time(ev[1]) / args.reps
     lm_gbs = lm_head_bytes() / (lm_ms * 1e-3) / 1e9
 
-    # Context fusion at long context: [n][12800] x [12800][2560] bf16 on MFMA
-    # plus the RMSNorm epilogue (dflash_fuse_context), n = 32768 by default.
-    fusion = None
-    if args.fusion_rows > 0:
-        nf = args.fusion_rows
-        gen = torch.Generator(device="cuda").manual_seed(5)
-        taps_f = torch.randn((nf, synth.N_TAPS * synth.HIDDEN), generator=gen, device="cuda")
-        taps_f = taps_f.to(torch.bfloat16).view(torch.int16)
-        fdr = Drafter(dw, KVRing(256), max_rows=nf)
-        ctx_f = fdr.fuse(taps_f)
-        for _ in range(3):  # the clock settles under sustained MFMA load
-            fdr.fuse(taps_f, ctx_f)
-        reps_f = max(5, args.reps // 5)
+    def time_calls(fn, reps, warm=3):
+        """Mean ms per call of `fn` over `reps` back-to-back calls after `warm`
+        untimed ones (HIP events on the stream the calls run on)."""
+        for _ in range(warm):
+            fn()
         ev[0].record()
-        for _ in range(reps_f):
-            fdr.fuse(taps_f, ctx_f)
+        for _ in range(reps):
+            fn()
         ev[1].record()
         torch.cuda.synchronize()
-        f_ms = ev[0].elapsed_time(ev[1]) / reps_f
-        flops = 2.0 * nf * synth.N_TAPS * synth.HIDDEN * synth.HIDDEN
-        fusion = {"rows": nf, "shape": f"{nf}x{synth.N_TAPS * synth.HIDDEN} @ "
-                                       f"{synth.N_TAPS * synth.HIDDEN}x{synth.HIDDEN} bf16",
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    HT = synth.N_TAPS * synth.HIDDEN
+    KVN = 2 * synth.N_LAYERS * synth.N_KV_HEADS * synth.HEAD_DIM  # Wk/Wv rows, all layers
+
+    def gpu_taps(n, seed):
+        gen = torch.Generator(device="cuda").manual_seed(seed)
+        t = torch.randn((n, HT), generator=gen, device="cuda")
+        return t.to(torch.bfloat16).view(torch.int16)
+
+    # Long resident context: the 32768-row context fusion [n][12800] x
+    # [12800][2560] bf16 on MFMA plus the RMSNorm epilogue (dflash_fuse_context),
+    # the K/V projection of those rows into cells at positions
+    # 229376..262143 (dflash_project_ctx_kv: [n][2560] x [2560][5120] GEMM, then
+    # per-head norm, RoPE and the fp16 ring store), and the draft pass of a
+    # block of 8 at 262144 over all 32768 resident cells.
+    fusion = None
+    long_ctx = None
+    if args.fusion_rows > 0:
+        nf = args.fusion_rows
+        taps_f = gpu_taps(nf, 5)
+        lring = KVRing(synth.WINDOW, synth.WINDOW)
+        fdr = Drafter(dw, lring, max_rows=nf)
+        ctx_f = fdr.fuse(taps_f)
+        # the clock settles under sustained MFMA load during the warm-up calls
+        f_ms = time_calls(lambda: fdr.fuse(taps_f, ctx_f), max(5, args.reps // 5))
+        flops = 2.0 * nf * HT * synth.HIDDEN
+        fusion = {"rows": nf, "shape": f"{nf}x{HT} @ {HT}x{synth.HIDDEN} bf16",
                   "ms": round(f_ms, 4), "TFLOPs": round(flops / (f_ms * 1e-3) / 1e12, 1),
                   "frac_bf16_mfma_peak": round(flops / (f_ms * 1e-3) / 2.5e15, 4),
                   "includes": "k_gemm_bf16_nt + k_rownorm (dflash_fuse_context)"}
-        del fdr, taps_f, ctx_f
+        if nf == synth.WINDOW:
+            pos0 = 7 * synth.WINDOW  # 229376: the last 32768 positions before 262144
+            p_ms = time_calls(lambda: fdr.project(ctx_f, pos0), max(5, args.reps // 5))
+            p_flops = 2.0 * nf * synth.HIDDEN * KVN
+            p = pos0 + nf
+            l_ms = time_calls(lambda: fdr.draft(p, 11, BLOCK, cand=cand), args.reps, warm=5)
+            l_bytes = pass_bytes(nf)
+            long_ctx = {"cells": nf, "positions": [pos0, p - 1], "block_at": p,
+                        "projection": {"shape": f"{nf}x{synth.HIDDEN} @ {synth.HIDDEN}x{KVN} bf16",
+                                       "ms": round(p_ms, 4),
+                                       "TFLOPs": round(p_flops / (p_ms * 1e-3) / 1e12, 1),
+                                       "frac_bf16_mfma_peak": round(p_flops / (p_ms * 1e-3) / 2.5e15, 4),
+                                       "includes": "k_gemm_bf16_nt + k_kv_post (dflash_project_ctx_kv)"},
+                        "draft": {"ms_per_pass": round(l_ms, 4), "passes_per_s": round(1e3 / l_ms, 2),
+                                  "algorithmic_bytes": l_bytes,
+                                  "achieved_GBs": round(l_bytes / (l_ms * 1e-3) / 1e9, 1),
+                                  "frac_hbm_peak": round(l_bytes / (l_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+        del fdr, taps_f, ctx_f, lring
         torch.cuda.empty_cache()
+
+    # Short prompt: fusion and K/V projection of a 2432-position prompt, then a
+    # block of 8 drafted at 2432 over those cells.
+    ns = 2432
+    taps_s = gpu_taps(ns, 6)
+    sdr = Drafter(dw, KVRing(2560, 2560), max_rows=ns)
+    ctx_s = sdr.fuse(taps_s)
+    s_f_ms = time_calls(lambda: sdr.fuse(taps_s, ctx_s), args.reps // 5 or 1)
+    s_p_ms = time_calls(lambda: sdr.project(ctx_s, 0), args.reps // 5 or 1)
+    s_d_ms = time_calls(lambda: sdr.draft(ns, 11, BLOCK, cand=cand), args.reps, warm=5)
+    s_fl, s_pl, s_bytes = 2.0 * ns * HT * synth.HIDDEN, 2.0 * ns * synth.HIDDEN * KVN, pass_bytes(ns)
+    short = {"ctx": ns, "block": BLOCK,
+             "fusion": {"ms": round(s_f_ms, 4), "TFLOPs": round(s_fl / (s_f_ms * 1e-3) / 1e12, 1),
+                        "frac_bf16_mfma_peak": round(s_fl / (s_f_ms * 1e-3) / 2.5e15, 4)},
+             "projection": {"ms": round(s_p_ms, 4), "TFLOPs": round(s_pl / (s_p_ms * 1e-3) / 1e12, 1),
+                            "frac_bf16_mfma_peak": round(s_pl / (s_p_ms * 1e-3) / 2.5e15, 4)},
+             "draft": {"ms_per_pass": round(s_d_ms, 4), "passes_per_s": round(1e3 / s_d_ms, 2),
+                       "algorithmic_bytes": s_bytes,
+                       "achieved_GBs": round(s_bytes / (s_d_ms * 1e-3) / 1e9, 1),
+                       "frac_hbm_peak": round(s_bytes / (s_d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+    del sdr, taps_s, ctx_s
+    torch.cuda.empty_cache()
 
     # Quantized backbone (Q8_0 / Q4_0 layer matrices, bf16 LM head): draft
     # passes at ctx 8192, block 4, on a context projected by those weights.
@@ -316,6 +371,8 @@ def main():
                                "achieved_GBs": round(lm_gbs, 1),
                                "frac_hbm_peak": round(lm_gbs / HBM_PEAK_GBS, 4)},
         "fusion_gemm": fusion,
+        "long_context": long_ctx,
+        "short_prompt": short,
         "quantized_backbone": quant or None,
         "accepted_offered": [state["acc"], state["off"]],
         "cpu_baseline": cpu,

@@ -357,7 +357,7 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
       a.out = part;
       a.S = 1;
       HIP_TRY(launch_gemv(a, st));
-      HIP_TRY(launch_kv_post(part, 1, 0, KV_N, rows, pos0 + c0, knorms, w->rms_eps, theta, rk, rv,
+      HIP_TRY(launch_kv_post(part, KV_N, rows, pos0 + c0, knorms, w->rms_eps, theta, rk, rv,
                              kv->capacity, st));
     }
   } else {
@@ -373,8 +373,7 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
       wt = seg1(dq, KV_N);
     }
     HIP_TRY(launch_gemm_bf16(x, H, n, wt, H, y, KV_N, KV_N, st));
-    HIP_TRY(launch_kv_post(y, 1, 0, KV_N, n, pos0, knorms, w->rms_eps, theta, rk, rv,
-                           kv->capacity, st));
+    HIP_TRY(launch_kv_post(y, KV_N, n, pos0, knorms, w->rms_eps, theta, rk, rv, kv->capacity, st));
   }
   return DFLASH_OK;
 }

@@ -219,11 +219,11 @@ hipError_t launch_rownorm(float* h, const float* part, int S, size_t part_split_
                           int part_row_stride, int rows, const uint16_t* gain, float eps,
                           uint16_t* out, int out_stride, uint16_t* out2, hipStream_t st);
 
-// Context K/V epilogue: y [n][KV_N] (row stride ldy, S partial splits) ->
+// Context K/V epilogue: y [n][KV_N] (row stride ldy) ->
 // k-norm + RoPE + fp16 into the ring.
-hipError_t launch_kv_post(const float* y, int S, size_t split_stride, int ldy, int n,
-                          int64_t pos0, const void* const* k_norms, float eps, double theta,
-                          uint16_t* ring_k, uint16_t* ring_vt, int capacity, hipStream_t st);
+hipError_t launch_kv_post(const float* y, int ldy, int n, int64_t pos0, const void* const* k_norms,
+                          float eps, double theta, uint16_t* ring_k, uint16_t* ring_vt, int capacity,
+                          hipStream_t st);
 
 // C[M][N] (fp32, ldc) = A[M][K] (bf16, lda) * W[N][K]^T
 hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w, int K,

@@ -3,7 +3,8 @@
 Builds the synthetic drafter (bf16 by default), commits context positions
 0..8191, then runs `--passes` draft passes of `--block` rows at position 8192
 back to back (or, with `--fuse-rows n`, `--passes` context fusions of n
-rows).  With `--copy-mib M` it first copies an M MiB device buffer `--copies`
+rows; with `--project-rows n`, `--passes` K/V projections of n fused rows
+into a 32768-cell ring at positions 229376..).  With `--copy-mib M` it first copies an M MiB device buffer `--copies`
 times (a plain copy kernel of known size, whose HBM counters calibrate those
 of the pass kernel).  Prints one line per step it finishes.
 
@@ -26,6 +27,9 @@ def main(argv=None) -> int:
     ap.add_argument("--fuse-rows", type=int, default=0,
                     help="instead of draft passes: context fusion of this many rows "
                          "(the bf16 GEMM + RMSNorm), --passes times")
+    ap.add_argument("--project-rows", type=int, default=0,
+                    help="instead of draft passes: K/V projection of this many rows "
+                         "(the bf16 GEMM + per-head norm / RoPE / ring store), --passes times")
     args = ap.parse_args(argv)
 
     import torch
@@ -55,6 +59,17 @@ def main(argv=None) -> int:
             fdr.fuse(taps, ctx)
         torch.cuda.synchronize()
         print(f"{args.passes} fusions of {nf} rows done", flush=True)
+        return 0
+    if args.project_rows > 0:
+        nr = args.project_rows
+        gen = torch.Generator(device="cuda").manual_seed(5)
+        ctx = torch.randn((nr, synth.HIDDEN), generator=gen, device="cuda")
+        ctx = ctx.to(torch.bfloat16).view(torch.int16)
+        pdr = Drafter(dw, KVRing(synth.WINDOW, synth.WINDOW), max_rows=nr)
+        for _ in range(args.passes):
+            pdr.project(ctx, 7 * synth.WINDOW)
+        torch.cuda.synchronize()
+        print(f"{args.passes} projections of {nr} rows done", flush=True)
         return 0
     dr = Drafter(dw, KVRing(synth.WINDOW, synth.WINDOW), max_rows=2048)
     for s0 in range(0, args.ctx, 2048):

@@ -168,10 +168,13 @@ def ring_cells(kv: KVRing, positions):
     return K, V
 
 
-@pytest.mark.parametrize("n,pos0,cap", [(1, 0, 256), (40, 1000, 1024), (300, 229376, 32768)])
+@pytest.mark.parametrize("n,pos0,cap", [(1, 0, 256), (40, 1000, 1024), (300, 229376, 32768),
+                                         (200, 1000, 1024)])
 def test_project_ctx_kv(dev_w, ow, n, pos0, cap):
-    """Skinny path with ring wrap-around (pos0 = 1000, capacity 1024) and
-    the GEMM path at 256K-range positions."""
+    """Skinny path with ring wrap-around (pos0 = 1000, capacity 1024), the
+    GEMM path at 256K-range positions, and the GEMM path starting inside a
+    32-cell value block and wrapping around the ring.  Cells outside the
+    projected range must stay untouched (the ring starts zeroed)."""
     say(f"project n={n} pos0={pos0} cap={cap}")
     ctx = synth.make_rows(n, synth.HIDDEN, seed=77)
     kv = KVRing(cap, window=cap)
@@ -184,6 +187,9 @@ def test_project_ctx_kv(dev_w, ow, n, pos0, cap):
     ev = row_rel_err(gV, V)
     say(f"project n={n} K err {ek:.3e} V err {ev:.3e}")
     assert ek <= TOL and ev <= TOL
+    other = np.setdiff1d(np.arange(cap), np.arange(pos0, pos0 + n) % cap)
+    assert not kv.k.cpu().numpy()[:, :, other, :].any()
+    assert not kv.values().cpu().numpy()[:, :, other, :].any()
 
 
 def test_project_full_size_sampled(dev_w, ow):
