@@ -333,6 +333,31 @@ def main():
             del qdr, qkv_ring, qw
             torch.cuda.empty_cache()
 
+    # Attainable rates of this device, for reference beside the kernels: a
+    # 1 GiB device-to-device copy (bytes read + written per second) and the
+    # vendor BLAS (torch.mm) on the context-fusion shape.
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    c_ms = time_calls(lambda: dst.copy_(src), 10)
+    copy_gbs = 2 * src.numel() * 4 / (c_ms * 1e-3) / 1e9
+    del src, dst
+    attainable = {"copy_1GiB": {"ms": round(c_ms, 4), "GBs_read_plus_write": round(copy_gbs, 1),
+                                "frac_hbm_peak": round(copy_gbs / HBM_PEAK_GBS, 4)}}
+    if args.fusion_rows > 0:
+        nf = args.fusion_rows
+        gen = torch.Generator(device="cuda").manual_seed(7)
+        a_ = torch.randn((nf, HT), generator=gen, device="cuda").to(torch.bfloat16)
+        b_ = torch.randn((HT, synth.HIDDEN), generator=gen, device="cuda").to(torch.bfloat16)
+        v_ms = time_calls(lambda: torch.mm(a_, b_), max(5, args.reps // 5))
+        v_fl = 2.0 * nf * HT * synth.HIDDEN
+        attainable["vendor_bf16_gemm"] = {"shape": f"{nf}x{HT} @ {HT}x{synth.HIDDEN}",
+                                          "ms": round(v_ms, 4),
+                                          "TFLOPs": round(v_fl / (v_ms * 1e-3) / 1e12, 1),
+                                          "frac_bf16_mfma_peak": round(v_fl / (v_ms * 1e-3) / 2.5e15, 4),
+                                          "note": "torch.mm (bf16 output, no norm)"}
+        del a_, b_
+        torch.cuda.empty_cache()
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(host_w, args.cpu_seconds)
@@ -373,6 +398,7 @@ def main():
         "fusion_gemm": fusion,
         "long_context": long_ctx,
         "short_prompt": short,
+        "attainable": attainable,
         "quantized_backbone": quant or None,
         "accepted_offered": [state["acc"], state["off"]],
         "cpu_baseline": cpu,

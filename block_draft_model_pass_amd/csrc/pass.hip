@@ -3,9 +3,11 @@
 // "Target feature taps" -- anchor and mask rows, non-causal block attention,
 // scale 1/16; "Parity validation" -- stage order).
 //
-// One 8-wave block per CU, launched cooperatively so all blocks are resident.
-// Phases are separated by a grid barrier (monotonic arrival counters, bounded
-// spin):
+// One 8-wave block per CU (a plain launch of at most as many blocks as the
+// device has CUs; every block is resident while the device runs nothing
+// else).  Phases are separated by a grid barrier (monotonic arrival counters,
+// bounded spin: a wait that gives up sets a status word and the pass reports
+// cand = -1):
 //
 //   per layer: QKV  -> ATTN (q/k norm + RoPE + partials) -> MERGE
 //              -> O (+ residual, row sums of squares) -> GATE/UP -> DOWN (+ residual)
