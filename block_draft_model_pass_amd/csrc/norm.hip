@@ -72,116 +72,123 @@ constexpr int KV_NT = 256;  // threads of a k_kv_post block
 // NeoX rotation by pos * theta^(-2i/256) (pairs i, i+128; angle, sin and cos
 // in fp64), values are stored as they are; both in fp16.
 //
-// grid (groups, L, 2): block (b, l, z) covers the 32 cells of the b-th
-// aligned 32-cell group that the rows touch -- rows rb .. rb+31 with
-// rb = 32 (pos0 / 32 + b) - pos0, only those in [0, n) written -- for layer
-// l's two key heads (z = 0) or two value heads (z = 1).  Groups are the
-// blocks of the value layout (32 cells, head dim outer), and cap % 32 == 0,
-// so a group never wraps.
-//  - keys: 8 threads per cell, thread p holding pairs 16p .. 16p+15 (two
-//    64-byte runs of the row); the fp64 cos/sin of its 16 angles serve both
-//    heads, the sum of squares is an 8-lane shuffle reduction, stores are
-//    32-byte runs.
-//  - values: thread t holds head dimension t and writes its 32 cells as 64
-//    contiguous bytes (per-element stores where the group is partial).
+// grid (groups8, L, 2 nz): keys (z < nz) or values, layer l = y, both heads
+// of the kind per block (nz = 1) or one (nz = 2, calls of at most 64 rows):
+//  - keys: block b covers the 8 cells of the b-th aligned 8-cell group the
+//    rows touch (rows rb .. rb+7, rb = 8 (pos0 / 8 + b) - pos0; only rows in
+//    [0, n) are written), 32 threads per cell, thread p holding pairs
+//    4p .. 4p+3: its 4 fp64 angles (inverse frequencies from a per-block
+//    table) serve both key heads of the layer -- a short chain per thread, so
+//    a commit of a few rows is not held up by them; the sum of squares is a
+//    32-lane shuffle reduction, stores are 8-byte runs.
+//  - values: block b < groups32 covers the b-th aligned 32-cell group (the
+//    blocks of the value layout: 32 cells, head dim outer; cap % 32 == 0, so a
+//    group never wraps); thread t holds head dimension t and writes its 32
+//    cells as 64 contiguous bytes (per-element stores where the group is
+//    partial).  Blocks past groups32 have nothing to do.
 __global__ __launch_bounds__(KV_NT) void k_kv_post(const float* y, int ldy, int n, int64_t pos0,
                                                    KNorms kn, float eps, double theta,
                                                    uint16_t* ring_k, uint16_t* ring_vt, int cap) {
   const int b = blockIdx.x, l = blockIdx.y, t = threadIdx.x;
-  const int64_t gp = (pos0 / BLK_CELLS + b) * BLK_CELLS;  // position of the group's cell 0
-  const int rb = static_cast<int>(gp - pos0);               // its row (negative if before pos0)
-  const size_t gcell = static_cast<size_t>(gp % cap);
-  if (blockIdx.z == 0) {
+  // gridDim.z = 2 nz: nz = 1 (a block takes both heads of its kind) or NKV
+  // (one head per block, for calls of a few rows, where latency matters more
+  // than sharing the angles).
+  const int nz = gridDim.z / 2, kind = blockIdx.z / nz, hpb = NKV / nz, j0 = (blockIdx.z % nz) * hpb;
+  if (kind == 0) {
+    constexpr int CPB = 8, TPC = KV_NT / CPB;  // cells per block, threads per cell (4 pairs each)
     __shared__ double invf[D / 2];
     if (t < D / 2) invf[t] = pow(theta, -2.0 * static_cast<double>(t) / static_cast<double>(D));
     __syncthreads();
-    const int c = t >> 3, p = t & 7, row = rb + c;
+    const int64_t gp = (pos0 / CPB + b) * CPB;
+    const int c = t / TPC, p = t % TPC, row = static_cast<int>(gp - pos0) + c;
     const bool valid = row >= 0 && row < n;
     const int rowc = row < 0 ? 0 : (row < n ? row : n - 1);  // in-bounds reads for unused cells
-    float fc[16], fs[16];
+    const size_t cell = static_cast<size_t>((gp + c) % cap);
+    float fc[4], fs[4];
     const double pos = static_cast<double>(gp + c);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < 4; ++k) {
       double sn, cs;
-      sincos(pos * invf[16 * p + k], &sn, &cs);
+      sincos(pos * invf[4 * p + k], &sn, &cs);
       fc[k] = static_cast<float>(cs);
       fs[k] = static_cast<float>(sn);
     }
     const uint16_t* g = kn.g[l];
-    const uint4* gl = reinterpret_cast<const uint4*>(g + 16 * p);
-    const uint4* gh = reinterpret_cast<const uint4*>(g + D / 2 + 16 * p);
-    const uint4 gv[4] = {gl[0], gl[1], gh[0], gh[1]};
+    const uint2 gl = *reinterpret_cast<const uint2*>(g + 4 * p);
+    const uint2 gh = *reinterpret_cast<const uint2*>(g + D / 2 + 4 * p);
+    const float ga[4] = {bf16_to_f32(static_cast<uint16_t>(gl.x)), bf16_to_f32(static_cast<uint16_t>(gl.x >> 16)),
+                         bf16_to_f32(static_cast<uint16_t>(gl.y)), bf16_to_f32(static_cast<uint16_t>(gl.y >> 16))};
+    const float gc[4] = {bf16_to_f32(static_cast<uint16_t>(gh.x)), bf16_to_f32(static_cast<uint16_t>(gh.x >> 16)),
+                         bf16_to_f32(static_cast<uint16_t>(gh.y)), bf16_to_f32(static_cast<uint16_t>(gh.y >> 16))};
 #pragma unroll
-    for (int j = 0; j < NKV; ++j) {
-      const float* yr = y + static_cast<size_t>(rowc) * ldy + l * (2 * NKV * D) + j * D + 16 * p;
-      float lo[16], hi[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 u = *reinterpret_cast<const f32x4*>(yr + 4 * q);
-        const f32x4 v = *reinterpret_cast<const f32x4*>(yr + D / 2 + 4 * q);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lo[4 * q + e] = u[e];
-          hi[4 * q + e] = v[e];
-        }
-      }
+    for (int jj = 0; jj < NKV; ++jj) {
+      if (jj >= hpb) break;
+      const int j = j0 + jj;
+      const float* yr = y + static_cast<size_t>(rowc) * ldy + l * (2 * NKV * D) + j * D + 4 * p;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(yr);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(yr + D / 2);
       float ss = 0.f;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) ss += lo[k] * lo[k] + hi[k] * hi[k];
+      for (int k = 0; k < 4; ++k) ss += lo[k] * lo[k] + hi[k] * hi[k];
       ss += __shfl_xor(ss, 1);
       ss += __shfl_xor(ss, 2);
       ss += __shfl_xor(ss, 4);
+      ss += __shfl_xor(ss, 8);
+      ss += __shfl_xor(ss, 16);
       const float sc = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
-      uint32_t olo[8], ohi[8];
+      uint32_t olo[2], ohi[2];
 #pragma unroll
-      for (int k = 0; k < 16; k += 2) {
+      for (int k = 0; k < 4; k += 2) {
         float a[2], cc[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int kk = k + e;
-          const uint32_t gw = reinterpret_cast<const uint32_t*>(&gv[kk / 8])[(kk % 8) / 2];
-          const uint32_t hw = reinterpret_cast<const uint32_t*>(&gv[2 + kk / 8])[(kk % 8) / 2];
-          const float ga = bf16_to_f32(static_cast<uint16_t>(kk & 1 ? gw >> 16 : gw));
-          const float gc = bf16_to_f32(static_cast<uint16_t>(kk & 1 ? hw >> 16 : hw));
-          const float x = lo[kk] * (sc * ga), z = hi[kk] * (sc * gc);
-          a[e] = x * fc[kk] - z * fs[kk];
-          cc[e] = z * fc[kk] + x * fs[kk];
+          const float x = lo[k + e] * (sc * ga[k + e]), z = hi[k + e] * (sc * gc[k + e]);
+          a[e] = x * fc[k + e] - z * fs[k + e];
+          cc[e] = z * fc[k + e] + x * fs[k + e];
         }
         olo[k / 2] = f32_to_f16_bits(a[0]) | (static_cast<uint32_t>(f32_to_f16_bits(a[1])) << 16);
         ohi[k / 2] = f32_to_f16_bits(cc[0]) | (static_cast<uint32_t>(f32_to_f16_bits(cc[1])) << 16);
       }
       if (valid) {
-        uint16_t* k = ring_k + ((static_cast<size_t>(l) * NKV + j) * cap + gcell + c) * D + 16 * p;
-        uint4* kl = reinterpret_cast<uint4*>(k);
-        uint4* kh = reinterpret_cast<uint4*>(k + D / 2);
-        kl[0] = make_uint4(olo[0], olo[1], olo[2], olo[3]);
-        kl[1] = make_uint4(olo[4], olo[5], olo[6], olo[7]);
-        kh[0] = make_uint4(ohi[0], ohi[1], ohi[2], ohi[3]);
-        kh[1] = make_uint4(ohi[4], ohi[5], ohi[6], ohi[7]);
+        uint16_t* k = ring_k + ((static_cast<size_t>(l) * NKV + j) * cap + cell) * D + 4 * p;
+        *reinterpret_cast<uint2*>(k) = make_uint2(olo[0], olo[1]);
+        *reinterpret_cast<uint2*>(k + D / 2) = make_uint2(ohi[0], ohi[1]);
       }
     }
   } else {
+    const int64_t groups32 = (pos0 + n - 1) / BLK_CELLS - pos0 / BLK_CELLS + 1;
+    if (b >= groups32) return;
+    const int64_t gp = (pos0 / BLK_CELLS + b) * BLK_CELLS;  // position of the group's cell 0
+    const int rb = static_cast<int>(gp - pos0);               // its row (negative if before pos0)
+    const size_t gcell = static_cast<size_t>(gp % cap);
     const bool full = rb >= 0 && rb + BLK_CELLS <= n;
 #pragma unroll
-    for (int j = 0; j < NKV; ++j) {
+    for (int jj = 0; jj < NKV; ++jj) {
+      if (jj >= hpb) break;
+      const int j = j0 + jj;
       const float* ycol = y + l * (2 * NKV * D) + (NKV + j) * D + t;
       uint16_t* v = ring_vt + (static_cast<size_t>(l) * NKV + j) * D * cap + (gcell / BLK_CELLS) * (D * BLK_CELLS) +
                     static_cast<size_t>(t) * BLK_CELLS;
-      if (full) {
-        uint32_t o[BLK_CELLS / 2];
+      // All 32 loads go out together (rows outside [0, n) re-read a row of
+      // the call and are never stored).
+      uint32_t o[BLK_CELLS / 2];
 #pragma unroll
-        for (int c = 0; c < BLK_CELLS; c += 2) {
-          const float v0 = ycol[static_cast<size_t>(rb + c) * ldy];
-          const float v1 = ycol[static_cast<size_t>(rb + c + 1) * ldy];
-          o[c / 2] = f32_to_f16_bits(v0) | (static_cast<uint32_t>(f32_to_f16_bits(v1)) << 16);
-        }
+      for (int c = 0; c < BLK_CELLS; c += 2) {
+        const int r0 = rb + c < 0 ? 0 : (rb + c < n ? rb + c : n - 1);
+        const int r1 = rb + c + 1 < 0 ? 0 : (rb + c + 1 < n ? rb + c + 1 : n - 1);
+        const float v0 = ycol[static_cast<size_t>(r0) * ldy];
+        const float v1 = ycol[static_cast<size_t>(r1) * ldy];
+        o[c / 2] = f32_to_f16_bits(v0) | (static_cast<uint32_t>(f32_to_f16_bits(v1)) << 16);
+      }
+      if (full) {
         uint4* v4 = reinterpret_cast<uint4*>(v);
 #pragma unroll
         for (int q = 0; q < 4; ++q) v4[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
       } else {
+#pragma unroll
         for (int c = 0; c < BLK_CELLS; ++c) {
           const int row = rb + c;
-          if (row >= 0 && row < n) v[c] = f32_to_f16_bits(ycol[static_cast<size_t>(row) * ldy]);
+          if (row >= 0 && row < n) v[c] = static_cast<uint16_t>(o[c / 2] >> (16 * (c & 1)));
         }
       }
     }
@@ -220,9 +227,11 @@ hipError_t launch_kv_post(const float* y, int ldy, int n, int64_t pos0, const vo
   if (capacity % BLK_CELLS || pos0 < 0 || ldy % 4) return hipErrorInvalidValue;
   KNorms kn;
   for (int l = 0; l < L; ++l) kn.g[l] = static_cast<const uint16_t*>(k_norms[l]);
-  const int64_t groups = (pos0 + n - 1) / BLK_CELLS - pos0 / BLK_CELLS + 1;
+  // 8-cell key groups; the value blocks use the first groups32 of them.
+  const int64_t groups = (pos0 + n - 1) / 8 - pos0 / 8 + 1;
   if (groups > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_kv_post, dim3(static_cast<unsigned>(groups), L, 2), dim3(KV_NT), 0, st, y, ldy,
+  const int nz = n <= 64 ? NKV : 1;
+  hipLaunchKernelGGL(k_kv_post, dim3(static_cast<unsigned>(groups), L, 2 * nz), dim3(KV_NT), 0, st, y, ldy,
                      n, pos0, kn, eps, theta, ring_k, ring_vt, capacity);
   return hipGetLastError();
 }
