@@ -16,10 +16,10 @@
 // a stage's slot is free as soon as the rendezvous after its reads has
 // passed and five stages are in flight while one is multiplied.  The MFMAs
 // of a step start right after its rendezvous; the next stage's reads and the
-// refill loads go out between groups of 8 MFMAs.  Stage rows are 64
-// bytes (32 bf16); 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 3),
-// which keeps the 16-row fragment reads free of bank conflicts (measured);
-// each load instruction fills 1 KiB of LDS (16 rows) in
+// refill loads go out in two halves between groups of 16 MFMAs.  Stage rows
+// are 64 bytes (32 bf16); 16-byte chunk c of row r sits at chunk
+// c ^ ((r >> 1) & 3), which keeps the 16-row fragment reads free of bank
+// conflicts (measured); each load instruction fills 1 KiB of LDS (16 rows) in
 // lane order, so a lane fetches the global chunk that the swizzle places at
 // its slot.
 //
@@ -224,9 +224,10 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     // The MFMAs start right after the rendezvous: stage kt+1's fragment
-    // reads and the refill's loads go out between groups of 8 MFMAs (issued
-    // together by all eight waves at the rendezvous, the loads filled the
-    // address queue of the vector memory unit and held the MFMAs back).
+    // reads and the refill's loads go out in two halves, each after a group
+    // of 16 MFMAs (issued together by all eight waves at the rendezvous, the
+    // loads filled the address queue of the vector memory unit and held the
+    // MFMAs back; measured: groups of 16 beat groups of 8, 4 and 32).
     // Both are unconditional: after the last stage the reads hit a slot no
     // load fills and are never used (a conditional read would keep the
     // set's previous contents live as well, a third set of registers), and
@@ -236,14 +237,16 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
     // Raised wave priority while this wave issues its MFMAs (measured: ~0.5%).
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int i = 2 * q; i < 2 * q + 2; ++i)
+      for (int i = 4 * h; i < 4 * h + 4; ++i)
 #pragma unroll
         for (int jn = 0; jn < 4; ++jn) acc[i][jn] = mfma_bf16(as_uint4(ac[i]), as_uint4(wc[jn]), acc[i][jn]);
       __builtin_amdgcn_sched_barrier(0);
-      read_group(nxt, wn_, an, q);
-      issue_one(refill, ks, q);
+      read_group(nxt, wn_, an, 2 * h);
+      read_group(nxt, wn_, an, 2 * h + 1);
+      issue_one(refill, ks, 2 * h);
+      issue_one(refill, ks, 2 * h + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
