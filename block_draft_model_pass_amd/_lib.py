@@ -15,6 +15,7 @@ DFLASH_EGEOMETRY = -2
 DFLASH_ERANGE = -3
 DFLASH_EWORKSPACE = -4
 DFLASH_EHIP = -5
+DFLASH_ENONFINITE = -6
 
 DFLASH_W_BF16 = 0
 DFLASH_W_Q8_0 = 1
@@ -91,6 +92,8 @@ def load() -> ctypes.CDLL:
     lib.dflash_lm_head_argmax.restype = c_int32
     lib.dflash_verify_greedy.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_void_p]
     lib.dflash_verify_greedy.restype = c_int32
+    lib.dflash_check_finite.argtypes = [c_void_p, c_int64, c_int32, c_void_p, c_void_p]
+    lib.dflash_check_finite.restype = c_int32
     lib.dflash_strerror.argtypes = [c_int32]
     lib.dflash_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -151,3 +154,8 @@ def dflash_lm_head_argmax(w, hidden, rows, cand, logits_opt, ws, ws_bytes, strea
 def dflash_verify_greedy(cand, target, k, out, stream=None, check=True):
     rc = load().dflash_verify_greedy(cand, target, k, out, stream)
     return _check(rc, "dflash_verify_greedy") if check else rc
+
+
+def dflash_check_finite(x, count, dtype, status, stream=None, check=True):
+    rc = load().dflash_check_finite(x, count, dtype, status, stream)
+    return _check(rc, "dflash_check_finite") if check else rc

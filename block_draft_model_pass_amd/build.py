@@ -21,7 +21,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
 ]
-SOURCES = ["api.hip", "gemv.hip", "norm.hip", "gemm.hip", "pass.hip", "pack.hip"]
+SOURCES = ["api.hip", "gemv.hip", "norm.hip", "gemm.hip", "pass.hip", "pack.hip", "check.hip"]
 
 
 def _compile(src: str) -> str:

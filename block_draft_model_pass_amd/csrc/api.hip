@@ -496,6 +496,16 @@ extern "C" int32_t dflash_verify_greedy(const int32_t* cand, const int32_t* targ
   return DFLASH_OK;
 }
 
+extern "C" int32_t dflash_check_finite(const void* x, int64_t count, int32_t dtype, int32_t* status,
+                                       void* stream) {
+  if (!status || (reinterpret_cast<uintptr_t>(status) & 3) || count < 0 || dtype < 0 || dtype > 2)
+    return DFLASH_EINVAL;
+  if (count > 0 && (!x || !a16(x))) return DFLASH_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIP_TRY(launch_check_finite(x, count, dtype, status, DFLASH_ENONFINITE, st));
+  return DFLASH_OK;
+}
+
 extern "C" const char* dflash_strerror(int32_t code) {
   switch (code) {
     case DFLASH_OK: return "ok";
@@ -504,6 +514,7 @@ extern "C" const char* dflash_strerror(int32_t code) {
     case DFLASH_ERANGE: return "K/V ring capacity/window/range violation";
     case DFLASH_EWORKSPACE: return "workspace too small";
     case DFLASH_EHIP: return "HIP launch failed";
+    case DFLASH_ENONFINITE: return "non-finite value found";
     default: return "unknown error";
   }
 }

@@ -229,6 +229,11 @@ hipError_t launch_kv_post(const float* y, int ldy, int n, int64_t pos0, const vo
 hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w, int K,
                             float* C, int ldc, int N, hipStream_t st);
 
+// Finite check: *status = 0, then `code` if any of x[0..count) (dtype 0 bf16,
+// 1 fp16, 2 fp32; 16-byte aligned) is NaN or infinite.
+hipError_t launch_check_finite(const void* x, int64_t count, int dtype, int32_t* status, int32_t code,
+                               hipStream_t st);
+
 // The whole proposal pass as one persistent kernel (plus a small init kernel).
 struct PassLaunch {
   int fmt;                 // WFormat of the layer matrices (bytes behind the pointers)

@@ -54,6 +54,8 @@ extern "C" {
                                 multiple of 256, or n > capacity in one call */
 #define DFLASH_EWORKSPACE -4 /* workspace smaller than dflash_workspace_size() */
 #define DFLASH_EHIP       -5 /* a kernel launch failed */
+#define DFLASH_ENONFINITE -6 /* written by dflash_check_finite into its device
+                                status word: a NaN or infinity was found */
 
 /* Fixed drafter geometry ("Drafter runtime" on the PR #1426 page). */
 #define DFLASH_HIDDEN     2560
@@ -228,6 +230,24 @@ int32_t dflash_lm_head_argmax(const dflash_weights* w, const void* hidden, int32
  *           continuation token).  k in [0, 7]. */
 int32_t dflash_verify_greedy(const int32_t* cand, const int32_t* target, int32_t k,
                              int32_t* out, void* stream);
+
+/* Optional finite check of a device buffer, for callers that want the
+ * pages' refusal of non-finite values (RFC #366 page, "3. First small
+ * experiment: verifier and rollback correctness", pass criteria: no
+ * non-finite values are introduced; the DFlash2 test list on the PR #3322
+ * page: nonfinite refusal).  No other entry point calls it: it costs one read
+ * of the buffer, so it is a debugging aid -- e.g. on the taps before
+ * dflash_fuse_context, on the context or the K/V ring after
+ * dflash_project_ctx_kv, on logits_opt / hidden_opt after dflash_draft_block.
+ *   x     : device buffer of `count` elements (16-byte aligned)
+ *   dtype : 0 = bf16, 1 = fp16, 2 = fp32
+ *   status: int32 device word; enqueued on `stream`, it is set to DFLASH_OK
+ *           and then, if any of the count elements is NaN or +-infinity (all
+ *           exponent bits set), to DFLASH_ENONFINITE.  count 0 -> DFLASH_OK.
+ * Returns DFLASH_EINVAL for a null or misaligned pointer (x may be NULL only
+ * when count is 0), count < 0 or an unknown dtype. */
+int32_t dflash_check_finite(const void* x, int64_t count, int32_t dtype, int32_t* status,
+                            void* stream);
 
 /* Static description of a return code (host string, never NULL). */
 const char* dflash_strerror(int32_t code);

@@ -90,9 +90,22 @@ def test_workspace_size(lib):
 
 
 def test_strerror_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5, -99):
+    for code in (0, -1, -2, -3, -4, -5, -6, -99):
         assert isinstance(_lib.dflash_strerror(code), str)
     assert _lib.dflash_strerror(-4) == "workspace too small"
+    assert _lib.dflash_strerror(_lib.DFLASH_ENONFINITE) == "non-finite value found"
+
+
+def test_check_finite_arguments(lib):
+    """Rejected on the host before anything is enqueued (no device needed)."""
+    E = _lib.DFLASH_EINVAL
+    assert _lib.dflash_check_finite(A, 16, 0, None, check=False) == E       # no status word
+    assert _lib.dflash_check_finite(A, 16, 0, A + 2, check=False) == E      # misaligned status
+    assert _lib.dflash_check_finite(None, 16, 0, A, check=False) == E       # no buffer
+    assert _lib.dflash_check_finite(A + 8, 16, 2, A, check=False) == E      # misaligned buffer
+    assert _lib.dflash_check_finite(A, -1, 0, A, check=False) == E         # negative count
+    for dtype in (-1, 3):
+        assert _lib.dflash_check_finite(A, 16, dtype, A, check=False) == E
 
 
 @pytest.mark.parametrize("field,value", [
