@@ -305,8 +305,14 @@ extern "C" int32_t dflash_fuse_context(const dflash_weights* w, const void* taps
       HIP_TRY(launch_dequant_bf16(w->fc, fmt, H, T * H, dq, st));
       wt = seg1(dq, H);
     }
-    HIP_TRY(launch_gemm_bf16(x, T * H, n, wt, T * H, y, H, H, st));
-    HIP_TRY(launch_rownorm(nullptr, y, 1, 0, H, n, u16p(w->hidden_norm), w->rms_eps, out, H,
+    // Fewer 256 x 256 output tiles than compute units (n < 6400 rows): split
+    // the k range in two (the fp32 region holds two partial outputs, which
+    // the row norm sums).
+    const int tiles = (n + 255) / 256 * (H / 256);
+    const int S = tiles < 256 ? 2 : 1;
+    const size_t cs = static_cast<size_t>(n) * H;
+    HIP_TRY(launch_gemm_bf16(x, T * H, n, wt, T * H, y, H, H, S, cs, st));
+    HIP_TRY(launch_rownorm(nullptr, y, S, cs, H, n, u16p(w->hidden_norm), w->rms_eps, out, H,
                            nullptr, st));
   }
   return DFLASH_OK;
@@ -372,7 +378,7 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
       }
       wt = seg1(dq, KV_N);
     }
-    HIP_TRY(launch_gemm_bf16(x, H, n, wt, H, y, KV_N, KV_N, st));
+    HIP_TRY(launch_gemm_bf16(x, H, n, wt, H, y, KV_N, KV_N, 1, 0, st));
     HIP_TRY(launch_kv_post(y, KV_N, n, pos0, knorms, w->rms_eps, theta, rk, rv, kv->capacity, st));
   }
   return DFLASH_OK;

@@ -227,7 +227,7 @@ hipError_t launch_kv_post(const float* y, int ldy, int n, int64_t pos0, const vo
 
 // C[M][N] (fp32, ldc) = A[M][K] (bf16, lda) * W[N][K]^T
 hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w, int K,
-                            float* C, int ldc, int N, hipStream_t st);
+                            float* C, int ldc, int N, int nsplit, size_t c_split, hipStream_t st);
 
 // Finite check: *status = 0, then `code` if any of x[0..count) (dtype 0 bf16,
 // 1 fp16, 2 fp32; 16-byte aligned) is NaN or infinite.

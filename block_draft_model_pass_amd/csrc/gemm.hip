@@ -24,7 +24,9 @@
 // its slot.
 //
 // Tiles are dealt to the XCDs in contiguous runs (the hardware deals blocks
-// round robin), so the blocks on one XCD share A panels in its L2.
+// round robin), so the blocks on one XCD share A panels in its L2.  With
+// fewer tiles than CUs the k range can be split S ways (partial outputs S
+// apart, summed by the consumer).
 #include "common.h"
 
 namespace dfl {
@@ -86,9 +88,13 @@ __device__ __forceinline__ uint4 as_uint4(u32x4 v) { return __builtin_bit_cast(u
 // LDS element offset of chunk c of stage row `row` (A rows 0..255, W rows 256..511).
 __device__ __forceinline__ int lds_off(int row, int c) { return row * BK + ((c ^ kswz(row)) << 3); }
 
+// Split-K: block q of the tiles x S grid computes the k range
+// [s K, (s+1) K) of tile t (t' = s tiles + t) into C + s c_split; W rows are
+// ldw elements apart (S K).
 __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict__ A, int lda,
-                                                     int M, SegTable w, int K,
-                                                     float* __restrict__ C, int ldc, int nN) {
+                                                     int M, SegTable w, int K, int ldw,
+                                                     float* __restrict__ C, int ldc, int nN,
+                                                     int tiles, size_t c_split) {
   // Five separate stage arrays (not one indexed ring): every access names its
   // stage statically, so the compiler can tell a stage being read from the
   // stages still being filled and does not wait for those loads.
@@ -104,13 +110,16 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
   const int nb = gridDim.x;
   const int x = blockIdx.x & 7, jb = blockIdx.x >> 3;
   const int q = nb >> 3, rem = nb & 7;
-  const int t = x * q + (x < rem ? x : rem) + jb;
+  const int tq = x * q + (x < rem ? x : rem) + jb;
+  const int split = tq / tiles, t = tq - split * tiles;
   const int m0 = (t / nN) * BM, n0 = (t % nN) * BN;
+  const size_t k0 = static_cast<size_t>(split) * K;
+  C += split * c_split;
 
   int seg = 0, base = 0;
   for (int i = 0; i + 1 < w.nseg; ++i)
     if (n0 >= w.row_end[i]) { seg = i + 1; base = w.row_end[i]; }
-  const uint16_t* wb = static_cast<const uint16_t*>(w.ptr[seg]) + static_cast<size_t>(n0 - base) * K;
+  const uint16_t* wb = static_cast<const uint16_t*>(w.ptr[seg]) + static_cast<size_t>(n0 - base) * ldw + k0;
 
   // The stages are written only by direct-to-LDS loads; ordinary stores keep
   // the compiler from treating their contents as undefined.
@@ -131,10 +140,10 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
   // address arithmetic is repeated per stage.
   const bool loads_a = wave < 4;
   const int last_a = (m0 + BM <= M ? m0 + BM : M) - 1;
-  const char* rbase = loads_a ? reinterpret_cast<const char*>(A + static_cast<size_t>(m0) * lda)
+  const char* rbase = loads_a ? reinterpret_cast<const char*>(A + static_cast<size_t>(m0) * lda + k0)
                               : reinterpret_cast<const char*>(wb);
   const uint32_t extent = loads_a ? 2u * static_cast<uint32_t>((last_a - m0) * lda + K)
-                                  : 2u * static_cast<uint32_t>(BN * K);
+                                  : 2u * static_cast<uint32_t>((BN - 1) * ldw + K);
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rbase), 0, static_cast<int>(extent), 0x00020000);
   uint32_t voff[4];
@@ -146,7 +155,7 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
       const int gm = m0 + row < M ? m0 + row : M - 1;
       voff[i] = 2u * static_cast<uint32_t>((gm - m0) * lda + 8 * c);
     } else {
-      voff[i] = 2u * static_cast<uint32_t>((row - BM) * K + 8 * c);
+      voff[i] = 2u * static_cast<uint32_t>((row - BM) * ldw + 8 * c);
     }
     ldst[i] = blk * 16 * BK;  // element offset of the block inside a stage
   }
@@ -296,16 +305,18 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
 }  // namespace
 
 hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w, int K, float* C,
-                            int ldc, int N, hipStream_t st) {
+                            int ldc, int N, int nsplit, size_t c_split, hipStream_t st) {
   if (M <= 0) return hipSuccess;
-  if (N % BN || K % (2 * STAGES * BK) || lda % 8) return hipErrorInvalidValue;  // 12800: 40 x 10 x 32
+  if (nsplit < 1 || K % nsplit) return hipErrorInvalidValue;
+  const int Ks = K / nsplit;
+  if (N % BN || Ks % (2 * STAGES * BK) || lda % 8) return hipErrorInvalidValue;  // 12800: 40 x 10 x 32
   for (int i = 0; i < w.nseg; ++i)  // a block's 256 rows never straddle two matrices
     if (w.row_end[i] % BN) return hipErrorInvalidValue;
   const int nN = N / BN, nM = (M + BM - 1) / BM;
   const long long tiles = static_cast<long long>(nN) * nM;
-  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_gemm_bf16_nt, dim3(static_cast<unsigned>(tiles)), dim3(NT), 0, st, A, lda, M,
-                     w, K, C, ldc, nN);
+  if (tiles * nsplit > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_gemm_bf16_nt, dim3(static_cast<unsigned>(tiles * nsplit)), dim3(NT), 0, st, A, lda,
+                     M, w, Ks, K, C, ldc, nN, static_cast<int>(tiles), c_split);
   return hipGetLastError();
 }
 
