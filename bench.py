@@ -154,6 +154,7 @@ def main():
     # Context 0..8191 and the taps of every position a job can commit.
     span = CTX + JOB_TOKENS + BLOCK
     taps_all = to_device(synth.make_taps(range(span)))
+    taps_ptr, tap_row_bytes = taps_all.data_ptr(), taps_all.stride(0) * taps_all.element_size()
     dr.commit(taps_all[:CTX], 0)
     n_pass = args.steps + args.warmup
     draws = [synth.target_draws(t, K) for t in range(n_pass)]
@@ -178,7 +179,7 @@ def main():
         dr.verify(cand, tgt, K, out=out)
         a, nxt = out.tolist()  # the cycle's one device->host read
         p = state["p"]
-        dr.commit(taps_all[p:p + a + 1], p)
+        dr.commit_ptr(taps_ptr + p * tap_row_bytes, a + 1, p)
         state["acc"] += a
         state["off"] += K
         state["p"], state["anchor"] = p + a + 1, nxt

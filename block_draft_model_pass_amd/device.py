@@ -98,8 +98,11 @@ class Drafter:
         self.kv = kv
         self.ws_bytes = dflash_workspace_size(weights.desc, max_rows, max_block)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.ws_ptr = self.ws.data_ptr()
         self.max_rows = max_rows
         self.device = device
+        # fused context rows of commit(): reused, so a decode step allocates nothing
+        self.ctx_buf = torch.empty((max_rows, synth.HIDDEN), dtype=torch.int16, device=device)
 
     def fuse(self, taps: torch.Tensor, ctx: torch.Tensor | None = None) -> torch.Tensor:
         n = taps.shape[0]
@@ -114,9 +117,23 @@ class Drafter:
                               self.ws.data_ptr(), self.ws_bytes, stream_ptr())
 
     def commit(self, taps: torch.Tensor, pos0: int) -> torch.Tensor:
-        ctx = self.fuse(taps)
-        self.project(ctx, pos0)
-        return ctx
+        """Fuse and project taps [n][12800] (n <= max_rows) into cells
+        pos0 .. pos0+n-1; returns the fused rows (a view of the reused
+        context buffer, valid until the next commit)."""
+        n = taps.shape[0]
+        self.commit_ptr(taps.data_ptr(), n, pos0)
+        return self.ctx_buf[:n]
+
+    def commit_ptr(self, taps_ptr: int, n: int, pos0: int):
+        """commit() on a raw device pointer to n rows of taps: no tensor is
+        created or allocated on this path."""
+        if not 0 <= n <= self.max_rows:
+            raise ValueError(f"commit of {n} rows: this Drafter holds at most {self.max_rows}")
+        st = stream_ptr()
+        ctx = self.ctx_buf.data_ptr()
+        dflash_fuse_context(self.w.desc, taps_ptr, n, ctx, self.ws_ptr, self.ws_bytes, st)
+        dflash_project_ctx_kv(self.w.desc, ctx, n, pos0, self.kv.desc, self.ws_ptr,
+                              self.ws_bytes, st)
 
     def draft(self, p: int, anchor: int, block: int, mask_id: int = synth.MASK_ID,
               cand: torch.Tensor | None = None, logits: torch.Tensor | None = None,
