@@ -141,6 +141,26 @@ def test_few_row_paths_without_streaming_copies(dev_w, ow, n):
     assert err <= TOL and ek <= TOL and ev <= TOL
 
 
+@pytest.mark.parametrize("n", [2432, 2700, 6401])
+def test_fuse_context_split_sampled(dev_w, ow, n):
+    """Many-row fusion around the k-split rule: fewer output tiles than
+    compute units split the k range in two (2432 rows: 100 tiles; 2700 rows:
+    110 tiles), 260 tiles do not (6401 rows, ragged last tile); the oracle
+    recomputes sampled rows including the ends of the first panel and of the
+    buffer."""
+    say(f"fuse split n={n}")
+    taps = synth.make_taps(range(5000, 5000 + n))
+    dr = Drafter(dev_w, KVRing(256), max_rows=n)
+    ctx = dr.fuse(to_device(taps))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 255, 256, n - 2, n - 1],
+                                     np.random.default_rng(n).integers(0, n, 19)]))
+    ref = O.bf16_decode(O.fuse_context(ow, taps[rows]))
+    err = row_rel_err(dec_bf16(ctx)[rows], ref)
+    say(f"fuse split n={n} rel err {err:.3e}")
+    assert err <= TOL
+
+
 def test_fuse_context_full_size_sampled(dev_w, ow):
     """32768 x 12800 @ 12800 x 2560 (the long-context fusion GEMM); the
     oracle recomputes 40 sampled rows including both ends."""
