@@ -299,8 +299,11 @@ extern "C" int32_t dflash_fuse_context(const dflash_weights* w, const void* taps
     }
   } else {
     float* y = at<float>(ws, Lw.y);
-    SegTable wt = seg1(w->fc, H);
-    if (fmt != W_BF16) {  // decode once to bf16, then the bf16 GEMM
+    // bf16: the streaming copy of fc when there is one (contiguous 1 KiB
+    // loads); quantized: decode once to row-major bf16
+    const bool wp = fmt == W_BF16 && w->packed;
+    SegTable wt = seg1(wp ? packed_fc(w) : w->fc, H);
+    if (fmt != W_BF16) {
       uint16_t* dq = at<uint16_t>(ws, Lw.y + rows_bytes(n, fmt) - 2 * DQ_ELEMS);
       HIP_TRY(launch_dequant_bf16(w->fc, fmt, H, T * H, dq, st));
       wt = seg1(dq, H);
@@ -311,7 +314,7 @@ extern "C" int32_t dflash_fuse_context(const dflash_weights* w, const void* taps
     const int tiles = (n + 255) / 256 * (H / 256);
     const int S = tiles < 256 ? 2 : 1;
     const size_t cs = static_cast<size_t>(n) * H;
-    HIP_TRY(launch_gemm_bf16(x, T * H, n, wt, T * H, y, H, H, S, cs, st));
+    HIP_TRY(launch_gemm_bf16(x, T * H, n, wt, wp, T * H, y, H, H, S, cs, st));
     HIP_TRY(launch_rownorm(nullptr, y, S, cs, H, n, u16p(w->hidden_norm), w->rms_eps, out, H,
                            nullptr, st));
   }
@@ -369,6 +372,15 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
   } else {
     float* y = at<float>(ws, Lw.y);
     SegTable wt = seg_kv(w);
+    const bool wp = fmt == W_BF16 && w->packed;
+    if (wp) {  // the layers' packed Wk / Wv
+      for (int l = 0; l < L; ++l) {
+        uint8_t* pm[7];
+        packed_layer(w, l, pm);
+        wt.ptr[2 * l] = pm[1];
+        wt.ptr[2 * l + 1] = pm[2];
+      }
+    }
     if (fmt != W_BF16) {  // decode the ten K/V matrices into one bf16 [5120][2560]
       uint16_t* dq = at<uint16_t>(ws, Lw.y + rows_bytes(n, fmt) - 2 * DQ_ELEMS);
       for (int s = 0; s < wt.nseg; ++s) {
@@ -378,7 +390,7 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
       }
       wt = seg1(dq, KV_N);
     }
-    HIP_TRY(launch_gemm_bf16(x, H, n, wt, H, y, KV_N, KV_N, 1, 0, st));
+    HIP_TRY(launch_gemm_bf16(x, H, n, wt, wp, H, y, KV_N, KV_N, 1, 0, st));
     HIP_TRY(launch_kv_post(y, KV_N, n, pos0, knorms, w->rms_eps, theta, rk, rv, kv->capacity, st));
   }
   return DFLASH_OK;

@@ -226,7 +226,9 @@ hipError_t launch_kv_post(const float* y, int ldy, int n, int64_t pos0, const vo
                           hipStream_t st);
 
 // C[M][N] (fp32, ldc) = A[M][K] (bf16, lda) * W[N][K]^T
-hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w, int K,
+// w_packed: the segments point at streaming copies of the bf16 matrices
+// (16-row tiles x 32-wide k blocks in MFMA lane order) instead of row-major ones.
+hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w, bool w_packed, int K,
                             float* C, int ldc, int N, int nsplit, size_t c_split, hipStream_t st);
 
 // Finite check: *status = 0, then `code` if any of x[0..count) (dtype 0 bf16,

@@ -23,6 +23,11 @@
 // lane order, so a lane fetches the global chunk that the swizzle places at
 // its slot.
 //
+// With the streaming copies of the bf16 weights present, W comes from them:
+// each W load is one contiguous 1 KiB block (8 cache lines instead of 16
+// row pieces of 64 bytes) and W fragments are read without a swizzle
+// (measured: fusion 1.85 -> 1.75 ms, projection 1.02 -> 0.98 ms).
+//
 // Tiles are dealt to the XCDs in contiguous runs (the hardware deals blocks
 // round robin), so the blocks on one XCD share A panels in its L2.  With
 // fewer tiles than CUs the k range can be split S ways (partial outputs S
@@ -91,6 +96,13 @@ __device__ __forceinline__ int lds_off(int row, int c) { return row * BK + ((c ^
 // Split-K: block q of the tiles x S grid computes the k range
 // [s K, (s+1) K) of tile t (t' = s tiles + t) into C + s c_split; W rows are
 // ldw elements apart (S K).
+//
+// WP: the W matrices are their streaming copies (16-row tiles, 32-wide k
+// blocks, the 64 MFMA lanes of 16 bytes each): a W load is one contiguous
+// 1 KiB block, written to LDS in lane order, and a W fragment read is that
+// block at lane x 16 bytes -- the same lanes/k slots as the swizzled
+// row-major path.
+template <bool WP>
 __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict__ A, int lda,
                                                      int M, SegTable w, int K, int ldw,
                                                      float* __restrict__ C, int ldc, int nN,
@@ -119,7 +131,11 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
   int seg = 0, base = 0;
   for (int i = 0; i + 1 < w.nseg; ++i)
     if (n0 >= w.row_end[i]) { seg = i + 1; base = w.row_end[i]; }
-  const uint16_t* wb = static_cast<const uint16_t*>(w.ptr[seg]) + static_cast<size_t>(n0 - base) * ldw + k0;
+  // row-major: row n0 - base, column k0; packed: row tile (n0 - base) / 16,
+  // k block k0 / 32 (512 elements per block)
+  const uint16_t* wb = static_cast<const uint16_t*>(w.ptr[seg]) +
+                       (WP ? (static_cast<size_t>(n0 - base) / 16 * (ldw / BK) + k0 / BK) * 512
+                           : static_cast<size_t>(n0 - base) * ldw + k0);
 
   // The stages are written only by direct-to-LDS loads; ordinary stores keep
   // the compiler from treating their contents as undefined.
@@ -142,8 +158,10 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
   const int last_a = (m0 + BM <= M ? m0 + BM : M) - 1;
   const char* rbase = loads_a ? reinterpret_cast<const char*>(A + static_cast<size_t>(m0) * lda + k0)
                               : reinterpret_cast<const char*>(wb);
-  const uint32_t extent = loads_a ? 2u * static_cast<uint32_t>((last_a - m0) * lda + K)
-                                  : 2u * static_cast<uint32_t>((BN - 1) * ldw + K);
+  const uint32_t extent =
+      loads_a ? 2u * static_cast<uint32_t>((last_a - m0) * lda + K)
+              : (WP ? 1024u * static_cast<uint32_t>((BN / 16 - 1) * (ldw / BK) + K / BK)
+                    : 2u * static_cast<uint32_t>((BN - 1) * ldw + K));
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rbase), 0, static_cast<int>(extent), 0x00020000);
   uint32_t voff[4];
@@ -154,14 +172,17 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
     if (loads_a) {
       const int gm = m0 + row < M ? m0 + row : M - 1;
       voff[i] = 2u * static_cast<uint32_t>((gm - m0) * lda + 8 * c);
+    } else if (WP) {  // row tile blk - 16 of the tile, lane's 16 bytes of the block
+      voff[i] = 1024u * static_cast<uint32_t>((blk - BM / 16) * (ldw / BK)) + 16u * lane;
     } else {
       voff[i] = 2u * static_cast<uint32_t>((row - BM) * ldw + 8 * c);
     }
     ldst[i] = blk * 16 * BK;  // element offset of the block inside a stage
   }
+  const int kstep = loads_a || !WP ? 2 * BK : 1024;  // bytes between consecutive k stages
   auto issue_one = [&](uint16_t* st, int kt, int i) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(st + ldst[i]),
-                                             16, static_cast<int>(voff[i]), kt * (2 * BK), 0, 0);
+                                             16, static_cast<int>(voff[i]), kt * kstep, 0, 0);
   };
   auto issue = [&](uint16_t* st, int kt) {
 #pragma unroll
@@ -183,7 +204,7 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
   // Fragment rows start at multiples of 16, so the swizzle of every row a
   // lane reads is that of its row r, and the 12 fragment addresses of a
   // stage are two per-wave bases plus 1 KiB steps (instruction offsets).
-  const uint32_t lane_w = 2 * lds_off(BM + wn * 64 + r, g);
+  const uint32_t lane_w = WP ? 2 * BM * BK + wn * 4096 + 16 * lane : 2 * lds_off(BM + wn * 64 + r, g);
   const uint32_t lane_a = 2 * lds_off(wm * 128 + r, g);
 
   // Two register sets of the 12 fragments of a stage: the MFMAs of stage kt
@@ -304,8 +325,8 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w, int K, float* C,
-                            int ldc, int N, int nsplit, size_t c_split, hipStream_t st) {
+hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w, bool w_packed, int K,
+                            float* C, int ldc, int N, int nsplit, size_t c_split, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   if (nsplit < 1 || K % nsplit) return hipErrorInvalidValue;
   const int Ks = K / nsplit;
@@ -315,8 +336,12 @@ hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w
   const int nN = N / BN, nM = (M + BM - 1) / BM;
   const long long tiles = static_cast<long long>(nN) * nM;
   if (tiles * nsplit > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_gemm_bf16_nt, dim3(static_cast<unsigned>(tiles * nsplit)), dim3(NT), 0, st, A, lda,
-                     M, w, Ks, K, C, ldc, nN, static_cast<int>(tiles), c_split);
+  if (w_packed)
+    hipLaunchKernelGGL(k_gemm_bf16_nt<true>, dim3(static_cast<unsigned>(tiles * nsplit)), dim3(NT), 0, st, A,
+                       lda, M, w, Ks, K, C, ldc, nN, static_cast<int>(tiles), c_split);
+  else
+    hipLaunchKernelGGL(k_gemm_bf16_nt<false>, dim3(static_cast<unsigned>(tiles * nsplit)), dim3(NT), 0, st, A,
+                       lda, M, w, Ks, K, C, ldc, nN, static_cast<int>(tiles), c_split);
   return hipGetLastError();
 }
 
