@@ -114,10 +114,11 @@ typedef struct {
    * matrices and fc, in the backbone's format), written by
    * dflash_pack_weights after the weights are loaded (and again whenever
    * those tensors change).  Required by dflash_draft_block (NULL ->
-   * DFLASH_EINVAL); used when set by dflash_lm_head_argmax and by the
-   * few-row (<= 64) paths of dflash_fuse_context / dflash_project_ctx_kv,
-   * which otherwise read the row-major tensors above, as the many-row paths
-   * always do.  Caller-owned, like everything else. */
+   * DFLASH_EINVAL); used when set by dflash_lm_head_argmax, by the few-row
+   * (<= 64) paths of dflash_fuse_context / dflash_project_ctx_kv and, for a
+   * bf16 backbone, by their many-row paths too; without it they read the
+   * row-major tensors above (a quantized backbone's many-row paths always
+   * decode those).  Caller-owned, like everything else. */
   void* packed;
 } dflash_weights;
 
