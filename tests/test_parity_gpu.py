@@ -118,10 +118,11 @@ def test_fuse_context(dev_w, ow, n):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("n", [13, 40])
+@pytest.mark.parametrize("n", [13, 40, 300])
 def test_few_row_paths_without_streaming_copies(dev_w, ow, n):
-    """The few-row fusion and projection read the row-major tensors when the
-    descriptor carries no streaming copies: same bars."""
+    """Fusion and projection read the row-major tensors when the descriptor
+    carries no streaming copies -- the few-row GEMV (13, 40) and the many-row
+    GEMM (300, k split in two): same bars."""
     saved = dev_w.desc.packed
     dev_w.desc.packed = None
     try:
