@@ -299,14 +299,15 @@ extern "C" int32_t dflash_fuse_context(const dflash_weights* w, const void* taps
     }
   } else {
     float* y = at<float>(ws, Lw.y);
-    // bf16: the streaming copy of fc when there is one (contiguous 1 KiB
-    // loads); quantized: decode once to row-major bf16
-    const bool wp = fmt == W_BF16 && w->packed;
+    // W in the streaming layout (contiguous 1 KiB loads): bf16 -> fc's
+    // streaming copy when there is one; quantized -> decoded once into it
+    bool wp = fmt == W_BF16 && w->packed;
     SegTable wt = seg1(wp ? packed_fc(w) : w->fc, H);
     if (fmt != W_BF16) {
       uint16_t* dq = at<uint16_t>(ws, Lw.y + rows_bytes(n, fmt) - 2 * DQ_ELEMS);
-      HIP_TRY(launch_dequant_bf16(w->fc, fmt, H, T * H, dq, st));
+      HIP_TRY(launch_dequant_bf16(w->fc, fmt, H, T * H, dq, 0, st));
       wt = seg1(dq, H);
+      wp = true;
     }
     // Fewer 256 x 256 output tiles than compute units (n < 6400 rows): split
     // the k range in two (the fp32 region holds two partial outputs, which
@@ -372,7 +373,7 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
   } else {
     float* y = at<float>(ws, Lw.y);
     SegTable wt = seg_kv(w);
-    const bool wp = fmt == W_BF16 && w->packed;
+    bool wp = fmt == W_BF16 && w->packed;
     if (wp) {  // the layers' packed Wk / Wv
       for (int l = 0; l < L; ++l) {
         uint8_t* pm[7];
@@ -381,14 +382,14 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
         wt.ptr[2 * l + 1] = pm[2];
       }
     }
-    if (fmt != W_BF16) {  // decode the ten K/V matrices into one bf16 [5120][2560]
+    if (fmt != W_BF16) {  // decode the ten K/V matrices into one bf16 [5120][2560], streaming layout
       uint16_t* dq = at<uint16_t>(ws, Lw.y + rows_bytes(n, fmt) - 2 * DQ_ELEMS);
       for (int s = 0; s < wt.nseg; ++s) {
         const int r0 = s ? wt.row_end[s - 1] : 0;
-        HIP_TRY(launch_dequant_bf16(wt.ptr[s], fmt, wt.row_end[s] - r0, H,
-                                    dq + static_cast<size_t>(r0) * H, st));
+        HIP_TRY(launch_dequant_bf16(wt.ptr[s], fmt, wt.row_end[s] - r0, H, dq, r0, st));
       }
       wt = seg1(dq, KV_N);
+      wp = true;
     }
     HIP_TRY(launch_gemm_bf16(x, H, n, wt, wp, H, y, KV_N, KV_N, 1, 0, st));
     HIP_TRY(launch_kv_post(y, KV_N, n, pos0, knorms, w->rms_eps, theta, rk, rv, kv->capacity, st));

@@ -203,8 +203,9 @@ hipError_t launch_pack_bf16(const void* src, int N, int K, void* dst, hipStream_
 hipError_t launch_pack_units(const void* src, int N, int per_row, int unit, void* dst,
                              hipStream_t st);
 
-// Quantized [rows][K] matrix (fmt Q8_0 / Q4_0) -> bf16 [rows][K].
-hipError_t launch_dequant_bf16(const void* src, int fmt, int rows, int K, uint16_t* dst,
+// Quantized [rows][K] matrix (fmt Q8_0 / Q4_0) -> rows row0 .. row0+rows-1
+// of a bf16 [.][K] matrix in the streaming layout (rows, row0 multiples of 16).
+hipError_t launch_dequant_bf16(const void* src, int fmt, int rows, int K, uint16_t* dst, int row0,
                                hipStream_t st);
 
 // LM head + greedy argmax over the vocabulary.

@@ -207,10 +207,13 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(GemvArgs a) {
 }
 
 // Quantized matrix -> bf16 copy (value q * scale, rounded once), for the
-// many-row GEMM path.  One thread per 8 output elements.
+// many-row GEMM path, in the streaming layout of a bf16 [row0 + rows][K]
+// matrix (16-row tiles, 32-wide k blocks, MFMA lane order; the 8 elements a
+// thread produces are one lane's contiguous 16 bytes there).  One thread per
+// 8 output elements.
 template <int FMT>
 __global__ __launch_bounds__(256) void k_dequant_bf16(const uint8_t* src, int rows, int K,
-                                                      uint16_t* dst) {
+                                                      uint16_t* dst, int row0) {
   const size_t n8 = static_cast<size_t>(rows) * K / 8;
   for (size_t e = blockIdx.x * 256ull + threadIdx.x; e < n8; e += static_cast<size_t>(gridDim.x) * 256) {
     const size_t k0 = e * 8;  // first element (row-major)
@@ -239,7 +242,9 @@ __global__ __launch_bounds__(256) void k_dequant_bf16(const uint8_t* src, int ro
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       o[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
-    *reinterpret_cast<uint4*>(dst + k0) = make_uint4(o[0], o[1], o[2], o[3]);
+    const size_t n = row0 + k0 / K, k = k0 % K;
+    const size_t at = ((n / 16 * (K / 32) + k / 32) * 64 + n % 16 + 16 * ((k % 32) / 8)) * 8;
+    *reinterpret_cast<uint4*>(dst + at) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -390,17 +395,17 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_dequant_bf16(const void* src, int fmt, int rows, int K, uint16_t* dst,
+hipError_t launch_dequant_bf16(const void* src, int fmt, int rows, int K, uint16_t* dst, int row0,
                                hipStream_t st) {
-  if (rows < 0 || K % 32) return hipErrorInvalidValue;
+  if (rows < 0 || K % 32 || rows % 16 || row0 % 16 || row0 < 0) return hipErrorInvalidValue;
   if (rows == 0) return hipSuccess;
   const size_t n8 = static_cast<size_t>(rows) * K / 8;
   const int grid = static_cast<int>(n8 / 256 < 4096 ? (n8 + 255) / 256 : 4096);
   const uint8_t* s8 = static_cast<const uint8_t*>(src);
   if (fmt == W_Q8_0)
-    hipLaunchKernelGGL(k_dequant_bf16<W_Q8_0>, dim3(grid), dim3(256), 0, st, s8, rows, K, dst);
+    hipLaunchKernelGGL(k_dequant_bf16<W_Q8_0>, dim3(grid), dim3(256), 0, st, s8, rows, K, dst, row0);
   else if (fmt == W_Q4_0)
-    hipLaunchKernelGGL(k_dequant_bf16<W_Q4_0>, dim3(grid), dim3(256), 0, st, s8, rows, K, dst);
+    hipLaunchKernelGGL(k_dequant_bf16<W_Q4_0>, dim3(grid), dim3(256), 0, st, s8, rows, K, dst, row0);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
