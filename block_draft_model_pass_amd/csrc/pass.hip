@@ -1006,24 +1006,25 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KV
 }
 
 // Merge of the chunks of one (KV head, query tile, query row) -- a group.
-// The last ceil(groups / 2) blocks merge two groups each, one per 256-thread
-// half, so that the O-projection blocks (the first 160) are free to stream
-// their weights during this phase.  In a half, 32 threads cover the 256 head
-// dims of one chunk (8 each) and 8 such slots take chunks slot, slot + 8, ...
-// with 16-byte loads; wave 0 of the half turns the chunks' maxima and sums
-// into weights w_c = 2^(m_c - M) l_c (chunk outputs are already normalised
-// by l_c).  Partials of this layer were written once, so plain loads read
-// them.
-constexpr int MRG_U = NCH_PASS / 8;  // chunks per slot (16)
+// The last `groups` blocks (192 at 8 block rows; the launch requires a grid
+// at least that large) merge one group each.  32 threads cover the 256 head
+// dims of one chunk (8 each) and 16 such slots take chunks slot, slot + 16,
+// ... with 16-byte loads; wave 0 turns the chunks' maxima and sums into
+// weights w_c = 2^(m_c - M) l_c (chunk outputs are already normalised by
+// l_c).  The maxima and sums are loaded before the chunk outputs, so the
+// weights wait only for them.  Partials of this layer were written once, so
+// plain loads read them.  (Two groups per block on the last 96 blocks, which
+// left the first 160 free to start their O-projection prefetch at once, was
+// 3 us per pass slower.)
+constexpr int MRG_U = NCH_PASS / 16;  // chunks per slot (8)
 
 template <int FMT>
 __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
   const int ngroup = NKV * a.nqt * 16;
-  const int nmb = (ngroup + 1) / 2;
-  const int w0 = gridDim.x - nmb;
+  const int w0 = gridDim.x - ngroup;
   if (blockIdx.x >= w0) {
-    const int tid = otid(), half = tid >> 8, ht = tid & 255, lane = tid & 63;
-    const int grp = 2 * (blockIdx.x - w0) + half;
+    const int tid = otid(), lane = tid & 63;
+    const int grp = blockIdx.x - w0;
     const int gc = grp < ngroup ? grp : 0;  // addresses stay inside the partials
     const int n = gc & 15, t = (gc >> 4) % a.nqt, j = (gc >> 4) / a.nqt;
     const bool act = grp < ngroup && t * 16 + n < G * a.B;
@@ -1033,23 +1034,28 @@ __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
     const uint16_t* po = a.po + l * POSTRIDE;
     const float* pm = a.pm + l * PMSTRIDE;
     const float* pl = a.pl + l * PMSTRIDE;
-    const int slot = ht >> 5, dp = ht & 31;
+    const int slot = tid >> 5, dp = tid & 31;
+    float mraw[2], lraw[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int c = lane + 64 * q;
+      mraw[q] = gld<float>(pm + row0 + (c < nc ? c : 0) * cstride);
+      lraw[q] = gld<float>(pl + row0 + (c < nc ? c : 0) * cstride);
+    }
     uint4 ov[MRG_U];
 #pragma unroll
     for (int u = 0; u < MRG_U; ++u) {
-      const int c = slot + 8 * u;
+      const int c = slot + 16 * u;
       ov[u] = gld<uint4>(po + (row0 + (c < nc ? c : 0) * cstride) * D + 8 * dp);  // c >= nc: unused
     }
-    if ((ht >> 6) == 0) {  // wave 0 of the half: chunk weights
+    if (wid() == 0) {  // chunk weights
       float mv[2], lv[2];
       float M = NEG_INF;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int c = lane + 64 * q;
-        const float mraw = gld<float>(pm + row0 + (c < nc ? c : 0) * cstride);
-        const float lraw = gld<float>(pl + row0 + (c < nc ? c : 0) * cstride);
-        mv[q] = act && c < nc ? mraw : NEG_INF;
-        lv[q] = act && c < nc ? lraw : 0.f;
+        mv[q] = act && c < nc ? mraw[q] : NEG_INF;
+        lv[q] = act && c < nc ? lraw[q] : 0.f;
         M = fmaxf(M, mv[q]);
       }
 #pragma unroll
@@ -1059,11 +1065,11 @@ __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
       for (int q = 0; q < 2; ++q) {
         const int c = lane + 64 * q;
         const float wt = act && c < nc ? exp2f(mv[q] - M) * lv[q] : 0.f;
-        s.mw[half * NCH_PASS + c] = wt;
+        s.mw[c] = wt;
         Ls += wt;
       }
       Ls = wave_sum(Ls);
-      if (lane == 0) s.scal[half] = Ls > 0.f ? 1.0f / Ls : 0.f;
+      if (lane == 0) s.scal[0] = Ls > 0.f ? 1.0f / Ls : 0.f;
     }
     lds_sync();
     float acc[8];
@@ -1071,9 +1077,9 @@ __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
 #pragma unroll
     for (int u = 0; u < MRG_U; ++u) {
-      const int c = slot + 8 * u;
+      const int c = slot + 16 * u;
       if (c < nc) {
-        const float wt = s.mw[half * NCH_PASS + c];
+        const float wt = s.mw[c];
         const uint32_t wd[4] = {ov[u].x, ov[u].y, ov[u].z, ov[u].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1082,19 +1088,19 @@ __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
         }
       }
     }
-    // slots 1..7 hand their sums to slot 0 (fixed order: deterministic)
-    float* red = reinterpret_cast<float*>(s.x);  // [2][8][256]
+    // slots 1..15 hand their sums to slot 0 (fixed order: deterministic)
+    float* red = reinterpret_cast<float*>(s.x);  // [16][256]
     if (slot > 0) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) red[(half * 8 + slot) * D + 8 * dp + i] = acc[i];
+      for (int i = 0; i < 8; ++i) red[slot * D + 8 * dp + i] = acc[i];
     }
     lds_sync();
     if (slot == 0 && act) {
-      for (int sl = 1; sl < 8; ++sl) {
+      for (int sl = 1; sl < 16; ++sl) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += red[(half * 8 + sl) * D + 8 * dp + i];
+        for (int i = 0; i < 8; ++i) acc[i] += red[sl * D + 8 * dp + i];
       }
-      const float sc = s.scal[half];
+      const float sc = s.scal[0];
       uint32_t pk[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
