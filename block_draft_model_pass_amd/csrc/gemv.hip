@@ -374,7 +374,9 @@ __global__ void k_verify(const int32_t* cand, const int32_t* target, int k, int3
 
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t st) {
   if (a.B < 1 || a.B > GEMV_ROWS || a.N % 16 || a.K % 128) return hipErrorInvalidValue;
-  constexpr int NW = 4, KBW = 5;  // 4 waves x 640 k per block and split
+  // 10 waves x 256 k per block and split (4 x 640 and 5 x 512 were 1.2 and
+  // 2.9 us slower on the 8-row fc GEMV)
+  constexpr int NW = 10, KBW = 2;
   if ((a.K / 128) % (NW * KBW) != 0 || a.S != a.K / (128 * NW * KBW)) return hipErrorInvalidValue;
   const dim3 grid(a.N / 16, a.S), block(NW * 64);
   if (a.packed) {
