@@ -1472,21 +1472,31 @@ __global__ __launch_bounds__(256) void k_pass_init(LayerTab tab, LayerTab* tab_o
   if (b == 0 && threadIdx.x == 0) *tab_out = tab;
   const int tok = b == 0 ? anchor : mask;
   const uint16_t* row = embed + static_cast<size_t>(tok) * H;
-  float sq = 0.f;
-  for (int e = threadIdx.x; e < H; e += 256) {
-    const float v = bf16_to_f32(row[e]);
-    h[static_cast<size_t>(b) * H + e] = v;
-    h16[static_cast<size_t>(b) * H + e] = f32_to_f16_bits(v);
-    sq += v * v;
-  }
-  sq = block_sum<256>(sq, red);
-  if (threadIdx.x == 0) ss[b] = sq;
+  // All of the row's loads are issued before any store (a store could alias
+  // the row, so a load after it would wait for it: one memory round trip per
+  // element group), and the RoPE table is computed while they are in flight.
+  constexpr int PER = H / 256;
+  static_assert(H % 256 == 0, "embedding row split over 256 threads");
+  uint16_t raw[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) raw[i] = row[threadIdx.x + 256 * i];
   if (threadIdx.x < D / 2) {
     const double inv = pow(theta, -2.0 * static_cast<double>(threadIdx.x) / static_cast<double>(D));
     double sn, cs;
     sincos(static_cast<double>(p + b) * inv, &sn, &cs);
     rope[b * (D / 2) + threadIdx.x] = make_float2(static_cast<float>(cs), static_cast<float>(sn));
   }
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    const float v = bf16_to_f32(raw[i]);
+    h[static_cast<size_t>(b) * H + e] = v;
+    h16[static_cast<size_t>(b) * H + e] = f32_to_f16_bits(v);
+    sq += v * v;
+  }
+  sq = block_sum<256>(sq, red);
+  if (threadIdx.x == 0) ss[b] = sq;
 }
 
 }  // namespace

@@ -14,7 +14,7 @@ import torch
 from block_draft_model_pass_amd import _lib, synth
 from block_draft_model_pass_amd.device import Drafter, KVRing, stream_ptr
 from oracle import dflash_oracle as O
-from test_parity_gpu import MARGIN, TOL, dec_bf16, dev_w, host_w, ow, row_rel_err, say  # noqa: F401
+from test_parity_gpu import MARGIN, TOL, check_cands, dec_bf16, dev_w, host_w, ow, row_rel_err, say  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
@@ -51,8 +51,7 @@ def test_lm_head_argmax(dev_w, ow, rows, packed):
     say(f"lm head rows={rows} packed={packed} logits err {err:.3e} cand {cand.tolist()} "
         f"ref {ocand.tolist()} margins {np.round(margin, 3).tolist()}")
     assert err <= TOL
-    sure = margin > MARGIN
-    assert np.array_equal(cand[sure], ocand[sure])
+    check_cands(cand, ocand, ref.astype(np.float32), margin)
 
 
 def test_lm_head_layouts_agree_bitwise(dev_w):
