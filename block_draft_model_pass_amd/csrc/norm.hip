@@ -96,14 +96,28 @@ __global__ __launch_bounds__(KV_NT) void k_kv_post(const float* y, int ldy, int 
   const int nz = gridDim.z / 2, kind = blockIdx.z / nz, hpb = NKV / nz, j0 = (blockIdx.z % nz) * hpb;
   if (kind == 0) {
     constexpr int CPB = 8, TPC = KV_NT / CPB;  // cells per block, threads per cell (4 pairs each)
-    __shared__ double invf[D / 2];
-    if (t < D / 2) invf[t] = pow(theta, -2.0 * static_cast<double>(t) / static_cast<double>(D));
-    __syncthreads();
     const int64_t gp = (pos0 / CPB + b) * CPB;
     const int c = t / TPC, p = t % TPC, row = static_cast<int>(gp - pos0) + c;
     const bool valid = row >= 0 && row < n;
     const int rowc = row < 0 ? 0 : (row < n ? row : n - 1);  // in-bounds reads for unused cells
     const size_t cell = static_cast<size_t>((gp + c) % cap);
+    // The projected values and the gains are loaded first, so that the
+    // angles below are computed while they are in flight (head slots past
+    // this block's heads re-read its first head and are never used).
+    f32x4 lo[NKV], hi[NKV];
+#pragma unroll
+    for (int jj = 0; jj < NKV; ++jj) {
+      const int j = jj < hpb ? j0 + jj : j0;
+      const float* yr = y + static_cast<size_t>(rowc) * ldy + l * (2 * NKV * D) + j * D + 4 * p;
+      lo[jj] = *reinterpret_cast<const f32x4*>(yr);
+      hi[jj] = *reinterpret_cast<const f32x4*>(yr + D / 2);
+    }
+    const uint16_t* g = kn.g[l];
+    const uint2 gl = *reinterpret_cast<const uint2*>(g + 4 * p);
+    const uint2 gh = *reinterpret_cast<const uint2*>(g + D / 2 + 4 * p);
+    __shared__ double invf[D / 2];
+    if (t < D / 2) invf[t] = pow(theta, -2.0 * static_cast<double>(t) / static_cast<double>(D));
+    __syncthreads();
     float fc[4], fs[4];
     const double pos = static_cast<double>(gp + c);
 #pragma unroll
@@ -113,9 +127,6 @@ __global__ __launch_bounds__(KV_NT) void k_kv_post(const float* y, int ldy, int 
       fc[k] = static_cast<float>(cs);
       fs[k] = static_cast<float>(sn);
     }
-    const uint16_t* g = kn.g[l];
-    const uint2 gl = *reinterpret_cast<const uint2*>(g + 4 * p);
-    const uint2 gh = *reinterpret_cast<const uint2*>(g + D / 2 + 4 * p);
     const float ga[4] = {bf16_to_f32(static_cast<uint16_t>(gl.x)), bf16_to_f32(static_cast<uint16_t>(gl.x >> 16)),
                          bf16_to_f32(static_cast<uint16_t>(gl.y)), bf16_to_f32(static_cast<uint16_t>(gl.y >> 16))};
     const float gc[4] = {bf16_to_f32(static_cast<uint16_t>(gh.x)), bf16_to_f32(static_cast<uint16_t>(gh.x >> 16)),
@@ -124,12 +135,9 @@ __global__ __launch_bounds__(KV_NT) void k_kv_post(const float* y, int ldy, int 
     for (int jj = 0; jj < NKV; ++jj) {
       if (jj >= hpb) break;
       const int j = j0 + jj;
-      const float* yr = y + static_cast<size_t>(rowc) * ldy + l * (2 * NKV * D) + j * D + 4 * p;
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(yr);
-      const f32x4 hi = *reinterpret_cast<const f32x4*>(yr + D / 2);
       float ss = 0.f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) ss += lo[k] * lo[k] + hi[k] * hi[k];
+      for (int k = 0; k < 4; ++k) ss += lo[jj][k] * lo[jj][k] + hi[jj][k] * hi[jj][k];
       ss += __shfl_xor(ss, 1);
       ss += __shfl_xor(ss, 2);
       ss += __shfl_xor(ss, 4);
@@ -142,7 +150,7 @@ __global__ __launch_bounds__(KV_NT) void k_kv_post(const float* y, int ldy, int 
         float a[2], cc[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const float x = lo[k + e] * (sc * ga[k + e]), z = hi[k + e] * (sc * gc[k + e]);
+          const float x = lo[jj][k + e] * (sc * ga[k + e]), z = hi[jj][k + e] * (sc * gc[k + e]);
           a[e] = x * fc[k + e] - z * fs[k + e];
           cc[e] = z * fc[k + e] + x * fs[k + e];
         }
