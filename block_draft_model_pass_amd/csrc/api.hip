@@ -39,7 +39,10 @@ int pass_grid() {
 }
 constexpr int SMALL_ROWS = 64;        // fuse/project: skinny path up to here
 constexpr int FC_SPLITS = 5;          // k splits of the fc GEMV (K = 12800)
+constexpr int KV_SPLITS = 2;          // k splits of the Wk / Wv GEMV (K = 2560)
 constexpr size_t PART_FLOATS = static_cast<size_t>(FC_SPLITS) * GEMV_ROWS * H;
+static_assert(static_cast<size_t>(KV_SPLITS) * GEMV_ROWS * KV_N <= PART_FLOATS,
+              "the Wk / Wv partials share the fc partials' workspace");
 
 struct Layout {
   size_t part, po, pm, pl, keys, rope, ss, qkv, hv, h16, ov, uv, bar, tab, y;
@@ -365,10 +368,10 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
       a.x_stride = H;
       a.B = rows;
       a.out = part;
-      a.S = 1;
+      a.S = KV_SPLITS;
       HIP_TRY(launch_gemv(a, st));
-      HIP_TRY(launch_kv_post(part, KV_N, rows, pos0 + c0, knorms, w->rms_eps, theta, rk, rv,
-                             kv->capacity, st));
+      HIP_TRY(launch_kv_post(part, KV_N, KV_SPLITS, static_cast<size_t>(rows) * KV_N, rows, pos0 + c0,
+                             knorms, w->rms_eps, theta, rk, rv, kv->capacity, st));
     }
   } else {
     float* y = at<float>(ws, Lw.y);
@@ -392,7 +395,7 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
       wp = true;
     }
     HIP_TRY(launch_gemm_bf16(x, H, n, wt, wp, H, y, KV_N, KV_N, 1, 0, st));
-    HIP_TRY(launch_kv_post(y, KV_N, n, pos0, knorms, w->rms_eps, theta, rk, rv, kv->capacity, st));
+    HIP_TRY(launch_kv_post(y, KV_N, 1, 0, n, pos0, knorms, w->rms_eps, theta, rk, rv, kv->capacity, st));
   }
   return DFLASH_OK;
 }

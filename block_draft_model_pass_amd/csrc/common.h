@@ -220,11 +220,12 @@ hipError_t launch_rownorm(float* h, const float* part, int S, size_t part_split_
                           int part_row_stride, int rows, const uint16_t* gain, float eps,
                           uint16_t* out, int out_stride, uint16_t* out2, hipStream_t st);
 
-// Context K/V epilogue: y [n][KV_N] (row stride ldy) ->
+// Context K/V epilogue: y [n][KV_N] (row stride ldy; nsplit = 2: the sum of
+// two k-split partials, the second split_stride floats after the first) ->
 // k-norm + RoPE + fp16 into the ring.
-hipError_t launch_kv_post(const float* y, int ldy, int n, int64_t pos0, const void* const* k_norms,
-                          float eps, double theta, uint16_t* ring_k, uint16_t* ring_vt, int capacity,
-                          hipStream_t st);
+hipError_t launch_kv_post(const float* y, int ldy, int nsplit, size_t split_stride, int n,
+                          int64_t pos0, const void* const* k_norms, float eps, double theta,
+                          uint16_t* ring_k, uint16_t* ring_vt, int capacity, hipStream_t st);
 
 // C[M][N] (fp32, ldc) = A[M][K] (bf16, lda) * W[N][K]^T
 // w_packed: the segments point at streaming copies of the bf16 matrices

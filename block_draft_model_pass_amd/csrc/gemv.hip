@@ -370,14 +370,8 @@ __global__ void k_verify(const int32_t* cand, const int32_t* target, int k, int3
   }
 }
 
-}  // namespace
-
-hipError_t launch_gemv(const GemvArgs& a, hipStream_t st) {
-  if (a.B < 1 || a.B > GEMV_ROWS || a.N % 16 || a.K % 128) return hipErrorInvalidValue;
-  // 10 waves x 256 k per block and split (4 x 640 and 5 x 512 were 1.2 and
-  // 2.9 us slower on the 8-row fc GEMV)
-  constexpr int NW = 10, KBW = 2;
-  if ((a.K / 128) % (NW * KBW) != 0 || a.S != a.K / (128 * NW * KBW)) return hipErrorInvalidValue;
+template <int NW, int KBW>
+hipError_t launch_gemv_nw(const GemvArgs& a, hipStream_t st) {
   const dim3 grid(a.N / 16, a.S), block(NW * 64);
   if (a.packed) {
     switch (a.fmt) {
@@ -395,6 +389,21 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t st) {
     }
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t st) {
+  if (a.B < 1 || a.B > GEMV_ROWS || a.N % 16 || a.K % 128) return hipErrorInvalidValue;
+  // Each wave takes 256 k (KBW = 2); a block has 10 waves (2560 k per block
+  // and split: the fc GEMV, 5 splits) or 5 (1280 k: the Wk / Wv GEMV, 2
+  // splits, 640 blocks instead of 320 for 256 CUs).  4 waves x 640 k and 5 x
+  // 512 were 1.2 and 2.9 us slower on the 8-row fc GEMV.
+  constexpr int KBW = 2;
+  if (a.S < 1 || a.K % (128 * KBW * a.S) != 0) return hipErrorInvalidValue;
+  const int nw = a.K / (128 * KBW * a.S);
+  if (nw != 10 && nw != 5) return hipErrorInvalidValue;
+  return nw == 10 ? launch_gemv_nw<10, KBW>(a, st) : launch_gemv_nw<5, KBW>(a, st);
 }
 
 hipError_t launch_dequant_bf16(const void* src, int fmt, int rows, int K, uint16_t* dst, int row0,

@@ -70,7 +70,8 @@ constexpr int KV_NT = 256;  // threads of a k_kv_post block
 // Context K/V cells of n fused rows at positions pos0 .. pos0+n-1 (cell
 // pos % cap): keys get the per-head RMSNorm with the layer's k gain and the
 // NeoX rotation by pos * theta^(-2i/256) (pairs i, i+128; angle, sin and cos
-// in fp64), values are stored as they are; both in fp16.
+// in fp64), values are stored as they are; both in fp16.  NS = 2: y is the
+// sum of two k-split partials, ys floats apart.
 //
 // grid (groups8, L, 2 nz): keys (z < nz) or values, layer l = y, both heads
 // of the kind per block (nz = 1) or one (nz = 2, calls of at most 64 rows):
@@ -86,8 +87,9 @@ constexpr int KV_NT = 256;  // threads of a k_kv_post block
 //    group never wraps); thread t holds head dimension t and writes its 32
 //    cells as 64 contiguous bytes (per-element stores where the group is
 //    partial).  Blocks past groups32 have nothing to do.
-__global__ __launch_bounds__(KV_NT) void k_kv_post(const float* y, int ldy, int n, int64_t pos0,
-                                                   KNorms kn, float eps, double theta,
+template <int NS>
+__global__ __launch_bounds__(KV_NT) void k_kv_post(const float* y, int ldy, size_t ys, int n,
+                                                   int64_t pos0, KNorms kn, float eps, double theta,
                                                    uint16_t* ring_k, uint16_t* ring_vt, int cap) {
   const int b = blockIdx.x, l = blockIdx.y, t = threadIdx.x;
   // gridDim.z = 2 nz: nz = 1 (a block takes both heads of its kind) or NKV
@@ -111,6 +113,10 @@ __global__ __launch_bounds__(KV_NT) void k_kv_post(const float* y, int ldy, int 
       const float* yr = y + static_cast<size_t>(rowc) * ldy + l * (2 * NKV * D) + j * D + 4 * p;
       lo[jj] = *reinterpret_cast<const f32x4*>(yr);
       hi[jj] = *reinterpret_cast<const f32x4*>(yr + D / 2);
+      if constexpr (NS == 2) {
+        lo[jj] += *reinterpret_cast<const f32x4*>(yr + ys);
+        hi[jj] += *reinterpret_cast<const f32x4*>(yr + ys + D / 2);
+      }
     }
     const uint16_t* g = kn.g[l];
     const uint2 gl = *reinterpret_cast<const uint2*>(g + 4 * p);
@@ -184,8 +190,12 @@ __global__ __launch_bounds__(KV_NT) void k_kv_post(const float* y, int ldy, int 
       for (int c = 0; c < BLK_CELLS; c += 2) {
         const int r0 = rb + c < 0 ? 0 : (rb + c < n ? rb + c : n - 1);
         const int r1 = rb + c + 1 < 0 ? 0 : (rb + c + 1 < n ? rb + c + 1 : n - 1);
-        const float v0 = ycol[static_cast<size_t>(r0) * ldy];
-        const float v1 = ycol[static_cast<size_t>(r1) * ldy];
+        float v0 = ycol[static_cast<size_t>(r0) * ldy];
+        float v1 = ycol[static_cast<size_t>(r1) * ldy];
+        if constexpr (NS == 2) {
+          v0 += ycol[static_cast<size_t>(r0) * ldy + ys];
+          v1 += ycol[static_cast<size_t>(r1) * ldy + ys];
+        }
         o[c / 2] = f32_to_f16_bits(v0) | (static_cast<uint32_t>(f32_to_f16_bits(v1)) << 16);
       }
       if (full) {
@@ -232,19 +242,25 @@ hipError_t launch_rownorm(float* h, const float* part, int S, size_t part_split_
   return hipGetLastError();
 }
 
-hipError_t launch_kv_post(const float* y, int ldy, int n, int64_t pos0, const void* const* k_norms,
-                          float eps, double theta, uint16_t* ring_k, uint16_t* ring_vt, int capacity,
-                          hipStream_t st) {
+hipError_t launch_kv_post(const float* y, int ldy, int nsplit, size_t split_stride, int n,
+                          int64_t pos0, const void* const* k_norms, float eps, double theta,
+                          uint16_t* ring_k, uint16_t* ring_vt, int capacity, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  if (capacity % BLK_CELLS || pos0 < 0 || ldy % 4) return hipErrorInvalidValue;
+  if (capacity % BLK_CELLS || pos0 < 0 || ldy % 4 || nsplit < 1 || nsplit > 2 || split_stride % 4)
+    return hipErrorInvalidValue;
   KNorms kn;
   for (int l = 0; l < L; ++l) kn.g[l] = static_cast<const uint16_t*>(k_norms[l]);
   // 8-cell key groups; the value blocks use the first groups32 of them.
   const int64_t groups = (pos0 + n - 1) / 8 - pos0 / 8 + 1;
   if (groups > 0x7fffffff) return hipErrorInvalidValue;
   const int nz = n <= 64 ? NKV : 1;
-  hipLaunchKernelGGL(k_kv_post, dim3(static_cast<unsigned>(groups), L, 2 * nz), dim3(KV_NT), 0, st, y, ldy,
-                     n, pos0, kn, eps, theta, ring_k, ring_vt, capacity);
+  const dim3 grid(static_cast<unsigned>(groups), L, 2 * nz);
+  if (nsplit == 2)
+    hipLaunchKernelGGL(k_kv_post<2>, grid, dim3(KV_NT), 0, st, y, ldy, split_stride, n, pos0, kn, eps,
+                       theta, ring_k, ring_vt, capacity);
+  else
+    hipLaunchKernelGGL(k_kv_post<1>, grid, dim3(KV_NT), 0, st, y, ldy, size_t{0}, n, pos0, kn, eps,
+                       theta, ring_k, ring_vt, capacity);
   return hipGetLastError();
 }
 
