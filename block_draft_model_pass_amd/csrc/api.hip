@@ -38,7 +38,7 @@ int pass_grid() {
   return cache[dev];
 }
 constexpr int SMALL_ROWS = 64;        // fuse/project: skinny path up to here
-constexpr int FC_SPLITS = 5;          // k splits of the fc GEMV (K = 12800)
+constexpr int FC_SPLITS = 10;         // k splits of the fc GEMV (K = 12800)
 constexpr int KV_SPLITS = 2;          // k splits of the Wk / Wv GEMV (K = 2560)
 constexpr size_t PART_FLOATS = static_cast<size_t>(FC_SPLITS) * GEMV_ROWS * H;
 static_assert(static_cast<size_t>(KV_SPLITS) * GEMV_ROWS * KV_N <= PART_FLOATS,

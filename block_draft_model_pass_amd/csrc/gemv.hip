@@ -395,15 +395,14 @@ hipError_t launch_gemv_nw(const GemvArgs& a, hipStream_t st) {
 
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t st) {
   if (a.B < 1 || a.B > GEMV_ROWS || a.N % 16 || a.K % 128) return hipErrorInvalidValue;
-  // Each wave takes 256 k (KBW = 2); a block has 10 waves (2560 k per block
-  // and split: the fc GEMV, 5 splits) or 5 (1280 k: the Wk / Wv GEMV, 2
-  // splits, 640 blocks instead of 320 for 256 CUs).  4 waves x 640 k and 5 x
-  // 512 were 1.2 and 2.9 us slower on the 8-row fc GEMV.
-  constexpr int KBW = 2;
-  if (a.S < 1 || a.K % (128 * KBW * a.S) != 0) return hipErrorInvalidValue;
-  const int nw = a.K / (128 * KBW * a.S);
-  if (nw != 10 && nw != 5) return hipErrorInvalidValue;
-  return nw == 10 ? launch_gemv_nw<10, KBW>(a, st) : launch_gemv_nw<5, KBW>(a, st);
+  // Each wave takes 256 k and a block 5 waves (1280 k per block and split):
+  // the fc GEMV runs in 10 k splits (1600 blocks), the Wk / Wv GEMV in 2 (640
+  // blocks for 256 CUs).  On an 8-row commit, 10 waves in 5 splits were 1 us
+  // slower for fc, and 4 waves x 640 k 2 us; one split of 10 waves was 1.2 us
+  // slower for Wk / Wv.
+  constexpr int NW = 5, KBW = 2;
+  if (a.S < 1 || a.K != a.S * 128 * NW * KBW) return hipErrorInvalidValue;
+  return launch_gemv_nw<NW, KBW>(a, st);
 }
 
 hipError_t launch_dequant_bf16(const void* src, int fmt, int rows, int K, uint16_t* dst, int row0,

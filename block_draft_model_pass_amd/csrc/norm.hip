@@ -228,12 +228,8 @@ hipError_t launch_rownorm(float* h, const float* part, int S, size_t part_split_
       hipLaunchKernelGGL(k_rownorm<2>, dim3(rows), dim3(NT), 0, st, h, part, part_split_stride,
                          part_row_stride, gain, eps, out, out_stride, out2);
       break;
-    case 3:
-      hipLaunchKernelGGL(k_rownorm<3>, dim3(rows), dim3(NT), 0, st, h, part, part_split_stride,
-                         part_row_stride, gain, eps, out, out_stride, out2);
-      break;
-    case 5:
-      hipLaunchKernelGGL(k_rownorm<5>, dim3(rows), dim3(NT), 0, st, h, part, part_split_stride,
+    case 10:
+      hipLaunchKernelGGL(k_rownorm<10>, dim3(rows), dim3(NT), 0, st, h, part, part_split_stride,
                          part_row_stride, gain, eps, out, out_stride, out2);
       break;
     default:
