@@ -337,8 +337,34 @@ def draft_block(w: dict, ctx_k: np.ndarray, ctx_v: np.ndarray, p: int,
         cand.append(c)
         top2 = np.partition(l32, -2)[-2:]
         margin.append(float(top2[1]) - float(top2[0]))
+    conf = [candidate_confidence(logits[r]) for r in range(B - 1)]
     return dict(cand=np.array(cand, dtype=np.int64), logits=logits,
-                hidden=z, margin=np.array(margin), x_last=h)
+                hidden=z, margin=np.array(margin), x_last=h, conf=np.array(conf))
+
+
+def candidate_confidence(logits_row) -> float:
+    """Probability the drafter's own distribution gives its greedy candidate:
+    the softmax of the row's logits over the whole vocabulary, evaluated at
+    the argmax, p = exp(l_c) / sum_v exp(l_v).  (PR #3322 "support the
+    official Flash-Next DFlash2 checkpoint", section "Long-prompt diagnosis
+    and fix": proposals are gated by a probability floor, spec-min-p.  The
+    pages do not print the formula; this is the plain reading: softmax of
+    the drafter's logits, no temperature.)  exp is taken after subtracting
+    the maximum, which changes nothing mathematically."""
+    l = np.asarray(logits_row, dtype=np.float64)
+    c = argmax_lowest(l.astype(np.float32))
+    e = np.exp(l - l.max())
+    return float(e[c] / e.sum())
+
+
+def gate_candidates(conf, min_p: float) -> int:
+    """Confidence gate (same section): the proposal keeps its candidates in
+    order up to, not including, the first whose probability is below the
+    floor; returns how many are kept.  A floor of 0 keeps all."""
+    n = 0
+    while n < len(conf) and conf[n] >= min_p:
+        n += 1
+    return n
 
 
 def verify_greedy(cand, target):

@@ -485,3 +485,60 @@ def test_block_attention_is_non_causal():
     base = _tiny_random_pass()
     r = _tiny_random_pass(row_tokens=[2, 10, 10, 10, 7])
     assert not np.allclose(r["hidden"][1], base["hidden"][1])
+
+
+# ------------------------------------------------------------ confidence gate
+
+def test_confidence_uniform_logits_is_one_over_vocab():
+    """Equal logits: every id has probability 1/V (closed form)."""
+    for v in (1, 7, 151936):
+        assert O.candidate_confidence(np.full(v, 0.37)) == pytest.approx(1.0 / v, rel=1e-12)
+
+
+def test_confidence_one_raised_logit_closed_form():
+    """One logit a above n-1 zeros: p = e^a / (e^a + n - 1); the candidate is
+    the raised id wherever it sits (a wrong index or a min instead of a max
+    gives 1 / (e^a + n - 1))."""
+    for n, a, at in ((10, 2.0, 0), (1000, 5.5, 617), (151936, 12.25, 151935)):
+        row = np.zeros(n)
+        row[at] = a
+        want = math.exp(a) / (math.exp(a) + n - 1)
+        assert O.candidate_confidence(row) == pytest.approx(want, rel=1e-12)
+
+
+def test_confidence_two_level_logits_and_ties():
+    """k ids at a and n-k at b: p = e^a / (k e^a + (n-k) e^b) for the lowest
+    of the tied top ids."""
+    n, k, a, b = 50, 3, 1.5, -0.25
+    row = np.full(n, b)
+    row[[4, 9, 30]] = a
+    want = math.exp(a) / (k * math.exp(a) + (n - k) * math.exp(b))
+    assert O.candidate_confidence(row) == pytest.approx(want, rel=1e-12)
+
+
+def test_confidence_is_shift_invariant_and_does_not_overflow():
+    """Softmax ignores a common shift; logits near 1e3 stay finite."""
+    rng = np.random.default_rng(5)
+    row = rng.normal(size=4096) * 3
+    base = O.candidate_confidence(row)
+    assert 0.0 < base < 1.0
+    assert O.candidate_confidence(row + 1000.0) == pytest.approx(base, rel=1e-9)
+    assert O.candidate_confidence(row - 1000.0) == pytest.approx(base, rel=1e-9)
+
+
+def test_confidence_matches_brute_force_on_tiny_rows():
+    """Probability of the argmax by summing exp over a 4-entry row written
+    out by hand."""
+    row = [0.5, -1.0, 2.0, 0.0]
+    want = math.exp(2.0) / (math.exp(0.5) + math.exp(-1.0) + math.exp(2.0) + math.exp(0.0))
+    assert O.candidate_confidence(row) == pytest.approx(want, rel=1e-12)
+
+
+def test_gate_stops_at_first_candidate_below_floor():
+    conf = [0.9, 0.5, 0.05, 0.8]
+    assert O.gate_candidates(conf, 0.0) == 4
+    assert O.gate_candidates(conf, 0.1) == 2   # the later 0.8 is cut too
+    assert O.gate_candidates(conf, 0.5) == 2   # at the floor is kept
+    assert O.gate_candidates(conf, 0.51) == 1
+    assert O.gate_candidates(conf, 0.95) == 0
+    assert O.gate_candidates([], 0.5) == 0
