@@ -213,6 +213,22 @@ def main():
         rep_ms.append(ev[0].elapsed_time(ev[1]) / args.reps)
     draft_ms = float(np.median(rep_ms))
     draft_gbs = pass_bytes(CTX) / (draft_ms * 1e-3) / 1e9
+    # The same pass with the confidence gate (softmax normaliser kept in the
+    # LM-head sweep, floor 0.5): same weight bytes, a few exp per logit.
+    g_cand = torch.empty(BLOCK - 1, dtype=torch.int32, device="cuda")
+    g_conf = torch.empty(BLOCK - 1, dtype=torch.float32, device="cuda")
+    g_keep = torch.empty(1, dtype=torch.int32, device="cuda")
+    for _ in range(20):
+        dr.draft_gated(CTX, 11, BLOCK, 0.5, cand=g_cand, conf=g_conf, n_keep=g_keep)
+    g_ms = []
+    for _ in range(5):
+        ev[0].record()
+        for _ in range(args.reps):
+            dr.draft_gated(CTX, 11, BLOCK, 0.5, cand=g_cand, conf=g_conf, n_keep=g_keep)
+        ev[1].record()
+        torch.cuda.synchronize()
+        g_ms.append(ev[0].elapsed_time(ev[1]) / args.reps)
+    gated_ms = float(np.median(g_ms))
 
     # Standalone LM head + greedy argmax (the pass's largest single stream),
     # for reference beside the whole-pass kernel.
@@ -397,6 +413,11 @@ def main():
                      "unit": "GB/s", "frac": round(draft_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(), "launch_ms": round(draft_ms, 4),
                      "bytes_per_launch": pass_bytes(CTX)},
+        "gated_draft": {"entry": "dflash_draft_block_gated (min_p 0.5)",
+                        "ms_per_pass": round(gated_ms, 4),
+                        "ms_range_of_5_repeats": [round(min(g_ms), 4), round(max(g_ms), 4)],
+                        "passes_per_s": round(1e3 / gated_ms, 2),
+                        "overhead_vs_plain": round(gated_ms / draft_ms - 1.0, 4)},
         "lm_head_standalone": {"kernel": "k_lmhead_bf16 + k_argmax_reduce (dflash_lm_head_argmax)",
                                "ms": round(lm_ms, 4), "bytes": lm_head_bytes(),
                                "achieved_GBs": round(lm_gbs, 1),

@@ -87,6 +87,11 @@ def load() -> ctypes.CDLL:
                                        c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_size_t, c_void_p]
     lib.dflash_draft_block.restype = c_int32
+    lib.dflash_draft_block_gated.argtypes = [P(dflash_weights), P(dflash_kv), c_int64,
+                                             c_int32, c_int32, c_int32, ctypes.c_float,
+                                             c_void_p, c_void_p, c_void_p, c_void_p,
+                                             c_size_t, c_void_p]
+    lib.dflash_draft_block_gated.restype = c_int32
     lib.dflash_lm_head_argmax.argtypes = [P(dflash_weights), c_void_p, c_int32, c_void_p,
                                           c_void_p, c_void_p, c_size_t, c_void_p]
     lib.dflash_lm_head_argmax.restype = c_int32
@@ -142,6 +147,13 @@ def dflash_draft_block(w, kv, p, anchor_id, mask_id, block, cand, logits_opt,
     rc = load().dflash_draft_block(_ref(w), _ref(kv), p, anchor_id, mask_id, block, cand,
                                    logits_opt, hidden_opt, ws, ws_bytes, stream)
     return _check(rc, "dflash_draft_block") if check else rc
+
+
+def dflash_draft_block_gated(w, kv, p, anchor_id, mask_id, block, min_p, cand, conf,
+                             n_keep, ws, ws_bytes, stream=None, check=True):
+    rc = load().dflash_draft_block_gated(_ref(w), _ref(kv), p, anchor_id, mask_id, block,
+                                         min_p, cand, conf, n_keep, ws, ws_bytes, stream)
+    return _check(rc, "dflash_draft_block_gated") if check else rc
 
 
 def dflash_lm_head_argmax(w, hidden, rows, cand, logits_opt, ws, ws_bytes, stream=None,

@@ -45,7 +45,7 @@ static_assert(static_cast<size_t>(KV_SPLITS) * GEMV_ROWS * KV_N <= PART_FLOATS,
               "the Wk / Wv partials share the fc partials' workspace");
 
 struct Layout {
-  size_t part, po, pm, pl, keys, rope, ss, qkv, hv, h16, ov, uv, bar, tab, y;
+  size_t part, po, pm, pl, keys, lse, rope, ss, qkv, hv, h16, ov, uv, bar, tab, y;
   size_t fixed;  // bytes before y
 };
 
@@ -63,6 +63,7 @@ Layout layout() {
   L.pm = take(off, pass_pml_bytes());
   L.pl = take(off, pass_pml_bytes());
   L.keys = take(off, sizeof(uint64_t) * KEYS_MAX * MAXB);
+  L.lse = take(off, sizeof(uint64_t) * KEYS_MAX * MAXB);
   L.rope = take(off, sizeof(float) * 2 * MAXB * (D / 2));
   // per-layer / per-version copies used by the persistent pass
   constexpr size_t HV = 2 * dfl::L + 1, NL = dfl::L;
@@ -400,10 +401,13 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
   return DFLASH_OK;
 }
 
-extern "C" int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* kv, int64_t p,
-                                      int32_t anchor_id, int32_t mask_id, int32_t block,
-                                      int32_t* cand, void* logits_opt, void* hidden_opt,
-                                      void* ws, size_t ws_bytes, void* stream) {
+namespace {
+// Shared body of dflash_draft_block and dflash_draft_block_gated (conf and
+// nkeep null for the former).
+int32_t draft_block_impl(const dflash_weights* w, const dflash_kv* kv, int64_t p,
+                         int32_t anchor_id, int32_t mask_id, int32_t block, int32_t* cand,
+                         float* conf, int32_t* nkeep, float min_p, void* logits_opt,
+                         void* hidden_opt, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_weights(w);
   if (rc) return rc;
   rc = check_kv(kv);
@@ -487,8 +491,34 @@ extern "C" int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* 
   q.cand = cand;
   q.logits = static_cast<uint16_t*>(logits_opt);
   q.hidden = static_cast<uint16_t*>(hidden_opt);
+  q.lse = at<uint64_t>(ws, Lw.lse);
+  q.conf = conf;
+  q.nkeep = nkeep;
+  q.min_p = min_p;
   HIP_TRY(launch_draft_pass(q, st));
   return DFLASH_OK;
+}
+}  // namespace
+
+extern "C" int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* kv, int64_t p,
+                                      int32_t anchor_id, int32_t mask_id, int32_t block,
+                                      int32_t* cand, void* logits_opt, void* hidden_opt,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  return draft_block_impl(w, kv, p, anchor_id, mask_id, block, cand, nullptr, nullptr, 0.f,
+                          logits_opt, hidden_opt, ws, ws_bytes, stream);
+}
+
+extern "C" int32_t dflash_draft_block_gated(const dflash_weights* w, const dflash_kv* kv,
+                                            int64_t p, int32_t anchor_id, int32_t mask_id,
+                                            int32_t block, float min_p, int32_t* cand,
+                                            float* conf, int32_t* n_keep, void* ws,
+                                            size_t ws_bytes, void* stream) {
+  if (block < 2 || !cand || !conf || !n_keep) return DFLASH_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(conf) & 3u) || (reinterpret_cast<uintptr_t>(n_keep) & 3u))
+    return DFLASH_EINVAL;
+  if (!(min_p >= 0.f && min_p <= 1.f)) return DFLASH_EINVAL;  // rejects NaN too
+  return draft_block_impl(w, kv, p, anchor_id, mask_id, block, cand, conf, n_keep, min_p,
+                          nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 extern "C" int32_t dflash_lm_head_argmax(const dflash_weights* w, const void* hidden,

@@ -277,6 +277,7 @@ struct PassLaunch {
   uint16_t* o16;
   uint16_t* u16;
   uint64_t* keys;
+  uint64_t* lse;             // [grid][8] softmax (max, sum) pairs
   unsigned* bar;
   void* tab;                 // workspace room for the per-layer pointer table
   unsigned spin_limit;
@@ -284,6 +285,9 @@ struct PassLaunch {
   int32_t* cand;
   uint16_t* logits;
   uint16_t* hidden;
+  float* conf = nullptr;     // [B-1] candidate probabilities, or null
+  int32_t* nkeep = nullptr;  // confidence-gated candidate count, or null
+  float min_p = 0.f;
 };
 
 hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st);

@@ -159,12 +159,16 @@ struct PassArgs {
   uint16_t* o16;     // [L][8][NQ*D]
   uint16_t* u16;     // [L][8][F]
   uint64_t* keys;    // [grid][8]
+  uint64_t* lse;     // [grid][8] per-block (max, sum) pairs of the softmax sweep
   unsigned* bar;     // barrier words (BAR_*)
   unsigned spin_limit;
   // outputs
   int32_t* cand;
   uint16_t* logits;
   uint16_t* hidden;
+  float* conf;       // [B-1] or null: softmax probability of each candidate
+  int32_t* nkeep;    // or null: leading candidates whose conf >= min_p
+  float min_p;
 };
 
 struct Smem {
@@ -173,6 +177,8 @@ struct Smem {
   float scal[64];              // per-row scales / merge weights
   float mw[4 * 256];           // merge: chunk weights and partial sums
   uint64_t best[2][64];
+  float2 lse[2][64];
+  float cf[MAXB];
 };
 
 // The layer table through the constant address space: indexed by the
@@ -1306,6 +1312,24 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// Online log-sum-exp state (m, s) of a set of logits: m their maximum, s the
+// sum of exp(l - m).  Merging two states rescales both sums to the larger
+// maximum; an empty state is (-inf, 0).
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;
+  s = s * expf(m - M) + s2 * expf(m2 - M);
+  m = M;
+}
+__device__ __forceinline__ uint64_t lse_pack(float m, float s) {
+  return static_cast<uint64_t>(__float_as_uint(m)) |
+         (static_cast<uint64_t>(__float_as_uint(s)) << 32);
+}
+__device__ __forceinline__ void lse_unpack(uint64_t v, float& m, float& s) {
+  m = __uint_as_float(static_cast<uint32_t>(v));
+  s = __uint_as_float(static_cast<uint32_t>(v >> 32));
+}
+
 __device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, uint4 (&W)[20]) {
   const int w = blockIdx.x, wave = wid(), lane = otid() & 63;
   const int r = lane & 15, g = lane >> 4;
@@ -1320,6 +1344,7 @@ __device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, uin
   const bool xv = r + 1 < a.B;
   const uint16_t* xr = s.x + (xv ? r + 1 : 1) * XS;
   uint64_t best = 0;
+  float lm = -INFINITY, ls = 0.f;  // softmax state of this lane's logits
   uint4 W2[20];
   int p = w;
   while (p < npairs) {
@@ -1337,6 +1362,10 @@ __device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, uin
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           best = umax64(best, argmax_key(acc[i], static_cast<uint32_t>(tile * 16 + 4 * g + i)));
+        if (a.conf) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lse_merge(lm, ls, acc[i], 1.f);
+        }
         if (a.logits) {
           uint16_t o[4];
 #pragma unroll
@@ -1364,6 +1393,10 @@ __device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, uin
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           best = umax64(best, argmax_key(acc[i], static_cast<uint32_t>(tile2 * 16 + 4 * g + i)));
+        if (a.conf) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lse_merge(lm, ls, acc[i], 1.f);
+        }
         if (a.logits) {
           uint16_t o[4];
 #pragma unroll
@@ -1382,27 +1415,67 @@ __device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, uin
     best = umax64(best, shfl_xor_u64(best, 16));
     best = umax64(best, shfl_xor_u64(best, 32));
     if (g == 0) s.best[wave >> 2][r] = best;
+    if (a.conf) {
+#pragma unroll
+      for (int o = 16; o < 64; o <<= 1)
+        lse_merge(lm, ls, __shfl_xor(lm, o, 64), __shfl_xor(ls, o, 64));
+      if (g == 0) s.lse[wave >> 2][r] = make_float2(lm, ls);
+    }
   }
   lds_sync();
-  if (otid() < MAXB)
+  if (otid() < MAXB) {
     st_coh64(a.keys + static_cast<size_t>(w) * MAXB + otid(),
              umax64(s.best[0][otid()], s.best[1][otid()]));
+    if (a.conf) {
+      float m = s.lse[0][otid()].x, sm = s.lse[0][otid()].y;
+      lse_merge(m, sm, s.lse[1][otid()].x, s.lse[1][otid()].y);
+      st_coh64(a.lse + static_cast<size_t>(w) * MAXB + otid(), lse_pack(m, sm));
+    }
+  }
   wait_stores();
 }
 
-__device__ __forceinline__ void argmax_final(const PassArgs& a) {
+__device__ __forceinline__ void argmax_final(const PassArgs& a, Smem& s) {
   if (blockIdx.x != 0) return;
   const int wave = wid(), lane = otid() & 63;
-  if (wave + 1 >= a.B) return;  // wave b reduces mask row b + 1
-  uint64_t best = 0;
-  for (int i = lane; i < static_cast<int>(gridDim.x); i += 64)
-    best = umax64(best, ld_coh64(a.keys + static_cast<size_t>(i) * MAXB + wave));
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) best = umax64(best, shfl_xor_u64(best, o));
   // a grid barrier that gave up waiting leaves the pass's results undefined:
   // report it through the candidates
   const bool timed_out = ld_coh32(a.bar + BAR_STATUS) != 0u;
-  if (lane == 0) a.cand[wave] = timed_out ? -1 : static_cast<int32_t>(~static_cast<uint32_t>(best));
+  if (wave + 1 < a.B) {  // wave b reduces mask row b + 1
+    uint64_t best = 0;
+    for (int i = lane; i < static_cast<int>(gridDim.x); i += 64)
+      best = umax64(best, ld_coh64(a.keys + static_cast<size_t>(i) * MAXB + wave));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) best = umax64(best, shfl_xor_u64(best, o));
+    if (lane == 0) a.cand[wave] = timed_out ? -1 : static_cast<int32_t>(~static_cast<uint32_t>(best));
+    if (a.conf) {
+      // p(cand) = exp(l_max - logsumexp(l)) = 1 / sum_v exp(l_v - l_max):
+      // the state's maximum is the candidate's own logit
+      float m = -INFINITY, sm = 0.f;
+      for (int i = lane; i < static_cast<int>(gridDim.x); i += 64) {
+        float m2, s2;
+        lse_unpack(ld_coh64(a.lse + static_cast<size_t>(i) * MAXB + wave), m2, s2);
+        lse_merge(m, sm, m2, s2);
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1)
+        lse_merge(m, sm, __shfl_xor(m, o, 64), __shfl_xor(sm, o, 64));
+      const float c = timed_out ? __uint_as_float(0x7fc00000u) : 1.f / sm;
+      if (lane == 0) {
+        a.conf[wave] = c;
+        s.cf[wave] = c;
+      }
+    }
+  }
+  if (a.nkeep) {
+    // confidence gate: candidates are kept up to the first one below min_p
+    lds_sync();
+    if (otid() == 0) {
+      int n = 0;
+      while (n + 1 < a.B && s.cf[n] >= a.min_p) ++n;
+      *a.nkeep = timed_out ? 0 : n;
+    }
+  }
 }
 
 template <int FMT>
@@ -1451,7 +1524,7 @@ __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
   if (a.B > 1) {
     lm_phase(a, s, np, Wl);
     grid_sync(a, bk);
-    argmax_final(a);
+    argmax_final(a, s);
   } else if (blockIdx.x == 0 && a.hidden) {
     build_x_norm<W_BF16>(a, s, 2 * L, np, a.final_norm);
     for (int e = otid(); e < H; e += NTHR) a.hidden[e] = s.x[e];
@@ -1551,6 +1624,10 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
   a.o16 = q.o16;
   a.u16 = q.u16;
   a.keys = q.keys;
+  a.lse = q.lse;
+  a.conf = q.conf;
+  a.nkeep = q.nkeep;
+  a.min_p = q.min_p;
   a.bar = q.bar;
   a.spin_limit = q.spin_limit;
   a.cand = q.cand;

@@ -147,6 +147,24 @@ class Drafter:
                            self.ws.data_ptr(), self.ws_bytes, stream_ptr())
         return cand
 
+    def draft_gated(self, p: int, anchor: int, block: int, min_p: float,
+                    mask_id: int = synth.MASK_ID, cand: torch.Tensor | None = None,
+                    conf: torch.Tensor | None = None, n_keep: torch.Tensor | None = None):
+        """draft() plus each candidate's softmax probability and the number of
+        leading candidates at or above the floor min_p; returns
+        (cand, conf, n_keep) device tensors."""
+        if cand is None:
+            cand = torch.empty(block - 1, dtype=torch.int32, device=self.device)
+        if conf is None:
+            conf = torch.empty(block - 1, dtype=torch.float32, device=self.device)
+        if n_keep is None:
+            n_keep = torch.empty(1, dtype=torch.int32, device=self.device)
+        _lib.dflash_draft_block_gated(self.w.desc, self.kv.desc, p, anchor, mask_id, block,
+                                      min_p, cand.data_ptr(), conf.data_ptr(),
+                                      n_keep.data_ptr(), self.ws.data_ptr(), self.ws_bytes,
+                                      stream_ptr())
+        return cand, conf, n_keep
+
     def lm_head_argmax(self, hidden: torch.Tensor, cand: torch.Tensor,
                        logits: torch.Tensor | None = None) -> torch.Tensor:
         _lib.dflash_lm_head_argmax(self.w.desc, hidden.data_ptr(), hidden.shape[0],

@@ -22,6 +22,9 @@ def main(argv=None) -> int:
     ap.add_argument("--block", type=int, default=8)
     ap.add_argument("--ctx", type=int, default=8192)
     ap.add_argument("--fmt", default="bf16", choices=["bf16", "q8_0", "q4_0"])
+    ap.add_argument("--gated", type=float, default=None, metavar="MIN_P",
+                    help="draft with the confidence gate at this floor "
+                         "(dflash_draft_block_gated)")
     ap.add_argument("--copy-mib", type=int, default=0)
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--fuse-rows", type=int, default=0,
@@ -77,10 +80,17 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     print(f"context 0..{args.ctx - 1} committed ({args.fmt})", flush=True)
     cand = torch.empty(8, dtype=torch.int32, device="cuda")
+    conf = torch.empty(8, dtype=torch.float32, device="cuda")
+    keep = torch.empty(1, dtype=torch.int32, device="cuda")
     for i in range(args.passes):
-        dr.draft(args.ctx, 11, args.block, cand=cand)
+        if args.gated is None:
+            dr.draft(args.ctx, 11, args.block, cand=cand)
+        else:
+            dr.draft_gated(args.ctx, 11, args.block, args.gated, cand=cand[:args.block - 1],
+                           conf=conf[:args.block - 1], n_keep=keep)
     torch.cuda.synchronize()
-    print(f"{args.passes} draft passes done, block {args.block}", flush=True)
+    gate = "" if args.gated is None else f", gated at min_p {args.gated}"
+    print(f"{args.passes} draft passes done, block {args.block}{gate}", flush=True)
     return 0
 
 

@@ -209,6 +209,28 @@ int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* kv, int64_t
                            int32_t* cand, void* logits_opt, void* hidden_opt,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* One proposal pass with a confidence gate (PR #3322 "support the official
+ * Flash-Next DFlash2 checkpoint", section "Long-prompt diagnosis and fix": the
+ * spec-min-p probability floor, default 0.5, cut verify rows 133 -> 113; its
+ * later snapshot's 256K run uses spec_min_p=0.7).  Reading: a candidate's
+ * probability is its softmax probability under the drafter's logits.  Same
+ * pass, inputs and cand as dflash_draft_block; in the same vocabulary sweep
+ * the LM head also keeps each mask row's softmax normaliser, so that
+ *   conf  : fp32 [block-1]  conf[i] = softmax(logits_i)[cand[i]]
+ *                           = exp(l_max - logsumexp(logits_i)) = 1 / sum_v exp(l_v - l_max),
+ *                           on the fp32 logits the argmax is decided on
+ *   n_keep: int32 device word = number of leading candidates with
+ *           conf >= min_p (the proposal is cut at the first one below it;
+ *           min_p = 0 keeps all block-1)
+ * block in [2, 8]; min_p in [0, 1] (else DFLASH_EINVAL); cand, conf, n_keep
+ * non-null and 4-byte aligned.  No logits / hidden outputs.  No extra weight
+ * traffic.  A pass whose barriers gave up waiting sets cand to -1, conf to
+ * NaN and n_keep to 0. */
+int32_t dflash_draft_block_gated(const dflash_weights* w, const dflash_kv* kv, int64_t p,
+                                 int32_t anchor_id, int32_t mask_id, int32_t block,
+                                 float min_p, int32_t* cand, float* conf, int32_t* n_keep,
+                                 void* ws, size_t ws_bytes, void* stream);
+
 /* Greedy argmax through the shared LM head ("Drafter runtime": target LM head
  * reused directly; greedy proposal path) for final-normed hidden rows:
  *   hidden    : bf16 [rows][2560]  final-normed hidden states

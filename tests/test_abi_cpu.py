@@ -146,6 +146,16 @@ def test_null_and_bad_arguments(lib):
     assert _lib.dflash_draft_block(w, kv, 5, 1, 2, 8, None, None, None, A, big,
                                    check=False) == E
     assert _lib.dflash_project_ctx_kv(w, A, 4, -5, kv, A, big, check=False) == E
+    G = _lib.dflash_draft_block_gated
+    for block in (0, 1, 9):  # the gate needs at least one candidate
+        assert G(w, kv, 100, 1, 2, block, 0.5, A, A, A, A, big, check=False) == E
+    for min_p in (-0.1, 1.5, float("nan")):
+        assert G(w, kv, 100, 1, 2, 8, min_p, A, A, A, A, big, check=False) == E
+    assert G(w, kv, 100, 1, 2, 8, 0.5, A, None, A, A, big, check=False) == E
+    assert G(w, kv, 100, 1, 2, 8, 0.5, A, A, None, A, big, check=False) == E
+    assert G(w, kv, 100, 1, 2, 8, 0.5, None, A, A, A, big, check=False) == E
+    assert G(w, kv, 100, 1, 2, 8, 0.5, A, A + 2, A, A, big, check=False) == E
+    assert G(w, kv, 100, -1, 2, 8, 0.5, A, A, A, A, big, check=False) == E
     assert _lib.dflash_lm_head_argmax(w, A, 0, A, None, A, big, check=False) == E
     assert _lib.dflash_lm_head_argmax(w, A, 9, A, None, A, big, check=False) == E
     assert _lib.dflash_lm_head_argmax(w, None, 3, A, None, A, big, check=False) == E
