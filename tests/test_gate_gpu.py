@@ -73,6 +73,25 @@ def floors_from(conf_ref, bar):
 @pytest.mark.parametrize("n,block,cap,window", [(0, 2, 256, 256), (40, 5, 1024, 1024),
                                                 (1500, 8, 1024, 512), (300, 8, 32768, 32768)])
 def test_gated_pass_matches_oracle(dev_w, ow, n, block, cap, window):
+    gate_case(dev_w, ow, n, block, cap, window)
+
+
+def test_gated_pass_with_peaked_distributions(host_w, ow):
+    """Synthetic weights give nearly flat next-token distributions (conf near
+    3e-4).  Scaling the final-norm gain by 6 on both sides scales every logit
+    by 6, so the candidates' probabilities spread over orders of magnitude
+    and floors between them cut the proposal part-way."""
+    g = (host_w["final_norm"].astype(np.uint32) << 16).view(np.float32)
+    hw = dict(host_w)
+    hw["final_norm"] = synth.bf16_bits_from_f32(g * 6.0)
+    ow2 = dict(ow)  # shares the decoded-matrix cache; the gain is decoded per call
+    ow2["final_norm"] = hw["final_norm"]
+    dw = DeviceWeights(hw)
+    keeps = gate_case(dw, ow2, 40, 8, 1024, 1024)
+    say(f"[gate peaked] n_keep over the floors: {sorted(set(keeps))}")
+
+
+def gate_case(dev_w, ow, n, block, cap, window):
     p = n
     say(f"[gate] n={n} block={block} cap={cap} window={window}")
     g = O.geometry(window=window)
@@ -101,6 +120,7 @@ def test_gated_pass_matches_oracle(dev_w, ow, n, block, cap, window):
     floors = floors_from(ref["conf"], bar)
     say(f"[gate] max logit err {dl:.3e}, conf bar (log) {bar:.3e}, "
         f"oracle conf {np.array2string(ref['conf'], precision=4)}")
+    keeps = []
     for f in floors:
         cand, conf, nk = dr.draft_gated(p, anchor, block, float(f))
         torch.cuda.synchronize()
@@ -115,7 +135,9 @@ def test_gated_pass_matches_oracle(dev_w, ow, n, block, cap, window):
         assert err.max() <= bar, (f, cf, ref["conf"], err, bar)
         assert k == O.gate_candidates(cf, f), (f, cf, k)
         assert k == O.gate_candidates(ref["conf"], f), (f, cf, ref["conf"], k)
+        keeps.append(k)
     say(f"[gate] {len(floors)} floors checked, gpu conf {np.array2string(cf, precision=4)}")
+    return keeps
 
 
 def test_gated_pass_at_full_context_size(dev_w):
