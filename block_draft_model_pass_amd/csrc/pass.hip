@@ -1321,6 +1321,16 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   s = s * expf(m - M) + s2 * expf(m2 - M);
   m = M;
 }
+// Adds one logit v to a state with a single exponential: the smaller of v
+// and m is scaled by exp(-|v - m|), on the hardware exp2 (exp(x) =
+// 2^(x log2 e); -inf -> 0, so the empty state takes its first value exactly).
+__device__ __forceinline__ void lse_add(float& m, float& s, float v) {
+  const float d = v - m;
+  const float e = __builtin_amdgcn_exp2f(-fabsf(d) * 1.4426950408889634f);
+  const bool up = d > 0.f;
+  s = up ? fmaf(s, e, 1.f) : s + e;
+  m = up ? v : m;
+}
 __device__ __forceinline__ uint64_t lse_pack(float m, float s) {
   return static_cast<uint64_t>(__float_as_uint(m)) |
          (static_cast<uint64_t>(__float_as_uint(s)) << 32);
@@ -1364,7 +1374,7 @@ __device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, uin
           best = umax64(best, argmax_key(acc[i], static_cast<uint32_t>(tile * 16 + 4 * g + i)));
         if (a.conf) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) lse_merge(lm, ls, acc[i], 1.f);
+          for (int i = 0; i < 4; ++i) lse_add(lm, ls, acc[i]);
         }
         if (a.logits) {
           uint16_t o[4];
@@ -1395,7 +1405,7 @@ __device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, uin
           best = umax64(best, argmax_key(acc[i], static_cast<uint32_t>(tile2 * 16 + 4 * g + i)));
         if (a.conf) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) lse_merge(lm, ls, acc[i], 1.f);
+          for (int i = 0; i < 4; ++i) lse_add(lm, ls, acc[i]);
         }
         if (a.logits) {
           uint16_t o[4];
