@@ -487,6 +487,166 @@ def test_block_attention_is_non_causal():
     assert not np.allclose(r["hidden"][1], base["hidden"][1])
 
 
+# ------------------------------------------------------------ q/k path
+# Pins in which a score depends on the query's norm, gain and position and on
+# the block keys' rotation (PR #1426 "Drafter runtime": per-head q/k RMSNorm
+# before full-head NeoX RoPE at each row's own position p + i; "Correctness
+# debugging and fixes": rows must not share the anchor's position; "Parity
+# validation": the "q normed" stage).  TINY has head_dim 4, so the pair
+# (0, 2) turns at frequency theta^0 = 1: a vector (c, 0, 0, 0) at position m
+# becomes (c cos m, 0, c sin m, 0).
+
+def _rms1(v, gain0, dim=4):
+    """RMSNorm of a head vector (v, 0, ..., 0) over `dim` entries, entry 0
+    only: v / sqrt(v^2 / dim + eps) * gain0 (closed form of the norm)."""
+    return v / math.sqrt(v * v / dim + 1e-6) * gain0
+
+
+def _x0(e, H=8):
+    """Input RMSNorm (unit gains) of a constant row of value e: every entry
+    is e / sqrt(e^2 + eps)."""
+    return e / math.sqrt(e * e + 1e-6)
+
+
+def test_query_norm_gain_and_row_position_against_one_context_key():
+    """One visible context cell with key kappa (cos phi, 0, sin phi, 0) and
+    value Vc; block keys and values are zero (Wk = Wv = 0).  Query head h is
+    (a_h x_0, 0, 0, 0) before its norm, so after the norm (gain g0 = 1.5) and
+    RoPE at p + i its score against the context key is
+    scale * q0_h * kappa * cos(p + i - phi) with q0_h the closed-form norm.
+    The block's three zero keys add e^0 each to the softmax denominator, so
+    the head output is w Vc with w = e^s / (e^s + 3).  Wo copies head 1
+    (group 0) into h[0:4] and head 2 (group 1) into h[4:8]."""
+    H, D, B, p, phi = 8, 4, 3, 1, 0.7
+    a = [0.5, -0.75, 1.25, 2.0]
+    wq = np.zeros((16, H), dtype=np.float32)
+    for h in range(4):
+        wq[h * D, 0] = a[h]
+    wo = np.zeros((H, 16), dtype=np.float32)
+    for i in range(4):
+        wo[i, 1 * D + i] = 1.0
+        wo[4 + i, 2 * D + i] = 1.0
+    qn = np.ones(4, dtype=np.float32)
+    qn[0] = 1.5
+    fill = {"embed": _const_embed({1: 1.0, 10: 2.0}), "layers.0.wq": wq,
+            "layers.0.wk": np.zeros((8, H)), "layers.0.wv": np.zeros((8, H)),
+            "layers.0.q_norm": qn, "layers.0.wo": wo, "layers.0.wd": np.zeros((H, 6)),
+            "layers.1.wo": np.zeros((H, 16)), "layers.1.wd": np.zeros((H, 6))}
+    w = tiny_weights(fill, seed=21)
+    kappa = [8.0, -6.0]
+    Vc = np.array([[1.0, -2.0, 3.0, 0.5], [-1.0, 0.25, 2.0, 4.0]])
+    ck = np.zeros((2, 2, 1, D))
+    cv = np.zeros((2, 2, 1, D))
+    for j in range(2):
+        ck[0, j, 0] = [kappa[j] * math.cos(phi), 0.0, kappa[j] * math.sin(phi), 0.0]
+        cv[0, j, 0] = Vc[j]
+    r = O.draft_block(w, ck, cv, p=p, anchor_id=1, mask_id=10, block=B, g=TINY)
+    for i, e in enumerate((1.0, 2.0, 2.0)):
+        m = p + i
+        want = [e] * H
+        for head, j, off in ((1, 0, 0), (2, 1, 4)):
+            q0 = _rms1(a[head] * _x0(e), 1.5)
+            s = (1.0 / 16.0) * q0 * kappa[j] * math.cos(m - phi)
+            wgt = math.exp(s) / (math.exp(s) + B)
+            for d in range(D):
+                want[off + d] += wgt * Vc[j, d]
+        assert np.allclose(r["x_last"][i], want, rtol=1e-9, atol=1e-12), (i, r["x_last"][i], want)
+
+
+def test_block_keys_rotate_at_their_own_positions():
+    """No visible context keys carry weight (four zero cells: score 0, value
+    0); queries and keys of all three block rows are (c, 0, 0, 0) before
+    their norms (gains 4 and 3), so q = 8 (cos m_i, 0, sin m_i, 0) and the
+    stored fp16 key of row r is (k cos m_r, 0, k sin m_r, 0) rounded to fp16,
+    k = 6.  Values are +c_j (anchor) and -c_j (mask rows: their embedding
+    alternates sign and Wv reads entry 1).  The output of row i is
+    sum_r w_ir v_r with w_ir = e^(s_ir) / (sum_r' e^(s_ir') + 4) and
+    s_ir = (1/16) q_i . k_r: the block keys enter at their own positions
+    p + r, so the scores depend on m_i - m_r only up to the fp16 rounding."""
+    H, D, B, p = 8, 4, 3, 5
+    E = np.zeros((11, H), dtype=np.float32)
+    E[1] = 1.0
+    E[10] = [1.0, -1.0] * 4
+    wq = np.zeros((16, H), dtype=np.float32)
+    for h in range(4):
+        wq[h * D, 0] = 1.0
+    wk = np.zeros((8, H), dtype=np.float32)
+    wk[0, 0] = wk[D, 0] = 1.0
+    cvals = np.array([[1.0, 2.0, -1.0, 0.5], [0.25, -3.0, 1.5, 2.0]])
+    wv = np.zeros((8, H), dtype=np.float32)
+    for j in range(2):
+        wv[j * D:(j + 1) * D, 1] = cvals[j]
+    wo = np.zeros((H, 16), dtype=np.float32)
+    for i in range(4):
+        wo[i, 0 * D + i] = 1.0        # head 0 (group 0) -> h[0:4]
+        wo[4 + i, 3 * D + i] = 1.0    # head 3 (group 1) -> h[4:8]
+    qn = np.array([4.0, 1, 1, 1], dtype=np.float32)
+    kn = np.array([3.0, 1, 1, 1], dtype=np.float32)
+    fill = {"embed": E, "layers.0.wq": wq, "layers.0.wk": wk, "layers.0.wv": wv,
+            "layers.0.q_norm": qn, "layers.0.k_norm": kn, "layers.0.wo": wo,
+            "layers.0.wd": np.zeros((H, 6)), "layers.1.wo": np.zeros((H, 16)),
+            "layers.1.wd": np.zeros((H, 6))}
+    w = tiny_weights(fill, seed=22)
+    z = np.zeros((2, 2, 4, D))
+    r = O.draft_block(w, z, z, p=p, anchor_id=1, mask_id=10, block=B, g=TINY)
+    x0 = _x0(1.0)                       # |entries| of both rows after the norm
+    q0, k0 = _rms1(x0, 4.0), _rms1(x0, 3.0)
+    f16 = lambda v: float(np.float16(v))
+    keys = [(f16(k0 * math.cos(p + rr)), f16(k0 * math.sin(p + rr))) for rr in range(B)]
+    sign = [1.0, -1.0, -1.0]            # entry 1 of the anchor / mask rows
+    for i, e_row in enumerate((E[1], E[10], E[10])):
+        m = p + i
+        s = [(1.0 / 16.0) * q0 * (math.cos(m) * kc + math.sin(m) * ks) for kc, ks in keys]
+        den = sum(math.exp(v) for v in s) + 4.0
+        want = e_row.astype(np.float64).copy()
+        for j, off in ((0, 0), (1, 4)):
+            for d in range(D):
+                want[off + d] += sum(math.exp(s[rr]) / den * f16(sign[rr] * x0 * cvals[j, d])
+                                     for rr in range(B))
+        assert np.allclose(r["x_last"][i], want, rtol=1e-9, atol=1e-12), (i, r["x_last"][i], want)
+
+
+def test_query_and_key_norms_remove_projection_scale():
+    """The per-head q/k RMSNorm makes the pass independent of the scale of
+    Wq and Wk (up to eps): multiplying every layer's Wq by 4 and Wk by 1/4
+    (exact in bf16) leaves the outputs unchanged to within the eps term and
+    one fp16 rounding of a block key; dropping either norm would scale the
+    scores by 4."""
+    base = _tiny_random_pass()
+    w = tiny_weights(seed=11)
+    for l in range(2):
+        for name, f in (("wq", 4.0), ("wk", 0.25)):
+            v = O.bf16_decode(w[f"layers.{l}.{name}"]) * f
+            w[f"layers.{l}.{name}"] = b16(v.astype(np.float32))
+    rng = np.random.default_rng(12)
+    Kc = O.f16_round(rng.standard_normal((2, 2, 3, 4)))
+    Vc = O.f16_round(rng.standard_normal((2, 2, 3, 4)))
+    r = O.draft_block(w, Kc, Vc, p=3, anchor_id=2, mask_id=10, block=5, g=TINY)
+    scale = np.abs(base["x_last"]).max()
+    assert np.abs(r["x_last"] - base["x_last"]).max() <= 2e-3 * scale
+    assert np.abs(r["logits"] - base["logits"]).max() <= 2e-3 * np.abs(base["logits"]).max()
+
+
+def test_mask_rows_with_distinct_tokens_permute_with_their_positions():
+    """Mask rows carrying distinct tokens (so distinct queries, keys and
+    values): permuting the (token, position) pairs among the mask rows
+    permutes the outputs exactly, and swapping only the positions of two
+    distinct rows changes both of them (the queries are roped at the row's
+    own position, not the anchor's)."""
+    toks = [2, 3, 5, 7, 9]
+    pos = [3, 4, 5, 6, 7]
+    base = _tiny_random_pass(row_tokens=toks, row_positions=pos)
+    sigma = [3, 1, 4, 2]
+    r = _tiny_random_pass(row_tokens=[toks[0]] + [toks[s] for s in sigma],
+                          row_positions=[pos[0]] + [pos[s] for s in sigma])
+    assert np.array_equal(r["hidden"][0], base["hidden"][0])
+    for i, s in enumerate(sigma, start=1):
+        assert np.array_equal(r["hidden"][i], base["hidden"][s])
+    sw = _tiny_random_pass(row_tokens=toks, row_positions=[3, 5, 4, 6, 7])
+    assert not np.allclose(sw["hidden"][1], base["hidden"][1])
+    assert not np.allclose(sw["hidden"][2], base["hidden"][2])
+
+
 # ------------------------------------------------------------ confidence gate
 
 def test_confidence_uniform_logits_is_one_over_vocab():
