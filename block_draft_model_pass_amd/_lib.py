@@ -16,6 +16,7 @@ DFLASH_ERANGE = -3
 DFLASH_EWORKSPACE = -4
 DFLASH_EHIP = -5
 DFLASH_ENONFINITE = -6
+DFLASH_ETIMEOUT = -7
 
 DFLASH_W_BF16 = 0
 DFLASH_W_Q8_0 = 1
@@ -97,6 +98,11 @@ def load() -> ctypes.CDLL:
     lib.dflash_lm_head_argmax.restype = c_int32
     lib.dflash_verify_greedy.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_void_p]
     lib.dflash_verify_greedy.restype = c_int32
+    lib.dflash_verify_greedy_gated.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                               c_void_p]
+    lib.dflash_verify_greedy_gated.restype = c_int32
+    lib.dflash_draft_status.argtypes = [c_void_p, c_size_t, c_void_p, c_void_p]
+    lib.dflash_draft_status.restype = c_int32
     lib.dflash_check_finite.argtypes = [c_void_p, c_int64, c_int32, c_void_p, c_void_p]
     lib.dflash_check_finite.restype = c_int32
     lib.dflash_strerror.argtypes = [c_int32]
@@ -171,3 +177,14 @@ def dflash_verify_greedy(cand, target, k, out, stream=None, check=True):
 def dflash_check_finite(x, count, dtype, status, stream=None, check=True):
     rc = load().dflash_check_finite(x, count, dtype, status, stream)
     return _check(rc, "dflash_check_finite") if check else rc
+
+
+def dflash_verify_greedy_gated(cand, target, k_max, n_keep, out, stream=None, check=True):
+    rc = load().dflash_verify_greedy_gated(cand, target, k_max, n_keep, out, stream)
+    return _check(rc, "dflash_verify_greedy_gated") if check else rc
+
+
+def dflash_draft_status(ws, ws_bytes, status, stream=None, check=True):
+    rc = load().dflash_draft_status(ws, ws_bytes, status, stream)
+    return _check(rc, "dflash_draft_status") if check else rc
+

@@ -19,6 +19,8 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 VALU forms stay off (scalar fp32 code only)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # only the C ABI (DFLASH_API in dflash.h) is exported
+    "-fvisibility=hidden", "-fvisibility-inlines-hidden",
     "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
 ]
 SOURCES = ["api.hip", "gemv.hip", "norm.hip", "gemm.hip", "pass.hip", "pack.hip", "check.hip"]
@@ -40,7 +42,8 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs,
+           f"-Wl,--version-script={os.path.join(CSRC, 'exports.map')}", "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

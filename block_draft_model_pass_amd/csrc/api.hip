@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+
 using namespace dfl;
 
 namespace {
@@ -14,15 +15,31 @@ namespace {
 constexpr int NCH_TARGET = 64;        // chunks per KV head aimed for
 constexpr int LMH_GRID = 256;         // standalone LM-head kernel: one block per CU
 constexpr int KEYS_MAX = 1024;        // argmax key slots (blocks of either LM-head launch)
-constexpr unsigned SPIN_LIMIT = 1u << 24;  // grid-barrier wait bound (~0.5 s)
+constexpr long BARRIER_WAIT_US = 500000;   // grid-barrier wait bound (0.5 s of wall clock)
+constexpr long BARRIER_WAIT_US_MAX = 10000000;
 
-// The barrier wait bound in polls: SPIN_LIMIT, or DFLASH_SPIN_LIMIT from the
-// environment (read on every call) so that tests can drive the timeout path.
-unsigned spin_limit() {
-  const char* e = getenv("DFLASH_SPIN_LIMIT");
-  if (!e || !*e) return SPIN_LIMIT;
-  const unsigned long v = strtoul(e, nullptr, 10);
-  return v >= 1 && v <= SPIN_LIMIT ? static_cast<unsigned>(v) : SPIN_LIMIT;
+// The barrier wait bound in microseconds: BARRIER_WAIT_US, or
+// DFLASH_BARRIER_TIMEOUT_US from the environment (read on every call, 0 ..
+// 10^7) so that tests can drive the give-up path.
+long barrier_wait_us() {
+  const char* e = getenv("DFLASH_BARRIER_TIMEOUT_US");
+  if (!e || !*e) return BARRIER_WAIT_US;
+  char* end = nullptr;
+  const long v = strtol(e, &end, 10);
+  return end && *end == 0 && v >= 0 && v <= BARRIER_WAIT_US_MAX ? v : BARRIER_WAIT_US;
+}
+
+// Constant-clock ticks per microsecond per device (a hardware property).
+double ticks_per_us() {
+  static double cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0.0;
+  if (cache[dev] == 0.0) {
+    double t = 0.0;
+    if (wall_clock_ticks_per_us(dev, &t) != hipSuccess) return 0.0;
+    cache[dev] = t;
+  }
+  return cache[dev];
 }
 
 // Co-resident grid of the pass kernel per device (a hardware property).
@@ -101,7 +118,10 @@ T* at(void* ws, size_t off) {
 // Device buffers are read and written with 16-byte vector accesses.
 bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_weights(const dflash_weights* w) {
+// Row-major matrices (fc, the 35 layer matrices, the LM head) may be null
+// once w->packed holds their streaming copies: every call then reads those.
+// Packing itself (need_rowmajor) reads the row-major tensors.
+int check_weights(const dflash_weights* w, bool need_rowmajor = false) {
   if (!w) return DFLASH_EINVAL;
   if (w->hidden != H || w->n_layers != L || w->n_q_heads != NQ || w->n_kv_heads != NKV ||
       w->head_dim != D || w->ffn != F || w->n_taps != T)
@@ -112,17 +132,20 @@ int check_weights(const dflash_weights* w) {
   if (w->backbone_type != DFLASH_W_BF16 && w->backbone_type != DFLASH_W_Q8_0 &&
       w->backbone_type != DFLASH_W_Q4_0)
     return DFLASH_EINVAL;
-  if (!w->fc || !w->hidden_norm || !w->final_norm || !w->embed || !w->lm_head)
+  const bool rm = need_rowmajor || !w->packed;  // row-major matrices required
+  if (!w->hidden_norm || !w->final_norm || !w->embed || (rm && (!w->fc || !w->lm_head)))
     return DFLASH_EINVAL;
   if (!a16(w->fc) || !a16(w->hidden_norm) || !a16(w->final_norm) || !a16(w->embed) ||
       !a16(w->lm_head) || !a16(w->packed))
     return DFLASH_EINVAL;
   for (int l = 0; l < L; ++l) {
     const dflash_layer_weights& y = w->layer[l];
-    const void* t[11] = {y.in_norm, y.wq, y.wk, y.wv, y.q_norm, y.k_norm,
-                         y.wo,      y.post_norm, y.wg, y.wu, y.wd};
-    for (const void* p : t)
+    const void* gains[4] = {y.in_norm, y.q_norm, y.k_norm, y.post_norm};
+    const void* mats[7] = {y.wq, y.wk, y.wv, y.wo, y.wg, y.wu, y.wd};
+    for (const void* p : gains)
       if (!p || !a16(p)) return DFLASH_EINVAL;
+    for (const void* p : mats)
+      if ((rm && !p) || !a16(p)) return DFLASH_EINVAL;
   }
   return DFLASH_OK;
 }
@@ -251,7 +274,7 @@ extern "C" size_t dflash_packed_size(const dflash_weights* w) {
 }
 
 extern "C" int32_t dflash_pack_weights(const dflash_weights* w, void* stream) {
-  int rc = check_weights(w);
+  int rc = check_weights(w, true);
   if (rc) return rc;
   if (!w->packed) return DFLASH_EINVAL;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -309,7 +332,8 @@ extern "C" int32_t dflash_fuse_context(const dflash_weights* w, const void* taps
     SegTable wt = seg1(wp ? packed_fc(w) : w->fc, H);
     if (fmt != W_BF16) {
       uint16_t* dq = at<uint16_t>(ws, Lw.y + rows_bytes(n, fmt) - 2 * DQ_ELEMS);
-      HIP_TRY(launch_dequant_bf16(w->fc, fmt, H, T * H, dq, 0, st));
+      const bool pk = w->packed != nullptr;
+      HIP_TRY(launch_dequant_bf16(pk ? packed_fc(w) : w->fc, fmt, H, T * H, dq, 0, pk, st));
       wt = seg1(dq, H);
       wp = true;
     }
@@ -377,8 +401,8 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
   } else {
     float* y = at<float>(ws, Lw.y);
     SegTable wt = seg_kv(w);
-    bool wp = fmt == W_BF16 && w->packed;
-    if (wp) {  // the layers' packed Wk / Wv
+    bool wp = w->packed != nullptr;
+    if (wp) {  // the layers' packed Wk / Wv (bf16, or quantized blocks decoded below)
       for (int l = 0; l < L; ++l) {
         uint8_t* pm[7];
         packed_layer(w, l, pm);
@@ -390,7 +414,7 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
       uint16_t* dq = at<uint16_t>(ws, Lw.y + rows_bytes(n, fmt) - 2 * DQ_ELEMS);
       for (int s = 0; s < wt.nseg; ++s) {
         const int r0 = s ? wt.row_end[s - 1] : 0;
-        HIP_TRY(launch_dequant_bf16(wt.ptr[s], fmt, wt.row_end[s] - r0, H, dq, r0, st));
+        HIP_TRY(launch_dequant_bf16(wt.ptr[s], fmt, wt.row_end[s] - r0, H, dq, r0, wp, st));
       }
       wt = seg1(dq, KV_N);
       wp = true;
@@ -486,7 +510,9 @@ int32_t draft_block_impl(const dflash_weights* w, const dflash_kv* kv, int64_t p
   q.keys = at<uint64_t>(ws, Lw.keys);
   q.bar = at<unsigned>(ws, Lw.bar);
   q.tab = at<void>(ws, Lw.tab);
-  q.spin_limit = spin_limit();
+  const double tpu = ticks_per_us();
+  if (tpu <= 0.0) return DFLASH_EHIP;
+  q.wait_ticks = static_cast<uint64_t>(static_cast<double>(barrier_wait_us()) * tpu);
   q.grid = grid;
   q.cand = cand;
   q.logits = static_cast<uint16_t*>(logits_opt);
@@ -543,8 +569,31 @@ extern "C" int32_t dflash_verify_greedy(const int32_t* cand, const int32_t* targ
                                         int32_t* out, void* stream) {
   if (k < 0 || k > MAXB - 1) return DFLASH_EINVAL;
   if (!target || !out || (k > 0 && !cand)) return DFLASH_EINVAL;
-  if (launch_verify(cand, target, k, out, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (launch_verify(cand, target, k, nullptr, out, static_cast<hipStream_t>(stream)) != hipSuccess)
     return DFLASH_EHIP;
+  return DFLASH_OK;
+}
+
+extern "C" int32_t dflash_verify_greedy_gated(const int32_t* cand, const int32_t* target,
+                                              int32_t k_max, const int32_t* n_keep, int32_t* out,
+                                              void* stream) {
+  if (k_max < 0 || k_max > MAXB - 1) return DFLASH_EINVAL;
+  if (!target || !out || !n_keep || (k_max > 0 && !cand)) return DFLASH_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(n_keep) & 3u) || (reinterpret_cast<uintptr_t>(out) & 3u) ||
+      (reinterpret_cast<uintptr_t>(target) & 3u) || (reinterpret_cast<uintptr_t>(cand) & 3u))
+    return DFLASH_EINVAL;
+  if (launch_verify(cand, target, k_max, n_keep, out, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DFLASH_EHIP;
+  return DFLASH_OK;
+}
+
+extern "C" int32_t dflash_draft_status(const void* ws, size_t ws_bytes, int32_t* status,
+                                       void* stream) {
+  if (!ws || !status || !a16(ws) || (reinterpret_cast<uintptr_t>(status) & 3u)) return DFLASH_EINVAL;
+  const Layout Lw = layout();
+  if (ws_bytes < Lw.fixed) return DFLASH_EWORKSPACE;
+  HIP_TRY(launch_pass_status(at<const unsigned>(const_cast<void*>(ws), Lw.bar), status,
+                             DFLASH_ETIMEOUT, static_cast<hipStream_t>(stream)));
   return DFLASH_OK;
 }
 
@@ -567,6 +616,7 @@ extern "C" const char* dflash_strerror(int32_t code) {
     case DFLASH_EWORKSPACE: return "workspace too small";
     case DFLASH_EHIP: return "HIP launch failed";
     case DFLASH_ENONFINITE: return "non-finite value found";
+    case DFLASH_ETIMEOUT: return "proposal pass gave up waiting at a grid barrier";
     default: return "unknown error";
   }
 }

@@ -205,8 +205,9 @@ hipError_t launch_pack_units(const void* src, int N, int per_row, int unit, void
 
 // Quantized [rows][K] matrix (fmt Q8_0 / Q4_0) -> rows row0 .. row0+rows-1
 // of a bf16 [.][K] matrix in the streaming layout (rows, row0 multiples of 16).
+// src: row-major blocks, or the matrix's streaming copy when `packed`.
 hipError_t launch_dequant_bf16(const void* src, int fmt, int rows, int K, uint16_t* dst, int row0,
-                               hipStream_t st);
+                               bool packed, hipStream_t st);
 
 // LM head + greedy argmax over the vocabulary.
 // lm: row-major [vocab][2560], or its streaming copy when `packed`.
@@ -280,7 +281,7 @@ struct PassLaunch {
   uint64_t* lse;             // [grid][8] softmax (max, sum) pairs
   unsigned* bar;
   void* tab;                 // workspace room for the per-layer pointer table
-  unsigned spin_limit;
+  uint64_t wait_ticks;       // grid-barrier wait bound in constant-clock ticks
   int grid;
   int32_t* cand;
   uint16_t* logits;
@@ -299,7 +300,14 @@ size_t pass_smem_bytes();
 size_t pass_tab_bytes();
 size_t pass_bar_bytes();
 
-hipError_t launch_verify(const int32_t* cand, const int32_t* target, int k, int32_t* out,
-                         hipStream_t st);
+// Greedy verify of k candidates, or of min(max(*k_dev, 0), k) when k_dev is set.
+hipError_t launch_verify(const int32_t* cand, const int32_t* target, int k, const int32_t* k_dev,
+                         int32_t* out, hipStream_t st);
+// *status = code if the barrier words `bar` of the last pass record a wait
+// that gave up, else 0.
+hipError_t launch_pass_status(const unsigned* bar, int32_t* status, int32_t code, hipStream_t st);
+// Constant-clock ticks per microsecond on `device` (the counter the pass's
+// barrier bound reads).
+hipError_t wall_clock_ticks_per_us(int device, double* ticks);
 
 }  // namespace dfl

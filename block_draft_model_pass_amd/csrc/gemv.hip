@@ -206,35 +206,43 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(GemvArgs a) {
   }
 }
 
-// Quantized matrix -> bf16 copy (value q * scale, rounded once), for the
-// many-row GEMM path, in the streaming layout of a bf16 [row0 + rows][K]
-// matrix (16-row tiles, 32-wide k blocks, MFMA lane order; the 8 elements a
-// thread produces are one lane's contiguous 16 bytes there).  One thread per
-// 8 output elements.
-template <int FMT>
+// Quantized [rows][K] (fmt Q8_0 / Q4_0) -> rows row0.. of a bf16 [.][K]
+// matrix in the streaming layout (the 8 bf16 values of an output group are
+// one lane's contiguous 16 bytes there).  One thread per 8 output elements.
+// The source is either the row-major blocks (quants row-major, then scales
+// row-major) or, with PACKED, the matrix's streaming copy (quants as 64-byte
+// row pieces in MFMA lane order, scales regrouped per 16-row tile and piece).
+template <int FMT, bool PACKED>
 __global__ __launch_bounds__(256) void k_dequant_bf16(const uint8_t* src, int rows, int K,
                                                       uint16_t* dst, int row0) {
   const size_t n8 = static_cast<size_t>(rows) * K / 8;
+  const size_t qbytes = FMT == W_Q8_0 ? static_cast<size_t>(rows) * K : static_cast<size_t>(rows) * K / 2;
   for (size_t e = blockIdx.x * 256ull + threadIdx.x; e < n8; e += static_cast<size_t>(gridDim.x) * 256) {
-    const size_t k0 = e * 8;  // first element (row-major)
-    const size_t blk = k0 / 32;
-    const float s = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(
-        src + (FMT == W_Q8_0 ? static_cast<size_t>(rows) * K : static_cast<size_t>(rows) * K / 2) + 2 * blk));
-    float v[8];
-    if constexpr (FMT == W_Q8_0) {
-      const uint2 q = *reinterpret_cast<const uint2*>(src + k0);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t word = i < 4 ? q.x : q.y;
-        v[i] = static_cast<float>(static_cast<int8_t>(word >> (8 * (i & 3)))) * s;
-      }
+    const size_t r = e * 8 / K, k = e * 8 % K;  // row and first element of the group
+    // byte offset of the group's quants (8 bytes for Q8_0; for Q4_0 the 8
+    // bytes holding its nibbles) and element offset of its block scale
+    size_t qoff, soff;
+    if constexpr (!PACKED) {
+      qoff = FMT == W_Q8_0 ? r * K + k : r * K / 2 + 16 * (k / 32) + (k % 16);
+      soff = r * (K / 32) + k / 32;
     } else {
-      // element j of a block: byte j % 16, low nibble if j < 16 else high
-      const int j0 = static_cast<int>(k0 % 32);
-      const uint8_t* by = src + blk * 16 + (j0 & 15);
+      const size_t kpc = FMT == W_Q8_0 ? 64 : 128;  // k per 64-byte piece
+      const size_t P = K / kpc, pc = (r / 16) * P + k / kpc;
+      const size_t jb = FMT == W_Q8_0 ? k % 64 : 16 * ((k % 128) / 32) + (k % 16);
+      qoff = (pc * 64 + r % 16 + 16 * (jb / 16)) * 16 + jb % 16;
+      soff = (pc * 16 + r % 16) * (FMT == W_Q8_0 ? 2 : 4) + (k % kpc) / 32;
+    }
+    const float s = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(src + qbytes + 2 * soff));
+    const uint2 q = *reinterpret_cast<const uint2*>(src + qoff);
+    float v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int nib = j0 < 16 ? (by[i] & 15) : (by[i] >> 4);
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t word = i < 4 ? q.x : q.y;
+      const uint32_t byte = (word >> (8 * (i & 3))) & 0xffu;
+      if constexpr (FMT == W_Q8_0) {
+        v[i] = static_cast<float>(static_cast<int8_t>(byte)) * s;
+      } else {  // element j of a block: byte j % 16, low nibble if j < 16 else high
+        const int nib = k % 32 < 16 ? static_cast<int>(byte & 15u) : static_cast<int>(byte >> 4);
         v[i] = static_cast<float>(nib - 8) * s;
       }
     }
@@ -242,7 +250,7 @@ __global__ __launch_bounds__(256) void k_dequant_bf16(const uint8_t* src, int ro
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       o[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
-    const size_t n = row0 + k0 / K, k = k0 % K;
+    const size_t n = row0 + r;
     const size_t at = ((n / 16 * (K / 32) + k / 32) * 64 + n % 16 + 16 * ((k % 32) / 8)) * 8;
     *reinterpret_cast<uint4*>(dst + at) = make_uint4(o[0], o[1], o[2], o[3]);
   }
@@ -356,8 +364,12 @@ __global__ __launch_bounds__(MAXB * 64) void k_argmax_reduce(const uint64_t* key
 }
 
 // accepted = longest prefix with cand == target; all loads issued at once.
-__global__ void k_verify(const int32_t* cand, const int32_t* target, int k, int32_t* out) {
+__global__ void k_verify(const int32_t* cand, const int32_t* target, int kmax,
+                         const int32_t* k_dev, int32_t* out) {
   const int lane = threadIdx.x;
+  // k from a device word (the confidence gate's count), clamped to [0, kmax]
+  const int kd = k_dev ? *k_dev : kmax;
+  const int k = kd < 0 ? 0 : (kd > kmax ? kmax : kd);
   const int c = lane < k ? cand[lane] : 0;
   const int t = lane <= k ? target[lane] : 0;
   const bool miss = lane < k && c != t;
@@ -406,16 +418,21 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_dequant_bf16(const void* src, int fmt, int rows, int K, uint16_t* dst, int row0,
-                               hipStream_t st) {
+                               bool packed, hipStream_t st) {
   if (rows < 0 || K % 32 || rows % 16 || row0 % 16 || row0 < 0) return hipErrorInvalidValue;
   if (rows == 0) return hipSuccess;
   const size_t n8 = static_cast<size_t>(rows) * K / 8;
   const int grid = static_cast<int>(n8 / 256 < 4096 ? (n8 + 255) / 256 : 4096);
   const uint8_t* s8 = static_cast<const uint8_t*>(src);
-  if (fmt == W_Q8_0)
-    hipLaunchKernelGGL(k_dequant_bf16<W_Q8_0>, dim3(grid), dim3(256), 0, st, s8, rows, K, dst, row0);
+  if (packed && (K % (fmt == W_Q8_0 ? 64 : 128))) return hipErrorInvalidValue;
+  if (fmt == W_Q8_0 && packed)
+    hipLaunchKernelGGL((k_dequant_bf16<W_Q8_0, true>), dim3(grid), dim3(256), 0, st, s8, rows, K, dst, row0);
+  else if (fmt == W_Q8_0)
+    hipLaunchKernelGGL((k_dequant_bf16<W_Q8_0, false>), dim3(grid), dim3(256), 0, st, s8, rows, K, dst, row0);
+  else if (fmt == W_Q4_0 && packed)
+    hipLaunchKernelGGL((k_dequant_bf16<W_Q4_0, true>), dim3(grid), dim3(256), 0, st, s8, rows, K, dst, row0);
   else if (fmt == W_Q4_0)
-    hipLaunchKernelGGL(k_dequant_bf16<W_Q4_0>, dim3(grid), dim3(256), 0, st, s8, rows, K, dst, row0);
+    hipLaunchKernelGGL((k_dequant_bf16<W_Q4_0, false>), dim3(grid), dim3(256), 0, st, s8, rows, K, dst, row0);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -439,9 +456,9 @@ hipError_t launch_lmhead_argmax(const uint16_t* lm, bool packed, int vocab, cons
   return hipGetLastError();
 }
 
-hipError_t launch_verify(const int32_t* cand, const int32_t* target, int k, int32_t* out,
-                         hipStream_t st) {
-  hipLaunchKernelGGL(k_verify, dim3(1), dim3(64), 0, st, cand, target, k, out);
+hipError_t launch_verify(const int32_t* cand, const int32_t* target, int k, const int32_t* k_dev,
+                         int32_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_verify, dim3(1), dim3(64), 0, st, cand, target, k, k_dev, out);
   return hipGetLastError();
 }
 

@@ -161,7 +161,7 @@ struct PassArgs {
   uint64_t* keys;    // [grid][8]
   uint64_t* lse;     // [grid][8] per-block (max, sum) pairs of the softmax sweep
   unsigned* bar;     // barrier words (BAR_*)
-  unsigned spin_limit;
+  uint64_t wait_ticks;  // barrier wait bound, constant-clock ticks
   // outputs
   int32_t* cand;
   uint16_t* logits;
@@ -254,15 +254,29 @@ __device__ __forceinline__ unsigned ald(unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Barrier state of one block: barriers passed, and (thread 0) whether this
+// pass has given up waiting.
+struct BarState {
+  unsigned k = 0;
+  bool quit = false;
+};
+
 // Grid barrier whose waiting wave (wave 0) issues its share of the next
 // phase's weight loads between its arrival and its polling: its arrival
 // atomics go out ahead of those loads, while its loads still stream during
 // the wait.  (A wave's loads complete in order, so a prefetch issued before
 // the arrival would hold the arrival back by the prefetch's latency.)
+//
+// The wait is bounded in wall-clock time (the constant-rate counter read by
+// s_memrealtime): a wait longer than a.wait_ticks (plus 16 polls) sets the
+// status word and gives up.  A block that gave up, or that finds the status word set (checked
+// every 64 polls), waits at no later barrier of the pass, so a pass whose
+// blocks cannot all be resident ends after about one bound instead of
+// hanging the stream.
 template <class Pf>
-__device__ __forceinline__ void grid_sync_pf(const PassArgs& a, unsigned& k, Pf&& wave0_prefetch) {
+__device__ __forceinline__ void grid_sync_pf(const PassArgs& a, BarState& b, Pf&& wave0_prefetch) {
   lds_sync();
-  ++k;
+  const unsigned k = ++b.k;
   const unsigned goal = k * (gridDim.x < 8 ? gridDim.x : 8);
   bool wait = false;
   const unsigned x = blockIdx.x & 7;  // blocks are dealt to the XCDs round robin
@@ -281,12 +295,25 @@ __device__ __forceinline__ void grid_sync_pf(const PassArgs& a, unsigned& k, Pf&
     }
   }
   if (wid() == 0) wave0_prefetch();
-  if (otid() == 0 && wait) {
+  if (otid() == 0 && wait && !b.quit) {
+    // The clock and the status word are read every 16 and 64 polls only (a
+    // counter read per poll would delay seeing the release); the clock starts
+    // at the 16th poll, so a wait gives up after the bound plus 16 polls.
+    uint64_t t0 = 0;
     unsigned n = 0;
     while (ald(a.bar + BAR_REL + 32 * x) < k) {
       __builtin_amdgcn_s_sleep(2);
-      if (++n > a.spin_limit) {  // bounded: never hang the device
+      if ((++n & 15) != 0) continue;
+      if ((n & 63) == 0 && ald(a.bar + BAR_STATUS) != 0u) {  // another block gave up
+        b.quit = true;
+        break;
+      }
+      const uint64_t now = __builtin_amdgcn_s_memrealtime();
+      if (n == 16) {
+        t0 = now;
+      } else if (now - t0 > a.wait_ticks) {  // bounded: never hang
         __hip_atomic_store(a.bar + BAR_STATUS, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        b.quit = true;
         break;
       }
     }
@@ -294,8 +321,8 @@ __device__ __forceinline__ void grid_sync_pf(const PassArgs& a, unsigned& k, Pf&
   lds_sync();
 }
 
-__device__ __forceinline__ void grid_sync(const PassArgs& a, unsigned& k) {
-  grid_sync_pf(a, k, [] {});
+__device__ __forceinline__ void grid_sync(const PassArgs& a, BarState& b) {
+  grid_sync_pf(a, b, [] {});
 }
 
 // ---------------------------------------------------------------- GEMV pieces
@@ -1492,7 +1519,7 @@ template <int FMT>
 __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
   __shared__ Smem s;
   const bool pre = wid() != 0;  // waves other than 0 prefetch before barriers
-  unsigned bk = 0;  // barriers passed
+  BarState bk;      // barriers passed, give-up flag
   QkvTile<FMT> Wq;
   uint4 Wl[20];     // LM head (bf16) slice, prefetched after the last layer
   // Layer 0 QKV weights stream while the grid lines up.
@@ -1582,6 +1609,10 @@ __global__ __launch_bounds__(256) void k_pass_init(LayerTab tab, LayerTab* tab_o
   if (threadIdx.x == 0) ss[b] = sq;
 }
 
+__global__ void k_pass_status(const unsigned* bar, int32_t* status, int32_t code) {
+  if (threadIdx.x == 0) *status = ld_coh32(bar + BAR_STATUS) != 0u ? code : 0;
+}
+
 }  // namespace
 
 size_t pass_smem_bytes() { return sizeof(Smem); }
@@ -1639,7 +1670,7 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
   a.nkeep = q.nkeep;
   a.min_p = q.min_p;
   a.bar = q.bar;
-  a.spin_limit = q.spin_limit;
+  a.wait_ticks = q.wait_ticks;
   a.cand = q.cand;
   a.logits = q.logits;
   a.hidden = q.hidden;
@@ -1664,6 +1695,20 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
   // from becoming resident for longer than the barriers' bounded wait, the
   // pass reports it through cand = -1 instead of hanging.
   return hipLaunchKernel(kern, dim3(q.grid), dim3(NTHR), args, 0, st);
+}
+
+hipError_t launch_pass_status(const unsigned* bar, int32_t* status, int32_t code, hipStream_t st) {
+  hipLaunchKernelGGL(k_pass_status, dim3(1), dim3(64), 0, st, bar, status, code);
+  return hipGetLastError();
+}
+
+hipError_t wall_clock_ticks_per_us(int device, double* ticks) {
+  int khz = 0;
+  const hipError_t e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device);
+  if (e != hipSuccess) return e;
+  if (khz <= 0) return hipErrorInvalidValue;
+  *ticks = static_cast<double>(khz) / 1000.0;
+  return hipSuccess;
 }
 
 hipError_t draft_pass_max_grid(int device, int* grid) {

@@ -36,10 +36,19 @@ def stream_ptr() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-class DeviceWeights:
-    """All drafter tensors in HBM plus the dflash_weights descriptor."""
+# Row-major matrices whose streaming copies dflash_pack_weights writes.
+MATRICES = ("fc", "lm_head") + tuple(f"layers.{l}.{m}" for l in range(synth.N_LAYERS)
+                                     for m in synth.MATRIX_KINDS)
 
-    def __init__(self, host: dict, device="cuda"):
+
+class DeviceWeights:
+    """All drafter tensors in HBM plus the dflash_weights descriptor.
+
+    With packed_only=True the row-major matrices are released once their
+    streaming copies are written and their descriptor pointers set to NULL:
+    every call then reads the copies, so the matrices are held once."""
+
+    def __init__(self, host: dict, device="cuda", packed_only: bool = False):
         require_gpu()
         self.format = host.get("__format__", "bf16")
         self.t = {k: to_device(v, device) for k, v in host.items() if not k.startswith("__")}
@@ -63,6 +72,21 @@ class DeviceWeights:
         dflash_pack_weights(d, stream_ptr())
         self.desc = d
         self.vocab = d.vocab
+        self.packed_only = packed_only
+        if packed_only:
+            torch.cuda.current_stream().synchronize()  # packing has read them
+            d.fc = d.lm_head = None
+            for l in range(synth.N_LAYERS):
+                for m in synth.MATRIX_KINDS:
+                    setattr(d.layer[l], m, None)
+            for name in MATRICES:
+                del self.t[name]
+
+    def repack(self):
+        """Rewrite the streaming copies after the row-major tensors changed."""
+        if self.packed_only:
+            raise RuntimeError("the row-major matrices were released")
+        dflash_pack_weights(self.desc, stream_ptr())
 
 
 class KVRing:
@@ -172,6 +196,24 @@ class Drafter:
                                    logits.data_ptr() if logits is not None else None,
                                    self.ws.data_ptr(), self.ws_bytes, stream_ptr())
         return cand
+
+    def verify_gated(self, cand: torch.Tensor, target: torch.Tensor, k_max: int,
+                     n_keep: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+        """Greedy verify of the first min(max(n_keep, 0), k_max) candidates,
+        the count read on the device."""
+        if out is None:
+            out = torch.empty(2, dtype=torch.int32, device=self.device)
+        _lib.dflash_verify_greedy_gated(cand.data_ptr(), target.data_ptr(), k_max,
+                                        n_keep.data_ptr(), out.data_ptr(), stream_ptr())
+        return out
+
+    def status(self, out: torch.Tensor | None = None) -> torch.Tensor:
+        """Device word: DFLASH_OK, or DFLASH_ETIMEOUT if the last pass gave up
+        waiting at a grid barrier."""
+        if out is None:
+            out = torch.empty(1, dtype=torch.int32, device=self.device)
+        _lib.dflash_draft_status(self.ws_ptr, self.ws_bytes, out.data_ptr(), stream_ptr())
+        return out
 
     def verify(self, cand: torch.Tensor, target: torch.Tensor, k: int,
                out: torch.Tensor | None = None) -> torch.Tensor:

@@ -40,6 +40,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Exported entry points; the library is built with hidden visibility, so
+ * these are its only dynamic symbols. */
+#define DFLASH_API __attribute__((visibility("default")))
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -51,11 +55,18 @@ extern "C" {
                                 position < 0 */
 #define DFLASH_EGEOMETRY  -2 /* descriptor differs from the DFlash geometry */
 #define DFLASH_ERANGE     -3 /* K/V ring: window > capacity, capacity not a
-                                multiple of 256, or n > capacity in one call */
+                                multiple of 256, or n > capacity in one call
+                                (the only way one projection call can overwrite
+                                a cell of the window that ends at its last
+                                position: with window <= capacity, the cells it
+                                evicts are older than that window) */
 #define DFLASH_EWORKSPACE -4 /* workspace smaller than dflash_workspace_size() */
 #define DFLASH_EHIP       -5 /* a kernel launch failed */
 #define DFLASH_ENONFINITE -6 /* written by dflash_check_finite into its device
                                 status word: a NaN or infinity was found */
+#define DFLASH_ETIMEOUT   -7 /* written by dflash_draft_status into its device
+                                status word: the last proposal pass gave up
+                                waiting at a grid barrier (outputs undefined) */
 
 /* Fixed drafter geometry ("Drafter runtime" on the PR #1426 page). */
 #define DFLASH_HIDDEN     2560
@@ -114,11 +125,13 @@ typedef struct {
    * matrices and fc, in the backbone's format), written by
    * dflash_pack_weights after the weights are loaded (and again whenever
    * those tensors change).  Required by dflash_draft_block (NULL ->
-   * DFLASH_EINVAL); used when set by dflash_lm_head_argmax, by the few-row
-   * (<= 64) paths of dflash_fuse_context / dflash_project_ctx_kv and, for a
-   * bf16 backbone, by their many-row paths too; without it they read the
-   * row-major tensors above (a quantized backbone's many-row paths always
-   * decode those).  Caller-owned, like everything else. */
+   * DFLASH_EINVAL).  When it is set, every call reads the matrices from it
+   * (a quantized backbone's many-row fusion / projection decodes its blocks
+   * from here) and the row-major matrix pointers above (fc, the 35 layer
+   * matrices, lm_head) may be NULL: the weights can then be held once, in
+   * the streaming layout.  Gains and the embedding are always read from
+   * their own pointers.  Without it, the row-major matrices are required and
+   * read directly.  Caller-owned, like everything else. */
   void* packed;
 } dflash_weights;
 
@@ -142,14 +155,14 @@ typedef struct {
 /* Bytes of device workspace needed for calls with up to `max_rows` context
  * rows (fuse/project) and blocks of up to `max_block` rows (draft).  Returns 0
  * for invalid arguments. */
-size_t dflash_workspace_size(const dflash_weights* w, int32_t max_rows,
+DFLASH_API size_t dflash_workspace_size(const dflash_weights* w, int32_t max_rows,
                              int32_t max_block);
 
 /* Bytes of the streaming copies: 2 * vocab * 2560 for the LM head plus the
  * 35 layer matrices (5 x (6144*2560 + 2*512*2560 + 2560*6144 + 2*7680*2560 +
  * 2560*7680) weights) and fc (2560*12800 weights) at 2 (bf16), 34/32 (Q8_0)
  * or 18/32 (Q4_0) bytes per weight.  0 for an invalid descriptor. */
-size_t dflash_packed_size(const dflash_weights* w);
+DFLASH_API size_t dflash_packed_size(const dflash_weights* w);
 
 /* Writes the streaming copies into w->packed, enqueued on `stream`.  A bf16
  * [N][K] matrix becomes, in order, its 16-row tiles; within a tile its
@@ -169,13 +182,13 @@ size_t dflash_packed_size(const dflash_weights* w);
  * the S = 2 (Q8_0) or 4 (Q4_0) scales of piece kb of row n at
  * ((n/16 * P + kb) * 16 + n%16) * S + s.
  * Returns DFLASH_EINVAL if w->packed is NULL. */
-int32_t dflash_pack_weights(const dflash_weights* w, void* stream);
+DFLASH_API int32_t dflash_pack_weights(const dflash_weights* w, void* stream);
 
 /* Context fusion ("Drafter runtime": rmsnorm(fc(concat(target taps)))).
  *   taps: bf16 [n][5][2560], the five target taps of each position in tap order
  *   ctx : bf16 [n][2560] output, ctx[t] = rmsnorm(fc . concat(taps[t]), hidden_norm)
  * n may be 0 (no work).  ws/ws_bytes: workspace. */
-int32_t dflash_fuse_context(const dflash_weights* w, const void* taps, int32_t n,
+DFLASH_API int32_t dflash_fuse_context(const dflash_weights* w, const void* taps, int32_t n,
                             void* ctx, void* ws, size_t ws_bytes, void* stream);
 
 /* Per-layer context K/V projection ("Drafter runtime": the fused context is
@@ -184,7 +197,7 @@ int32_t dflash_fuse_context(const dflash_weights* w, const void* taps, int32_t n
  *   K_l[j][m % cap] = fp16(RoPE_m(rmsnorm(Wk_l ctx[t])_j, k_norm_l))
  *   V_l[j][m % cap] = fp16((Wv_l ctx[t])_j)
  *   ctx: bf16 [n][2560] (output of dflash_fuse_context); pos0 >= 0; n <= capacity. */
-int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ctx, int32_t n,
+DFLASH_API int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ctx, int32_t n,
                               int64_t pos0, const dflash_kv* kv, void* ws,
                               size_t ws_bytes, void* stream);
 
@@ -198,13 +211,17 @@ int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ctx, int32_t 
  * block in [1, 8]; anchor_id, mask_id in [0, vocab); p >= 0.  Reads the
  * streaming copy w->packed (see dflash_pack_weights), which must be current.
  * The pass is one persistent kernel of one block per compute unit whose
- * blocks wait for each other: it needs the whole device.  If other work keeps
- * some of its blocks from starting for about half a second, the pass gives up
- * waiting and sets every cand to -1 (its outputs are then undefined).  The
- * bound, in barrier polls, is 2^24 unless the environment variable
- * DFLASH_SPIN_LIMIT (read by the host on each call, 1 .. 2^24) sets a smaller
- * one -- meant for tests of this path. */
-int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* kv, int64_t p,
+ * blocks wait for each other: it needs the whole device.  Every wait at a
+ * grid barrier is bounded in wall-clock time (the device's constant-rate
+ * counter): if other work keeps some of its blocks from starting for longer
+ * than 0.5 s, the pass gives up, sets every cand to -1 and records the
+ * give-up in the workspace (dflash_draft_status reads it); its outputs are
+ * then undefined.  After one give-up no later barrier of the pass waits, so
+ * the pass still ends about one bound after it started waiting.  The
+ * environment variable DFLASH_BARRIER_TIMEOUT_US (read by the host on each
+ * call, 0 .. 10000000 microseconds; 0 = give up after about 32 polls that
+ * do not see the release) replaces the 0.5 s bound -- meant for tests. */
+DFLASH_API int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* kv, int64_t p,
                            int32_t anchor_id, int32_t mask_id, int32_t block,
                            int32_t* cand, void* logits_opt, void* hidden_opt,
                            void* ws, size_t ws_bytes, void* stream);
@@ -226,7 +243,7 @@ int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* kv, int64_t
  * non-null and 4-byte aligned.  No logits / hidden outputs.  No extra weight
  * traffic.  A pass whose barriers gave up waiting sets cand to -1, conf to
  * NaN and n_keep to 0. */
-int32_t dflash_draft_block_gated(const dflash_weights* w, const dflash_kv* kv, int64_t p,
+DFLASH_API int32_t dflash_draft_block_gated(const dflash_weights* w, const dflash_kv* kv, int64_t p,
                                  int32_t anchor_id, int32_t mask_id, int32_t block,
                                  float min_p, int32_t* cand, float* conf, int32_t* n_keep,
                                  void* ws, size_t ws_bytes, void* stream);
@@ -239,7 +256,7 @@ int32_t dflash_draft_block_gated(const dflash_weights* w, const dflash_kv* kv, i
  *   logits_opt: bf16 [rows][vocab] or NULL
  * rows in [1, 8].  Reads w->packed when set, else w->lm_head; both give the
  * same bits.  dflash_draft_block computes the same readout on its mask rows. */
-int32_t dflash_lm_head_argmax(const dflash_weights* w, const void* hidden, int32_t rows,
+DFLASH_API int32_t dflash_lm_head_argmax(const dflash_weights* w, const void* hidden, int32_t rows,
                               int32_t* cand, void* logits_opt, void* ws, size_t ws_bytes,
                               void* stream);
 
@@ -251,8 +268,28 @@ int32_t dflash_lm_head_argmax(const dflash_weights* w, const void* hidden, int32
  *   out   : int32 [2] = {accepted, next}: accepted = longest prefix with
  *           cand[i] == target[i]; next = target[accepted] (the verifier's
  *           continuation token).  k in [0, 7]. */
-int32_t dflash_verify_greedy(const int32_t* cand, const int32_t* target, int32_t k,
+DFLASH_API int32_t dflash_verify_greedy(const int32_t* cand, const int32_t* target, int32_t k,
                              int32_t* out, void* stream);
+
+/* Greedy verification of the candidates a confidence gate kept, with the
+ * count read on the device (the n_keep word of dflash_draft_block_gated), so
+ * that truncating the proposal needs no device-to-host read (PR #3322,
+ * "Long-prompt diagnosis and fix": the floor cuts the rows the target
+ * verifies).  Same as dflash_verify_greedy with k = min(max(*n_keep, 0),
+ * k_max), read when the kernel runs:
+ *   cand  : int32 [k_max]     target: int32 [k_max+1] (entries past k+1 unused)
+ *   n_keep: int32 device word  out: int32 [2] = {accepted, next}
+ * k_max in [0, 7]; all pointers 4-byte aligned. */
+DFLASH_API int32_t dflash_verify_greedy_gated(const int32_t* cand, const int32_t* target, int32_t k_max,
+                                   const int32_t* n_keep, int32_t* out, void* stream);
+
+/* Outcome of the last proposal pass (dflash_draft_block or
+ * dflash_draft_block_gated) enqueued with the workspace `ws`: writes, in
+ * stream order after that pass, DFLASH_OK or DFLASH_ETIMEOUT (the pass gave
+ * up waiting at a grid barrier) into the int32 device word `status`.  Lets
+ * callers that read only logits_opt / hidden_opt, or block 1 (no
+ * candidates), see a give-up.  Undefined before the workspace's first pass. */
+DFLASH_API int32_t dflash_draft_status(const void* ws, size_t ws_bytes, int32_t* status, void* stream);
 
 /* Optional finite check of a device buffer, for callers that want the
  * pages' refusal of non-finite values (RFC #366 page, "3. First small
@@ -269,11 +306,11 @@ int32_t dflash_verify_greedy(const int32_t* cand, const int32_t* target, int32_t
  *           exponent bits set), to DFLASH_ENONFINITE.  count 0 -> DFLASH_OK.
  * Returns DFLASH_EINVAL for a null or misaligned pointer (x may be NULL only
  * when count is 0), count < 0 or an unknown dtype. */
-int32_t dflash_check_finite(const void* x, int64_t count, int32_t dtype, int32_t* status,
+DFLASH_API int32_t dflash_check_finite(const void* x, int64_t count, int32_t dtype, int32_t* status,
                             void* stream);
 
 /* Static description of a return code (host string, never NULL). */
-const char* dflash_strerror(int32_t code);
+DFLASH_API const char* dflash_strerror(int32_t code);
 
 #ifdef __cplusplus
 }

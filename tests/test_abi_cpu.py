@@ -45,6 +45,15 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, s)
 
 
+def test_library_exports_only_the_c_abi():
+    """Hidden visibility plus a version script: the dynamic symbol table holds
+    the header's entry points and nothing else (no C++ internals)."""
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    defined = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    assert defined == set(header_symbols()), sorted(defined ^ set(header_symbols()))
+
+
 def test_library_has_no_torch_dependency():
     out = subprocess.run(["readelf", "-d", _lib.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
@@ -94,6 +103,7 @@ def test_strerror_strings(lib):
         assert isinstance(_lib.dflash_strerror(code), str)
     assert _lib.dflash_strerror(-4) == "workspace too small"
     assert _lib.dflash_strerror(_lib.DFLASH_ENONFINITE) == "non-finite value found"
+    assert "gave up" in _lib.dflash_strerror(_lib.DFLASH_ETIMEOUT)
 
 
 def test_check_finite_arguments(lib):
@@ -235,3 +245,51 @@ def test_misaligned_pointers_are_rejected(lib):
     w.packed = A + 4
     assert _lib.dflash_draft_block(w, kv, 10, 1, 2, 8, A, None, None, A, big,
                                    check=False) == E
+
+
+def test_gated_verify_and_status_arguments(lib):
+    """The verify that reads its count on the device and the pass-status
+    readout validate their arguments on the host."""
+    E = _lib.DFLASH_EINVAL
+    V = _lib.dflash_verify_greedy_gated
+    assert V(A, A, 8, A, A, check=False) == E          # k_max > 7
+    assert V(A, A, -1, A, A, check=False) == E
+    assert V(A, A, 7, None, A, check=False) == E       # no count word
+    assert V(A, None, 7, A, A, check=False) == E
+    assert V(A, A, 7, A, None, check=False) == E
+    assert V(None, A, 3, A, A, check=False) == E       # candidates needed when k_max > 0
+    assert V(A, A, 7, A + 2, A, check=False) == E      # misaligned count word
+    need = _lib.dflash_workspace_size(fake_weights(), 0, 8)
+    S = _lib.dflash_draft_status
+    assert S(None, need, A, check=False) == E
+    assert S(A, need, None, check=False) == E
+    assert S(A, need, A + 1, check=False) == E
+    assert S(A + 8, need, A, check=False) == E
+    assert S(A, need - 1, A, check=False) == _lib.DFLASH_EWORKSPACE
+
+
+def test_packed_copy_may_stand_in_for_row_major_matrices(lib):
+    """With the streaming copies set, the row-major matrices (fc, the layer
+    matrices, the LM head) may be null -- the weights are then held once;
+    without them, or when packing, they are required.  Gains and the
+    embedding are always required."""
+    big = 1 << 40
+    E = _lib.DFLASH_EINVAL
+    w = fake_weights()
+    w.packed = A
+    w.fc = w.lm_head = None
+    for l in range(5):
+        for f in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+            setattr(w.layer[l], f, None)
+    assert _lib.dflash_fuse_context(w, A, 0, A, A, big, check=False) == 0   # checks pass, no work
+    assert _lib.dflash_project_ctx_kv(w, A, 0, 0, fake_kv(), A, big, check=False) == 0
+    assert _lib.dflash_packed_size(w) > 0
+    assert _lib.dflash_pack_weights(w, None, check=False) == E             # packing reads them
+    w.packed = None
+    assert _lib.dflash_fuse_context(w, A, 0, A, A, big, check=False) == E
+    w.packed = A
+    w.layer[2].q_norm = None
+    assert _lib.dflash_fuse_context(w, A, 0, A, A, big, check=False) == E
+    w.layer[2].q_norm = A
+    w.embed = None
+    assert _lib.dflash_fuse_context(w, A, 0, A, A, big, check=False) == E

@@ -187,14 +187,14 @@ def test_gated_pass_at_full_context_size(dev_w):
 
 
 def test_gated_timeout_reports_nan_and_zero(dev_w, monkeypatch):
-    """A pass whose barriers give up waiting (bound forced from the host to
-    one poll) reports cand -1, conf NaN and n_keep 0; the next pass is whole."""
+    """A pass whose barriers give up waiting (wall-clock bound forced from the
+    host to 0) reports cand -1, conf NaN and n_keep 0; the next pass is whole."""
     kv = KVRing(256)
     dr = Drafter(dev_w, kv)
-    monkeypatch.setenv("DFLASH_SPIN_LIMIT", "1")
+    monkeypatch.setenv("DFLASH_BARRIER_TIMEOUT_US", "0")
     cand, conf, nk = dr.draft_gated(100, 11, 8, 0.0)
     torch.cuda.synchronize()
-    monkeypatch.delenv("DFLASH_SPIN_LIMIT")
+    monkeypatch.delenv("DFLASH_BARRIER_TIMEOUT_US")
     c, cf, k = cand.cpu().numpy().copy(), conf.cpu().numpy().copy(), int(nk.cpu().item())
     cand2, conf2, nk2 = dr.draft_gated(100, 11, 8, 0.0)
     torch.cuda.synchronize()

@@ -1,0 +1,332 @@
+"""GPU parity at the sizes the benchmark times, plus the boundary paths added
+beside the four operations: the decode loop at 8192 resident cells (block
+8), the quantized backbones at 8192 cells (block 4), exact ties in the
+vocabulary argmax, the prompt-tail flow (only the last `window` positions of
+a longer prompt fused and projected), weights held only as streaming copies,
+the gated verify that reads its count on the device, and a pass whose grid
+barriers give up.
+
+Bars are those of test_parity_gpu: ids exact where the oracle's top-2 margin
+exceeds 0.05 (elsewhere the id must be a near-maximum of the oracle's
+logits); logits and hidden states within 2e-2 per-row relative error.
+"""
+import math
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from block_draft_model_pass_amd import _lib, synth
+from block_draft_model_pass_amd.device import DeviceWeights, Drafter, KVRing, to_device
+from oracle import dflash_oracle as O
+from test_parity_gpu import (MARGIN, TOL, check_cands, check_draft, dec_bf16, end_to_end,
+                             gpu_draft, row_rel_err, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def host_w():
+    return synth.make_weights()
+
+
+@pytest.fixture(scope="module")
+def dev_w(host_w):
+    return DeviceWeights(host_w)
+
+
+@pytest.fixture(scope="module")
+def ow(host_w):
+    return O.enable_cache(dict(host_w))
+
+
+def conf_bars(lg, ref, c):
+    """Per-row bound on |log conf_gpu - log conf_oracle| from the observed
+    logit error (see test_gate_gpu): the max moves by at most the error at
+    either argmax, logsumexp by the softmax-weighted error plus half the
+    largest squared error."""
+    lo = ref["logits"]
+    d = np.abs(lg - lo) + np.abs(lg) * 2.0 ** -8
+    pr = np.exp(lo - lo.max(axis=1, keepdims=True))
+    pr /= pr.sum(axis=1, keepdims=True)
+    return np.array([max(d[i, ref["cand"][i]], d[i, c[i]]) + (pr[i] * d[i]).sum()
+                     + 0.5 * d[i].max() ** 2 + 1e-5 for i in range(len(c))])
+
+
+# ------------------------------------------------------------------ decode loop, ctx 8192
+
+def test_decode_loop_ctx8192_block8(dev_w, ow):
+    """The timed workload: 8192 context cells committed through the GEMM
+    paths on both sides, then propose -> verify -> commit with block 8.  Each
+    pass's target is built from the ORACLE's candidates (Bernoulli(0.75)
+    draws) and handed to both verifiers, so a wrong GPU candidate changes the
+    GPU's accepted length; both sides then commit the same cells (the
+    oracle's accepted length), so every pass is compared: ids by the margin
+    rule, logits and hidden states by the 2e-2 bar, the GPU's verify against
+    the oracle's verify of the GPU's candidates, and the accepted length
+    against the oracle's wherever the deciding candidates coincide (near-tie
+    rows may legitimately pick another id).  The gated pass at the same
+    anchor must give the same ids and each candidate's softmax probability
+    within the bound the logit error allows."""
+    ctx0, passes, B = 8192, 10, 8
+    K = B - 1
+    say("decode loop ctx=8192 block=8")
+    kv = KVRing(32768)
+    dr = Drafter(dev_w, kv, max_rows=ctx0)
+    taps0 = synth.make_taps(range(ctx0))
+    dr.commit(to_device(taps0), 0)
+    store = O.ContextStore()
+    store.put(*O.project_ctx_kv(ow, O.fuse_context(ow, taps0), 0), 0)
+    del taps0
+    p, anchor = ctx0, synth.anchor_token(0)
+    cand = torch.empty(K, dtype=torch.int32, device="cuda")
+    logits = torch.empty((K, dev_w.vocab), dtype=torch.int16, device="cuda")
+    hidden = torch.empty((B, synth.HIDDEN), dtype=torch.int16, device="cuda")
+    out = torch.empty(2, dtype=torch.int32, device="cuda")
+    same, acc, off = 0, 0, 0
+    for t in range(passes):
+        dr.draft(p, anchor, B, cand=cand, logits=logits, hidden=hidden)
+        gc, gconf, _ = dr.draft_gated(p, anchor, B, 0.5)
+        torch.cuda.synchronize()
+        ck, cv = store.window(p)
+        ref = O.draft_block(ow, ck, cv, p, anchor, synth.MASK_ID, B)
+        c = cand.cpu().numpy()
+        check_draft((cand, logits, hidden), ref, B, f"loop8192 t={t} p={p}")
+        assert np.array_equal(gc.cpu().numpy(), c)
+        lg = dec_bf16(logits)
+        bars = conf_bars(lg, ref, c)
+        err = np.abs(np.log(gconf.cpu().numpy().astype(np.float64)) - np.log(ref["conf"]))
+        assert np.all(err <= bars), (err, bars)
+        tgt = synth.synthetic_target(ref["cand"], t)
+        dr.verify(cand, to_device(tgt), K, out=out)
+        a, nxt = out.cpu().tolist()
+        oa, onxt = O.verify_greedy(ref["cand"], tgt)
+        # the GPU's verify on its own candidates is the oracle's verify on
+        # them; where its candidates equal the oracle's up to the oracle's
+        # first mismatch (the rows that decide the accepted length), the
+        # accepted length and continuation are the oracle's
+        assert (a, nxt) == O.verify_greedy(c, tgt), (t, a, nxt, c, tgt)
+        d = min(oa + 1, K)
+        if np.array_equal(c[:d], ref["cand"][:d]):
+            assert (a, nxt) == (oa, onxt), (t, a, oa, nxt, onxt)
+            same += 1
+        say(f"[loop8192 t={t}] accepted gpu {a} oracle {oa}; conf err {err.max():.2e}")
+        # both sides commit the oracle's accepted cells and continue from its anchor
+        taps = synth.make_taps(range(p, p + oa + 1))
+        dr.commit(to_device(taps), p)
+        store.put(*O.project_ctx_kv(ow, O.fuse_context(ow, taps), p), p)
+        acc += oa
+        off += K
+        p, anchor = p + oa + 1, onxt
+    say(f"[loop8192] {passes} passes compared, {same} with the oracle's deciding candidates "
+        f"(accepted length equal); accepted/offered {acc}/{off}")
+    assert same >= 6
+
+
+# ------------------------------------------------------------------ quantized, ctx 8192
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+def test_quant_draft_ctx8192_block4(fmt):
+    """The quantized-backbone workload: 8192 cells fused and projected from
+    Q8_0 / Q4_0 weights (blocks decoded on both sides; the oracle exactly),
+    one block of 4 at 8192."""
+    say(f"quantized {fmt} ctx 8192 block 4")
+    host = synth.make_weights(fmt=fmt)
+    dev = DeviceWeights(host)
+    ow = O.enable_cache(dict(host))
+    end_to_end(dev, ow, 8192, 4, tag=f"{fmt} ctx8192 b4")
+    del dev
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ ties
+
+def test_argmax_exact_ties_take_the_lowest_id(host_w):
+    """Copies of the LM-head row of mask row 1's candidate c give exactly
+    equal fp32 logits.  A copy at a higher id (another block's tiles) leaves
+    c; a copy at a lower id, in the same 16-row tile or in another block's
+    tiles, wins -- in the pass's cross-block key reduction, in the gated
+    pass, and in the standalone LM-head argmax on the pass's hidden rows."""
+    hw = dict(host_w)
+    hw["lm_head"] = host_w["lm_head"].copy()
+    dev = DeviceWeights(hw)
+    kv = KVRing(1024)
+    dr = Drafter(dev, kv, max_rows=64)
+    n = 40
+    dr.commit(to_device(synth.make_taps(range(n))), 0)
+    B, V = 8, dev.vocab
+    anchor = synth.anchor_token(n)
+    cand0, _, hidden0 = gpu_draft(dr, n, anchor, B, V)
+    base = cand0.cpu().numpy().copy()
+    c = int(base[0])
+    lm = dev.t["lm_head"]  # row-major bf16 [V][2560] (int16 view)
+    row_c = lm[c].clone()
+    far = 32 * 57 + 5   # another tile pair, hence another block of the sweep
+    cases = []
+    if c + far < V:
+        cases.append(("higher, other block", c + far))
+    if c % 16 != 15:
+        cases.append(("higher, same tile", c + 1))
+    if c % 16:
+        cases.append(("lower, same tile", c - 1))
+    if c >= far:
+        cases.append(("lower, other block", c - far))
+    assert any(d < c for _, d in cases) and any(d > c for _, d in cases), (c, cases)
+    rows_c = np.where(base == c)[0]
+    for name, d in cases:
+        want = min(c, d)
+        saved = lm[d].clone()
+        lm[d] = row_c
+        dev.repack()
+        cand, logits, hidden = gpu_draft(dr, n, anchor, B, V)
+        lg = logits.cpu().numpy()
+        assert np.array_equal(lg[:, c], lg[:, d]), name      # exact tie (bf16 copies)
+        got = cand.cpu().numpy()
+        gcand, _, _ = dr.draft_gated(n, anchor, B, 0.0)
+        zc = torch.empty(B - 1, dtype=torch.int32, device="cuda")
+        dr.lm_head_argmax(hidden[1:].contiguous(), zc)
+        torch.cuda.synchronize()
+        g2, z2 = gcand.cpu().numpy(), zc.cpu().numpy()
+        say(f"[tie {name}] c={c} copy at {d}: pass {got[rows_c].tolist()} gated "
+            f"{g2[rows_c].tolist()} standalone {z2[rows_c].tolist()} (want {want})")
+        assert (got[rows_c] == want).all(), (name, got, want)
+        assert (g2[rows_c] == want).all(), (name, g2, want)
+        assert (z2[rows_c] == want).all(), (name, z2, want)
+        lm[d] = saved
+    dev.repack()
+    del dev
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ prompt tail
+
+def test_prompt_tail_fusion_matches_full_prompt(dev_w, ow):
+    """A 3000-position prompt with a 1024-cell window: the GPU fuses and
+    projects only positions 1976..2999 (its tail; the GEMM path), the oracle
+    the whole prompt; the block drafted at 3000 sees the same window on both
+    sides, so the results must agree (PR #3322 later snapshot, "How to
+    enable the pushed optimization options": prompt-tail fusion; PR #1426
+    "Current limitations": a bounded drafter window)."""
+    n, window = 3000, 1024
+    say(f"prompt tail n={n} window={window}")
+    taps = synth.make_taps(range(n))
+    g = O.geometry(window=window)
+    store = O.ContextStore(g)
+    store.put(*O.project_ctx_kv(ow, O.fuse_context(ow, taps), 0), 0)
+    kv = KVRing(window, window=window)
+    dr = Drafter(dev_w, kv, max_rows=window)
+    dr.commit(to_device(taps[n - window:]), n - window)
+    anchor = synth.anchor_token(n)
+    res = gpu_draft(dr, n, anchor, 8, dev_w.vocab)
+    ck, cv = store.window(n)
+    assert ck.shape[2] == window
+    ref = O.draft_block(ow, ck, cv, n, anchor, synth.MASK_ID, 8, g)
+    check_draft(res, ref, 8, "prompt tail")
+
+
+# ------------------------------------------------------------------ packed-only weights
+
+@pytest.mark.parametrize("fmt", ["bf16", "q8_0"])
+def test_weights_held_only_as_streaming_copies(fmt):
+    """Row-major matrices released after packing (their pointers NULL): the
+    few-row and many-row fusion / projection (a quantized backbone decodes
+    its blocks from the streaming copy), the draft pass and the standalone
+    LM head all read the copies and match the oracle."""
+    say(f"packed-only weights {fmt}")
+    host = synth.make_weights(fmt=fmt)
+    dev = DeviceWeights(host, packed_only=True)
+    assert dev.desc.fc is None and dev.desc.layer[3].wd is None
+    ow = O.enable_cache(dict(host))
+    for n, block in ((13, 4), (300, 8)):
+        (cand, _, hidden), ref = end_to_end(dev, ow, n, block, cap=1024, window=1024,
+                                            tag=f"packed-only {fmt} ctx{n}")
+        dr = Drafter(dev, KVRing(256))
+        zc = torch.empty(block - 1, dtype=torch.int32, device="cuda")
+        dr.lm_head_argmax(hidden[1:].contiguous(), zc)
+        torch.cuda.synchronize()
+        check_cands(zc.cpu().numpy(), ref["cand"], ref["logits"], ref["margin"])
+    del dev
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ gated verify
+
+def test_verify_gated_reads_count_on_device():
+    """dflash_verify_greedy_gated equals the oracle's verify on the first
+    min(max(n_keep, 0), k_max) candidates, for counts below, inside and above
+    the range, with no host read between the count's producer and the
+    verify."""
+    rng = np.random.default_rng(3)
+    out = torch.empty(2, dtype=torch.int32, device="cuda")
+    nk = torch.empty(1, dtype=torch.int32, device="cuda")
+    for trial in range(120):
+        k_max = int(rng.integers(0, 8))
+        cand = rng.integers(0, 3, size=k_max).tolist()
+        tgt = rng.integers(0, 3, size=k_max + 1).tolist()
+        keep = int(rng.integers(-2, k_max + 3))
+        c = torch.tensor(cand + [0], dtype=torch.int32, device="cuda")
+        t = torch.tensor(tgt, dtype=torch.int32, device="cuda")
+        nk.fill_(keep)
+        _lib.dflash_verify_greedy_gated(c.data_ptr(), t.data_ptr(), k_max, nk.data_ptr(),
+                                        out.data_ptr())
+        torch.cuda.synchronize()
+        k = min(max(keep, 0), k_max)
+        assert tuple(out.cpu().tolist()) == O.verify_greedy(cand[:k], tgt[:k + 1]), \
+            (cand, tgt, keep, k_max)
+
+
+def test_gated_draft_then_gated_verify_on_device(dev_w, ow):
+    """The gate's n_keep feeds the verify directly on the device: accepted
+    length and continuation equal the oracle's verify on the kept prefix."""
+    kv = KVRing(1024)
+    dr = Drafter(dev_w, kv, max_rows=64)
+    n, B = 40, 8
+    taps = synth.make_taps(range(n))
+    dr.commit(to_device(taps), 0)
+    anchor = synth.anchor_token(n)
+    out = torch.empty(2, dtype=torch.int32, device="cuda")
+    for i, floor in enumerate((0.0, 2.9e-4, 1.0)):
+        cand, conf, nk = dr.draft_gated(n, anchor, B, floor)
+        tg = to_device(synth.random_targets(B - 1, index=i))
+        tg[:3].copy_(cand[:3])  # the target agrees with the first three candidates
+        dr.verify_gated(cand, tg, B - 1, nk, out=out)
+        torch.cuda.synchronize()
+        k = int(nk.cpu().item())
+        c, t = cand.cpu().numpy(), tg.cpu().numpy()
+        assert k == O.gate_candidates(conf.cpu().numpy().astype(np.float64), floor)
+        assert tuple(out.cpu().tolist()) == O.verify_greedy(c[:k], t[:k + 1]), (k, c, t)
+        say(f"[gated verify] floor {floor}: n_keep {k}, out {out.cpu().tolist()}")
+
+
+# ------------------------------------------------------------------ barrier give-up
+
+def test_barrier_give_up_is_reported_and_bounded(dev_w, monkeypatch):
+    """Bound 0 (set from the host): waits give up after about 32 unanswered
+    polls, the pass writes cand = -1, dflash_draft_status reports
+    DFLASH_ETIMEOUT, and the pass returns promptly (no later barrier waits
+    once one gave up).  With a 0.2 s bound and a free device no wait gives
+    up: the status is DFLASH_OK and the candidates are the default bound's."""
+    kv = KVRing(256)
+    dr = Drafter(dev_w, kv)
+    good = dr.draft(100, 11, 8).cpu().numpy().copy()
+    st0 = int(dr.status().cpu().item())
+    monkeypatch.setenv("DFLASH_BARRIER_TIMEOUT_US", "0")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    bad = dr.draft(100, 11, 8)
+    st = dr.status()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    bad, st = bad.cpu().numpy().copy(), int(st.cpu().item())
+    monkeypatch.setenv("DFLASH_BARRIER_TIMEOUT_US", "200000")
+    again = dr.draft(100, 11, 8).cpu().numpy().copy()
+    st2 = int(dr.status().cpu().item())
+    monkeypatch.delenv("DFLASH_BARRIER_TIMEOUT_US")
+    say(f"give-up path: good {good.tolist()} forced {bad.tolist()} status {st0}/{st}/{st2} "
+        f"forced pass {dt * 1e3:.2f} ms")
+    assert st0 == _lib.DFLASH_OK and st2 == _lib.DFLASH_OK
+    assert st == _lib.DFLASH_ETIMEOUT
+    assert (bad == -1).all()
+    assert dt < 0.25
+    assert np.array_equal(good, again)

@@ -374,18 +374,18 @@ def test_decode_loop_short(dev_w, ow):
 
 
 def test_barrier_timeout_reports_minus_one(dev_w, monkeypatch):
-    """A grid barrier that stops waiting (forced from the host with a bound
-    of one poll) makes the pass report cand = -1; the next pass, with the
-    default bound, is correct again (every pass starts from fresh barrier
-    words).  No kernel waits unboundedly on this path."""
+    """A grid barrier that stops waiting (forced from the host with a
+    wall-clock bound of 0) makes the pass report cand = -1; the next pass,
+    with the default bound, is correct again (every pass starts from fresh
+    barrier words).  No kernel waits unboundedly on this path."""
     kv = KVRing(256)
     dr = Drafter(dev_w, kv)
     good = dr.draft(100, 11, 8).cpu().numpy().copy()
     torch.cuda.synchronize()
-    monkeypatch.setenv("DFLASH_SPIN_LIMIT", "1")
+    monkeypatch.setenv("DFLASH_BARRIER_TIMEOUT_US", "0")
     bad = dr.draft(100, 11, 8).cpu().numpy().copy()
     torch.cuda.synchronize()
-    monkeypatch.delenv("DFLASH_SPIN_LIMIT")
+    monkeypatch.delenv("DFLASH_BARRIER_TIMEOUT_US")
     again = dr.draft(100, 11, 8).cpu().numpy().copy()
     torch.cuda.synchronize()
     say(f"timeout path: good {good.tolist()} forced {bad.tolist()} again {again.tolist()}")
