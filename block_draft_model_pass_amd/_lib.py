@@ -88,6 +88,10 @@ def load() -> ctypes.CDLL:
                                        c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_size_t, c_void_p]
     lib.dflash_draft_block.restype = c_int32
+    lib.dflash_draft_block_static.argtypes = [P(dflash_weights), P(dflash_kv), c_int64,
+                                              c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                              c_void_p, c_void_p]
+    lib.dflash_draft_block_static.restype = c_int32
     lib.dflash_draft_block_gated.argtypes = [P(dflash_weights), P(dflash_kv), c_int64,
                                              c_int32, c_int32, c_int32, ctypes.c_float,
                                              c_void_p, c_void_p, c_void_p, c_void_p,
@@ -188,3 +192,9 @@ def dflash_draft_status(ws, ws_bytes, status, stream=None, check=True):
     rc = load().dflash_draft_status(ws, ws_bytes, status, stream)
     return _check(rc, "dflash_draft_status") if check else rc
 
+
+def dflash_draft_block_static(w, kv, p, anchor_id, mask_id, block, cand, logits_opt,
+                              hidden_opt, stream=None, check=True):
+    rc = load().dflash_draft_block_static(_ref(w), _ref(kv), p, anchor_id, mask_id, block, cand,
+                                          logits_opt, hidden_opt, stream)
+    return _check(rc, "dflash_draft_block_static") if check else rc

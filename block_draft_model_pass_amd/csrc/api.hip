@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 
 using namespace dfl;
 
@@ -258,6 +259,31 @@ SegTable seg_kv(const dflash_weights* w) {
 
 const uint16_t* u16p(const void* p) { return static_cast<const uint16_t*>(p); }
 
+// Workspace of dflash_draft_block_static, for callers that cannot allocate:
+// a file-scope device array (each device the library runs on holds its own
+// copy until the process ends).  The pass needs layout().fixed bytes of it
+// whatever the context length or block size.  In host code `scratch` names a
+// host-side stand-in, never the device memory: its device address is looked
+// up once per device (scratch_on_device) and only that address is used.
+constexpr size_t SCRATCH_BYTES = static_cast<size_t>(66) << 20;
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device (null on failure),
+// looked up on the first call on that device.
+void* scratch_on_device() {
+  static std::mutex mu;
+  static void* ptr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptr[dev] = a;
+  }
+  return ptr[dev];
+}
+
 }  // namespace
 
 extern "C" size_t dflash_workspace_size(const dflash_weights* w, int32_t max_rows,
@@ -428,10 +454,13 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
 namespace {
 // Shared body of dflash_draft_block and dflash_draft_block_gated (conf and
 // nkeep null for the former).
+// static_ws: the workspace is the library's device array (ws and ws_bytes
+// ignored), resolved after the arguments are checked.
 int32_t draft_block_impl(const dflash_weights* w, const dflash_kv* kv, int64_t p,
                          int32_t anchor_id, int32_t mask_id, int32_t block, int32_t* cand,
                          float* conf, int32_t* nkeep, float min_p, void* logits_opt,
-                         void* hidden_opt, void* ws, size_t ws_bytes, void* stream) {
+                         void* hidden_opt, void* ws, size_t ws_bytes, void* stream,
+                         bool static_ws = false) {
   int rc = check_weights(w);
   if (rc) return rc;
   rc = check_kv(kv);
@@ -439,10 +468,15 @@ int32_t draft_block_impl(const dflash_weights* w, const dflash_kv* kv, int64_t p
   if (block < 1 || block > MAXB || p < 0) return DFLASH_EINVAL;
   if (anchor_id < 0 || anchor_id >= w->vocab || mask_id < 0 || mask_id >= w->vocab)
     return DFLASH_EINVAL;
-  if (!ws || (block > 1 && !cand)) return DFLASH_EINVAL;
+  if ((!ws && !static_ws) || (block > 1 && !cand)) return DFLASH_EINVAL;
   if (!a16(ws) || !a16(logits_opt) || !a16(hidden_opt) || (reinterpret_cast<uintptr_t>(cand) & 3u))
     return DFLASH_EINVAL;
   const Layout Lw = layout();
+  if (static_ws) {
+    ws = scratch_on_device();
+    ws_bytes = SCRATCH_BYTES;
+    if (!ws) return DFLASH_EHIP;
+  }
   if (ws_bytes < Lw.fixed) return DFLASH_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (!w->packed) return DFLASH_EINVAL;  // the streaming copy (dflash_pack_weights)
@@ -532,6 +566,15 @@ extern "C" int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* 
                                       void* ws, size_t ws_bytes, void* stream) {
   return draft_block_impl(w, kv, p, anchor_id, mask_id, block, cand, nullptr, nullptr, 0.f,
                           logits_opt, hidden_opt, ws, ws_bytes, stream);
+}
+
+extern "C" int32_t dflash_draft_block_static(const dflash_weights* w, const dflash_kv* kv,
+                                             int64_t p, int32_t anchor_id, int32_t mask_id,
+                                             int32_t block, int32_t* cand, void* logits_opt,
+                                             void* hidden_opt, void* stream) {
+  static_assert(SCRATCH_BYTES % 256 == 0, "scratch holds whole 256-byte workspace regions");
+  return draft_block_impl(w, kv, p, anchor_id, mask_id, block, cand, nullptr, nullptr, 0.f,
+                          logits_opt, hidden_opt, nullptr, 0, stream, true);
 }
 
 extern "C" int32_t dflash_draft_block_gated(const dflash_weights* w, const dflash_kv* kv,

@@ -226,6 +226,23 @@ DFLASH_API int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* 
                            int32_t* cand, void* logits_opt, void* hidden_opt,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* dflash_draft_block for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument; the pass runs in a 66 MiB device array
+ * inside the library (each device the library runs on holds its own copy
+ * from the first call until the process ends; the pass needs 65.6 MiB of it
+ * whatever the context length and block size, and a layout that would not
+ * fit returns DFLASH_EWORKSPACE).  The call allocates nothing: on its first
+ * call on a device it only looks up the array's device address.  Same
+ * arguments (minus the workspace), checks, outputs and give-up behaviour as
+ * dflash_draft_block.  Every call on one device shares that device's array:
+ * calls on one device must be ordered on one stream (calls that overlap in
+ * time on one device race and give undefined results). */
+DFLASH_API int32_t dflash_draft_block_static(const dflash_weights* w, const dflash_kv* kv, int64_t p,
+                                  int32_t anchor_id, int32_t mask_id, int32_t block,
+                                  int32_t* cand, void* logits_opt, void* hidden_opt,
+                                  void* stream);
+
 /* One proposal pass with a confidence gate (PR #3322 "support the official
  * Flash-Next DFlash2 checkpoint", section "Long-prompt diagnosis and fix": the
  * spec-min-p probability floor, default 0.5, cut verify rows 133 -> 113; its

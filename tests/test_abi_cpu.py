@@ -293,3 +293,24 @@ def test_packed_copy_may_stand_in_for_row_major_matrices(lib):
     w.layer[2].q_norm = A
     w.embed = None
     assert _lib.dflash_fuse_context(w, A, 0, A, A, big, check=False) == E
+
+
+def test_static_workspace_pass_arguments(lib):
+    """dflash_draft_block_static checks its arguments like dflash_draft_block
+    before it touches a device (no workspace argument)."""
+    w = fake_weights()
+    w.packed = A
+    kv = fake_kv()
+    E = _lib.DFLASH_EINVAL
+    S = _lib.dflash_draft_block_static
+    for block in (0, 9):
+        assert S(w, kv, 100, 1, 2, block, A, None, None, check=False) == E
+    assert S(w, kv, -1, 1, 2, 8, A, None, None, check=False) == E
+    assert S(w, kv, 100, -1, 2, 8, A, None, None, check=False) == E
+    assert S(w, kv, 100, 1, 2, 8, None, None, None, check=False) == E
+    assert S(w, kv, 100, 1, 2, 8, A + 2, None, None, check=False) == E
+    assert S(w, kv, 100, 1, 2, 8, A, A + 8, None, check=False) == E
+    assert S(fake_weights(hidden=4096), kv, 100, 1, 2, 8, A, None, None, check=False) == \
+        _lib.DFLASH_EGEOMETRY
+    assert S(w, fake_kv(1000, 1000), 100, 1, 2, 8, A, None, None, check=False) == \
+        _lib.DFLASH_ERANGE
