@@ -36,18 +36,18 @@ METRIC = "DFlash draft passes/sec (ctx 8192, block 8) + achieved HBM GB/s vs pea
 BYTES_PER_WEIGHT = {"bf16": 2.0, "q8_0": 34 / 32, "q4_0": 18 / 32}
 
 
-def pass_bytes(n_ctx: int, block: int = BLOCK, fmt: str = "bf16") -> int:
+def pass_bytes(n_ctx: int, block: int = BLOCK, fmt: str = "bf16", lm_fmt: str = "bf16") -> int:
     """Algorithmic HBM bytes of one draft pass: every layer matrix (in its
-    storage format) and the bf16 LM head once, the gains, the distinct
-    embedding rows and n_ctx fp16 K/V cells (5 layers x 2 KV heads x 256 x
-    K and V)."""
+    storage format) and the LM head (bf16 or Q8_0) once, the gains, the
+    distinct embedding rows and n_ctx fp16 K/V cells (5 layers x 2 KV heads
+    x 256 x K and V)."""
     from block_draft_model_pass_amd import synth as S
     H, D, F = S.HIDDEN, S.HEAD_DIM, S.FFN
     qkv = (S.N_Q_HEADS + 2 * S.N_KV_HEADS) * D * H
     layer = qkv + H * S.N_Q_HEADS * D + 2 * F * H + H * F
     mats = int(round(BYTES_PER_WEIGHT[fmt] * S.N_LAYERS * layer))
     gains = 2 * (S.N_LAYERS * (2 * H + 2 * D) + H)
-    lm = 2 * S.VOCAB * H if block > 1 else 0
+    lm = int(round(BYTES_PER_WEIGHT[lm_fmt] * S.VOCAB * H)) if block > 1 else 0
     emb = 2 * H * (2 if block > 1 else 1)
     kv = n_ctx * S.N_LAYERS * S.N_KV_HEADS * D * 2 * 2
     return mats + gains + lm + emb + kv
@@ -328,29 +328,38 @@ def main():
 
     # Quantized backbone (Q8_0 / Q4_0 layer matrices, bf16 LM head): draft
     # passes at ctx 8192, block 4, on a context projected by those weights.
-    quant = {}
+    # Also the Q8_0 shared LM head: bf16 backbone at blocks 8 and 4, and with
+    # a Q8_0 backbone at block 4 (every streamed matrix in Q8_0).
+    quant, q8_lm = {}, {}
     if not args.no_quant:
-        for fmt in ("q8_0", "q4_0"):
-            qw = DeviceWeights(synth.make_weights(fmt=fmt))
+        runs = (("q8_0", "bf16", (4,)), ("q4_0", "bf16", (4,)), ("q8_0", "q8_0", (4,)),
+                ("bf16", "q8_0", (8, 4)))
+        for fmt, lmf, blocks in runs:
+            qw = DeviceWeights(synth.make_weights(fmt=fmt, lm_fmt=lmf))
             qkv_ring = KVRing(synth.WINDOW, synth.WINDOW)
             qdr = Drafter(qw, qkv_ring, max_rows=2048)
             for s0 in range(0, CTX, 2048):
                 qdr.commit(to_device(synth.make_taps(range(s0, s0 + 2048))), s0)
-            qb = 4
-            for _ in range(5):
-                qdr.draft(CTX, 11, qb, cand=cand)
-            ev[0].record()
-            for _ in range(args.reps):
-                qdr.draft(CTX, 11, qb, cand=cand)
-            ev[1].record()
-            torch.cuda.synchronize()
-            q_ms = ev[0].elapsed_time(ev[1]) / args.reps
-            q_bytes = pass_bytes(CTX, qb, fmt)
-            q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
-            quant[fmt] = {"ctx": CTX, "block": qb, "ms_per_pass": round(q_ms, 4),
-                          "passes_per_s": round(1e3 / q_ms, 2), "algorithmic_bytes": q_bytes,
-                          "achieved_GBs": round(q_gbs, 1),
-                          "frac_hbm_peak": round(q_gbs / HBM_PEAK_GBS, 4)}
+            for qb in blocks:
+                for _ in range(5):
+                    qdr.draft(CTX, 11, qb, cand=cand)
+                ev[0].record()
+                for _ in range(args.reps):
+                    qdr.draft(CTX, 11, qb, cand=cand)
+                ev[1].record()
+                torch.cuda.synchronize()
+                q_ms = ev[0].elapsed_time(ev[1]) / args.reps
+                q_bytes = pass_bytes(CTX, qb, fmt, lmf)
+                q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
+                rec = {"ctx": CTX, "block": qb, "backbone": fmt, "lm_head": lmf,
+                       "ms_per_pass": round(q_ms, 4),
+                       "passes_per_s": round(1e3 / q_ms, 2), "algorithmic_bytes": q_bytes,
+                       "achieved_GBs": round(q_gbs, 1),
+                       "frac_hbm_peak": round(q_gbs / HBM_PEAK_GBS, 4)}
+                if fmt == "bf16":
+                    q8_lm[f"block{qb}"] = rec
+                else:
+                    quant[fmt if lmf == "bf16" else f"{fmt}+{lmf}_lm_head"] = rec
             del qdr, qkv_ring, qw
             torch.cuda.empty_cache()
 
@@ -427,6 +436,7 @@ def main():
         "short_prompt": short,
         "attainable": attainable,
         "quantized_backbone": quant or None,
+        "q8_0_lm_head": q8_lm or None,
         "accepted_offered": [state["acc"], state["off"]],
         "cpu_baseline": cpu,
     }

@@ -41,6 +41,7 @@ class dflash_weights(ctypes.Structure):
         ("layer", dflash_layer_weights * 5),
         ("final_norm", c_void_p), ("embed", c_void_p), ("lm_head", c_void_p),
         ("packed", c_void_p),
+        ("lm_head_type", c_int32),
     ]
 
 

@@ -133,6 +133,7 @@ int check_weights(const dflash_weights* w, bool need_rowmajor = false) {
   if (w->backbone_type != DFLASH_W_BF16 && w->backbone_type != DFLASH_W_Q8_0 &&
       w->backbone_type != DFLASH_W_Q4_0)
     return DFLASH_EINVAL;
+  if (w->lm_head_type != DFLASH_W_BF16 && w->lm_head_type != DFLASH_W_Q8_0) return DFLASH_EINVAL;
   const bool rm = need_rowmajor || !w->packed;  // row-major matrices required
   if (!w->hidden_norm || !w->final_norm || !w->embed || (rm && (!w->fc || !w->lm_head)))
     return DFLASH_EINVAL;
@@ -181,21 +182,24 @@ size_t layer_bytes(int fmt) {
   return b;
 }
 
+// The LM head's streaming copy comes first, in its own format.
+size_t lm_bytes(const dflash_weights* w) {
+  return mat_bytes(w->lm_head_type, static_cast<size_t>(w->vocab), H);
+}
+
 size_t packed_bytes(const dflash_weights* w) {
-  return sizeof(uint16_t) * static_cast<size_t>(w->vocab) * H + L * layer_bytes(w->backbone_type) +
+  return lm_bytes(w) + L * layer_bytes(w->backbone_type) +
          mat_bytes(w->backbone_type, H, static_cast<size_t>(T) * H);
 }
 
 // Packed copy of fc [2560][12800], after the layers.
 uint8_t* packed_fc(const dflash_weights* w) {
-  return static_cast<uint8_t*>(w->packed) + sizeof(uint16_t) * static_cast<size_t>(w->vocab) * H +
-         L * layer_bytes(w->backbone_type);
+  return static_cast<uint8_t*>(w->packed) + lm_bytes(w) + L * layer_bytes(w->backbone_type);
 }
 
 // Packed copies of layer l's seven matrices, in LAYER_MATS order.
 void packed_layer(const dflash_weights* w, int l, uint8_t* (&out)[7]) {
-  uint8_t* p = static_cast<uint8_t*>(w->packed) + sizeof(uint16_t) * static_cast<size_t>(w->vocab) * H +
-               l * layer_bytes(w->backbone_type);
+  uint8_t* p = static_cast<uint8_t*>(w->packed) + lm_bytes(w) + l * layer_bytes(w->backbone_type);
   for (int i = 0; i < 7; ++i) {
     out[i] = p;
     p += mat_bytes(w->backbone_type, LAYER_MATS[i].N, LAYER_MATS[i].K);
@@ -304,7 +308,7 @@ extern "C" int32_t dflash_pack_weights(const dflash_weights* w, void* stream) {
   if (rc) return rc;
   if (!w->packed) return DFLASH_EINVAL;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  HIP_TRY(launch_pack_bf16(w->lm_head, w->vocab, H, w->packed, st));
+  HIP_TRY(pack_matrix(w->lm_head_type, w->lm_head, w->vocab, H, w->packed, st));
   for (int l = 0; l < L; ++l) {
     const dflash_layer_weights& y = w->layer[l];
     const void* src[7] = {y.wq, y.wk, y.wv, y.wo, y.wg, y.wu, y.wd};
@@ -502,7 +506,8 @@ int32_t draft_block_impl(const dflash_weights* w, const dflash_kv* kv, int64_t p
   }
   q.final_norm = u16p(w->final_norm);
   q.embed = u16p(w->embed);
-  q.lm = u16p(w->packed);  // streaming copy of the LM head
+  q.lm = u16p(w->packed);  // streaming copy of the LM head (bf16 or Q8_0)
+  q.lm_fmt = w->lm_head_type;
   q.vocab = w->vocab;
   q.eps = w->rms_eps;
   q.scale_log2 = w->attn_scale * 1.4426950408889634f;
@@ -600,8 +605,8 @@ extern "C" int32_t dflash_lm_head_argmax(const dflash_weights* w, const void* hi
     return DFLASH_EINVAL;
   const Layout Lw = layout();
   if (ws_bytes < Lw.fixed) return DFLASH_EWORKSPACE;
-  HIP_TRY(launch_lmhead_argmax(w->packed ? u16p(w->packed) : u16p(w->lm_head), w->packed != nullptr,
-                               w->vocab, u16p(hidden), rows,
+  HIP_TRY(launch_lmhead_argmax(w->packed ? w->packed : w->lm_head, w->lm_head_type,
+                               w->packed != nullptr, w->vocab, u16p(hidden), rows,
                                at<uint64_t>(ws, Lw.keys), LMH_GRID,
                                static_cast<uint16_t*>(logits_opt), cand,
                                static_cast<hipStream_t>(stream)));

@@ -210,8 +210,9 @@ hipError_t launch_dequant_bf16(const void* src, int fmt, int rows, int K, uint16
                                bool packed, hipStream_t st);
 
 // LM head + greedy argmax over the vocabulary.
-// lm: row-major [vocab][2560], or its streaming copy when `packed`.
-hipError_t launch_lmhead_argmax(const uint16_t* lm, bool packed, int vocab, const uint16_t* z,
+// lm: [vocab][2560] in format fmt (bf16 or Q8_0 blocks), row-major or its
+// streaming copy when `packed`.
+hipError_t launch_lmhead_argmax(const void* lm, int fmt, bool packed, int vocab, const uint16_t* z,
                                 int B, uint64_t* keys, int grid, uint16_t* logits_opt,
                                 int32_t* cand, hipStream_t st);
 
@@ -242,6 +243,7 @@ hipError_t launch_check_finite(const void* x, int64_t count, int dtype, int32_t*
 // The whole proposal pass as one persistent kernel (plus a small init kernel).
 struct PassLaunch {
   int fmt;                 // WFormat of the layer matrices (bytes behind the pointers)
+  int lm_fmt = W_BF16;     // WFormat of the LM head's streaming copy (bf16 or Q8_0)
   const uint16_t* wq[L];
   const uint16_t* wk[L];
   const uint16_t* wv[L];

@@ -341,6 +341,103 @@ __global__ __launch_bounds__(NW * 64) void k_lmhead_bf16(const uint16_t* lm, int
   }
 }
 
+// Q8_0 LM head: the same sweep as k_lmhead_bf16 over a [vocab][2560] matrix of
+// Q8_0 blocks (row-major quants then scales, or the streaming copy: 64-byte
+// row pieces in MFMA lane order, scales per 16-row tile and piece).  One
+// 16-byte load holds 16 int8 of one quant block (64 k per load over the four
+// lane groups); decoded to fp16 in registers (scale * q, one rounding) and
+// run on MFMA f16 against the activations converted once to fp16.
+template <int NW, int KBW, bool PACKED>
+__device__ __forceinline__ void load_lm_q8(uint4 (&w)[2 * KBW], uint32_t (&sc)[2 * KBW],
+                                           const uint8_t* lm, int vocab, int t, int r, int kbeg,
+                                           int g) {
+  const size_t qbytes = static_cast<size_t>(vocab) * H;
+  const size_t row = static_cast<size_t>(t) * 16 + r;
+#pragma unroll
+  for (int i = 0; i < 2 * KBW; ++i) {
+    if constexpr (PACKED) {
+      const size_t pc = static_cast<size_t>(t) * (H / 64) + kbeg / 64 + i;
+      w[i] = ld16_stream(reinterpret_cast<const uint16_t*>(lm + (pc * 64 + r + 16 * g) * 16));
+      sc[i] = *reinterpret_cast<const uint16_t*>(lm + qbytes + 2 * (pc * 32 + r * 2 + (g >> 1)));
+    } else {
+      const size_t k = static_cast<size_t>(kbeg) + 64 * i + 16 * g;
+      w[i] = ld16_stream(reinterpret_cast<const uint16_t*>(lm + row * H + k));
+      sc[i] = *reinterpret_cast<const uint16_t*>(lm + qbytes + 2 * (row * (H / 32) + k / 32));
+    }
+  }
+}
+
+template <int KBW>
+__device__ __forceinline__ f32x4 mma_chain_q8(const uint4 (&w)[2 * KBW],
+                                              const uint32_t (&sc)[2 * KBW],
+                                              const uint4 (&x)[4 * KBW]) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 2 * KBW; ++i) {
+    const h2 s2 = scale_h2(sc[i]);
+    acc = mfma_f16(dq8(w[i].x, w[i].y, s2), x[2 * i], acc);
+    acc = mfma_f16(dq8(w[i].z, w[i].w, s2), x[2 * i + 1], acc);
+  }
+  return acc;
+}
+
+template <int NW, int KBW, bool PACKED>
+__global__ __launch_bounds__(NW * 64) void k_lmhead_q8(const uint8_t* lm, int ntiles, int vocab,
+                                                       const uint16_t* z, int B, uint64_t* keys,
+                                                       uint16_t* logits) {
+  __shared__ f32x4 red[2][NW - 1][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const bool xv = r < B;
+  const int kbeg = wave * (KBW * 128);
+  uint4 x[4 * KBW];
+  const uint16_t* xrow = z + static_cast<size_t>(xv ? r : 0) * H;
+#pragma unroll
+  for (int i = 0; i < 4 * KBW; ++i)
+    x[i] = xv ? bf16x8_to_f16(ld16(xrow + kbeg + xslot<W_Q8_0>(i, g))) : make_uint4(0, 0, 0, 0);
+  uint64_t best = 0;
+  const int step = gridDim.x;
+  int t = blockIdx.x;
+  uint4 wa[2 * KBW], wb[2 * KBW];
+  uint32_t sa[2 * KBW], sb[2 * KBW];
+  if (t < ntiles) load_lm_q8<NW, KBW, PACKED>(wa, sa, lm, vocab, t, r, kbeg, g);
+  int parity = 0;
+  while (t < ntiles) {
+    const int tn = t + step;
+    if (tn < ntiles) load_lm_q8<NW, KBW, PACKED>(wb, sb, lm, vocab, tn, r, kbeg, g);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc = mma_chain_q8<KBW>(wa, sa, x);
+    if (wave > 0) red[parity][wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 0; w < NW - 1; ++w) acc += red[parity][w][lane];
+      lm_epilogue(acc, t * 16, r, g, xv, vocab, logits, best);
+    }
+    parity ^= 1;
+    t = tn;
+    if (t >= ntiles) break;
+    const int tn2 = t + step;
+    if (tn2 < ntiles) load_lm_q8<NW, KBW, PACKED>(wa, sa, lm, vocab, tn2, r, kbeg, g);
+    __builtin_amdgcn_sched_barrier(0);
+    acc = mma_chain_q8<KBW>(wb, sb, x);
+    if (wave > 0) red[parity][wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 0; w < NW - 1; ++w) acc += red[parity][w][lane];
+      lm_epilogue(acc, t * 16, r, g, xv, vocab, logits, best);
+    }
+    parity ^= 1;
+    t = tn2;
+  }
+  if (wave == 0) {
+    best = umax64(best, shfl_xor_u64(best, 16));
+    best = umax64(best, shfl_xor_u64(best, 32));
+    if (g == 0 && xv) keys[static_cast<size_t>(blockIdx.x) * MAXB + r] = best;
+  }
+}
+
 // cand[b] = index part of the largest key over all blocks; wave b takes row b.
 __global__ __launch_bounds__(MAXB * 64) void k_argmax_reduce(const uint64_t* keys, int nblk,
                                                              int B, int32_t* cand) {
@@ -438,18 +535,28 @@ hipError_t launch_dequant_bf16(const void* src, int fmt, int rows, int K, uint16
   return hipGetLastError();
 }
 
-hipError_t launch_lmhead_argmax(const uint16_t* lm, bool packed, int vocab, const uint16_t* z,
+hipError_t launch_lmhead_argmax(const void* lm, int fmt, bool packed, int vocab, const uint16_t* z,
                                 int B, uint64_t* keys, int grid, uint16_t* logits_opt,
                                 int32_t* cand, hipStream_t st) {
   if (B < 1 || B > MAXB || vocab % 16) return hipErrorInvalidValue;
   const int ntiles = vocab / 16;
   if (grid > ntiles) grid = ntiles;
-  if (packed)
-    hipLaunchKernelGGL((k_lmhead_bf16<4, 5, true>), dim3(grid), dim3(256), 0, st, lm, ntiles, vocab,
+  const uint16_t* l16 = static_cast<const uint16_t*>(lm);
+  const uint8_t* l8 = static_cast<const uint8_t*>(lm);
+  if (fmt == W_BF16 && packed)
+    hipLaunchKernelGGL((k_lmhead_bf16<4, 5, true>), dim3(grid), dim3(256), 0, st, l16, ntiles, vocab,
+                       z, B, keys, logits_opt);
+  else if (fmt == W_BF16)
+    hipLaunchKernelGGL((k_lmhead_bf16<4, 5, false>), dim3(grid), dim3(256), 0, st, l16, ntiles, vocab,
+                       z, B, keys, logits_opt);
+  else if (fmt == W_Q8_0 && packed)
+    hipLaunchKernelGGL((k_lmhead_q8<4, 5, true>), dim3(grid), dim3(256), 0, st, l8, ntiles, vocab,
+                       z, B, keys, logits_opt);
+  else if (fmt == W_Q8_0)
+    hipLaunchKernelGGL((k_lmhead_q8<4, 5, false>), dim3(grid), dim3(256), 0, st, l8, ntiles, vocab,
                        z, B, keys, logits_opt);
   else
-    hipLaunchKernelGGL((k_lmhead_bf16<4, 5, false>), dim3(grid), dim3(256), 0, st, lm, ntiles, vocab,
-                       z, B, keys, logits_opt);
+    return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_argmax_reduce, dim3(1), dim3(MAXB * 64), 0, st, keys, grid, B, cand);

@@ -1321,13 +1321,31 @@ __device__ __forceinline__ void down_phase(const PassArgs& a, Smem& s, int l, Do
 }
 
 // LM head: tile pairs p = w, w + grid, ...; wave v takes tile 2p + v/4 and k
-// quarter v%4.  Activations: final-normed rows 1..B-1 (row b in LDS row b).
-__device__ __forceinline__ void lm_prefetch(const PassArgs& a, int pair, uint4 (&W)[20], bool go) {
+// quarter v%4.  Activations: final-normed rows 1..B-1 (row b in LDS row b),
+// bf16 next to a bf16 LM head, fp16 next to a Q8_0 one (decoded in registers
+// like the quantized layer matrices: one load carries 64 k and its scale).
+template <int LMF> using LmTile = WTile<LMF, 640 / KPerLoad<LMF>::v>;
+
+template <int LMF>
+__device__ __forceinline__ void lm_prefetch(const PassArgs& a, int pair, LmTile<LMF>& W, bool go) {
   const int wave = wid(), lane = otid() & 63;
   const int tile = 2 * pair + (wave >> 2);
   const bool has = tile < a.vocab / 16;
-  load_tile<20>(W, a.lm, H, (has ? tile : 0) * 16 + (lane & 15), (wave & 3) * 640, lane >> 4, 20,
-                go && has);
+  const int row = (has ? tile : 0) * 16 + (lane & 15);
+  if constexpr (LMF == W_BF16) {
+    load_tile<20>(W.q, a.lm, H, row, (wave & 3) * 640, lane >> 4, 20, go && has);
+    W.s[0] = 0u;
+  } else {
+    constexpr int N = 640 / KPerLoad<LMF>::v;
+    load_wt<LMF, N>(W, WMat{a.lm, a.vocab, H}, row, (wave & 3) * 640, lane >> 4, N, go && has);
+  }
+}
+
+template <int LMF>
+__device__ __forceinline__ f32x4 lm_mma(const LmTile<LMF>& W, const uint16_t* xr, int g) {
+  const int kbeg = (wid() & 3) * 640;
+  if constexpr (LMF == W_BF16) return mma_tile<20>(W.q, xr, kbeg, g, 20);
+  else return mma_wt<LMF, 640 / KPerLoad<LMF>::v>(W, xr, kbeg, g, 640 / KPerLoad<LMF>::v);
 }
 
 __device__ __forceinline__ uint64_t umax64(uint64_t x, uint64_t y) { return x > y ? x : y; }
@@ -1367,30 +1385,38 @@ __device__ __forceinline__ void lse_unpack(uint64_t v, float& m, float& s) {
   s = __uint_as_float(static_cast<uint32_t>(v >> 32));
 }
 
-__device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, uint4 (&W)[20]) {
+// hidden_opt rows (bf16) from the final-normed LDS rows: copied when they
+// are bf16, converted when they are fp16 (next to a Q8_0 LM head).
+template <int XF>
+__device__ __forceinline__ void write_hidden(const PassArgs& a, const Smem& s) {
+  constexpr int XS = H + XS_PAD;
+  for (int e = otid(); e < a.B * H; e += NTHR) {
+    const uint16_t v = s.x[(e / H) * XS + (e % H)];
+    a.hidden[e] = XF == W_BF16 ? v : f32_to_bf16(f16_bits_to_f32(v));
+  }
+}
+
+template <int LMF>
+__device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, LmTile<LMF>& W) {
   const int w = blockIdx.x, wave = wid(), lane = otid() & 63;
   const int r = lane & 15, g = lane >> 4;
   const int ntiles = a.vocab / 16, npairs = (ntiles + 1) / 2;
-  build_x_norm<W_BF16>(a, s, 2 * L, np, a.final_norm);
+  build_x_norm<LMF>(a, s, 2 * L, np, a.final_norm);
   constexpr int XS = H + XS_PAD;
-  if (w == 0 && a.hidden) {
-    for (int e = otid(); e < a.B * H; e += NTHR)
-      a.hidden[e] = s.x[(e / H) * XS + (e % H)];
-  }
+  if (w == 0 && a.hidden) write_hidden<LMF>(a, s);
   // mask row r + 1 of the block feeds MFMA column r
   const bool xv = r + 1 < a.B;
   const uint16_t* xr = s.x + (xv ? r + 1 : 1) * XS;
   uint64_t best = 0;
   float lm = -INFINITY, ls = 0.f;  // softmax state of this lane's logits
-  uint4 W2[20];
+  LmTile<LMF> W2;
   int p = w;
   while (p < npairs) {
     // round with W, prefetch into W2
     const int pn = p + gridDim.x;
-    lm_prefetch(a, pn, W2, pn < npairs);
+    lm_prefetch<LMF>(a, pn, W2, pn < npairs);
     const int tile = 2 * p + (wave >> 2);
-    f32x4 acc = tile < ntiles ? mma_tile<20>(W, xr, (wave & 3) * 640, g, 20)
-                              : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc = tile < ntiles ? lm_mma<LMF>(W, xr, g) : f32x4{0.f, 0.f, 0.f, 0.f};
     s.red[wave][lane] = acc;
     lds_sync();
     if ((wave & 3) == 0 && tile < ntiles) {
@@ -1418,10 +1444,9 @@ __device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, uin
     if (p >= npairs) break;
     // round with W2, prefetch into W
     const int pn2 = p + gridDim.x;
-    lm_prefetch(a, pn2, W, pn2 < npairs);
+    lm_prefetch<LMF>(a, pn2, W, pn2 < npairs);
     const int tile2 = 2 * p + (wave >> 2);
-    acc = tile2 < ntiles ? mma_tile<20>(W2, xr, (wave & 3) * 640, g, 20)
-                         : f32x4{0.f, 0.f, 0.f, 0.f};
+    acc = tile2 < ntiles ? lm_mma<LMF>(W2, xr, g) : f32x4{0.f, 0.f, 0.f, 0.f};
     s.red[wave][lane] = acc;
     lds_sync();
     if ((wave & 3) == 0 && tile2 < ntiles) {
@@ -1515,13 +1540,13 @@ __device__ __forceinline__ void argmax_final(const PassArgs& a, Smem& s) {
   }
 }
 
-template <int FMT>
+template <int FMT, int LMF>
 __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
   __shared__ Smem s;
   const bool pre = wid() != 0;  // waves other than 0 prefetch before barriers
   BarState bk;      // barriers passed, give-up flag
   QkvTile<FMT> Wq;
-  uint4 Wl[20];     // LM head (bf16) slice, prefetched after the last layer
+  LmTile<LMF> Wl;   // LM head slice, prefetched after the last layer
   // Layer 0 QKV weights stream while the grid lines up.
   qkv_prefetch<FMT>(a, 0, Wq, pre);
   // h, ss, the RoPE table and the layer table come from the init kernel
@@ -1551,15 +1576,15 @@ __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
     // idle), so neither carries a value around the loop.
     const bool last = l + 1 == L;
     qkv_prefetch<FMT>(a, last ? l : l + 1, Wq, pre && !last);
-    lm_prefetch(a, blockIdx.x, Wl, pre && last && a.B > 1);
+    lm_prefetch<LMF>(a, blockIdx.x, Wl, pre && last && a.B > 1);
     grid_sync_pf(a, bk, [&] {
       qkv_prefetch<FMT>(a, last ? l : l + 1, Wq, !last);
-      lm_prefetch(a, blockIdx.x, Wl, last && a.B > 1);
+      lm_prefetch<LMF>(a, blockIdx.x, Wl, last && a.B > 1);
     });
     np = NT_H;
   }
   if (a.B > 1) {
-    lm_phase(a, s, np, Wl);
+    lm_phase<LMF>(a, s, np, Wl);
     grid_sync(a, bk);
     argmax_final(a, s);
   } else if (blockIdx.x == 0 && a.hidden) {
@@ -1621,6 +1646,22 @@ size_t pass_bar_bytes() { return sizeof(unsigned) * BAR_WORDS; }
 size_t pass_po_bytes() { return sizeof(uint16_t) * L * POSTRIDE; }
 size_t pass_pml_bytes() { return sizeof(float) * L * PMSTRIDE; }
 
+namespace {
+// The pass kernel for a backbone format and an LM-head format.
+const void* pass_kernel(int fmt, int lm_fmt) {
+  if (lm_fmt == W_BF16) {
+    if (fmt == W_BF16) return reinterpret_cast<const void*>(k_draft_pass<W_BF16, W_BF16>);
+    if (fmt == W_Q8_0) return reinterpret_cast<const void*>(k_draft_pass<W_Q8_0, W_BF16>);
+    if (fmt == W_Q4_0) return reinterpret_cast<const void*>(k_draft_pass<W_Q4_0, W_BF16>);
+  } else if (lm_fmt == W_Q8_0) {
+    if (fmt == W_BF16) return reinterpret_cast<const void*>(k_draft_pass<W_BF16, W_Q8_0>);
+    if (fmt == W_Q8_0) return reinterpret_cast<const void*>(k_draft_pass<W_Q8_0, W_Q8_0>);
+    if (fmt == W_Q4_0) return reinterpret_cast<const void*>(k_draft_pass<W_Q4_0, W_Q8_0>);
+  }
+  return nullptr;
+}
+}  // namespace
+
 hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
   LayerTab tab;
   for (int l = 0; l < L; ++l) {
@@ -1675,7 +1716,8 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
   a.logits = q.logits;
   a.hidden = q.hidden;
   // every phase assumes at least one block per work item of its first round
-  if (q.fmt < W_BF16 || q.fmt > W_Q4_0) return hipErrorInvalidValue;
+  if (q.fmt < W_BF16 || q.fmt > W_Q4_0 || (q.lm_fmt != W_BF16 && q.lm_fmt != W_Q8_0))
+    return hipErrorInvalidValue;
   if (q.nch < 1 || q.nch > 128 || q.grid < NKV * q.nch || q.grid < QKV_N / 32 ||
       q.grid < NKV * a.nqt * 16 || q.grid > 1024)
     return hipErrorInvalidValue;
@@ -1684,9 +1726,8 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
                      q.h, q.h16, q.ss, q.rope, q.bar);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const void* kern = q.fmt == W_Q8_0   ? reinterpret_cast<const void*>(k_draft_pass<W_Q8_0>)
-                     : q.fmt == W_Q4_0 ? reinterpret_cast<const void*>(k_draft_pass<W_Q4_0>)
-                                       : reinterpret_cast<const void*>(k_draft_pass<W_BF16>);
+  const void* kern = pass_kernel(q.fmt, q.lm_fmt);
+  if (!kern) return hipErrorInvalidValue;
   void* args[] = {&a};
   // A plain launch: the grid is at most one block per CU, the most the device
   // holds at once (draft_pass_max_grid), so every block is resident as soon
@@ -1716,14 +1757,13 @@ hipError_t draft_pass_max_grid(int device, int* grid) {
   hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
   if (e != hipSuccess) return e;
   // one block per CU for every weight format's instantiation
-  const void* kerns[3] = {reinterpret_cast<const void*>(k_draft_pass<W_BF16>),
-                          reinterpret_cast<const void*>(k_draft_pass<W_Q8_0>),
-                          reinterpret_cast<const void*>(k_draft_pass<W_Q4_0>)};
   int ok = 1;
-  for (const void* k : kerns) {
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k, NTHR, 0);
-    if (e != hipSuccess) return e;
-    ok = ok && per > 0;
+  for (int f = W_BF16; f <= W_Q4_0; ++f) {
+    for (int lf : {static_cast<int>(W_BF16), static_cast<int>(W_Q8_0)}) {
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, pass_kernel(f, lf), NTHR, 0);
+      if (e != hipSuccess) return e;
+      ok = ok && per > 0;
+    }
   }
   *grid = ok ? cus : 0;
   return hipSuccess;

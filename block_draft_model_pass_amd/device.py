@@ -58,6 +58,8 @@ class DeviceWeights:
         d.vocab, d.n_taps = self.t["embed"].shape[0], synth.N_TAPS
         d.rope_theta, d.attn_scale, d.rms_eps = synth.ROPE_THETA, synth.ATTN_SCALE, synth.RMS_EPS
         d.backbone_type = _FORMATS[self.format]
+        self.lm_format = host.get("__lm_format__", "bf16")
+        d.lm_head_type = _FORMATS[self.lm_format]
         d.fc = self.t["fc"].data_ptr()
         d.hidden_norm = self.t["hidden_norm"].data_ptr()
         for l in range(synth.N_LAYERS):

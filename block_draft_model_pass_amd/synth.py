@@ -164,27 +164,30 @@ def quantize_q4_0(w: np.ndarray) -> np.ndarray:
 
 
 def make_weights(seed: int = SEED_WEIGHTS, fmt: str = "bf16",
-                 geom: dict | None = None) -> dict:
+                 geom: dict | None = None, lm_fmt: str = "bf16") -> dict:
     """All drafter tensors, the embedding and the LM head, keyed by name.
 
     bf16 tensors are uint16 bit patterns of their shape.  With fmt 'q8_0' or
     'q4_0' the 36 backbone matrices (fc and the 35 layer matrices) are flat
-    uint8 buffers in the layout described in the module docstring; gains,
-    embedding and LM head stay bf16."""
-    assert fmt in ("bf16", "q8_0", "q4_0")
+    uint8 buffers in the layout described in the module docstring; gains and
+    the embedding stay bf16.  lm_fmt 'q8_0' stores the LM head as Q8_0 blocks
+    (same draws, quantized) in the same layout."""
+    assert fmt in ("bf16", "q8_0", "q4_0") and lm_fmt in ("bf16", "q8_0")
     out = {}
     for ti, (name, shape, kind) in enumerate(weight_specs(geom)):
         words = (seed, ti)
+        qfmt = lm_fmt if name == "lm_head" else (fmt if kind == "matrix" else "bf16")
         if kind == "gain":
             out[name] = _bf16_normal(words, shape, 0.02, 1.0)
-        elif kind == "table" or fmt == "bf16":
+        elif qfmt == "bf16":
             out[name] = _bf16_normal(words, shape, 0.02)
         else:
             v = _normal_f32(words, int(np.prod(shape)), 0.02, 0.0)
             v = v.reshape(shape)
-            out[name] = (quantize_q8_0(v) if fmt == "q8_0"
+            out[name] = (quantize_q8_0(v) if qfmt == "q8_0"
                          else quantize_q4_0(v))
     out["__format__"] = fmt
+    out["__lm_format__"] = lm_fmt
     return out
 
 

@@ -86,7 +86,8 @@ extern "C" {
  *   Q4_0: N*K/2 bytes (row-major, 16 bytes per block: element j of a block in
  *         the low nibble of byte j, element j+16 in the high nibble), then
  *         N*K/32 fp16 scales; weight = scale * (nibble - 8).
- * Gains, the embedding and the LM head are always bf16. */
+ * Gains and the embedding are always bf16; the LM head is bf16 or Q8_0
+ * (lm_head_type). */
 typedef enum {
   DFLASH_W_BF16 = 0,
   DFLASH_W_Q8_0 = 1,
@@ -133,6 +134,17 @@ typedef struct {
    * their own pointers.  Without it, the row-major matrices are required and
    * read directly.  Caller-owned, like everything else. */
   void* packed;
+  /* Storage format of lm_head (PR #3322 later snapshot, "How to enable the
+   * pushed optimization options": a shared LM head in Q8_0):
+   * DFLASH_W_BF16 (0) or DFLASH_W_Q8_0 -- blocks of 32 consecutive input-dim
+   * weights of one vocabulary row with an fp16 scale, stored like the Q8_0
+   * backbone (vocab*2560 int8 row-major, then vocab*80 fp16 scales).  The
+   * embedding stays bf16 (a Q8_0 LM head is never tied to it).  With Q8_0
+   * the pass and dflash_lm_head_argmax decode the blocks in registers and
+   * take the contraction in fp16 x fp16 -> fp32; logits, argmax and the
+   * confidence gate are otherwise unchanged.  Appended after `packed` so the
+   * fields above keep their offsets. */
+  int32_t lm_head_type;
 } dflash_weights;
 
 /* Drafter-owned context K/V ("Owned DFlash K/V state": fp16, one state per
@@ -158,10 +170,11 @@ typedef struct {
 DFLASH_API size_t dflash_workspace_size(const dflash_weights* w, int32_t max_rows,
                              int32_t max_block);
 
-/* Bytes of the streaming copies: 2 * vocab * 2560 for the LM head plus the
- * 35 layer matrices (5 x (6144*2560 + 2*512*2560 + 2560*6144 + 2*7680*2560 +
- * 2560*7680) weights) and fc (2560*12800 weights) at 2 (bf16), 34/32 (Q8_0)
- * or 18/32 (Q4_0) bytes per weight.  0 for an invalid descriptor. */
+/* Bytes of the streaming copies: vocab * 2560 LM-head weights at 2 (bf16) or
+ * 34/32 (Q8_0) bytes each, plus the 35 layer matrices (5 x (6144*2560 +
+ * 2*512*2560 + 2560*6144 + 2*7680*2560 + 2560*7680) weights) and fc
+ * (2560*12800 weights) at 2 (bf16), 34/32 (Q8_0) or 18/32 (Q4_0) bytes per
+ * weight.  0 for an invalid descriptor. */
 DFLASH_API size_t dflash_packed_size(const dflash_weights* w);
 
 /* Writes the streaming copies into w->packed, enqueued on `stream`.  A bf16
@@ -171,7 +184,7 @@ DFLASH_API size_t dflash_packed_size(const dflash_weights* w);
  * 64-lane load of the draft pass reads 1 KiB of contiguous memory instead of
  * 64 bytes from each of 16 rows.  Element (n, k) sits at
  * ((n/16 * K/32 + k/32) * 64 + n%16 + 16 * ((k%32)/8)) * 8 + k%8.
- * Order in the buffer: lm_head [vocab][2560]; then for each layer 0..4:
+ * Order in the buffer: lm_head [vocab][2560] (in lm_head_type); then for each layer 0..4:
  * wq [6144][2560], wk [512][2560], wv [512][2560], wo [2560][6144],
  * wg [7680][2560], wu [7680][2560], wd [2560][7680]; then fc [2560][12800].
  * A Q8_0 / Q4_0 matrix

@@ -110,9 +110,19 @@ def dequant_q4_0(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
     return ((nib - 8.0) * d).reshape(rows, cols)
 
 
+def storage_format(w: dict, name: str) -> str:
+    """Format of a stored matrix: the LM head has its own (bf16, or Q8_0 for
+    the shared quantized head of PR #3322's later snapshot, "How to enable
+    the pushed optimization options"); every other matrix has the
+    backbone's."""
+    if name == "lm_head":
+        return w.get("__lm_format__", "bf16")
+    return w.get("__format__", "bf16")
+
+
 def matrix(w: dict, name: str, shape) -> np.ndarray:
     """A weight matrix [out][in] as float64, whatever its stored format."""
-    fmt = w.get("__format__", "bf16")
+    fmt = storage_format(w, name)
     a = w[name]
     if a.dtype == np.uint16:
         return bf16_decode(a).reshape(shape)

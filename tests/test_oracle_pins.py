@@ -487,6 +487,36 @@ def test_block_attention_is_non_causal():
     assert not np.allclose(r["hidden"][1], base["hidden"][1])
 
 
+def test_q8_0_lm_head_logits_closed_form():
+    """A Q8_0 LM head (hidden 32, one quant block per vocabulary row): with
+    the attention and MLP branches zeroed the hidden state is the final norm
+    of the embedding row, here the constant 1/sqrt(1 + eps), so logit v is
+    d_v * sum_j q_vj / sqrt(1 + eps).  Pins that the LM head's own format
+    is used (not the backbone's), the int8 sign and the fp16 scale."""
+    G = O.geometry(hidden=32, n_layers=1, n_q_heads=2, n_kv_heads=1, head_dim=4,
+                   ffn=8, vocab=5, window=4)
+    rng = np.random.default_rng(31)
+    w = {"__format__": "bf16", "__lm_format__": "q8_0"}
+    for name, shape, kind in synth.weight_specs(G):
+        if kind == "gain":
+            w[name] = b16(np.ones(shape, dtype=np.float32))
+        elif name in ("layers.0.wo", "layers.0.wd"):
+            w[name] = b16(np.zeros(shape, dtype=np.float32))
+        else:
+            w[name] = b16(rng.integers(-8, 9, size=shape).astype(np.float32) / 16)
+    w["embed"] = b16(np.ones((5, 32), dtype=np.float32))
+    q = rng.integers(-127, 128, size=(5, 32)).astype(np.int8)
+    q[3] = 127                       # the largest row sum
+    q[1] = -127
+    d = np.array([0.5, 0.25, 2.0 ** -6, 0.125, 1.5], dtype=np.float16)
+    w["lm_head"] = np.concatenate([q.reshape(-1).view(np.uint8), d.view(np.uint8)])
+    z = np.zeros((1, 1, 0, 4))
+    r = O.draft_block(w, z, z, p=0, anchor_id=2, mask_id=4, block=3, g=G)
+    want = d.astype(np.float64) * q.astype(np.float64).sum(axis=1) / math.sqrt(1 + 1e-6)
+    assert np.allclose(r["logits"], np.tile(want, (2, 1)), rtol=1e-12)
+    assert list(r["cand"]) == [int(np.argmax(want))] * 2
+
+
 # ------------------------------------------------------------ q/k path
 # Pins in which a score depends on the query's norm, gain and position and on
 # the block keys' rotation (PR #1426 "Drafter runtime": per-head q/k RMSNorm
