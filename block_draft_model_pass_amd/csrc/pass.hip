@@ -14,8 +14,10 @@
 //   then:      LM head + greedy argmax -> final reduction by block 0
 //
 // Weights never depend on activations, so every wave issues the loads of its
-// next weight slice *before* it waits at a barrier; HBM keeps streaming while
-// the grid synchronises and while activations are rebuilt in LDS.
+// next weight slice while its block waits at a barrier (right after the
+// block's arrival, so that a full load queue never delays the arrival); HBM
+// keeps streaming while the grid synchronises and while activations are
+// rebuilt in LDS.
 //
 // The L2 caches of the eight XCDs are not coherent with each other, and an
 // agent-scope fence (L2 writeback or invalidate) costs about 2 us per
@@ -261,11 +263,15 @@ struct BarState {
   bool quit = false;
 };
 
-// Grid barrier whose waiting wave (wave 0) issues its share of the next
-// phase's weight loads between its arrival and its polling: its arrival
-// atomics go out ahead of those loads, while its loads still stream during
-// the wait.  (A wave's loads complete in order, so a prefetch issued before
-// the arrival would hold the arrival back by the prefetch's latency.)
+// Grid barrier during which every wave issues its share of the next phase's
+// weight loads (`prefetch`), after thread 0's arrival atomics (and, for the
+// last arrival, the release): an s_barrier holds waves 1..7 until then.  The
+// arrival atomics thus never queue behind the prefetch -- a wave's loads
+// complete in order, and a CU whose load queue is full stalls further issue
+// -- while the loads still stream during the wait.  (Issuing the prefetch of
+// waves 1..7 before the arrival instead delayed arrivals by their issue
+// stalls: measured 467 -> 445 us per pass at ctx 8192, block 8, with every
+// barrier contributing.)
 //
 // The wait is bounded in wall-clock time (the constant-rate counter read by
 // s_memrealtime): a wait longer than a.wait_ticks (plus 16 polls) sets the
@@ -274,7 +280,7 @@ struct BarState {
 // blocks cannot all be resident ends after about one bound instead of
 // hanging the stream.
 template <class Pf>
-__device__ __forceinline__ void grid_sync_pf(const PassArgs& a, BarState& b, Pf&& wave0_prefetch) {
+__device__ __forceinline__ void grid_sync_pf(const PassArgs& a, BarState& b, Pf&& prefetch) {
   lds_sync();
   const unsigned k = ++b.k;
   const unsigned goal = k * (gridDim.x < 8 ? gridDim.x : 8);
@@ -294,7 +300,8 @@ __device__ __forceinline__ void grid_sync_pf(const PassArgs& a, BarState& b, Pf&
       wait = false;
     }
   }
-  if (wid() == 0) wave0_prefetch();
+  __builtin_amdgcn_s_barrier();  // thread 0's arrival has gone out
+  prefetch();
   if (otid() == 0 && wait && !b.quit) {
     // The clock and the status word are read every 16 and 64 polls only (a
     // counter read per poll would delay seeing the release); the clock starts
@@ -1276,14 +1283,13 @@ __device__ __forceinline__ void down_range(int wave, int& kbeg, int& klen) {
 template <int FMT>
 using DownTile = WTile<FMT, (FMT == W_Q4_0 ? 1024 : F / NWAVE) / KPerLoad<FMT>::v>;
 
-// Down projection tile w for blocks w < 160.  Only waves 1..DOWN_PRE_LAST
-// prefetch their k range during the gate/up phase (which those blocks spend
-// streaming two gate/up tile pairs): a full prefetch would lengthen that
-// phase by as much as it shortens this one.  Wave 0 loads its range while it
-// waits at the barrier, the others after it.
+// Down projection tile w for blocks w < 160.  Only waves 0..DOWN_PRE_LAST
+// load their k range at the barrier that ends the gate/up phase (which those
+// blocks spend streaming two gate/up tile pairs); the others load theirs at
+// the start of the phase, behind the activations.
 constexpr int DOWN_PRE_LAST = 3;
 
-__device__ __forceinline__ bool down_pre(int wave) { return wave >= 1 && wave <= DOWN_PRE_LAST; }
+__device__ __forceinline__ bool down_pre(int wave) { return wave <= DOWN_PRE_LAST; }
 
 template <int FMT>
 __device__ __forceinline__ void down_prefetch(const PassArgs& a, int l, DownTile<FMT>& W, bool go) {
@@ -1543,40 +1549,32 @@ __device__ __forceinline__ void argmax_final(const PassArgs& a, Smem& s) {
 template <int FMT, int LMF>
 __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
   __shared__ Smem s;
-  const bool pre = wid() != 0;  // waves other than 0 prefetch before barriers
   BarState bk;      // barriers passed, give-up flag
   QkvTile<FMT> Wq;
   LmTile<LMF> Wl;   // LM head slice, prefetched after the last layer
-  // Layer 0 QKV weights stream while the grid lines up.
-  qkv_prefetch<FMT>(a, 0, Wq, pre);
-  // h, ss, the RoPE table and the layer table come from the init kernel
+  // Layer 0 QKV weights stream while the grid lines up; h, ss, the RoPE
+  // table and the layer table come from the init kernel.
   grid_sync_pf(a, bk, [&] { qkv_prefetch<FMT>(a, 0, Wq, true); });
   int np = 1;    // sums of squares of h: one entry per row from the init kernel
   for (int l = 0; l < L; ++l) {
     qkv_phase<FMT>(a, s, l, np, Wq);
     KVRegs R0, R1;
-    attn_prefetch(a, l, R0, R1, pre);
     grid_sync_pf(a, bk, [&] { attn_prefetch(a, l, R0, R1, true); });
     attn_phase(a, s, l, R0, R1);
     grid_sync(a, bk);
     merge_phase<FMT>(a, s, l);
     OTile<FMT> Wo;
-    o_prefetch<FMT>(a, l, Wo, pre);
     grid_sync_pf(a, bk, [&] { o_prefetch<FMT>(a, l, Wo, true); });
     o_phase<FMT>(a, s, l, Wo);
     GuTile<FMT> Wg;
-    gu_prefetch<FMT>(a, l, blockIdx.x, Wg, pre);
     grid_sync_pf(a, bk, [&] { gu_prefetch<FMT>(a, l, blockIdx.x, Wg, true); });
     gu_phase<FMT>(a, s, l, NT_H, Wg);
     DownTile<FMT> Wd;
-    down_prefetch<FMT>(a, l, Wd, down_pre(wid()));
-    grid_sync_pf(a, bk, [&] { down_prefetch<FMT>(a, l, Wd, true); });
+    grid_sync_pf(a, bk, [&] { down_prefetch<FMT>(a, l, Wd, down_pre(wid())); });
     down_phase<FMT>(a, s, l, Wd);
     // Both prefetch targets are assigned on every iteration (zeros when
     // idle), so neither carries a value around the loop.
     const bool last = l + 1 == L;
-    qkv_prefetch<FMT>(a, last ? l : l + 1, Wq, pre && !last);
-    lm_prefetch<LMF>(a, blockIdx.x, Wl, pre && last && a.B > 1);
     grid_sync_pf(a, bk, [&] {
       qkv_prefetch<FMT>(a, last ? l : l + 1, Wq, !last);
       lm_prefetch<LMF>(a, blockIdx.x, Wl, last && a.B > 1);
