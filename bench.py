@@ -5,8 +5,10 @@ Workload (one step = one decode cycle): 8192 resident context cells, a block
 of anchor + 7 masks (block 8) drafted at the next position, greedy
 verification against a seeded stand-in target that agrees with each
 candidate with probability 0.75, and the commit (fusion + K/V projection) of
-the accepted cells plus the anchor.  Jobs of 96 committed tokens restart at
-position 8192 (position-addressed cells make rejected drafts harmless).
+the accepted cells plus the anchor -- done by the next cycle's pass
+(dflash_draft_block_commit: one launch commits and drafts).  Jobs of 96
+committed tokens restart at position 8192 (position-addressed cells make
+rejected drafts harmless).
 
 Prints one JSON line.  Inputs are resident in HBM before timing starts.
 """
@@ -169,34 +171,51 @@ def main():
     out = torch.empty(2, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
 
-    state = {"p": CTX, "anchor": synth.anchor_token(0), "job": 0, "acc": 0, "off": 0}
+    def run_cycles(fused: bool):
+        """W warm-up then K timed decode cycles; returns (seconds, accepted,
+        offered).  Fused: one dflash_draft_block_commit per cycle commits the
+        previous cycle's accepted cells and drafts the next block; otherwise
+        draft, then the commit as its own fuse + project calls."""
+        st = {"p": CTX, "anchor": synth.anchor_token(0), "job": 0, "acc": 0, "off": 0, "n": 0}
 
-    def cycle(t):
-        dr.draft(state["p"], state["anchor"], BLOCK, cand=cand)
-        # stand-in target: the candidate where the draw matched, else another id
-        tgt = tgt_all[t]
-        torch.where(match[t], cand, torch.remainder(cand + offset[t], V), out=tgt[:K])
-        dr.verify(cand, tgt, K, out=out)
-        a, nxt = out.tolist()  # the cycle's one device->host read
-        p = state["p"]
-        dr.commit_ptr(taps_ptr + p * tap_row_bytes, a + 1, p)
-        state["acc"] += a
-        state["off"] += K
-        state["p"], state["anchor"] = p + a + 1, nxt
-        if state["p"] - CTX >= JOB_TOKENS:
-            state["job"] += 1
-            state["p"], state["anchor"] = CTX, synth.anchor_token(state["job"])
+        def cycle(t):
+            p = st["p"]
+            if fused:
+                n = st["n"]
+                dr.draft_commit(taps_ptr + (p - n) * tap_row_bytes if n else None, n, p,
+                                st["anchor"], BLOCK, cand=cand)
+            else:
+                dr.draft(p, st["anchor"], BLOCK, cand=cand)
+            # stand-in target: the candidate where the draw matched, else another id
+            tgt = tgt_all[t]
+            torch.where(match[t], cand, torch.remainder(cand + offset[t], V), out=tgt[:K])
+            dr.verify(cand, tgt, K, out=out)
+            a, nxt = out.tolist()  # the cycle's one device->host read
+            if fused:
+                st["n"] = a + 1  # committed by the next cycle's pass
+            else:
+                dr.commit_ptr(taps_ptr + p * tap_row_bytes, a + 1, p)
+            st["acc"] += a
+            st["off"] += K
+            st["p"], st["anchor"] = p + a + 1, nxt
+            if st["p"] - CTX >= JOB_TOKENS:
+                st["job"] += 1
+                st["p"], st["anchor"], st["n"] = CTX, synth.anchor_token(st["job"]), 0
 
-    for t in range(args.warmup):
-        cycle(t)
-    state["acc"] = state["off"] = 0
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for t in range(args.warmup, n_pass):
-        cycle(t)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
+        for t in range(args.warmup):
+            cycle(t)
+        st["acc"] = st["off"] = 0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(args.warmup, n_pass):
+            cycle(t)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, st["acc"], st["off"]
+
+    dt_unfused, _, _ = run_cycles(False)
+    dt, acc, off = run_cycles(True)
     value = args.steps / dt
+    state = {"acc": acc, "off": off}
 
     # Draft pass alone, back to back at ctx 8192 (HIP events on the stream):
     # the median of 5 repeats of `reps` passes after 20 warm-up passes.
@@ -407,8 +426,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": "DFlash decode cycle: 8192 resident context cells, block 8 "
                                "(anchor + 7 masks), greedy verify vs Bernoulli(0.75) stand-in "
-                               "target, commit of accepted cells; 96-token jobs",
+                               "target; the accepted cells are committed by the next cycle's "
+                               "pass (dflash_draft_block_commit); 96-token jobs",
                    "ctx": CTX, "block": BLOCK, "vocab": V, "backbone": "bf16"},
+        "decode_cycle_unfused": {"ms_per_cycle": round(1e3 * dt_unfused / args.steps, 4),
+                                 "cycles_per_s": round(args.steps / dt_unfused, 3),
+                                 "note": "draft, verify, then the commit as separate fuse + "
+                                         "project calls"},
         "draft_only": {"ms_per_pass": round(draft_ms, 4),
                        "ms_range_of_5_repeats": [round(min(rep_ms), 4), round(max(rep_ms), 4)],
                        "passes_per_s": round(1e3 / draft_ms, 2),

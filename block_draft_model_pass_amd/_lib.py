@@ -89,6 +89,11 @@ def load() -> ctypes.CDLL:
                                        c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_size_t, c_void_p]
     lib.dflash_draft_block.restype = c_int32
+    lib.dflash_draft_block_commit.argtypes = [P(dflash_weights), P(dflash_kv), c_void_p,
+                                              c_int32, c_int64, c_int32, c_int32, c_int32,
+                                              c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                              c_void_p]
+    lib.dflash_draft_block_commit.restype = c_int32
     lib.dflash_draft_block_static.argtypes = [P(dflash_weights), P(dflash_kv), c_int64,
                                               c_int32, c_int32, c_int32, c_void_p, c_void_p,
                                               c_void_p, c_void_p]
@@ -199,3 +204,11 @@ def dflash_draft_block_static(w, kv, p, anchor_id, mask_id, block, cand, logits_
     rc = load().dflash_draft_block_static(_ref(w), _ref(kv), p, anchor_id, mask_id, block, cand,
                                           logits_opt, hidden_opt, stream)
     return _check(rc, "dflash_draft_block_static") if check else rc
+
+
+def dflash_draft_block_commit(w, kv, taps, n_commit, p, anchor_id, mask_id, block, cand,
+                              logits_opt, hidden_opt, ws, ws_bytes, stream=None, check=True):
+    rc = load().dflash_draft_block_commit(_ref(w), _ref(kv), taps, n_commit, p, anchor_id,
+                                          mask_id, block, cand, logits_opt, hidden_opt, ws,
+                                          ws_bytes, stream)
+    return _check(rc, "dflash_draft_block_commit") if check else rc

@@ -63,7 +63,7 @@ static_assert(static_cast<size_t>(KV_SPLITS) * GEMV_ROWS * KV_N <= PART_FLOATS,
               "the Wk / Wv partials share the fc partials' workspace");
 
 struct Layout {
-  size_t part, po, pm, pl, keys, lse, rope, ss, qkv, hv, h16, ov, uv, bar, tab, y;
+  size_t part, po, pm, pl, keys, lse, rope, ss, qkv, hv, h16, ov, uv, bar, tab, yc, ckv, y;
   size_t fixed;  // bytes before y
 };
 
@@ -82,7 +82,7 @@ Layout layout() {
   L.pl = take(off, pass_pml_bytes());
   L.keys = take(off, sizeof(uint64_t) * KEYS_MAX * MAXB);
   L.lse = take(off, sizeof(uint64_t) * KEYS_MAX * MAXB);
-  L.rope = take(off, sizeof(float) * 2 * MAXB * (D / 2));
+  L.rope = take(off, sizeof(float) * 2 * (2 * MAXB) * (D / 2));  // block rows, commit rows
   // per-layer / per-version copies used by the persistent pass
   constexpr size_t HV = 2 * dfl::L + 1, NL = dfl::L;
   L.ss = take(off, sizeof(float) * HV * (H / 16) * MAXB);
@@ -93,6 +93,9 @@ Layout layout() {
   L.uv = take(off, 2 * NL * MAXB * F);
   L.bar = take(off, pass_bar_bytes());
   L.tab = take(off, pass_tab_bytes());
+  // commit rows of the fused draft-commit cycle: fc outputs, raw K | V
+  L.yc = take(off, sizeof(float) * MAXB * H);
+  L.ckv = take(off, sizeof(float) * dfl::L * MAXB * 2 * NKV * D);
   L.fixed = off;
   L.y = off;
   return L;
@@ -460,16 +463,19 @@ namespace {
 // nkeep null for the former).
 // static_ws: the workspace is the library's device array (ws and ws_bytes
 // ignored), resolved after the arguments are checked.
+// taps / nc: commit rows of the fused draft-commit cycle (nc = 0: none),
+// at positions p - nc .. p - 1.
 int32_t draft_block_impl(const dflash_weights* w, const dflash_kv* kv, int64_t p,
                          int32_t anchor_id, int32_t mask_id, int32_t block, int32_t* cand,
                          float* conf, int32_t* nkeep, float min_p, void* logits_opt,
                          void* hidden_opt, void* ws, size_t ws_bytes, void* stream,
-                         bool static_ws = false) {
+                         bool static_ws = false, const void* taps = nullptr, int32_t nc = 0) {
   int rc = check_weights(w);
   if (rc) return rc;
   rc = check_kv(kv);
   if (rc) return rc;
   if (block < 1 || block > MAXB || p < 0) return DFLASH_EINVAL;
+  if (nc < 0 || nc > MAXB || p < nc || (nc > 0 && (!taps || !a16(taps)))) return DFLASH_EINVAL;
   if (anchor_id < 0 || anchor_id >= w->vocab || mask_id < 0 || mask_id >= w->vocab)
     return DFLASH_EINVAL;
   if ((!ws && !static_ws) || (block > 1 && !cand)) return DFLASH_EINVAL;
@@ -518,12 +524,14 @@ int32_t draft_block_impl(const dflash_weights* w, const dflash_kv* kv, int64_t p
   // Attention split over the visible context [lo, p): one block per (KV head,
   // chunk of cb 32-cell blocks), at most min(grid / 2, 128) chunks per head;
   // the last chunk of each head also takes the block rows.
+  // Commit rows (positions p-nc .. p-1) are attended to from the workspace:
+  // the ring is read at [lo, p - nc).
   q.lo = p - kv->window > 0 ? p - kv->window : 0;
-  q.hi = p;
-  if (p > q.lo) {
+  q.hi = p - nc;
+  if (q.hi > q.lo) {
     const int maxch = grid / 2 < 128 ? grid / 2 : 128;
     q.p0 = q.lo & ~static_cast<int64_t>(31);
-    q.nb = static_cast<int>((p - q.p0 + 31) / 32);
+    q.nb = static_cast<int>((q.hi - q.p0 + 31) / 32);
     q.cb = (q.nb + maxch - 1) / maxch;
     q.nch = (q.nb + q.cb - 1) / q.cb;
   } else {
@@ -560,6 +568,13 @@ int32_t draft_block_impl(const dflash_weights* w, const dflash_kv* kv, int64_t p
   q.conf = conf;
   q.nkeep = nkeep;
   q.min_p = min_p;
+  q.nc = nc;
+  q.pos0 = p - nc;
+  q.taps = static_cast<const uint16_t*>(taps);
+  q.fc = packed_fc(w);
+  q.hidden_norm = u16p(w->hidden_norm);
+  q.yc = at<float>(ws, Lw.yc);
+  q.ckv = at<float>(ws, Lw.ckv);
   HIP_TRY(launch_draft_pass(q, st));
   return DFLASH_OK;
 }
@@ -571,6 +586,15 @@ extern "C" int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* 
                                       void* ws, size_t ws_bytes, void* stream) {
   return draft_block_impl(w, kv, p, anchor_id, mask_id, block, cand, nullptr, nullptr, 0.f,
                           logits_opt, hidden_opt, ws, ws_bytes, stream);
+}
+
+extern "C" int32_t dflash_draft_block_commit(const dflash_weights* w, const dflash_kv* kv,
+                                             const void* taps, int32_t n_commit, int64_t p,
+                                             int32_t anchor_id, int32_t mask_id, int32_t block,
+                                             int32_t* cand, void* logits_opt, void* hidden_opt,
+                                             void* ws, size_t ws_bytes, void* stream) {
+  return draft_block_impl(w, kv, p, anchor_id, mask_id, block, cand, nullptr, nullptr, 0.f,
+                          logits_opt, hidden_opt, ws, ws_bytes, stream, false, taps, n_commit);
 }
 
 extern "C" int32_t dflash_draft_block_static(const dflash_weights* w, const dflash_kv* kv,

@@ -273,7 +273,7 @@ struct PassLaunch {
   uint16_t* h16;
   float* ss;
   uint16_t* qkv;           // fp16 [5][8][7168]
-  float2* rope;
+  float2* rope;             // [16][128]
   uint16_t* po;            // chunk outputs, fp16, normalised by the chunk sum
   float* pm;
   float* pl;
@@ -288,6 +288,14 @@ struct PassLaunch {
   int32_t* cand;
   uint16_t* logits;
   uint16_t* hidden;
+  // fused draft-commit cycle: nc commit rows of taps at positions pos0..pos0+nc-1
+  const uint16_t* taps = nullptr;
+  const void* fc = nullptr;  // streaming copy of fc (backbone format)
+  const uint16_t* hidden_norm = nullptr;
+  int nc = 0;
+  int64_t pos0 = 0;
+  float* yc = nullptr;       // [8][2560] fp32
+  float* ckv = nullptr;      // [5][8][1024] fp32
   float* conf = nullptr;     // [B-1] candidate probabilities, or null
   int32_t* nkeep = nullptr;  // confidence-gated candidate count, or null
   float min_p = 0.f;

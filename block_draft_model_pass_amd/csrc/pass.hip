@@ -89,6 +89,10 @@ __device__ __forceinline__ T gld(const void* p) {
   }
 }
 
+__device__ __forceinline__ void gst16(uint16_t* p, uint16_t v) {
+  *reinterpret_cast<GA uint16_t*>(reinterpret_cast<uintptr_t>(p)) = v;
+}
+
 __device__ __forceinline__ uint4 ldw(const uint16_t* p) {
   return __builtin_bit_cast(
       uint4, __builtin_nontemporal_load(reinterpret_cast<const GA u32x4*>(reinterpret_cast<uintptr_t>(p))));
@@ -154,7 +158,7 @@ struct PassArgs {
   uint16_t* h16;     // [HV][8][H] fp16 copies: the input of the RMSNorm builds
   float* ss;         // [HV][NT_H][8] per-tile sums of squares of each h version
   uint16_t* qkv;     // [L][8][QKV_N] fp16 (raw q, k, v before the head norms)
-  const float2* rope;  // [8][128] (cos, sin)
+  const float2* rope;  // [16][128] (cos, sin): block rows, then commit rows at 8 + t
   uint16_t* po;
   float* pm;
   float* pl;
@@ -164,6 +168,17 @@ struct PassArgs {
   uint64_t* lse;     // [grid][8] per-block (max, sum) pairs of the softmax sweep
   unsigned* bar;     // barrier words (BAR_*)
   uint64_t wait_ticks;  // barrier wait bound, constant-clock ticks
+  // Commit rows of the fused draft-commit cycle: nc (0..8) rows of target taps
+  // for positions pos0 .. pos0+nc-1 (= p-nc .. p-1), fused and projected
+  // inside this pass (their cells are written to the ring and attended to
+  // from the workspace; the ring is read at [lo, hi) with hi = pos0).
+  const uint16_t* taps;   // bf16 [nc][5][2560]
+  const void* fc;         // streaming copy of fc, in the backbone's format
+  const uint16_t* hidden_norm;
+  int nc;
+  int64_t pos0;
+  float* yc;              // [8][H] fc outputs of the commit rows (fp32)
+  float* ckv;             // [L][8][1024] raw Wk | Wv outputs of the commit rows (fp32)
   // outputs
   int32_t* cand;
   uint16_t* logits;
@@ -632,6 +647,145 @@ __device__ __forceinline__ void residual_epilogue(const PassArgs& a, f32x4 acc, 
 
 // ---------------------------------------------------------------- phases
 
+// ---------------------------------------------------------------- commit rows
+//
+// Fused draft-commit cycle: the nc commit rows (the cells the last verify
+// accepted) are fused (fc, then RMSNorm) and projected (each layer's Wk / Wv)
+// inside the pass.  Their K/V projection rides the QKV phase's Wk / Wv tiles
+// as MFMA columns 8..15 (the block rows use columns 0..7), so it streams no
+// extra weight bytes; only fc (65.5 MB bf16) is added, in an FC phase before
+// the first barrier.
+//
+// FC phase: block w < 160 owns fc output tile w (16 of the 2560 rows) over the
+// whole 12800-wide k range, so the five taps' partial sums meet inside the
+// block (deterministic).  Three rounds take taps (0, 1), (2, 3), (4, -): a
+// round stages its two taps' rows in LDS (rows 0..7 and 8..15, in the MFMA
+// input format) and waves 4h .. 4h+3 take tap 2r+h in k quarters of 640; the
+// next round's weights are issued right after the round's tap loads.
+template <int FMT> using FcTile = WTile<FMT, 640 / KPerLoad<FMT>::v>;
+
+template <int FMT>
+__device__ __forceinline__ void fc_load(const PassArgs& a, int round, FcTile<FMT>& W) {
+  const int w = blockIdx.x, wave = wid(), lane = otid() & 63;
+  const int tap = 2 * round + (wave >> 2);
+  constexpr int N = 640 / KPerLoad<FMT>::v;
+  load_wt<FMT, N>(W, WMat{a.fc, H, T * H}, w * 16 + (lane & 15),
+                  (tap < T ? tap : 0) * H + (wave & 3) * 640, lane >> 4, N, tap < T);
+}
+
+constexpr int FC_U = 2 * MAXB * (H / 8) / NTHR;  // 16-byte tap groups per thread per round (10)
+
+// Loads of round r's taps: group e = (half h, row t, 8-element group k8) ->
+// tap 2r + h of commit row t.  Rows past nc (or a missing tap) re-read a
+// valid group and are stored as zeros.
+__device__ __forceinline__ void fc_tap_load(const PassArgs& a, int round, uint4 (&v)[FC_U]) {
+  const int tid = otid();
+#pragma unroll
+  for (int u = 0; u < FC_U; ++u) {
+    const int e = tid + u * NTHR;
+    const int h = e / (MAXB * (H / 8)), t = (e / (H / 8)) % MAXB, k8 = e % (H / 8);
+    const int tap = 2 * round + h;
+    const bool ok = t < a.nc && tap < T;
+    v[u] = gld<uint4>(a.taps + (static_cast<size_t>(ok ? t : 0) * T + (ok ? tap : 0)) * H + 8 * k8);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void fc_tap_store(const PassArgs& a, Smem& s, int round,
+                                             const uint4 (&v)[FC_U]) {
+  constexpr int XS = H + XS_PAD;
+  const int tid = otid();
+#pragma unroll
+  for (int u = 0; u < FC_U; ++u) {
+    const int e = tid + u * NTHR;
+    const int h = e / (MAXB * (H / 8)), t = (e / (H / 8)) % MAXB, k8 = e % (H / 8);
+    const bool ok = t < a.nc && 2 * round + h < T;
+    uint4 x = ok ? v[u] : make_uint4(0, 0, 0, 0);
+    if constexpr (FMT != W_BF16) {  // fp16 next to decoded quantized weights
+      uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        wv[i] = static_cast<uint32_t>(f32_to_f16_bits(bf16_to_f32(static_cast<uint16_t>(wv[i])))) |
+                (static_cast<uint32_t>(f32_to_f16_bits(bf16_to_f32(static_cast<uint16_t>(wv[i] >> 16)))) << 16);
+      x = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+    *reinterpret_cast<uint4*>(s.x + (h * MAXB + t) * XS + 8 * k8) = x;
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void fc_phase(const PassArgs& a, Smem& s) {
+  if (a.nc == 0 || blockIdx.x >= NT_H) return;
+  const int wave = wid(), lane = otid() & 63, r = lane & 15, g = lane >> 4;
+  constexpr int XS = H + XS_PAD;
+  constexpr int N = 640 / KPerLoad<FMT>::v;
+  const uint16_t* xr = s.x + ((wave >> 2) * MAXB + (r & 7)) * XS;  // columns 8..15 repeat 0..7
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  FcTile<FMT> W0, W1;
+  uint4 tv[FC_U];
+  fc_tap_load(a, 0, tv);
+  fc_load<FMT>(a, 0, W0);
+  fc_load<FMT>(a, 1, W1);
+  fc_tap_store<FMT>(a, s, 0, tv);
+  lds_sync();
+  acc += mma_wt<FMT, N>(W0, xr, (wave & 3) * 640, g, N);
+  lds_sync();
+  fc_tap_load(a, 1, tv);
+  fc_load<FMT>(a, 2, W0);
+  fc_tap_store<FMT>(a, s, 1, tv);
+  lds_sync();
+  acc += mma_wt<FMT, N>(W1, xr, (wave & 3) * 640, g, N);
+  lds_sync();
+  fc_tap_load(a, 2, tv);
+  fc_tap_store<FMT>(a, s, 2, tv);
+  lds_sync();
+  if (wave < 4) acc += mma_wt<FMT, N>(W0, xr, (wave & 3) * 640, g, N);  // tap 4
+  s.red[wave][lane] = acc;
+  lds_sync();
+  if (wave == 0) {
+    acc = group_sum(s, 0, NWAVE, lane);
+    if (r < a.nc) st_coh_f4(a.yc + static_cast<size_t>(r) * H + blockIdx.x * 16 + 4 * g, acc);
+  }
+  wait_stores();
+}
+
+// Commit rows into LDS rows 8 .. 8+nc-1 for the Wk / Wv tiles of the QKV
+// phase: c = bf16(rmsnorm(y) * hidden_norm) (the fused context row, in bf16
+// as the fusion hands it to the projection), in the MFMA input format.  Wave
+// t builds row t; rows past nc are zeros.
+template <int FMT>
+__device__ __forceinline__ void commit_rows_build(const PassArgs& a, Smem& s) {
+  constexpr int XS = H + XS_PAD;
+  const int wave = wid(), lane = otid() & 63;
+  const int t = wave < a.nc ? wave : 0;
+  float4 v[10];
+  uint2 gn[10];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    v[i] = gld<float4>(a.yc + static_cast<size_t>(t) * H + 4 * (lane + 64 * i));
+    gn[i] = gld<uint2>(a.hidden_norm + 4 * (lane + 64 * i));
+  }
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < 10; ++i) sq += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+  sq = wave_sum(sq);
+  const float sc = 1.0f / sqrtf(sq / static_cast<float>(H) + a.eps);
+  const bool live = wave < a.nc;
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const float y4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    const uint32_t gw[2] = {gn[i].x, gn[i].y};
+    uint16_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t c = f32_to_bf16(y4[e] * sc * bf16_to_f32(static_cast<uint16_t>(gw[e >> 1] >> (16 * (e & 1)))));
+      o[e] = live ? (FMT == W_BF16 ? c : f32_to_f16_bits(bf16_to_f32(c))) : 0;
+    }
+    *reinterpret_cast<uint2*>(s.x + (MAXB + wave) * XS + 4 * (lane + 64 * i)) =
+        make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
+  }
+}
+
 // Work of one block for the QKV phase: tiles 2w and 2w+1 of the 448 fused
 // q|k|v row tiles; wave v takes tile 2w + v/4 and k quarter v%4 (640 k).
 // Tiles never straddle the q / k / v matrices (6144 and 512 rows).
@@ -657,21 +811,28 @@ __device__ __forceinline__ void qkv_prefetch(const PassArgs& a, int l, QkvTile<F
   load_wt<FMT, N>(W, m, row0 + (lane & 15), (wave & 3) * 640, lane >> 4, N, go && has);
 }
 
+// Blocks whose two tiles are Wk / Wv rows (the ctx K/V projection's rows).
+__device__ __forceinline__ bool qkv_kv_block(int w) { return 2 * w * 16 >= NQ * D && qkv_has(w); }
+
 template <int FMT>
 __device__ __forceinline__ void qkv_phase(const PassArgs& a, Smem& s, int l, int np, QkvTile<FMT>& W) {
   const int w = blockIdx.x, wave = wid(), lane = otid() & 63;
   const int r = lane & 15, g = lane >> 4;
   const bool has = qkv_has(w);
+  // commit rows ride the Wk / Wv tiles as MFMA columns 8..15
+  const bool cm = a.nc > 0 && qkv_kv_block(w);
   // activation loads first: a wave's loads complete in order, and every wave
   // waits for the activations at the LDS rendezvous
   XnRegs x;
   if (has) xn_load(a, x, 2 * l, np, ctab(a)->in_norm[l]);
+  if (cm) commit_rows_build<FMT>(a, s);
   if (has) xn_finish<FMT>(a, s, x);
   if (has) {
     const int tile = 2 * w + (wave >> 2);
     constexpr int XS = H + XS_PAD;
     constexpr int N = 640 / KPerLoad<FMT>::v;
-    f32x4 acc = mma_wt<FMT, N>(W, s.x + xrow(r, a.B) * XS, (wave & 3) * 640, g, N);
+    const int xr = r < MAXB ? xrow(r, a.B) : (cm ? r : 0);
+    f32x4 acc = mma_wt<FMT, N>(W, s.x + xr * XS, (wave & 3) * 640, g, N);
     s.red[wave][lane] = acc;
     lds_sync();
     if ((wave & 3) == 0) {
@@ -682,6 +843,10 @@ __device__ __forceinline__ void qkv_phase(const PassArgs& a, Smem& s, int l, int
                      (static_cast<uint64_t>(f32_to_f16_bits(acc[1])) << 16) |
                      (static_cast<uint64_t>(f32_to_f16_bits(acc[2])) << 32) |
                      (static_cast<uint64_t>(f32_to_f16_bits(acc[3])) << 48));
+      else if (cm && r >= MAXB && r - MAXB < a.nc)  // raw K | V of commit row r - 8, fp32
+        st_coh_f4(a.ckv + (static_cast<size_t>(l) * MAXB + (r - MAXB)) * (2 * NKV * D) +
+                      tile * 16 - NQ * D + 4 * g,
+                  acc);
     }
   }
   wait_stores();
@@ -938,35 +1103,89 @@ __device__ __forceinline__ void attn_query(const PassArgs& a, int l, int j, int 
 }
 
 // Block rows' keys and values of KV head j into LDS (keys [32][256] with rows
-// b < B, values [256][32]); wave b = row b.
+// b < B, values [256][32]); wave b = row b.  With commit rows (the fused
+// draft-commit cycle), wave t also finishes commit row t: k-norm and RoPE at
+// pos0 + t on its raw fp32 projection, fp16 K and V written to the ring cell
+// of that position (read by later passes), and -- when the position is inside
+// the window -- the same fp16 key and value as cell B + t - t0 of the LDS
+// block (t0 = the first visible commit row), so the rows block holds
+// nrows() keys.
+__device__ __forceinline__ int commit_first_visible(const PassArgs& a) {
+  const int64_t d = a.lo - a.pos0;
+  return d <= 0 ? 0 : (d >= a.nc ? a.nc : static_cast<int>(d));
+}
+__device__ __forceinline__ int nrows(const PassArgs& a) {
+  return a.B + a.nc - commit_first_visible(a);
+}
+
 __device__ __forceinline__ void attn_block_rows(const PassArgs& a, int l, int j, uint16_t* kl,
                                                 uint16_t* vl) {
   const int wave = wid(), lane = otid() & 63;
-  if (wave >= a.B) return;
-  const int b = wave;
-  const uint16_t* kr = a.qkv + l * QSTRIDE + static_cast<size_t>(b) * QKV_N + NQ * D + j * D;
-  const uint16_t* vr = kr + NKV * D;
-  float k0 = f16_bits_to_f32(gld<uint16_t>(kr + lane)), k1 = f16_bits_to_f32(gld<uint16_t>(kr + lane + 64));
-  float k2 = f16_bits_to_f32(gld<uint16_t>(kr + lane + 128)), k3 = f16_bits_to_f32(gld<uint16_t>(kr + lane + 192));
-  float vv[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) vv[q] = f16_bits_to_f32(gld<uint16_t>(vr + lane + 64 * q));
-  const float sq = wave_sum(k0 * k0 + k1 * k1 + k2 * k2 + k3 * k3);
-  const float sc = 1.0f / sqrtf(sq / static_cast<float>(D) + a.eps);
   const uint16_t* gn = ctab(a)->k_norm[l];
-  k0 *= sc * bf16_to_f32(gld<uint16_t>(gn + lane));
-  k1 *= sc * bf16_to_f32(gld<uint16_t>(gn + lane + 64));
-  k2 *= sc * bf16_to_f32(gld<uint16_t>(gn + lane + 128));
-  k3 *= sc * bf16_to_f32(gld<uint16_t>(gn + lane + 192));
-  const float2 c0 = gld<float2>(a.rope + b * (D / 2) + lane);
-  const float2 c1 = gld<float2>(a.rope + b * (D / 2) + lane + 64);
-  const float kv[4] = {k0 * c0.x - k2 * c0.y, k1 * c1.x - k3 * c1.y, k2 * c0.x + k0 * c0.y,
-                       k3 * c1.x + k1 * c1.y};
+  float gk[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int d = lane + 64 * q;
-    kl[kswz(b, d >> 3) + (d & 7)] = f32_to_f16_bits(kv[q]);
-    vl[vswz(d, b >> 2) + (b & 3)] = f32_to_f16_bits(vv[q]);
+  for (int q = 0; q < 4; ++q) gk[q] = bf16_to_f32(gld<uint16_t>(gn + lane + 64 * q));
+  if (wave < a.B) {
+    const int b = wave;
+    const uint16_t* kr = a.qkv + l * QSTRIDE + static_cast<size_t>(b) * QKV_N + NQ * D + j * D;
+    const uint16_t* vr = kr + NKV * D;
+    float k0 = f16_bits_to_f32(gld<uint16_t>(kr + lane)), k1 = f16_bits_to_f32(gld<uint16_t>(kr + lane + 64));
+    float k2 = f16_bits_to_f32(gld<uint16_t>(kr + lane + 128)), k3 = f16_bits_to_f32(gld<uint16_t>(kr + lane + 192));
+    float vv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) vv[q] = f16_bits_to_f32(gld<uint16_t>(vr + lane + 64 * q));
+    const float sq = wave_sum(k0 * k0 + k1 * k1 + k2 * k2 + k3 * k3);
+    const float sc = 1.0f / sqrtf(sq / static_cast<float>(D) + a.eps);
+    k0 *= sc * gk[0];
+    k1 *= sc * gk[1];
+    k2 *= sc * gk[2];
+    k3 *= sc * gk[3];
+    const float2 c0 = gld<float2>(a.rope + b * (D / 2) + lane);
+    const float2 c1 = gld<float2>(a.rope + b * (D / 2) + lane + 64);
+    const float kv[4] = {k0 * c0.x - k2 * c0.y, k1 * c1.x - k3 * c1.y, k2 * c0.x + k0 * c0.y,
+                         k3 * c1.x + k1 * c1.y};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = lane + 64 * q;
+      kl[kswz(b, d >> 3) + (d & 7)] = f32_to_f16_bits(kv[q]);
+      vl[vswz(d, b >> 2) + (b & 3)] = f32_to_f16_bits(vv[q]);
+    }
+  }
+  if (wave < a.nc) {
+    const int t = wave;
+    const float* kr = a.ckv + (static_cast<size_t>(l) * MAXB + t) * (2 * NKV * D) + j * D;
+    const float* vr = kr + NKV * D;
+    float k[4], vv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      k[q] = gld<float>(kr + lane + 64 * q);
+      vv[q] = gld<float>(vr + lane + 64 * q);
+    }
+    const float sq = wave_sum(k[0] * k[0] + k[1] * k[1] + k[2] * k[2] + k[3] * k[3]);
+    const float sc = 1.0f / sqrtf(sq / static_cast<float>(D) + a.eps);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) k[q] *= sc * gk[q];
+    const float2 c0 = gld<float2>(a.rope + (MAXB + t) * (D / 2) + lane);
+    const float2 c1 = gld<float2>(a.rope + (MAXB + t) * (D / 2) + lane + 64);
+    const float kv[4] = {k[0] * c0.x - k[2] * c0.y, k[1] * c1.x - k[3] * c1.y,
+                         k[2] * c0.x + k[0] * c0.y, k[3] * c1.x + k[1] * c1.y};
+    const int cell = static_cast<int>((a.pos0 + t) % a.cap);
+    uint16_t* rk = const_cast<uint16_t*>(a.ring_k) + ((static_cast<size_t>(l) * NKV + j) * a.cap + cell) * D;
+    uint16_t* rv = const_cast<uint16_t*>(a.ring_vt) + (static_cast<size_t>(l) * NKV + j) * D * a.cap +
+                   static_cast<size_t>(cell / BLK_CELLS) * D * BLK_CELLS + cell % BLK_CELLS;
+    const int t0 = commit_first_visible(a);
+    const int c = a.B + t - t0;  // LDS cell of a visible commit row
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = lane + 64 * q;
+      const uint16_t kb = f32_to_f16_bits(kv[q]), vb = f32_to_f16_bits(vv[q]);
+      gst16(rk + d, kb);
+      gst16(rv + static_cast<size_t>(d) * BLK_CELLS, vb);
+      if (t >= t0) {
+        kl[kswz(c, d >> 3) + (d & 7)] = kb;
+        vl[vswz(d, c >> 2) + (c & 3)] = vb;
+      }
+    }
   }
 }
 
@@ -1021,7 +1240,7 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KV
     }
     if (rows) {
       lds_sync();
-      if (wave < a.nqt) attn_block(kl, vl, 0, 0, a.B, a.scale_log2, qf, o, m, lsum, n, g);
+      if (wave < a.nqt) attn_block(kl, vl, 0, 0, nrows(a), a.scale_log2, qf, o, m, lsum, n, g);
     }
     if (wave < a.nqt) {
       lsum = group4_sum(lsum);
@@ -1552,8 +1771,10 @@ __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
   BarState bk;      // barriers passed, give-up flag
   QkvTile<FMT> Wq;
   LmTile<LMF> Wl;   // LM head slice, prefetched after the last layer
-  // Layer 0 QKV weights stream while the grid lines up; h, ss, the RoPE
-  // table and the layer table come from the init kernel.
+  // Commit rows (fused draft-commit cycle) through fc first; then layer 0
+  // QKV weights stream while the grid lines up.  h, ss, the RoPE table and
+  // the layer table come from the init kernel.
+  fc_phase<FMT>(a, s);
   grid_sync_pf(a, bk, [&] { qkv_prefetch<FMT>(a, 0, Wq, true); });
   int np = 1;    // sums of squares of h: one entry per row from the init kernel
   for (int l = 0; l < L; ++l) {
@@ -1591,18 +1812,26 @@ __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
   }
 }
 
-// h[b] = E[token_b], per-row sum of squares, RoPE table of p .. p+B-1, and the
-// barrier words of the pass kernel.  grid B, block 256.
+// h[b] = E[token_b], per-row sum of squares, RoPE table of p .. p+B-1 (rows
+// 0..B-1) and of the commit positions pos0 .. pos0+nc-1 (rows 8..8+nc-1), and
+// the barrier words of the pass kernel.  grid max(B, nc), block 256.
 __global__ __launch_bounds__(256) void k_pass_init(LayerTab tab, LayerTab* tab_out,
                                                    const uint16_t* embed, int anchor, int mask,
-                                                   int64_t p, double theta, float* h,
-                                                   uint16_t* h16, float* ss, float2* rope,
-                                                   unsigned* bar) {
+                                                   int B, int64_t p, int nc, int64_t pos0,
+                                                   double theta, float* h, uint16_t* h16,
+                                                   float* ss, float2* rope, unsigned* bar) {
   __shared__ float red[4];
   const int b = blockIdx.x;
   if (b == 0)
     for (int i = threadIdx.x; i < BAR_WORDS; i += 256) bar[i] = 0u;
   if (b == 0 && threadIdx.x == 0) *tab_out = tab;
+  if (b < nc && threadIdx.x < D / 2) {
+    const double inv = pow(theta, -2.0 * static_cast<double>(threadIdx.x) / static_cast<double>(D));
+    double sn, cs;
+    sincos(static_cast<double>(pos0 + b) * inv, &sn, &cs);
+    rope[(MAXB + b) * (D / 2) + threadIdx.x] = make_float2(static_cast<float>(cs), static_cast<float>(sn));
+  }
+  if (b >= B) return;  // block-uniform
   const int tok = b == 0 ? anchor : mask;
   const uint16_t* row = embed + static_cast<size_t>(tok) * H;
   // All of the row's loads are issued before any store (a store could alias
@@ -1710,6 +1939,13 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
   a.min_p = q.min_p;
   a.bar = q.bar;
   a.wait_ticks = q.wait_ticks;
+  a.taps = q.taps;
+  a.fc = q.fc;
+  a.hidden_norm = q.hidden_norm;
+  a.nc = q.nc;
+  a.pos0 = q.pos0;
+  a.yc = q.yc;
+  a.ckv = q.ckv;
   a.cand = q.cand;
   a.logits = q.logits;
   a.hidden = q.hidden;
@@ -1719,9 +1955,11 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
   if (q.nch < 1 || q.nch > 128 || q.grid < NKV * q.nch || q.grid < QKV_N / 32 ||
       q.grid < NKV * a.nqt * 16 || q.grid > 1024)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_pass_init, dim3(q.B), dim3(256), 0, st, tab,
-                     reinterpret_cast<LayerTab*>(q.tab), q.embed, q.anchor, q.mask, q.p, q.theta,
-                     q.h, q.h16, q.ss, q.rope, q.bar);
+  if (q.nc < 0 || q.nc > MAXB || (q.nc > 0 && (!q.taps || !q.fc || !q.yc || !q.ckv || q.grid < NT_H)))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_pass_init, dim3(q.B > q.nc ? q.B : q.nc), dim3(256), 0, st, tab,
+                     reinterpret_cast<LayerTab*>(q.tab), q.embed, q.anchor, q.mask, q.B, q.p, q.nc,
+                     q.pos0, q.theta, q.h, q.h16, q.ss, q.rope, q.bar);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const void* kern = pass_kernel(q.fmt, q.lm_fmt);

@@ -173,6 +173,22 @@ class Drafter:
                            self.ws.data_ptr(), self.ws_bytes, stream_ptr())
         return cand
 
+    def draft_commit(self, taps_ptr: int | None, n_commit: int, p: int, anchor: int, block: int,
+                     mask_id: int = synth.MASK_ID, cand: torch.Tensor | None = None,
+                     logits: torch.Tensor | None = None,
+                     hidden: torch.Tensor | None = None) -> torch.Tensor:
+        """One pass that commits n_commit rows of taps (a device pointer to
+        [n_commit][5][2560] bf16) at positions p-n_commit .. p-1 and drafts
+        the block at p (dflash_draft_block_commit)."""
+        if cand is None:
+            cand = torch.empty(max(block - 1, 1), dtype=torch.int32, device=self.device)
+        _lib.dflash_draft_block_commit(self.w.desc, self.kv.desc, taps_ptr, n_commit, p, anchor,
+                                       mask_id, block, cand.data_ptr(),
+                                       logits.data_ptr() if logits is not None else None,
+                                       hidden.data_ptr() if hidden is not None else None,
+                                       self.ws_ptr, self.ws_bytes, stream_ptr())
+        return cand
+
     def draft_gated(self, p: int, anchor: int, block: int, min_p: float,
                     mask_id: int = synth.MASK_ID, cand: torch.Tensor | None = None,
                     conf: torch.Tensor | None = None, n_keep: torch.Tensor | None = None):

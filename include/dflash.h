@@ -239,11 +239,35 @@ DFLASH_API int32_t dflash_draft_block(const dflash_weights* w, const dflash_kv* 
                            int32_t* cand, void* logits_opt, void* hidden_opt,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* One decode cycle's drafter work as one pass ("Speculative decode
+ * integration" on the PR #1426 page: propose [anchor, K candidates], verify,
+ * commit the accepted cells plus the verifier's continuation token as the
+ * next anchor; position-addressed cells).  Equivalent to
+ *   dflash_fuse_context(taps, n_commit) ; dflash_project_ctx_kv(ctx, n_commit,
+ *   pos0 = p - n_commit) ; dflash_draft_block(p, ...)
+ * with one launch: the commit rows' fusion runs as a first phase of the pass
+ * and their per-layer K/V projection rides the pass's own Wk / Wv weight
+ * stream (extra MFMA columns), so a cycle streams the backbone once.  The
+ * commit cells are written to the ring (as dflash_project_ctx_kv would) and
+ * attended to by this pass from the workspace.
+ *   taps    : bf16 [n_commit][5][2560], the target taps of positions
+ *             p - n_commit .. p - 1 (the anchor and accepted candidates of
+ *             the previous cycle); may be NULL when n_commit is 0
+ *   n_commit: 0 .. 8 (0: a plain dflash_draft_block); p >= n_commit
+ * Other arguments, outputs, checks and give-up behaviour as
+ * dflash_draft_block.  The candidates and logits agree with the separate
+ * calls within rounding (the fusion's sums run in another order). */
+DFLASH_API int32_t dflash_draft_block_commit(const dflash_weights* w, const dflash_kv* kv,
+                                  const void* taps, int32_t n_commit, int64_t p,
+                                  int32_t anchor_id, int32_t mask_id, int32_t block,
+                                  int32_t* cand, void* logits_opt, void* hidden_opt,
+                                  void* ws, size_t ws_bytes, void* stream);
+
 /* dflash_draft_block for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): no workspace argument; the pass runs in a 66 MiB device array
  * inside the library (each device the library runs on holds its own copy
- * from the first call until the process ends; the pass needs 65.6 MiB of it
+ * from the first call until the process ends; the pass needs 65.8 MiB of it
  * whatever the context length and block size, and a layout that would not
  * fit returns DFLASH_EWORKSPACE).  The call allocates nothing: on its first
  * call on a device it only looks up the array's device address.  Same

@@ -319,3 +319,23 @@ def test_static_workspace_pass_arguments(lib):
         _lib.DFLASH_EGEOMETRY
     assert S(w, fake_kv(1000, 1000), 100, 1, 2, 8, A, None, None, check=False) == \
         _lib.DFLASH_ERANGE
+
+
+def test_fused_commit_pass_arguments(lib):
+    """dflash_draft_block_commit: n_commit in [0, 8], p >= n_commit, taps
+    non-null and 16-byte aligned when there are commit rows."""
+    w = fake_weights()
+    w.packed = A
+    kv = fake_kv()
+    big = 1 << 40
+    E = _lib.DFLASH_EINVAL
+    C = _lib.dflash_draft_block_commit
+    for nc in (-1, 9):
+        assert C(w, kv, A, nc, 100, 1, 2, 8, A, None, None, A, big, check=False) == E
+    assert C(w, kv, A, 5, 4, 1, 2, 8, A, None, None, A, big, check=False) == E      # p < n_commit
+    assert C(w, kv, None, 3, 100, 1, 2, 8, A, None, None, A, big, check=False) == E  # no taps
+    assert C(w, kv, A + 8, 3, 100, 1, 2, 8, A, None, None, A, big, check=False) == E
+    assert C(w, kv, A, 3, 100, 1, 2, 9, A, None, None, A, big, check=False) == E    # block
+    need = _lib.dflash_workspace_size(w, 0, 8)
+    assert C(w, kv, A, 3, 100, 1, 2, 8, A, None, None, A, need - 1, check=False) == \
+        _lib.DFLASH_EWORKSPACE
