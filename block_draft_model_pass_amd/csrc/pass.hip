@@ -190,6 +190,8 @@ struct PassArgs {
 
 struct Smem {
   uint16_t x[MAXB * XS_MAX];   // activations (GEMV phases) / block keys+values (ATTN)
+  uint16_t gain[H];            // RMSNorm gain of the phase (staged)
+  float ssb[NT_H * MAXB];      // per-tile sums of squares of the phase's h version (staged)
   f32x4 red[NWAVE][64];        // cross-wave reduction
   float scal[64];              // per-row scales / merge weights
   float mw[4 * 256];           // merge: chunk weights and partial sums
@@ -505,6 +507,50 @@ __device__ __forceinline__ f32x4 group_sum(Smem& s, int w0, int n, int lane) {
   return acc;
 }
 
+// ---------------------------------------------------------------- staged activations
+//
+// A wave's loads complete in issue order, so an activation read issued after
+// a wave's weight prefetch waits for the whole prefetch.  In the QKV, O, DOWN
+// and LM phases the activations are therefore read by one wave that
+// prefetches no weights at the barrier (ACT_WAVE): right after the release it
+// copies them straight into LDS (buffer loads with an LDS destination, no
+// registers), waits for them, then issues its own weight slice; the other
+// waves' slices were issued during the barrier.  (ATTN and GU keep the
+// register path: there the late slice of ACT_WAVE -- a K/V block share, or
+// two gate/up pairs -- costs more than the earlier activations save.)
+constexpr int ACT_WAVE = NWAVE - 1;
+
+__device__ __forceinline__ bool act_wave() { return wid() == ACT_WAVE; }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// 64 lanes x 16 bytes from the resource (lane byte offset voff; bytes past its
+// extent read as zeros) into 1 KiB of LDS at dst (lane i -> dst + 16 i).
+__device__ __forceinline__ void g2lds(__amdgpu_buffer_rsrc_t rs, void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16,
+                                           static_cast<int>(voff), 0, 0, 0);
+}
+
+// Rows 0..B-1 of a global [rows][K] fp16/bf16 matrix (K * 2 a multiple of
+// 1 KiB) into LDS rows of stride K + XS_PAD, by the calling wave.
+template <int K>
+__device__ __forceinline__ void stage_rows(const PassArgs& a, Smem& s, const uint16_t* src) {
+  static_assert((K * 2) % 1024 == 0, "rows are whole KiB");
+  constexpr int XS = K + XS_PAD, C = K * 2 / 1024;
+  const int lane = otid() & 63;
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(src, static_cast<uint32_t>(a.B) * K * 2);
+  for (int b = 0; b < a.B; ++b)
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      g2lds(rs, s.x + b * XS + 512 * c, static_cast<uint32_t>(b * K * 2 + 1024 * c + 16 * lane));
+}
+
+// Wait for this wave's LDS-destination loads (and everything before them).
+__device__ __forceinline__ void staged_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // x[b][k] = h[b][k] * rsqrt(mean_k h^2 + eps) * gain[k] for b < B, rounded to
 // the activation format XF (bf16, or fp16 beside quantized weights), into
 // LDS rows of stride H + pad.  np per-tile sums of squares are reduced in a
@@ -572,49 +618,66 @@ __device__ __forceinline__ void xn_finish(const PassArgs& a, Smem& s, const XnRe
   lds_sync();
 }
 
-template <int XF>
-__device__ __forceinline__ void build_x_norm(const PassArgs& a, Smem& s, int ver, int np,
-                                             const uint16_t* gain) {
-  XnRegs x;
-  xn_load(a, x, ver, np, gain);
-  xn_finish<XF>(a, s, x);
-}
-
-// Copy activations [B][K] from global into LDS rows of stride K + pad, in
-// two halves like the norm: cx_load issues every load in one round (groups
-// past the block's rows re-read group 0 and are never stored), cx_store
-// writes LDS.
-template <int K>
-struct CxRegs {
-  static constexpr int U = (MAXB * K / 8 + NTHR - 1) / NTHR;
-  uint4 v[U];
-};
-
-template <int K>
-__device__ __forceinline__ void cx_load(const PassArgs& a, CxRegs<K>& c, const uint16_t* src) {
-  const int tid = otid();
-  const int n8 = a.B * (K / 8);
+// x rows = act(h[ver] * rsqrt(mean h^2 + eps) * gain) from a staged copy:
+// ACT_WAVE copies the fp16 h rows into the LDS x rows, the gain and the np
+// per-tile sums of squares; wave b < B then reduces row b's sums (fixed
+// order) and every thread normalises its groups in place.  `after` runs on
+// ACT_WAVE once its copies have landed (its weight slice).
+template <int XF, class After>
+__device__ __forceinline__ void build_x_norm_staged(const PassArgs& a, Smem& s, int ver, int np,
+                                                    const uint16_t* gain, After&& after) {
+  const int tid = otid(), wave = wid(), lane = tid & 63;
+  if (act_wave()) {
+    stage_rows<H>(a, s, a.h16 + ver * HSTRIDE);
+    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gain, H * 2);
 #pragma unroll
-  for (int u = 0; u < CxRegs<K>::U; ++u) {
-    const int e = tid + u * NTHR;
-    c.v[u] = gld<uint4>(src + 8 * (e < n8 ? e : 0));
+    for (int c = 0; c < H * 2 / 1024; ++c) g2lds(rg, s.gain + 512 * c, 1024 * c + 16 * lane);
+    const __amdgpu_buffer_rsrc_t rq =
+        buf_rsrc(a.ss + ver * SSTRIDE, static_cast<uint32_t>(np) * MAXB * 4);
+    for (int c = 0; c * 1024 < np * MAXB * 4; ++c) g2lds(rq, s.ssb + 256 * c, 1024 * c + 16 * lane);
+    staged_wait();
+    after();
   }
-}
-
-template <int K>
-__device__ __forceinline__ void cx_store(const PassArgs& a, Smem& s, const CxRegs<K>& c) {
-  const int tid = otid();
-  constexpr int XS = K + XS_PAD;
-  const int n8 = a.B * (K / 8);
+  lds_sync();
+  if (wave < a.B) {
+    float v = 0.f;
+    for (int i = lane; i < np; i += 64) v += s.ssb[i * MAXB + wave];
+    v = wave_sum(v);
+    if (lane == 0) s.scal[wave] = 1.0f / sqrtf(v / static_cast<float>(H) + a.eps);
+  }
+  lds_sync();
+  constexpr int XS = H + XS_PAD;
+  const int n8 = a.B * (H / 8);
 #pragma unroll
-  for (int u = 0; u < CxRegs<K>::U; ++u) {
+  for (int u = 0; u < XN8; ++u) {
     const int e = tid + u * NTHR;
     if (e < n8) {
-      const int b = e / (K / 8), k = (e % (K / 8)) * 8;
-      *reinterpret_cast<uint4*>(s.x + b * XS + k) = c.v[u];
+      const int b = e / (H / 8), k = (e % (H / 8)) * 8;
+      const float sc = s.scal[b];
+      uint4* px = reinterpret_cast<uint4*>(s.x + b * XS + k);
+      const uint4 hv = *px;
+      const uint4 gv = *reinterpret_cast<const uint4*>(s.gain + k);
+      const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+      const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t y0 = act16<XF>(f16_bits_to_f32(static_cast<uint16_t>(hw[i])) * sc *
+                                      bf16_to_f32(static_cast<uint16_t>(gw[i])));
+        const uint16_t y1 = act16<XF>(f16_bits_to_f32(static_cast<uint16_t>(hw[i] >> 16)) * sc *
+                                      bf16_to_f32(static_cast<uint16_t>(gw[i] >> 16)));
+        o[i] = y0 | (static_cast<uint32_t>(y1) << 16);
+      }
+      *px = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
   lds_sync();
+}
+
+template <int XF>
+__device__ __forceinline__ void build_x_norm(const PassArgs& a, Smem& s, int ver, int np,
+                                             const uint16_t* gain) {
+  build_x_norm_staged<XF>(a, s, ver, np, gain, [] {});
 }
 
 // The residual rows this lane updates (tile's 16 columns, row r), loaded at
@@ -821,12 +884,14 @@ __device__ __forceinline__ void qkv_phase(const PassArgs& a, Smem& s, int l, int
   const bool has = qkv_has(w);
   // commit rows ride the Wk / Wv tiles as MFMA columns 8..15
   const bool cm = a.nc > 0 && qkv_kv_block(w);
-  // activation loads first: a wave's loads complete in order, and every wave
-  // waits for the activations at the LDS rendezvous
-  XnRegs x;
-  if (has) xn_load(a, x, 2 * l, np, ctab(a)->in_norm[l]);
-  if (cm) commit_rows_build<FMT>(a, s);
-  if (has) xn_finish<FMT>(a, s, x);
+  // activations staged by ACT_WAVE, which then issues its weight slice
+  if (has)
+    build_x_norm_staged<FMT>(a, s, 2 * l, np, ctab(a)->in_norm[l],
+                             [&] { qkv_prefetch<FMT>(a, l, W, true); });
+  if (cm) {
+    commit_rows_build<FMT>(a, s);
+    lds_sync();
+  }
   if (has) {
     const int tile = 2 * w + (wave >> 2);
     constexpr int XS = H + XS_PAD;
@@ -1391,10 +1456,13 @@ __device__ __forceinline__ void o_phase(const PassArgs& a, Smem& s, int l, OTile
   const int w = blockIdx.x, wave = wid(), lane = otid() & 63;
   const int r = lane & 15, g = lane >> 4;
   if (w < NT_H) {
-    CxRegs<NQ * D> cx;
-    cx_load(a, cx, a.o16 + l * OSTRIDE);
+    if (act_wave()) {  // attention output rows straight into LDS, then its weight slice
+      stage_rows<NQ * D>(a, s, a.o16 + l * OSTRIDE);
+      staged_wait();
+      o_prefetch<FMT>(a, l, W, true);
+    }
     const float4 hres = residual_load(a, w, r, g, 2 * l);  // used by wave 0
-    cx_store(a, s, cx);
+    lds_sync();
     constexpr int XS = NQ * D + XS_PAD;
     constexpr int N = 768 / KPerLoad<FMT>::v;
     f32x4 acc = mma_wt<FMT, N>(W, s.x + xrow(r, a.B) * XS, wave * 768, g, N);
@@ -1527,11 +1595,13 @@ __device__ __forceinline__ void down_phase(const PassArgs& a, Smem& s, int l, Do
   const int r = lane & 15, g = lane >> 4;
   const int tile = w;
   if (w < NT_H) {
-    CxRegs<F> cx;
-    cx_load(a, cx, a.u16 + l * USTRIDE);
-    const float4 hres = residual_load(a, tile, r, g, 2 * l + 1);  // used by wave 0
+    if (act_wave()) {  // MLP product rows straight into LDS
+      stage_rows<F>(a, s, a.u16 + l * USTRIDE);
+      staged_wait();
+    }
     if (wave > DOWN_PRE_LAST) down_prefetch<FMT>(a, l, W, true);
-    cx_store(a, s, cx);
+    const float4 hres = residual_load(a, tile, r, g, 2 * l + 1);  // used by wave 0
+    lds_sync();
     int kbeg, klen;
     down_range<FMT>(wave, kbeg, klen);
     constexpr int XS = F + XS_PAD;
@@ -1626,7 +1696,9 @@ __device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, LmT
   const int w = blockIdx.x, wave = wid(), lane = otid() & 63;
   const int r = lane & 15, g = lane >> 4;
   const int ntiles = a.vocab / 16, npairs = (ntiles + 1) / 2;
-  build_x_norm<LMF>(a, s, 2 * L, np, a.final_norm);
+  build_x_norm_staged<LMF>(a, s, 2 * L, np, a.final_norm, [&] {
+    if (a.B > 1) lm_prefetch<LMF>(a, w, W, true);
+  });
   constexpr int XS = H + XS_PAD;
   if (w == 0 && a.hidden) write_hidden<LMF>(a, s);
   // mask row r + 1 of the block feeds MFMA column r
@@ -1775,7 +1847,7 @@ __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
   // QKV weights stream while the grid lines up.  h, ss, the RoPE table and
   // the layer table come from the init kernel.
   fc_phase<FMT>(a, s);
-  grid_sync_pf(a, bk, [&] { qkv_prefetch<FMT>(a, 0, Wq, true); });
+  grid_sync_pf(a, bk, [&] { qkv_prefetch<FMT>(a, 0, Wq, !act_wave()); });
   int np = 1;    // sums of squares of h: one entry per row from the init kernel
   for (int l = 0; l < L; ++l) {
     qkv_phase<FMT>(a, s, l, np, Wq);
@@ -1785,7 +1857,7 @@ __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
     grid_sync(a, bk);
     merge_phase<FMT>(a, s, l);
     OTile<FMT> Wo;
-    grid_sync_pf(a, bk, [&] { o_prefetch<FMT>(a, l, Wo, true); });
+    grid_sync_pf(a, bk, [&] { o_prefetch<FMT>(a, l, Wo, !act_wave()); });
     o_phase<FMT>(a, s, l, Wo);
     GuTile<FMT> Wg;
     grid_sync_pf(a, bk, [&] { gu_prefetch<FMT>(a, l, blockIdx.x, Wg, true); });
@@ -1797,8 +1869,8 @@ __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
     // idle), so neither carries a value around the loop.
     const bool last = l + 1 == L;
     grid_sync_pf(a, bk, [&] {
-      qkv_prefetch<FMT>(a, last ? l : l + 1, Wq, !last);
-      lm_prefetch<LMF>(a, blockIdx.x, Wl, last && a.B > 1);
+      qkv_prefetch<FMT>(a, last ? l : l + 1, Wq, !last && !act_wave());
+      lm_prefetch<LMF>(a, blockIdx.x, Wl, last && a.B > 1 && !act_wave());
     });
     np = NT_H;
   }
