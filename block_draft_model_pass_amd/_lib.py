@@ -18,6 +18,11 @@ DFLASH_EHIP = -5
 DFLASH_ENONFINITE = -6
 DFLASH_ETIMEOUT = -7
 
+DFLASH_STAGE_RESIDUAL = 0
+DFLASH_STAGE_QKV = 1
+DFLASH_STAGE_ATTN = 2
+DFLASH_STAGE_MLP = 3
+
 DFLASH_W_BF16 = 0
 DFLASH_W_Q8_0 = 1
 DFLASH_W_Q4_0 = 2
@@ -115,6 +120,9 @@ def load() -> ctypes.CDLL:
     lib.dflash_draft_status.restype = c_int32
     lib.dflash_check_finite.argtypes = [c_void_p, c_int64, c_int32, c_void_p, c_void_p]
     lib.dflash_check_finite.restype = c_int32
+    lib.dflash_draft_stage.argtypes = [c_void_p, c_size_t, c_int32, c_int32, c_int32, c_void_p,
+                                       c_size_t, c_void_p]
+    lib.dflash_draft_stage.restype = c_int32
     lib.dflash_strerror.argtypes = [c_int32]
     lib.dflash_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -192,6 +200,11 @@ def dflash_check_finite(x, count, dtype, status, stream=None, check=True):
 def dflash_verify_greedy_gated(cand, target, k_max, n_keep, out, stream=None, check=True):
     rc = load().dflash_verify_greedy_gated(cand, target, k_max, n_keep, out, stream)
     return _check(rc, "dflash_verify_greedy_gated") if check else rc
+
+
+def dflash_draft_stage(ws, ws_bytes, stage, index, rows, dst, dst_bytes, stream=None, check=True):
+    rc = load().dflash_draft_stage(ws, ws_bytes, stage, index, rows, dst, dst_bytes, stream)
+    return _check(rc, "dflash_draft_stage") if check else rc
 
 
 def dflash_draft_status(ws, ws_bytes, status, stream=None, check=True):

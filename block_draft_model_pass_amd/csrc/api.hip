@@ -669,6 +669,38 @@ extern "C" int32_t dflash_draft_status(const void* ws, size_t ws_bytes, int32_t*
   return DFLASH_OK;
 }
 
+extern "C" int32_t dflash_draft_stage(const void* ws, size_t ws_bytes, int32_t stage, int32_t index,
+                                      int32_t rows, void* dst, size_t dst_bytes, void* stream) {
+  if (!ws || !dst || !a16(ws) || !a16(dst) || rows < 1 || rows > MAXB) return DFLASH_EINVAL;
+  const Layout Lw = layout();
+  if (ws_bytes < Lw.fixed) return DFLASH_EWORKSPACE;
+  // per-layer regions hold MAXB rows each; rows 0..rows-1 are contiguous
+  size_t base, row_bytes, slot_bytes;
+  int32_t count;
+  switch (stage) {
+    case DFLASH_STAGE_RESIDUAL:
+      base = Lw.hv, row_bytes = sizeof(float) * H, count = 2 * dfl::L + 1;
+      break;
+    case DFLASH_STAGE_QKV:
+      base = Lw.qkv, row_bytes = 2 * static_cast<size_t>(QKV_N), count = dfl::L;
+      break;
+    case DFLASH_STAGE_ATTN:
+      base = Lw.ov, row_bytes = 2 * static_cast<size_t>(NQ) * D, count = dfl::L;
+      break;
+    case DFLASH_STAGE_MLP:
+      base = Lw.uv, row_bytes = 2 * static_cast<size_t>(F), count = dfl::L;
+      break;
+    default: return DFLASH_EINVAL;
+  }
+  if (index < 0 || index >= count) return DFLASH_EINVAL;
+  slot_bytes = row_bytes * MAXB;
+  const size_t n = row_bytes * static_cast<size_t>(rows);
+  if (dst_bytes < n) return DFLASH_EINVAL;
+  HIP_TRY(hipMemcpyAsync(dst, static_cast<const char*>(ws) + base + slot_bytes * index, n,
+                         hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream)));
+  return DFLASH_OK;
+}
+
 extern "C" int32_t dflash_check_finite(const void* x, int64_t count, int32_t dtype, int32_t* status,
                                        void* stream) {
   if (!status || (reinterpret_cast<uintptr_t>(status) & 3) || count < 0 || dtype < 0 || dtype > 2)

@@ -233,6 +233,18 @@ class Drafter:
         _lib.dflash_draft_status(self.ws_ptr, self.ws_bytes, out.data_ptr(), stream_ptr())
         return out
 
+    def stage(self, stage: int, index: int, rows: int) -> torch.Tensor:
+        """Copy of one intermediate of the last pass run in this workspace
+        (dflash_draft_stage): fp32 [rows][2560] for the residual stream,
+        16-bit [rows][n] otherwise (raw bits as int16)."""
+        width = {_lib.DFLASH_STAGE_RESIDUAL: 2560, _lib.DFLASH_STAGE_QKV: 7168,
+                 _lib.DFLASH_STAGE_ATTN: 6144, _lib.DFLASH_STAGE_MLP: 7680}[stage]
+        dt = torch.float32 if stage == _lib.DFLASH_STAGE_RESIDUAL else torch.int16
+        out = torch.empty((rows, width), dtype=dt, device=self.device)
+        _lib.dflash_draft_stage(self.ws_ptr, self.ws_bytes, stage, index, rows, out.data_ptr(),
+                                out.numel() * out.element_size(), stream_ptr())
+        return out
+
     def verify(self, cand: torch.Tensor, target: torch.Tensor, k: int,
                out: torch.Tensor | None = None) -> torch.Tensor:
         if out is None:

@@ -363,6 +363,36 @@ DFLASH_API int32_t dflash_draft_status(const void* ws, size_t ws_bytes, int32_t*
 DFLASH_API int32_t dflash_check_finite(const void* x, int64_t count, int32_t dtype, int32_t* status,
                             void* stream);
 
+/* Stage readout of the last proposal pass run in a workspace, for stage-wise
+ * parity ("Parity validation" on the PR #1426 page compares every block row
+ * at every stage of the layer, not only the logits).  The pass keeps each
+ * layer's intermediates in the caller's workspace; this copies one of them,
+ * rows 0..rows-1 (rows = the pass's block, 1..8), into dst on `stream`:
+ *   DFLASH_STAGE_RESIDUAL, index v in [0, 2*5]: fp32 [rows][2560], the
+ *     residual stream: v = 0 the block-token embeddings, v = 2l+1 after
+ *     layer l's attention residual, v = 2l+2 after its MLP residual (v = 10
+ *     is the input of the final norm)
+ *   DFLASH_STAGE_QKV, index l in [0, 5): fp16 [rows][7168], layer l's raw
+ *     projections q (24 heads x 256) | k (2 x 256) | v (2 x 256) before the
+ *     q/k norms
+ *   DFLASH_STAGE_ATTN, index l: [rows][24 x 256] attention output of layer
+ *     l (head-major, before the output projection), in the activation format
+ *     (bf16 beside bf16 weights, fp16 beside Q8_0 / Q4_0 weights)
+ *   DFLASH_STAGE_MLP, index l: [rows][7680] SiLU(gate) * up of layer l, in
+ *     the activation format
+ * dst: device buffer of at least dst_bytes >= the stage's size.  Valid after
+ * dflash_draft_block, _gated or _commit on this workspace has run (stream
+ * order) and before the next call that uses it; a pass that gave up at a
+ * barrier leaves them undefined.  Errors: DFLASH_EINVAL (null / misaligned
+ * pointer, unknown stage, index or rows out of range, dst_bytes too small),
+ * DFLASH_EWORKSPACE, DFLASH_EHIP. */
+#define DFLASH_STAGE_RESIDUAL 0
+#define DFLASH_STAGE_QKV      1
+#define DFLASH_STAGE_ATTN     2
+#define DFLASH_STAGE_MLP      3
+DFLASH_API int32_t dflash_draft_stage(const void* ws, size_t ws_bytes, int32_t stage, int32_t index,
+                                      int32_t rows, void* dst, size_t dst_bytes, void* stream);
+
 /* Static description of a return code (host string, never NULL). */
 DFLASH_API const char* dflash_strerror(int32_t code);
 

@@ -276,7 +276,7 @@ def project_ctx_kv(w: dict, ctx_bits: np.ndarray, pos0: int,
 def draft_block(w: dict, ctx_k: np.ndarray, ctx_v: np.ndarray, p: int,
                 anchor_id: int, mask_id: int, block: int,
                 g: dict | None = None, row_tokens=None,
-                row_positions=None) -> dict:
+                row_positions=None, stages: dict | None = None) -> dict:
     """One parallel proposal pass over the block [anchor, mask x (block-1)].
 
     ctx_k / ctx_v: [L][n_kv][n][D] for the context positions visible from p,
@@ -297,7 +297,15 @@ def draft_block(w: dict, ctx_k: np.ndarray, ctx_v: np.ndarray, p: int,
 
     row_tokens / row_positions override the per-row token ids and positions;
     they exist only so tests can probe the structure of the pass (mask-row
-    order, non-causality).  Block keys are always taken in position order."""
+    order, non-causality).  Block keys are always taken in position order.
+
+    stages, if a dict, receives the intermediates of this same computation
+    for stage-wise comparison ("Parity validation" table): "resid" the
+    residual stream after the embedding and after every attention and MLP
+    residual (2L + 1 arrays [B][H]); per layer, "qkv" the raw q | k | v
+    projections before the q/k norms [B][(nq + 2 nkv) D], "attn" the
+    attention output before the output projection [B][nq D] and "mlp"
+    SiLU(gate) * up [B][F]."""
     g = g or GEOMETRY
     H, D, L = g["hidden"], g["head_dim"], g["n_layers"]
     nq, nkv, F, V = g["n_q_heads"], g["n_kv_heads"], g["ffn"], g["vocab"]
@@ -315,12 +323,16 @@ def draft_block(w: dict, ctx_k: np.ndarray, ctx_v: np.ndarray, p: int,
     order = np.argsort(pos, kind="stable")  # block keys in position order
     E = w["embed"].reshape(V, H)
     h = bf16_decode(E[tokens])
+    rec = stages if stages is not None else {}
+    rec.update(resid=[h], qkv=[], attn=[], mlp=[])
     for l in range(L):
         pre = f"layers.{l}."
         x = rmsnorm(h, gain(w, pre + "in_norm"), eps)
         q = matvec_rows(w, pre + "wq", (nq * D, H), x).reshape(B, nq, D)
         k = matvec_rows(w, pre + "wk", (nkv * D, H), x).reshape(B, nkv, D)
         v = matvec_rows(w, pre + "wv", (nkv * D, H), x).reshape(B, nkv, D)
+        rec["qkv"].append(np.concatenate([q.reshape(B, -1), k.reshape(B, -1),
+                                          v.reshape(B, -1)], axis=1))
         q = rmsnorm(q, gain(w, pre + "q_norm"), eps)
         k = rmsnorm(k, gain(w, pre + "k_norm"), eps)
         q = rope_neox(q.transpose(1, 0, 2), pos, theta)       # [nq][B][D]
@@ -332,11 +344,15 @@ def draft_block(w: dict, ctx_k: np.ndarray, ctx_v: np.ndarray, p: int,
             vals = np.concatenate([ctx_v[l, j], v[j][order]], axis=0)
             for hh in range(j * grp, (j + 1) * grp):
                 o[:, hh, :] = attention(q[hh], keys, vals, scale)
+        rec["attn"].append(o.reshape(B, nq * D))
         h = h + matvec_rows(w, pre + "wo", (H, nq * D), o.reshape(B, nq * D))
+        rec["resid"].append(h)
         y = rmsnorm(h, gain(w, pre + "post_norm"), eps)
         gt = matvec_rows(w, pre + "wg", (F, H), y)
         up = matvec_rows(w, pre + "wu", (F, H), y)
-        h = h + matvec_rows(w, pre + "wd", (H, F), silu(gt) * up)
+        rec["mlp"].append(silu(gt) * up)
+        h = h + matvec_rows(w, pre + "wd", (H, F), rec["mlp"][-1])
+        rec["resid"].append(h)
     z = rmsnorm(h, gain(w, "final_norm"), eps)
     logits = matvec_rows(w, "lm_head", (V, H), z[1:], chunk=16384) if B > 1 \
         else np.zeros((0, V))

@@ -273,6 +273,32 @@ def test_gated_verify_and_status_arguments(lib):
     assert S(A, need - 1, A, check=False) == _lib.DFLASH_EWORKSPACE
 
 
+def test_stage_readout_arguments(lib):
+    """dflash_draft_stage checks its stage, index, rows and sizes on the host
+    before it enqueues the copy."""
+    E = _lib.DFLASH_EINVAL
+    need = _lib.dflash_workspace_size(fake_weights(), 0, 8)
+    R, Q, T, M = (_lib.DFLASH_STAGE_RESIDUAL, _lib.DFLASH_STAGE_QKV, _lib.DFLASH_STAGE_ATTN,
+                  _lib.DFLASH_STAGE_MLP)
+    big = 1 << 20
+
+    def S(ws=A, nb=need, st=R, idx=0, rows=8, dst=A, db=big):
+        return _lib.dflash_draft_stage(ws, nb, st, idx, rows, dst, db, None, check=False)
+
+    assert S(ws=None) == E and S(dst=None) == E
+    assert S(ws=A + 8) == E and S(dst=A + 4) == E
+    assert S(rows=0) == E and S(rows=9) == E
+    assert S(st=4) == E and S(st=-1) == E
+    assert S(st=R, idx=11) == E and S(st=R, idx=-1) == E
+    for st in (Q, T, M):
+        assert S(st=st, idx=5) == E
+    assert S(st=R, rows=8, db=8 * 2560 * 4 - 1) == E
+    assert S(st=Q, rows=3, db=3 * 7168 * 2 - 2) == E
+    assert S(st=T, rows=1, db=6144 * 2 - 2) == E
+    assert S(st=M, rows=2, db=2 * 7680 * 2 - 2) == E
+    assert S(nb=need // 4) == _lib.DFLASH_EWORKSPACE
+
+
 def test_packed_copy_may_stand_in_for_row_major_matrices(lib):
     """With the streaming copies set, the row-major matrices (fc, the layer
     matrices, the LM head) may be null -- the weights are then held once;

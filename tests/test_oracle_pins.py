@@ -407,6 +407,50 @@ def test_pass_uniform_attention_over_window_and_block():
         assert np.allclose(r["x_last"][row], want, rtol=1e-3, atol=1e-3), row
 
 
+def test_pass_stage_record_in_the_uniform_attention_case():
+    """The stages the pass records (for stage-wise comparison) in the
+    uniform-attention case above: the raw v projection is the Wv column, the
+    attention output of head 0 / head 3 is the mean of its group's values,
+    the residual after layer 0's attention is the embedding plus those means,
+    Wd = 0 leaves the MLP residual unchanged, and the last record is the
+    stream the final norm reads."""
+    H, D = 8, 4
+    E = _const_embed({1: 1.0, 10: 2.0})
+    wv = np.zeros((2 * D, H), dtype=np.float32)
+    wv[:, 0] = [1, 2, 3, 4, -1, -2, -3, -4]
+    wo = np.zeros((H, 16), dtype=np.float32)
+    for i in range(4):
+        wo[i, 0 * D + i] = 1.0
+        wo[4 + i, 3 * D + i] = 1.0
+    fill = {"embed": E, "layers.0.wv": wv, "layers.0.wo": wo,
+            "layers.0.wq": np.zeros((16, H)), "layers.0.wk": np.zeros((8, H)),
+            "layers.0.wd": np.zeros((H, 6)), "layers.1.wo": np.zeros((H, 16)),
+            "layers.1.wd": np.zeros((H, 6))}
+    w = tiny_weights(fill)
+    rng = np.random.default_rng(8)
+    p = 6
+    store = O.ContextStore(TINY)
+    store.put(rng.standard_normal((2, 2, p, D)), O.f16_round(rng.standard_normal((2, 2, p, D))), 0)
+    ck, cv = store.window(p)
+    rec = {}
+    r = O.draft_block(w, ck, cv, p=p, anchor_id=1, mask_id=10, block=3, g=TINY, stages=rec)
+    assert len(rec["resid"]) == 5 and len(rec["qkv"]) == len(rec["attn"]) == len(rec["mlp"]) == 2
+    assert [a.shape for a in rec["qkv"]] == [(3, 16 + 8 + 8)] * 2
+    v_blk = np.array([1, 2, 3, 4, -1, -2, -3, -4], dtype=np.float64)
+    assert np.allclose(rec["qkv"][0][:, 24:], v_blk, rtol=1e-3)
+    assert np.allclose(rec["qkv"][0][:, :24], 0.0)
+    vg0 = np.concatenate([cv[0, 0], np.repeat(v_blk[None, :4], 3, 0)]).mean(0)
+    vg1 = np.concatenate([cv[0, 1], np.repeat(v_blk[None, 4:], 3, 0)]).mean(0)
+    for row, e in ((0, 1.0), (1, 2.0), (2, 2.0)):
+        assert np.allclose(rec["attn"][0][row, 0:4], vg0, rtol=1e-3, atol=1e-3)
+        assert np.allclose(rec["attn"][0][row, 12:16], vg1, rtol=1e-3, atol=1e-3)
+        assert np.allclose(rec["resid"][0][row], e)
+        assert np.allclose(rec["resid"][1][row], np.concatenate([e + vg0, e + vg1]),
+                           rtol=1e-3, atol=1e-3)
+    assert np.array_equal(rec["resid"][2], rec["resid"][1])      # Wd = 0
+    assert np.array_equal(rec["resid"][4], r["x_last"])
+
+
 def test_pass_mlp_special_case():
     """Attention contributes nothing (Wv = Wo = 0); Wg picks y_0 * a, Wu
     picks y_0 * b, Wd sends unit j to h_j: h_j += silu(a y_0) * b y_0 for
