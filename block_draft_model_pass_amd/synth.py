@@ -18,7 +18,9 @@ Quantized backbones use a structure-of-arrays byte layout per matrix
 bytes, followed by ``N*K/32`` little-endian fp16 block scales in row order.
 Q4_0: within each 32-element block element ``j`` is the low nibble of byte
 ``j`` and element ``j+16`` the high nibble; the stored nibble is the value
-plus 8.
+plus 8.  Q5_0: the same nibbles and scales, then ``N*K/32`` little-endian
+uint32 words, bit ``j`` of a block's word the fifth bit of element ``j``;
+the stored 5-bit code is the value plus 16.
 """
 from __future__ import annotations
 
@@ -163,16 +165,37 @@ def quantize_q4_0(w: np.ndarray) -> np.ndarray:
     return np.concatenate([packed.reshape(-1), d16.reshape(-1).view(np.uint8)])
 
 
+def quantize_q5_0(w: np.ndarray) -> np.ndarray:
+    """Q5_0 bytes for an fp32 matrix [N][K]: per block the element of largest
+    magnitude maps to -16; scale = that element / -16 stored as fp16; code =
+    clip(round(w/scale) + 16, 0, 31), its low nibble packed as in Q4_0 and
+    its fifth bit in the block's high-bit word."""
+    N, K = w.shape
+    assert K % 32 == 0
+    blk = w.reshape(N, K // 32, 32).astype(np.float32)
+    idx = np.abs(blk).argmax(axis=2)
+    vmax = np.take_along_axis(blk, idx[:, :, None], axis=2)[:, :, 0]
+    d16 = (vmax / np.float32(-16.0)).astype(np.float16)
+    d32 = d16.astype(np.float32)
+    inv = np.where(d32 != 0, np.float32(1.0) / np.where(d32 != 0, d32, 1), 0)
+    code = np.clip(np.rint(blk * inv[:, :, None]) + 16, 0, 31).astype(np.uint32)
+    nib = (code & 15).astype(np.uint8)
+    packed = (nib[:, :, :16] | (nib[:, :, 16:] << 4)).astype(np.uint8)
+    hw = ((code >> 4) << np.arange(32, dtype=np.uint32)).sum(axis=2, dtype=np.uint32)
+    return np.concatenate([packed.reshape(-1), d16.reshape(-1).view(np.uint8),
+                           hw.astype("<u4").reshape(-1).view(np.uint8)])
+
+
 def make_weights(seed: int = SEED_WEIGHTS, fmt: str = "bf16",
                  geom: dict | None = None, lm_fmt: str = "bf16") -> dict:
     """All drafter tensors, the embedding and the LM head, keyed by name.
 
-    bf16 tensors are uint16 bit patterns of their shape.  With fmt 'q8_0' or
-    'q4_0' the 36 backbone matrices (fc and the 35 layer matrices) are flat
+    bf16 tensors are uint16 bit patterns of their shape.  With fmt 'q8_0',
+    'q4_0' or 'q5_0' the 36 backbone matrices (fc and the 35 layer matrices) are flat
     uint8 buffers in the layout described in the module docstring; gains and
     the embedding stay bf16.  lm_fmt 'q8_0' stores the LM head as Q8_0 blocks
     (same draws, quantized) in the same layout."""
-    assert fmt in ("bf16", "q8_0", "q4_0") and lm_fmt in ("bf16", "q8_0")
+    assert fmt in ("bf16", "q8_0", "q4_0", "q5_0") and lm_fmt in ("bf16", "q8_0")
     out = {}
     for ti, (name, shape, kind) in enumerate(weight_specs(geom)):
         words = (seed, ti)
@@ -184,8 +207,8 @@ def make_weights(seed: int = SEED_WEIGHTS, fmt: str = "bf16",
         else:
             v = _normal_f32(words, int(np.prod(shape)), 0.02, 0.0)
             v = v.reshape(shape)
-            out[name] = (quantize_q8_0(v) if qfmt == "q8_0"
-                         else quantize_q4_0(v))
+            out[name] = {"q8_0": quantize_q8_0, "q4_0": quantize_q4_0,
+                         "q5_0": quantize_q5_0}[qfmt](v)
     out["__format__"] = fmt
     out["__lm_format__"] = lm_fmt
     return out

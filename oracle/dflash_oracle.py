@@ -81,7 +81,7 @@ def f16_round(x) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# Weight access, including the Q8_0 / Q4_0 block formats
+# Weight access, including the Q8_0 / Q4_0 / Q5_0 block formats
 # --------------------------------------------------------------------------
 
 def dequant_q8_0(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
@@ -110,6 +110,26 @@ def dequant_q4_0(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
     return ((nib - 8.0) * d).reshape(rows, cols)
 
 
+def dequant_q5_0(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """Q5_0: blocks of 32 weights, fp16 scale d, a 5-bit code per weight:
+    the low four bits as in Q4_0 (element j of the block in the low nibble of
+    byte j, element j+16 in the high nibble) and the fifth in bit j of the
+    block's 32-bit word; value = d * (code - 16).  (PR #3322 names Q5_0
+    among the backbone formats without defining it; this is the plain
+    reading of a 5-bit sibling of Q4_0: offset half the code range.)  Byte
+    layout: rows*cols/2 packed bytes, rows*cols/32 fp16 scales, then
+    rows*cols/32 little-endian uint32 high-bit words."""
+    nb = rows * cols // 2
+    ns = rows * cols // 32
+    by = raw[:nb].reshape(rows, cols // 32, 16)
+    nib = np.concatenate([by & 0x0F, by >> 4], axis=2).astype(np.int64)
+    d = f16_decode(raw[nb:nb + 2 * ns].view(np.uint16)).reshape(rows, cols // 32, 1)
+    hw = raw[nb + 2 * ns:nb + 6 * ns].view("<u4").astype(np.int64).reshape(rows, cols // 32, 1)
+    hbit = (hw >> np.arange(32)) & 1
+    code = nib | (hbit << 4)
+    return ((code - 16).astype(np.float64) * d).reshape(rows, cols)
+
+
 def storage_format(w: dict, name: str) -> str:
     """Format of a stored matrix: the LM head has its own (bf16, or Q8_0 for
     the shared quantized head of PR #3322's later snapshot, "How to enable
@@ -130,6 +150,8 @@ def matrix(w: dict, name: str, shape) -> np.ndarray:
         return dequant_q8_0(a, *shape)
     if fmt == "q4_0":
         return dequant_q4_0(a, *shape)
+    if fmt == "q5_0":
+        return dequant_q5_0(a, *shape)
     raise ValueError(f"unknown weight format for {name}")
 
 

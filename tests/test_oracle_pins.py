@@ -104,6 +104,42 @@ def test_q4_0_dequant_hand_block():
     assert list(got) == want
 
 
+def test_q5_0_dequant_hand_block():
+    """Codes c_j = (7 j + 3) mod 32 (all 32 values once): low nibble of
+    element j in byte j % 16 (high half for j >= 16), fifth bit in bit j of
+    the word; value d * (c_j - 16)."""
+    code = [(7 * j + 3) % 32 for j in range(32)]
+    assert sorted(code) == list(range(32))
+    raw_q = bytes((code[j] & 15) | ((code[j + 16] & 15) << 4) for j in range(16))
+    word = sum((c >> 4) << j for j, c in enumerate(code))
+    d = np.array([0.375], dtype=np.float16)
+    raw = np.frombuffer(raw_q + d.tobytes() + int(word).to_bytes(4, "little"), dtype=np.uint8)
+    got = O.dequant_q5_0(raw.copy(), 1, 32)[0]
+    assert list(got) == [0.375 * (c - 16) for c in code]
+
+
+def test_q5_0_is_q4_0_shifted_by_its_fifth_bit():
+    """Same nibbles and scales: with every fifth bit clear a Q5_0 value is the
+    Q4_0 value minus 8 d, with every bit set plus 8 d (two rows, two blocks
+    each, mixed bits checked element by element)."""
+    rng = np.random.default_rng(3)
+    rows, cols = 2, 64
+    q = rng.integers(0, 256, rows * cols // 2, dtype=np.uint8)
+    d = rng.standard_normal(rows * cols // 32).astype(np.float16)
+    q4 = O.dequant_q4_0(np.concatenate([q, d.view(np.uint8)]), rows, cols)
+    dd = np.repeat(d.astype(np.float64).reshape(rows, cols // 32), 32, axis=1)
+    for words, shift in ((np.zeros(4, np.uint32), -8), (np.full(4, 0xFFFFFFFF, np.uint32), 8)):
+        raw = np.concatenate([q, d.view(np.uint8), words.astype("<u4").view(np.uint8)])
+        assert np.array_equal(O.dequant_q5_0(raw, rows, cols), q4 + shift * dd)
+    words = rng.integers(0, 2 ** 32, 4, dtype=np.uint64).astype(np.uint32)
+    raw = np.concatenate([q, d.view(np.uint8), words.astype("<u4").view(np.uint8)])
+    got = O.dequant_q5_0(raw, rows, cols)
+    for r in range(rows):
+        for k in range(cols):
+            bit = (int(words[r * 2 + k // 32]) >> (k % 32)) & 1
+            assert got[r, k] == q4[r, k] + (8 if bit else -8) * dd[r, k]
+
+
 def test_quant_round_trip_within_half_step():
     """The harness quantizers and the oracle's decoders agree: every decoded
     weight is within half a quantisation step of the fp32 source."""
@@ -119,6 +155,12 @@ def test_quant_round_trip_within_half_step():
     err4 = np.abs(d4 - w).reshape(4, 2, 32)
     assert np.all(err4 <= step4[..., None] * 1.0 + 1e-4)
     assert np.mean(err4 <= step4[..., None] * 0.5 + 1e-4) > 0.9
+    # Q5_0 codes span -16..15 steps of amax/16: the same one-step clip bound.
+    d5 = O.dequant_q5_0(synth.quantize_q5_0(w), 4, 64)
+    step5 = np.abs(w.reshape(4, 2, 32)).max(axis=2) / 16
+    err5 = np.abs(d5 - w).reshape(4, 2, 32)
+    assert np.all(err5 <= step5[..., None] * 1.0 + 1e-4)
+    assert np.mean(err5 <= step5[..., None] * 0.5 + 1e-4) > 0.9
 
 
 # ---------------------------------------------------------------- rmsnorm
