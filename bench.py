@@ -34,8 +34,9 @@ METRIC = "DFlash draft passes/sec (ctx 8192, block 8) + achieved HBM GB/s vs pea
 
 
 # Stored bytes per weight of the layer matrices: bf16, Q8_0 (32 int8 + fp16
-# scale per 32 weights), Q4_0 (16 bytes of nibbles + fp16 scale per 32).
-BYTES_PER_WEIGHT = {"bf16": 2.0, "q8_0": 34 / 32, "q4_0": 18 / 32}
+# scale per 32 weights), Q4_0 (16 bytes of nibbles + fp16 scale per 32), Q5_0
+# (Q4_0 plus a 4-byte word of fifth bits per 32).
+BYTES_PER_WEIGHT = {"bf16": 2.0, "q8_0": 34 / 32, "q4_0": 18 / 32, "q5_0": 22 / 32}
 
 
 def pass_bytes(n_ctx: int, block: int = BLOCK, fmt: str = "bf16", lm_fmt: str = "bf16") -> int:
@@ -132,7 +133,7 @@ def main():
     ap.add_argument("--fusion-rows", type=int, default=32768,
                     help="rows of the timed context-fusion GEMM (0 = skip)")
     ap.add_argument("--no-quant", action="store_true",
-                    help="skip the Q8_0 / Q4_0 backbone passes (ctx 8192, block 4)")
+                    help="skip the Q8_0 / Q4_0 / Q5_0 backbone passes (ctx 8192, block 4)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -345,14 +346,14 @@ def main():
     del sdr, taps_s, ctx_s
     torch.cuda.empty_cache()
 
-    # Quantized backbone (Q8_0 / Q4_0 layer matrices, bf16 LM head): draft
+    # Quantized backbone (Q8_0 / Q4_0 / Q5_0 layer matrices, bf16 LM head): draft
     # passes at ctx 8192, block 4, on a context projected by those weights.
     # Also the Q8_0 shared LM head: bf16 backbone at blocks 8 and 4, and with
     # a Q8_0 backbone at block 4 (every streamed matrix in Q8_0).
     quant, q8_lm = {}, {}
     if not args.no_quant:
-        runs = (("q8_0", "bf16", (4,)), ("q4_0", "bf16", (4,)), ("q8_0", "q8_0", (4,)),
-                ("bf16", "q8_0", (8, 4)))
+        runs = (("q8_0", "bf16", (4,)), ("q4_0", "bf16", (4,)), ("q5_0", "bf16", (4,)),
+                ("q8_0", "q8_0", (4,)), ("bf16", "q8_0", (8, 4)))
         for fmt, lmf, blocks in runs:
             qw = DeviceWeights(synth.make_weights(fmt=fmt, lm_fmt=lmf))
             qkv_ring = KVRing(synth.WINDOW, synth.WINDOW)

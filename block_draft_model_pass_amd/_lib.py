@@ -26,6 +26,7 @@ DFLASH_STAGE_MLP = 3
 DFLASH_W_BF16 = 0
 DFLASH_W_Q8_0 = 1
 DFLASH_W_Q4_0 = 2
+DFLASH_W_Q5_0 = 3
 
 LAYER_FIELDS = ("in_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo",
                 "post_norm", "wg", "wu", "wd")

@@ -134,7 +134,7 @@ int check_weights(const dflash_weights* w, bool need_rowmajor = false) {
   if (w->rope_theta != 1.0e7f || w->attn_scale != 0.0625f || w->rms_eps != 1.0e-6f)
     return DFLASH_EGEOMETRY;
   if (w->backbone_type != DFLASH_W_BF16 && w->backbone_type != DFLASH_W_Q8_0 &&
-      w->backbone_type != DFLASH_W_Q4_0)
+      w->backbone_type != DFLASH_W_Q4_0 && w->backbone_type != DFLASH_W_Q5_0)
     return DFLASH_EINVAL;
   if (w->lm_head_type != DFLASH_W_BF16 && w->lm_head_type != DFLASH_W_Q8_0) return DFLASH_EINVAL;
   const bool rm = need_rowmajor || !w->packed;  // row-major matrices required
@@ -164,18 +164,20 @@ int check_kv(const dflash_kv* kv) {
 
 // The streaming copies inside w->packed: the LM head (bf16), then every
 // layer's wq, wk, wv, wo, wg, wu, wd in the backbone's format: bf16, or the
-// Q8_0 / Q4_0 quants followed by their block scales, both regrouped per
-// 16-row tile and 64-byte row piece.
+// quants followed by their block scales (and Q5_0's high-bit words), all
+// regrouped per 16-row tile and 64-byte row piece.
 struct PackedMat {
   int N, K;
 };
 constexpr PackedMat LAYER_MATS[7] = {{NQ * D, H}, {NKV * D, H}, {NKV * D, H}, {H, NQ * D},
                                      {F, H},      {F, H},       {H, F}};
 
-// Bytes of one [N][K] matrix in format fmt (quants, then scales).
+// Bytes of one [N][K] matrix in format fmt (quants, then scales, then
+// Q5_0's high-bit words).
 size_t mat_bytes(int fmt, size_t N, size_t K) {
   if (fmt == DFLASH_W_Q8_0) return N * K + N * (K / 32) * 2;
   if (fmt == DFLASH_W_Q4_0) return N * K / 2 + N * (K / 32) * 2;
+  if (fmt == DFLASH_W_Q5_0) return N * K / 2 + N * (K / 32) * 6;
   return 2 * N * K;
 }
 
@@ -212,7 +214,8 @@ void packed_layer(const dflash_weights* w, int l, uint8_t* (&out)[7]) {
 // One matrix into its streaming copy: the 64-byte row pieces of the quants
 // (or bf16 values) move as the bf16 shuffle moves 32-element blocks; the
 // scales of a quantized matrix follow as 4-byte (Q8_0: one 64-k piece) or
-// 8-byte (Q4_0: one 128-k piece) units per row.
+// 8-byte (Q4_0 / Q5_0: one 128-k piece) units per row, and Q5_0's high-bit
+// words as 16-byte units with their bits reordered for the decoder.
 hipError_t pack_matrix(int fmt, const void* src, int N, int K, void* dst, hipStream_t st) {
   if (fmt == DFLASH_W_BF16) return launch_pack_bf16(src, N, K, dst, st);
   const size_t qbytes = fmt == DFLASH_W_Q8_0 ? static_cast<size_t>(N) * K : static_cast<size_t>(N) * K / 2;
@@ -220,8 +223,12 @@ hipError_t pack_matrix(int fmt, const void* src, int N, int K, void* dst, hipStr
   hipError_t e = launch_pack_bf16(src, N, kq, dst, st);
   if (e != hipSuccess) return e;
   const int per_row = fmt == DFLASH_W_Q8_0 ? K / 64 : K / 128;
-  return launch_pack_units(static_cast<const uint8_t*>(src) + qbytes, N, per_row,
-                           fmt == DFLASH_W_Q8_0 ? 4 : 8, static_cast<uint8_t*>(dst) + qbytes, st);
+  const uint8_t* s8 = static_cast<const uint8_t*>(src);
+  uint8_t* d8 = static_cast<uint8_t*>(dst);
+  e = launch_pack_units(s8 + qbytes, N, per_row, fmt == DFLASH_W_Q8_0 ? 4 : 8, d8 + qbytes, st);
+  if (e != hipSuccess || fmt != DFLASH_W_Q5_0) return e;
+  const size_t sbytes = static_cast<size_t>(N) * (K / 32) * 2;
+  return launch_pack_q5_bits(s8 + qbytes + sbytes, N, per_row, d8 + qbytes + sbytes, st);
 }
 
 SegTable seg1(const void* p, int rows) {

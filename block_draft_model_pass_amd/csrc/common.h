@@ -125,13 +125,16 @@ struct SegTable {
   int nseg;
 };
 
-enum WFormat { W_BF16 = 0, W_Q8_0 = 1, W_Q4_0 = 2 };
+enum WFormat { W_BF16 = 0, W_Q8_0 = 1, W_Q4_0 = 2, W_Q5_0 = 3 };
+
+// Formats whose 64-byte quant pieces cover 128 k (nibbles).
+constexpr bool nibble_fmt(int fmt) { return fmt == W_Q4_0 || fmt == W_Q5_0; }
 
 // ---------------------------------------------------------------- quantized weights
-// Q8_0 / Q4_0 blocks ("Quantized drafter" formats: 32 consecutive input-dim
-// weights of one output row share an fp16 scale) are decoded to fp16 in
-// registers.  The integer (q, or nibble - 8) is exact in fp16; the only
-// rounding is that of q * scale (relative 2^-11).  A decoded group is the 8
+// Q8_0 / Q4_0 / Q5_0 blocks (32 consecutive input-dim weights of one output
+// row share an fp16 scale) are decoded to fp16 in registers.  The integer
+// (q, nibble - 8, or 5-bit code - 16) is exact in fp16; the only rounding is
+// that of q * scale (relative 2^-11).  A decoded group is the 8
 // fp16 values one lane feeds to one MFMA 16x16x32 f16.
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -171,6 +174,36 @@ __device__ __forceinline__ uint4 dq4(uint32_t w0, uint32_t w1, bool hi, h2 s) {
                     dq_pair(u8pair_f16(n1, 0), off, s), dq_pair(u8pair_f16(n1, 1), off, s));
 }
 
+// Q5_0: the low (hi = false) or high nibbles of the 8 bytes w0, w1 with
+// their fifth bits hb0 / hb1 already at bits 4, 12, 20, 28 (one per byte),
+// minus 16, times s.
+__device__ __forceinline__ uint4 dq5(uint32_t w0, uint32_t w1, bool hi, uint32_t hb0, uint32_t hb1,
+                                     h2 s) {
+  const h2 off = {static_cast<_Float16>(1040.0f), static_cast<_Float16>(1040.0f)};
+  const uint32_t n0 = ((hi ? w0 >> 4 : w0) & 0x0f0f0f0fu) | hb0;
+  const uint32_t n1 = ((hi ? w1 >> 4 : w1) & 0x0f0f0f0fu) | hb1;
+  return make_uint4(dq_pair(u8pair_f16(n0, 0), off, s), dq_pair(u8pair_f16(n0, 1), off, s),
+                    dq_pair(u8pair_f16(n1, 0), off, s), dq_pair(u8pair_f16(n1, 1), off, s));
+}
+
+// Fifth bits of elements 4 C .. 4 C + 3 of a Q5_0 block at bits 4, 12, 20,
+// 28, from the block's word in the streaming copy, where the bit of element
+// 4 C + c sits at bit C + 8 c (one shift and a mask) ...
+template <int C>
+__device__ __forceinline__ uint32_t q5_bits_packed(uint32_t hw) {
+  if constexpr (C <= 4) return (hw << (4 - C)) & 0x10101010u;
+  else return (hw >> (C - 4)) & 0x10101010u;
+}
+
+// ... or from the row-major word (bit j = element j): the nibble t of bits
+// 4 C .. 4 C + 3 spread to one bit per byte (t * 0x204081 puts bit i of t at
+// bit 8 i, no carries since the four copies do not overlap).
+template <int C>
+__device__ __forceinline__ uint32_t q5_bits_rowmajor(uint32_t hw) {
+  const uint32_t t = (hw >> (4 * C)) & 0xfu;
+  return ((t * 0x00204081u) & 0x01010101u) << 4;
+}
+
 // Activation element in the MFMA input format of a weight format: bf16 next
 // to bf16 weights, fp16 next to decoded quantized weights.
 template <int FMT>
@@ -202,8 +235,13 @@ hipError_t launch_pack_bf16(const void* src, int N, int K, void* dst, hipStream_
 // tiles x per_row x 16 rows (the block scales of a packed quantized matrix).
 hipError_t launch_pack_units(const void* src, int N, int per_row, int unit, void* dst,
                              hipStream_t st);
+// Q5_0 high-bit words of an [N][per_row * 4] array (one word per 32-element
+// block, bit j = element j) regrouped as 16-row tiles x per_row x 16 rows of
+// 16-byte units, each word's bits reordered: element 8 a + 4 b + c at bit
+// 2 a + b + 8 c.
+hipError_t launch_pack_q5_bits(const void* src, int N, int per_row, void* dst, hipStream_t st);
 
-// Quantized [rows][K] matrix (fmt Q8_0 / Q4_0) -> rows row0 .. row0+rows-1
+// Quantized [rows][K] matrix (fmt Q8_0 / Q4_0 / Q5_0) -> rows row0 .. row0+rows-1
 // of a bf16 [.][K] matrix in the streaming layout (rows, row0 multiples of 16).
 // src: row-major blocks, or the matrix's streaming copy when `packed`.
 hipError_t launch_dequant_bf16(const void* src, int fmt, int rows, int K, uint16_t* dst, int row0,

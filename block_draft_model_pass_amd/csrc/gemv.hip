@@ -105,11 +105,12 @@ template <int FMT> struct KPerLoad;  // k covered by one 16-byte load of all fou
 template <> struct KPerLoad<W_BF16> { static constexpr int v = 32; };
 template <> struct KPerLoad<W_Q8_0> { static constexpr int v = 64; };
 template <> struct KPerLoad<W_Q4_0> { static constexpr int v = 128; };
+template <> struct KPerLoad<W_Q5_0> { static constexpr int v = 128; };
 
 // k offset (from the wave's kbeg) of the i-th 8-element activation group of
 // lane group g, matching the weight slots of each format:
 //   bf16 load i -> k = 32 i + 8 g;  Q8_0 load i -> 16 elements at 64 i + 16 g;
-//   Q4_0 load i -> the 32-element quant block at 128 i + 32 g.
+//   Q4_0 / Q5_0 load i -> the 32-element quant block at 128 i + 32 g.
 template <int FMT>
 __device__ __forceinline__ int xslot(int i, int g) {
   if constexpr (FMT == W_BF16) return 32 * i + 8 * g;
@@ -147,12 +148,15 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(GemvArgs a) {
   const size_t rk = static_cast<size_t>(row) * a.K;
   const size_t sb = static_cast<size_t>(row) * (a.K / 32) + kbeg / 32;
   uint4 w[NL];
-  uint32_t sc[NL];
+  uint32_t sc[NL], hw[FMT == W_Q5_0 ? NL : 1];
+  // Q5_0 high-bit words follow the quants and the scales
+  const uint8_t* hb = sr.base + static_cast<size_t>(sr.rows) * a.K / 2 + static_cast<size_t>(sr.rows) * a.K / 16;
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     if constexpr (PACKED) {
       // streaming copy: 16-row tile, then 64-byte row pieces (32 bf16, 64
-      // Q8_0 or 128 Q4_0 k), then the lanes; scales per tile and piece
+      // Q8_0 or 128 Q4_0 / Q5_0 k), then the lanes; scales (and high-bit
+      // words) per tile and piece
       constexpr int PK = FMT == W_BF16 ? 32 : (FMT == W_Q8_0 ? 64 : 128);
       const size_t pc = static_cast<size_t>(row >> 4) * (a.K / PK) + kbeg / PK + i;
       w[i] = ld16_stream(reinterpret_cast<const uint16_t*>(sr.base + (pc * 64 + r + 16 * g) * 16));
@@ -164,6 +168,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(GemvArgs a) {
       else
         sc[i] = *reinterpret_cast<const uint16_t*>(sr.base + static_cast<size_t>(sr.rows) * a.K / 2 +
                                                    2 * (pc * 64 + r * 4 + g));
+      if constexpr (FMT == W_Q5_0) hw[i] = *reinterpret_cast<const uint32_t*>(hb + 4 * (pc * 64 + r * 4 + g));
     } else if constexpr (FMT == W_BF16) {
       w[i] = ld16_stream(reinterpret_cast<const uint16_t*>(sr.base) + rk + kbeg + 32 * i + 8 * g);
       sc[i] = 0;
@@ -175,6 +180,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(GemvArgs a) {
       w[i] = ld16_stream(reinterpret_cast<const uint16_t*>(sr.base + (rk + kbeg) / 2 + 64 * i + 16 * g));
       sc[i] = *reinterpret_cast<const uint16_t*>(sr.base + static_cast<size_t>(sr.rows) * a.K / 2 +
                                                  2 * (sb + 4 * i + g));
+      if constexpr (FMT == W_Q5_0) hw[i] = *reinterpret_cast<const uint32_t*>(hb + 4 * (sb + 4 * i + g));
     }
   }
   uint4 x[NX];
@@ -191,12 +197,30 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(GemvArgs a) {
       const h2 s2 = scale_h2(sc[i]);
       acc = mfma_f16(dq8(w[i].x, w[i].y, s2), bf16x8_to_f16(x[2 * i]), acc);
       acc = mfma_f16(dq8(w[i].z, w[i].w, s2), bf16x8_to_f16(x[2 * i + 1]), acc);
-    } else {
+    } else if constexpr (FMT == W_Q4_0) {
       const h2 s2 = scale_h2(sc[i]);
       acc = mfma_f16(dq4(w[i].x, w[i].y, false, s2), bf16x8_to_f16(x[4 * i]), acc);
       acc = mfma_f16(dq4(w[i].z, w[i].w, false, s2), bf16x8_to_f16(x[4 * i + 1]), acc);
       acc = mfma_f16(dq4(w[i].x, w[i].y, true, s2), bf16x8_to_f16(x[4 * i + 2]), acc);
       acc = mfma_f16(dq4(w[i].z, w[i].w, true, s2), bf16x8_to_f16(x[4 * i + 3]), acc);
+    } else {  // Q5_0: elements 4 C .. 4 C + 3 take the fifth bits of group C
+      const h2 s2 = scale_h2(sc[i]);
+      uint32_t b[8];
+      if constexpr (PACKED) {
+        b[0] = q5_bits_packed<0>(hw[i]), b[1] = q5_bits_packed<1>(hw[i]);
+        b[2] = q5_bits_packed<2>(hw[i]), b[3] = q5_bits_packed<3>(hw[i]);
+        b[4] = q5_bits_packed<4>(hw[i]), b[5] = q5_bits_packed<5>(hw[i]);
+        b[6] = q5_bits_packed<6>(hw[i]), b[7] = q5_bits_packed<7>(hw[i]);
+      } else {
+        b[0] = q5_bits_rowmajor<0>(hw[i]), b[1] = q5_bits_rowmajor<1>(hw[i]);
+        b[2] = q5_bits_rowmajor<2>(hw[i]), b[3] = q5_bits_rowmajor<3>(hw[i]);
+        b[4] = q5_bits_rowmajor<4>(hw[i]), b[5] = q5_bits_rowmajor<5>(hw[i]);
+        b[6] = q5_bits_rowmajor<6>(hw[i]), b[7] = q5_bits_rowmajor<7>(hw[i]);
+      }
+      acc = mfma_f16(dq5(w[i].x, w[i].y, false, b[0], b[1], s2), bf16x8_to_f16(x[4 * i]), acc);
+      acc = mfma_f16(dq5(w[i].z, w[i].w, false, b[2], b[3], s2), bf16x8_to_f16(x[4 * i + 1]), acc);
+      acc = mfma_f16(dq5(w[i].x, w[i].y, true, b[4], b[5], s2), bf16x8_to_f16(x[4 * i + 2]), acc);
+      acc = mfma_f16(dq5(w[i].z, w[i].w, true, b[6], b[7], s2), bf16x8_to_f16(x[4 * i + 3]), acc);
     }
   }
   acc = reduce_waves<NW>(acc, red, wave, lane);
@@ -206,7 +230,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(GemvArgs a) {
   }
 }
 
-// Quantized [rows][K] (fmt Q8_0 / Q4_0) -> rows row0.. of a bf16 [.][K]
+// Quantized [rows][K] (fmt Q8_0 / Q4_0 / Q5_0) -> rows row0.. of a bf16 [.][K]
 // matrix in the streaming layout (the 8 bf16 values of an output group are
 // one lane's contiguous 16 bytes there).  One thread per 8 output elements.
 // The source is either the row-major blocks (quants row-major, then scales
@@ -219,7 +243,7 @@ __global__ __launch_bounds__(256) void k_dequant_bf16(const uint8_t* src, int ro
   const size_t qbytes = FMT == W_Q8_0 ? static_cast<size_t>(rows) * K : static_cast<size_t>(rows) * K / 2;
   for (size_t e = blockIdx.x * 256ull + threadIdx.x; e < n8; e += static_cast<size_t>(gridDim.x) * 256) {
     const size_t r = e * 8 / K, k = e * 8 % K;  // row and first element of the group
-    // byte offset of the group's quants (8 bytes for Q8_0; for Q4_0 the 8
+    // byte offset of the group's quants (8 bytes for Q8_0; for Q4_0 / Q5_0 the 8
     // bytes holding its nibbles) and element offset of its block scale
     size_t qoff, soff;
     if constexpr (!PACKED) {
@@ -234,6 +258,11 @@ __global__ __launch_bounds__(256) void k_dequant_bf16(const uint8_t* src, int ro
     }
     const float s = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(src + qbytes + 2 * soff));
     const uint2 q = *reinterpret_cast<const uint2*>(src + qoff);
+    // Q5_0: the block's high-bit word (same index as its scale), after the scales
+    uint32_t hw = 0;
+    if constexpr (FMT == W_Q5_0)
+      hw = *reinterpret_cast<const uint32_t*>(src + qbytes + static_cast<size_t>(rows) * (K / 32) * 2 +
+                                              4 * soff);
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -243,7 +272,13 @@ __global__ __launch_bounds__(256) void k_dequant_bf16(const uint8_t* src, int ro
         v[i] = static_cast<float>(static_cast<int8_t>(byte)) * s;
       } else {  // element j of a block: byte j % 16, low nibble if j < 16 else high
         const int nib = k % 32 < 16 ? static_cast<int>(byte & 15u) : static_cast<int>(byte >> 4);
-        v[i] = static_cast<float>(nib - 8) * s;
+        if constexpr (FMT == W_Q4_0) {
+          v[i] = static_cast<float>(nib - 8) * s;
+        } else {  // fifth bit of element j: bit j, or bit 2 (j/8) + (j/4)%2 + 8 (j%4) when packed
+          const int j = static_cast<int>(k % 32) + i;
+          const int bit = PACKED ? 2 * (j >> 3) + ((j >> 2) & 1) + 8 * (j & 3) : j;
+          v[i] = static_cast<float>((nib | static_cast<int>(((hw >> bit) & 1u) << 4)) - 16) * s;
+        }
       }
     }
     uint32_t o[4];
@@ -487,6 +522,7 @@ hipError_t launch_gemv_nw(const GemvArgs& a, hipStream_t st) {
       case W_BF16: hipLaunchKernelGGL((k_gemv<W_BF16, NW, KBW, true>), grid, block, 0, st, a); break;
       case W_Q8_0: hipLaunchKernelGGL((k_gemv<W_Q8_0, NW, KBW, true>), grid, block, 0, st, a); break;
       case W_Q4_0: hipLaunchKernelGGL((k_gemv<W_Q4_0, NW, KBW, true>), grid, block, 0, st, a); break;
+      case W_Q5_0: hipLaunchKernelGGL((k_gemv<W_Q5_0, NW, KBW, true>), grid, block, 0, st, a); break;
       default: return hipErrorInvalidValue;
     }
   } else {
@@ -494,6 +530,7 @@ hipError_t launch_gemv_nw(const GemvArgs& a, hipStream_t st) {
       case W_BF16: hipLaunchKernelGGL((k_gemv<W_BF16, NW, KBW, false>), grid, block, 0, st, a); break;
       case W_Q8_0: hipLaunchKernelGGL((k_gemv<W_Q8_0, NW, KBW, false>), grid, block, 0, st, a); break;
       case W_Q4_0: hipLaunchKernelGGL((k_gemv<W_Q4_0, NW, KBW, false>), grid, block, 0, st, a); break;
+      case W_Q5_0: hipLaunchKernelGGL((k_gemv<W_Q5_0, NW, KBW, false>), grid, block, 0, st, a); break;
       default: return hipErrorInvalidValue;
     }
   }
@@ -530,6 +567,10 @@ hipError_t launch_dequant_bf16(const void* src, int fmt, int rows, int K, uint16
     hipLaunchKernelGGL((k_dequant_bf16<W_Q4_0, true>), dim3(grid), dim3(256), 0, st, s8, rows, K, dst, row0);
   else if (fmt == W_Q4_0)
     hipLaunchKernelGGL((k_dequant_bf16<W_Q4_0, false>), dim3(grid), dim3(256), 0, st, s8, rows, K, dst, row0);
+  else if (fmt == W_Q5_0 && packed)
+    hipLaunchKernelGGL((k_dequant_bf16<W_Q5_0, true>), dim3(grid), dim3(256), 0, st, s8, rows, K, dst, row0);
+  else if (fmt == W_Q5_0)
+    hipLaunchKernelGGL((k_dequant_bf16<W_Q5_0, false>), dim3(grid), dim3(256), 0, st, s8, rows, K, dst, row0);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

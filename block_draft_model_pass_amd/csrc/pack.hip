@@ -4,8 +4,9 @@
 // A 64-lane load of one k block then reads 1 KiB of contiguous memory
 // (instead of 64 bytes from each of 16 rows 5 KiB or more apart, which
 // streams at about 2/3 of the rate on MI355X).  The same byte shuffle packs
-// Q8_0 / Q4_0 quants (64-byte row pieces = 64 or 128 k); their fp16 block
-// scales are packed per 16-row tile and k piece as 16 rows x U bytes.
+// Q8_0 / Q4_0 / Q5_0 quants (64-byte row pieces = 64 or 128 k); their fp16
+// block scales (and Q5_0's high-bit words) are packed per 16-row tile and k
+// piece as 16 rows x U bytes.
 #include "common.h"
 
 namespace dfl {
@@ -42,7 +43,41 @@ __global__ __launch_bounds__(256) void k_pack_units(const uint8_t* __restrict__ 
   }
 }
 
+// Fifth bit of block element e = 8 a + 4 b + c moves to bit 2 a + b + 8 c.
+__device__ __forceinline__ uint32_t q5_reorder(uint32_t w) {
+  uint32_t o = 0;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    const int a = e >> 3, b = (e >> 2) & 1, c = e & 3;
+    o |= ((w >> e) & 1u) << (2 * a + b + 8 * c);
+  }
+  return o;
+}
+
+// 16-byte units (the 4 words of one 128-k piece of a row): dst unit
+// ((r / 16) * per_row + j) * 16 + r % 16 takes source unit r * per_row + j.
+__global__ __launch_bounds__(256) void k_pack_q5_bits(const uint32_t* __restrict__ src, int N,
+                                                      int per_row, uint32_t* __restrict__ dst) {
+  const size_t n = static_cast<size_t>(N) * per_row;
+  for (size_t q = blockIdx.x * 256ull + threadIdx.x; q < n; q += static_cast<size_t>(gridDim.x) * 256) {
+    const size_t blk = q >> 4, r16 = q & 15;
+    const size_t t = blk / per_row, j = blk % per_row;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * ((16 * t + r16) * per_row + j));
+    *reinterpret_cast<uint4*>(dst + 4 * q) =
+        make_uint4(q5_reorder(v.x), q5_reorder(v.y), q5_reorder(v.z), q5_reorder(v.w));
+  }
+}
+
 }  // namespace
+
+hipError_t launch_pack_q5_bits(const void* src, int N, int per_row, void* dst, hipStream_t st) {
+  if (N <= 0 || N % 16 || per_row <= 0) return hipErrorInvalidValue;
+  const size_t n = static_cast<size_t>(N) * per_row;
+  const int grid = static_cast<int>(n / 256 < 8192 ? (n + 255) / 256 : 8192);
+  hipLaunchKernelGGL(k_pack_q5_bits, dim3(grid), dim3(256), 0, st, static_cast<const uint32_t*>(src),
+                     N, per_row, static_cast<uint32_t*>(dst));
+  return hipGetLastError();
+}
 
 hipError_t launch_pack_units(const void* src, int N, int per_row, int unit, void* dst,
                              hipStream_t st) {

@@ -404,6 +404,7 @@ __device__ __forceinline__ int xrow(int r, int B) { return r < B ? r : 0; }
 //          + 8 m), all inside quant block kbeg/32 + 2 i + g/2.
 //   Q4_0 : load i is the whole quant block kbeg/32 + 4 i + g (four MFMAs:
 //          elements 8 m .. 8 m + 7 of the block).
+//   Q5_0 : as Q4_0, plus the block's 32-bit word of fifth bits.
 // Every format is read from the matrix's streaming copy, where the 64 lanes'
 // 16 bytes of one load are 1 KiB of contiguous memory (and the quantized
 // formats' scales of that load 64 or 128 contiguous bytes).
@@ -413,11 +414,13 @@ template <int FMT> struct KPerLoad;  // k covered by one load of all four lane g
 template <> struct KPerLoad<W_BF16> { static constexpr int v = 32; };
 template <> struct KPerLoad<W_Q8_0> { static constexpr int v = 64; };
 template <> struct KPerLoad<W_Q4_0> { static constexpr int v = 128; };
+template <> struct KPerLoad<W_Q5_0> { static constexpr int v = 128; };
 
 template <int FMT, int N>
 struct WTile {
   uint4 q[N];
   uint32_t s[FMT == W_BF16 ? 1 : N];
+  uint32_t h[FMT == W_Q5_0 ? N : 1];  // Q5_0 fifth bits (streaming-copy bit order)
 };
 
 struct WMat {
@@ -450,11 +453,13 @@ __device__ __forceinline__ void load_wt(WTile<FMT, N>& t, WMat m, int row, int k
         t.q[i0] = ldb(b + (pc * 64 + (row & 15) + 16 * g) * 16);
         t.s[i0] = gld<uint16_t>(b + static_cast<size_t>(m.rows) * m.K +
                                 2 * (pc * 32 + (row & 15) * 2 + (g >> 1)));
-      } else {  // piece = 128 k: 1 KiB of quants, 128 B of scales
+      } else {  // piece = 128 k: 1 KiB of quants, 128 B of scales (Q5_0: 256 B of bits)
         const size_t pc = static_cast<size_t>(row >> 4) * (m.K >> 7) + (kbeg >> 7) + i;
+        const size_t sq = static_cast<size_t>(m.rows) * m.K / 2;
         t.q[i0] = ldb(b + (pc * 64 + (row & 15) + 16 * g) * 16);
-        t.s[i0] = gld<uint16_t>(b + static_cast<size_t>(m.rows) * m.K / 2 +
-                                2 * (pc * 64 + (row & 15) * 4 + g));
+        t.s[i0] = gld<uint16_t>(b + sq + 2 * (pc * 64 + (row & 15) * 4 + g));
+        if constexpr (FMT == W_Q5_0)
+          t.h[i0] = gld<uint32_t>(b + sq + sq / 8 + 4 * (pc * 64 + (row & 15) * 4 + g));
       }
     }
   } else {
@@ -462,9 +467,11 @@ __device__ __forceinline__ void load_wt(WTile<FMT, N>& t, WMat m, int row, int k
     for (int i0 = 0; i0 < N; ++i0) {
       t.q[i0] = make_uint4(0, 0, 0, 0);
       if constexpr (FMT != W_BF16) t.s[i0] = 0u;
+      if constexpr (FMT == W_Q5_0) t.h[i0] = 0u;
     }
   }
   if constexpr (FMT == W_BF16) t.s[0] = 0u;
+  if constexpr (FMT != W_Q5_0) t.h[0] = 0u;
 }
 
 template <int FMT, int N>
@@ -483,7 +490,7 @@ __device__ __forceinline__ f32x4 mma_wt(const WTile<FMT, N>& t, const uint16_t* 
         const uint4 x1 = *reinterpret_cast<const uint4*>(xp + 8);
         acc = mfma_f16(dq8(t.q[i].x, t.q[i].y, sc), x0, acc);
         acc = mfma_f16(dq8(t.q[i].z, t.q[i].w, sc), x1, acc);
-      } else {
+      } else if constexpr (FMT == W_Q4_0) {
         const h2 sc = scale_h2(t.s[i]);
         const uint16_t* xp = xr + kbeg + 128 * i + 32 * g;
         const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
@@ -494,6 +501,22 @@ __device__ __forceinline__ f32x4 mma_wt(const WTile<FMT, N>& t, const uint16_t* 
         acc = mfma_f16(dq4(t.q[i].z, t.q[i].w, false, sc), x1, acc);
         acc = mfma_f16(dq4(t.q[i].x, t.q[i].y, true, sc), x2, acc);
         acc = mfma_f16(dq4(t.q[i].z, t.q[i].w, true, sc), x3, acc);
+      } else {  // Q5_0: elements 4 C .. 4 C + 3 take the fifth bits of group C
+        const h2 sc = scale_h2(t.s[i]);
+        const uint32_t hw = t.h[i];
+        const uint16_t* xp = xr + kbeg + 128 * i + 32 * g;
+        const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
+        const uint4 x1 = *reinterpret_cast<const uint4*>(xp + 8);
+        const uint4 x2 = *reinterpret_cast<const uint4*>(xp + 16);
+        const uint4 x3 = *reinterpret_cast<const uint4*>(xp + 24);
+        acc = mfma_f16(dq5(t.q[i].x, t.q[i].y, false, q5_bits_packed<0>(hw), q5_bits_packed<1>(hw), sc),
+                       x0, acc);
+        acc = mfma_f16(dq5(t.q[i].z, t.q[i].w, false, q5_bits_packed<2>(hw), q5_bits_packed<3>(hw), sc),
+                       x1, acc);
+        acc = mfma_f16(dq5(t.q[i].x, t.q[i].y, true, q5_bits_packed<4>(hw), q5_bits_packed<5>(hw), sc),
+                       x2, acc);
+        acc = mfma_f16(dq5(t.q[i].z, t.q[i].w, true, q5_bits_packed<6>(hw), q5_bits_packed<7>(hw), sc),
+                       x3, acc);
       }
     }
   }
@@ -1551,11 +1574,11 @@ __device__ __forceinline__ void gu_phase(const PassArgs& a, Smem& s, int l, int 
 }
 
 // Down projection: block w < 160 owns row tile w and wave v a k range: 960
-// each for bf16 and Q8_0 (30 and 15 loads); Q4_0 loads cover 128 k, so its
-// waves 0-3 take 1024 (k < 4096) and waves 4-7 take 896.
+// each for bf16 and Q8_0 (30 and 15 loads); Q4_0 / Q5_0 loads cover 128 k,
+// so their waves 0-3 take 1024 (k < 4096) and waves 4-7 take 896.
 template <int FMT>
 __device__ __forceinline__ void down_range(int wave, int& kbeg, int& klen) {
-  if constexpr (FMT != W_Q4_0) {
+  if constexpr (!nibble_fmt(FMT)) {
     kbeg = wave * (F / NWAVE);
     klen = F / NWAVE;
   } else if (wave < 4) {
@@ -1568,7 +1591,7 @@ __device__ __forceinline__ void down_range(int wave, int& kbeg, int& klen) {
 }
 
 template <int FMT>
-using DownTile = WTile<FMT, (FMT == W_Q4_0 ? 1024 : F / NWAVE) / KPerLoad<FMT>::v>;
+using DownTile = WTile<FMT, (nibble_fmt(FMT) ? 1024 : F / NWAVE) / KPerLoad<FMT>::v>;
 
 // Down projection tile w for blocks w < 160.  Only waves 0..DOWN_PRE_LAST
 // load their k range at the barrier that ends the gate/up phase (which those
@@ -1952,10 +1975,12 @@ const void* pass_kernel(int fmt, int lm_fmt) {
     if (fmt == W_BF16) return reinterpret_cast<const void*>(k_draft_pass<W_BF16, W_BF16>);
     if (fmt == W_Q8_0) return reinterpret_cast<const void*>(k_draft_pass<W_Q8_0, W_BF16>);
     if (fmt == W_Q4_0) return reinterpret_cast<const void*>(k_draft_pass<W_Q4_0, W_BF16>);
+    if (fmt == W_Q5_0) return reinterpret_cast<const void*>(k_draft_pass<W_Q5_0, W_BF16>);
   } else if (lm_fmt == W_Q8_0) {
     if (fmt == W_BF16) return reinterpret_cast<const void*>(k_draft_pass<W_BF16, W_Q8_0>);
     if (fmt == W_Q8_0) return reinterpret_cast<const void*>(k_draft_pass<W_Q8_0, W_Q8_0>);
     if (fmt == W_Q4_0) return reinterpret_cast<const void*>(k_draft_pass<W_Q4_0, W_Q8_0>);
+    if (fmt == W_Q5_0) return reinterpret_cast<const void*>(k_draft_pass<W_Q5_0, W_Q8_0>);
   }
   return nullptr;
 }
@@ -2022,7 +2047,7 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
   a.logits = q.logits;
   a.hidden = q.hidden;
   // every phase assumes at least one block per work item of its first round
-  if (q.fmt < W_BF16 || q.fmt > W_Q4_0 || (q.lm_fmt != W_BF16 && q.lm_fmt != W_Q8_0))
+  if (q.fmt < W_BF16 || q.fmt > W_Q5_0 || (q.lm_fmt != W_BF16 && q.lm_fmt != W_Q8_0))
     return hipErrorInvalidValue;
   if (q.nch < 1 || q.nch > 128 || q.grid < NKV * q.nch || q.grid < QKV_N / 32 ||
       q.grid < NKV * a.nqt * 16 || q.grid > 1024)
@@ -2066,7 +2091,7 @@ hipError_t draft_pass_max_grid(int device, int* grid) {
   if (e != hipSuccess) return e;
   // one block per CU for every weight format's instantiation
   int ok = 1;
-  for (int f = W_BF16; f <= W_Q4_0; ++f) {
+  for (int f = W_BF16; f <= W_Q5_0; ++f) {
     for (int lf : {static_cast<int>(W_BF16), static_cast<int>(W_Q8_0)}) {
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, pass_kernel(f, lf), NTHR, 0);
       if (e != hipSuccess) return e;

@@ -14,7 +14,8 @@ from ._lib import (dflash_draft_block, dflash_fuse_context, dflash_kv,
                    dflash_workspace_size)
 
 _FORMATS = {"bf16": _lib.DFLASH_W_BF16, "q8_0": _lib.DFLASH_W_Q8_0,
-            "q4_0": _lib.DFLASH_W_Q4_0}
+            "q4_0": _lib.DFLASH_W_Q4_0,
+            "q5_0": _lib.DFLASH_W_Q5_0}
 
 
 def require_gpu():

@@ -21,7 +21,7 @@ def main(argv=None) -> int:
     ap.add_argument("--passes", type=int, default=20)
     ap.add_argument("--block", type=int, default=8)
     ap.add_argument("--ctx", type=int, default=8192)
-    ap.add_argument("--fmt", default="bf16", choices=["bf16", "q8_0", "q4_0"])
+    ap.add_argument("--fmt", default="bf16", choices=["bf16", "q8_0", "q4_0", "q5_0"])
     ap.add_argument("--gated", type=float, default=None, metavar="MIN_P",
                     help="draft with the confidence gate at this floor "
                          "(dflash_draft_block_gated)")

@@ -78,20 +78,26 @@ extern "C" {
 #define DFLASH_TAPS       5
 #define DFLASH_MAX_BLOCK  8   /* anchor + at most 7 candidates ("Current limitations") */
 
-/* Storage format of the 36 backbone matrices (fc and the 35 layer matrices).
- * Q8_0 / Q4_0 use 32-element blocks along the input dimension of each output
- * row, one fp16 scale per block.  A quantized [N][K] matrix is one buffer:
+/* Storage format of the 36 backbone matrices (fc and the 35 layer matrices;
+ * the PR #3322 pages list BF16, Q8_0, Q5_0 and Q4_0 backbones).  The
+ * quantized formats use 32-element blocks along the input dimension of each
+ * output row, one fp16 scale per block.  A quantized [N][K] matrix is one
+ * buffer:
  *   Q8_0: N*K int8 values (row-major), then N*K/32 fp16 scales (row-major);
  *         weight = scale * q.
  *   Q4_0: N*K/2 bytes (row-major, 16 bytes per block: element j of a block in
  *         the low nibble of byte j, element j+16 in the high nibble), then
  *         N*K/32 fp16 scales; weight = scale * (nibble - 8).
+ *   Q5_0: Q4_0's nibbles and scales, then N*K/32 little-endian uint32 words
+ *         (row-major, one per block: bit j is the fifth bit of element j);
+ *         weight = scale * ((nibble | bit << 4) - 16).
  * Gains and the embedding are always bf16; the LM head is bf16 or Q8_0
  * (lm_head_type). */
 typedef enum {
   DFLASH_W_BF16 = 0,
   DFLASH_W_Q8_0 = 1,
-  DFLASH_W_Q4_0 = 2
+  DFLASH_W_Q4_0 = 2,
+  DFLASH_W_Q5_0 = 3
 } dflash_wtype;
 
 typedef struct {
@@ -173,8 +179,8 @@ DFLASH_API size_t dflash_workspace_size(const dflash_weights* w, int32_t max_row
 /* Bytes of the streaming copies: vocab * 2560 LM-head weights at 2 (bf16) or
  * 34/32 (Q8_0) bytes each, plus the 35 layer matrices (5 x (6144*2560 +
  * 2*512*2560 + 2560*6144 + 2*7680*2560 + 2560*7680) weights) and fc
- * (2560*12800 weights) at 2 (bf16), 34/32 (Q8_0) or 18/32 (Q4_0) bytes per
- * weight.  0 for an invalid descriptor. */
+ * (2560*12800 weights) at 2 (bf16), 34/32 (Q8_0), 18/32 (Q4_0) or 22/32
+ * (Q5_0) bytes per weight.  0 for an invalid descriptor. */
 DFLASH_API size_t dflash_packed_size(const dflash_weights* w);
 
 /* Writes the streaming copies into w->packed, enqueued on `stream`.  A bf16
@@ -187,13 +193,17 @@ DFLASH_API size_t dflash_packed_size(const dflash_weights* w);
  * Order in the buffer: lm_head [vocab][2560] (in lm_head_type); then for each layer 0..4:
  * wq [6144][2560], wk [512][2560], wv [512][2560], wo [2560][6144],
  * wg [7680][2560], wu [7680][2560], wd [2560][7680]; then fc [2560][12800].
- * A Q8_0 / Q4_0 matrix
- * keeps its two parts: its quants get the same shuffle with each row seen as
- * 64-byte pieces (64 k for Q8_0, 128 k for Q4_0) in place of 32-element bf16
- * blocks, i.e. byte j of piece kb of row n at ((n/16 * P + kb) * 64 + n%16 +
- * 16 * (j/16)) * 16 + j%16 with P pieces per row; its fp16 scales follow,
- * the S = 2 (Q8_0) or 4 (Q4_0) scales of piece kb of row n at
- * ((n/16 * P + kb) * 16 + n%16) * S + s.
+ * A quantized matrix
+ * keeps its parts: its quants get the same shuffle with each row seen as
+ * 64-byte pieces (64 k for Q8_0, 128 k for Q4_0 / Q5_0) in place of
+ * 32-element bf16 blocks, i.e. byte j of piece kb of row n at
+ * ((n/16 * P + kb) * 64 + n%16 + 16 * (j/16)) * 16 + j%16 with P pieces per
+ * row; its fp16 scales follow, the S = 2 (Q8_0) or 4 (Q4_0, Q5_0) scales of
+ * piece kb of row n at ((n/16 * P + kb) * 16 + n%16) * S + s.  Q5_0's
+ * high-bit words come last, word s of piece kb of row n at
+ * ((n/16 * P + kb) * 16 + n%16) * 4 + s, each with its bits reordered for
+ * the decoder: the fifth bit of element e = 8 a + 4 b + c of the block
+ * (a < 4, b < 2, c < 4) at bit 2 a + b + 8 c.
  * Returns DFLASH_EINVAL if w->packed is NULL. */
 DFLASH_API int32_t dflash_pack_weights(const dflash_weights* w, void* stream);
 

@@ -211,13 +211,16 @@ def test_packed_copy_size_and_checks(lib):
     assert _lib.dflash_packed_size(w) == lm + 2 * weights
     q8 = _lib.dflash_packed_size(fake_weights(backbone_type=_lib.DFLASH_W_Q8_0))
     q4 = _lib.dflash_packed_size(fake_weights(backbone_type=_lib.DFLASH_W_Q4_0))
+    q5 = _lib.dflash_packed_size(fake_weights(backbone_type=_lib.DFLASH_W_Q5_0))
     assert q8 == lm + weights * 34 // 32
     assert q4 == lm + weights * 18 // 32
+    assert q5 == lm + weights * 22 // 32
+    assert _lib.dflash_packed_size(fake_weights(backbone_type=4)) == 0
     assert _lib.dflash_packed_size(fake_weights(hidden=4096)) == 0
     # a Q8_0 LM head: vocab * 2560 weights at 34/32 bytes, ahead of the layers
     assert _lib.dflash_packed_size(fake_weights(lm_head_type=_lib.DFLASH_W_Q8_0)) == \
         synth.VOCAB * 2560 * 34 // 32 + 2 * weights
-    for bad in (_lib.DFLASH_W_Q4_0, 3, -1):  # bf16 or Q8_0 only
+    for bad in (_lib.DFLASH_W_Q4_0, _lib.DFLASH_W_Q5_0, 4, -1):  # bf16 or Q8_0 only
         assert _lib.dflash_packed_size(fake_weights(lm_head_type=bad)) == 0
     assert _lib.dflash_pack_weights(w, None, check=False) == _lib.DFLASH_EINVAL
     big = 1 << 40

@@ -30,6 +30,7 @@ def test_layer_matrix_bytes():
     (32, 4, "bf16", 1_708_922_880),      # smallest configuration
     (8192, 4, "q8_0", 1_356_257_280),    # 34 bytes per 32 weights
     (8192, 4, "q4_0", 1_123_604_480),    # 18 bytes per 32 weights
+    (8192, 4, "q5_0", 1_181_767_680),    # 22 bytes per 32 weights: q4_0 + 465_305_600 / 8
 ])
 def test_pass_bytes(ctx, block, fmt, expected):
     assert bench.pass_bytes(ctx, block, fmt) == expected

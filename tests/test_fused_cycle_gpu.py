@@ -104,7 +104,7 @@ def test_fused_cycle_matches_oracle(dev_w, ow, n_ctx, nc, block, cap, window):
     fused_case(dev_w, ow, n_ctx, nc, block, cap, window, tag=f"{n_ctx}+{nc}")
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0", "q5_0"])
 def test_fused_cycle_quantized(fmt):
     """Quantized fc and Wk / Wv: the commit rows' fusion decodes the fc blocks
     in the FC phase, the projection the Wk / Wv blocks in the QKV phase."""

@@ -126,7 +126,7 @@ def test_decode_loop_ctx8192_block8(dev_w, ow):
 
 # ------------------------------------------------------------------ quantized, ctx 8192
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0", "q5_0"])
 def test_quant_draft_ctx8192_block4(fmt):
     """The quantized-backbone workload: 8192 cells fused and projected from
     Q8_0 / Q4_0 weights (blocks decoded on both sides; the oracle exactly),

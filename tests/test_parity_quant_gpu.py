@@ -1,4 +1,4 @@
-"""GPU parity of the quantized backbone (Q8_0 and Q4_0 storage of fc and the
+"""GPU parity of the quantized backbone (Q8_0, Q4_0 and Q5_0 storage of fc and the
 35 layer matrices; gains, embedding and LM head stay bf16) against the CPU
 oracle, which decodes every block exactly (scale * q in fp64).
 
@@ -20,7 +20,7 @@ from test_parity_gpu import TOL, dec_bf16, end_to_end, ring_cells, row_rel_err, 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(scope="module", params=["q8_0", "q4_0"])
+@pytest.fixture(scope="module", params=["q8_0", "q4_0", "q5_0"])
 def qset(request):
     fmt = request.param
     say(f"quantized weights {fmt}")
@@ -79,7 +79,9 @@ def test_quant_streaming_copy_layout(qset):
     """Packed quants and scales of wq and wd (layers 0 and 4) against the
     host bytes, by the layout the header documents: byte j of 64-byte piece
     kb of row n at ((n/16 * P + kb) * 64 + n%16 + 16 * (j/16)) * 16 + j%16;
-    the S scales of piece kb of row n at ((n/16 * P + kb) * 16 + n%16) * S + s."""
+    the S scales of piece kb of row n at ((n/16 * P + kb) * 16 + n%16) * S + s;
+    Q5_0's high-bit words after them at ((n/16 * P + kb) * 16 + n%16) * 4 + s,
+    the fifth bit of element 8 a + 4 b + c at bit 2 a + b + 8 c."""
     fmt, dev, _ = qset
     host = synth.make_weights(fmt=fmt)
     packed = dev.packed.cpu().numpy()
@@ -87,7 +89,8 @@ def test_quant_streaming_copy_layout(qset):
     shapes = [("wq", 6144, H), ("wk", 512, H), ("wv", 512, H), ("wo", H, 6144),
               ("wg", 7680, H), ("wu", 7680, H), ("wd", H, 7680)]
     qb = (lambda n, k: n * k) if fmt == "q8_0" else (lambda n, k: n * k // 2)
-    mat_bytes = {name: qb(n, k) + n * (k // 32) * 2 for name, n, k in shapes}
+    hb = 4 if fmt == "q5_0" else 0  # high-bit word bytes per block
+    mat_bytes = {name: qb(n, k) + n * (k // 32) * (2 + hb) for name, n, k in shapes}
     layer_bytes = sum(mat_bytes.values())
     rng = np.random.default_rng(11)
     for l in (0, 4):
@@ -105,12 +108,22 @@ def test_quant_streaming_copy_layout(qset):
                 idx = ((rows // 16 * P + kb) * 64 + rows % 16 + 16 * (j // 16)) * 16 + j % 16
                 assert np.array_equal(got[idx], raw[rows * rowb + js])
                 S = 2 if fmt == "q8_0" else 4
-                scales = raw[qb(n, k):].view(np.uint16).reshape(n, k // 32)
-                gs = got[qb(n, k):].view(np.uint16)
+                ns = n * (k // 32)
+                scales = raw[qb(n, k):qb(n, k) + 2 * ns].view(np.uint16).reshape(n, k // 32)
+                gs = got[qb(n, k):qb(n, k) + 2 * ns].view(np.uint16)
                 rows = rng.integers(0, n, 3000)
                 blk = rng.integers(0, k // 32, 3000)
                 kb, sidx = blk // S, blk % S
                 assert np.array_equal(gs[((rows // 16 * P + kb) * 16 + rows % 16) * S + sidx],
                                       scales[rows, blk])
+                if hb:
+                    sq = qb(n, k) + n * (k // 32) * 2
+                    words = raw[sq:].view("<u4").reshape(n, k // 32)
+                    gw = got[sq:].view("<u4")
+                    at = ((rows // 16 * P + kb) * 16 + rows % 16) * S + sidx
+                    for e in range(32):
+                        a, b, c = e >> 3, (e >> 2) & 1, e & 3
+                        assert np.array_equal((gw[at] >> (2 * a + b + 8 * c)) & 1,
+                                              (words[rows, blk] >> e) & 1), e
             off += mb
-    assert packed.size == 2 * V * H + 5 * layer_bytes + qb(H, 5 * H) + H * (5 * H // 32) * 2
+    assert packed.size == 2 * V * H + 5 * layer_bytes + qb(H, 5 * H) + H * (5 * H // 32) * (2 + hb)

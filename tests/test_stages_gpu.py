@@ -8,7 +8,7 @@ ones (draft_block's `stages`) on the same seeded inputs:
             attention (2l+1) and MLP (2l+2) residual -- fp32
   qkv l     raw q | k | v projections before the q/k norms -- fp16
   attn l    attention output before the output projection -- activation
-            format (bf16 beside bf16 weights, fp16 beside Q8_0 / Q4_0)
+            format (bf16 beside bf16 weights, fp16 beside quantized ones)
   mlp l     SiLU(gate) * up -- activation format
 
 Each stage is held to the bar of the final outputs, 2e-2 per-row relative
@@ -108,7 +108,7 @@ def test_stages_bf16_ctx8192_block8(dev_w, ow):
     staged_case(dev_w, ow, 8192, 8, tag="bf16 ctx8192 b8")
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0", "q5_0"])
 def test_stages_quantized(fmt):
     host = synth.make_weights(fmt=fmt)
     dev = DeviceWeights(host)
