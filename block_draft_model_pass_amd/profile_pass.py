@@ -25,6 +25,9 @@ def main(argv=None) -> int:
     ap.add_argument("--gated", type=float, default=None, metavar="MIN_P",
                     help="draft with the confidence gate at this floor "
                          "(dflash_draft_block_gated)")
+    ap.add_argument("--commit", type=int, default=0, metavar="N",
+                    help="fused draft-commit passes: each commits the N positions "
+                         "before ctx and drafts at ctx (dflash_draft_block_commit)")
     ap.add_argument("--copy-mib", type=int, default=0)
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--fuse-rows", type=int, default=0,
@@ -75,21 +78,26 @@ def main(argv=None) -> int:
         print(f"{args.passes} projections of {nr} rows done", flush=True)
         return 0
     dr = Drafter(dw, KVRing(synth.WINDOW, synth.WINDOW), max_rows=2048)
-    for s0 in range(0, args.ctx, 2048):
-        dr.commit(to_device(synth.make_taps(range(s0, min(args.ctx, s0 + 2048)))), s0)
+    nc = args.commit
+    for s0 in range(0, args.ctx - nc, 2048):
+        dr.commit(to_device(synth.make_taps(range(s0, min(args.ctx - nc, s0 + 2048)))), s0)
+    ctaps = to_device(synth.make_taps(range(args.ctx - nc, args.ctx))) if nc else None
     torch.cuda.synchronize()
-    print(f"context 0..{args.ctx - 1} committed ({args.fmt})", flush=True)
+    print(f"context 0..{args.ctx - nc - 1} committed ({args.fmt})", flush=True)
     cand = torch.empty(8, dtype=torch.int32, device="cuda")
     conf = torch.empty(8, dtype=torch.float32, device="cuda")
     keep = torch.empty(1, dtype=torch.int32, device="cuda")
     for i in range(args.passes):
-        if args.gated is None:
+        if nc:  # the same nc cells rewritten every pass
+            dr.draft_commit(ctaps.data_ptr(), nc, args.ctx, 11, args.block, cand=cand)
+        elif args.gated is None:
             dr.draft(args.ctx, 11, args.block, cand=cand)
         else:
             dr.draft_gated(args.ctx, 11, args.block, args.gated, cand=cand[:args.block - 1],
                            conf=conf[:args.block - 1], n_keep=keep)
     torch.cuda.synchronize()
     gate = "" if args.gated is None else f", gated at min_p {args.gated}"
+    gate += f", committing {nc} cells each" if nc else ""
     print(f"{args.passes} draft passes done, block {args.block}{gate}", flush=True)
     return 0
 
