@@ -5,10 +5,14 @@ Workload (one step = one decode cycle): 8192 resident context cells, a block
 of anchor + 7 masks (block 8) drafted at the next position, greedy
 verification against a seeded stand-in target that agrees with each
 candidate with probability 0.75, and the commit (fusion + K/V projection) of
-the accepted cells plus the anchor -- done by the next cycle's pass
-(dflash_draft_block_commit: one launch commits and drafts).  Jobs of 96
-committed tokens restart at position 8192 (position-addressed cells make
-rejected drafts harmless).
+the accepted cells plus the anchor -- done by the next cycle's pass (one
+launch commits and drafts).  The timed cycles keep their positions in device
+words that the verify advances (dflash_draft_block_commit_dev,
+dflash_verify_greedy_advance), so no cycle reads from the device; jobs of 26
+cycles (about 96 committed tokens) restart at position 8192
+(position-addressed cells make rejected drafts harmless).  The same cycle
+with host-side positions (one device-to-host read per cycle) and with the
+commit as separate calls are reported beside it.
 
 Prints one JSON line.  Inputs are resident in HBM before timing starts.
 """
@@ -29,6 +33,7 @@ if ROOT not in sys.path:
 CTX = 8192
 BLOCK = 8
 JOB_TOKENS = 96
+JOB_CYCLES = 26   # cycles per job of the device-resident loop (about 96 tokens at p = 0.75)
 HBM_PEAK_GBS = 8000.0
 METRIC = "DFlash draft passes/sec (ctx 8192, block 8) + achieved HBM GB/s vs peak"
 
@@ -92,7 +97,6 @@ def lm_head_bytes() -> int:
 
 def cpu_baseline(host_w, budget_s: float):
     """The oracle's decode cycle at ctx 8192 / block 8 on the host cores."""
-    from threadpoolctl import threadpool_info
 
     from block_draft_model_pass_amd import synth
     from oracle import dflash_oracle as O
@@ -116,10 +120,96 @@ def cpu_baseline(host_w, budget_s: float):
         p, anchor = p + a + 1, nxt
         n += 1
     dt = time.perf_counter() - t0
-    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    return {"value": n / dt, "unit": "passes/s", "cores": int(threads), "kind": "oracle",
+    info = host_cpu()
+    return {"value": n / dt, "unit": "passes/s", "cores": info["blas_threads"], "kind": "oracle",
             "sample": f"{n} decode cycles (draft + verify + commit) of the fp64 numpy oracle "
-                      f"at ctx {CTX}, block {BLOCK}, {dt:.1f} s; weights pre-decoded"}
+                      f"at ctx {CTX}, block {BLOCK}, {dt:.1f} s; weights pre-decoded; "
+                      f"{info['model']}, {info['cores']} cores available"}
+
+
+def host_cpu() -> dict:
+    """CPU model, the cores this process may run on and the BLAS threads."""
+    from threadpoolctl import threadpool_info
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    return {"model": model, "cores": len(os.sched_getaffinity(0)), "blas_threads": int(threads)}
+
+
+def cpu_plan():
+    """The CPU-baseline table: one oracle draft pass (median of 3) for the
+    smallest configuration (ctx 32, block 4), the short prompt (ctx 2432,
+    block 8), the decode-loop shape (ctx 8192, block 8) and the quantized
+    backbones (ctx 8192, block 4), the first two also on one thread, plus
+    the short prompt's fusion and projection in full.  The oracle is the
+    fp64 numpy one, as it stands; every matrix is decoded once before the
+    timed calls.  Prints a markdown table and one JSON line."""
+    import json as _json
+    from threadpoolctl import threadpool_limits
+
+    from block_draft_model_pass_amd import synth
+    from oracle import dflash_oracle as O
+    info = host_cpu()
+    print(f"CPU: {info['model']}; {info['cores']} cores available, "
+          f"BLAS threads {info['blas_threads']}", flush=True)
+    rows = []
+
+    def med(fn, n=3):
+        ts = []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    def context(w, n):
+        store = O.ContextStore()
+        for s0 in range(0, n, 2048):
+            taps = synth.make_taps(range(s0, min(n, s0 + 2048)))
+            store.put(*O.project_ctx_kv(w, O.fuse_context(w, taps), s0), s0)
+        return store
+
+    def add(name, sec, nbytes=None, threads="all"):
+        rec = {"config": name, "threads": threads, "seconds": round(sec, 3),
+               "per_s": round(1.0 / sec, 3)}
+        if nbytes:
+            rec["GBs"] = round(nbytes / sec / 1e9, 2)
+        rows.append(rec)
+        print(_json.dumps(rec), flush=True)
+
+    for fmt in ("bf16", "q8_0", "q4_0", "q5_0"):
+        w = O.enable_cache(dict(synth.make_weights(fmt=fmt)))
+        shapes = ((32, 4), (2432, 8), (8192, 8)) if fmt == "bf16" else ((8192, 4),)
+        for n, b in shapes:
+            store = context(w, n)
+            ck, cv = store.window(n)
+            anchor = synth.anchor_token(n)
+            run = lambda: O.draft_block(w, ck, cv, n, anchor, synth.MASK_ID, b)  # noqa: E731
+            run()  # decodes and caches every matrix
+            add(f"draft ctx {n} block {b} {fmt}", med(run), pass_bytes(n, b, fmt))
+            if fmt == "bf16" and n < 8192:
+                with threadpool_limits(limits=1):
+                    add(f"draft ctx {n} block {b} {fmt}", med(run), pass_bytes(n, b, fmt),
+                        threads=1)
+            if fmt == "bf16" and n == 2432:
+                taps = synth.make_taps(range(n))
+                ctx = O.fuse_context(w, taps)
+                add("fusion 2432 x 12800 @ 12800 x 2560", med(lambda: O.fuse_context(w, taps), 1))
+                add("K/V projection 2432 rows", med(lambda: O.project_ctx_kv(w, ctx, 0), 1))
+        del w
+    print("| measurement | threads | s | per s | GB/s |")
+    print("|---|---|---:|---:|---:|")
+    for r in rows:
+        print(f"| {r['config']} | {r['threads']} | {r['seconds']} | {r['per_s']} | "
+              f"{r.get('GBs', '')} |")
+    print(_json.dumps({"cpu": info, "kind": "oracle (fp64 numpy)", "rows": rows}))
 
 
 def main():
@@ -132,9 +222,15 @@ def main():
     ap.add_argument("--reps", type=int, default=50, help="repeats of the event-timed kernels")
     ap.add_argument("--fusion-rows", type=int, default=32768,
                     help="rows of the timed context-fusion GEMM (0 = skip)")
+    ap.add_argument("--cpu-plan", action="store_true",
+                    help="only time the CPU oracle over the baseline plan's configurations "
+                         "(no GPU) and print the table")
     ap.add_argument("--no-quant", action="store_true",
                     help="skip the Q8_0 / Q4_0 / Q5_0 backbone passes (ctx 8192, block 4)")
     args = ap.parse_args()
+    if args.cpu_plan:
+        cpu_plan()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the pass would shard as described in DESIGN.md but no multi-GPU path exists.",
@@ -155,7 +251,7 @@ def main():
     K = BLOCK - 1
 
     # Context 0..8191 and the taps of every position a job can commit.
-    span = CTX + JOB_TOKENS + BLOCK
+    span = CTX + max(JOB_TOKENS, JOB_CYCLES * BLOCK) + BLOCK
     taps_all = to_device(synth.make_taps(range(span)))
     taps_ptr, tap_row_bytes = taps_all.data_ptr(), taps_all.stride(0) * taps_all.element_size()
     dr.commit(taps_all[:CTX], 0)
@@ -213,8 +309,46 @@ def main():
         torch.cuda.synchronize()
         return time.perf_counter() - t0, st["acc"], st["off"]
 
+    def run_device_cycles():
+        """The fused cycle with its positions in device words: the pass reads
+        {p, anchor, n_commit} and the verify advances them
+        (dflash_draft_block_commit_dev, dflash_verify_greedy_advance), so no
+        cycle reads from the device; a job restarts at position 8192 every
+        JOB_CYCLES cycles by a device-to-device copy of its initial state.
+        Returns (seconds, accepted, offered) over the timed cycles."""
+        taps_ctx = taps_all[CTX:]
+        jobs = (n_pass + JOB_CYCLES - 1) // JOB_CYCLES
+        init = torch.tensor([[CTX, synth.anchor_token(j), 0] for j in range(jobs)],
+                            dtype=torch.int64, device="cuda")
+        dstate = torch.empty(3, dtype=torch.int64, device="cuda")
+        outs = torch.empty((n_pass, 2), dtype=torch.int32, device="cuda")
+        tgts = torch.zeros((n_pass, K + 1), dtype=torch.int32, device="cuda")
+        tgts[:, K] = tgt_all[:, K]
+
+        def cycle(t):
+            if t % JOB_CYCLES == 0:
+                dstate.copy_(init[t // JOB_CYCLES])
+            dr.draft_commit_dev(taps_ctx, CTX, dstate, BLOCK, cand=cand)
+            torch.where(match[t], cand, torch.remainder(cand + offset[t], V), out=tgts[t, :K])
+            dr.verify_advance(cand, tgts[t], K, dstate, out=outs[t])
+
+        for t in range(args.warmup):
+            cycle(t)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(args.warmup, n_pass):
+            cycle(t)
+        torch.cuda.synchronize()
+        dt_ = time.perf_counter() - t0
+        a_ = outs[args.warmup:, 0].sum().item()
+        st = torch.empty(1, dtype=torch.int32, device="cuda")
+        dr.status(st)
+        assert int(st.item()) == 0, "device-resident cycle: a pass reported a failure"
+        return dt_, int(a_), K * args.steps
+
     dt_unfused, _, _ = run_cycles(False)
-    dt, acc, off = run_cycles(True)
+    dt_host, _, _ = run_cycles(True)
+    dt, acc, off = run_device_cycles()
     value = args.steps / dt
     state = {"acc": acc, "off": off}
 
@@ -428,8 +562,16 @@ def main():
         "config": {"workload": "DFlash decode cycle: 8192 resident context cells, block 8 "
                                "(anchor + 7 masks), greedy verify vs Bernoulli(0.75) stand-in "
                                "target; the accepted cells are committed by the next cycle's "
-                               "pass (dflash_draft_block_commit); 96-token jobs",
+                               "pass; positions in device words advanced by the verify "
+                               "(dflash_draft_block_commit_dev, dflash_verify_greedy_advance), "
+                               f"jobs of {JOB_CYCLES} cycles from position 8192",
                    "ctx": CTX, "block": BLOCK, "vocab": V, "backbone": "bf16"},
+        "decode_cycle_host_positions": {
+            "ms_per_cycle": round(1e3 * dt_host / args.steps, 4),
+            "cycles_per_s": round(args.steps / dt_host, 3),
+            "note": "the same fused cycle with the positions as host arguments "
+                    "(dflash_draft_block_commit): one device-to-host read of (accepted, "
+                    "next) per cycle; 96-token jobs"},
         "decode_cycle_unfused": {"ms_per_cycle": round(1e3 * dt_unfused / args.steps, 4),
                                  "cycles_per_s": round(args.steps / dt_unfused, 3),
                                  "note": "draft, verify, then the commit as separate fuse + "

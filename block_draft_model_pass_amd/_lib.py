@@ -100,6 +100,14 @@ def load() -> ctypes.CDLL:
                                               c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                               c_void_p]
     lib.dflash_draft_block_commit.restype = c_int32
+    lib.dflash_draft_block_commit_dev.argtypes = [P(dflash_weights), P(dflash_kv), c_void_p,
+                                                  c_int64, c_int64, c_void_p, c_int32, c_int32,
+                                                  c_void_p, c_void_p, c_void_p, c_void_p,
+                                                  c_size_t, c_void_p]
+    lib.dflash_draft_block_commit_dev.restype = c_int32
+    lib.dflash_verify_greedy_advance.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                                 c_void_p]
+    lib.dflash_verify_greedy_advance.restype = c_int32
     lib.dflash_draft_block_static.argtypes = [P(dflash_weights), P(dflash_kv), c_int64,
                                               c_int32, c_int32, c_int32, c_void_p, c_void_p,
                                               c_void_p, c_void_p]
@@ -218,6 +226,20 @@ def dflash_draft_block_static(w, kv, p, anchor_id, mask_id, block, cand, logits_
     rc = load().dflash_draft_block_static(_ref(w), _ref(kv), p, anchor_id, mask_id, block, cand,
                                           logits_opt, hidden_opt, stream)
     return _check(rc, "dflash_draft_block_static") if check else rc
+
+
+def dflash_draft_block_commit_dev(w, kv, taps, taps_pos0, taps_rows, state, mask_id, block,
+                                  cand, logits_opt, hidden_opt, ws, ws_bytes, stream=None,
+                                  check=True):
+    rc = load().dflash_draft_block_commit_dev(_ref(w), _ref(kv), taps, taps_pos0, taps_rows,
+                                              state, mask_id, block, cand, logits_opt,
+                                              hidden_opt, ws, ws_bytes, stream)
+    return _check(rc, "dflash_draft_block_commit_dev") if check else rc
+
+
+def dflash_verify_greedy_advance(cand, target, k, state, out, stream=None, check=True):
+    rc = load().dflash_verify_greedy_advance(cand, target, k, state, out, stream)
+    return _check(rc, "dflash_verify_greedy_advance") if check else rc
 
 
 def dflash_draft_block_commit(w, kv, taps, n_commit, p, anchor_id, mask_id, block, cand,

@@ -472,15 +472,32 @@ namespace {
 // ignored), resolved after the arguments are checked.
 // taps / nc: commit rows of the fused draft-commit cycle (nc = 0: none),
 // at positions p - nc .. p - 1.
+// Positions of a pass held in device memory: {p, anchor, n_commit} (int64),
+// with the commit taps as rows of a position-indexed buffer.
+struct DevPos {
+  const int64_t* state;
+  const void* taps;
+  int64_t taps_pos0, taps_rows;
+};
+
 int32_t draft_block_impl(const dflash_weights* w, const dflash_kv* kv, int64_t p,
                          int32_t anchor_id, int32_t mask_id, int32_t block, int32_t* cand,
                          float* conf, int32_t* nkeep, float min_p, void* logits_opt,
                          void* hidden_opt, void* ws, size_t ws_bytes, void* stream,
-                         bool static_ws = false, const void* taps = nullptr, int32_t nc = 0) {
+                         bool static_ws = false, const void* taps = nullptr, int32_t nc = 0,
+                         const DevPos* dev = nullptr) {
   int rc = check_weights(w);
   if (rc) return rc;
   rc = check_kv(kv);
   if (rc) return rc;
+  if (dev) {  // p, the anchor and n_commit are checked by the kernels when they read them
+    if (!dev->state || (reinterpret_cast<uintptr_t>(dev->state) & 7u) || !dev->taps ||
+        !a16(dev->taps) || dev->taps_pos0 < 0 || dev->taps_rows < 0)
+      return DFLASH_EINVAL;
+    p = 0;
+    anchor_id = 0;
+    nc = 0;
+  }
   if (block < 1 || block > MAXB || p < 0) return DFLASH_EINVAL;
   if (nc < 0 || nc > MAXB || p < nc || (nc > 0 && (!taps || !a16(taps)))) return DFLASH_EINVAL;
   if (anchor_id < 0 || anchor_id >= w->vocab || mask_id < 0 || mask_id >= w->vocab)
@@ -582,6 +599,14 @@ int32_t draft_block_impl(const dflash_weights* w, const dflash_kv* kv, int64_t p
   q.hidden_norm = u16p(w->hidden_norm);
   q.yc = at<float>(ws, Lw.yc);
   q.ckv = at<float>(ws, Lw.ckv);
+  if (dev) {
+    q.dstate = dev->state;
+    q.taps_base = static_cast<const uint16_t*>(dev->taps);
+    q.taps_pos0 = dev->taps_pos0;
+    q.taps_rows = dev->taps_rows;
+    q.window = kv->window;
+    q.maxch = grid / 2 < 128 ? grid / 2 : 128;
+  }
   HIP_TRY(launch_draft_pass(q, st));
   return DFLASH_OK;
 }
@@ -602,6 +627,17 @@ extern "C" int32_t dflash_draft_block_commit(const dflash_weights* w, const dfla
                                              void* ws, size_t ws_bytes, void* stream) {
   return draft_block_impl(w, kv, p, anchor_id, mask_id, block, cand, nullptr, nullptr, 0.f,
                           logits_opt, hidden_opt, ws, ws_bytes, stream, false, taps, n_commit);
+}
+
+extern "C" int32_t dflash_draft_block_commit_dev(const dflash_weights* w, const dflash_kv* kv,
+                                                 const void* taps, int64_t taps_pos0,
+                                                 int64_t taps_rows, const int64_t* state,
+                                                 int32_t mask_id, int32_t block, int32_t* cand,
+                                                 void* logits_opt, void* hidden_opt, void* ws,
+                                                 size_t ws_bytes, void* stream) {
+  const DevPos dev{state, taps, taps_pos0, taps_rows};
+  return draft_block_impl(w, kv, 0, 0, mask_id, block, cand, nullptr, nullptr, 0.f, logits_opt,
+                          hidden_opt, ws, ws_bytes, stream, false, nullptr, 0, &dev);
 }
 
 extern "C" int32_t dflash_draft_block_static(const dflash_weights* w, const dflash_kv* kv,
@@ -648,7 +684,7 @@ extern "C" int32_t dflash_verify_greedy(const int32_t* cand, const int32_t* targ
                                         int32_t* out, void* stream) {
   if (k < 0 || k > MAXB - 1) return DFLASH_EINVAL;
   if (!target || !out || (k > 0 && !cand)) return DFLASH_EINVAL;
-  if (launch_verify(cand, target, k, nullptr, out, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (launch_verify(cand, target, k, nullptr, out, nullptr, static_cast<hipStream_t>(stream)) != hipSuccess)
     return DFLASH_EHIP;
   return DFLASH_OK;
 }
@@ -661,7 +697,21 @@ extern "C" int32_t dflash_verify_greedy_gated(const int32_t* cand, const int32_t
   if ((reinterpret_cast<uintptr_t>(n_keep) & 3u) || (reinterpret_cast<uintptr_t>(out) & 3u) ||
       (reinterpret_cast<uintptr_t>(target) & 3u) || (reinterpret_cast<uintptr_t>(cand) & 3u))
     return DFLASH_EINVAL;
-  if (launch_verify(cand, target, k_max, n_keep, out, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (launch_verify(cand, target, k_max, n_keep, out, nullptr, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DFLASH_EHIP;
+  return DFLASH_OK;
+}
+
+extern "C" int32_t dflash_verify_greedy_advance(const int32_t* cand, const int32_t* target,
+                                                int32_t k, int64_t* state, int32_t* out,
+                                                void* stream) {
+  if (k < 0 || k > MAXB - 1) return DFLASH_EINVAL;
+  if (!target || !out || !state || (k > 0 && !cand)) return DFLASH_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(state) & 7u) || (reinterpret_cast<uintptr_t>(out) & 3u) ||
+      (reinterpret_cast<uintptr_t>(target) & 3u) || (reinterpret_cast<uintptr_t>(cand) & 3u))
+    return DFLASH_EINVAL;
+  if (launch_verify(cand, target, k, nullptr, out, state, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
     return DFLASH_EHIP;
   return DFLASH_OK;
 }
@@ -672,7 +722,7 @@ extern "C" int32_t dflash_draft_status(const void* ws, size_t ws_bytes, int32_t*
   const Layout Lw = layout();
   if (ws_bytes < Lw.fixed) return DFLASH_EWORKSPACE;
   HIP_TRY(launch_pass_status(at<const unsigned>(const_cast<void*>(ws), Lw.bar), status,
-                             DFLASH_ETIMEOUT, static_cast<hipStream_t>(stream)));
+                             DFLASH_ETIMEOUT, DFLASH_EINVAL, static_cast<hipStream_t>(stream)));
   return DFLASH_OK;
 }
 

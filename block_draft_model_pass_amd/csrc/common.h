@@ -337,6 +337,15 @@ struct PassLaunch {
   float* conf = nullptr;     // [B-1] candidate probabilities, or null
   int32_t* nkeep = nullptr;  // confidence-gated candidate count, or null
   float min_p = 0.f;
+  // Positions from device memory: with dstate set, p, the anchor and nc are
+  // read from dstate[0..2] by the kernels and the fields above that derive
+  // from them (lo, hi, p0, nb, cb, nch, pos0, taps) are ignored; the commit
+  // taps are rows of taps_base, row r holding position taps_pos0 + r.
+  const int64_t* dstate = nullptr;
+  const uint16_t* taps_base = nullptr;
+  int64_t taps_pos0 = 0, taps_rows = 0;
+  int64_t window = 0;
+  int maxch = 0;             // most chunks per KV head
 };
 
 hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st);
@@ -348,12 +357,16 @@ size_t pass_smem_bytes();
 size_t pass_tab_bytes();
 size_t pass_bar_bytes();
 
-// Greedy verify of k candidates, or of min(max(*k_dev, 0), k) when k_dev is set.
+// Greedy verify of k candidates, or of min(max(*k_dev, 0), k) when k_dev is
+// set; with `state` ({p, anchor, n_commit}, int64) it also advances the
+// device-resident positions.
 hipError_t launch_verify(const int32_t* cand, const int32_t* target, int k, const int32_t* k_dev,
-                         int32_t* out, hipStream_t st);
-// *status = code if the barrier words `bar` of the last pass record a wait
-// that gave up, else 0.
-hipError_t launch_pass_status(const unsigned* bar, int32_t* status, int32_t code, hipStream_t st);
+                         int32_t* out, int64_t* state, hipStream_t st);
+// *status = timeout_code if the barrier words `bar` of the last pass record
+// a wait that gave up, invalid_code if the pass found its device-resident
+// positions invalid and did nothing, else 0.
+hipError_t launch_pass_status(const unsigned* bar, int32_t* status, int32_t timeout_code,
+                              int32_t invalid_code, hipStream_t st);
 // Constant-clock ticks per microsecond on `device` (the counter the pass's
 // barrier bound reads).
 hipError_t wall_clock_ticks_per_us(int device, double* ticks);

@@ -496,8 +496,11 @@ __global__ __launch_bounds__(MAXB * 64) void k_argmax_reduce(const uint64_t* key
 }
 
 // accepted = longest prefix with cand == target; all loads issued at once.
+// With `state` (the device-resident positions {p, anchor, n_commit}), the
+// cycle advances: the accepted cells and the continuation token's position
+// are committed by the next pass, p += a + 1, anchor = next, n_commit = a + 1.
 __global__ void k_verify(const int32_t* cand, const int32_t* target, int kmax,
-                         const int32_t* k_dev, int32_t* out) {
+                         const int32_t* k_dev, int32_t* out, int64_t* state) {
   const int lane = threadIdx.x;
   // k from a device word (the confidence gate's count), clamped to [0, kmax]
   const int kd = k_dev ? *k_dev : kmax;
@@ -511,6 +514,11 @@ __global__ void k_verify(const int32_t* cand, const int32_t* target, int kmax,
   if (lane == 0) {
     out[0] = a;
     out[1] = nxt;
+    if (state) {
+      state[0] += a + 1;
+      state[1] = nxt;
+      state[2] = a + 1;
+    }
   }
 }
 
@@ -605,8 +613,8 @@ hipError_t launch_lmhead_argmax(const void* lm, int fmt, bool packed, int vocab,
 }
 
 hipError_t launch_verify(const int32_t* cand, const int32_t* target, int k, const int32_t* k_dev,
-                         int32_t* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_verify, dim3(1), dim3(64), 0, st, cand, target, k, k_dev, out);
+                         int32_t* out, int64_t* state, hipStream_t st) {
+  hipLaunchKernelGGL(k_verify, dim3(1), dim3(64), 0, st, cand, target, k, k_dev, out, state);
   return hipGetLastError();
 }
 

@@ -186,6 +186,16 @@ struct PassArgs {
   float* conf;       // [B-1] or null: softmax probability of each candidate
   int32_t* nkeep;    // or null: leading candidates whose conf >= min_p
   float min_p;
+  // Device-resident positions (the decode cycle with no host round trip):
+  // when dstate is set, p, the anchor and nc come from dstate[0..2] and lo,
+  // hi, p0, nb, cb, nch, nc, pos0 and taps are derived from them at the start
+  // of the pass (resolve_positions), exactly as the host derives them
+  // otherwise; the commit taps are rows of taps_base (row r = position
+  // taps_pos0 + r).
+  const int64_t* dstate;
+  const uint16_t* taps_base;
+  int64_t taps_pos0, taps_rows, window;
+  int maxch;
 };
 
 struct Smem {
@@ -268,6 +278,9 @@ __device__ __forceinline__ void st_coh_f4(float* p, f32x4 v) {
 // round trip is slow while the weight stream saturates HBM.
 // Per-XCD release words at [640 + 32 x] (see grid_sync_pf).
 constexpr int BAR_STATUS = 0, BAR_TOP = 64, BAR_XCD = 128, BAR_REL = 640, BAR_WORDS = 1024;
+// BAR_STATUS values: a barrier wait gave up, or the device-resident positions
+// were invalid (the pass then did nothing but report it)
+constexpr unsigned ST_TIMEOUT = 1u, ST_INVALID = 2u;
 
 __device__ __forceinline__ unsigned ald(unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -336,7 +349,7 @@ __device__ __forceinline__ void grid_sync_pf(const PassArgs& a, BarState& b, Pf&
       if (n == 16) {
         t0 = now;
       } else if (now - t0 > a.wait_ticks) {  // bounded: never hang
-        __hip_atomic_store(a.bar + BAR_STATUS, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.bar + BAR_STATUS, ST_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         b.quit = true;
         break;
       }
@@ -1817,6 +1830,55 @@ __device__ __forceinline__ void lm_phase(const PassArgs& a, Smem& s, int np, LmT
   wait_stores();
 }
 
+// ---------------------------------------------------------------- device-resident positions
+
+// The pass's positions from dstate = {p, anchor, nc} and the derived split
+// of the visible context, computed the way the host computes them for the
+// host-argument entry points: the ring is read at [lo, hi) with lo = max(0,
+// p - window), hi = p - nc; 32-cell blocks from p0 = lo rounded down to 32;
+// at most maxch chunks per KV head.  ok = false when the state is outside
+// what the host entry points accept (then nothing may be read from it).
+struct PosState {
+  int64_t p, lo, hi, p0, pos0;
+  int nb, cb, nch, nc, anchor;
+  bool ok;
+};
+
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+  const uint64_t u = static_cast<uint64_t>(v);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ PosState resolve_positions(const int64_t* st, int64_t window, int maxch,
+                                                      int vocab, int64_t taps_pos0,
+                                                      int64_t taps_rows) {
+  PosState r;
+  r.p = uni64(static_cast<int64_t>(ld_coh64(st)));
+  const int64_t anchor = uni64(static_cast<int64_t>(ld_coh64(st + 1)));
+  const int64_t nc = uni64(static_cast<int64_t>(ld_coh64(st + 2)));
+  r.ok = r.p >= 0 && nc >= 0 && nc <= MAXB && r.p >= nc && anchor >= 0 && anchor < vocab &&
+         (nc == 0 || (r.p - nc >= taps_pos0 && r.p <= taps_pos0 + taps_rows));
+  r.nc = r.ok ? static_cast<int>(nc) : 0;
+  r.anchor = r.ok ? static_cast<int>(anchor) : 0;
+  r.lo = r.p - window > 0 ? r.p - window : 0;
+  r.hi = r.p - r.nc;
+  r.pos0 = r.hi;
+  if (r.ok && r.hi > r.lo) {
+    r.p0 = r.lo & ~static_cast<int64_t>(31);
+    r.nb = static_cast<int>((r.hi - r.p0 + 31) / 32);
+    r.cb = (r.nb + maxch - 1) / maxch;
+    r.nch = (r.nb + r.cb - 1) / r.cb;
+  } else {
+    r.p0 = 0;
+    r.nb = 0;
+    r.cb = 1;
+    r.nch = 1;
+  }
+  return r;
+}
+
 __device__ __forceinline__ void argmax_final(const PassArgs& a, Smem& s) {
   if (blockIdx.x != 0) return;
   const int wave = wid(), lane = otid() & 63;
@@ -1861,8 +1923,33 @@ __device__ __forceinline__ void argmax_final(const PassArgs& a, Smem& s) {
 }
 
 template <int FMT, int LMF>
-__global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
+__global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs args) {
   __shared__ Smem s;
+  PassArgs a = args;
+  if (a.dstate) {  // positions from device memory (uniform: every block reads the same words)
+    const PosState ps = resolve_positions(a.dstate, a.window, a.maxch, a.vocab, a.taps_pos0,
+                                          a.taps_rows);
+    if (!ps.ok) {  // nothing is read from an invalid state; report it
+      if (blockIdx.x == 0 && otid() == 0) {
+        __hip_atomic_store(a.bar + BAR_STATUS, ST_INVALID, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        for (int b = 0; b + 1 < a.B; ++b) a.cand[b] = -1;
+        if (a.conf)
+          for (int b = 0; b + 1 < a.B; ++b) a.conf[b] = __uint_as_float(0x7fc00000u);
+        if (a.nkeep) *a.nkeep = 0;
+      }
+      return;
+    }
+    a.lo = ps.lo;
+    a.hi = ps.hi;
+    a.p0 = ps.p0;
+    a.nb = ps.nb;
+    a.cb = ps.cb;
+    a.nch = ps.nch;
+    a.nc = ps.nc;
+    a.pos0 = ps.pos0;
+    a.taps = ps.nc ? a.taps_base + static_cast<size_t>(ps.pos0 - a.taps_pos0) * T * H : nullptr;
+  }
   BarState bk;      // barriers passed, give-up flag
   QkvTile<FMT> Wq;
   LmTile<LMF> Wl;   // LM head slice, prefetched after the last layer
@@ -1910,16 +1997,34 @@ __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs a) {
 // h[b] = E[token_b], per-row sum of squares, RoPE table of p .. p+B-1 (rows
 // 0..B-1) and of the commit positions pos0 .. pos0+nc-1 (rows 8..8+nc-1), and
 // the barrier words of the pass kernel.  grid max(B, nc), block 256.
+// Positions read by the init kernel when they live in device memory (the
+// same state and bounds the pass reads).
+struct InitPos {
+  const int64_t* dstate;
+  int64_t window, taps_pos0, taps_rows;
+  int maxch, vocab;
+};
+
 __global__ __launch_bounds__(256) void k_pass_init(LayerTab tab, LayerTab* tab_out,
                                                    const uint16_t* embed, int anchor, int mask,
                                                    int B, int64_t p, int nc, int64_t pos0,
                                                    double theta, float* h, uint16_t* h16,
-                                                   float* ss, float2* rope, unsigned* bar) {
+                                                   float* ss, float2* rope, unsigned* bar,
+                                                   InitPos dp) {
   __shared__ float red[4];
   const int b = blockIdx.x;
   if (b == 0)
     for (int i = threadIdx.x; i < BAR_WORDS; i += 256) bar[i] = 0u;
   if (b == 0 && threadIdx.x == 0) *tab_out = tab;
+  if (dp.dstate) {
+    const PosState ps = resolve_positions(dp.dstate, dp.window, dp.maxch, dp.vocab, dp.taps_pos0,
+                                          dp.taps_rows);
+    if (!ps.ok) return;  // the pass reports it
+    anchor = ps.anchor;
+    p = ps.p;
+    nc = ps.nc;
+    pos0 = ps.pos0;
+  }
   if (b < nc && threadIdx.x < D / 2) {
     const double inv = pow(theta, -2.0 * static_cast<double>(threadIdx.x) / static_cast<double>(D));
     double sn, cs;
@@ -1956,8 +2061,12 @@ __global__ __launch_bounds__(256) void k_pass_init(LayerTab tab, LayerTab* tab_o
   if (threadIdx.x == 0) ss[b] = sq;
 }
 
-__global__ void k_pass_status(const unsigned* bar, int32_t* status, int32_t code) {
-  if (threadIdx.x == 0) *status = ld_coh32(bar + BAR_STATUS) != 0u ? code : 0;
+__global__ void k_pass_status(const unsigned* bar, int32_t* status, int32_t timeout_code,
+                              int32_t invalid_code) {
+  if (threadIdx.x == 0) {
+    const uint32_t v = ld_coh32(bar + BAR_STATUS);
+    *status = v == 0u ? 0 : (v == ST_INVALID ? invalid_code : timeout_code);
+  }
 }
 
 }  // namespace
@@ -2046,6 +2155,12 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
   a.cand = q.cand;
   a.logits = q.logits;
   a.hidden = q.hidden;
+  a.dstate = q.dstate;
+  a.taps_base = q.taps_base;
+  a.taps_pos0 = q.taps_pos0;
+  a.taps_rows = q.taps_rows;
+  a.window = q.window;
+  a.maxch = q.maxch;
   // every phase assumes at least one block per work item of its first round
   if (q.fmt < W_BF16 || q.fmt > W_Q5_0 || (q.lm_fmt != W_BF16 && q.lm_fmt != W_Q8_0))
     return hipErrorInvalidValue;
@@ -2054,9 +2169,16 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
     return hipErrorInvalidValue;
   if (q.nc < 0 || q.nc > MAXB || (q.nc > 0 && (!q.taps || !q.fc || !q.yc || !q.ckv || q.grid < NT_H)))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_pass_init, dim3(q.B > q.nc ? q.B : q.nc), dim3(256), 0, st, tab,
+  // device-resident positions: up to MAXB commit rows, at most maxch chunks per head
+  if (q.dstate && (!q.taps_base || !q.fc || !q.yc || !q.ckv || q.grid < NT_H || q.maxch < 1 ||
+                   q.maxch > 128 || q.grid < NKV * q.maxch || q.window < 1 || q.taps_pos0 < 0 ||
+                   q.taps_rows < 0))
+    return hipErrorInvalidValue;
+  InitPos dp{q.dstate, q.window, q.taps_pos0, q.taps_rows, q.maxch, q.vocab};
+  const int init_grid = q.dstate ? MAXB : (q.B > q.nc ? q.B : q.nc);
+  hipLaunchKernelGGL(k_pass_init, dim3(init_grid), dim3(256), 0, st, tab,
                      reinterpret_cast<LayerTab*>(q.tab), q.embed, q.anchor, q.mask, q.B, q.p, q.nc,
-                     q.pos0, q.theta, q.h, q.h16, q.ss, q.rope, q.bar);
+                     q.pos0, q.theta, q.h, q.h16, q.ss, q.rope, q.bar, dp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const void* kern = pass_kernel(q.fmt, q.lm_fmt);
@@ -2071,8 +2193,10 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
   return hipLaunchKernel(kern, dim3(q.grid), dim3(NTHR), args, 0, st);
 }
 
-hipError_t launch_pass_status(const unsigned* bar, int32_t* status, int32_t code, hipStream_t st) {
-  hipLaunchKernelGGL(k_pass_status, dim3(1), dim3(64), 0, st, bar, status, code);
+hipError_t launch_pass_status(const unsigned* bar, int32_t* status, int32_t timeout_code,
+                              int32_t invalid_code, hipStream_t st) {
+  hipLaunchKernelGGL(k_pass_status, dim3(1), dim3(64), 0, st, bar, status, timeout_code,
+                     invalid_code);
   return hipGetLastError();
 }
 

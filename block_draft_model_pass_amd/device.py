@@ -190,6 +190,34 @@ class Drafter:
                                        self.ws_ptr, self.ws_bytes, stream_ptr())
         return cand
 
+    def draft_commit_dev(self, taps: torch.Tensor, taps_pos0: int, state: torch.Tensor,
+                         block: int, mask_id: int = synth.MASK_ID,
+                         cand: torch.Tensor | None = None, logits: torch.Tensor | None = None,
+                         hidden: torch.Tensor | None = None) -> torch.Tensor:
+        """draft_commit with p, the anchor and the commit count read from the
+        int64 device words state = {p, anchor, n_commit}; taps holds the taps
+        of positions taps_pos0 .. taps_pos0 + len(taps) - 1
+        (dflash_draft_block_commit_dev)."""
+        if cand is None:
+            cand = torch.empty(max(block - 1, 1), dtype=torch.int32, device=self.device)
+        _lib.dflash_draft_block_commit_dev(self.w.desc, self.kv.desc, taps.data_ptr(), taps_pos0,
+                                           taps.shape[0], state.data_ptr(), mask_id, block,
+                                           cand.data_ptr(),
+                                           logits.data_ptr() if logits is not None else None,
+                                           hidden.data_ptr() if hidden is not None else None,
+                                           self.ws_ptr, self.ws_bytes, stream_ptr())
+        return cand
+
+    def verify_advance(self, cand: torch.Tensor, target: torch.Tensor, k: int,
+                       state: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+        """verify() that also advances state = {p, anchor, n_commit}
+        (dflash_verify_greedy_advance)."""
+        if out is None:
+            out = torch.empty(2, dtype=torch.int32, device=self.device)
+        _lib.dflash_verify_greedy_advance(cand.data_ptr(), target.data_ptr(), k,
+                                          state.data_ptr(), out.data_ptr(), stream_ptr())
+        return out
+
     def draft_gated(self, p: int, anchor: int, block: int, min_p: float,
                     mask_id: int = synth.MASK_ID, cand: torch.Tensor | None = None,
                     conf: torch.Tensor | None = None, n_keep: torch.Tensor | None = None):
@@ -227,8 +255,9 @@ class Drafter:
         return out
 
     def status(self, out: torch.Tensor | None = None) -> torch.Tensor:
-        """Device word: DFLASH_OK, or DFLASH_ETIMEOUT if the last pass gave up
-        waiting at a grid barrier."""
+        """Device word: DFLASH_OK, DFLASH_ETIMEOUT if the last pass gave up
+        waiting at a grid barrier, or DFLASH_EINVAL if it found its
+        device-resident positions invalid."""
         if out is None:
             out = torch.empty(1, dtype=torch.int32, device=self.device)
         _lib.dflash_draft_status(self.ws_ptr, self.ws_bytes, out.data_ptr(), stream_ptr())

@@ -273,6 +273,31 @@ DFLASH_API int32_t dflash_draft_block_commit(const dflash_weights* w, const dfla
                                   int32_t* cand, void* logits_opt, void* hidden_opt,
                                   void* ws, size_t ws_bytes, void* stream);
 
+/* The decode cycle with its positions in device memory, so that a cycle
+ * needs no device-to-host read ("Speculative decode integration" on the PR
+ * #1426 page: each cycle commits what the last verify accepted and drafts at
+ * the next position; the PR #3322 page's "Draft attention fix (2026-10-20)"
+ * replays drafting windows from a graph).  Same pass as
+ * dflash_draft_block_commit, with p, anchor_id and n_commit read by the
+ * kernels, when they run, from
+ *   state : int64 [3] device words {p, anchor_id, n_commit} (8-byte
+ *           aligned), advanced by dflash_verify_greedy_advance
+ *   taps  : bf16 [taps_rows][5][2560] device buffer, row r holding the target
+ *           taps of position taps_pos0 + r; the commit rows are positions
+ *           p - n_commit .. p - 1, which must lie in it
+ * The state is checked on the device as the host entry points check their
+ * arguments (p >= n_commit, n_commit in 0..8, anchor_id in [0, vocab), the
+ * commit rows inside taps); when it fails the pass reads nothing from it,
+ * writes cand = -1 (conf NaN, n_keep 0) and dflash_draft_status reports
+ * DFLASH_EINVAL.  Host checks (returned): as dflash_draft_block, plus state
+ * and taps non-NULL and aligned, taps_pos0 >= 0, taps_rows >= 0. */
+DFLASH_API int32_t dflash_draft_block_commit_dev(const dflash_weights* w, const dflash_kv* kv,
+                                                 const void* taps, int64_t taps_pos0,
+                                                 int64_t taps_rows, const int64_t* state,
+                                                 int32_t mask_id, int32_t block, int32_t* cand,
+                                                 void* logits_opt, void* hidden_opt, void* ws,
+                                                 size_t ws_bytes, void* stream);
+
 /* dflash_draft_block for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): no workspace argument; the pass runs in a 66 MiB device array
@@ -335,6 +360,19 @@ DFLASH_API int32_t dflash_lm_head_argmax(const dflash_weights* w, const void* hi
 DFLASH_API int32_t dflash_verify_greedy(const int32_t* cand, const int32_t* target, int32_t k,
                              int32_t* out, void* stream);
 
+/* dflash_verify_greedy that also advances a device-resident decode state
+ * (the state words of dflash_draft_block_commit_dev): after computing
+ * out = {accepted, next} it sets p += accepted + 1, anchor_id = next and
+ * n_commit = accepted + 1, so the next cycle's pass commits the accepted
+ * candidates' cells and the anchor's and drafts after them (RFC #366,
+ * "Verification and state management": the accepted tokens plus the
+ * verifier's continuation token are committed).  state: int64 [3], 8-byte
+ * aligned; other arguments as dflash_verify_greedy (pointers 4-byte
+ * aligned). */
+DFLASH_API int32_t dflash_verify_greedy_advance(const int32_t* cand, const int32_t* target,
+                                                int32_t k, int64_t* state, int32_t* out,
+                                                void* stream);
+
 /* Greedy verification of the candidates a confidence gate kept, with the
  * count read on the device (the n_keep word of dflash_draft_block_gated), so
  * that truncating the proposal needs no device-to-host read (PR #3322,
@@ -347,12 +385,14 @@ DFLASH_API int32_t dflash_verify_greedy(const int32_t* cand, const int32_t* targ
 DFLASH_API int32_t dflash_verify_greedy_gated(const int32_t* cand, const int32_t* target, int32_t k_max,
                                    const int32_t* n_keep, int32_t* out, void* stream);
 
-/* Outcome of the last proposal pass (dflash_draft_block or
- * dflash_draft_block_gated) enqueued with the workspace `ws`: writes, in
- * stream order after that pass, DFLASH_OK or DFLASH_ETIMEOUT (the pass gave
- * up waiting at a grid barrier) into the int32 device word `status`.  Lets
- * callers that read only logits_opt / hidden_opt, or block 1 (no
- * candidates), see a give-up.  Undefined before the workspace's first pass. */
+/* Outcome of the last proposal pass (any dflash_draft_block* entry point
+ * with a workspace) enqueued with the workspace `ws`: writes, in stream order
+ * after that pass, DFLASH_OK, DFLASH_ETIMEOUT (the pass gave up waiting at a
+ * grid barrier) or DFLASH_EINVAL (dflash_draft_block_commit_dev found its
+ * device state invalid and did nothing) into the int32 device word
+ * `status`.  Lets callers that read only logits_opt / hidden_opt, or block 1
+ * (no candidates), see a give-up.  Undefined before the workspace's first
+ * pass. */
 DFLASH_API int32_t dflash_draft_status(const void* ws, size_t ws_bytes, int32_t* status, void* stream);
 
 /* Optional finite check of a device buffer, for callers that want the

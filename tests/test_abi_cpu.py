@@ -302,6 +302,35 @@ def test_stage_readout_arguments(lib):
     assert S(nb=need // 4) == _lib.DFLASH_EWORKSPACE
 
 
+def test_device_cycle_arguments(lib):
+    """The device-resident cycle's host checks: state and taps present and
+    aligned, taps_pos0 / taps_rows non-negative, block and mask as for
+    dflash_draft_block; the advancing verify checks k and its pointers."""
+    E = _lib.DFLASH_EINVAL
+    w, kv = fake_weights(), fake_kv()
+    need = _lib.dflash_workspace_size(w, 0, 8)
+
+    def D(taps=A, pos0=0, rows=64, state=A, mask=2, block=8, cand=A, ws=A, nb=need):
+        return _lib.dflash_draft_block_commit_dev(w, kv, taps, pos0, rows, state, mask, block,
+                                                  cand, None, None, ws, nb, None, check=False)
+
+    assert D(state=None) == E and D(state=A + 4) == E
+    assert D(taps=None) == E and D(taps=A + 8) == E
+    assert D(pos0=-1) == E and D(rows=-1) == E
+    assert D(block=0) == E and D(block=9) == E and D(mask=-1) == E
+    assert D(cand=None) == E and D(ws=None) == E
+    assert D(nb=need - 1) == _lib.DFLASH_EWORKSPACE
+    V = _lib.dflash_verify_greedy_advance
+    assert V(A, A, 8, A, A, check=False) == E
+    assert V(A, A, -1, A, A, check=False) == E
+    assert V(A, A, 7, None, A, check=False) == E
+    assert V(A, A, 7, A + 4, A, check=False) == E       # state: 8-byte words
+    assert V(A, None, 7, A, A, check=False) == E
+    assert V(A, A, 7, A, None, check=False) == E
+    assert V(None, A, 3, A, A, check=False) == E
+    assert V(A, A, 7, A, A + 2, check=False) == E
+
+
 def test_packed_copy_may_stand_in_for_row_major_matrices(lib):
     """With the streaming copies set, the row-major matrices (fc, the layer
     matrices, the LM head) may be null -- the weights are then held once;
