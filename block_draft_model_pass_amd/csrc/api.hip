@@ -63,7 +63,7 @@ static_assert(static_cast<size_t>(KV_SPLITS) * GEMV_ROWS * KV_N <= PART_FLOATS,
               "the Wk / Wv partials share the fc partials' workspace");
 
 struct Layout {
-  size_t part, po, pm, pl, keys, lse, rope, ss, qkv, hv, h16, ov, uv, bar, tab, yc, ckv, y;
+  size_t part, po, pm, pl, keys, lse, rope, ss, qkv, hv, h16, ov, uv, bar, tab, yc, cn, ckv, y;
   size_t fixed;  // bytes before y
 };
 
@@ -93,8 +93,9 @@ Layout layout() {
   L.uv = take(off, 2 * NL * MAXB * F);
   L.bar = take(off, pass_bar_bytes());
   L.tab = take(off, pass_tab_bytes());
-  // commit rows of the fused draft-commit cycle: fc outputs, raw K | V
+  // commit rows of the fused draft-commit cycle: fc outputs, fused rows, raw K | V
   L.yc = take(off, sizeof(float) * MAXB * H);
+  L.cn = take(off, sizeof(uint16_t) * MAXB * H);
   L.ckv = take(off, sizeof(float) * dfl::L * MAXB * 2 * NKV * D);
   L.fixed = off;
   L.y = off;
@@ -598,6 +599,7 @@ int32_t draft_block_impl(const dflash_weights* w, const dflash_kv* kv, int64_t p
   q.fc = packed_fc(w);
   q.hidden_norm = u16p(w->hidden_norm);
   q.yc = at<float>(ws, Lw.yc);
+  q.cn = at<uint16_t>(ws, Lw.cn);
   q.ckv = at<float>(ws, Lw.ckv);
   if (dev) {
     q.dstate = dev->state;

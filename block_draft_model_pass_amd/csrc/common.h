@@ -333,6 +333,7 @@ struct PassLaunch {
   int nc = 0;
   int64_t pos0 = 0;
   float* yc = nullptr;       // [8][2560] fp32
+  uint16_t* cn = nullptr;    // [8][2560] the commit rows' fused context (MFMA input format)
   float* ckv = nullptr;      // [5][8][1024] fp32
   float* conf = nullptr;     // [B-1] candidate probabilities, or null
   int32_t* nkeep = nullptr;  // confidence-gated candidate count, or null

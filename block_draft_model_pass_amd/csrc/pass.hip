@@ -178,6 +178,8 @@ struct PassArgs {
   int nc;
   int64_t pos0;
   float* yc;              // [8][H] fc outputs of the commit rows (fp32)
+  uint16_t* cn;           // [8][H] their fused context rows in the MFMA input format,
+                          // built in layer 0 and staged from here by later layers
   float* ckv;             // [L][8][1024] raw Wk | Wv outputs of the commit rows (fp32)
   // outputs
   int32_t* cand;
@@ -659,9 +661,10 @@ __device__ __forceinline__ void xn_finish(const PassArgs& a, Smem& s, const XnRe
 // per-tile sums of squares; wave b < B then reduces row b's sums (fixed
 // order) and every thread normalises its groups in place.  `after` runs on
 // ACT_WAVE once its copies have landed (its weight slice).
-template <int XF, class After>
+template <int XF, class Pre, class After>
 __device__ __forceinline__ void build_x_norm_staged(const PassArgs& a, Smem& s, int ver, int np,
-                                                    const uint16_t* gain, After&& after) {
+                                                    const uint16_t* gain, Pre&& pre,
+                                                    After&& after) {
   const int tid = otid(), wave = wid(), lane = tid & 63;
   if (act_wave()) {
     stage_rows<H>(a, s, a.h16 + ver * HSTRIDE);
@@ -671,6 +674,7 @@ __device__ __forceinline__ void build_x_norm_staged(const PassArgs& a, Smem& s, 
     const __amdgpu_buffer_rsrc_t rq =
         buf_rsrc(a.ss + ver * SSTRIDE, static_cast<uint32_t>(np) * MAXB * 4);
     for (int c = 0; c * 1024 < np * MAXB * 4; ++c) g2lds(rq, s.ssb + 256 * c, 1024 * c + 16 * lane);
+    pre();  // more rows staged in the same round
     staged_wait();
     after();
   }
@@ -710,10 +714,16 @@ __device__ __forceinline__ void build_x_norm_staged(const PassArgs& a, Smem& s, 
   lds_sync();
 }
 
+template <int XF, class After>
+__device__ __forceinline__ void build_x_norm_staged(const PassArgs& a, Smem& s, int ver, int np,
+                                                    const uint16_t* gain, After&& after) {
+  build_x_norm_staged<XF>(a, s, ver, np, gain, [] {}, after);
+}
+
 template <int XF>
 __device__ __forceinline__ void build_x_norm(const PassArgs& a, Smem& s, int ver, int np,
                                              const uint16_t* gain) {
-  build_x_norm_staged<XF>(a, s, ver, np, gain, [] {});
+  build_x_norm_staged<XF>(a, s, ver, np, gain, [] {}, [] {});
 }
 
 // The residual rows this lane updates (tile's 16 columns, row r), loaded at
@@ -912,21 +922,52 @@ __device__ __forceinline__ void qkv_prefetch(const PassArgs& a, int l, QkvTile<F
 
 // Blocks whose two tiles are Wk / Wv rows (the ctx K/V projection's rows).
 __device__ __forceinline__ bool qkv_kv_block(int w) { return 2 * w * 16 >= NQ * D && qkv_has(w); }
+constexpr int QKV_KV_FIRST = NQ * D / 32;  // the first block with Wk / Wv tiles
+
+// The commit rows built in LDS rows 8..15 (layer 0) into a.cn for the later
+// layers' QKV phases (read there after several barriers: coherent stores).
+__device__ __forceinline__ void commit_rows_keep(const PassArgs& a, Smem& s) {
+  constexpr int XS = H + XS_PAD, U = MAXB * (H / 8) / NTHR;
+  static_assert(MAXB * (H / 8) % NTHR == 0, "whole 16-byte groups per thread");
+  const int tid = otid();
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int e = tid + u * NTHR, t = e / (H / 8), k8 = e % (H / 8);
+    st_coh128(a.cn + static_cast<size_t>(t) * H + 8 * k8,
+              *reinterpret_cast<const uint4*>(s.x + (MAXB + t) * XS + 8 * k8));
+  }
+}
 
 template <int FMT>
 __device__ __forceinline__ void qkv_phase(const PassArgs& a, Smem& s, int l, int np, QkvTile<FMT>& W) {
   const int w = blockIdx.x, wave = wid(), lane = otid() & 63;
   const int r = lane & 15, g = lane >> 4;
   const bool has = qkv_has(w);
-  // commit rows ride the Wk / Wv tiles as MFMA columns 8..15
+  // commit rows ride the Wk / Wv tiles as MFMA columns 8..15: built from the
+  // fc outputs in layer 0 (and kept in a.cn by the first such block), staged
+  // from a.cn with the activations in later layers
   const bool cm = a.nc > 0 && qkv_kv_block(w);
   // activations staged by ACT_WAVE, which then issues its weight slice
   if (has)
-    build_x_norm_staged<FMT>(a, s, 2 * l, np, ctab(a)->in_norm[l],
-                             [&] { qkv_prefetch<FMT>(a, l, W, true); });
-  if (cm) {
+    build_x_norm_staged<FMT>(
+        a, s, 2 * l, np, ctab(a)->in_norm[l],
+        [&] {
+          if (cm && l > 0) {
+            constexpr int XS = H + XS_PAD;
+            const int lane = otid() & 63;
+            const __amdgpu_buffer_rsrc_t rc = buf_rsrc(a.cn, MAXB * H * 2);
+            for (int t = 0; t < MAXB; ++t)
+#pragma unroll
+              for (int c = 0; c < H * 2 / 1024; ++c)
+                g2lds(rc, s.x + (MAXB + t) * XS + 512 * c,
+                      static_cast<uint32_t>(t * H * 2 + 1024 * c + 16 * lane));
+          }
+        },
+        [&] { qkv_prefetch<FMT>(a, l, W, true); });
+  if (cm && l == 0) {
     commit_rows_build<FMT>(a, s);
     lds_sync();
+    if (w == QKV_KV_FIRST) commit_rows_keep(a, s);
   }
   if (has) {
     const int tile = 2 * w + (wave >> 2);
@@ -1954,10 +1995,15 @@ __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs args) {
   QkvTile<FMT> Wq;
   LmTile<LMF> Wl;   // LM head slice, prefetched after the last layer
   // Commit rows (fused draft-commit cycle) through fc first; then layer 0
-  // QKV weights stream while the grid lines up.  h, ss, the RoPE table and
-  // the layer table come from the init kernel.
+  // QKV weights stream while the grid lines up at the barrier that publishes
+  // the commit rows' fc outputs.  Without commit rows there is nothing to
+  // wait for -- h, ss, the RoPE table and the layer table come from the init
+  // kernel, visible from the start -- and every block skips that barrier.
   fc_phase<FMT>(a, s);
-  grid_sync_pf(a, bk, [&] { qkv_prefetch<FMT>(a, 0, Wq, !act_wave()); });
+  if (a.nc > 0)
+    grid_sync_pf(a, bk, [&] { qkv_prefetch<FMT>(a, 0, Wq, !act_wave()); });
+  else
+    qkv_prefetch<FMT>(a, 0, Wq, !act_wave());
   int np = 1;    // sums of squares of h: one entry per row from the init kernel
   for (int l = 0; l < L; ++l) {
     qkv_phase<FMT>(a, s, l, np, Wq);
@@ -2151,6 +2197,7 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
   a.nc = q.nc;
   a.pos0 = q.pos0;
   a.yc = q.yc;
+  a.cn = q.cn;
   a.ckv = q.ckv;
   a.cand = q.cand;
   a.logits = q.logits;
@@ -2167,10 +2214,11 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
   if (q.nch < 1 || q.nch > 128 || q.grid < NKV * q.nch || q.grid < QKV_N / 32 ||
       q.grid < NKV * a.nqt * 16 || q.grid > 1024)
     return hipErrorInvalidValue;
-  if (q.nc < 0 || q.nc > MAXB || (q.nc > 0 && (!q.taps || !q.fc || !q.yc || !q.ckv || q.grid < NT_H)))
+  if (q.nc < 0 || q.nc > MAXB ||
+      (q.nc > 0 && (!q.taps || !q.fc || !q.yc || !q.cn || !q.ckv || q.grid < NT_H)))
     return hipErrorInvalidValue;
   // device-resident positions: up to MAXB commit rows, at most maxch chunks per head
-  if (q.dstate && (!q.taps_base || !q.fc || !q.yc || !q.ckv || q.grid < NT_H || q.maxch < 1 ||
+  if (q.dstate && (!q.taps_base || !q.fc || !q.yc || !q.cn || !q.ckv || q.grid < NT_H || q.maxch < 1 ||
                    q.maxch > 128 || q.grid < NKV * q.maxch || q.window < 1 || q.taps_pos0 < 0 ||
                    q.taps_rows < 0))
     return hipErrorInvalidValue;
