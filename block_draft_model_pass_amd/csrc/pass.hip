@@ -45,6 +45,7 @@ namespace dfl {
 namespace {
 
 constexpr int NWAVE = 8;
+constexpr int ACT_WAVE = NWAVE - 1;  // the activation-staging wave (see "staged activations")
 constexpr int NTHR = NWAVE * 64;
 constexpr int XS_PAD = 8;                 // bf16 padding of an LDS activation row
 constexpr int XS_MAX = F + XS_PAD;        // widest activation row (down projection)
@@ -305,13 +306,19 @@ struct BarState {
 // stalls: measured 467 -> 445 us per pass at ctx 8192, block 8, with every
 // barrier contributing.)
 //
+// The release is polled by one lane whose wave issued no prefetch at this
+// barrier when there is one (`quiet_poller`: the staging wave, ACT_WAVE) --
+// the poll loads of a wave that just issued its prefetch return only after
+// that prefetch, in issue order, so such a block saw the release late --
+// else by thread 0.
+//
 // The wait is bounded in wall-clock time (the constant-rate counter read by
 // s_memrealtime): a wait longer than a.wait_ticks (plus 16 polls) sets the
 // status word and gives up.  A block that gave up, or that finds the status word set (checked
 // every 64 polls), waits at no later barrier of the pass, so a pass whose
 // blocks cannot all be resident ends after about one bound instead of
 // hanging the stream.
-template <class Pf>
+template <bool quiet_poller = false, class Pf>
 __device__ __forceinline__ void grid_sync_pf(const PassArgs& a, BarState& b, Pf&& prefetch) {
   lds_sync();
   const unsigned k = ++b.k;
@@ -334,7 +341,8 @@ __device__ __forceinline__ void grid_sync_pf(const PassArgs& a, BarState& b, Pf&
   }
   __builtin_amdgcn_s_barrier();  // thread 0's arrival has gone out
   prefetch();
-  if (otid() == 0 && wait && !b.quit) {
+  const bool poller = quiet_poller ? otid() == ACT_WAVE * 64 : (otid() == 0 && wait);
+  if (poller && !b.quit) {
     // The clock and the status word are read every 16 and 64 polls only (a
     // counter read per poll would delay seeing the release); the clock starts
     // at the 16th poll, so a wait gives up after the bound plus 16 polls.
@@ -556,8 +564,6 @@ __device__ __forceinline__ f32x4 group_sum(Smem& s, int w0, int n, int lane) {
 // waves' slices were issued during the barrier.  (ATTN and GU keep the
 // register path: there the late slice of ACT_WAVE -- a K/V block share, or
 // two gate/up pairs -- costs more than the earlier activations save.)
-constexpr int ACT_WAVE = NWAVE - 1;
-
 __device__ __forceinline__ bool act_wave() { return wid() == ACT_WAVE; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
@@ -2001,7 +2007,7 @@ __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs args) {
   // kernel, visible from the start -- and every block skips that barrier.
   fc_phase<FMT>(a, s);
   if (a.nc > 0)
-    grid_sync_pf(a, bk, [&] { qkv_prefetch<FMT>(a, 0, Wq, !act_wave()); });
+    grid_sync_pf<true>(a, bk, [&] { qkv_prefetch<FMT>(a, 0, Wq, !act_wave()); });
   else
     qkv_prefetch<FMT>(a, 0, Wq, !act_wave());
   int np = 1;    // sums of squares of h: one entry per row from the init kernel
@@ -2013,18 +2019,19 @@ __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs args) {
     grid_sync(a, bk);
     merge_phase<FMT>(a, s, l);
     OTile<FMT> Wo;
-    grid_sync_pf(a, bk, [&] { o_prefetch<FMT>(a, l, Wo, !act_wave()); });
+    grid_sync_pf<true>(a, bk, [&] { o_prefetch<FMT>(a, l, Wo, !act_wave()); });
     o_phase<FMT>(a, s, l, Wo);
     GuTile<FMT> Wg;
     grid_sync_pf(a, bk, [&] { gu_prefetch<FMT>(a, l, blockIdx.x, Wg, true); });
     gu_phase<FMT>(a, s, l, NT_H, Wg);
     DownTile<FMT> Wd;
-    grid_sync_pf(a, bk, [&] { down_prefetch<FMT>(a, l, Wd, down_pre(wid())); });
+    grid_sync_pf<(ACT_WAVE > DOWN_PRE_LAST)>(a, bk,
+                                           [&] { down_prefetch<FMT>(a, l, Wd, down_pre(wid())); });
     down_phase<FMT>(a, s, l, Wd);
     // Both prefetch targets are assigned on every iteration (zeros when
     // idle), so neither carries a value around the loop.
     const bool last = l + 1 == L;
-    grid_sync_pf(a, bk, [&] {
+    grid_sync_pf<true>(a, bk, [&] {
       qkv_prefetch<FMT>(a, last ? l : l + 1, Wq, !last && !act_wave());
       lm_prefetch<LMF>(a, blockIdx.x, Wl, last && a.B > 1 && !act_wave());
     });
