@@ -13,7 +13,6 @@ using namespace dfl;
 
 namespace {
 
-constexpr int NCH_TARGET = 64;        // chunks per KV head aimed for
 constexpr int LMH_GRID = 256;         // standalone LM-head kernel: one block per CU
 constexpr int KEYS_MAX = 1024;        // argmax key slots (blocks of either LM-head launch)
 constexpr long BARRIER_WAIT_US = 500000;   // grid-barrier wait bound (0.5 s of wall clock)
@@ -63,7 +62,7 @@ static_assert(static_cast<size_t>(KV_SPLITS) * GEMV_ROWS * KV_N <= PART_FLOATS,
               "the Wk / Wv partials share the fc partials' workspace");
 
 struct Layout {
-  size_t part, po, pm, pl, keys, lse, rope, ss, qkv, hv, h16, ov, uv, bar, tab, yc, cn, ckv, y;
+  size_t part, po, pm, pl, keys, lse, rope, ss, qkv, hv, h16, ov, uv, bar, tab, yc, fcp, cn, ckv, y;
   size_t fixed;  // bytes before y
 };
 
@@ -95,6 +94,7 @@ Layout layout() {
   L.tab = take(off, pass_tab_bytes());
   // commit rows of the fused draft-commit cycle: fc outputs, fused rows, raw K | V
   L.yc = take(off, sizeof(float) * MAXB * H);
+  L.fcp = take(off, pass_fcp_bytes());
   L.cn = take(off, sizeof(uint16_t) * MAXB * H);
   L.ckv = take(off, sizeof(float) * dfl::L * MAXB * 2 * NKV * D);
   L.fixed = off;
@@ -280,7 +280,7 @@ const uint16_t* u16p(const void* p) { return static_cast<const uint16_t*>(p); }
 // whatever the context length or block size.  In host code `scratch` names a
 // host-side stand-in, never the device memory: its device address is looked
 // up once per device (scratch_on_device) and only that address is used.
-constexpr size_t SCRATCH_BYTES = static_cast<size_t>(66) << 20;
+constexpr size_t SCRATCH_BYTES = static_cast<size_t>(67) << 20;
 static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
 
 // Device address of `scratch` on the current device (null on failure),
@@ -599,6 +599,7 @@ int32_t draft_block_impl(const dflash_weights* w, const dflash_kv* kv, int64_t p
   q.fc = packed_fc(w);
   q.hidden_norm = u16p(w->hidden_norm);
   q.yc = at<float>(ws, Lw.yc);
+  q.fcp = at<float>(ws, Lw.fcp);
   q.cn = at<uint16_t>(ws, Lw.cn);
   q.ckv = at<float>(ws, Lw.ckv);
   if (dev) {

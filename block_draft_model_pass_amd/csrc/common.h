@@ -333,6 +333,7 @@ struct PassLaunch {
   int nc = 0;
   int64_t pos0 = 0;
   float* yc = nullptr;       // [8][2560] fp32
+  float* fcp = nullptr;      // FC-phase tile partials (pass_fcp_bytes)
   uint16_t* cn = nullptr;    // [8][2560] the commit rows' fused context (MFMA input format)
   float* ckv = nullptr;      // [5][8][1024] fp32
   float* conf = nullptr;     // [B-1] candidate probabilities, or null
@@ -357,6 +358,7 @@ size_t pass_pml_bytes();  // chunk maxima (or sums), all layers
 size_t pass_smem_bytes();
 size_t pass_tab_bytes();
 size_t pass_bar_bytes();
+size_t pass_fcp_bytes();  // FC-phase tile partials of the fused draft-commit pass
 
 // Greedy verify of k candidates, or of min(max(*k_dev, 0), k) when k_dev is
 // set; with `state` ({p, anchor, n_commit}, int64) it also advances the

@@ -179,6 +179,7 @@ struct PassArgs {
   int nc;
   int64_t pos0;
   float* yc;              // [8][H] fc outputs of the commit rows (fp32)
+  float* fcp;             // [160][8][64][4] the FC phase's per-block tile partials
   uint16_t* cn;           // [8][H] their fused context rows in the MFMA input format,
                           // built in layer 0 and staged from here by later layers
   float* ckv;             // [L][8][1024] raw Wk | Wv outputs of the commit rows (fp32)
@@ -280,7 +281,10 @@ __device__ __forceinline__ void st_coh_f4(float* p, f32x4 v) {
 // stores and the waiters' next poll, which matters because every memory
 // round trip is slow while the weight stream saturates HBM.
 // Per-XCD release words at [640 + 32 x] (see grid_sync_pf).
-constexpr int BAR_STATUS = 0, BAR_TOP = 64, BAR_XCD = 128, BAR_REL = 640, BAR_WORDS = 1024;
+constexpr int BAR_STATUS = 0, BAR_TOP = 64, BAR_XCD = 128, BAR_REL = 640, BAR_FC = 1024,
+              BAR_FCDONE = BAR_FC + 160, BAR_WORDS = 1024 + 256;
+// BAR_FC: arrival counters of the FC phase's 160 tiles; BAR_FCDONE: tiles
+// whose fc outputs are written
 // BAR_STATUS values: a barrier wait gave up, or the device-resident positions
 // were invalid (the pass then did nothing but report it)
 constexpr unsigned ST_TIMEOUT = 1u, ST_INVALID = 2u;
@@ -771,97 +775,191 @@ __device__ __forceinline__ void residual_epilogue(const PassArgs& a, f32x4 acc, 
 // extra weight bytes; only fc (65.5 MB bf16) is added, in an FC phase before
 // the first barrier.
 //
-// FC phase: block w < 160 owns fc output tile w (16 of the 2560 rows) over the
-// whole 12800-wide k range, so the five taps' partial sums meet inside the
-// block (deterministic).  Three rounds take taps (0, 1), (2, 3), (4, -): a
-// round stages its two taps' rows in LDS (rows 0..7 and 8..15, in the MFMA
-// input format) and waves 4h .. 4h+3 take tap 2r+h in k quarters of 640; the
-// next round's weights are issued right after the round's tap loads.
-template <int FMT> using FcTile = WTile<FMT, 640 / KPerLoad<FMT>::v>;
+// FC phase: fc's 160 output tiles (16 of the 2560 rows) x 50 k slices of 256
+// (of the 12800 = 5 taps x 2560) are 8000 work items dealt to the grid in
+// contiguous runs (block b: items [8000 b / G, 8000 (b+1) / G), 31 or 32 at
+// G = 256, spanning at most two tiles), so every block streams ~1/G of fc.
+// Each wave takes every 8th item of its block's run: the item's weights
+// (its 16 rows x 256 k) and the commit rows' taps at the same k slots, both
+// straight into registers (lanes of MFMA columns 8..15 load no taps), with
+// the next item's loads in flight while the current one runs; per tile it
+// keeps one accumulator.  The block's waves are summed in LDS into one
+// partial per tile it touched (16 rows x 8 commit rows, fp32), written to
+// the workspace; the last of a tile's 2-3 contributing blocks (an arrival
+// counter per tile) sums the tile's partials in contributor order -- the
+// result does not depend on which block finishes last -- and writes the
+// tile's 16 columns of the fc outputs.
+constexpr int FC_SLICE = 256, FC_SLICES = T * H / FC_SLICE, FC_ITEMS = NT_H * FC_SLICES;
+constexpr int FC_CONTRIB = 4;  // most blocks sharing a tile: 3 at 224 <= G <= 256, 4 up to G = 384
+constexpr int FC_GRID_MAX = 384;
+template <int FMT> using FcTile = WTile<FMT, FC_SLICE / KPerLoad<FMT>::v>;
 
+__device__ __forceinline__ int fc_lo(int b, int G) { return b * FC_ITEMS / G; }
+__device__ __forceinline__ int fc_owner(int item, int G) { return ((item + 1) * G - 1) / FC_ITEMS; }
+
+// k offset (from the item's first k) of the 8-element activation group j of
+// lane group g, matching the weight slots of each format (see load_wt).
 template <int FMT>
-__device__ __forceinline__ void fc_load(const PassArgs& a, int round, FcTile<FMT>& W) {
-  const int w = blockIdx.x, wave = wid(), lane = otid() & 63;
-  const int tap = 2 * round + (wave >> 2);
-  constexpr int N = 640 / KPerLoad<FMT>::v;
-  load_wt<FMT, N>(W, WMat{a.fc, H, T * H}, w * 16 + (lane & 15),
-                  (tap < T ? tap : 0) * H + (wave & 3) * 640, lane >> 4, N, tap < T);
+__device__ __forceinline__ int fc_xslot(int j, int g) {
+  if constexpr (FMT == W_BF16) return 32 * j + 8 * g;
+  else if constexpr (FMT == W_Q8_0) return 64 * (j >> 1) + 16 * g + 8 * (j & 1);
+  else return 128 * (j >> 2) + 32 * g + 8 * (j & 3);
 }
 
-constexpr int FC_U = 2 * MAXB * (H / 8) / NTHR;  // 16-byte tap groups per thread per round (10)
-
-// Loads of round r's taps: group e = (half h, row t, 8-element group k8) ->
-// tap 2r + h of commit row t.  Rows past nc (or a missing tap) re-read a
-// valid group and are stored as zeros.
-__device__ __forceinline__ void fc_tap_load(const PassArgs& a, int round, uint4 (&v)[FC_U]) {
-  const int tid = otid();
+// One item's loads: weights of rows 16 t.. at k = 256 s.., and taps of commit
+// row n (lanes n < 8 that hold a commit row; the others get zeros).
+template <int FMT>
+__device__ __forceinline__ void fc_item_load(const PassArgs& a, int item, bool valid, FcTile<FMT>& W,
+                                             uint4 (&x)[8]) {
+  const int lane = otid() & 63, n = lane & 15, g = lane >> 4;
+  const int it = valid ? item : 0;
+  const int t = it / FC_SLICES, k0 = (it % FC_SLICES) * FC_SLICE;
+  constexpr int N = FC_SLICE / KPerLoad<FMT>::v;
+  load_wt<FMT, N>(W, WMat{a.fc, H, T * H}, t * 16 + n, k0, g, N, valid);
+  const bool xv = valid && n < a.nc;
+  const uint16_t* xr = a.taps + static_cast<size_t>(xv ? n : 0) * (T * H) + k0;
 #pragma unroll
-  for (int u = 0; u < FC_U; ++u) {
-    const int e = tid + u * NTHR;
-    const int h = e / (MAXB * (H / 8)), t = (e / (H / 8)) % MAXB, k8 = e % (H / 8);
-    const int tap = 2 * round + h;
-    const bool ok = t < a.nc && tap < T;
-    v[u] = gld<uint4>(a.taps + (static_cast<size_t>(ok ? t : 0) * T + (ok ? tap : 0)) * H + 8 * k8);
-  }
+  for (int j = 0; j < 8; ++j) x[j] = xv ? gld<uint4>(xr + fc_xslot<FMT>(j, g)) : make_uint4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = static_cast<uint32_t>(f32_to_f16_bits(bf16_to_f32(static_cast<uint16_t>(w[i])))) |
+           (static_cast<uint32_t>(f32_to_f16_bits(bf16_to_f32(static_cast<uint16_t>(w[i] >> 16)))) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 template <int FMT>
-__device__ __forceinline__ void fc_tap_store(const PassArgs& a, Smem& s, int round,
-                                             const uint4 (&v)[FC_U]) {
-  constexpr int XS = H + XS_PAD;
-  const int tid = otid();
+__device__ __forceinline__ f32x4 fc_item_mma(const FcTile<FMT>& W, const uint4 (&x)[8], f32x4 acc) {
+  constexpr int N = FC_SLICE / KPerLoad<FMT>::v;
 #pragma unroll
-  for (int u = 0; u < FC_U; ++u) {
-    const int e = tid + u * NTHR;
-    const int h = e / (MAXB * (H / 8)), t = (e / (H / 8)) % MAXB, k8 = e % (H / 8);
-    const bool ok = t < a.nc && 2 * round + h < T;
-    uint4 x = ok ? v[u] : make_uint4(0, 0, 0, 0);
-    if constexpr (FMT != W_BF16) {  // fp16 next to decoded quantized weights
-      uint32_t wv[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        wv[i] = static_cast<uint32_t>(f32_to_f16_bits(bf16_to_f32(static_cast<uint16_t>(wv[i])))) |
-                (static_cast<uint32_t>(f32_to_f16_bits(bf16_to_f32(static_cast<uint16_t>(wv[i] >> 16)))) << 16);
-      x = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  for (int i = 0; i < N; ++i) {
+    if constexpr (FMT == W_BF16) {
+      acc = mfma_bf16(W.q[i], x[i], acc);
+    } else if constexpr (FMT == W_Q8_0) {
+      const h2 sc = scale_h2(W.s[i]);
+      acc = mfma_f16(dq8(W.q[i].x, W.q[i].y, sc), bf16x8_to_f16x8(x[2 * i]), acc);
+      acc = mfma_f16(dq8(W.q[i].z, W.q[i].w, sc), bf16x8_to_f16x8(x[2 * i + 1]), acc);
+    } else if constexpr (FMT == W_Q4_0) {
+      const h2 sc = scale_h2(W.s[i]);
+      acc = mfma_f16(dq4(W.q[i].x, W.q[i].y, false, sc), bf16x8_to_f16x8(x[4 * i]), acc);
+      acc = mfma_f16(dq4(W.q[i].z, W.q[i].w, false, sc), bf16x8_to_f16x8(x[4 * i + 1]), acc);
+      acc = mfma_f16(dq4(W.q[i].x, W.q[i].y, true, sc), bf16x8_to_f16x8(x[4 * i + 2]), acc);
+      acc = mfma_f16(dq4(W.q[i].z, W.q[i].w, true, sc), bf16x8_to_f16x8(x[4 * i + 3]), acc);
+    } else {
+      const h2 sc = scale_h2(W.s[i]);
+      const uint32_t hw = W.h[i];
+      acc = mfma_f16(dq5(W.q[i].x, W.q[i].y, false, q5_bits_packed<0>(hw), q5_bits_packed<1>(hw), sc),
+                     bf16x8_to_f16x8(x[4 * i]), acc);
+      acc = mfma_f16(dq5(W.q[i].z, W.q[i].w, false, q5_bits_packed<2>(hw), q5_bits_packed<3>(hw), sc),
+                     bf16x8_to_f16x8(x[4 * i + 1]), acc);
+      acc = mfma_f16(dq5(W.q[i].x, W.q[i].y, true, q5_bits_packed<4>(hw), q5_bits_packed<5>(hw), sc),
+                     bf16x8_to_f16x8(x[4 * i + 2]), acc);
+      acc = mfma_f16(dq5(W.q[i].z, W.q[i].w, true, q5_bits_packed<6>(hw), q5_bits_packed<7>(hw), sc),
+                     bf16x8_to_f16x8(x[4 * i + 3]), acc);
     }
-    *reinterpret_cast<uint4*>(s.x + (h * MAXB + t) * XS + 8 * k8) = x;
   }
+  return acc;
 }
 
 template <int FMT>
 __device__ __forceinline__ void fc_phase(const PassArgs& a, Smem& s) {
-  if (a.nc == 0 || blockIdx.x >= NT_H) return;
-  const int wave = wid(), lane = otid() & 63, r = lane & 15, g = lane >> 4;
-  constexpr int XS = H + XS_PAD;
-  constexpr int N = 640 / KPerLoad<FMT>::v;
-  const uint16_t* xr = s.x + ((wave >> 2) * MAXB + (r & 7)) * XS;  // columns 8..15 repeat 0..7
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (a.nc == 0) return;
+  const int G = static_cast<int>(gridDim.x), b = blockIdx.x;
+  const int wave = wid(), lane = otid() & 63, n = lane & 15, g = lane >> 4;
+  const int lo = fc_lo(b, G), hi = fc_lo(b + 1, G);
+  const int t0 = lo / FC_SLICES;          // first tile of the run
+  const int nt = (hi - 1) / FC_SLICES - t0 + 1;  // 1 or 2 tiles
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  // two register sets, alternating (rounds unrolled in pairs: no dynamic
+  // indexing of register arrays)
   FcTile<FMT> W0, W1;
-  uint4 tv[FC_U];
-  fc_tap_load(a, 0, tv);
-  fc_load<FMT>(a, 0, W0);
-  fc_load<FMT>(a, 1, W1);
-  fc_tap_store<FMT>(a, s, 0, tv);
-  lds_sync();
-  acc += mma_wt<FMT, N>(W0, xr, (wave & 3) * 640, g, N);
-  lds_sync();
-  fc_tap_load(a, 1, tv);
-  fc_load<FMT>(a, 2, W0);
-  fc_tap_store<FMT>(a, s, 1, tv);
-  lds_sync();
-  acc += mma_wt<FMT, N>(W1, xr, (wave & 3) * 640, g, N);
-  lds_sync();
-  fc_tap_load(a, 2, tv);
-  fc_tap_store<FMT>(a, s, 2, tv);
-  lds_sync();
-  if (wave < 4) acc += mma_wt<FMT, N>(W0, xr, (wave & 3) * 640, g, N);  // tap 4
-  s.red[wave][lane] = acc;
-  lds_sync();
-  if (wave == 0) {
-    acc = group_sum(s, 0, NWAVE, lane);
-    if (r < a.nc) st_coh_f4(a.yc + static_cast<size_t>(r) * H + blockIdx.x * 16 + 4 * g, acc);
+  uint4 x0[8], x1[8];
+  auto run = [&](int cur, const FcTile<FMT>& W, const uint4 (&x)[8]) {
+    if (cur < hi) {
+      if (cur / FC_SLICES == t0) acc0 = fc_item_mma<FMT>(W, x, acc0);
+      else acc1 = fc_item_mma<FMT>(W, x, acc1);
+    }
+  };
+  const int rounds = (hi - lo + NWAVE - 1) / NWAVE;
+  fc_item_load<FMT>(a, lo + wave, lo + wave < hi, W0, x0);
+  for (int r = 0; r < rounds; r += 2) {
+    const int c0 = lo + wave + NWAVE * r, c1 = c0 + NWAVE, c2 = c1 + NWAVE;
+    if (r + 1 < rounds) fc_item_load<FMT>(a, c1, c1 < hi, W1, x1);
+    run(c0, W0, x0);
+    if (r + 1 < rounds) {
+      if (r + 2 < rounds) fc_item_load<FMT>(a, c2, c2 < hi, W0, x0);
+      run(c1, W1, x1);
+    }
+  }
+  // the block's partial of each tile it touched: waves summed in LDS (fixed order)
+  float* part = a.fcp;
+  for (int ti = 0; ti < nt; ++ti) {
+    s.red[wave][lane] = ti == 0 ? acc0 : acc1;
+    lds_sync();
+    if (wave == 0) {
+      const f32x4 v = group_sum(s, 0, NWAVE, lane);
+      const int t = t0 + ti, q = b - fc_owner(t * FC_SLICES, G);  // contributor index
+      st_coh_f4(part + ((static_cast<size_t>(t) * FC_CONTRIB + q) * 64 + lane) * 4, v);
+    }
+    lds_sync();
   }
   wait_stores();
+  // arrival per tile; the last contributor sums the partials in contributor order
+  if (otid() == 0) {
+    for (int ti = 0; ti < nt; ++ti) {
+      const int t = t0 + ti;
+      const int q0 = fc_owner(t * FC_SLICES, G), q1 = fc_owner(t * FC_SLICES + FC_SLICES - 1, G);
+      const unsigned prev = __hip_atomic_fetch_add(a.bar + BAR_FC + t, 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      s.scal[ti] = prev == static_cast<unsigned>(q1 - q0) ? 1.f : 0.f;
+    }
+  }
+  lds_sync();
+  if (wave == 0) {
+    for (int ti = 0; ti < nt; ++ti) {
+      if (s.scal[ti] != 0.f) {
+        const int t = t0 + ti;
+        const int q0 = fc_owner(t * FC_SLICES, G), q1 = fc_owner(t * FC_SLICES + FC_SLICES - 1, G);
+        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q <= q1 - q0; ++q) {
+          const uint4 u = ld_coh128(part + ((static_cast<size_t>(t) * FC_CONTRIB + q) * 64 + lane) * 4);
+          sum += f32x4{__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                       __uint_as_float(u.w)};
+        }
+        // lane (n, g) holds rows 4g..4g+3 of the tile for commit row n
+        if (n < a.nc) st_coh_f4(a.yc + static_cast<size_t>(n) * H + t * 16 + 4 * g, sum);
+      }
+    }
+    wait_stores();
+    // the tiles this block completed are announced once their outputs are out
+    if (lane == 0)
+      for (int ti = 0; ti < nt; ++ti)
+        if (s.scal[ti] != 0.f)
+          __hip_atomic_fetch_add(a.bar + BAR_FCDONE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Wait (thread 0, bounded in wall-clock time like a barrier) until every fc
+// output tile is written: only the blocks that build the commit rows wait,
+// so the pass needs no grid barrier after the FC phase.
+__device__ __forceinline__ void fc_wait(const PassArgs& a) {
+  uint64_t t0 = 0;
+  unsigned n = 0;
+  while (ald(a.bar + BAR_FCDONE) < static_cast<unsigned>(NT_H)) {
+    __builtin_amdgcn_s_sleep(2);
+    if ((++n & 15) != 0) continue;
+    if ((n & 63) == 0 && ald(a.bar + BAR_STATUS) != 0u) break;  // the pass gave up
+    const uint64_t now = __builtin_amdgcn_s_memrealtime();
+    if (n == 16) {
+      t0 = now;
+    } else if (now - t0 > a.wait_ticks) {
+      __hip_atomic_store(a.bar + BAR_STATUS, ST_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+  }
 }
 
 // Commit rows into LDS rows 8 .. 8+nc-1 for the Wk / Wv tiles of the QKV
@@ -971,6 +1069,8 @@ __device__ __forceinline__ void qkv_phase(const PassArgs& a, Smem& s, int l, int
         },
         [&] { qkv_prefetch<FMT>(a, l, W, true); });
   if (cm && l == 0) {
+    if (otid() == 0) fc_wait(a);
+    lds_sync();
     commit_rows_build<FMT>(a, s);
     lds_sync();
     if (w == QKV_KV_FIRST) commit_rows_keep(a, s);
@@ -2000,16 +2100,13 @@ __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs args) {
   BarState bk;      // barriers passed, give-up flag
   QkvTile<FMT> Wq;
   LmTile<LMF> Wl;   // LM head slice, prefetched after the last layer
-  // Commit rows (fused draft-commit cycle) through fc first; then layer 0
-  // QKV weights stream while the grid lines up at the barrier that publishes
-  // the commit rows' fc outputs.  Without commit rows there is nothing to
-  // wait for -- h, ss, the RoPE table and the layer table come from the init
-  // kernel, visible from the start -- and every block skips that barrier.
+  // Commit rows (fused draft-commit cycle) through fc first; then each block
+  // goes straight on to layer 0's QKV phase (h, ss, the RoPE table and the
+  // layer table come from the init kernel, visible from the start): only the
+  // blocks that project the commit rows wait, there, until every fc output
+  // tile is written (fc_wait) -- no grid barrier.
   fc_phase<FMT>(a, s);
-  if (a.nc > 0)
-    grid_sync_pf<true>(a, bk, [&] { qkv_prefetch<FMT>(a, 0, Wq, !act_wave()); });
-  else
-    qkv_prefetch<FMT>(a, 0, Wq, !act_wave());
+  qkv_prefetch<FMT>(a, 0, Wq, !act_wave());
   int np = 1;    // sums of squares of h: one entry per row from the init kernel
   for (int l = 0; l < L; ++l) {
     qkv_phase<FMT>(a, s, l, np, Wq);
@@ -2127,6 +2224,7 @@ __global__ void k_pass_status(const unsigned* bar, int32_t* status, int32_t time
 size_t pass_smem_bytes() { return sizeof(Smem); }
 size_t pass_tab_bytes() { return sizeof(LayerTab); }
 size_t pass_bar_bytes() { return sizeof(unsigned) * BAR_WORDS; }
+size_t pass_fcp_bytes() { return sizeof(float) * NT_H * FC_CONTRIB * 64 * 4; }
 size_t pass_po_bytes() { return sizeof(uint16_t) * L * POSTRIDE; }
 size_t pass_pml_bytes() { return sizeof(float) * L * PMSTRIDE; }
 
@@ -2204,6 +2302,7 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
   a.nc = q.nc;
   a.pos0 = q.pos0;
   a.yc = q.yc;
+  a.fcp = q.fcp;
   a.cn = q.cn;
   a.ckv = q.ckv;
   a.cand = q.cand;
@@ -2222,10 +2321,12 @@ hipError_t launch_draft_pass(const PassLaunch& q, hipStream_t st) {
       q.grid < NKV * a.nqt * 16 || q.grid > 1024)
     return hipErrorInvalidValue;
   if (q.nc < 0 || q.nc > MAXB ||
-      (q.nc > 0 && (!q.taps || !q.fc || !q.yc || !q.cn || !q.ckv || q.grid < NT_H)))
+      (q.nc > 0 && (!q.taps || !q.fc || !q.yc || !q.fcp || !q.cn || !q.ckv || q.grid < NT_H ||
+                    q.grid > FC_GRID_MAX)))
     return hipErrorInvalidValue;
   // device-resident positions: up to MAXB commit rows, at most maxch chunks per head
-  if (q.dstate && (!q.taps_base || !q.fc || !q.yc || !q.cn || !q.ckv || q.grid < NT_H || q.maxch < 1 ||
+  if (q.dstate && (!q.taps_base || !q.fc || !q.yc || !q.fcp || !q.cn || !q.ckv || q.grid < NT_H ||
+                   q.grid > FC_GRID_MAX || q.maxch < 1 ||
                    q.maxch > 128 || q.grid < NKV * q.maxch || q.window < 1 || q.taps_pos0 < 0 ||
                    q.taps_rows < 0))
     return hipErrorInvalidValue;

@@ -300,9 +300,9 @@ DFLASH_API int32_t dflash_draft_block_commit_dev(const dflash_weights* w, const 
 
 /* dflash_draft_block for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
- * hipMalloc): no workspace argument; the pass runs in a 66 MiB device array
+ * hipMalloc): no workspace argument; the pass runs in a 67 MiB device array
  * inside the library (each device the library runs on holds its own copy
- * from the first call until the process ends; the pass needs 65.8 MiB of it
+ * from the first call until the process ends; the pass needs 66.5 MiB of it
  * whatever the context length and block size, and a layout that would not
  * fit returns DFLASH_EWORKSPACE).  The call allocates nothing: on its first
  * call on a device it only looks up the array's device address.  Same
