@@ -346,9 +346,57 @@ def main():
         assert int(st.item()) == 0, "device-resident cycle: a pass reported a failure"
         return dt_, int(a_), K * args.steps
 
+    def run_graph_cycles():
+        """The device-resident cycle with each job of JOB_CYCLES cycles
+        captured once as a HIP graph (the state reset, then every cycle's
+        pass, stand-in target and verify) and replayed per job; between
+        replays the host copies the next job's target draws into the graph's
+        input buffers.  Returns (seconds, cycles) over the timed jobs."""
+        taps_ctx = taps_all[CTX:]
+        jobs = max(1, args.steps // JOB_CYCLES)
+        init = torch.tensor([[CTX, synth.anchor_token(j), 0] for j in range(jobs + 1)],
+                            dtype=torch.int64, device="cuda")
+        s0 = torch.empty(3, dtype=torch.int64, device="cuda")
+        dstate = torch.empty(3, dtype=torch.int64, device="cuda")
+        m_job = torch.empty((JOB_CYCLES, K), dtype=match.dtype, device="cuda")
+        o_job = torch.empty((JOB_CYCLES, K), dtype=torch.int32, device="cuda")
+        t_job = torch.zeros((JOB_CYCLES, K + 1), dtype=torch.int32, device="cuda")
+        o_out = torch.empty((JOB_CYCLES, 2), dtype=torch.int32, device="cuda")
+
+        def load(j):  # job j's draws (cycles j*JOB_CYCLES ..., wrapping over the drawn ones)
+            idx = torch.arange(j * JOB_CYCLES, (j + 1) * JOB_CYCLES, device="cuda") % n_pass
+            m_job.copy_(match[idx])
+            o_job.copy_(offset[idx])
+            t_job[:, K] = tgt_all[idx, K]
+            s0.copy_(init[j])
+
+        load(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            dstate.copy_(s0)
+            for c in range(JOB_CYCLES):
+                dr.draft_commit_dev(taps_ctx, CTX, dstate, BLOCK, cand=cand)
+                torch.where(m_job[c], cand, torch.remainder(cand + o_job[c], V), out=t_job[c, :K])
+                dr.verify_advance(cand, t_job[c], K, dstate, out=o_out[c])
+        g.replay()  # warm-up job
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for j in range(1, jobs + 1):
+            load(j)
+            g.replay()
+        torch.cuda.synchronize()
+        dt_ = time.perf_counter() - t0
+        st = torch.empty(1, dtype=torch.int32, device="cuda")
+        dr.status(st)
+        assert int(st.item()) == 0, "graph-replayed cycle: a pass reported a failure"
+        del g
+        return dt_, jobs * JOB_CYCLES
+
     dt_unfused, _, _ = run_cycles(False)
     dt_host, _, _ = run_cycles(True)
     dt, acc, off = run_device_cycles()
+    dt_graph, n_graph = run_graph_cycles()
     value = args.steps / dt
     state = {"acc": acc, "off": off}
 
@@ -572,6 +620,12 @@ def main():
             "note": "the same fused cycle with the positions as host arguments "
                     "(dflash_draft_block_commit): one device-to-host read of (accepted, "
                     "next) per cycle; 96-token jobs"},
+        "decode_cycle_graph": {"ms_per_cycle": round(1e3 * dt_graph / n_graph, 4),
+                               "cycles_per_s": round(n_graph / dt_graph, 3),
+                               "cycles": n_graph,
+                               "note": f"the device-resident cycle with each job of {JOB_CYCLES} "
+                                       "cycles captured once as a HIP graph and replayed; the "
+                                       "next job's draws are copied in between replays"},
         "decode_cycle_unfused": {"ms_per_cycle": round(1e3 * dt_unfused / args.steps, 4),
                                  "cycles_per_s": round(args.steps / dt_unfused, 3),
                                  "note": "draft, verify, then the commit as separate fuse + "

@@ -179,7 +179,7 @@ struct PassArgs {
   int nc;
   int64_t pos0;
   float* yc;              // [8][H] fc outputs of the commit rows (fp32)
-  float* fcp;             // [160][8][64][4] the FC phase's per-block tile partials
+  float* fcp;             // [160][4][64][4] the FC phase's per-block tile partials
   uint16_t* cn;           // [8][H] their fused context rows in the MFMA input format,
                           // built in layer 0 and staged from here by later layers
   float* ckv;             // [L][8][1024] raw Wk | Wv outputs of the commit rows (fp32)
@@ -237,17 +237,11 @@ __device__ __forceinline__ uint64_t ld_coh64(const void* p) {
 __device__ __forceinline__ void st_coh64(void* p, uint64_t v) {
   __hip_atomic_store(g64(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ld_cohf(const float* p) {
-  return __uint_as_float(__hip_atomic_load(g32(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
 __device__ __forceinline__ void st_cohf(float* p, float v) {
   __hip_atomic_store(g32(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t ld_coh32(const void* p) {
   return __hip_atomic_load(g32(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_coh32(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(g32(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint4 ld_coh128(const void* p) {
   const uint64_t a = ld_coh64(p), b = ld_coh64(static_cast<const char*>(p) + 8);
@@ -257,11 +251,6 @@ __device__ __forceinline__ uint4 ld_coh128(const void* p) {
 __device__ __forceinline__ void st_coh128(void* p, uint4 v) {
   st_coh64(p, static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32));
   st_coh64(static_cast<char*>(p) + 8, static_cast<uint64_t>(v.z) | (static_cast<uint64_t>(v.w) << 32));
-}
-__device__ __forceinline__ float4 ld_coh_f4(const float* p) {
-  const uint4 u = ld_coh128(p);
-  return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
-                     __uint_as_float(u.w));
 }
 __device__ __forceinline__ void st_coh_f4(float* p, f32x4 v) {
   st_coh128(p, make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
@@ -279,12 +268,12 @@ __device__ __forceinline__ void st_coh_f4(float* p, f32x4 v) {
 // (32 pollers per line instead of all 256 on the counter's: measured 9 us
 // less per pass).  No resets: the critical path is two atomics, the release
 // stores and the waiters' next poll, which matters because every memory
-// round trip is slow while the weight stream saturates HBM.
-// Per-XCD release words at [640 + 32 x] (see grid_sync_pf).
+// round trip is slow while the weight stream saturates HBM.  The FC phase
+// (fused draft-commit cycle) adds an arrival counter per fc output tile at
+// [1024 + t] and the count of written tiles at [1184].
 constexpr int BAR_STATUS = 0, BAR_TOP = 64, BAR_XCD = 128, BAR_REL = 640, BAR_FC = 1024,
-              BAR_FCDONE = BAR_FC + 160, BAR_WORDS = 1024 + 256;
-// BAR_FC: arrival counters of the FC phase's 160 tiles; BAR_FCDONE: tiles
-// whose fc outputs are written
+              BAR_FCDONE = BAR_FC + NT_H, BAR_WORDS = 1024 + 256;
+static_assert(BAR_FCDONE < BAR_WORDS, "the FC words fit the barrier words");
 // BAR_STATUS values: a barrier wait gave up, or the device-resident positions
 // were invalid (the pass then did nothing but report it)
 constexpr unsigned ST_TIMEOUT = 1u, ST_INVALID = 2u;
@@ -772,8 +761,8 @@ __device__ __forceinline__ void residual_epilogue(const PassArgs& a, f32x4 acc, 
 // accepted) are fused (fc, then RMSNorm) and projected (each layer's Wk / Wv)
 // inside the pass.  Their K/V projection rides the QKV phase's Wk / Wv tiles
 // as MFMA columns 8..15 (the block rows use columns 0..7), so it streams no
-// extra weight bytes; only fc (65.5 MB bf16) is added, in an FC phase before
-// the first barrier.
+// extra weight bytes; only fc (65.5 MB bf16) is added, in an FC phase at the
+// start of the pass.
 //
 // FC phase: fc's 160 output tiles (16 of the 2560 rows) x 50 k slices of 256
 // (of the 12800 = 5 taps x 2560) are 8000 work items dealt to the grid in
