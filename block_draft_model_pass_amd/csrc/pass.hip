@@ -248,6 +248,13 @@ __device__ __forceinline__ uint4 ld_coh128(const void* p) {
   return make_uint4(static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32),
                     static_cast<uint32_t>(b), static_cast<uint32_t>(b >> 32));
 }
+// One 16-byte store with the same cache policy as the agent-scope stores
+// above (sc1: visible to the other XCDs once acknowledged); not atomic as a
+// whole -- for data read only after a barrier.
+__device__ __forceinline__ void st_coh128w(void* p, uint4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(__builtin_bit_cast(u32x4, v))
+               : "memory");
+}
 __device__ __forceinline__ void st_coh128(void* p, uint4 v) {
   st_coh64(p, static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32));
   st_coh64(static_cast<char*>(p) + 8, static_cast<uint64_t>(v.z) | (static_cast<uint64_t>(v.w) << 32));
@@ -1486,15 +1493,32 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KV
         st_cohf(a.pm + l * PMSTRIDE + base * 16 + n, m);
         st_cohf(a.pl + l * PMSTRIDE + base * 16 + n, lsum);
       }
+    }
+    // The normalised chunk output leaves through LDS: a lane holds 4 dims of
+    // one query row per 16-dim tile, so direct stores would write 32-byte
+    // pieces of 16 rows per instruction; staged as rows (stride D + 8), each
+    // store instruction writes two whole 512-byte rows, 16 bytes per lane.
+    lds_sync();  // every wave is done with the K/V blocks in s.x
+    if (wave < a.nqt) {
+      constexpr int RS = D + 8;
+      uint16_t* st = s.x + wave * 16 * RS;
       const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-      uint16_t* op = a.po + l * POSTRIDE + (base * 16 + n) * D + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) {
-        const uint64_t lo = static_cast<uint64_t>(f32_to_f16_bits(o[dt][0] * inv)) |
-                            (static_cast<uint64_t>(f32_to_f16_bits(o[dt][1] * inv)) << 16);
-        const uint64_t hi = static_cast<uint64_t>(f32_to_f16_bits(o[dt][2] * inv)) |
-                            (static_cast<uint64_t>(f32_to_f16_bits(o[dt][3] * inv)) << 16);
-        st_coh64(op + 16 * dt, lo | (hi << 32));
+        const uint32_t lo = static_cast<uint32_t>(f32_to_f16_bits(o[dt][0] * inv)) |
+                            (static_cast<uint32_t>(f32_to_f16_bits(o[dt][1] * inv)) << 16);
+        const uint32_t hi = static_cast<uint32_t>(f32_to_f16_bits(o[dt][2] * inv)) |
+                            (static_cast<uint32_t>(f32_to_f16_bits(o[dt][3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(st + n * RS + 16 * dt + 4 * g) = make_uint2(lo, hi);
+      }
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const size_t base = (static_cast<size_t>(j) * a.nch + c) * a.nqt + wave;
+      uint16_t* op = a.po + l * POSTRIDE + base * 16 * D;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int row = 2 * k + (lane >> 5), c8 = lane & 31;
+        st_coh128w(op + row * D + 8 * c8, *reinterpret_cast<const uint4*>(st + row * RS + 8 * c8));
       }
     }
   }
