@@ -248,13 +248,6 @@ __device__ __forceinline__ uint4 ld_coh128(const void* p) {
   return make_uint4(static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32),
                     static_cast<uint32_t>(b), static_cast<uint32_t>(b >> 32));
 }
-// One 16-byte store with the same cache policy as the agent-scope stores
-// above (sc1: visible to the other XCDs once acknowledged); not atomic as a
-// whole -- for data read only after a barrier.
-__device__ __forceinline__ void st_coh128w(void* p, uint4 v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(__builtin_bit_cast(u32x4, v))
-               : "memory");
-}
 __device__ __forceinline__ void st_coh128(void* p, uint4 v) {
   st_coh64(p, static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32));
   st_coh64(static_cast<char*>(p) + 8, static_cast<uint64_t>(v.z) | (static_cast<uint64_t>(v.w) << 32));
@@ -565,6 +558,10 @@ __device__ __forceinline__ f32x4 group_sum(Smem& s, int w0, int n, int lane) {
 // register path: there the late slice of ACT_WAVE -- a K/V block share, or
 // two gate/up pairs -- costs more than the earlier activations save.)
 __device__ __forceinline__ bool act_wave() { return wid() == ACT_WAVE; }
+
+// Cache-policy operand of the buffer builtins: sc1, as on the agent-scope
+// stores (write-through, visible to the other XCDs once acknowledged).
+constexpr int CPOL_SC1 = 16;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
@@ -1513,12 +1510,17 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KV
       }
       __builtin_amdgcn_wave_barrier();
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // 16-byte stores with the agent-scope stores' cache policy (sc1:
+      // visible to the other XCDs once acknowledged), through a buffer
+      // resource over this wave's 16 rows
       const size_t base = (static_cast<size_t>(j) * a.nch + c) * a.nqt + wave;
-      uint16_t* op = a.po + l * POSTRIDE + base * 16 * D;
+      const __amdgpu_buffer_rsrc_t ro = buf_rsrc(a.po + l * POSTRIDE + base * 16 * D, 16 * D * 2);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int row = 2 * k + (lane >> 5), c8 = lane & 31;
-        st_coh128w(op + row * D + 8 * c8, *reinterpret_cast<const uint4*>(st + row * RS + 8 * c8));
+        __builtin_amdgcn_raw_buffer_store_b128(
+            *reinterpret_cast<const u32x4*>(st + row * RS + 8 * c8), ro,
+            2 * (row * D + 8 * c8), 0, CPOL_SC1);
       }
     }
   }
