@@ -1485,10 +1485,11 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KV
     }
     if (wave < a.nqt) {
       lsum = group4_sum(lsum);
-      const size_t base = (static_cast<size_t>(j) * a.nch + c) * a.nqt + wave;
       if (g == 0) {
-        st_cohf(a.pm + l * PMSTRIDE + base * 16 + n, m);
-        st_cohf(a.pl + l * PMSTRIDE + base * 16 + n, lsum);
+        // [head][query tile][row][chunk]: a group's chunks side by side for the merge
+        const size_t mi = ((static_cast<size_t>(j) * a.nqt + wave) * 16 + n) * NCH_PASS + c;
+        st_cohf(a.pm + l * PMSTRIDE + mi, m);
+        st_cohf(a.pl + l * PMSTRIDE + mi, lsum);
       }
     }
     // The normalised chunk output leaves through LDS: a lane holds 4 dims of
@@ -1534,7 +1535,9 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KV
 // ... with 16-byte loads; wave 0 turns the chunks' maxima and sums into
 // weights w_c = 2^(m_c - M) l_c (chunk outputs are already normalised by
 // l_c).  The maxima and sums are loaded before the chunk outputs, so the
-// weights wait only for them.  Partials of this layer were written once, so
+// weights wait only for them; they are laid out [head][query tile][row]
+// [chunk], so a group's 128 maxima are 512 contiguous bytes (with the chunk
+// outputs' layout they would sit 384 bytes apart, a cache line each).  Partials of this layer were written once, so
 // plain loads read them.  (Two groups per block on the last 96 blocks, which
 // left the first 160 free to start their O-projection prefetch at once, was
 // 3 us per pass slower.)
@@ -1553,6 +1556,7 @@ __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
     const int nc = a.nch;
     const size_t cstride = static_cast<size_t>(a.nqt) * 16;
     const size_t row0 = (static_cast<size_t>(j) * nc * a.nqt + t) * 16 + n;
+    const size_t mrow = ((static_cast<size_t>(j) * a.nqt + t) * 16 + n) * NCH_PASS;
     const uint16_t* po = a.po + l * POSTRIDE;
     const float* pm = a.pm + l * PMSTRIDE;
     const float* pl = a.pl + l * PMSTRIDE;
@@ -1561,8 +1565,8 @@ __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int c = lane + 64 * q;
-      mraw[q] = gld<float>(pm + row0 + (c < nc ? c : 0) * cstride);
-      lraw[q] = gld<float>(pl + row0 + (c < nc ? c : 0) * cstride);
+      mraw[q] = gld<float>(pm + mrow + (c < nc ? c : 0));
+      lraw[q] = gld<float>(pl + mrow + (c < nc ? c : 0));
     }
     uint4 ov[MRG_U];
 #pragma unroll
