@@ -55,6 +55,12 @@ int pass_grid() {
   return cache[dev];
 }
 constexpr int SMALL_ROWS = 64;        // fuse/project: skinny path up to here
+// Projections of more rows write their cells from the GEMM's epilogue (the
+// same bits as the GEMM's fp32 output through k_kv_post): 0.974 -> 0.863 ms
+// at 32768 rows, 0.098 -> 0.089 ms at 2432; with fewer 256-row tiles than
+// the CUs hold, one tile's epilogue is the critical path and the separate
+// kernel is faster (0.078 vs 0.082 ms at 1536 rows).
+constexpr int KV_FUSED_MIN_ROWS = 2048;
 constexpr int FC_SPLITS = 10;         // k splits of the fc GEMV (K = 12800)
 constexpr int KV_SPLITS = 2;          // k splits of the Wk / Wv GEMV (K = 2560)
 constexpr size_t PART_FLOATS = static_cast<size_t>(FC_SPLITS) * GEMV_ROWS * H;
@@ -440,7 +446,6 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
                              knorms, w->rms_eps, theta, rk, rv, kv->capacity, st));
     }
   } else {
-    float* y = at<float>(ws, Lw.y);
     SegTable wt = seg_kv(w);
     bool wp = w->packed != nullptr;
     if (wp) {  // the layers' packed Wk / Wv (bf16, or quantized blocks decoded below)
@@ -460,8 +465,25 @@ extern "C" int32_t dflash_project_ctx_kv(const dflash_weights* w, const void* ct
       wt = seg1(dq, KV_N);
       wp = true;
     }
-    HIP_TRY(launch_gemm_bf16(x, H, n, wt, wp, H, y, KV_N, KV_N, 1, 0, st));
-    HIP_TRY(launch_kv_post(y, KV_N, 1, 0, n, pos0, knorms, w->rms_eps, theta, rk, rv, kv->capacity, st));
+    if (n > KV_FUSED_MIN_ROWS) {
+      // the cells come straight out of the GEMM's epilogue; the fp32 output
+      // region holds the rows' RoPE table instead
+      float2* rope = at<float2>(ws, Lw.y);
+      HIP_TRY(launch_rope_rows(rope, pos0, n, theta, st));
+      KvEpi ke;
+      ke.ring_k = rk;
+      ke.ring_vt = rv;
+      ke.cap = kv->capacity;
+      ke.pos0 = pos0;
+      ke.rope = rope;
+      for (int l = 0; l < L; ++l) ke.kg[l] = static_cast<const uint16_t*>(knorms[l]);
+      ke.eps = w->rms_eps;
+      HIP_TRY(launch_gemm_kv_bf16(x, H, n, wt, wp, ke, st));
+    } else {  // fewer tiles than CUs: the separate epilogue kernel spreads wider
+      float* y = at<float>(ws, Lw.y);
+      HIP_TRY(launch_gemm_bf16(x, H, n, wt, wp, H, y, KV_N, KV_N, 1, 0, st));
+      HIP_TRY(launch_kv_post(y, KV_N, 1, 0, n, pos0, knorms, w->rms_eps, theta, rk, rv, kv->capacity, st));
+    }
   }
   return DFLASH_OK;
 }

@@ -273,6 +273,28 @@ hipError_t launch_kv_post(const float* y, int ldy, int nsplit, size_t split_stri
 hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w, bool w_packed, int K,
                             float* C, int ldc, int N, int nsplit, size_t c_split, hipStream_t st);
 
+// RoPE table of n consecutive positions pos0 ..: tab[row][i] = (cos, sin) of
+// (pos0 + row) * theta^(-2i/256), i < 128, computed in fp64 and rounded to
+// fp32 (the angles of the context keys).
+hipError_t launch_rope_rows(float2* tab, int64_t pos0, int n, double theta, hipStream_t st);
+
+// Context K/V projection with the cells as the GEMM's epilogue: for the
+// [Wk_0; Wv_0; ...; Wk_4; Wv_4] weights (N = 5120, K = 2560) each 256-column
+// tile is one head of one layer; key tiles get the per-head k-norm and RoPE
+// (rope: launch_rope_rows of pos0), value tiles are transposed into the
+// ring's 32-cell blocks; both in fp16, row m into cell (pos0 + m) % capacity.
+struct KvEpi {
+  uint16_t* ring_k;
+  uint16_t* ring_vt;
+  int cap;
+  int64_t pos0;
+  const float2* rope;
+  const uint16_t* kg[L];   // k-norm gains (bf16)
+  float eps;
+};
+hipError_t launch_gemm_kv_bf16(const uint16_t* A, int lda, int M, const SegTable& w, bool w_packed,
+                               const KvEpi& kv, hipStream_t st);
+
 // Finite check: *status = 0, then `code` if any of x[0..count) (dtype 0 bf16,
 // 1 fp16, 2 fp32; 16-byte aligned) is NaN or infinite.
 hipError_t launch_check_finite(const void* x, int64_t count, int dtype, int32_t* status, int32_t code,

@@ -93,6 +93,141 @@ __device__ __forceinline__ uint4 as_uint4(u32x4 v) { return __builtin_bit_cast(u
 // LDS element offset of chunk c of stage row `row` (A rows 0..255, W rows 256..511).
 __device__ __forceinline__ int lds_off(int row, int c) { return row * BK + ((c ^ kswz(row)) << 3); }
 
+// ---------------------------------------------------------------- K/V epilogue
+//
+// A tile of the K/V projection is 256 positions x one head (256 dims) of one
+// layer: columns n0 .. n0+255 of [Wk_0; Wv_0; ...] are layer n0 / 1024, keys
+// for (n0 % 1024) < 512, head (n0 % 512) / 256.  Once the k loop is done the
+// stage ring is free: each half of the tile (the 128 rows of the waves with
+// wm = h) goes through four stage arrays as fp32 [32 rows][256] each (16-float
+// groups XOR-swizzled by (row / 4) % 4, so the accumulator writes of the four
+// lane groups hit different banks), then
+//  - keys: 32 threads per row, thread p holding the NeoX pairs 4p .. 4p+3
+//    (dims 4p.. and 128 + 4p..): sum of squares, 32-lane reduction, scale
+//    with the k gain, rotation by the row's (cos, sin) from the table, fp16;
+//    the same operations in the same order as the stand-alone K/V epilogue
+//    kernel, with the fused multiply-adds written out in both, so the cells
+//    are the same bits;
+//  - values: thread (dim d, group) reads the 32 cells of an aligned 32-cell
+//    group and writes the group's 64 contiguous bytes of the ring's value
+//    block (cells of groups that straddle a half or the tile one by one).
+// Every row of A is one position, pos0 + row; rows past M are not stored.
+
+// Row `row` (0..127) of the staged half: array row / 32, row row % 32.
+__device__ __forceinline__ float* half_row(uint16_t* s0, uint16_t* s1, uint16_t* s2, uint16_t* s3,
+                                           int row) {
+  const int q = row >> 5;
+  uint16_t* a = q == 0 ? s0 : (q == 1 ? s1 : (q == 2 ? s2 : s3));
+  return reinterpret_cast<float*>(a) + (row & 31) * 256;
+}
+__device__ __forceinline__ int half_col(int row, int col) { return col ^ (((row >> 2) & 3) << 4); }
+
+__device__ __forceinline__ void kv_epilogue(const f32x4 (&acc)[8][4], uint16_t* st0, uint16_t* st1,
+                                            uint16_t* st2, uint16_t* st3, int m0, int n0, int M,
+                                            int wm, int wn, int r, int g, int tid, const KvEpi& kv) {
+  constexpr int LW = 2 * NKV * D;  // 1024 columns per layer
+  const int l = n0 / LW, kind = (n0 % LW) / (NKV * D), j = (n0 % (NKV * D)) / D;
+  const size_t head = static_cast<size_t>(l) * NKV + j;
+  __syncthreads();  // no wave reads the stage ring any more
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = i * 16 + 4 * g + e;
+          float* pr = half_row(st0, st1, st2, st3, row);
+#pragma unroll
+          for (int jn = 0; jn < 4; ++jn) pr[half_col(row, wn * 64 + jn * 16 + r)] = acc[i][jn][e];
+        }
+    }
+    __syncthreads();
+    const int r0 = m0 + h * 128;                       // row of A of the half's row 0
+    const int nvalid = M - r0 < 128 ? M - r0 : 128;    // rows of A in this half
+    if (kind == 0) {
+      const int p = tid & 31, rs = tid >> 5;           // 16 rows per round
+      const uint16_t* gk = kv.kg[l];
+      const uint2 gl = *reinterpret_cast<const uint2*>(gk + 4 * p);
+      const uint2 gh = *reinterpret_cast<const uint2*>(gk + D / 2 + 4 * p);
+      const float ga[4] = {bf16_to_f32(static_cast<uint16_t>(gl.x)), bf16_to_f32(static_cast<uint16_t>(gl.x >> 16)),
+                           bf16_to_f32(static_cast<uint16_t>(gl.y)), bf16_to_f32(static_cast<uint16_t>(gl.y >> 16))};
+      const float gc[4] = {bf16_to_f32(static_cast<uint16_t>(gh.x)), bf16_to_f32(static_cast<uint16_t>(gh.x >> 16)),
+                           bf16_to_f32(static_cast<uint16_t>(gh.y)), bf16_to_f32(static_cast<uint16_t>(gh.y >> 16))};
+#pragma unroll 2
+      for (int it = 0; it < 8; ++it) {
+        const int row = it * 16 + rs;
+        const bool valid = row < nvalid;
+        const int ra = valid ? r0 + row : 0;           // in-bounds table row for unused rows
+        const float4 cs01 = *reinterpret_cast<const float4*>(kv.rope + static_cast<size_t>(ra) * (D / 2) + 4 * p);
+        const float4 cs23 = *reinterpret_cast<const float4*>(kv.rope + static_cast<size_t>(ra) * (D / 2) + 4 * p + 2);
+        const float fc[4] = {cs01.x, cs01.z, cs23.x, cs23.z}, fs[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
+        const float* pr = half_row(st0, st1, st2, st3, row);
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(pr + half_col(row, 4 * p));
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(pr + half_col(row, D / 2 + 4 * p));
+        float ss = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ss += fmaf(hi[k], hi[k], lo[k] * lo[k]);
+        ss += __shfl_xor(ss, 1);
+        ss += __shfl_xor(ss, 2);
+        ss += __shfl_xor(ss, 4);
+        ss += __shfl_xor(ss, 8);
+        ss += __shfl_xor(ss, 16);
+        const float sc = 1.0f / sqrtf(ss / static_cast<float>(D) + kv.eps);
+        uint32_t olo[2], ohi[2];
+#pragma unroll
+        for (int k = 0; k < 4; k += 2) {
+          float a[2], cc[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float x = lo[k + e] * (sc * ga[k + e]), z = hi[k + e] * (sc * gc[k + e]);
+            a[e] = fmaf(x, fc[k + e], -(z * fs[k + e]));
+            cc[e] = fmaf(z, fc[k + e], x * fs[k + e]);
+          }
+          olo[k / 2] = f32_to_f16_bits(a[0]) | (static_cast<uint32_t>(f32_to_f16_bits(a[1])) << 16);
+          ohi[k / 2] = f32_to_f16_bits(cc[0]) | (static_cast<uint32_t>(f32_to_f16_bits(cc[1])) << 16);
+        }
+        if (valid) {
+          const size_t cell = static_cast<size_t>((kv.pos0 + r0 + row) % kv.cap);
+          uint16_t* k = kv.ring_k + (head * kv.cap + cell) * D + 4 * p;
+          *reinterpret_cast<uint2*>(k) = make_uint2(olo[0], olo[1]);
+          *reinterpret_cast<uint2*>(k + D / 2) = make_uint2(ohi[0], ohi[1]);
+        }
+      }
+    } else if (nvalid > 0) {
+      const int d = tid & (D - 1), gsel = tid >> 8;    // 2 groups per round
+      const int64_t P0 = kv.pos0 + r0;                 // position of the half's row 0
+      const int64_t g0 = P0 / BLK_CELLS;
+      const int ngr = static_cast<int>((P0 + nvalid - 1) / BLK_CELLS - g0 + 1);
+      uint16_t* vcol = kv.ring_vt + head * D * kv.cap + static_cast<size_t>(d) * BLK_CELLS;
+      for (int gi = gsel; gi < ngr; gi += 2) {
+        const int64_t gp = (g0 + gi) * BLK_CELLS;      // position of the group's cell 0
+        const int rb = static_cast<int>(gp - P0);      // its row in the half (may be < 0)
+        uint16_t* v = vcol + static_cast<size_t>((gp % kv.cap) / BLK_CELLS) * (D * BLK_CELLS);
+        if (rb >= 0 && rb + BLK_CELLS <= nvalid) {
+          uint32_t o[BLK_CELLS / 2];
+#pragma unroll
+          for (int c = 0; c < BLK_CELLS; c += 2) {
+            const int ra = rb + c, rc = rb + c + 1;
+            const float v0 = half_row(st0, st1, st2, st3, ra)[half_col(ra, d)];
+            const float v1 = half_row(st0, st1, st2, st3, rc)[half_col(rc, d)];
+            o[c / 2] = f32_to_f16_bits(v0) | (static_cast<uint32_t>(f32_to_f16_bits(v1)) << 16);
+          }
+          uint4* v4 = reinterpret_cast<uint4*>(v);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v4[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+        } else {
+          for (int c = 0; c < BLK_CELLS; ++c) {
+            const int row = rb + c;
+            if (row >= 0 && row < nvalid) v[c] = f32_to_f16_bits(half_row(st0, st1, st2, st3, row)[half_col(row, d)]);
+          }
+        }
+      }
+    }
+    __syncthreads();  // the half's stage arrays are free again
+  }
+}
+
 // Split-K: block q of the tiles x S grid computes the k range
 // [s K, (s+1) K) of tile t (t' = s tiles + t) into C + s c_split; W rows are
 // ldw elements apart (S K).
@@ -102,11 +237,12 @@ __device__ __forceinline__ int lds_off(int row, int c) { return row * BK + ((c ^
 // 1 KiB block, written to LDS in lane order, and a W fragment read is that
 // block at lane x 16 bytes -- the same lanes/k slots as the swizzled
 // row-major path.
-template <bool WP>
+// EPI = 0: fp32 C.  EPI = 1: the context K/V cells (kv_epilogue).
+template <bool WP, int EPI>
 __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict__ A, int lda,
                                                      int M, SegTable w, int K, int ldw,
                                                      float* __restrict__ C, int ldc, int nN,
-                                                     int tiles, size_t c_split) {
+                                                     int tiles, size_t c_split, KvEpi kv) {
   // Five separate stage arrays (not one indexed ring): every access names its
   // stage statically, so the compiler can tell a stage being read from the
   // stages still being filled and does not wait for those loads.
@@ -310,17 +446,21 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
   lds_wait_all(wfa, afa);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+  if constexpr (EPI == 0) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = m0 + wm * 128 + i * 16 + 4 * g + e;
-      if (row < M) {
-        float* cr = C + static_cast<size_t>(row) * ldc + n0 + wn * 64 + r;
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + wm * 128 + i * 16 + 4 * g + e;
+        if (row < M) {
+          float* cr = C + static_cast<size_t>(row) * ldc + n0 + wn * 64 + r;
 #pragma unroll
-        for (int jn = 0; jn < 4; ++jn) cr[jn * 16] = acc[i][jn][e];
+          for (int jn = 0; jn < 4; ++jn) cr[jn * 16] = acc[i][jn][e];
+        }
       }
-    }
+  } else {
+    kv_epilogue(acc, st0, st1, st2, st3, m0, n0, M, wm, wn, r, g, tid, kv);
+  }
 }
 
 }  // namespace
@@ -336,12 +476,33 @@ hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w
   const int nN = N / BN, nM = (M + BM - 1) / BM;
   const long long tiles = static_cast<long long>(nN) * nM;
   if (tiles * nsplit > 0x7fffffff) return hipErrorInvalidValue;
+  const KvEpi none{};
   if (w_packed)
-    hipLaunchKernelGGL(k_gemm_bf16_nt<true>, dim3(static_cast<unsigned>(tiles * nsplit)), dim3(NT), 0, st, A,
-                       lda, M, w, Ks, K, C, ldc, nN, static_cast<int>(tiles), c_split);
+    hipLaunchKernelGGL((k_gemm_bf16_nt<true, 0>), dim3(static_cast<unsigned>(tiles * nsplit)), dim3(NT), 0, st, A,
+                       lda, M, w, Ks, K, C, ldc, nN, static_cast<int>(tiles), c_split, none);
   else
-    hipLaunchKernelGGL(k_gemm_bf16_nt<false>, dim3(static_cast<unsigned>(tiles * nsplit)), dim3(NT), 0, st, A,
-                       lda, M, w, Ks, K, C, ldc, nN, static_cast<int>(tiles), c_split);
+    hipLaunchKernelGGL((k_gemm_bf16_nt<false, 0>), dim3(static_cast<unsigned>(tiles * nsplit)), dim3(NT), 0, st, A,
+                       lda, M, w, Ks, K, C, ldc, nN, static_cast<int>(tiles), c_split, none);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_kv_bf16(const uint16_t* A, int lda, int M, const SegTable& w, bool w_packed,
+                               const KvEpi& kv, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  constexpr int N = KV_N, K = H;
+  if (lda % 8 || kv.cap <= 0 || kv.cap % BLK_CELLS || kv.pos0 < 0 || !kv.rope) return hipErrorInvalidValue;
+  for (int i = 0; i < w.nseg; ++i)
+    if (w.row_end[i] % BN) return hipErrorInvalidValue;
+  if (w.nseg < 1 || w.row_end[w.nseg - 1] != N) return hipErrorInvalidValue;
+  const int nN = N / BN, nM = (M + BM - 1) / BM;
+  const long long tiles = static_cast<long long>(nN) * nM;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  if (w_packed)
+    hipLaunchKernelGGL((k_gemm_bf16_nt<true, 1>), dim3(static_cast<unsigned>(tiles)), dim3(NT), 0, st, A, lda,
+                       M, w, K, K, nullptr, 0, nN, static_cast<int>(tiles), size_t{0}, kv);
+  else
+    hipLaunchKernelGGL((k_gemm_bf16_nt<false, 1>), dim3(static_cast<unsigned>(tiles)), dim3(NT), 0, st, A, lda,
+                       M, w, K, K, nullptr, 0, nN, static_cast<int>(tiles), size_t{0}, kv);
   return hipGetLastError();
 }
 

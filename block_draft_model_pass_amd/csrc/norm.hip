@@ -143,7 +143,7 @@ __global__ __launch_bounds__(KV_NT) void k_kv_post(const float* y, int ldy, size
       const int j = j0 + jj;
       float ss = 0.f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) ss += lo[jj][k] * lo[jj][k] + hi[jj][k] * hi[jj][k];
+      for (int k = 0; k < 4; ++k) ss += fmaf(hi[jj][k], hi[jj][k], lo[jj][k] * lo[jj][k]);
       ss += __shfl_xor(ss, 1);
       ss += __shfl_xor(ss, 2);
       ss += __shfl_xor(ss, 4);
@@ -157,8 +157,8 @@ __global__ __launch_bounds__(KV_NT) void k_kv_post(const float* y, int ldy, size
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const float x = lo[jj][k + e] * (sc * ga[k + e]), z = hi[jj][k + e] * (sc * gc[k + e]);
-          a[e] = x * fc[k + e] - z * fs[k + e];
-          cc[e] = z * fc[k + e] + x * fs[k + e];
+          a[e] = fmaf(x, fc[k + e], -(z * fs[k + e]));
+          cc[e] = fmaf(z, fc[k + e], x * fs[k + e]);
         }
         olo[k / 2] = f32_to_f16_bits(a[0]) | (static_cast<uint32_t>(f32_to_f16_bits(a[1])) << 16);
         ohi[k / 2] = f32_to_f16_bits(cc[0]) | (static_cast<uint32_t>(f32_to_f16_bits(cc[1])) << 16);
@@ -213,7 +213,27 @@ __global__ __launch_bounds__(KV_NT) void k_kv_post(const float* y, int ldy, size
   }
 }
 
+// RoPE table of rows pos0 .. pos0 + n - 1: one block per 2 rows, thread t
+// -> (row 2b + t / 128, pair t % 128); inverse frequencies and angles in fp64
+// exactly as k_kv_post computes them.
+__global__ __launch_bounds__(256) void k_rope_rows(float2* tab, int64_t pos0, int n, double theta) {
+  const int t = threadIdx.x, row = 2 * blockIdx.x + (t >> 7), i = t & 127;
+  if (row >= n) return;
+  const double invf = pow(theta, -2.0 * static_cast<double>(i) / static_cast<double>(D));
+  double sn, cs;
+  sincos(static_cast<double>(pos0 + row) * invf, &sn, &cs);
+  tab[static_cast<size_t>(row) * (D / 2) + i] = make_float2(static_cast<float>(cs), static_cast<float>(sn));
+}
+
 }  // namespace
+
+hipError_t launch_rope_rows(float2* tab, int64_t pos0, int n, double theta, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (pos0 < 0 || !tab) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_rope_rows, dim3(static_cast<unsigned>((n + 1) / 2)), dim3(256), 0, st, tab, pos0, n,
+                     theta);
+  return hipGetLastError();
+}
 
 hipError_t launch_rownorm(float* h, const float* part, int S, size_t part_split_stride,
                           int part_row_stride, int rows, const uint16_t* gain, float eps,

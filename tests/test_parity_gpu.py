@@ -202,13 +202,18 @@ def ring_cells(kv: KVRing, positions):
 
 
 @pytest.mark.parametrize("n,pos0,cap", [(1, 0, 256), (40, 1000, 1024), (300, 229376, 32768),
-                                         (200, 1000, 1024), (150, 1001, 1024)])
+                                         (200, 1000, 1024), (150, 1001, 1024),
+                                         (2500, 1001, 2560), (2200, 229379, 32768)])
 def test_project_ctx_kv(dev_w, ow, n, pos0, cap):
     """Skinny path with ring wrap-around (pos0 = 1000, capacity 1024), the
     GEMM path at 256K-range positions, and the GEMM path starting inside a
     32-cell value block and wrapping around the ring, with pos0 a multiple
-    of 4 (values stored 4 cells at a time) and not.  Cells outside the
-    projected range must stay untouched (the ring starts zeroed)."""
+    of 4 (values stored 4 cells at a time) and not.  Above 2048 rows the
+    cells come from the GEMM's own epilogue: there with ring wrap-around,
+    value blocks cut by the tile and half-tile boundaries (pos0 = 1001 and
+    229379, not multiples of 32) and a partial last tile (2200 rows).  Cells
+    outside the projected range must stay untouched (the ring starts
+    zeroed)."""
     say(f"project n={n} pos0={pos0} cap={cap}")
     ctx = synth.make_rows(n, synth.HIDDEN, seed=77)
     kv = KVRing(cap, window=cap)

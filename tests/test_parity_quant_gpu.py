@@ -46,12 +46,13 @@ def test_quant_fuse_context(qset, n):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("n", [40, 300])
+@pytest.mark.parametrize("n", [40, 300, 2200])  # 2200: cells from the GEMM's epilogue
 def test_quant_project_ctx_kv(qset, n):
     fmt, dev, ow = qset
     pos0 = 1000
     ctx = synth.make_rows(n, synth.HIDDEN, seed=79)
-    kv = KVRing(2048, window=2048)
+    cap = 4096 if n > 2048 else 2048
+    kv = KVRing(cap, window=cap)
     dr = Drafter(dev, kv, max_rows=n)
     dr.project(to_device(ctx), pos0)
     torch.cuda.synchronize()
