@@ -154,7 +154,7 @@ __device__ __forceinline__ void kv_epilogue(const f32x4 (&acc)[8][4], uint16_t* 
                            bf16_to_f32(static_cast<uint16_t>(gl.y)), bf16_to_f32(static_cast<uint16_t>(gl.y >> 16))};
       const float gc[4] = {bf16_to_f32(static_cast<uint16_t>(gh.x)), bf16_to_f32(static_cast<uint16_t>(gh.x >> 16)),
                            bf16_to_f32(static_cast<uint16_t>(gh.y)), bf16_to_f32(static_cast<uint16_t>(gh.y >> 16))};
-#pragma unroll 2
+#pragma unroll 4
       for (int it = 0; it < 8; ++it) {
         const int row = it * 16 + rs;
         const bool valid = row < nvalid;

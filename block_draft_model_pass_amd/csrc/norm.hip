@@ -213,16 +213,18 @@ __global__ __launch_bounds__(KV_NT) void k_kv_post(const float* y, int ldy, size
   }
 }
 
-// RoPE table of rows pos0 .. pos0 + n - 1: one block per 2 rows, thread t
-// -> (row 2b + t / 128, pair t % 128); inverse frequencies and angles in fp64
-// exactly as k_kv_post computes them.
-__global__ __launch_bounds__(256) void k_rope_rows(float2* tab, int64_t pos0, int n, double theta) {
-  const int t = threadIdx.x, row = 2 * blockIdx.x + (t >> 7), i = t & 127;
-  if (row >= n) return;
+// RoPE table of rows pos0 .. pos0 + n - 1: block b takes rows rpb b ..
+// rpb b + rpb - 1, thread i the pair i: its inverse frequency once, then the
+// angle of each row; in fp64 exactly as k_kv_post computes them.
+__global__ __launch_bounds__(D / 2) void k_rope_rows(float2* tab, int64_t pos0, int n, int rpb, double theta) {
+  const int i = threadIdx.x, r0 = rpb * blockIdx.x;
   const double invf = pow(theta, -2.0 * static_cast<double>(i) / static_cast<double>(D));
-  double sn, cs;
-  sincos(static_cast<double>(pos0 + row) * invf, &sn, &cs);
-  tab[static_cast<size_t>(row) * (D / 2) + i] = make_float2(static_cast<float>(cs), static_cast<float>(sn));
+  const int r1 = n - r0 < rpb ? n - r0 : rpb;
+  for (int r = 0; r < r1; ++r) {
+    double sn, cs;
+    sincos(static_cast<double>(pos0 + r0 + r) * invf, &sn, &cs);
+    tab[static_cast<size_t>(r0 + r) * (D / 2) + i] = make_float2(static_cast<float>(cs), static_cast<float>(sn));
+  }
 }
 
 }  // namespace
@@ -230,8 +232,11 @@ __global__ __launch_bounds__(256) void k_rope_rows(float2* tab, int64_t pos0, in
 hipError_t launch_rope_rows(float2* tab, int64_t pos0, int n, double theta, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   if (pos0 < 0 || !tab) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_rope_rows, dim3(static_cast<unsigned>((n + 1) / 2)), dim3(256), 0, st, tab, pos0, n,
-                     theta);
+  // rows per block: up to 32 (one pow per thread for many rows), while the
+  // grid keeps at least ~512 blocks for the fp64 sincos
+  const int rpb = n >= 32 * 512 ? 32 : (n >= 2 * 512 ? n / 512 : 1);
+  hipLaunchKernelGGL(k_rope_rows, dim3(static_cast<unsigned>((n + rpb - 1) / rpb)), dim3(D / 2), 0, st, tab,
+                     pos0, n, rpb, theta);
   return hipGetLastError();
 }
 
