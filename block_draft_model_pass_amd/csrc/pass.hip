@@ -1109,11 +1109,13 @@ __device__ __forceinline__ void qkv_phase(const PassArgs& a, Smem& s, int l, int
 // Block w < 2 nch takes KV head j = w / nch and chunk c = w % nch of the
 // visible context (cb blocks of 32 cells); the last chunk of each head also
 // takes the block rows' own keys.  Context K/V never depends on this pass, so
-// each thread loads its share of the chunk's first two 32-cell blocks (16 KiB
-// of K and 16 KiB of V^T each, 4 x 16 bytes per thread per block) *before*
-// the barrier that precedes the phase; blocks then go through LDS in pairs.
-// Waves t < nqt own 16 query rows each.  A chunk leaves its output
-// normalised by its own softmax sum, in fp16, with its maximum and sum.
+// the chunk's first two 32-cell blocks (16 KiB of K and 16 KiB of V^T each)
+// are loaded straight into LDS during the barrier that precedes the phase,
+// with the layer's q / k norm gains and the RoPE rows (attn_stage); later
+// pairs (long contexts) go through registers, each loaded while the
+// previous pair runs.  Waves t < nqt own 16 query rows each.  A chunk leaves
+// its output normalised by its own softmax sum, in fp16, with its maximum
+// and sum.
 
 struct KVRegs {
   uint4 v[4];
@@ -1147,15 +1149,24 @@ __device__ __forceinline__ void attn_load(const PassArgs& a, int l, int ib_globa
   }
 }
 
-// LDS layouts of one 32-cell block, XOR-swizzled so that an MFMA operand
-// read (16 rows at the same offset) touches every bank once:
-//   keys   [32 cells][256]: 16-byte chunk c of cell r sits at chunk c ^ (r & 15)
-//   values [256 dims][32] : 8-byte chunk c of dim d sits at chunk c ^ ((d >> 1) & 7)
-// Offsets are in fp16 elements.
-__device__ __forceinline__ int kswz(int cell, int c16) { return cell * D + ((c16 ^ (cell & 15)) << 3); }
-__device__ __forceinline__ int vswz(int dim, int c8) {
-  return dim * BLK_CELLS + ((c8 ^ ((dim >> 1) & 7)) << 2);
-}
+// LDS layouts of one 32-cell block, XOR-swizzled in 16-byte pieces, so that
+// every MFMA operand read below touches each bank once and a piece can come
+// straight from the ring by a 16-byte load with an LDS destination:
+//   keys   [32 cells][256]: 16-byte piece c of cell r sits at piece c ^ kf(r)
+//   values [256 dims][32] : 16-byte piece q of dim d (cells 8q..8q+7) sits at
+//                           piece q ^ vf(d)
+// Row n of a block's first 16-row score tile is cell kcell(n), of its second
+// kcell(n) + 4: the lanes of group g then hold the scores of cells 8g..8g+7,
+// which is one 16-byte piece of a value row -- the k slots of the P.V MFMA.
+// (kf(kcell(n)) = kf(kcell(n) + 4) = n, so a key read by 16 rows at one piece
+// hits 16 distinct pieces; vf gives 8 consecutive dims distinct (d & 1, vf)
+// and 16 distinct (d & 3, vf).)  Offsets are in fp16 elements.
+__device__ __forceinline__ int kf(int cell) { return (cell & 3) | ((cell >> 1) & 12); }
+__device__ __forceinline__ int vf(int dim) { return (((dim >> 1) ^ (dim >> 3)) & 1) | ((dim >> 1) & 2); }
+__device__ __forceinline__ int kcell(int n) { return 8 * (n >> 2) + (n & 3); }
+__device__ __forceinline__ int kswz(int cell, int c16) { return cell * D + ((c16 ^ kf(cell)) << 3); }
+__device__ __forceinline__ int vswz(int dim, int q) { return dim * BLK_CELLS + ((q ^ vf(dim)) << 3); }
+__device__ __forceinline__ int vel(int dim, int cell) { return vswz(dim, cell >> 3) + (cell & 7); }
 
 __device__ __forceinline__ void attn_store(const KVRegs& R, uint16_t* kbuf, uint16_t* vbuf) {
   const int tid = otid();
@@ -1163,24 +1174,60 @@ __device__ __forceinline__ void attn_store(const KVRegs& R, uint16_t* kbuf, uint
   for (int u = 0; u < 2; ++u) {
     const int e = tid + u * NTHR;
     *reinterpret_cast<uint4*>(kbuf + kswz(e >> 5, e & 31)) = R.v[u];
-    const int dim = e >> 2, c8 = 2 * (e & 3);
-    const uint4 v = R.v[2 + u];
-    *reinterpret_cast<uint2*>(vbuf + vswz(dim, c8)) = make_uint2(v.x, v.y);
-    *reinterpret_cast<uint2*>(vbuf + vswz(dim, c8 + 1)) = make_uint2(v.z, v.w);
+    *reinterpret_cast<uint4*>(vbuf + vswz(e >> 2, e & 3)) = R.v[2 + u];
   }
 }
 
-// Waves other than 0 load their share of the chunk's first block before the
-// barrier; wave 0 (which runs the barrier) loads its share while it waits.
-__device__ __forceinline__ void attn_prefetch(const PassArgs& a, int l, KVRegs& R0, KVRegs& R1,
-                                              bool go) {
-  const int w = blockIdx.x;
-  const bool has = w < NKV * a.nch;
-  const int j = has ? w / a.nch : 0, c = has ? w % a.nch : 0;
+// LDS of the attention phase, in fp16 elements of s.x: the two block
+// buffers of a pair (keys of block b at 2 b x 8192, its values right after),
+// the block rows' buffer (4 x 8192), and the staged per-layer constants: the
+// q-norm and k-norm gains (bf16, 1 KiB slots) and the RoPE rows of the block
+// rows (rows 0..B-1) and commit rows (rows MAXB..) at their table rows.
+constexpr int ATT_QG = 6 * BLK_CELLS * D, ATT_KG = ATT_QG + 512, ATT_ROPE = ATT_QG + 1024;
+static_assert(ATT_ROPE + 2 * MAXB * 2 * D <= MAXB * XS_MAX, "staged constants fit in s.x");  // 1 KiB rows
+// Waves 6 and 7 load, with an LDS destination, at the barrier before the
+// phase (the query waves t < nqt <= 6 load nothing there, so their query
+// loads go out at the release): wave 7 first the per-layer constants, then
+// both waves 32 KiB each of the chunk's first two K/V blocks -- exactly
+// KV_DMA_LOADS loads each (an absent block reads as zeros), so that wave 7
+// can wait for its constants alone.  Load i of a block's keys or values
+// fills LDS bytes [1024 i, 1024 i + 1024) lane by lane, each lane reading
+// the ring piece that belongs at its slot of the swizzled layout.
+constexpr int KV_DMA_W0 = NWAVE - 2, KV_DMA_LOADS = 32;
+static_assert(NQT_MAX <= KV_DMA_W0, "the K/V waves own no query rows");
+static_assert(ACT_WAVE >= KV_DMA_W0, "the staging wave is a K/V wave");
+__device__ __forceinline__ void attn_stage(const PassArgs& a, Smem& s, int l) {
+  const int w = blockIdx.x, wave = wid();
+  if (w >= NKV * a.nch || wave < KV_DMA_W0) return;
+  const int lane = otid() & 63;
+  if (wave == ACT_WAVE) {
+    g2lds(buf_rsrc(ctab(a)->q_norm[l], D * 2), s.x + ATT_QG, 16 * lane);
+    g2lds(buf_rsrc(ctab(a)->k_norm[l], D * 2), s.x + ATT_KG, 16 * lane);
+    const __amdgpu_buffer_rsrc_t rr = buf_rsrc(a.rope, 2 * MAXB * D * 4);
+    for (int r = 0; r < a.B; ++r) g2lds(rr, s.x + ATT_ROPE + r * 2 * D, r * D * 4 + 16 * lane);
+    for (int r = MAXB; r < MAXB + a.nc; ++r) g2lds(rr, s.x + ATT_ROPE + r * 2 * D, r * D * 4 + 16 * lane);
+  }
+  const int j = w / a.nch, c = w % a.nch;
   const int blk0 = c * a.cb;
-  const int nblk = has && a.nb > blk0 ? min(a.cb, a.nb - blk0) : 0;
-  attn_load(a, l, blk0, j, R0, go && nblk > 0);
-  attn_load(a, l, blk0 + 1, j, R1, go && nblk > 1);
+  const int nblk = a.nb > blk0 ? min(a.cb, a.nb - blk0) : 0;
+  const int b = wave - KV_DMA_W0;  // this wave's block of the pair
+  const uint16_t *kp = a.ring_k, *vp = a.ring_vt;
+  const bool has = b < nblk && attn_block_src(a, l, blk0 + b, kp, vp, j);
+  const uint32_t bytes = has ? BLK_CELLS * D * 2 : 0;
+  const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kp, bytes), rv = buf_rsrc(vp, bytes);
+  uint16_t* kb = s.x + 2 * b * BLK_CELLS * D;
+  uint16_t* vb = kb + BLK_CELLS * D;
+  const int kcl = lane >> 5, kpc = lane & 31, vdl = lane >> 2, vq = lane & 3;
+#pragma unroll
+  for (int pc = 0; pc < 16; ++pc) {
+    const int cell = 2 * pc + kcl;
+    g2lds(rk, kb + 512 * pc, static_cast<uint32_t>(cell * D * 2 + 16 * (kpc ^ kf(cell))));
+  }
+#pragma unroll
+  for (int pc = 0; pc < 16; ++pc) {
+    const int dim = 16 * pc + vdl;
+    g2lds(rv, vb + 512 * pc, static_cast<uint32_t>(dim * BLK_CELLS * 2 + 16 * (vq ^ vf(dim))));
+  }
 }
 
 // One 32-cell block from LDS (keys [32][256], values [256][32]) for this
@@ -1192,15 +1239,15 @@ __device__ __forceinline__ void attn_block(const uint16_t* kb, const uint16_t* v
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int si = 0; si < 8; ++si) {
-    s0 = mfma_f16(*reinterpret_cast<const uint4*>(kb + kswz(n, g + 4 * si)), qf[si], s0);
-    s1 = mfma_f16(*reinterpret_cast<const uint4*>(kb + kswz(16 + n, g + 4 * si)), qf[si], s1);
+    s0 = mfma_f16(*reinterpret_cast<const uint4*>(kb + kswz(kcell(n), g + 4 * si)), qf[si], s0);
+    s1 = mfma_f16(*reinterpret_cast<const uint4*>(kb + kswz(kcell(n) + 4, g + 4 * si)), qf[si], s1);
   }
   const bool full = pb >= lo && pb + 32 <= hi;
   float x[8];
   bool ok[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t q0 = pb + 4 * g + i, q1 = q0 + 16;
+    const int64_t q0 = pb + 8 * g + i, q1 = q0 + 4;  // cells of s0[i], s1[i]
     ok[i] = full || (q0 >= lo && q0 < hi);
     ok[4 + i] = full || (q1 >= lo && q1 < hi);
     x[i] = ok[i] ? s0[i] * scale_log2 : NEG_INF;
@@ -1232,9 +1279,8 @@ __device__ __forceinline__ void attn_block(const uint16_t* kb, const uint16_t* v
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt) {
     o[dt] *= alpha;
-    const uint2 x0 = *reinterpret_cast<const uint2*>(vb + vswz(16 * dt + n, g));
-    const uint2 x1 = *reinterpret_cast<const uint2*>(vb + vswz(16 * dt + n, g + 4));
-    const uint4 v = make_uint4(x0.x & vm[0], x0.y & vm[1], x1.x & vm[2], x1.y & vm[3]);
+    const uint4 x = *reinterpret_cast<const uint4*>(vb + vswz(16 * dt + n, g));
+    const uint4 v = make_uint4(x.x & vm[0], x.y & vm[1], x.z & vm[2], x.w & vm[3]);
     o[dt] = mfma_f16(v, pf, o[dt]);
   }
 }
@@ -1252,10 +1298,11 @@ __device__ __forceinline__ void attn_pair_full(const uint16_t* kb0, const uint16
 #pragma unroll
   for (int si = 0; si < 8; ++si) {
     const int c = g + 4 * si;
-    sc[0] = mfma_f16(*reinterpret_cast<const uint4*>(kb0 + kswz(n, c)), qf[si], sc[0]);
-    sc[1] = mfma_f16(*reinterpret_cast<const uint4*>(kb0 + kswz(16 + n, c)), qf[si], sc[1]);
-    sc[2] = mfma_f16(*reinterpret_cast<const uint4*>(kb1 + kswz(n, c)), qf[si], sc[2]);
-    sc[3] = mfma_f16(*reinterpret_cast<const uint4*>(kb1 + kswz(16 + n, c)), qf[si], sc[3]);
+    const int c0 = kcell(n), c1 = c0 + 4;
+    sc[0] = mfma_f16(*reinterpret_cast<const uint4*>(kb0 + kswz(c0, c)), qf[si], sc[0]);
+    sc[1] = mfma_f16(*reinterpret_cast<const uint4*>(kb0 + kswz(c1, c)), qf[si], sc[1]);
+    sc[2] = mfma_f16(*reinterpret_cast<const uint4*>(kb1 + kswz(c0, c)), qf[si], sc[2]);
+    sc[3] = mfma_f16(*reinterpret_cast<const uint4*>(kb1 + kswz(c1, c)), qf[si], sc[3]);
   }
   float x[16];
 #pragma unroll
@@ -1287,28 +1334,33 @@ __device__ __forceinline__ void attn_pair_full(const uint16_t* kb0, const uint16
   for (int dt = 0; dt < 16; ++dt) {
     o[dt] *= alpha;
     const int d = 16 * dt + n;
-    const uint2 a0 = *reinterpret_cast<const uint2*>(vb0 + vswz(d, g));
-    const uint2 a1 = *reinterpret_cast<const uint2*>(vb0 + vswz(d, g + 4));
-    o[dt] = mfma_f16(make_uint4(a0.x, a0.y, a1.x, a1.y), pf0, o[dt]);
-    const uint2 b0 = *reinterpret_cast<const uint2*>(vb1 + vswz(d, g));
-    const uint2 b1 = *reinterpret_cast<const uint2*>(vb1 + vswz(d, g + 4));
-    o[dt] = mfma_f16(make_uint4(b0.x, b0.y, b1.x, b1.y), pf1, o[dt]);
+    o[dt] = mfma_f16(*reinterpret_cast<const uint4*>(vb0 + vswz(d, g)), pf0, o[dt]);
+    o[dt] = mfma_f16(*reinterpret_cast<const uint4*>(vb1 + vswz(d, g)), pf1, o[dt]);
   }
 }
 
 // Query operand of this wave: qrow r = 16 t + n -> (row r / 12, head 12 j +
 // r % 12); RMSNorm over the head (the lane holds 64 of its 256 values), then
 // NeoX RoPE: dims 32 s + 8 g + e and 32 (s + 4) + 8 g + e form a pair.
-__device__ __forceinline__ void attn_query(const PassArgs& a, int l, int j, int t, int n, int g,
-                                           uint4 (&qf)[8]) {
+__device__ __forceinline__ void attn_query_load(const PassArgs& a, int l, int j, int t, int n, int g,
+                                                uint4 (&u)[8]) {
   const int r = t * 16 + n;
   const bool qv = r < G * a.B;
   const int bi = qv ? r / G : 0, hl = qv ? r % G : 0;
   const uint16_t* qraw = a.qkv + l * QSTRIDE + static_cast<size_t>(bi) * QKV_N + (j * G + hl) * D;
+#pragma unroll
+  for (int si = 0; si < 8; ++si) u[si] = gld<uint4>(qraw + 32 * si + 8 * g);
+}
+
+__device__ __forceinline__ void attn_query(const PassArgs& a, const Smem& s, int t, int n, int g,
+                                           const uint4 (&u8)[8], uint4 (&qf)[8]) {
+  const int r = t * 16 + n;
+  const bool qv = r < G * a.B;
+  const int bi = qv ? r / G : 0;
   float qv8[8][8];
 #pragma unroll
   for (int si = 0; si < 8; ++si) {
-    const uint4 u = gld<uint4>(qraw + 32 * si + 8 * g);
+    const uint4 u = u8[si];
     const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1323,12 +1375,13 @@ __device__ __forceinline__ void attn_query(const PassArgs& a, int l, int j, int 
     for (int e = 0; e < 8; ++e) sq += qv8[si][e] * qv8[si][e];
   sq = group4_sum(sq);
   const float sc = 1.0f / sqrtf(sq / static_cast<float>(D) + a.eps);
-  const uint16_t* gq = ctab(a)->q_norm[l];
+  const uint16_t* gq = s.x + ATT_QG;
+  const float2* rope = reinterpret_cast<const float2*>(s.x + ATT_ROPE);
   uint32_t pk[8][4];
 #pragma unroll
   for (int si = 0; si < 4; ++si) {
-    const uint4 ga = gld<uint4>(gq + 32 * si + 8 * g);
-    const uint4 gb = gld<uint4>(gq + 32 * (si + 4) + 8 * g);
+    const uint4 ga = *reinterpret_cast<const uint4*>(gq + 32 * si + 8 * g);
+    const uint4 gb = *reinterpret_cast<const uint4*>(gq + 32 * (si + 4) + 8 * g);
     const uint32_t gav[4] = {ga.x, ga.y, ga.z, ga.w}, gbv[4] = {gb.x, gb.y, gb.z, gb.w};
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
@@ -1339,7 +1392,7 @@ __device__ __forceinline__ void attn_query(const PassArgs& a, int l, int j, int 
         const float ga_f = bf16_to_f32((gav[ee >> 1] >> (16 * (ee & 1))) & 0xffff);
         const float gb_f = bf16_to_f32((gbv[ee >> 1] >> (16 * (ee & 1))) & 0xffff);
         const float x0 = qv8[si][ee] * sc * ga_f, x1 = qv8[si + 4][ee] * sc * gb_f;
-        const float2 cs = gld<float2>(a.rope + bi * (D / 2) + 32 * si + 8 * g + ee);
+        const float2 cs = rope[bi * (D / 2) + 32 * si + 8 * g + ee];
         lo2[h2] = x0 * cs.x - x1 * cs.y;
         hi2[h2] = x1 * cs.x + x0 * cs.y;
       }
@@ -1370,13 +1423,14 @@ __device__ __forceinline__ int nrows(const PassArgs& a) {
   return a.B + a.nc - commit_first_visible(a);
 }
 
-__device__ __forceinline__ void attn_block_rows(const PassArgs& a, int l, int j, uint16_t* kl,
-                                                uint16_t* vl) {
+__device__ __forceinline__ void attn_block_rows(const PassArgs& a, const Smem& s, int l, int j,
+                                                uint16_t* kl, uint16_t* vl) {
   const int wave = wid(), lane = otid() & 63;
-  const uint16_t* gn = ctab(a)->k_norm[l];
+  const uint16_t* gn = s.x + ATT_KG;
+  const float2* rope = reinterpret_cast<const float2*>(s.x + ATT_ROPE);
   float gk[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) gk[q] = bf16_to_f32(gld<uint16_t>(gn + lane + 64 * q));
+  for (int q = 0; q < 4; ++q) gk[q] = bf16_to_f32(gn[lane + 64 * q]);
   if (wave < a.B) {
     const int b = wave;
     const uint16_t* kr = a.qkv + l * QSTRIDE + static_cast<size_t>(b) * QKV_N + NQ * D + j * D;
@@ -1392,15 +1446,15 @@ __device__ __forceinline__ void attn_block_rows(const PassArgs& a, int l, int j,
     k1 *= sc * gk[1];
     k2 *= sc * gk[2];
     k3 *= sc * gk[3];
-    const float2 c0 = gld<float2>(a.rope + b * (D / 2) + lane);
-    const float2 c1 = gld<float2>(a.rope + b * (D / 2) + lane + 64);
+    const float2 c0 = rope[b * (D / 2) + lane];
+    const float2 c1 = rope[b * (D / 2) + lane + 64];
     const float kv[4] = {k0 * c0.x - k2 * c0.y, k1 * c1.x - k3 * c1.y, k2 * c0.x + k0 * c0.y,
                          k3 * c1.x + k1 * c1.y};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int d = lane + 64 * q;
       kl[kswz(b, d >> 3) + (d & 7)] = f32_to_f16_bits(kv[q]);
-      vl[vswz(d, b >> 2) + (b & 3)] = f32_to_f16_bits(vv[q]);
+      vl[vel(d, b)] = f32_to_f16_bits(vv[q]);
     }
   }
   if (wave < a.nc) {
@@ -1417,8 +1471,8 @@ __device__ __forceinline__ void attn_block_rows(const PassArgs& a, int l, int j,
     const float sc = 1.0f / sqrtf(sq / static_cast<float>(D) + a.eps);
 #pragma unroll
     for (int q = 0; q < 4; ++q) k[q] *= sc * gk[q];
-    const float2 c0 = gld<float2>(a.rope + (MAXB + t) * (D / 2) + lane);
-    const float2 c1 = gld<float2>(a.rope + (MAXB + t) * (D / 2) + lane + 64);
+    const float2 c0 = rope[(MAXB + t) * (D / 2) + lane];
+    const float2 c1 = rope[(MAXB + t) * (D / 2) + lane + 64];
     const float kv[4] = {k[0] * c0.x - k[2] * c0.y, k[1] * c1.x - k[3] * c1.y,
                          k[2] * c0.x + k[0] * c0.y, k[3] * c1.x + k[1] * c1.y};
     const int cell = static_cast<int>((a.pos0 + t) % a.cap);
@@ -1435,14 +1489,13 @@ __device__ __forceinline__ void attn_block_rows(const PassArgs& a, int l, int j,
       gst16(rv + static_cast<size_t>(d) * BLK_CELLS, vb);
       if (t >= t0) {
         kl[kswz(c, d >> 3) + (d & 7)] = kb;
-        vl[vswz(d, c >> 2) + (c & 3)] = vb;
+        vl[vel(d, c)] = vb;
       }
     }
   }
 }
 
-__device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KVRegs& R0,
-                                           KVRegs& R1) {
+__device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l) {
   const int w = blockIdx.x;
   if (w < NKV * a.nch) {
     const int j = w / a.nch, c = w % a.nch;
@@ -1455,24 +1508,38 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l, KV
     uint16_t* kl = s.x + 4 * BLK_CELLS * D;
     uint16_t* vl = s.x + 5 * BLK_CELLS * D;
     uint4 qf[8];
-    if (wave < a.nqt) attn_query(a, l, j, wave, n, g, qf);
-    if (rows) attn_block_rows(a, l, j, kl, vl);
+    {
+      uint4 u[8];
+      if (wave < a.nqt) attn_query_load(a, l, j, wave, n, g, u);
+      // the staged gains and RoPE rows -- wave 7's loads before its
+      // KV_DMA_LOADS K/V loads -- are in LDS
+      if (wave == ACT_WAVE) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KV_DMA_LOADS) : "memory");
+      lds_sync();
+      if (wave < a.nqt) attn_query(a, s, wave, n, g, u, qf);
+    }
+    // the first pair's K/V has landed once the K/V waves' loads are done
+    if (wave >= KV_DMA_W0) wait_stores();
+    if (rows) attn_block_rows(a, s, l, j, kl, vl);
     float m = NEG_INF, lsum = 0.f;
     f32x4 o[16];
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // Blocks go through LDS in pairs (buffers at 0 and 2 x 8192): both are
-    // stored, then run together -- in one softmax update when both lie
-    // entirely inside the visible range.
+    // Blocks go through LDS in pairs (buffers at 0 and 2 x 8192; the first
+    // pair is already there, later ones are stored from registers), run
+    // together -- in one softmax update when both lie entirely inside the
+    // visible range.
+    KVRegs R0, R1;
     uint16_t* k0b = s.x;
     uint16_t* v0b = k0b + BLK_CELLS * D;
     uint16_t* k1b = s.x + 2 * BLK_CELLS * D;
     uint16_t* v1b = k1b + BLK_CELLS * D;
     for (int ib = 0; ib < nblk; ib += 2) {
       const bool two = ib + 1 < nblk;
-      if (ib > 0) lds_sync();  // every wave is done with the previous pair
-      attn_store(R0, k0b, v0b);
-      if (two) attn_store(R1, k1b, v1b);
+      if (ib > 0) {
+        lds_sync();  // every wave is done with the previous pair
+        attn_store(R0, k0b, v0b);
+        if (two) attn_store(R1, k1b, v1b);
+      }
       lds_sync();
       if (wave < a.nqt) {
         const int64_t pb0 = a.p0 + 32 * static_cast<int64_t>(blk0 + ib), pb1 = pb0 + 32;
@@ -2140,9 +2207,8 @@ __global__ __launch_bounds__(NTHR) void k_draft_pass(PassArgs args) {
   int np = 1;    // sums of squares of h: one entry per row from the init kernel
   for (int l = 0; l < L; ++l) {
     qkv_phase<FMT>(a, s, l, np, Wq);
-    KVRegs R0, R1;
-    grid_sync_pf(a, bk, [&] { attn_prefetch(a, l, R0, R1, true); });
-    attn_phase(a, s, l, R0, R1);
+    grid_sync_pf(a, bk, [&] { attn_stage(a, s, l); });
+    attn_phase(a, s, l);
     grid_sync(a, bk);
     merge_phase<FMT>(a, s, l);
     OTile<FMT> Wo;
