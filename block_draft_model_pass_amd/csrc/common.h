@@ -26,6 +26,7 @@ constexpr int BLK_CELLS = 32;    // cells of the block-key buffer
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- numbers
@@ -77,6 +78,13 @@ __device__ __forceinline__ f32x4 mfma_bf16(const uint4& a, const uint4& b, f32x4
 __device__ __forceinline__ f32x4 mfma_f16(const uint4& a, const uint4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// D[16][16] += A[16][16] * B[16][16]: the same lane layout with 4 k values
+// per lane (k slots 4*(l/16) .. +3).
+__device__ __forceinline__ f32x4 mfma_f16_k16(const uint2& a, const uint2& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c,
+                                               0, 0, 0);
 }
 
 // ---------------------------------------------------------------- reductions

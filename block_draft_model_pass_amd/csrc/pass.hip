@@ -1339,6 +1339,51 @@ __device__ __forceinline__ void attn_pair_full(const uint16_t* kb0, const uint16
   }
 }
 
+// The rows buffer: its nrows() <= 16 rows sit at cells kcell(r), so the
+// first 16-row score tile alone covers them (the lanes of group g hold rows
+// 4g .. 4g+3, cells 8g .. 8g+3: the first half of a value piece) and P.V
+// takes 16-deep MFMAs; rows at or past nr are masked.
+static_assert(2 * MAXB <= 16, "block and commit rows fit one score tile");
+__device__ __forceinline__ void attn_rows16(const uint16_t* kb, const uint16_t* vb, int nr, float scale_log2,
+                                            const uint4 (&qf)[8], f32x4 (&o)[16], float& m, float& lsum,
+                                            int n, int g) {
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int si = 0; si < 8; ++si)
+    s0 = mfma_f16(*reinterpret_cast<const uint4*>(kb + kswz(kcell(n), g + 4 * si)), qf[si], s0);
+  float x[4];
+  bool ok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ok[i] = 4 * g + i < nr;
+    x[i] = ok[i] ? s0[i] * scale_log2 : NEG_INF;
+  }
+  float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  bm = group4_max(bm);
+  const float mnew = fmaxf(m, bm);
+  const float muse = mnew == NEG_INF ? 0.f : mnew;
+  const float alpha = __builtin_amdgcn_exp2f(m - muse);
+  float pr[4], ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pr[i] = __builtin_amdgcn_exp2f(x[i] - muse);
+    ps += pr[i];
+  }
+  lsum = lsum * alpha + ps;
+  m = mnew;
+  const uint2 pf = make_uint2(
+      static_cast<uint32_t>(f32_to_f16_bits(pr[0])) | (static_cast<uint32_t>(f32_to_f16_bits(pr[1])) << 16),
+      static_cast<uint32_t>(f32_to_f16_bits(pr[2])) | (static_cast<uint32_t>(f32_to_f16_bits(pr[3])) << 16));
+  const uint32_t vm0 = (ok[0] ? 0x0000ffffu : 0u) | (ok[1] ? 0xffff0000u : 0u);
+  const uint32_t vm1 = (ok[2] ? 0x0000ffffu : 0u) | (ok[3] ? 0xffff0000u : 0u);
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) {
+    o[dt] *= alpha;
+    const uint2 v = *reinterpret_cast<const uint2*>(vb + vswz(16 * dt + n, g));
+    o[dt] = mfma_f16_k16(make_uint2(v.x & vm0, v.y & vm1), pf, o[dt]);
+  }
+}
+
 // Query operand of this wave: qrow r = 16 t + n -> (row r / 12, head 12 j +
 // r % 12); RMSNorm over the head (the lane holds 64 of its 256 values), then
 // NeoX RoPE: dims 32 s + 8 g + e and 32 (s + 4) + 8 g + e form a pair.
@@ -1407,14 +1452,15 @@ __device__ __forceinline__ void attn_query(const PassArgs& a, const Smem& s, int
     qf[si] = qv ? make_uint4(pk[si][0], pk[si][1], pk[si][2], pk[si][3]) : make_uint4(0, 0, 0, 0);
 }
 
-// Block rows' keys and values of KV head j into LDS (keys [32][256] with rows
-// b < B, values [256][32]); wave b = row b.  With commit rows (the fused
-// draft-commit cycle), wave t also finishes commit row t: k-norm and RoPE at
-// pos0 + t on its raw fp32 projection, fp16 K and V written to the ring cell
-// of that position (read by later passes), and -- when the position is inside
-// the window -- the same fp16 key and value as cell B + t - t0 of the LDS
-// block (t0 = the first visible commit row), so the rows block holds
-// nrows() keys.
+// Block rows' keys and values of KV head j into LDS (the block layouts: keys
+// [32][256], values [256][32]; row r of the rows buffer at cell kcell(r),
+// where the first score tile reads it); wave b = row b.  With commit rows
+// (the fused draft-commit cycle), wave t also finishes commit row t: k-norm
+// and RoPE at pos0 + t on its raw fp32 projection, fp16 K and V written to
+// the ring cell of that position (read by later passes), and -- when the
+// position is inside the window -- the same fp16 key and value as row
+// B + t - t0 of the rows buffer (t0 = the first visible commit row), so it
+// holds nrows() rows.
 __device__ __forceinline__ int commit_first_visible(const PassArgs& a) {
   const int64_t d = a.lo - a.pos0;
   return d <= 0 ? 0 : (d >= a.nc ? a.nc : static_cast<int>(d));
@@ -1450,11 +1496,12 @@ __device__ __forceinline__ void attn_block_rows(const PassArgs& a, const Smem& s
     const float2 c1 = rope[b * (D / 2) + lane + 64];
     const float kv[4] = {k0 * c0.x - k2 * c0.y, k1 * c1.x - k3 * c1.y, k2 * c0.x + k0 * c0.y,
                          k3 * c1.x + k1 * c1.y};
+    const int cell = kcell(b);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int d = lane + 64 * q;
-      kl[kswz(b, d >> 3) + (d & 7)] = f32_to_f16_bits(kv[q]);
-      vl[vel(d, b)] = f32_to_f16_bits(vv[q]);
+      kl[kswz(cell, d >> 3) + (d & 7)] = f32_to_f16_bits(kv[q]);
+      vl[vel(d, cell)] = f32_to_f16_bits(vv[q]);
     }
   }
   if (wave < a.nc) {
@@ -1480,7 +1527,7 @@ __device__ __forceinline__ void attn_block_rows(const PassArgs& a, const Smem& s
     uint16_t* rv = const_cast<uint16_t*>(a.ring_vt) + (static_cast<size_t>(l) * NKV + j) * D * a.cap +
                    static_cast<size_t>(cell / BLK_CELLS) * D * BLK_CELLS + cell % BLK_CELLS;
     const int t0 = commit_first_visible(a);
-    const int c = a.B + t - t0;  // LDS cell of a visible commit row
+    const int c = kcell(a.B + t - t0);  // LDS cell of a visible commit row
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int d = lane + 64 * q;
@@ -1559,7 +1606,7 @@ __device__ __forceinline__ void attn_phase(const PassArgs& a, Smem& s, int l) {
     }
     if (rows) {
       lds_sync();
-      if (wave < a.nqt) attn_block(kl, vl, 0, 0, nrows(a), a.scale_log2, qf, o, m, lsum, n, g);
+      if (wave < a.nqt) attn_rows16(kl, vl, nrows(a), a.scale_log2, qf, o, m, lsum, n, g);
     }
     if (wave < a.nqt) {
       lsum = group4_sum(lsum);
