@@ -89,23 +89,66 @@ __device__ __forceinline__ f32x4 mfma_f16_k16(const uint2& a, const uint2& b, f3
 
 // ---------------------------------------------------------------- reductions
 
+// Cross-lane reductions without LDS traffic (a lane shuffle is an LDS
+// instruction, ~100 cycles per step).  v_permlane32_swap and
+// v_permlane16_swap exchange the wave's halves / the rows of each row pair:
+// their two results combined give op(v(l), v(l ^ 32)) and op(v(l), v(l ^ 16))
+// in every lane.  DPP row rotations by 8, 4, 2 and 1 take the lane bits
+// below 16: once the higher bits are reduced, lane (l +- 2^k) mod 16 holds
+// the same bits as lane l ^ 2^k.  Every step therefore combines the same two
+// values, in the same order of steps, as an xor-shuffle reduction over
+// 32, 16, 8, 4, 2, 1 -- the results are bit-identical to it.  All 64 lanes
+// must be active.
+__device__ __forceinline__ uint2 swap32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return make_uint2(r[0], r[1]);
+}
+__device__ __forceinline__ uint2 swap16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return make_uint2(r[0], r[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_rot(float v) {  // CTRL: row_ror by 1, 2, 4, 8 = 0x121, 0x122, 0x124, 0x128
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  uint2 p = swap32(v);
+  v = __uint_as_float(p.x) + __uint_as_float(p.y);
+  p = swap16(v);
+  v = __uint_as_float(p.x) + __uint_as_float(p.y);
+  v += dpp_rot<0x128>(v);
+  v += dpp_rot<0x124>(v);
+  v += dpp_rot<0x122>(v);
+  v += dpp_rot<0x121>(v);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  uint2 p = swap32(v);
+  v = fmaxf(__uint_as_float(p.x), __uint_as_float(p.y));
+  p = swap16(v);
+  v = fmaxf(__uint_as_float(p.x), __uint_as_float(p.y));
+  v = fmaxf(v, dpp_rot<0x128>(v));
+  v = fmaxf(v, dpp_rot<0x124>(v));
+  v = fmaxf(v, dpp_rot<0x122>(v));
+  v = fmaxf(v, dpp_rot<0x121>(v));
   return v;
 }
 
 // Sum over the 4 lanes l, l^16, l^32, l^48 (the four k-groups of an MFMA column).
 __device__ __forceinline__ float group4_sum(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  uint2 p = swap16(v);
+  v = __uint_as_float(p.x) + __uint_as_float(p.y);
+  p = swap32(v);
+  return __uint_as_float(p.x) + __uint_as_float(p.y);
 }
 
 __device__ __forceinline__ float group4_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+  uint2 p = swap16(v);
+  v = fmaxf(__uint_as_float(p.x), __uint_as_float(p.y));
+  p = swap32(v);
+  return fmaxf(__uint_as_float(p.x), __uint_as_float(p.y));
 }
 
 // Block-wide sum for blockDim.x == NT (multiple of 64); all threads get it.

@@ -1709,8 +1709,7 @@ __device__ __forceinline__ void merge_phase(const PassArgs& a, Smem& s, int l) {
         lv[q] = act && c < nc ? lraw[q] : 0.f;
         M = fmaxf(M, mv[q]);
       }
-#pragma unroll
-      for (int o2 = 32; o2 > 0; o2 >>= 1) M = fmaxf(M, __shfl_xor(M, o2, 64));
+      M = wave_max(M);
       float Ls = 0.f;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
