@@ -203,7 +203,7 @@ struct PassArgs {
 };
 
 struct Smem {
-  uint16_t x[MAXB * XS_MAX];   // activations (GEMV phases) / block keys+values (ATTN)
+  uint16_t x[MAXB * XS_MAX];   // activations (GEMV phases) / K/V blocks, rows buffer, staged constants (ATTN)
   uint16_t gain[H];            // RMSNorm gain of the phase (staged)
   float ssb[NT_H * MAXB];      // per-tile sums of squares of the phase's h version (staged)
   f32x4 red[NWAVE][64];        // cross-wave reduction
@@ -293,9 +293,11 @@ struct BarState {
   bool quit = false;
 };
 
-// Grid barrier during which every wave issues its share of the next phase's
-// weight loads (`prefetch`), after thread 0's arrival atomics (and, for the
-// last arrival, the release): an s_barrier holds waves 1..7 until then.  The
+// Grid barrier during which the waves issue the next phase's first loads
+// (`prefetch`: each wave's weight slice; before the attention phase, the
+// K/V and constants loads of waves 6 and 7 into LDS), after thread 0's
+// arrival atomics (and, for the last arrival, the release): an s_barrier
+// holds waves 1..7 until then.  The
 // arrival atomics thus never queue behind the prefetch -- a wave's loads
 // complete in order, and a CU whose load queue is full stalls further issue
 // -- while the loads still stream during the wait.  (Issuing the prefetch of
@@ -1112,8 +1114,9 @@ __device__ __forceinline__ void qkv_phase(const PassArgs& a, Smem& s, int l, int
 // the chunk's first two 32-cell blocks (16 KiB of K and 16 KiB of V^T each)
 // are loaded straight into LDS during the barrier that precedes the phase,
 // with the layer's q / k norm gains and the RoPE rows (attn_stage); later
-// pairs (long contexts) go through registers, each loaded while the
-// previous pair runs.  Waves t < nqt own 16 query rows each.  A chunk leaves
+// pairs (long contexts) go through registers, each loaded once the previous
+// pair has run (its registers are free then).  Waves t < nqt own 16 query
+// rows each.  A chunk leaves
 // its output normalised by its own softmax sum, in fp16, with its maximum
 // and sum.
 
