@@ -3,6 +3,7 @@
 // positions and sizes travel as kernel arguments (no host staging buffers).
 #include "../../include/dflash.h"
 #include "common.h"
+#include "fuse.h"
 
 #include <stdlib.h>
 #include <string.h>
@@ -388,11 +389,20 @@ extern "C" int32_t dflash_fuse_context(const dflash_weights* w, const void* taps
     // the k range in two (the fp32 region holds two partial outputs, which
     // the row norm sums).
     const int tiles = (n + 255) / 256 * (H / 256);
-    const int S = tiles < 256 ? 2 : 1;
-    const size_t cs = static_cast<size_t>(n) * H;
-    HIP_TRY(launch_gemm_bf16(x, T * H, n, wt, wp, T * H, y, H, H, S, cs, st));
-    HIP_TRY(launch_rownorm(nullptr, y, S, cs, H, n, u16p(w->hidden_norm), w->rms_eps, out, H,
-                           nullptr, st));
+    if (tiles < 256) {
+      const size_t cs = static_cast<size_t>(n) * H;
+      HIP_TRY(launch_gemm_bf16(x, T * H, n, wt, wp, T * H, y, H, H, 2, cs, st));
+      HIP_TRY(launch_rownorm(nullptr, y, 2, cs, H, n, u16p(w->hidden_norm), w->rms_eps, out, H,
+                             nullptr, st));
+    } else {
+      // The GEMM writes the rows in bf16 with their fp32 tile sums of squares
+      // (half the bytes of fp32 rows, written as whole rows), inside the fp32
+      // region: y16 [n][H], then ss [n][H / 256].
+      uint16_t* y16 = reinterpret_cast<uint16_t*>(y);
+      float* ss = reinterpret_cast<float*>(y16 + static_cast<size_t>(n) * H);
+      HIP_TRY(launch_gemm_fuse_bf16(x, T * H, n, wt, wp, T * H, FuseEpi{y16, ss}, st));
+      HIP_TRY(launch_rownorm_tiles(y16, ss, n, u16p(w->hidden_norm), w->rms_eps, out, H, st));
+    }
   }
   return DFLASH_OK;
 }

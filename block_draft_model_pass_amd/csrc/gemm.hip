@@ -33,6 +33,7 @@
 // fewer tiles than CUs the k range can be split S ways (partial outputs S
 // apart, summed by the consumer).
 #include "common.h"
+#include "fuse.h"
 
 namespace dfl {
 
@@ -228,6 +229,47 @@ __device__ __forceinline__ void kv_epilogue(const f32x4 (&acc)[8][4], uint16_t* 
   }
 }
 
+// Fused context rows (EPI = 2): the two 128-row halves of the tile go
+// through the stage ring as fp32, as in kv_epilogue; then each wave takes one
+// row per round: its 64 lanes read the row's 256 values (16 bytes each; the
+// swizzle keeps a lane's 4 columns together), write them as bf16 (512
+// contiguous bytes) and reduce the row's sum of squares over the tile, from
+// the fp32 values, into ss[row][n0 / 256].  Rows past M are not stored.
+__device__ __forceinline__ void fuse_epilogue(const f32x4 (&acc)[8][4], uint16_t* st0, uint16_t* st1,
+                                              uint16_t* st2, uint16_t* st3, int m0, int n0, int M,
+                                              int wm, int wave, int lane, int r, int g, const FuseEpi& fe) {
+  const int wn = wave & 3;
+  __syncthreads();  // no wave reads the stage ring any more
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = i * 16 + 4 * g + e;
+          float* pr = half_row(st0, st1, st2, st3, row);
+#pragma unroll
+          for (int jn = 0; jn < 4; ++jn) pr[half_col(row, wn * 64 + jn * 16 + r)] = acc[i][jn][e];
+        }
+    }
+    __syncthreads();
+    const int r0 = m0 + h * 128;                       // row of A of the half's row 0
+    const int nvalid = M - r0 < 128 ? M - r0 : 128;    // rows of A in this half
+    for (int row = wave; row < nvalid; row += NT / 64) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(half_row(st0, st1, st2, st3, row) +
+                                                       half_col(row, 4 * lane));
+      const float ss = wave_sum(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]);
+      const size_t gr = static_cast<size_t>(r0 + row);
+      *reinterpret_cast<uint2*>(fe.y + gr * H + n0 + 4 * lane) =
+          make_uint2(f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16),
+                     f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16));
+      if (lane == 0) fe.ss[gr * (H / BN) + n0 / BN] = ss;
+    }
+    __syncthreads();  // the half's stage arrays are free again
+  }
+}
+
 // Split-K: block q of the tiles x S grid computes the k range
 // [s K, (s+1) K) of tile t (t' = s tiles + t) into C + s c_split; W rows are
 // ldw elements apart (S K).
@@ -237,12 +279,14 @@ __device__ __forceinline__ void kv_epilogue(const f32x4 (&acc)[8][4], uint16_t* 
 // 1 KiB block, written to LDS in lane order, and a W fragment read is that
 // block at lane x 16 bytes -- the same lanes/k slots as the swizzled
 // row-major path.
-// EPI = 0: fp32 C.  EPI = 1: the context K/V cells (kv_epilogue).
+// EPI = 0: fp32 C.  EPI = 1: the context K/V cells (kv_epilogue).  EPI = 2:
+// the fused context rows in bf16 and their tile sums of squares
+// (fuse_epilogue).
 template <bool WP, int EPI>
 __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict__ A, int lda,
                                                      int M, SegTable w, int K, int ldw,
                                                      float* __restrict__ C, int ldc, int nN,
-                                                     int tiles, size_t c_split, KvEpi kv) {
+                                                     int tiles, size_t c_split, KvEpi kv, FuseEpi fe) {
   // Five separate stage arrays (not one indexed ring): every access names its
   // stage statically, so the compiler can tell a stage being read from the
   // stages still being filled and does not wait for those loads.
@@ -458,8 +502,10 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16_nt(const uint16_t* __restrict_
           for (int jn = 0; jn < 4; ++jn) cr[jn * 16] = acc[i][jn][e];
         }
       }
-  } else {
+  } else if constexpr (EPI == 1) {
     kv_epilogue(acc, st0, st1, st2, st3, m0, n0, M, wm, wn, r, g, tid, kv);
+  } else {
+    fuse_epilogue(acc, st0, st1, st2, st3, m0, n0, M, wm, wave, lane, r, g, fe);
   }
 }
 
@@ -477,12 +523,13 @@ hipError_t launch_gemm_bf16(const uint16_t* A, int lda, int M, const SegTable& w
   const long long tiles = static_cast<long long>(nN) * nM;
   if (tiles * nsplit > 0x7fffffff) return hipErrorInvalidValue;
   const KvEpi none{};
+  const FuseEpi fnone{};
   if (w_packed)
     hipLaunchKernelGGL((k_gemm_bf16_nt<true, 0>), dim3(static_cast<unsigned>(tiles * nsplit)), dim3(NT), 0, st, A,
-                       lda, M, w, Ks, K, C, ldc, nN, static_cast<int>(tiles), c_split, none);
+                       lda, M, w, Ks, K, C, ldc, nN, static_cast<int>(tiles), c_split, none, fnone);
   else
     hipLaunchKernelGGL((k_gemm_bf16_nt<false, 0>), dim3(static_cast<unsigned>(tiles * nsplit)), dim3(NT), 0, st, A,
-                       lda, M, w, Ks, K, C, ldc, nN, static_cast<int>(tiles), c_split, none);
+                       lda, M, w, Ks, K, C, ldc, nN, static_cast<int>(tiles), c_split, none, fnone);
   return hipGetLastError();
 }
 
@@ -497,12 +544,34 @@ hipError_t launch_gemm_kv_bf16(const uint16_t* A, int lda, int M, const SegTable
   const int nN = N / BN, nM = (M + BM - 1) / BM;
   const long long tiles = static_cast<long long>(nN) * nM;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  const FuseEpi fnone{};
   if (w_packed)
     hipLaunchKernelGGL((k_gemm_bf16_nt<true, 1>), dim3(static_cast<unsigned>(tiles)), dim3(NT), 0, st, A, lda,
-                       M, w, K, K, nullptr, 0, nN, static_cast<int>(tiles), size_t{0}, kv);
+                       M, w, K, K, nullptr, 0, nN, static_cast<int>(tiles), size_t{0}, kv, fnone);
   else
     hipLaunchKernelGGL((k_gemm_bf16_nt<false, 1>), dim3(static_cast<unsigned>(tiles)), dim3(NT), 0, st, A, lda,
-                       M, w, K, K, nullptr, 0, nN, static_cast<int>(tiles), size_t{0}, kv);
+                       M, w, K, K, nullptr, 0, nN, static_cast<int>(tiles), size_t{0}, kv, fnone);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fuse_bf16(const uint16_t* A, int lda, int M, const SegTable& w, bool w_packed,
+                                 int K, const FuseEpi& fe, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  constexpr int N = H;
+  if (K % (2 * STAGES * BK) || lda % 8 || !fe.y || !fe.ss) return hipErrorInvalidValue;
+  for (int i = 0; i < w.nseg; ++i)
+    if (w.row_end[i] % BN) return hipErrorInvalidValue;
+  if (w.nseg < 1 || w.row_end[w.nseg - 1] != N) return hipErrorInvalidValue;
+  const int nN = N / BN, nM = (M + BM - 1) / BM;
+  const long long tiles = static_cast<long long>(nN) * nM;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  const KvEpi none{};
+  if (w_packed)
+    hipLaunchKernelGGL((k_gemm_bf16_nt<true, 2>), dim3(static_cast<unsigned>(tiles)), dim3(NT), 0, st, A, lda,
+                       M, w, K, K, nullptr, 0, nN, static_cast<int>(tiles), size_t{0}, none, fe);
+  else
+    hipLaunchKernelGGL((k_gemm_bf16_nt<false, 2>), dim3(static_cast<unsigned>(tiles)), dim3(NT), 0, st, A, lda,
+                       M, w, K, K, nullptr, 0, nN, static_cast<int>(tiles), size_t{0}, none, fe);
   return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 // cells (Strata PR #1426 page, "Drafter runtime": full-head NeoX
 // RoPE, theta 1e7; "Parity validation": q raw -> q normed -> q).
 #include "common.h"
+#include "fuse.h"
 
 namespace dfl {
 
@@ -58,6 +59,43 @@ __global__ __launch_bounds__(NT) void k_rownorm(float* h, const float* part, siz
     const uint2 o = make_uint2(y0 | (y1 << 16), y2 | (y3 << 16));
     *reinterpret_cast<uint2*>(out + static_cast<size_t>(b) * ostride + e) = o;
     if (out2) *reinterpret_cast<uint2*>(out2 + static_cast<size_t>(b) * H + e) = o;
+  }
+}
+
+// The RMSNorm of fused rows held in bf16 with their per-tile sums of squares
+// (fuse_epilogue): one row per block, the H / 256 tile sums added in order
+// (fp32, from the unrounded GEMM outputs), then each element scaled with the
+// gain.
+__global__ __launch_bounds__(NT) void k_rownorm_tiles(const uint16_t* y, const float* ss,
+                                                      const uint16_t* gain, float eps, uint16_t* out,
+                                                      int ostride) {
+  constexpr int NTILE = H / 256;
+  const int b = blockIdx.x;
+  uint2 yv[PER4], gv[PER4];
+#pragma unroll
+  for (int i = 0; i < PER4; ++i) {
+    const int e = 4 * (threadIdx.x + NT * i);
+    yv[i] = *reinterpret_cast<const uint2*>(y + static_cast<size_t>(b) * H + e);
+    gv[i] = *reinterpret_cast<const uint2*>(gain + e);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int t = 0; t < NTILE; ++t) sum += ss[static_cast<size_t>(b) * NTILE + t];
+  const float sc = 1.0f / sqrtf(sum / static_cast<float>(H) + eps);
+#pragma unroll
+  for (int i = 0; i < PER4; ++i) {
+    const int e = 4 * (threadIdx.x + NT * i);
+    const uint32_t w[2] = {yv[i].x, yv[i].y}, gw[2] = {gv[i].x, gv[i].y};
+    uint32_t o[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t lo = f32_to_bf16(bf16_to_f32(static_cast<uint16_t>(w[q])) * sc *
+                                      bf16_to_f32(static_cast<uint16_t>(gw[q])));
+      const uint32_t hi = f32_to_bf16(bf16_to_f32(static_cast<uint16_t>(w[q] >> 16)) * sc *
+                                      bf16_to_f32(static_cast<uint16_t>(gw[q] >> 16)));
+      o[q] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint2*>(out + static_cast<size_t>(b) * ostride + e) = make_uint2(o[0], o[1]);
   }
 }
 
@@ -260,6 +298,13 @@ hipError_t launch_rownorm(float* h, const float* part, int S, size_t part_split_
     default:
       return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_rownorm_tiles(const uint16_t* y, const float* ss, int rows, const uint16_t* gain,
+                                float eps, uint16_t* out, int out_stride, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rownorm_tiles, dim3(rows), dim3(NT), 0, st, y, ss, gain, eps, out, out_stride);
   return hipGetLastError();
 }
 
