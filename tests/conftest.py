@@ -1,4 +1,5 @@
 import os
+import re
 import sys
 
 import pytest
@@ -27,3 +28,33 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+# Errors against the oracle, collected from what each passed GPU test printed
+# (lines that name an error and carry figures in scientific notation), so that
+# the margin to each test's bar shows in the run's summary and not only in its
+# captured output.
+_ERR_FIGURE = re.compile(r"[0-9]\.[0-9]+e[-+][0-9]+")
+_ERRORS = []
+
+
+def pytest_runtest_logreport(report):
+    if report.when != "call" or not report.passed or "gpu" not in report.keywords:
+        return
+    figures = []
+    for name, text in report.sections:
+        if not name.startswith("Captured"):
+            continue
+        for line in text.splitlines():
+            if "err" in line.lower():
+                figures += [float(x) for x in _ERR_FIGURE.findall(line)]
+    if figures:
+        _ERRORS.append((report.nodeid.split("::", 1)[-1], max(figures), len(figures)))
+
+
+def pytest_terminal_summary(terminalreporter):
+    if not _ERRORS:
+        return
+    terminalreporter.section("largest error figure printed by each passed GPU test")
+    for test, worst, count in _ERRORS:
+        terminalreporter.write_line(f"{worst:.3e}  ({count:3d} figures)  {test}")
