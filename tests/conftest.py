@@ -31,10 +31,10 @@ def pytest_collection_modifyitems(config, items):
 
 
 # Errors against the oracle, collected from what each passed GPU test printed
-# (lines that name an error and carry figures in scientific notation), so that
-# the margin to each test's bar shows in the run's summary and not only in its
+# (a figure in scientific notation right after the word "err"), so that the
+# margin to each test's bar shows in the run's summary and not only in its
 # captured output.
-_ERR_FIGURE = re.compile(r"[0-9]\.[0-9]+e[-+][0-9]+")
+_ERR_FIGURE = re.compile(r"\berr\w*\s*[:=]?\s*([0-9]\.[0-9]+e[-+][0-9]+)")
 _ERRORS = []
 
 
@@ -45,9 +45,7 @@ def pytest_runtest_logreport(report):
     for name, text in report.sections:
         if not name.startswith("Captured"):
             continue
-        for line in text.splitlines():
-            if "err" in line.lower():
-                figures += [float(x) for x in _ERR_FIGURE.findall(line)]
+        figures += [float(x) for x in _ERR_FIGURE.findall(text)]
     if figures:
         _ERRORS.append((report.nodeid.split("::", 1)[-1], max(figures), len(figures)))
 
