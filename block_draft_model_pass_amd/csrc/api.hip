@@ -385,7 +385,7 @@ extern "C" int32_t dflash_fuse_context(const dflash_weights* w, const void* taps
       wt = seg1(dq, H);
       wp = true;
     }
-    // Fewer 256 x 256 output tiles than compute units (n < 6400 rows): split
+    // Fewer 256 x 256 output tiles than compute units (n <= 6400 rows): split
     // the k range in two (the fp32 region holds two partial outputs, which
     // the row norm sums).
     const int tiles = (n + 255) / 256 * (H / 256);
