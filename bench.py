@@ -232,9 +232,9 @@ def main():
         cpu_plan()
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the pass would shard as described in DESIGN.md but no multi-GPU path exists.",
-              file=sys.stderr)
+        print(f"bench.py: the draft pass runs on one GPU only (asked for --gpus {args.gpus}); "
+              "there is no multi-GPU path (the pass's split of the LM-head vocabulary and "
+              "of the KV heads over GPUs is not built).", file=sys.stderr)
         sys.exit(2)
 
     import torch
