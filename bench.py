@@ -486,7 +486,7 @@ def main():
                   "ms": round(f_ms, 4), "TFLOPs": round(flops / (f_ms * 1e-3) / 1e12, 1),
                   "frac_bf16_mfma_peak": round(flops / (f_ms * 1e-3) / 2.5e15, 4),
                   "includes": "k_gemm_bf16_nt (bf16 rows + tile sums of squares) + k_rownorm_tiles; "
-                              "up to 6400 rows k-split + k_rownorm (dflash_fuse_context)"}
+                              "k split in two + k_rownorm where that finishes sooner (dflash_fuse_context)"}
         if nf == synth.WINDOW:
             pos0 = 7 * synth.WINDOW  # 229376: the last 32768 positions before 262144
             p_ms = time_calls(lambda: fdr.project(ctx_f, pos0), max(5, args.reps // 5))

@@ -385,11 +385,16 @@ extern "C" int32_t dflash_fuse_context(const dflash_weights* w, const void* taps
       wt = seg1(dq, H);
       wp = true;
     }
-    // Fewer 256 x 256 output tiles than compute units (n <= 6400 rows): split
-    // the k range in two (the fp32 region holds two partial outputs, which
-    // the row norm sums).
+    // Each of the 256 compute units runs one 256 x 256 output tile at a time.
+    // The k range is split in two when there are fewer tiles than compute
+    // units (n <= 6400 rows), or when the halves finish in fewer tile times
+    // than whole tiles whose last wave leaves most units idle (8192 rows: 320
+    // tiles take two tile times, 640 halves three half tile times).  The fp32
+    // region then holds two partial outputs, which the row norm sums.
+    constexpr int CUS = 256;
     const int tiles = (n + 255) / 256 * (H / 256);
-    if (tiles < 256) {
+    const int waves1 = (tiles + CUS - 1) / CUS, waves2 = (2 * tiles + CUS - 1) / CUS;
+    if (tiles < CUS || waves2 < 2 * waves1) {
       const size_t cs = static_cast<size_t>(n) * H;
       HIP_TRY(launch_gemm_bf16(x, T * H, n, wt, wp, T * H, y, H, H, 2, cs, st));
       HIP_TRY(launch_rownorm(nullptr, y, 2, cs, H, n, u16p(w->hidden_norm), w->rms_eps, out, H,

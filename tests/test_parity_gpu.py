@@ -154,13 +154,14 @@ def test_few_row_paths_without_streaming_copies(dev_w, ow, n):
     assert err <= TOL and ek <= TOL and ev <= TOL
 
 
-@pytest.mark.parametrize("n", [2432, 2700, 6400, 6401])
+@pytest.mark.parametrize("n", [2432, 2700, 6400, 6401, 12801])
 def test_fuse_context_split_sampled(dev_w, ow, n):
     """Many-row fusion around the k-split rule: fewer output tiles than
     compute units split the k range in two (2432 rows: 100 tiles; 2700 rows:
-    110 tiles; 6400 rows: 250 tiles, the largest split case), 260 tiles do
-    not (6401 rows, ragged last tile: the GEMM writes bf16 rows and tile sums
-    of squares, which the tile norm reads); the oracle recomputes sampled rows
+    110 tiles; 6400 rows: 250 tiles), and so does a last wave of tiles that
+    leaves most units idle (6401 rows: 260 tiles, ragged); 510 tiles do not
+    (12801 rows, ragged last tile: the GEMM writes bf16 rows and tile sums of
+    squares, which the tile norm reads); the oracle recomputes sampled rows
     including the ends of the first panel and of the buffer."""
     say(f"fuse split n={n}")
     taps = synth.make_taps(range(5000, 5000 + n))
